@@ -1,0 +1,21 @@
+"""KATA (Kernelized Linear Attention Activations) causal forward and decode on MI355X.
+
+The compute path is the HIP library ``libkata.so`` (kernels for gfx950 behind a C
+ABI declared in ``include/kata.h``); this package is a thin ctypes binding over it
+plus the seeded input generators.  Importing the package does not load the
+library; the first call of an entry point does, and fails loudly if it is
+missing.
+"""
+_BINDING_NAMES = (
+    "KataError", "abi_version", "decode_step", "feature_map", "forward",
+    "forward_workspace_bytes", "library_path", "load_library",
+)
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

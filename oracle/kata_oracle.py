@@ -1,0 +1,245 @@
+"""Plain fp64 CPU oracle for the KATA causal forward pass and decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, calls or links it, and
+this module imports nothing from the product package.
+
+Sources (pages describing "Kernelized Linear Attention: Breaking the Capacity
+Wall with Symmetric Cones", arXiv 2607.17419):
+
+* [ABS]    the paper's abstract (fugumt.com entry for arXiv 2607.17419v1).
+* [TS-1]   gist.science technical summary of 2607.17419, section 1
+           ("Planteamiento del Problema"): normalised linear attention with a
+           fixed-size state and constant-time recurrent inference.
+* [TS-2.1] same summary, section 2.1 ("Marco Teorico"): nonnegative weights
+           certified by a self-dual cone; the denominator of normalised linear
+           attention acts as a parameter-free convex output gate.
+* [TS-2.2] same summary, section 2.2 ("Teoria de la Capacidad", item
+           "Cono PSD"): rank-one PSD feature psi(u) = u u^T, which squares the
+           raw inner product; capacity grows with the projection dimension p.
+* [TS-2.3] same summary, section 2.3: chunked form, exact O(T) chunked state.
+
+What is computed (plain definition, no blocking beyond bounding memory):
+
+    u_t = P q_t,  w_s = P k_s                    (projection to dimension p)
+    a_ts = <psi(u_t), psi(w_s)> = (u_t . w_s)^2   for s <= t, else 0
+    y_t  = sum_s a_ts v_s / sum_s a_ts            (0 where the sum is 0)
+
+with an optional initial state (S0, z0) that adds phi(q_t)^T S0 to the
+numerator and phi(q_t) . z0 to the denominator, phi(x) = vec((Px)(Px)^T) in
+the canonical row-major index i*p + j.  The final state is
+S_T = S0 + sum_s phi(k_s) v_s^T, z_T = z0 + sum_s phi(k_s).
+
+Readings where the pages leave a step open (each also listed in the design
+notes): the causal sum includes s = t (the convex gate of [TS-2.1] mixes in
+the current value); there is no temperature and no epsilon; a zero
+denominator gives y = 0; P is a p x d matrix per head.
+
+All arithmetic is float64.  bf16 inputs are decoded bit-exactly from their
+uint16 storage (``bf16_bits_to_f64``) so the oracle sees exactly the values
+the GPU sees.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "project",
+    "feature_full",
+    "feature_packed",
+    "weights",
+    "forward_quadratic",
+    "final_state",
+    "recurrence",
+    "decode_reference",
+]
+
+
+def bf16_bits_to_f64(bits):
+    """Decode bfloat16 values stored as uint16 bit patterns into float64.
+
+    bfloat16 is the upper half of an IEEE float32, so shifting the 16 stored
+    bits into the high half of a 32-bit word gives the float32 with the same
+    value; widening to float64 is exact.
+    """
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    with np.errstate(invalid="ignore"):   # NaN payloads widen to NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def project(x, P):
+    """u = P x for every vector of x ([..., d]) with P of shape [p, d] ([TS-2.2], [ABS]).
+
+    Returns [..., p] in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    return x @ P.T
+
+
+def feature_full(u):
+    """Rank-one PSD feature psi(u) = u u^T, flattened row-major: index i*p + j ([TS-2.2])."""
+    u = np.asarray(u, dtype=np.float64)
+    p = u.shape[-1]
+    return (u[..., :, None] * u[..., None, :]).reshape(u.shape[:-1] + (p * p,))
+
+
+def feature_packed(u):
+    """Symmetric packing of psi(u): the p(p+1)/2 entries i <= j in row-major order,
+    off-diagonal entries scaled by sqrt(2) so that the inner product of two
+    packed features equals that of the full features ([TS-2.2]).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    p = u.shape[-1]
+    iu, ju = np.triu_indices(p)
+    scale = np.where(iu == ju, 1.0, np.sqrt(2.0))
+    return u[..., iu] * u[..., ju] * scale
+
+
+def weights(q, k, P):
+    """Causal attention weights a_ts = ((P q_t) . (P k_s))^2 for s <= t, 0 otherwise.
+
+    q: [T, d], k: [T, d], P: [p, d].  Returns [T, T] float64.  Every entry is a
+    square, hence nonnegative ([TS-2.1], [ABS]).
+    """
+    u = project(q, P)
+    w = project(k, P)
+    a = (u @ w.T) ** 2
+    return np.tril(a)
+
+
+def _head_forward(q, k, v, P, S0, z0, rows, block):
+    """y for one head at the query rows ``rows`` (sorted int array)."""
+    u = project(q, P)            # [T, p]
+    w = project(k, P)            # [T, p]
+    v = np.asarray(v, dtype=np.float64)
+    dv = v.shape[1]
+    y = np.zeros((len(rows), dv))
+    for r0 in range(0, len(rows), block):
+        rr = rows[r0:r0 + block]
+        smax = int(rr[-1]) + 1
+        a = (u[rr] @ w[:smax].T) ** 2                   # [nb, smax]
+        a[np.arange(smax)[None, :] > rr[:, None]] = 0.0  # causal: keep s <= t
+        num = a @ v[:smax]
+        den = a.sum(axis=1)
+        if S0 is not None:
+            f = feature_full(u[rr])
+            num = num + f @ S0
+            den = den + f @ z0
+        ok = den != 0.0
+        y[r0:r0 + block][ok] = num[ok] / den[ok, None]
+    return y
+
+
+def forward_quadratic(q, k, v, P, S0=None, z0=None, rows=None, block=256):
+    """Causal normalised KATA attention by the O(T^2) definition.
+
+    q, k: [B, H, T, d]; v: [B, H, T, dv]; P: [H, p, d] (one projection per head);
+    S0: [B, H, p*p, dv] or None; z0: [B, H, p*p] or None; rows: optional sorted
+    query indices (evaluates y only there, e.g. to sample a long sequence).
+    Returns y: [B, H, len(rows) or T, dv] float64.
+
+    Definition ([TS-1], [TS-2.1], [TS-2.2], [ABS]): y_t = (sum_{s<=t} a_ts v_s
+    + phi(q_t)^T S0) / (sum_{s<=t} a_ts + phi(q_t) . z0), a_ts = ((Pq_t).(Pk_s))^2;
+    y_t = 0 where the denominator is 0.
+    """
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v); P = np.asarray(P)
+    B, H, T, _ = q.shape
+    dv = v.shape[-1]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.zeros((B, H, len(rows), dv))
+    has_init = S0 is not None or z0 is not None
+    pp = P.shape[1] * P.shape[1]
+    for b in range(B):
+        for h in range(H):
+            s0 = zz = None
+            if has_init:
+                s0 = np.zeros((pp, dv)) if S0 is None else np.asarray(S0[b, h], dtype=np.float64)
+                zz = np.zeros(pp) if z0 is None else np.asarray(z0[b, h], dtype=np.float64)
+            y[b, h] = _head_forward(q[b, h], k[b, h], v[b, h], P[h], s0, zz, rows, block)
+    return y
+
+
+def final_state(k, v, P, S0=None, z0=None):
+    """Final recurrent state after all tokens ([TS-1]: fixed-size state).
+
+    S_T = S0 + sum_s phi(k_s) v_s^T   ([B, H, p*p, dv])
+    z_T = z0 + sum_s phi(k_s)         ([B, H, p*p])
+    with phi the canonical full feature (row-major i*p + j).
+    """
+    k = np.asarray(k); v = np.asarray(v, dtype=np.float64); P = np.asarray(P)
+    B, H, T, _ = k.shape
+    p = P.shape[1]
+    ST = np.zeros((B, H, p * p, v.shape[-1]))
+    zT = np.zeros((B, H, p * p))
+    for b in range(B):
+        for h in range(H):
+            f = feature_full(project(k[b, h], P[h]))     # [T, p*p]
+            ST[b, h] = f.T @ v[b, h]
+            zT[b, h] = f.sum(axis=0)
+    if S0 is not None:
+        ST = ST + np.asarray(S0, dtype=np.float64)
+    if z0 is not None:
+        zT = zT + np.asarray(z0, dtype=np.float64)
+    return ST, zT
+
+
+def recurrence(q, k, v, P, S0=None, z0=None):
+    """Token-by-token recurrent form ([TS-1]: constant-time recurrent inference).
+
+    For each token in order: S += phi(k_t) v_t^T, z += phi(k_t), then
+    y_t = S^T phi(q_t) / (z . phi(q_t)) (0 when the denominator is 0).
+    Returns (y [B,H,T,dv], S_T, z_T).
+    """
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v, dtype=np.float64); P = np.asarray(P)
+    B, H, T, _ = q.shape
+    p = P.shape[1]
+    dv = v.shape[-1]
+    y = np.zeros((B, H, T, dv))
+    ST = np.zeros((B, H, p * p, dv))
+    zT = np.zeros((B, H, p * p))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((p * p, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            z = np.zeros(p * p) if z0 is None else np.array(z0[b, h], dtype=np.float64)
+            fq = feature_full(project(q[b, h], P[h]))
+            fk = feature_full(project(k[b, h], P[h]))
+            for t in range(T):
+                S += np.outer(fk[t], v[b, h, t])
+                z += fk[t]
+                den = fq[t] @ z
+                if den != 0.0:
+                    y[b, h, t] = (fq[t] @ S) / den
+            ST[b, h] = S
+            zT[b, h] = z
+    return y, ST, zT
+
+
+def decode_reference(S, z, q, k, v, P):
+    """One recurrent decode step for N independent streams ([TS-1], [ABS]).
+
+    S: [N, H, p*p, dv], z: [N, H, p*p] (state before the step), q, k: [N, H, d],
+    v: [N, H, dv], P: [H, p, d].  The step first folds the new token into the
+    state, then reads it out (the current token is part of its own causal sum):
+
+        S' = S + phi(k) v^T,  z' = z + phi(k),  y = S'^T phi(q) / (z' . phi(q)).
+
+    Returns (y [N, H, dv], S', z').
+    """
+    S = np.array(S, dtype=np.float64)
+    z = np.array(z, dtype=np.float64)
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v, dtype=np.float64); P = np.asarray(P)
+    N, H = q.shape[:2]
+    y = np.zeros(v.shape)
+    for h in range(H):
+        fq = feature_full(project(q[:, h], P[h]))    # [N, p*p]
+        fk = feature_full(project(k[:, h], P[h]))
+        S[:, h] += fk[:, :, None] * v[:, h, None, :]
+        z[:, h] += fk
+        den = np.einsum("nf,nf->n", fq, z[:, h])
+        num = np.einsum("nf,nfj->nj", fq, S[:, h])
+        ok = den != 0.0
+        y[ok, h] = num[ok] / den[ok, None]
+    return y, S, z

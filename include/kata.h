@@ -1,0 +1,172 @@
+/*
+ * kata.h - C ABI of libkata: the KATA (Kernelized Linear Attention Activations)
+ * causal forward pass and recurrent decode step on AMD MI355X (gfx950).
+ *
+ * Method: "Kernelized Linear Attention: Breaking the Capacity Wall with
+ * Symmetric Cones" (arXiv 2607.17419).  Citations below use
+ *   [ABS]    the paper's abstract (fugumt.com entry for 2607.17419v1),
+ *   [TS-x]   section x of the gist.science technical summary of the paper.
+ *
+ * What the library computes, per batch row b and head h, for tokens t = 0..T-1:
+ *
+ *   u_t = P_h q_t,  w_s = P_h k_s                      (P_h: p x d, [TS-2.2])
+ *   phi(x) = vec((P_h x)(P_h x)^T)                       (rank-one PSD feature, [TS-2.2])
+ *   S_t = S0 + sum_{s<=t} phi(k_s) v_s^T,  z_t = z0 + sum_{s<=t} phi(k_s)
+ *   y_t = S_t^T phi(q_t) / (z_t . phi(q_t))              ([TS-1], [TS-2.1]; y_t = 0 if the
+ *                                                        denominator is 0)
+ *
+ * i.e. normalised causal attention whose weights are ((P q_t).(P k_s))^2 >= 0.
+ * kata_forward evaluates it in the exact chunked-state form ([TS-2.3], [ABS]):
+ * per chunk of C tokens a state phi(K_c)^T [V_c | 1]; an associative prefix of
+ * those states (log depth in the number of chunks); per chunk the masked squared
+ * score tile times [V_c | 1] plus the prefix state read out through phi(Q_c);
+ * then the output gate (the division).  kata_decode_step is the constant-time
+ * recurrent step of the same attention ([TS-1], [ABS]).
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is DEVICE memory owned by the caller.  The library never
+ *    allocates, frees or synchronises; all work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and is complete when the stream
+ *    reaches it.  Outputs are undefined until then.
+ *  - Tensors are dense, row-major (C-contiguous) in the shapes given.
+ *  - Argument errors are detected on the host and returned before anything is
+ *    enqueued; KATA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ *    No exception crosses the boundary.  The functions keep no state between
+ *    calls and are safe to call from several host threads.
+ *  - State layout ("canonical"): S [.., p*p, dv] and z [.., p*p] float32 with
+ *    feature index i*p + j, i.e. S holds sum phi(k) v^T with phi = vec(w w^T).
+ *    The state is symmetric in (i, j); where the library READS a caller state
+ *    (S0/z0) it reads the entries with i <= j and takes the mirror entries as equal.
+ *  - Supported in this version: p = 16; (d, dv) = (16, 16) or (64, 64);
+ *    chunk in {32, 64, 128}; in_dtype F32 or BF16; any T >= 0 (a ragged last
+ *    chunk is handled); B*H <= 65535.  Other values return KATA_ERR_UNSUPPORTED.
+ */
+#ifndef KATA_H
+#define KATA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KATA_ABI_VERSION 1
+
+typedef enum {
+  KATA_OK = 0,
+  KATA_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  KATA_ERR_SHAPE = 2,        /* a size is negative / inconsistent / too large   */
+  KATA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (p, d, dv, chunk, dtype) */
+  KATA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
+  KATA_ERR_LAUNCH = 5        /* a kernel launch failed                          */
+} kata_status;
+
+typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype;
+
+/* How the inter-chunk state prefix is formed.
+ *  KATA_SCAN_ASSOC: chunk states are summed over leaves of `scan_leaf` chunks,
+ *    the leaf sums are combined by a log-depth (wavefront shuffle + LDS)
+ *    associative prefix, and each chunk's prefix inside a leaf is completed by a
+ *    running sum kept on chip ([TS-2.3], [ABS]: associative scan over chunk
+ *    states, depth O(log(T/C))).  scan_leaf = 1 materialises every chunk state.
+ *  KATA_SCAN_SEQUENTIAL: one leaf per sequence - the chunk states are propagated
+ *    strictly chunk after chunk (depth O(T/C)), the matched sequential baseline
+ *    the pages compare the scan against ([ABS]). */
+typedef enum { KATA_SCAN_ASSOC = 0, KATA_SCAN_SEQUENTIAL = 1 } kata_scan_mode;
+
+typedef struct {
+  int64_t B;              /* batch rows                                   */
+  int64_t H;              /* heads                                        */
+  int64_t T;              /* tokens per sequence (>= 0)                   */
+  int d;                  /* query/key head dimension                     */
+  int dv;                 /* value head dimension                         */
+  int p;                  /* projection dimension (16)                    */
+  int chunk;              /* chunk length C                               */
+  kata_dtype in_dtype;    /* dtype of q, k, v                             */
+  kata_dtype out_dtype;   /* dtype of y                                   */
+  kata_scan_mode scan;    /* see kata_scan_mode                           */
+  int scan_leaf;          /* chunks per leaf in KATA_SCAN_ASSOC; 0 = chosen by the library */
+} kata_forward_desc;
+
+/* ABI version of the loaded library (KATA_ABI_VERSION). */
+int kata_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kata_status_string(kata_status s);
+
+/* Bytes of device workspace kata_forward needs for `desc` (written to *bytes).
+ * The workspace holds the per-leaf chunk states and, after the call, their
+ * exclusive prefixes: B*H*n_leaf blocks of (ceil-packed) state, float32. */
+kata_status kata_forward_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+
+/* Causal KATA forward over whole sequences in the exact chunked-state form
+ * ([TS-2.3], [ABS]; definition in the header comment).
+ *   q  [B,H,T,d], k [B,H,T,d], v [B,H,T,dv]   in_dtype
+ *   P  [H,p,d]   float32 (one projection per head)
+ *   S0 [B,H,p*p,dv], z0 [B,H,p*p] float32 initial state, or both NULL for zero
+ *   y  [B,H,T,dv] out_dtype (written)
+ *   ST [B,H,p*p,dv], zT [B,H,p*p] float32 final state (written), or NULL if unwanted
+ *   workspace: device memory of at least kata_forward_workspace_bytes bytes,
+ *   owned by the caller, contents on entry ignored.
+ * Returns KATA_OK once everything is enqueued on `stream`. */
+kata_status kata_forward(const kata_forward_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* P,
+                         const float* S0, const float* z0,
+                         void* y,
+                         float* ST, float* zT,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* kata_forward that also records four caller-created hipEvent_t, all on `stream`:
+ * events[0] before kata_chunk_state, events[1] before kata_state_scan, events[2]
+ * before kata_chunk_intra and events[3] after it, so a caller can time each kernel
+ * of the chunked forward on the stream it runs on.  events == NULL behaves exactly
+ * like kata_forward; a NULL element returns KATA_ERR_NULL.  When nothing is launched
+ * for the chunked path (B*H == 0 or T == 0) no event is recorded. */
+kata_status kata_forward_timed(const kata_forward_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const float* P,
+                               const float* S0, const float* z0,
+                               void* y,
+                               float* ST, float* zT,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events);
+
+/* One recurrent decode step for N independent streams ([TS-1], [ABS]):
+ *   S += phi(k) v^T, z += phi(k)   (in place, canonical layout)
+ *   y  = S^T phi(q) / (z . phi(q)) (after the update; 0 if the denominator is 0)
+ *   S [N,H,p*p,dv], z [N,H,p*p] float32, read and written in place
+ *   q [N,H,d], k [N,H,d], v [N,H,dv] in_dtype; P [H,p,d] float32; y [N,H,dv] out_dtype.
+ * The state is updated in full (both mirror entries), so it stays canonical. */
+kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p,
+                             kata_dtype in_dtype, kata_dtype out_dtype,
+                             float* S, float* z,
+                             const void* q, const void* k, const void* v,
+                             const float* P, void* y, void* stream);
+
+/* Feature layouts for kata_feature_map. */
+typedef enum {
+  KATA_FEATURE_FULL = 0,         /* p*p entries, index i*p + j: phi = vec(u u^T)       */
+  KATA_FEATURE_PACKED_KEY = 1,   /* 9*p slots (delta, a): u_a u_{(a+delta) mod p},      */
+  KATA_FEATURE_PACKED_QUERY = 2  /*   delta = 0..8; query side weighted 2 off the        */
+} kata_feature_layout;           /*   diagonal; slots (8, a>=8) are 0 (see below)        */
+
+/* The feature map the chunk kernels build on chip, exposed for identity tests
+ * ([TS-2.2]: phi(q).phi(k) = ((Pq).(Pk))^2).  The packed layouts hold the
+ * p(p+1)/2 = 136 distinct entries of the symmetric u u^T in "circulant" order:
+ * slot (delta, a) = 16*delta + a holds u_a u_b with b = (a + delta) mod 16,
+ * delta = 0..8; for delta = 8 only a < 8 is distinct and slots a >= 8 hold 0.
+ * The key side carries weight 1, the query side weight 2 off the diagonal, so
+ * packed_query(q) . packed_key(k) = phi(q) . phi(k) exactly.
+ *   x [n,H,d] in dtype; P [H,p,d] float32; phi [n,H,p*p] (FULL) or [n,H,9*p] float32. */
+kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H, int d, int p,
+                             kata_feature_layout layout, kata_dtype dtype, float* phi,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATA_H */

@@ -1,0 +1,251 @@
+"""ctypes binding of libkata (include/kata.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkata.so.  torch supplies device memory (tensors) and the stream
+(the current torch stream unless one is passed).  The library is loaded on
+first use; a missing library raises KataError, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+KATA_OK, KATA_ERR_NULL, KATA_ERR_SHAPE, KATA_ERR_UNSUPPORTED, KATA_ERR_WORKSPACE, KATA_ERR_LAUNCH = range(6)
+KATA_F32, KATA_BF16 = 0, 1
+KATA_SCAN_ASSOC, KATA_SCAN_SEQUENTIAL = 0, 1
+FEATURE_LAYOUTS = {"full": 0, "packed_key": 1, "packed_query": 2}
+ABI_VERSION = 1
+P_DIM = 16
+N_PACKED = 9 * P_DIM
+
+
+class KataError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = f"{what}: " if what else ""
+        try:
+            s = _lib().kata_status_string(status).decode()
+        except Exception:  # library unavailable while formatting
+            s = f"status {status}"
+        super().__init__(msg + s)
+
+
+class ForwardDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("p", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("in_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int),
+        ("scan", ctypes.c_int),
+        ("scan_leaf", ctypes.c_int),
+    ]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.environ.get("KATA_LIBRARY", os.path.join(_PKG_DIR, "libkata.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkata.so and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise KataError(KATA_ERR_LAUNCH, f"libkata.so not found at {path}; build it with "
+                                         "`python -m kernelized_linear_attention_kata_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.kata_abi_version.restype = ci
+    lib.kata_abi_version.argtypes = []
+    lib.kata_status_string.restype = ctypes.c_char_p
+    lib.kata_status_string.argtypes = [ci]
+    lib.kata_forward_workspace_bytes.restype = ci
+    lib.kata_forward_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_forward.restype = ci
+    lib.kata_forward.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kata_forward_timed.restype = ci
+    lib.kata_forward_timed.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                       ctypes.POINTER(vp)]
+    lib.kata_decode_step.restype = ci
+    lib.kata_decode_step.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_feature_map.restype = ci
+    lib.kata_feature_map.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp, vp]
+    if lib.kata_abi_version() != ABI_VERSION:
+        raise KataError(KATA_ERR_UNSUPPORTED, f"libkata ABI {lib.kata_abi_version()} != {ABI_VERSION}")
+    _LIB = lib
+    return lib
+
+
+def _lib() -> ctypes.CDLL:
+    return load_library()
+
+
+def abi_version() -> int:
+    return _lib().kata_abi_version()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KATA_F32
+    if t == torch.bfloat16:
+        return KATA_BF16
+    raise KataError(KATA_ERR_UNSUPPORTED, f"dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream, device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != KATA_OK:
+        raise KataError(status, what)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def make_desc(B, H, T, d, dv, chunk, in_dtype, out_dtype, scan="assoc", scan_leaf=0, p=P_DIM) -> ForwardDesc:
+    return ForwardDesc(B=B, H=H, T=T, d=d, dv=dv, p=p, chunk=chunk, in_dtype=in_dtype, out_dtype=out_dtype,
+                       scan={"assoc": KATA_SCAN_ASSOC, "sequential": KATA_SCAN_SEQUENTIAL}[scan],
+                       scan_leaf=scan_leaf)
+
+
+def forward_workspace_bytes(B, H, T, d, dv, chunk, in_dtype=torch.bfloat16, out_dtype=None,
+                            scan="assoc", scan_leaf=0) -> int:
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_forward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_forward_workspace_bytes")
+    return int(n.value)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, chunk: int = 64, *,
+            S0: Optional[torch.Tensor] = None, z0: Optional[torch.Tensor] = None,
+            out_dtype: Optional[torch.dtype] = None, return_state: bool = False, scan: str = "assoc",
+            scan_leaf: int = 0, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            ST: Optional[torch.Tensor] = None, zT: Optional[torch.Tensor] = None, stream=None,
+            events=None):
+    """KATA causal forward (kata_forward).  q, k: [B,H,T,d]; v: [B,H,T,dv]; P: [H,16,d] fp32.
+
+    Returns y [B,H,T,dv] (out_dtype, default q's dtype), or (y, ST, zT) with the final
+    state when return_state.  Outputs and the workspace may be passed in preallocated.
+    events: optional four torch.cuda.Event(enable_timing=True), recorded on the stream
+    before the chunk-state, scan and intra kernels and after the last (kata_forward_timed).
+    """
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    ic, oc = _dtype_code(q.dtype), _dtype_code(out_dtype)
+    if (S0 is None) != (z0 is None):
+        raise ValueError("S0 and z0 go together")
+    if S0 is not None:
+        _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        _need(z0, "z0", (B, H, P_DIM * P_DIM), torch.float32, dev)
+    desc = make_desc(B, H, T, d, dv, chunk, ic, oc, scan, scan_leaf)
+    n = ctypes.c_size_t(0)
+    lib = _lib()
+    _check(lib.kata_forward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_forward_workspace_bytes")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    if return_state:
+        if ST is None:
+            ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
+        if zT is None:
+            zT = torch.empty((B, H, P_DIM * P_DIM), dtype=torch.float32, device=dev)
+        _need(ST, "ST", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        _need(zT, "zT", (B, H, P_DIM * P_DIM), torch.float32, dev)
+    else:
+        ST = zT = None
+    sh = _stream_handle(stream, dev)
+    evarr = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:      # torch creates the HIP event lazily on first record
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_forward_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(S0), _ptr(z0),
+                                _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
+    _check(st, "kata_forward")
+    return (y, ST, zT) if return_state else y
+
+
+def decode_step(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                P: torch.Tensor, *, out_dtype: torch.dtype = torch.float32, y: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """One recurrent step (kata_decode_step): S, z updated in place; returns y [N,H,dv]."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(S, "S", (N, H, P_DIM * P_DIM, dv), torch.float32, dev)
+    _need(z, "z", (N, H, P_DIM * P_DIM), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype), _ptr(S),
+                                 _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y),
+                                 _stream_handle(stream, dev))
+    _check(st, "kata_decode_step")
+    return y
+
+
+def feature_map(x: torch.Tensor, P: torch.Tensor, layout: str = "full", stream=None) -> torch.Tensor:
+    """phi for every vector of x [n,H,d] (kata_feature_map): [n,H,256] full or [n,H,144] packed."""
+    n, H, d = x.shape
+    dev = x.device
+    _need(x, "x", (n, H, d), device=dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    width = P_DIM * P_DIM if layout == "full" else N_PACKED
+    phi = torch.empty((n, H, width), dtype=torch.float32, device=dev)
+    st = _lib().kata_feature_map(_ptr(x), _ptr(P), n, H, d, P_DIM, FEATURE_LAYOUTS[layout], _dtype_code(x.dtype),
+                                 _ptr(phi), _stream_handle(stream, dev))
+    _check(st, "kata_feature_map")
+    return phi

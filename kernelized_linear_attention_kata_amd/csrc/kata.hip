@@ -1,0 +1,268 @@
+// kata.hip - libkata: host side of the C ABI declared in include/kata.h.
+//
+// Validates arguments on the host (nothing is enqueued on error), sizes the
+// workspace, selects the kernel instance for (input dtype, output dtype, chunk,
+// head dims) and enqueues the chunked forward as three stream-ordered launches:
+//   kata_chunk_state -> kata_state_scan -> kata_chunk_intra
+// (the chunked-state form with an associative inter-chunk scan described in the
+// gist.science summary of "Kernelized Linear Attention", arXiv 2607.17419,
+// section 2.3, and in the paper's abstract).
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+
+#include "../../include/kata.h"
+#include "kata_chunk.h"
+#include "kata_decode.h"
+#include "kata_scan.h"
+
+using namespace kata;
+
+namespace {
+
+struct Plan {
+  int64_t n_chunks = 0;
+  int64_t leaf = 1;        // chunks per leaf
+  int64_t n_leaf = 0;
+  int E = 0;               // floats per leaf state block
+  size_t ws_bytes = 0;
+};
+
+kata_status check_dtype(kata_dtype t) {
+  return (t == KATA_F32 || t == KATA_BF16) ? KATA_OK : KATA_ERR_UNSUPPORTED;
+}
+
+kata_status validate(const kata_forward_desc* d) {
+  if (!d) return KATA_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0 || d->chunk <= 0 ||
+      d->scan_leaf < 0)
+    return KATA_ERR_SHAPE;
+  if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
+  if (d->T > ((int64_t)1 << 40)) return KATA_ERR_SHAPE;
+  if (d->p != P_DIM) return KATA_ERR_UNSUPPORTED;
+  if (!((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (!(d->chunk == 32 || d->chunk == 64 || d->chunk == 128)) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(d->in_dtype) != KATA_OK || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (d->scan != KATA_SCAN_ASSOC && d->scan != KATA_SCAN_SEQUENTIAL) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+// Leaf size: SEQUENTIAL = the whole sequence; ASSOC = the caller's value, else about
+// four leaves of work per compute unit over all (b, h) so the per-leaf kernels fill
+// the 256 CUs while keeping the scanned state tensor small.
+Plan make_plan(const kata_forward_desc* d) {
+  Plan p;
+  p.n_chunks = (d->T + d->chunk - 1) / d->chunk;
+  const int64_t bh = d->B * d->H;
+  if (p.n_chunks == 0 || bh == 0) {
+    p.leaf = 1;
+  } else if (d->scan == KATA_SCAN_SEQUENTIAL) {
+    p.leaf = p.n_chunks;
+  } else if (d->scan_leaf > 0) {
+    p.leaf = d->scan_leaf < p.n_chunks ? d->scan_leaf : p.n_chunks;
+  } else {
+    const int64_t target_units = 1024;
+    int64_t leaf = (bh * p.n_chunks) / target_units;
+    if (leaf < 1) leaf = 1;
+    if (leaf > p.n_chunks) leaf = p.n_chunks;
+    p.leaf = leaf;
+  }
+  p.n_leaf = p.n_chunks == 0 ? 0 : (p.n_chunks + p.leaf - 1) / p.leaf;
+  p.E = DPACK * d->dv + DPACK;
+  p.ws_bytes = (size_t)bh * (size_t)p.n_leaf * (size_t)p.E * sizeof(float);
+  return p;
+}
+
+kata_status launch_status() {
+  return hipGetLastError() == hipSuccess ? KATA_OK : KATA_ERR_LAUNCH;
+}
+
+// Kernels whose LDS footprint exceeds the default 64 KiB dynamic limit need the
+// per-function attribute raised (gfx950 has 160 KiB of LDS per compute unit).
+template <typename F>
+kata_status allow_smem(F* fn, int bytes) {
+  if (bytes <= 65536) return KATA_OK;
+  return hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
+             ? KATA_OK
+             : KATA_ERR_LAUNCH;
+}
+
+__global__ void kata_copy_or_zero(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+template <class S, typename TIn, typename TOut>
+kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
+                        const void* v, const float* P, const float* S0, const float* z0, void* y,
+                        float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
+  const int64_t bh = d->B * d->H;
+  if (allow_smem(kata_chunk_state<S, TIn>, S::SMEM) != KATA_OK ||
+      allow_smem(kata_chunk_intra<S, TIn, TOut>, S::SMEM) != KATA_OK)
+    return KATA_ERR_LAUNCH;
+  const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
+  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return KATA_ERR_LAUNCH;
+  hipLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM, st, (const TIn*)k,
+                     (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  const int threads = (int)(pl.n_leaf >= 256 ? 256 : ((pl.n_leaf + 63) / 64) * 64);
+  const dim3 sgrid((unsigned)((pl.E + SCAN_COLS - 1) / SCAN_COLS), (unsigned)bh);
+  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return KATA_ERR_LAUNCH;
+  hipLaunchKernelGGL(kata_state_scan, sgrid, dim3(threads), 0, st, ws, pl.n_leaf, pl.E, S::DV, S0, z0, ST, zT);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  if (ev && hipEventRecord(ev[2], st) != hipSuccess) return KATA_ERR_LAUNCH;
+  hipLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, (const TIn*)q,
+                     (const TIn*)k, (const TIn*)v, P, ws, (TOut*)y, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  if (ev && hipEventRecord(ev[3], st) != hipSuccess) return KATA_ERR_LAUNCH;
+  return KATA_OK;
+}
+
+template <int C, int DIN, int DV>
+kata_status dispatch_dtypes(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
+                            const void* v, const float* P, const float* S0, const float* z0, void* y,
+                            float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
+  if (d->in_dtype == KATA_F32) {
+    using S = Shape<C, DIN, DV, true>;
+    if (d->out_dtype == KATA_F32) return run_forward<S, float, float>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+    return run_forward<S, float, bf16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+  }
+  using S = Shape<C, DIN, DV, false>;
+  if (d->out_dtype == KATA_F32) return run_forward<S, bf16, float>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+  return run_forward<S, bf16, bf16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+}
+
+template <int C>
+kata_status dispatch_dims(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
+                          const void* v, const float* P, const float* S0, const float* z0, void* y,
+                          float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
+  if (d->d == 16) return dispatch_dtypes<C, 16, 16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+  return dispatch_dtypes<C, 64, 64>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+}
+
+// The state export when there are no tokens: ST = S0 (or 0), zT = z0 (or 0).
+kata_status copy_initial_state(const kata_forward_desc* d, const float* S0, const float* z0, float* ST,
+                               float* zT, hipStream_t st) {
+  const int64_t nS = d->B * d->H * P_DIM * P_DIM * d->dv;
+  const int64_t nz = d->B * d->H * P_DIM * P_DIM;
+  if (ST) {
+    hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, ST, S0, nS);
+    hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, zT, z0, nz);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kata_abi_version(void) { return KATA_ABI_VERSION; }
+
+const char* kata_status_string(kata_status s) {
+  switch (s) {
+    case KATA_OK: return "KATA_OK";
+    case KATA_ERR_NULL: return "KATA_ERR_NULL: a required pointer is NULL";
+    case KATA_ERR_SHAPE: return "KATA_ERR_SHAPE: invalid or inconsistent size";
+    case KATA_ERR_UNSUPPORTED: return "KATA_ERR_UNSUPPORTED: p, d, dv, chunk, dtype or scan mode not supported";
+    case KATA_ERR_WORKSPACE: return "KATA_ERR_WORKSPACE: workspace missing or too small";
+    case KATA_ERR_LAUNCH: return "KATA_ERR_LAUNCH: a kernel launch failed";
+  }
+  return "KATA: unknown status";
+}
+
+kata_status kata_forward_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {
+  if (!bytes) return KATA_ERR_NULL;
+  const kata_status s = validate(desc);
+  if (s != KATA_OK) return s;
+  *bytes = make_plan(desc).ws_bytes;
+  return KATA_OK;
+}
+
+kata_status kata_forward_timed(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                               const float* P, const float* S0, const float* z0, void* y, float* ST, float* zT,
+                               void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  kata_status s = validate(desc);
+  if (s != KATA_OK) return s;
+  if ((S0 == nullptr) != (z0 == nullptr)) return KATA_ERR_NULL;
+  if ((ST == nullptr) != (zT == nullptr)) return KATA_ERR_NULL;
+  const Plan pl = make_plan(desc);
+  const int64_t bh = desc->B * desc->H;
+  hipStream_t st = (hipStream_t)stream;
+  if (bh == 0) return KATA_OK;
+  if (desc->T == 0) return copy_initial_state(desc, S0, z0, ST, zT, st);
+  if (!q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  if (!workspace || workspace_bytes < pl.ws_bytes) return KATA_ERR_WORKSPACE;
+  if (pl.n_leaf > 0x7fffffff) return KATA_ERR_SHAPE;
+  hipEvent_t ev[4];
+  hipEvent_t* evp = nullptr;
+  if (events) {
+    for (int i = 0; i < 4; ++i) {
+      if (!events[i]) return KATA_ERR_NULL;
+      ev[i] = (hipEvent_t)events[i];
+    }
+    evp = ev;
+  }
+  float* ws = (float*)workspace;
+  switch (desc->chunk) {
+    case 32: return dispatch_dims<32>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);
+    case 64: return dispatch_dims<64>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);
+    default: return dispatch_dims<128>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);
+  }
+}
+
+kata_status kata_forward(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                         const float* P, const float* S0, const float* z0, void* y, float* ST, float* zT,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return kata_forward_timed(desc, q, k, v, P, S0, z0, y, ST, zT, workspace, workspace_bytes, stream, nullptr);
+}
+
+kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                             kata_dtype out_dtype, float* S, float* z, const void* q, const void* k,
+                             const void* v, const float* P, void* y, void* stream) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N * H == 0) return KATA_OK;
+  if (N * H > 0x7fffffff) return KATA_ERR_SHAPE;
+  if (!S || !z || !q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)(N * H));
+#define KATA_DECODE(TI, TO, DVV)                                                                     \
+  hipLaunchKernelGGL((kata::kata_decode_step<TI, TO, DVV>), grid, dim3(256), 0, st, S, z, (const TI*)q, \
+                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DECODE(float, float, 64);
+    else if (fi) KATA_DECODE(float, bf16, 64);
+    else if (fo) KATA_DECODE(bf16, float, 64);
+    else KATA_DECODE(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DECODE(float, float, 16);
+    else if (fi) KATA_DECODE(float, bf16, 16);
+    else if (fo) KATA_DECODE(bf16, float, 16);
+    else KATA_DECODE(bf16, bf16, 16);
+  }
+#undef KATA_DECODE
+  return launch_status();
+}
+
+kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H, int d, int p,
+                             kata_feature_layout layout, kata_dtype dtype, float* phi, void* stream) {
+  if (n < 0 || H < 0 || d <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !(d == 16 || d == 64)) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (layout != KATA_FEATURE_FULL && layout != KATA_FEATURE_PACKED_KEY && layout != KATA_FEATURE_PACKED_QUERY)
+    return KATA_ERR_UNSUPPORTED;
+  if (n * H == 0) return KATA_OK;
+  if (n * H > 0x7fffffff) return KATA_ERR_SHAPE;
+  if (!x || !P || !phi) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)(n * H));
+  if (dtype == KATA_F32)
+    hipLaunchKernelGGL(kata::kata_feature<float>, grid, dim3(256), 0, st, (const float*)x, P, phi, (int)H, d, (int)layout);
+  else
+    hipLaunchKernelGGL(kata::kata_feature<bf16>, grid, dim3(256), 0, st, (const bf16*)x, P, phi, (int)H, d, (int)layout);
+  return launch_status();
+}
+
+}  // extern "C"

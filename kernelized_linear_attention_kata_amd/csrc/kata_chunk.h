@@ -1,0 +1,617 @@
+// kata_chunk.h - chunk-level kernels of the KATA causal forward on gfx950:
+//   kata_chunk_state  : per leaf of chunks, sum of the chunk states phi(K_c)^T [V_c | 1]
+//   kata_chunk_intra  : per leaf, for every chunk: prefix-state readout phi(Q_c) H_c,
+//                       masked squared score tile (U_c W_c^T)^2 times [V_c | 1], output
+//                       gate (the division), and the running state update H += phi(K_c)^T [V_c|1]
+// The chunked-state decomposition follows the hardware section of the gist.science
+// summary of "Kernelized Linear Attention" (arXiv 2607.17419, section 2.3: intra-chunk
+// work on matrix cores, inter-chunk state propagated by an associative scan) and the
+// exactness of that O(T) form stated in the paper's abstract.
+//
+// Work decomposition of one 256-thread workgroup (4 waves) over a chunk of C tokens:
+//  * token split  : wave w owns the 16-token M-blocks mb = w, w+4, ... < C/16 for the
+//                   projection u = P q, w = P k, the readout, the intra tile and y.
+//  * feature split: the packed state H (144 feature rows x dv columns, see below) is
+//                   held in MFMA accumulators; wave w owns rows of diagonals delta = w
+//                   and w+4 for every column block and, for delta = 8, the column blocks
+//                   nb = w (mod 4).  After each update the owners publish H as bf16 MFMA
+//                   B-fragments in LDS for the next chunk's readout.
+//
+// Packed symmetric feature ("circulant" order): slot (delta, a) = 16*delta + a holds
+// u_a * u_{(a+delta) mod 16} for delta = 0..8 (for delta = 8 only a < 8 is distinct;
+// slots a >= 8 are zero).  The 136 distinct entries of the symmetric u u^T are thus
+// stored once; the query side carries weight 2 off the diagonal so the packed inner
+// product equals the full one.  The rotation structure lets every lane build its
+// fragment from four 16-byte reads of its own token's u (no per-lane gathers).
+#pragma once
+
+#include "kata_common.h"
+
+namespace kata {
+
+// Compile-time shape of one kernel instance.
+template <int C_, int DIN_, int DV_, bool SPLIT_>
+struct Shape {
+  static constexpr int C = C_;          // chunk length (32, 64, 128)
+  static constexpr int DIN = DIN_;      // q/k head dim (16 or 64)
+  static constexpr int DV = DV_;        // value head dim (16 or 64)
+  static constexpr bool SPLIT = SPLIT_; // fp32 inputs: hi/lo bf16 operands
+  static constexpr int NB = DV / 16;    // value column blocks
+  static constexpr int NMB = C / 16;    // 16-token M-blocks per chunk
+  static constexpr int NJ = C / 32;     // 32-token K-blocks per chunk
+  static constexpr int KD = DIN >= 32 ? DIN / 32 : 1;   // projection K-blocks
+  static constexpr int MBW = (NMB + 3) / 4;             // M-blocks per wave (max)
+  static constexpr int USTR = 20;       // LDS row stride (floats) of U and W rows
+  static constexpr int WTSTR = C + 4;   // LDS row stride (floats) of W^T rows
+  // LDS footprint (bytes)
+  static constexpr int VF_BYTES = C * DV * 2;                 // V as bf16 B-fragments
+  static constexpr int HX_BYTES = READ_KB * NB * WAVE * 16;   // H as bf16 B-fragments
+  static constexpr int U_BYTES = C * USTR * 4;
+  static constexpr int WT_BYTES = P_DIM * WTSTR * 4;
+  static constexpr int Z_BYTES = DPACK * 4;
+  static constexpr int NSPLIT = SPLIT ? 2 : 1;
+  static constexpr int OFF_VF = 0;
+  static constexpr int OFF_HX = OFF_VF + NSPLIT * VF_BYTES;
+  static constexpr int OFF_U = OFF_HX + NSPLIT * HX_BYTES;
+  static constexpr int OFF_W = OFF_U + U_BYTES;
+  static constexpr int OFF_WT = OFF_W + U_BYTES;
+  static constexpr int OFF_Z = OFF_WT + WT_BYTES;
+  static constexpr int SMEM = OFF_Z + Z_BYTES;
+  // workspace block per leaf: packed S in accumulator-tile order, then packed z
+  static constexpr int E = DPACK * DV + DPACK;
+  static_assert(C == 32 || C == 64 || C == 128, "chunk");
+  static_assert(DV % 16 == 0 && DV <= 128, "dv");
+  static_assert(DIN == 16 || DIN % 32 == 0, "d");
+};
+
+// Offsets of an accumulator tile (delta, nb) inside a leaf's workspace block:
+// tile index delta*NB + nb, 256 floats per tile, lane-major, 4 floats per lane.
+template <class S>
+__device__ __forceinline__ int ws_tile_offset(int delta, int nb, int lane) {
+  return ((delta * S::NB + nb) * WAVE + lane) * 4;
+}
+
+// ---- per-chunk input staging ---------------------------------------------------
+
+// 8 consecutive input elements, loaded as 16-byte vectors.
+template <typename TIn> struct Vec8;
+template <> struct Vec8<bf16> {
+  bf16x8 x;
+  __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (bf16)0.f;
+  }
+  __device__ __forceinline__ float operator[](int i) const { return (float)x[i]; }
+};
+template <> struct Vec8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = zero4(); b = zero4(); }
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+// Register-resident copy of one chunk's inputs for this thread: the q/k MFMA
+// A-fragments of the wave's M-blocks and an 8-element slice of V per load.
+template <class S, typename TIn>
+struct ChunkIn {
+  static constexpr int NVL = (S::C * S::DV / 8 + 255) / 256;
+  Vec8<TIn> q[S::MBW][S::KD];
+  Vec8<TIn> k[S::MBW][S::KD];
+  Vec8<TIn> v[NVL];
+};
+
+// projection K-slot -> input column: lane group g, K-block kk, slot i
+template <class S>
+__device__ __forceinline__ int proj_col(int g, int kk, int i) {
+  if constexpr (S::DIN == 16) return 8 * g + i;          // one K-block, lanes g >= 2 padded
+  else return 16 * g + 8 * kk + i;                        // each lane reads 16 contiguous
+}
+template <class S>
+__device__ __forceinline__ bool proj_valid(int g) {
+  if constexpr (S::DIN == 16) return g < 2;
+  else return true;
+}
+
+template <class S, typename TIn, bool WANT_Q>
+__device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const TIn* __restrict__ q,
+                                           const TIn* __restrict__ k, const TIn* __restrict__ v,
+                                           int64_t base_tok, int64_t t0, int64_t T, int wave, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < S::MBW; ++m) {
+    const int mb = wave + 4 * m;
+    const int64_t t = t0 + mb * 16 + n;
+    const bool ok = (mb < S::NMB) && (t < T) && proj_valid<S>(g);
+#pragma unroll
+    for (int kk = 0; kk < S::KD; ++kk) {
+      const int64_t off = (base_tok + t) * S::DIN + proj_col<S>(g, kk, 0);
+      if (ok) {
+        if constexpr (WANT_Q) r.q[m][kk].load(q + off);
+        r.k[m][kk].load(k + off);
+      } else {
+        if constexpr (WANT_Q) r.q[m][kk].zero();
+        r.k[m][kk].zero();
+      }
+    }
+  }
+  const int tid = wave * WAVE + lane;
+#pragma unroll
+  for (int it = 0; it < ChunkIn<S, TIn>::NVL; ++it) {
+    const int e8 = tid + 256 * it;
+    const int s = e8 / (S::DV / 8), c8 = e8 % (S::DV / 8);
+    const int64_t t = t0 + s;
+    if ((e8 < S::C * S::DV / 8) && (t < T)) r.v[it].load(v + (base_tok + t) * S::DV + c8 * 8);
+    else r.v[it].zero();
+  }
+}
+
+// V element (s, col) of the chunk -> position in the B-fragment array
+// Vf[jj][nb][lane][slot]: K order within a 32-token block: slots 0..3 are tokens
+// 4g..4g+3, slots 4..7 are tokens 16+4g..16+4g+3 (matches the accumulator rows of
+// the intra score tiles, so those feed the next MFMA without data movement).
+template <class S>
+__device__ __forceinline__ int vf_index(int s, int col) {
+  const int jj = s >> 5, sp = s & 31;
+  const int half = sp >> 4, g = (sp & 15) >> 2, slot = half * 4 + (sp & 3);
+  const int nb = col >> 4, n = col & 15;
+  return (((jj * S::NB + nb) * WAVE) + g * 16 + n) * 8 + slot;
+}
+// token (within a 32-token K-block) held in slot i by lane group g
+__device__ __forceinline__ int kslot_token(int g, int i) {
+  return (i < 4) ? (4 * g + i) : (16 + 4 * g + (i - 4));
+}
+
+template <class S, typename TIn>
+__device__ __forceinline__ void stage_v(const ChunkIn<S, TIn>& r, bf16* vf_hi, bf16* vf_lo, int tid) {
+#pragma unroll
+  for (int it = 0; it < ChunkIn<S, TIn>::NVL; ++it) {
+    const int e8 = tid + 256 * it;
+    if (e8 < S::C * S::DV / 8) {
+      const int s = e8 / (S::DV / 8), c8 = e8 % (S::DV / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = r.v[it][i];
+        const int idx = vf_index<S>(s, c8 * 8 + i);
+        const bf16 hi = (bf16)x;
+        vf_hi[idx] = hi;
+        if constexpr (S::SPLIT) vf_lo[idx] = (bf16)(x - (float)hi);
+      }
+    }
+  }
+}
+
+template <class S>
+__device__ __forceinline__ Op8<S::SPLIT> load_vf(const bf16* vf_hi, const bf16* vf_lo, int jj, int nb, int lane) {
+  Op8<S::SPLIT> o;
+  const int idx = ((jj * S::NB + nb) * WAVE + lane) * 8;
+  o.hi = *reinterpret_cast<const bf16x8*>(vf_hi + idx);
+  if constexpr (S::SPLIT) o.lo = *reinterpret_cast<const bf16x8*>(vf_lo + idx);
+  return o;
+}
+
+// P as projection B-fragments (K = input column, N = projection index a = lane%16),
+// always split hi/lo since P is float32.
+template <class S>
+struct ProjP { Op8<true> f[S::KD]; };
+
+template <class S>
+__device__ __forceinline__ void load_P(ProjP<S>& pp, const float* __restrict__ P, int h, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < S::KD; ++kk) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x[i] = proj_valid<S>(g) ? P[((int64_t)h * P_DIM + n) * S::DIN + proj_col<S>(g, kk, i)] : 0.f;
+    pp.f[kk] = make8<true>(x);
+  }
+}
+
+// u (or w) rows of M-block m of this wave: returns the accumulator tile whose lane
+// (a = lane%16, g) holds row 4g + r, column a.
+template <class S, typename TIn>
+__device__ __forceinline__ f32x4 project_tile(const Vec8<TIn> (&x)[S::KD], const ProjP<S>& pp) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kk = 0; kk < S::KD; ++kk) {
+    if constexpr (S::SPLIT) {
+      float xf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xf[i] = x[kk][i];
+      acc = mma<true, true>(make8<true>(xf), pp.f[kk], acc);
+    } else {
+      Op8<false> a;
+      if constexpr (sizeof(TIn) == 2) {
+        a.hi = x[kk].x;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a.hi[i] = (bf16)x[kk][i];
+      }
+      acc = mma<false, true>(a, pp.f[kk], acc);
+    }
+  }
+  return acc;
+}
+
+// Build the packed phi(K)^T A-fragment for diagonal delta and 32-token K-block jj:
+// lane (a = lane%16, g) slot i holds key_weight * w_s[a] * w_s[(a+delta)%16] for the
+// token s = 32*jj + kslot_token(g, i).  WT is W^T in LDS ([a][s], row stride WTSTR).
+template <class S>
+__device__ __forceinline__ Op8<S::SPLIT> key_frag(const float* WT, int delta, int jj, int lane) {
+  const int a = lane & 15, g = lane >> 4;
+  const int b = (a + delta) & 15;
+  const float kw = key_weight(delta, a);
+  const float* ra = WT + a * S::WTSTR + 32 * jj + 4 * g;
+  const float* rb = WT + b * S::WTSTR + 32 * jj + 4 * g;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ra);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ra + 16);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(rb);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(rb + 16);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = kw * a0[i] * b0[i];
+    x[4 + i] = kw * a1[i] * b1[i];
+  }
+  return make8<S::SPLIT>(x);
+}
+
+// Feature-split ownership of the packed state accumulators.
+template <class S>
+struct StateAcc {
+  static constexpr int N8 = (S::NB + 3) / 4;   // delta = 8 column blocks per wave (max)
+  f32x4 s[2][S::NB];     // delta = wave, wave + 4
+  f32x4 s8[N8];          // delta = 8, nb = wave + 4*i
+  f32x4 z[2];            // ones-column tiles for delta = wave, wave + 4
+  f32x4 z8;              // delta = 8 (wave 0 only)
+};
+
+template <class S>
+__device__ __forceinline__ void state_zero(StateAcc<S>& st) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] = zero4();
+    st.z[j] = zero4();
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) st.s8[i] = zero4();
+  st.z8 = zero4();
+}
+
+// H += phi(K_c)^T [V_c | 1] for the tiles this wave owns.
+template <class S>
+__device__ __forceinline__ void state_update(StateAcc<S>& st, const float* WT, const bf16* vf_hi,
+                                             const bf16* vf_lo, int wave, int lane) {
+  Op8<false> ones;
+  const bf16 one = (bf16)((lane & 15) == 0 ? 1.f : 0.f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones.hi[i] = one;
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) {
+    Op8<S::SPLIT> vfr[S::NB];
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const Op8<S::SPLIT> kf = key_frag<S>(WT, wave + 4 * j, jj, lane);
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[j][nb]);
+      st.z[j] = mma<S::SPLIT, false>(kf, ones, st.z[j]);
+    }
+    if (wave < S::NB || wave == 0) {
+      const Op8<S::SPLIT> kf = key_frag<S>(WT, 8, jj, lane);
+#pragma unroll
+      for (int i = 0; i < StateAcc<S>::N8; ++i) {
+#pragma unroll
+        for (int nb = 0; nb < S::NB; ++nb)   // static register index: nb == wave + 4i
+          if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
+      }
+      if (wave == 0) st.z8 = mma<S::SPLIT, false>(kf, ones, st.z8);
+    }
+  }
+}
+
+// Stage one chunk for the state update: project keys (token split) into W^T in LDS,
+// scatter V into B-fragments.  U (queries) too when WANT_Q.
+template <class S, typename TIn, bool WANT_Q>
+__device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const ProjP<S>& pp, float* Us,
+                                            float* Ws, float* WT, bf16* vf_hi, bf16* vf_lo, int wave,
+                                            int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < S::MBW; ++m) {
+    const int mb = wave + 4 * m;
+    if (mb < S::NMB) {
+      const f32x4 w = project_tile<S, TIn>(r.k[m], pp);
+      *reinterpret_cast<f32x4*>(WT + n * S::WTSTR + mb * 16 + 4 * g) = w;
+      if constexpr (WANT_Q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ws[(mb * 16 + 4 * g + i) * S::USTR + n] = w[i];
+        const f32x4 u = project_tile<S, TIn>(r.q[m], pp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Us[(mb * 16 + 4 * g + i) * S::USTR + n] = u[i];
+      }
+    }
+  }
+  stage_v<S, TIn>(r, vf_hi, vf_lo, wave * WAVE + lane);
+}
+
+// ---- kata_chunk_state ----------------------------------------------------------
+// grid (n_leaf, B*H), block 256.  Writes the leaf's summed packed state to ws.
+template <class S, typename TIn>
+__global__ void __launch_bounds__(256)
+kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
+                 float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
+  bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
+  float* WT = reinterpret_cast<float*>(smem + S::OFF_WT);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t leaf = blockIdx.x;
+  const int64_t c0 = leaf * leaf_chunks;
+  const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
+  const int64_t base_tok = bh * T;
+
+  ProjP<S> pp;
+  load_P<S>(pp, P, h, lane);
+  StateAcc<S> st;
+  state_zero<S>(st);
+  ChunkIn<S, TIn> cur;
+  load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, c0 * S::C, T, wave, lane);
+  for (int c = 0; c < nch; ++c) {
+    stage_chunk<S, TIn, false>(cur, pp, nullptr, nullptr, WT, vf_hi, vf_lo, wave, lane);
+    if (c + 1 < nch) load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, (c0 + c + 1) * S::C, T, wave, lane);
+    __syncthreads();
+    state_update<S>(st, WT, vf_hi, vf_lo, wave, lane);
+    __syncthreads();
+  }
+  // write the leaf state (tile-native layout) and z
+  float* out = ws + (bh * (int64_t)gridDim.x + leaf) * S::E;
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int delta = wave + 4 * j;
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb)
+      *reinterpret_cast<f32x4*>(out + ws_tile_offset<S>(delta, nb, lane)) = st.s[j][nb];
+    if (n == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + delta * 16 + 4 * g) = st.z[j];
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) {
+    const int nb = wave + 4 * i;
+    if (nb < S::NB) *reinterpret_cast<f32x4*>(out + ws_tile_offset<S>(8, nb, lane)) = st.s8[i];
+  }
+  if (wave == 0 && n == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + 8 * 16 + 4 * g) = st.z8;
+}
+
+// ---- kata_chunk_intra ------------------------------------------------------------
+
+// Publish the state accumulators as bf16 readout B-fragments: Hx[kb][nb][lane][slot],
+// delta = 2*kb + slot/4 (delta 8 -> kb 4, slots 0..3).  z goes to LDS in fp32.
+template <class S>
+__device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi, bf16* hx_lo, float* zs,
+                                              int wave, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  auto put = [&](int delta, int nb, const f32x4& a) {
+    const int idx = (((delta >> 1) * S::NB + nb) * WAVE + lane) * 8 + (delta & 1) * 4;
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = (bf16)a[i];
+      if constexpr (S::SPLIT) lo[i] = (bf16)(a[i] - (float)hi[i]);
+    }
+    *reinterpret_cast<bf16x4*>(hx_hi + idx) = hi;
+    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = lo;
+  };
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int delta = wave + 4 * j;
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) put(delta, nb, st.s[j][nb]);
+    if (n == 0) *reinterpret_cast<f32x4*>(zs + delta * 16 + 4 * g) = st.z[j];
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) {
+    const int nb = wave + 4 * i;
+    if (nb < S::NB) put(8, nb, st.s8[i]);
+  }
+  if (wave == 0 && n == 0) *reinterpret_cast<f32x4*>(zs + 8 * 16 + 4 * g) = st.z8;
+}
+
+template <class S>
+__device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int wave, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int delta = wave + 4 * j;
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb)
+      st.s[j][nb] = *reinterpret_cast<const f32x4*>(in + ws_tile_offset<S>(delta, nb, lane));
+    st.z[j] = zero4();
+    if (n == 0) st.z[j] = *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + delta * 16 + 4 * g);
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) {
+    const int nb = wave + 4 * i;
+    st.s8[i] = (nb < S::NB) ? *reinterpret_cast<const f32x4*>(in + ws_tile_offset<S>(8, nb, lane)) : zero4();
+  }
+  st.z8 = zero4();
+  if (wave == 0 && n == 0) st.z8 = *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + 8 * 16 + 4 * g);
+}
+
+// Readout + intra tile + gate for one 16-token M-block mb of the chunk; writes y.
+template <class S, typename TOut>
+__device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
+                                              const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
+                                              const float* zs, TOut* __restrict__ y, int64_t base_tok,
+                                              int64_t t0, int64_t T, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  const int t = mb * 16 + n;    // token (within chunk) whose A-fragment row this lane builds
+
+  // rotated quads of u_t: Q[m] = u_t[4*((g+m)&3) .. +3]
+  f32x4 Q[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) Q[m] = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * ((g + m) & 3));
+  auto u_rot = [&](int delta, int i) -> float {   // u_t[(4g + i + delta) & 15]
+    const int m = delta >> 2, e = delta & 3;
+    const int j = i + e;
+    return j < 4 ? Q[m & 3][j] : Q[(m + 1) & 3][j - 4];
+  };
+
+  f32x4 O[S::NB];
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) O[nb] = zero4();
+  float den = 0.f;
+
+  // inter-chunk readout: O += phi(Q)^T-fragment x H-fragment, den += phi(q) . z (fp32)
+#pragma unroll
+  for (int kb = 0; kb < READ_KB; ++kb) {
+    float x[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int delta = 2 * kb + half;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (delta <= 8) {
+          const float f = query_weight(delta, 4 * g + i) * Q[0][i] * u_rot(delta, i);
+          x[half * 4 + i] = f;
+        } else {
+          x[half * 4 + i] = 0.f;
+        }
+      }
+      if (delta <= 8) {
+        const f32x4 zq = *reinterpret_cast<const f32x4*>(zs + delta * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) den += x[half * 4 + i] * zq[i];
+      }
+    }
+    const Op8<S::SPLIT> af = make8<S::SPLIT>(x);
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) {
+      const int idx = ((kb * S::NB + nb) * WAVE + lane) * 8;
+      Op8<S::SPLIT> bfr;
+      bfr.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
+      if constexpr (S::SPLIT) bfr.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
+      O[nb] = mma<S::SPLIT, S::SPLIT>(af, bfr, O[nb]);
+    }
+  }
+
+  // intra-chunk: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds X[s = 4g + r][t]
+  const f32x4 ub = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * g);
+  float ubv[4] = {ub[0], ub[1], ub[2], ub[3]};
+  const Op4<S::SPLIT> uf = make4<S::SPLIT>(ubv);
+  f32x4 A2[S::NMB];
+#pragma unroll
+  for (int j = 0; j < S::NMB; ++j) {
+    A2[j] = zero4();
+    if (j <= mb) {
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(Ws + (j * 16 + n) * S::USTR + 4 * g);
+      float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
+      const f32x4 X = mma<S::SPLIT, S::SPLIT>(make4<S::SPLIT>(wbv), uf, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = (j < mb) || (4 * g + r <= n);
+        const float a2 = keep ? X[r] * X[r] : 0.f;
+        A2[j][r] = a2;
+        den += a2;
+      }
+    }
+  }
+  // O += (A^2 masked) [V]: K-block jj = score tiles 2jj (slots 0..3) and 2jj+1 (slots 4..7)
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) {
+    if (2 * jj <= mb) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = A2[2 * jj][i];
+        x[4 + i] = (2 * jj + 1 < S::NMB) ? A2[2 * jj + 1][i] : 0.f;
+      }
+      const Op8<S::SPLIT> af = make8<S::SPLIT>(x);
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb)
+        O[nb] = mma<S::SPLIT, S::SPLIT>(af, load_vf<S>(vf_hi, vf_lo, jj, nb, lane), O[nb]);
+    }
+  }
+
+  // den(t) = sum over the 4 lane groups of this token's partial sums
+  den += __shfl_xor(den, 16);
+  den += __shfl_xor(den, 32);
+  // output gate: y = O / den; the O tile rows are tokens 4g + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float dr = __shfl(den, 4 * g + r);
+    const float inv = dr != 0.f ? 1.f / dr : 0.f;
+    const int64_t tok = t0 + mb * 16 + 4 * g + r;
+    if (tok < T) {
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) {
+        const float val = dr != 0.f ? O[nb][r] * inv : 0.f;
+        Elem<TOut>::store(y, (base_tok + tok) * S::DV + nb * 16 + n, val);
+      }
+    }
+  }
+}
+
+// grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.
+template <class S, typename TIn, typename TOut>
+__global__ void __launch_bounds__(256)
+kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                 const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
+                 int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
+  bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
+  bf16* hx_hi = reinterpret_cast<bf16*>(smem + S::OFF_HX);
+  bf16* hx_lo = reinterpret_cast<bf16*>(smem + S::OFF_HX + S::HX_BYTES);
+  float* Us = reinterpret_cast<float*>(smem + S::OFF_U);
+  float* Ws = reinterpret_cast<float*>(smem + S::OFF_W);
+  float* WT = reinterpret_cast<float*>(smem + S::OFF_WT);
+  float* zs = reinterpret_cast<float*>(smem + S::OFF_Z);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t leaf = blockIdx.x;
+  const int64_t c0 = leaf * leaf_chunks;
+  const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
+  const int64_t base_tok = bh * T;
+
+  // the readout K-block 4 holds delta = 8 in slots 0..3; slots 4..7 stay zero
+  for (int i = tid; i < S::NB * WAVE; i += 256) {
+    const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
+    *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  }
+  ProjP<S> pp;
+  load_P<S>(pp, P, h, lane);
+  StateAcc<S> st;
+  load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, lane);
+  publish_state<S>(st, hx_hi, hx_lo, zs, wave, lane);
+
+  ChunkIn<S, TIn> cur;
+  load_chunk<S, TIn, true>(cur, q, k, v, base_tok, c0 * S::C, T, wave, lane);
+  for (int c = 0; c < nch; ++c) {
+    const int64_t t0 = (c0 + c) * S::C;
+    stage_chunk<S, TIn, true>(cur, pp, Us, Ws, WT, vf_hi, vf_lo, wave, lane);
+    if (c + 1 < nch) load_chunk<S, TIn, true>(cur, q, k, v, base_tok, t0 + S::C, T, wave, lane);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m) {
+      const int mb = wave + 4 * m;
+      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, zs, y, base_tok, t0, T, lane);
+    }
+    const bool more = c + 1 < nch;
+    if (more) state_update<S>(st, WT, vf_hi, vf_lo, wave, lane);
+    __syncthreads();
+    if (more) publish_state<S>(st, hx_hi, hx_lo, zs, wave, lane);
+  }
+}
+
+}  // namespace kata

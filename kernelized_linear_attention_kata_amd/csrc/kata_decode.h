@@ -1,0 +1,129 @@
+// kata_decode.h - kata_decode_step (recurrent constant-time step) and the debug
+// feature map kernel.
+//
+// Recurrent form of normalised linear attention with a fixed-size state: the
+// gist.science summary of "Kernelized Linear Attention" (arXiv 2607.17419), section 1,
+// and the paper's abstract ("constant-time recurrent inference").  Rank-one PSD
+// feature phi(x) = vec((Px)(Px)^T): same summary, section 2.2.
+//
+// One workgroup (256 threads) per (stream, head).  The 256 x dv fp32 state is
+// streamed once in and once out with 16-byte accesses that cover contiguous 1 KB
+// per wavefront instruction; the readout partial sums are reduced with lane
+// shuffles and LDS.  The work is bound by HBM bandwidth (~0.5 flop per byte).
+#pragma once
+
+#include "kata_common.h"
+
+namespace kata {
+
+// u = P x for one vector: 256 threads, thread t computes the partial dot product of
+// row a = t/16 over the d/16 input columns j = (t%16) + 16 i, then 16-lane reduction.
+template <typename TIn>
+__device__ __forceinline__ float project_row(const TIn* __restrict__ x, const float* __restrict__ Ph, int d, int tid) {
+  const int a = tid >> 4, j0 = tid & 15;
+  float s = 0.f;
+  for (int j = j0; j < d; j += 16) s += Ph[a * d + j] * (float)x[j];
+  s += __shfl_xor(s, 8);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;   // valid in every lane of the 16-lane group of row a
+}
+
+// grid N*H, block 256.  dv in {16, 64}: each thread owns one 4-column quad.
+template <typename TIn, typename TOut, int DV>
+__global__ void __launch_bounds__(256)
+kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __restrict__ q,
+                 const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
+                 TOut* __restrict__ y, int H, int d) {
+  constexpr int D = P_DIM * P_DIM;
+  constexpr int QPR = DV / 4;               // float4 quads per state row
+  constexpr int ROWS_PER_IT = 256 / QPR;    // rows covered per pass of the block
+  constexpr int NIT = D / ROWS_PER_IT;
+  __shared__ float su[P_DIM], sw[P_DIM];
+  __shared__ float fu[D], fw[D];
+  __shared__ float red[4][DV];
+  __shared__ float dred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nh = blockIdx.x;
+  const int h = (int)(nh % H);
+  const float* Ph = P + (int64_t)h * P_DIM * d;
+
+  const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
+  const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
+  if ((tid & 15) == 0) { su[tid >> 4] = u; sw[tid >> 4] = w; }
+  __syncthreads();
+  {
+    const int a = tid >> 4, b = tid & 15;
+    fu[tid] = su[a] * su[b];
+    fw[tid] = sw[a] * sw[b];
+  }
+  __syncthreads();
+
+  const int c4 = tid % QPR;
+  f32x4 vv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vv[i] = (float)v[nh * DV + 4 * c4 + i];
+  float* Sh = S + nh * (int64_t)D * DV;
+  f32x4 acc = zero4();
+#pragma unroll 4
+  for (int it = 0; it < NIT; ++it) {
+    const int row = it * ROWS_PER_IT + tid / QPR;
+    f32x4* p = reinterpret_cast<f32x4*>(Sh + row * DV + 4 * c4);
+    f32x4 s = *p;
+    const float fwr = fw[row], fur = fu[row];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] += fwr * vv[i];
+    *p = s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += fur * s[i];
+  }
+  // z (one feature per thread) and the denominator
+  float* zh = z + nh * D;
+  const float zn = zh[tid] + fw[tid];
+  zh[tid] = zn;
+  float dp = fu[tid] * zn;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dp += __shfl_xor(dp, off);
+  // reduce acc over threads sharing the quad c4 (lanes equal mod QPR)
+#pragma unroll
+  for (int off = 32; off >= QPR; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+  }
+  if (lane < QPR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * lane + i] = acc[i];
+  }
+  if (lane == 0) dred[wave] = dp;
+  __syncthreads();
+  if (tid < DV) {
+    const float num = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float den = dred[0] + dred[1] + dred[2] + dred[3];
+    Elem<TOut>::store(y, nh * DV + tid, den != 0.f ? num / den : 0.f);
+  }
+}
+
+// Debug feature map: grid n*H, block 256.  layout 0 = full (256), 1 = packed key
+// side (144), 2 = packed query side (144).
+template <typename TIn>
+__global__ void __launch_bounds__(256)
+kata_feature(const TIn* __restrict__ x, const float* __restrict__ P, float* __restrict__ phi,
+             int H, int d, int layout) {
+  __shared__ float su[P_DIM];
+  const int tid = threadIdx.x;
+  const int64_t vi = blockIdx.x;
+  const int h = (int)(vi % H);
+  const float u = project_row<TIn>(x + vi * d, P + (int64_t)h * P_DIM * d, d, tid);
+  if ((tid & 15) == 0) su[tid >> 4] = u;
+  __syncthreads();
+  if (layout == 0) {
+    phi[vi * 256 + tid] = su[tid >> 4] * su[tid & 15];
+  } else if (tid < DPACK) {
+    const int delta = tid >> 4, a = tid & 15, b = (a + delta) & 15;
+    const float wgt = layout == 2 ? query_weight(delta, a) : key_weight(delta, a);
+    phi[vi * DPACK + tid] = wgt * su[a] * su[b];
+  }
+}
+
+}  // namespace kata

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad arguments
+on the host, before anything touches a GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kernelized_linear_attention_kata_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kata.h")
+
+
+def _lib_or_skip():
+    if not os.path.exists(Bd.library_path()):
+        pytest.skip("libkata.so not built (run __graft_entry__.build())")
+    return Bd.load_library()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kata_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("kata_forward", "kata_decode_step", "kata_forward_workspace_bytes", "kata_feature_map",
+                 "kata_abi_version", "kata_status_string"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib_or_skip()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib_or_skip()
+    assert lib.kata_abi_version() == 1
+    for s in range(6):
+        assert lib.kata_status_string(s).decode().startswith("KATA_")
+    assert b"unknown" in lib.kata_status_string(99)
+
+
+def _ws(desc):
+    lib = Bd.load_library()
+    n = ctypes.c_size_t(0)
+    st = lib.kata_forward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_formula():
+    _lib_or_skip()
+    # packed state block per leaf: 144 * dv + 144 floats
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "assoc", 16)
+    st, n = _ws(d)
+    assert st == 0 and n == 16 * (2048 // 16) * (144 * 64 + 144) * 4
+    d = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "sequential", 0)
+    st, n = _ws(d)
+    assert st == 0 and n == 6 * 1 * (144 * 65) * 4
+    d = Bd.make_desc(1, 1, 0, 16, 16, 32, Bd.KATA_F32, Bd.KATA_F32)
+    assert _ws(d) == (0, 0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", -1, Bd.KATA_ERR_SHAPE),
+    ("T", -5, Bd.KATA_ERR_SHAPE),
+    ("d", 0, Bd.KATA_ERR_SHAPE),
+    ("p", 8, Bd.KATA_ERR_UNSUPPORTED),
+    ("d", 32, Bd.KATA_ERR_UNSUPPORTED),
+    ("chunk", 48, Bd.KATA_ERR_UNSUPPORTED),
+    ("chunk", 0, Bd.KATA_ERR_SHAPE),
+    ("in_dtype", 7, Bd.KATA_ERR_UNSUPPORTED),
+    ("scan", 5, Bd.KATA_ERR_UNSUPPORTED),
+    ("H", 70000, Bd.KATA_ERR_SHAPE),
+    ("scan_leaf", -2, Bd.KATA_ERR_SHAPE),
+])
+def test_forward_rejects_bad_descriptors_before_launch(field, value, status):
+    lib = _lib_or_skip()
+    d = Bd.make_desc(1, 2, 128, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    setattr(d, field, value)
+    n = ctypes.c_size_t(0)
+    assert lib.kata_forward_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == status
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.kata_forward(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, None, fake,
+                            1 << 30, None) == status
+
+
+def test_forward_null_and_workspace_errors():
+    lib = _lib_or_skip()
+    d = Bd.make_desc(1, 2, 128, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.kata_forward(None, fake, fake, fake, fake, None, None, fake, None, None, fake, 1 << 30, None) \
+        == Bd.KATA_ERR_NULL
+    assert lib.kata_forward(ctypes.byref(d), None, fake, fake, fake, None, None, fake, None, None, fake,
+                            1 << 30, None) == Bd.KATA_ERR_NULL
+    # S0 without z0, ST without zT
+    assert lib.kata_forward(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None, None, fake,
+                            1 << 30, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_forward(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, fake, None, fake,
+                            1 << 30, None) == Bd.KATA_ERR_NULL
+    st, need = _ws(d)
+    assert st == 0 and need > 0
+    assert lib.kata_forward(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, None, None,
+                            1 << 30, None) == Bd.KATA_ERR_WORKSPACE
+    assert lib.kata_forward(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, None, fake,
+                            need - 1, None) == Bd.KATA_ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.kata_forward_workspace_bytes(ctypes.byref(d), None) == Bd.KATA_ERR_NULL
+    assert lib.kata_forward_workspace_bytes(None, ctypes.byref(n)) == Bd.KATA_ERR_NULL
+
+
+def test_forward_empty_batch_is_a_no_op():
+    lib = _lib_or_skip()
+    d = Bd.make_desc(0, 4, 128, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 0,
+                            None) == Bd.KATA_OK
+
+
+def test_decode_and_feature_reject_bad_arguments():
+    lib = _lib_or_skip()
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 7
+    assert lib.kata_decode_step(-1, 16, 64, 64, 16, 1, 0, *args, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_decode_step(4, 16, 64, 64, 8, 1, 0, *args, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step(4, 16, 64, 32, 16, 1, 0, *args, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step(4, 16, 64, 64, 16, 3, 0, *args, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step(4, 16, 64, 64, 16, 1, 0, None, fake, fake, fake, fake, fake, fake, None) \
+        == Bd.KATA_ERR_NULL
+    assert lib.kata_decode_step(0, 16, 64, 64, 16, 1, 0, None, None, None, None, None, None, None, None) \
+        == Bd.KATA_OK
+    assert lib.kata_feature_map(fake, fake, 4, 2, 64, 16, 5, 1, fake, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_feature_map(fake, fake, -1, 2, 64, 16, 0, 1, fake, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_feature_map(None, fake, 4, 2, 64, 16, 0, 1, fake, None) == Bd.KATA_ERR_NULL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("KATA_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(Bd, "_LIB", None)
+    with pytest.raises(Bd.KataError):
+        Bd.load_library()

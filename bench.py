@@ -2,7 +2,7 @@
 """Benchmark: KATA causal forward throughput on one MI355X.
 
 One step = one kata_forward call over the whole long-context workload
-(B=1, H=16, T=131072, d=dv=64, bf16 q/k/v, fp32 P, chunk 128 by default): the
+(B=1, H=16, T=131072, d=dv=64, bf16 q/k/v, fp32 P, chunk 64 by default): the
 chunk-state kernel, the associative scan of the leaf states with the final-state
 export, and the intra-chunk kernel (projection, packed PSD features, prefix
 readout, masked squared score tile, output gate).  Inputs are seeded synthetic
@@ -105,12 +105,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=128, choices=(32, 64, 128))
+    ap.add_argument("--chunk", type=int, default=64, choices=(32, 64, 128))
     ap.add_argument("--leaf", type=int, default=0, help="chunks per scan leaf (0 = library default)")
     ap.add_argument("--scan", default="assoc", choices=("assoc", "sequential"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=64)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -40,6 +40,7 @@ struct Shape {
   static constexpr int NMB = C / 16;    // 16-token M-blocks per chunk
   static constexpr int NJ = C / 32;     // 32-token K-blocks per chunk
   static constexpr int KD = DIN >= 32 ? DIN / 32 : 1;   // projection K-blocks
+  static constexpr int KV = DV >= 32 ? DV / 32 : 1;     // value-row K-blocks (transpose)
   static constexpr int MBW = (NMB + 3) / 4;             // M-blocks per wave (max)
   static constexpr int USTR = 20;       // LDS row stride (floats) of U and W rows
   static constexpr int WTSTR = C + 4;   // LDS row stride (floats) of W^T rows
@@ -94,14 +95,13 @@ template <> struct Vec8<float> {
   __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
-// Register-resident copy of one chunk's inputs for this thread: the q/k MFMA
-// A-fragments of the wave's M-blocks and an 8-element slice of V per load.
+// Register-resident copy of one chunk's inputs for this thread: the q/k/v rows of
+// the wave's 16-token M-blocks, laid out as MFMA A-fragments (lane = token row).
 template <class S, typename TIn>
 struct ChunkIn {
-  static constexpr int NVL = (S::C * S::DV / 8 + 255) / 256;
   Vec8<TIn> q[S::MBW][S::KD];
   Vec8<TIn> k[S::MBW][S::KD];
-  Vec8<TIn> v[NVL];
+  Vec8<TIn> v[S::MBW][S::KV];
 };
 
 // projection K-slot -> input column: lane group g, K-block kk, slot i
@@ -138,48 +138,69 @@ __device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const TIn* __rest
       }
     }
   }
-  const int tid = wave * WAVE + lane;
 #pragma unroll
-  for (int it = 0; it < ChunkIn<S, TIn>::NVL; ++it) {
-    const int e8 = tid + 256 * it;
-    const int s = e8 / (S::DV / 8), c8 = e8 % (S::DV / 8);
-    const int64_t t = t0 + s;
-    if ((e8 < S::C * S::DV / 8) && (t < T)) r.v[it].load(v + (base_tok + t) * S::DV + c8 * 8);
-    else r.v[it].zero();
+  for (int m = 0; m < S::MBW; ++m) {
+    const int mb = wave + 4 * m;
+    const int64_t t = t0 + mb * 16 + n;
+    const bool ok = (mb < S::NMB) && (t < T) && (S::DV >= 32 || g < 2);
+#pragma unroll
+    for (int kk = 0; kk < S::KV; ++kk) {
+      if (ok) r.v[m][kk].load(v + (base_tok + t) * S::DV + 32 * kk + 8 * g);
+      else r.v[m][kk].zero();
+    }
   }
 }
 
-// V element (s, col) of the chunk -> position in the B-fragment array
-// Vf[jj][nb][lane][slot]: K order within a 32-token block: slots 0..3 are tokens
-// 4g..4g+3, slots 4..7 are tokens 16+4g..16+4g+3 (matches the accumulator rows of
-// the intra score tiles, so those feed the next MFMA without data movement).
-template <class S>
-__device__ __forceinline__ int vf_index(int s, int col) {
-  const int jj = s >> 5, sp = s & 31;
-  const int half = sp >> 4, g = (sp & 15) >> 2, slot = half * 4 + (sp & 3);
-  const int nb = col >> 4, n = col & 15;
-  return (((jj * S::NB + nb) * WAVE) + g * 16 + n) * 8 + slot;
-}
-// token (within a 32-token K-block) held in slot i by lane group g
-__device__ __forceinline__ int kslot_token(int g, int i) {
-  return (i < 4) ? (4 * g + i) : (16 + 4 * g + (i - 4));
+// V as MFMA B-fragments in LDS: Vf[jj][nb][lane][slot], lane = 16g + n holds column
+// 16nb + n and, for the 32-token K-block jj, tokens 4g..4g+3 in slots 0..3 and
+// 16+4g..16+4g+3 in slots 4..7.  This K order is the row order of the accumulator
+// tiles of a 16-token M-block, so the squared score tiles of the intra part feed
+// the next MFMA without data movement.
+//
+// V arrives token-major (a row per lane); the transpose into column-per-lane
+// fragments is done on the matrix cores: C = V_rows x E with E a 0/1 column selector
+// (exact in bf16 -> fp32), whose accumulator tile holds V[4g+r][16nb+n] in lane (n, g),
+// i.e. 4 slots of the fragment, written with one 8-byte LDS store per lane.
+
+// selector B-fragment picking columns 16*h + n of a 32-column K-block
+__device__ __forceinline__ bf16x8 column_selector(int h, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  bf16x8 e;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = (bf16)((8 * g + i == 16 * h + n) ? 1.f : 0.f);
+  return e;
 }
 
 template <class S, typename TIn>
-__device__ __forceinline__ void stage_v(const ChunkIn<S, TIn>& r, bf16* vf_hi, bf16* vf_lo, int tid) {
+__device__ __forceinline__ void stage_v(const Vec8<TIn> (&vr)[S::KV], int mb, const bf16x8 (&sel)[2],
+                                        bf16* vf_hi, bf16* vf_lo, int lane) {
+  const int jj = mb >> 1, half = mb & 1;
+  bf16x8 xh[S::KV], xl[S::KV];
 #pragma unroll
-  for (int it = 0; it < ChunkIn<S, TIn>::NVL; ++it) {
-    const int e8 = tid + 256 * it;
-    if (e8 < S::C * S::DV / 8) {
-      const int s = e8 / (S::DV / 8), c8 = e8 % (S::DV / 8);
+  for (int kk = 0; kk < S::KV; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = r.v[it][i];
-        const int idx = vf_index<S>(s, c8 * 8 + i);
-        const bf16 hi = (bf16)x;
-        vf_hi[idx] = hi;
-        if constexpr (S::SPLIT) vf_lo[idx] = (bf16)(x - (float)hi);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const float x = vr[kk][i];
+      xh[kk][i] = (bf16)x;
+      if constexpr (S::SPLIT) xl[kk][i] = (bf16)(x - (float)xh[kk][i]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) {
+    const int kk = S::DV >= 32 ? nb >> 1 : 0;
+    const int h = S::DV >= 32 ? nb & 1 : 0;
+    const int idx = ((jj * S::NB + nb) * WAVE + lane) * 8 + half * 4;
+    const f32x4 ch = mfma32(xh[kk], sel[h], zero4());
+    bf16x4 bh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bh[r] = (bf16)ch[r];
+    *reinterpret_cast<bf16x4*>(vf_hi + idx) = bh;
+    if constexpr (S::SPLIT) {
+      const f32x4 cl = mfma32(xl[kk], sel[h], zero4());
+      bf16x4 bl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bl[r] = (bf16)cl[r];
+      *reinterpret_cast<bf16x4*>(vf_lo + idx) = bl;
     }
   }
 }
@@ -316,12 +337,12 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* WT, c
   }
 }
 
-// Stage one chunk for the state update: project keys (token split) into W^T in LDS,
-// scatter V into B-fragments.  U (queries) too when WANT_Q.
+// Stage one chunk: project keys (token split) into W^T in LDS (and queries into U,
+// plus W rows, when WANT_Q), transpose the wave's V rows into B-fragments.
 template <class S, typename TIn, bool WANT_Q>
-__device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const ProjP<S>& pp, float* Us,
-                                            float* Ws, float* WT, bf16* vf_hi, bf16* vf_lo, int wave,
-                                            int lane) {
+__device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const ProjP<S>& pp, const bf16x8 (&sel)[2],
+                                            float* Us, float* Ws, float* WT, bf16* vf_hi, bf16* vf_lo,
+                                            int wave, int lane) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int m = 0; m < S::MBW; ++m) {
@@ -336,9 +357,9 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const Proj
 #pragma unroll
         for (int i = 0; i < 4; ++i) Us[(mb * 16 + 4 * g + i) * S::USTR + n] = u[i];
       }
+      stage_v<S, TIn>(r.v[m], mb, sel, vf_hi, vf_lo, lane);
     }
   }
-  stage_v<S, TIn>(r, vf_hi, vf_lo, wave * WAVE + lane);
 }
 
 // ---- kata_chunk_state ----------------------------------------------------------
@@ -361,12 +382,13 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
 
   ProjP<S> pp;
   load_P<S>(pp, P, h, lane);
+  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
   ChunkIn<S, TIn> cur;
   load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, c0 * S::C, T, wave, lane);
   for (int c = 0; c < nch; ++c) {
-    stage_chunk<S, TIn, false>(cur, pp, nullptr, nullptr, WT, vf_hi, vf_lo, wave, lane);
+    stage_chunk<S, TIn, false>(cur, pp, sel, nullptr, nullptr, WT, vf_hi, vf_lo, wave, lane);
     if (c + 1 < nch) load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, (c0 + c + 1) * S::C, T, wave, lane);
     __syncthreads();
     state_update<S>(st, WT, vf_hi, vf_lo, wave, lane);
@@ -446,14 +468,32 @@ __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int
   if (wave == 0 && n == 0) st.z8 = *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + 8 * 16 + 4 * g);
 }
 
+// Vector store of 4 consecutive outputs.
+template <typename TOut> struct Store4;
+template <> struct Store4<float> {
+  static __device__ __forceinline__ void st(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+};
+template <> struct Store4<bf16> {
+  static __device__ __forceinline__ void st(bf16* p, const f32x4& x) {
+    bf16x4 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (bf16)x[i];
+    *reinterpret_cast<bf16x4*>(p) = b;
+  }
+};
+
 // Readout + intra tile + gate for one 16-token M-block mb of the chunk; writes y.
+// Everything is computed transposed, O^T = H^T phi(Q)^T + V^T (A o A o M)^T, by
+// feeding the same fragments to the MFMA in swapped operand order: lane (t, g) then
+// holds output columns 16nb + 4g .. 16nb + 4g + 3 of token t, so the denominator of
+// token t is lane-local and y leaves as 4-element vector stores.
 template <class S, typename TOut>
 __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
                                               const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
                                               const float* zs, TOut* __restrict__ y, int64_t base_tok,
                                               int64_t t0, int64_t T, int lane) {
   const int n = lane & 15, g = lane >> 4;
-  const int t = mb * 16 + n;    // token (within chunk) whose A-fragment row this lane builds
+  const int t = mb * 16 + n;    // token (within chunk) whose fragment column this lane builds
 
   // rotated quads of u_t: Q[m] = u_t[4*((g+m)&3) .. +3]
   f32x4 Q[4];
@@ -464,42 +504,48 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
     const int j = i + e;
     return j < 4 ? Q[m & 3][j] : Q[(m + 1) & 3][j - 4];
   };
+  // query-side weights folded into u_a: 1 on the diagonal, 2 off it, and for the
+  // diagonal delta = 8 only the 8 distinct slots a < 8 (lane groups g < 2) count
+  f32x4 ua1 = Q[0], ua2, ua8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ua2[i] = 2.f * Q[0][i];
+    ua8[i] = g < 2 ? ua2[i] : 0.f;
+  }
 
   f32x4 O[S::NB];
 #pragma unroll
   for (int nb = 0; nb < S::NB; ++nb) O[nb] = zero4();
   float den = 0.f;
 
-  // inter-chunk readout: O += phi(Q)^T-fragment x H-fragment, den += phi(q) . z (fp32)
+  // inter-chunk readout: O^T += H^T phi(Q)^T, den += phi(q) . z (fp32)
 #pragma unroll
   for (int kb = 0; kb < READ_KB; ++kb) {
     float x[8];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int delta = 2 * kb + half;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (delta <= 8) {
-          const float f = query_weight(delta, 4 * g + i) * Q[0][i] * u_rot(delta, i);
-          x[half * 4 + i] = f;
-        } else {
-          x[half * 4 + i] = 0.f;
-        }
-      }
       if (delta <= 8) {
+        const f32x4& ua = delta == 0 ? ua1 : (delta == 8 ? ua8 : ua2);
         const f32x4 zq = *reinterpret_cast<const f32x4*>(zs + delta * 16 + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) den += x[half * 4 + i] * zq[i];
+        for (int i = 0; i < 4; ++i) {
+          x[half * 4 + i] = ua[i] * u_rot(delta, i);
+          den += x[half * 4 + i] * zq[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[half * 4 + i] = 0.f;
       }
     }
-    const Op8<S::SPLIT> af = make8<S::SPLIT>(x);
+    const Op8<S::SPLIT> qf = make8<S::SPLIT>(x);
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) {
       const int idx = ((kb * S::NB + nb) * WAVE + lane) * 8;
-      Op8<S::SPLIT> bfr;
-      bfr.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
-      if constexpr (S::SPLIT) bfr.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
-      O[nb] = mma<S::SPLIT, S::SPLIT>(af, bfr, O[nb]);
+      Op8<S::SPLIT> hf;
+      hf.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
+      if constexpr (S::SPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
+      O[nb] = mma<S::SPLIT, S::SPLIT>(hf, qf, O[nb]);
     }
   }
 
@@ -524,7 +570,7 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
       }
     }
   }
-  // O += (A^2 masked) [V]: K-block jj = score tiles 2jj (slots 0..3) and 2jj+1 (slots 4..7)
+  // O^T += V^T (A^2 masked)^T: K-block jj = score tiles 2jj (slots 0..3), 2jj+1 (slots 4..7)
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) {
     if (2 * jj <= mb) {
@@ -537,25 +583,24 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
       const Op8<S::SPLIT> af = make8<S::SPLIT>(x);
 #pragma unroll
       for (int nb = 0; nb < S::NB; ++nb)
-        O[nb] = mma<S::SPLIT, S::SPLIT>(af, load_vf<S>(vf_hi, vf_lo, jj, nb, lane), O[nb]);
+        O[nb] = mma<S::SPLIT, S::SPLIT>(load_vf<S>(vf_hi, vf_lo, jj, nb, lane), af, O[nb]);
     }
   }
 
   // den(t) = sum over the 4 lane groups of this token's partial sums
   den += __shfl_xor(den, 16);
   den += __shfl_xor(den, 32);
-  // output gate: y = O / den; the O tile rows are tokens 4g + r
+  // output gate: y = O / den (0 where the denominator is 0)
+  const int64_t tok = t0 + t;
+  if (tok < T) {
+    const float inv = den != 0.f ? 1.f / den : 0.f;
+    TOut* yrow = y + (base_tok + tok) * S::DV + 4 * g;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float dr = __shfl(den, 4 * g + r);
-    const float inv = dr != 0.f ? 1.f / dr : 0.f;
-    const int64_t tok = t0 + mb * 16 + 4 * g + r;
-    if (tok < T) {
+    for (int nb = 0; nb < S::NB; ++nb) {
+      f32x4 o;
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) {
-        const float val = dr != 0.f ? O[nb][r] * inv : 0.f;
-        Elem<TOut>::store(y, (base_tok + tok) * S::DV + nb * 16 + n, val);
-      }
+      for (int r = 0; r < 4; ++r) o[r] = den != 0.f ? O[nb][r] * inv : 0.f;
+      Store4<TOut>::st(yrow + nb * 16, o);
     }
   }
 }
@@ -591,6 +636,7 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   }
   ProjP<S> pp;
   load_P<S>(pp, P, h, lane);
+  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, lane);
   publish_state<S>(st, hx_hi, hx_lo, zs, wave, lane);
@@ -599,7 +645,7 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   load_chunk<S, TIn, true>(cur, q, k, v, base_tok, c0 * S::C, T, wave, lane);
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = (c0 + c) * S::C;
-    stage_chunk<S, TIn, true>(cur, pp, Us, Ws, WT, vf_hi, vf_lo, wave, lane);
+    stage_chunk<S, TIn, true>(cur, pp, sel, Us, Ws, WT, vf_hi, vf_lo, wave, lane);
     if (c + 1 < nch) load_chunk<S, TIn, true>(cur, q, k, v, base_tok, t0 + S::C, T, wave, lane);
     __syncthreads();
 #pragma unroll

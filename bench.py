@@ -47,7 +47,7 @@ def source_hash() -> str:
 
 def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes):
     """Bytes each kernel must move at minimum (per launch), by the byte model of the path."""
-    E = 144 * dv + 144                    # packed leaf state block, floats
+    E = 144 * dv + 256                    # packed leaf state block (S slots + Z), floats
     states = B * H * n_leaf * E * 4
     tok = B * H * T
     return {
@@ -144,7 +144,7 @@ def main():
     y = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((B, H, 256, dv), dtype=torch.float32, device=dev)
     zT = torch.empty((B, H, 256), dtype=torch.float32, device=dev)
-    E = 144 * dv + 144
+    E = 144 * dv + 256
     n_leaf = ws_bytes // (B * H * E * 4)
     stream = torch.cuda.current_stream(dev)
 

@@ -47,9 +47,38 @@ kata_status validate(const kata_forward_desc* d) {
   return KATA_OK;
 }
 
-// Leaf size: SEQUENTIAL = the whole sequence; ASSOC = the caller's value, else about
-// four leaves of work per compute unit over all (b, h) so the per-leaf kernels fill
-// the 256 CUs while keeping the scanned state tensor small.
+// Concurrent workgroups of kata_chunk_intra on one MI355X (256 compute units): the
+// instance's waves per SIMD (one 4-wave workgroup per SIMD set) limited by its LDS.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kLdsPerCU = 160 * 1024;
+
+template <int C, int DV, bool SPLIT>
+int64_t intra_slots() {
+  using S = Shape<C, DV, DV, SPLIT>;
+  const int64_t by_lds = kLdsPerCU / S::SMEM;
+  const int64_t per_cu = by_lds < S::OCC_INTRA ? by_lds : S::OCC_INTRA;
+  return kComputeUnits * (per_cu < 1 ? 1 : per_cu);
+}
+
+int64_t slots_for(const kata_forward_desc* d) {
+  const bool split = d->in_dtype == KATA_F32;
+  if (d->dv == 16) {
+    if (d->chunk == 32) return split ? intra_slots<32, 16, true>() : intra_slots<32, 16, false>();
+    if (d->chunk == 64) return split ? intra_slots<64, 16, true>() : intra_slots<64, 16, false>();
+    return split ? intra_slots<128, 16, true>() : intra_slots<128, 16, false>();
+  }
+  if (d->chunk == 32) return split ? intra_slots<32, 64, true>() : intra_slots<32, 64, false>();
+  if (d->chunk == 64) return split ? intra_slots<64, 64, true>() : intra_slots<64, 64, false>();
+  return split ? intra_slots<128, 64, true>() : intra_slots<128, 64, false>();
+}
+
+// Leaf size: SEQUENTIAL = the whole sequence; ASSOC = the caller's value, else the
+// smallest number of leaves that fills the concurrent workgroup slots of the intra
+// kernel in whole rounds (leaves of at most kMaxLeaf chunks), so no round runs
+// partly empty and the scanned state tensor stays small.  The choice depends only
+// on the descriptor, so the workspace size is reproducible.
+constexpr int64_t kMaxLeaf = 64;
+
 Plan make_plan(const kata_forward_desc* d) {
   Plan p;
   p.n_chunks = (d->T + d->chunk - 1) / d->chunk;
@@ -61,14 +90,22 @@ Plan make_plan(const kata_forward_desc* d) {
   } else if (d->scan_leaf > 0) {
     p.leaf = d->scan_leaf < p.n_chunks ? d->scan_leaf : p.n_chunks;
   } else {
-    const int64_t target_units = 1024;
-    int64_t leaf = (bh * p.n_chunks) / target_units;
+    const int64_t slots = slots_for(d);
+    const int64_t units = bh * p.n_chunks;
+    int64_t rounds = (units + slots * kMaxLeaf - 1) / (slots * kMaxLeaf);
+    if (rounds < 1) rounds = 1;
+    const int64_t leaves_per_bh = (rounds * slots + bh - 1) / bh;      // want >= this many
+    int64_t leaf = (p.n_chunks + leaves_per_bh - 1) / leaves_per_bh;
     if (leaf < 1) leaf = 1;
     if (leaf > p.n_chunks) leaf = p.n_chunks;
+    // fewer leaves than slots per round would idle compute units: shrink the leaf
+    while (leaf > 1 && bh * ((p.n_chunks + leaf - 1) / leaf) < rounds * slots &&
+           bh * ((p.n_chunks + leaf - 2) / (leaf - 1)) <= rounds * slots)
+      --leaf;
     p.leaf = leaf;
   }
   p.n_leaf = p.n_chunks == 0 ? 0 : (p.n_chunks + p.leaf - 1) / p.leaf;
-  p.E = DPACK * d->dv + DPACK;
+  p.E = DPACK * d->dv + P_DIM * P_DIM;
   p.ws_bytes = (size_t)bh * (size_t)p.n_leaf * (size_t)p.E * sizeof(float);
   return p;
 }
@@ -97,12 +134,12 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
                         const void* v, const float* P, const float* S0, const float* z0, void* y,
                         float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
   const int64_t bh = d->B * d->H;
-  if (allow_smem(kata_chunk_state<S, TIn>, S::SMEM) != KATA_OK ||
+  if (allow_smem(kata_chunk_state<S, TIn>, S::SMEM_STATE) != KATA_OK ||
       allow_smem(kata_chunk_intra<S, TIn, TOut>, S::SMEM) != KATA_OK)
     return KATA_ERR_LAUNCH;
   const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return KATA_ERR_LAUNCH;
-  hipLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM, st, (const TIn*)k,
+  hipLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, (const TIn*)k,
                      (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int threads = (int)(pl.n_leaf >= 256 ? 256 : ((pl.n_leaf + 63) / 64) * 64);

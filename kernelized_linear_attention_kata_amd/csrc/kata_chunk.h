@@ -43,23 +43,30 @@ struct Shape {
   static constexpr int KV = DV >= 32 ? DV / 32 : 1;     // value-row K-blocks (transpose)
   static constexpr int MBW = (NMB + 3) / 4;             // M-blocks per wave (max)
   static constexpr int USTR = 20;       // LDS row stride (floats) of U and W rows
-  static constexpr int WTSTR = C + 4;   // LDS row stride (floats) of W^T rows
   // LDS footprint (bytes)
   static constexpr int VF_BYTES = C * DV * 2;                 // V as bf16 B-fragments
-  static constexpr int HX_BYTES = READ_KB * NB * WAVE * 16;   // H as bf16 B-fragments
-  static constexpr int U_BYTES = C * USTR * 4;
-  static constexpr int WT_BYTES = P_DIM * WTSTR * 4;
-  static constexpr int Z_BYTES = DPACK * 4;
+  static constexpr int HX_BYTES = READ_KB * NB * WAVE * 16;   // H as bf16 readout fragments
+  static constexpr int U_BYTES = C * USTR * 4;                // u rows (fp32), W rows likewise
+  static constexpr int WACC_BYTES = NMB * WAVE * 16;          // w tiles in accumulator layout
+  static constexpr int Z_BYTES = WAVE * 16;                   // Z (16 x 16) in accumulator layout
   static constexpr int NSPLIT = SPLIT ? 2 : 1;
   static constexpr int OFF_VF = 0;
   static constexpr int OFF_HX = OFF_VF + NSPLIT * VF_BYTES;
   static constexpr int OFF_U = OFF_HX + NSPLIT * HX_BYTES;
   static constexpr int OFF_W = OFF_U + U_BYTES;
-  static constexpr int OFF_WT = OFF_W + U_BYTES;
-  static constexpr int OFF_Z = OFF_WT + WT_BYTES;
+  static constexpr int OFF_WACC = OFF_W + U_BYTES;
+  static constexpr int OFF_Z = OFF_WACC + WACC_BYTES;
   static constexpr int SMEM = OFF_Z + Z_BYTES;
-  // workspace block per leaf: packed S in accumulator-tile order, then packed z
-  static constexpr int E = DPACK * DV + DPACK;
+  // kata_chunk_state needs only the V fragments and the w tiles
+  static constexpr int ST_OFF_WACC = NSPLIT * VF_BYTES;
+  static constexpr int SMEM_STATE = ST_OFF_WACC + WACC_BYTES;
+  // waves per SIMD each kernel is compiled for (register budget 512 / OCC): the
+  // largest that fits without spilling on gfx950
+  static constexpr int OCC_INTRA = DV <= 16 ? (C == 128 ? 3 : 4) : ((SPLIT || C == 128) ? 2 : 3);
+  static constexpr int OCC_STATE = DV <= 16 ? 4 : (SPLIT ? 2 : 3);
+  // workspace block per leaf: packed S in accumulator-tile order, then the 16 x 16
+  // normaliser matrix Z = sum w w^T (z = vec(Z)) as one accumulator tile
+  static constexpr int E = DPACK * DV + P_DIM * P_DIM;
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(DV % 16 == 0 && DV <= 128, "dv");
   static_assert(DIN == 16 || DIN % 32 == 0, "d");
@@ -258,25 +265,39 @@ __device__ __forceinline__ f32x4 project_tile(const Vec8<TIn> (&x)[S::KD], const
   return acc;
 }
 
-// Build the packed phi(K)^T A-fragment for diagonal delta and 32-token K-block jj:
-// lane (a = lane%16, g) slot i holds key_weight * w_s[a] * w_s[(a+delta)%16] for the
-// token s = 32*jj + kslot_token(g, i).  WT is W^T in LDS ([a][s], row stride WTSTR).
-template <class S>
-__device__ __forceinline__ Op8<S::SPLIT> key_frag(const float* WT, int delta, int jj, int lane) {
-  const int a = lane & 15, g = lane >> 4;
-  const int b = (a + delta) & 15;
-  const float kw = key_weight(delta, a);
-  const float* ra = WT + a * S::WTSTR + 32 * jj + 4 * g;
-  const float* rb = WT + b * S::WTSTR + 32 * jj + 4 * g;
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ra);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ra + 16);
-  const f32x4 b0 = *reinterpret_cast<const f32x4*>(rb);
-  const f32x4 b1 = *reinterpret_cast<const f32x4*>(rb + 16);
+// Row rotation inside each 16-lane row: lane a receives the value of lane
+// (a + DELTA) mod 16.  DPP row_ror:R moves lane i's value to lane (i + R) mod 16, so
+// the rotation is row_ror:(16 - DELTA).
+template <int DELTA>
+__device__ __forceinline__ float row_plus(float x) {
+  if constexpr (DELTA % 16 == 0) {
+    return x;
+  } else {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + (16 - DELTA % 16), 0xf, 0xf,
+                                                      false));
+  }
+}
+
+// Packed phi(K)^T A-fragment: lane (a = lane%16, g) slot i holds w_s[a] * w_s[b]
+// for the token s of slot i, with b = (a + delta) % 16.  wa0/wa1 are the key
+// projection tiles of the two 16-token M-blocks of the K-block in accumulator layout
+// (lane (a, g) holds w_{4g+r}[a]); wb0/wb1 the same tiles with the lanes rotated so
+// lane a holds w[(a + d0) % 16]; ROT (a compile-time DPP row rotation) adds the rest
+// of delta = d0 + ROT.  Slots (8, a >= 8) repeat the pairs of a < 8 and are zeroed.
+template <class S, int ROT, bool DELTA8>
+__device__ __forceinline__ Op8<S::SPLIT> key_frag(const f32x4& wa0, const f32x4& wa1, const f32x4& wb0,
+                                                  const f32x4& wb1, int lane) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = kw * a0[i] * b0[i];
-    x[4 + i] = kw * a1[i] * b1[i];
+    x[i] = wa0[i] * row_plus<ROT>(wb0[i]);
+    x[4 + i] = wa1[i] * row_plus<ROT>(wb1[i]);
+  }
+  if constexpr (DELTA8) {
+    if ((lane & 15) >= 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
   }
   return make8<S::SPLIT>(x);
 }
@@ -287,8 +308,7 @@ struct StateAcc {
   static constexpr int N8 = (S::NB + 3) / 4;   // delta = 8 column blocks per wave (max)
   f32x4 s[2][S::NB];     // delta = wave, wave + 4
   f32x4 s8[N8];          // delta = 8, nb = wave + 4*i
-  f32x4 z[2];            // ones-column tiles for delta = wave, wave + 4
-  f32x4 z8;              // delta = 8 (wave 0 only)
+  f32x4 Z;               // normaliser matrix, wave 0 only: lane (b, g) holds Z[4g+r][b]
 };
 
 template <class S>
@@ -297,51 +317,66 @@ __device__ __forceinline__ void state_zero(StateAcc<S>& st) {
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] = zero4();
-    st.z[j] = zero4();
   }
 #pragma unroll
   for (int i = 0; i < StateAcc<S>::N8; ++i) st.s8[i] = zero4();
-  st.z8 = zero4();
+  st.Z = zero4();
 }
 
-// H += phi(K_c)^T [V_c | 1] for the tiles this wave owns.
+// H += phi(K_c)^T V_c for the tiles this wave owns; wave 0 also Z += W_c^T W_c.
+// Wave w owns the diagonals w and w + 4 (and delta = 8 for some column blocks): it
+// reads its key tiles once plainly and once with the lanes rotated by w (a permuted,
+// conflict-free LDS read), after which every diagonal it needs is a fixed DPP
+// rotation (0, 4 or 8) away.  The z part of the chunk state, sum_s phi(k_s), is
+// vec(Z): the W fragment of a K-block is at the same time the A operand W^T (lane =
+// feature row a) and the B operand W (lane = column b), so one MFMA per K-block
+// updates all 256 entries.
 template <class S>
-__device__ __forceinline__ void state_update(StateAcc<S>& st, const float* WT, const bf16* vf_hi,
+__device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc, const bf16* vf_hi,
                                              const bf16* vf_lo, int wave, int lane) {
-  Op8<false> ones;
-  const bf16 one = (bf16)((lane & 15) == 0 ? 1.f : 0.f);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones.hi[i] = one;
+  const int rot_lane = (lane & ~15) | ((lane + wave) & 15);
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) {
+    const f32x4 wa0 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj) * WAVE + lane) * 4);
+    const f32x4 wa1 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj + 1) * WAVE + lane) * 4);
+    const f32x4 wr0 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj) * WAVE + rot_lane) * 4);
+    const f32x4 wr1 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj + 1) * WAVE + rot_lane) * 4);
     Op8<S::SPLIT> vfr[S::NB];
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
+    {
+      const Op8<S::SPLIT> kf = key_frag<S, 0, false>(wa0, wa1, wr0, wr1, lane);     // delta = w
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const Op8<S::SPLIT> kf = key_frag<S>(WT, wave + 4 * j, jj, lane);
-#pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[j][nb]);
-      st.z[j] = mma<S::SPLIT, false>(kf, ones, st.z[j]);
+      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
     }
-    if (wave < S::NB || wave == 0) {
-      const Op8<S::SPLIT> kf = key_frag<S>(WT, 8, jj, lane);
+    {
+      const Op8<S::SPLIT> kf = key_frag<S, 4, false>(wa0, wa1, wr0, wr1, lane);     // delta = w + 4
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
+    }
+    if (wave < S::NB) {
+      const Op8<S::SPLIT> kf = key_frag<S, 8, true>(wa0, wa1, wa0, wa1, lane);      // delta = 8
 #pragma unroll
       for (int i = 0; i < StateAcc<S>::N8; ++i) {
 #pragma unroll
         for (int nb = 0; nb < S::NB; ++nb)   // static register index: nb == wave + 4i
           if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
       }
-      if (wave == 0) st.z8 = mma<S::SPLIT, false>(kf, ones, st.z8);
+    }
+    if (wave == 0) {
+      float x[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+      const Op8<true> wf = make8<true>(x);   // hi/lo: Z feeds the denominator
+      st.Z = mma<true, true>(wf, wf, st.Z);
     }
   }
 }
 
-// Stage one chunk: project keys (token split) into W^T in LDS (and queries into U,
-// plus W rows, when WANT_Q), transpose the wave's V rows into B-fragments.
+// Stage one chunk: project keys (token split) into W tiles in LDS (accumulator
+// layout, one 16-byte slot per lane), queries into U rows and keys into W rows when
+// WANT_Q, and transpose the wave's V rows into B-fragments.
 template <class S, typename TIn, bool WANT_Q>
 __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const ProjP<S>& pp, const bf16x8 (&sel)[2],
-                                            float* Us, float* Ws, float* WT, bf16* vf_hi, bf16* vf_lo,
+                                            float* Us, float* Ws, float* Wacc, bf16* vf_hi, bf16* vf_lo,
                                             int wave, int lane) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -349,7 +384,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const Proj
     const int mb = wave + 4 * m;
     if (mb < S::NMB) {
       const f32x4 w = project_tile<S, TIn>(r.k[m], pp);
-      *reinterpret_cast<f32x4*>(WT + n * S::WTSTR + mb * 16 + 4 * g) = w;
+      *reinterpret_cast<f32x4*>(Wacc + (mb * WAVE + lane) * 4) = w;
       if constexpr (WANT_Q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ws[(mb * 16 + 4 * g + i) * S::USTR + n] = w[i];
@@ -365,14 +400,15 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const Proj
 // ---- kata_chunk_state ----------------------------------------------------------
 // grid (n_leaf, B*H), block 256.  Writes the leaf's summed packed state to ws.
 template <class S, typename TIn>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, S::OCC_STATE)
 kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
                  float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
   bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
-  float* WT = reinterpret_cast<float*>(smem + S::OFF_WT);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float* Wacc = reinterpret_cast<float*>(smem + S::ST_OFF_WACC);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
   const int64_t leaf = blockIdx.x;
@@ -388,39 +424,36 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   ChunkIn<S, TIn> cur;
   load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, c0 * S::C, T, wave, lane);
   for (int c = 0; c < nch; ++c) {
-    stage_chunk<S, TIn, false>(cur, pp, sel, nullptr, nullptr, WT, vf_hi, vf_lo, wave, lane);
+    stage_chunk<S, TIn, false>(cur, pp, sel, nullptr, nullptr, Wacc, vf_hi, vf_lo, wave, lane);
     if (c + 1 < nch) load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, (c0 + c + 1) * S::C, T, wave, lane);
     __syncthreads();
-    state_update<S>(st, WT, vf_hi, vf_lo, wave, lane);
+    state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);
     __syncthreads();
   }
-  // write the leaf state (tile-native layout) and z
+  // write the leaf state (tile-native layout) and Z
   float* out = ws + (bh * (int64_t)gridDim.x + leaf) * S::E;
-  const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int delta = wave + 4 * j;
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb)
       *reinterpret_cast<f32x4*>(out + ws_tile_offset<S>(delta, nb, lane)) = st.s[j][nb];
-    if (n == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + delta * 16 + 4 * g) = st.z[j];
   }
 #pragma unroll
   for (int i = 0; i < StateAcc<S>::N8; ++i) {
     const int nb = wave + 4 * i;
     if (nb < S::NB) *reinterpret_cast<f32x4*>(out + ws_tile_offset<S>(8, nb, lane)) = st.s8[i];
   }
-  if (wave == 0 && n == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + 8 * 16 + 4 * g) = st.z8;
+  if (wave == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + lane * 4) = st.Z;
 }
 
 // ---- kata_chunk_intra ------------------------------------------------------------
 
-// Publish the state accumulators as bf16 readout B-fragments: Hx[kb][nb][lane][slot],
-// delta = 2*kb + slot/4 (delta 8 -> kb 4, slots 0..3).  z goes to LDS in fp32.
+// Publish the state accumulators as bf16 readout fragments: Hx[kb][nb][lane][slot],
+// delta = 2*kb + slot/4 (delta 8 -> kb 4, slots 0..3); wave 0 publishes Z in fp32.
 template <class S>
-__device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi, bf16* hx_lo, float* zs,
+__device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi, bf16* hx_lo, float* Zs,
                                               int wave, int lane) {
-  const int n = lane & 15, g = lane >> 4;
   auto put = [&](int delta, int nb, const f32x4& a) {
     const int idx = (((delta >> 1) * S::NB + nb) * WAVE + lane) * 8 + (delta & 1) * 4;
     bf16x4 hi, lo;
@@ -437,35 +470,30 @@ __device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi
     const int delta = wave + 4 * j;
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) put(delta, nb, st.s[j][nb]);
-    if (n == 0) *reinterpret_cast<f32x4*>(zs + delta * 16 + 4 * g) = st.z[j];
   }
 #pragma unroll
   for (int i = 0; i < StateAcc<S>::N8; ++i) {
     const int nb = wave + 4 * i;
     if (nb < S::NB) put(8, nb, st.s8[i]);
   }
-  if (wave == 0 && n == 0) *reinterpret_cast<f32x4*>(zs + 8 * 16 + 4 * g) = st.z8;
+  if (wave == 0) *reinterpret_cast<f32x4*>(Zs + lane * 4) = st.Z;
 }
 
 template <class S>
 __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int wave, int lane) {
-  const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int delta = wave + 4 * j;
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb)
       st.s[j][nb] = *reinterpret_cast<const f32x4*>(in + ws_tile_offset<S>(delta, nb, lane));
-    st.z[j] = zero4();
-    if (n == 0) st.z[j] = *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + delta * 16 + 4 * g);
   }
 #pragma unroll
   for (int i = 0; i < StateAcc<S>::N8; ++i) {
     const int nb = wave + 4 * i;
     st.s8[i] = (nb < S::NB) ? *reinterpret_cast<const f32x4*>(in + ws_tile_offset<S>(8, nb, lane)) : zero4();
   }
-  st.z8 = zero4();
-  if (wave == 0 && n == 0) st.z8 = *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + 8 * 16 + 4 * g);
+  st.Z = wave == 0 ? *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + lane * 4) : zero4();
 }
 
 // Vector store of 4 consecutive outputs.
@@ -490,7 +518,7 @@ template <> struct Store4<bf16> {
 template <class S, typename TOut>
 __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
                                               const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
-                                              const float* zs, TOut* __restrict__ y, int64_t base_tok,
+                                              const float* Zs, TOut* __restrict__ y, int64_t base_tok,
                                               int64_t t0, int64_t T, int lane) {
   const int n = lane & 15, g = lane >> 4;
   const int t = mb * 16 + n;    // token (within chunk) whose fragment column this lane builds
@@ -516,26 +544,22 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   f32x4 O[S::NB];
 #pragma unroll
   for (int nb = 0; nb < S::NB; ++nb) O[nb] = zero4();
-  float den = 0.f;
 
-  // inter-chunk readout: O^T += H^T phi(Q)^T, den += phi(q) . z (fp32)
+  // inter-chunk readout: O^T += H^T phi(Q)^T
 #pragma unroll
   for (int kb = 0; kb < READ_KB; ++kb) {
     float x[8];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int delta = 2 * kb + half;
-      if (delta <= 8) {
-        const f32x4& ua = delta == 0 ? ua1 : (delta == 8 ? ua8 : ua2);
-        const f32x4 zq = *reinterpret_cast<const f32x4*>(zs + delta * 16 + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        if (delta <= 8) {
+          const f32x4& ua = delta == 0 ? ua1 : (delta == 8 ? ua8 : ua2);
           x[half * 4 + i] = ua[i] * u_rot(delta, i);
-          den += x[half * 4 + i] * zq[i];
+        } else {
+          x[half * 4 + i] = 0.f;
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[half * 4 + i] = 0.f;
       }
     }
     const Op8<S::SPLIT> qf = make8<S::SPLIT>(x);
@@ -547,6 +571,16 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
       if constexpr (S::SPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
       O[nb] = mma<S::SPLIT, S::SPLIT>(hf, qf, O[nb]);
     }
+  }
+  // phi(q_t) . z = u_t^T Z u_t: (Z U^T)[4g + r][t] from one 16x16x16 MFMA (Z symmetric,
+  // so its accumulator tile is its own A fragment), dotted with u_t[4g..4g+3]
+  float den;
+  {
+    const f32x4 zt = *reinterpret_cast<const f32x4*>(Zs + lane * 4);
+    float zv[4] = {zt[0], zt[1], zt[2], zt[3]};
+    float uv[4] = {Q[0][0], Q[0][1], Q[0][2], Q[0][3]};
+    const f32x4 zu = mma<true, true>(make4<true>(zv), make4<true>(uv), zero4());
+    den = zu[0] * Q[0][0] + zu[1] * Q[0][1] + zu[2] * Q[0][2] + zu[3] * Q[0][3];
   }
 
   // intra-chunk: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds X[s = 4g + r][t]
@@ -607,7 +641,7 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
 
 // grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.
 template <class S, typename TIn, typename TOut>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, S::OCC_INTRA)
 kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                  const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
                  int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
@@ -618,9 +652,10 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   bf16* hx_lo = reinterpret_cast<bf16*>(smem + S::OFF_HX + S::HX_BYTES);
   float* Us = reinterpret_cast<float*>(smem + S::OFF_U);
   float* Ws = reinterpret_cast<float*>(smem + S::OFF_W);
-  float* WT = reinterpret_cast<float*>(smem + S::OFF_WT);
-  float* zs = reinterpret_cast<float*>(smem + S::OFF_Z);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float* Wacc = reinterpret_cast<float*>(smem + S::OFF_WACC);
+  float* Zs = reinterpret_cast<float*>(smem + S::OFF_Z);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
   const int64_t leaf = blockIdx.x;
@@ -639,24 +674,24 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, lane);
-  publish_state<S>(st, hx_hi, hx_lo, zs, wave, lane);
+  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, lane);
 
   ChunkIn<S, TIn> cur;
   load_chunk<S, TIn, true>(cur, q, k, v, base_tok, c0 * S::C, T, wave, lane);
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = (c0 + c) * S::C;
-    stage_chunk<S, TIn, true>(cur, pp, sel, Us, Ws, WT, vf_hi, vf_lo, wave, lane);
+    stage_chunk<S, TIn, true>(cur, pp, sel, Us, Ws, Wacc, vf_hi, vf_lo, wave, lane);
     if (c + 1 < nch) load_chunk<S, TIn, true>(cur, q, k, v, base_tok, t0 + S::C, T, wave, lane);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < S::MBW; ++m) {
       const int mb = wave + 4 * m;
-      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, zs, y, base_tok, t0, T, lane);
+      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, y, base_tok, t0, T, lane);
     }
     const bool more = c + 1 < nch;
-    if (more) state_update<S>(st, WT, vf_hi, vf_lo, wave, lane);
+    if (more) state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);
     __syncthreads();
-    if (more) publish_state<S>(st, hx_hi, hx_lo, zs, wave, lane);
+    if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, lane);
   }
 }
 

@@ -6,7 +6,7 @@
 // state propagation is an associative scan (parallel prefix sum) of depth
 // O(log(T/C)).  The combine operator on states [S | z] is elementwise addition.
 //
-// Layout: ws[bh][leaf][e], e < E (packed state block, see kata_chunk.h).  One
+// Layout: ws[bh][leaf][e], e < E = 144*dv + 256 (packed S then Z, see kata_chunk.h).  One
 // workgroup owns 32 consecutive elements e of one (b, h) and walks the leaves in
 // passes of blockDim.x rows: lane = leaf row, so every lane moves 128 contiguous
 // bytes per pass.  Within a pass the prefix across rows is a log-depth
@@ -21,29 +21,36 @@ namespace kata {
 
 constexpr int SCAN_COLS = 32;
 
-// packed element e of a leaf block -> (feature pair (a, b), column, is_z); returns
-// false for the unused slots (delta = 8, a >= 8).
-__device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, int& col, bool& is_z) {
+// Element e of a leaf block -> canonical feature pair (a, b), value column and
+// whether it is a z entry.  S part: packed slot (delta, a) in accumulator-tile order,
+// pair (a, (a + delta) mod 16), stored once for both mirror entries (mirror = true
+// when a != b).  z part: the 16 x 16 matrix Z in accumulator-tile order (lane
+// (b, g) holds Z[4g + r][b]), every entry its own (mirror = false).  Returns false
+// for the unused packed slots (delta = 8, a >= 8).
+__device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, int& col, bool& is_z,
+                                               bool& mirror) {
   const int nb_count = dv / 16;
-  int delta;
   if (e < DPACK * dv) {
     const int tau = e >> 8, w = e & 255;
     const int l = w >> 2, r = w & 3;
     const int n = l & 15, g = l >> 4;
-    delta = tau / nb_count;
+    const int delta = tau / nb_count;
     const int nb = tau % nb_count;
     a = 4 * g + r;
     col = 16 * nb + n;
     is_z = false;
-  } else {
-    const int ez = e - DPACK * dv;
-    delta = ez >> 4;
-    a = ez & 15;
-    col = 0;
-    is_z = true;
+    if (delta == 8 && a >= 8) return false;
+    b = (a + delta) & 15;
+    mirror = a != b;
+    return true;
   }
-  if (delta == 8 && a >= 8) return false;
-  b = (a + delta) & 15;
+  const int ez = e - DPACK * dv;
+  const int l = ez >> 2, r = ez & 3;
+  b = l & 15;
+  a = 4 * (l >> 4) + r;
+  col = 0;
+  is_z = true;
+  mirror = false;
   return true;
 }
 
@@ -73,8 +80,8 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv,
     float c0 = 0.f;
     const int e = e0 + tid;
     int a, b, col;
-    bool is_z;
-    if (e < E && packed_to_pair(e, dv, a, b, col, is_z)) {
+    bool is_z, mirror;
+    if (e < E && packed_to_pair(e, dv, a, b, col, is_z, mirror)) {
       const int lo = a < b ? a : b, hi = a < b ? b : a;   // read the upper triangle
       if (!is_z && S0) c0 = S0[(bh * pp + lo * P_DIM + hi) * dv + col];
       if (is_z && z0) c0 = z0[bh * pp + lo * P_DIM + hi];
@@ -137,17 +144,14 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv,
   if (tid < SCAN_COLS && (ST || zT)) {
     const int e = e0 + tid;
     int a, b, col;
-    bool is_z;
-    if (e < E && packed_to_pair(e, dv, a, b, col, is_z)) {
+    bool is_z, mirror;
+    if (e < E && packed_to_pair(e, dv, a, b, col, is_z, mirror)) {
       const float val = carry[tid];
       if (!is_z && ST) {
         ST[(bh * pp + a * P_DIM + b) * dv + col] = val;
-        if (a != b) ST[(bh * pp + b * P_DIM + a) * dv + col] = val;
+        if (mirror) ST[(bh * pp + b * P_DIM + a) * dv + col] = val;
       }
-      if (is_z && zT) {
-        zT[bh * pp + a * P_DIM + b] = val;
-        if (a != b) zT[bh * pp + b * P_DIM + a] = val;
-      }
+      if (is_z && zT) zT[bh * pp + a * P_DIM + b] = val;
     }
   }
 }

@@ -54,13 +54,13 @@ def _ws(desc):
 
 def test_workspace_size_formula():
     _lib_or_skip()
-    # packed state block per leaf: 144 * dv + 144 floats
+    # packed state block per leaf: 144 * dv slots of S plus the 16 x 16 Z, floats
     d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "assoc", 16)
     st, n = _ws(d)
-    assert st == 0 and n == 16 * (2048 // 16) * (144 * 64 + 144) * 4
+    assert st == 0 and n == 16 * (2048 // 16) * (144 * 64 + 256) * 4
     d = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "sequential", 0)
     st, n = _ws(d)
-    assert st == 0 and n == 6 * 1 * (144 * 65) * 4
+    assert st == 0 and n == 6 * 1 * (144 * 64 + 256) * 4
     d = Bd.make_desc(1, 1, 0, 16, 16, 32, Bd.KATA_F32, Bd.KATA_F32)
     assert _ws(d) == (0, 0)
 

@@ -174,7 +174,12 @@ def test_deterministic():
 # ---- the scan: workspace after the call holds the exclusive prefix of the leaf states ---
 
 def unpack_leaf(block, dv):
-    """Packed leaf block (see kata_chunk.h) -> canonical (S [256, dv], z [256])."""
+    """Leaf block of the workspace -> canonical (S [256, dv], z [256]).
+
+    S: packed slots (delta, a) in accumulator-tile order: tile delta * (dv/16) + nb,
+    lane 16 g + n, element r holds S[(a, (a + delta) % 16)][16 nb + n], a = 4 g + r.
+    z: the 16 x 16 matrix Z after the 144 * dv S slots, lane 16 g + b element r holding
+    Z[4 g + r][b]."""
     nb = dv // 16
     S = np.zeros((256, dv))
     z = np.zeros(256)
@@ -190,9 +195,10 @@ def unpack_leaf(block, dv):
                     val = block[((delta * nb + blk) * 64 + lane) * 4 + r]
                     S[a * 16 + b, 16 * blk + n] = val
                     S[b * 16 + a, 16 * blk + n] = val
-            zval = block[144 * dv + 16 * delta + a]
-            z[a * 16 + b] = zval
-            z[b * 16 + a] = zval
+    for lane in range(64):
+        b, g = lane % 16, lane // 16
+        for r in range(4):
+            z[(4 * g + r) * 16 + b] = block[144 * dv + lane * 4 + r]
     return S, z
 
 
@@ -204,7 +210,7 @@ def test_scan_exclusive_prefix(leaf):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     kata.forward(q, k, v, P, chunk=64, scan_leaf=leaf, workspace=ws)
     torch.cuda.synchronize()
-    E = 144 * 64 + 144
+    E = 144 * 64 + 256
     n_leaf = -(-12 // leaf)
     W = ws.view(torch.float32).cpu().numpy().reshape(2, n_leaf, E)
     kh, vh = host64(case.k), host64(case.v)

@@ -38,7 +38,9 @@ kata_status validate(const kata_forward_desc* d) {
       d->scan_leaf < 0)
     return KATA_ERR_SHAPE;
   if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
-  if (d->T > ((int64_t)1 << 40)) return KATA_ERR_SHAPE;
+  // a sequence of q, k, v or y is addressed with 32-bit byte offsets (< 2 GiB)
+  const int64_t widest = (int64_t)(d->d > d->dv ? d->d : d->dv) * 4;
+  if (d->T > (((int64_t)1 << 31) - 4096) / widest - 256) return KATA_ERR_SHAPE;
   if (d->p != P_DIM) return KATA_ERR_UNSUPPORTED;
   if (!((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
   if (!(d->chunk == 32 || d->chunk == 64 || d->chunk == 128)) return KATA_ERR_UNSUPPORTED;

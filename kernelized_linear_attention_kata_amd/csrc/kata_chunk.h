@@ -81,11 +81,13 @@ __device__ __forceinline__ int ws_tile_offset(int delta, int nb, int lane) {
 
 // ---- per-chunk input staging ---------------------------------------------------
 
-// 8 consecutive input elements, loaded as 16-byte vectors.
+// 8 consecutive input elements, loaded as 16-byte vectors through a buffer resource.
 template <typename TIn> struct Vec8;
 template <> struct Vec8<bf16> {
   bf16x8 x;
-  __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off) {
+    x = __builtin_bit_cast(bf16x8, buf_load16(r, off));
+  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (bf16)0.f;
@@ -94,12 +96,17 @@ template <> struct Vec8<bf16> {
 };
 template <> struct Vec8<float> {
   f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off) {
+    a = __builtin_bit_cast(f32x4, buf_load16(r, off));
+    b = __builtin_bit_cast(f32x4, buf_load16(r, off >= BUF_OOB ? off : off + 16));
   }
   __device__ __forceinline__ void zero() { a = zero4(); b = zero4(); }
   __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+// Buffer resources over one (b, h) sequence of q, k, v and y.
+struct SeqRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v, y;
 };
 
 // Register-resident copy of one chunk's inputs for this thread: the q/k/v rows of
@@ -123,37 +130,37 @@ __device__ __forceinline__ bool proj_valid(int g) {
   else return true;
 }
 
+// Load the wave's q/k/v rows of the chunk starting at token t0 (within the sequence).
+// Rows at or past T fall outside the buffer and read as zero (no branches, so the
+// compiler can track the outstanding loads of each prefetch buffer exactly).
 template <class S, typename TIn, bool WANT_Q>
-__device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const TIn* __restrict__ q,
-                                           const TIn* __restrict__ k, const TIn* __restrict__ v,
-                                           int64_t base_tok, int64_t t0, int64_t T, int wave, int lane) {
+__device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const SeqRsrc& rs, int t0, int wave, int lane) {
   const int n = lane & 15, g = lane >> 4;
+  constexpr int ES = (int)sizeof(TIn);
 #pragma unroll
   for (int m = 0; m < S::MBW; ++m) {
     const int mb = wave + 4 * m;
-    const int64_t t = t0 + mb * 16 + n;
-    const bool ok = (mb < S::NMB) && (t < T) && proj_valid<S>(g);
+    if (S::NMB >= 4 * (m + 1) || mb < S::NMB) {       // wave-uniform
+      const int t = t0 + mb * 16 + n;
 #pragma unroll
-    for (int kk = 0; kk < S::KD; ++kk) {
-      const int64_t off = (base_tok + t) * S::DIN + proj_col<S>(g, kk, 0);
-      if (ok) {
-        if constexpr (WANT_Q) r.q[m][kk].load(q + off);
-        r.k[m][kk].load(k + off);
-      } else {
+      for (int kk = 0; kk < S::KD; ++kk) {
+        const int off = proj_valid<S>(g) ? (t * S::DIN + proj_col<S>(g, kk, 0)) * ES : BUF_OOB;
+        if constexpr (WANT_Q) r.q[m][kk].load(rs.q, off);
+        r.k[m][kk].load(rs.k, off);
+      }
+#pragma unroll
+      for (int kk = 0; kk < S::KV; ++kk) {
+        const int off = (S::DV >= 32 || g < 2) ? (t * S::DV + 32 * kk + 8 * g) * ES : BUF_OOB;
+        r.v[m][kk].load(rs.v, off);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < S::KD; ++kk) {
         if constexpr (WANT_Q) r.q[m][kk].zero();
         r.k[m][kk].zero();
       }
-    }
-  }
 #pragma unroll
-  for (int m = 0; m < S::MBW; ++m) {
-    const int mb = wave + 4 * m;
-    const int64_t t = t0 + mb * 16 + n;
-    const bool ok = (mb < S::NMB) && (t < T) && (S::DV >= 32 || g < 2);
-#pragma unroll
-    for (int kk = 0; kk < S::KV; ++kk) {
-      if (ok) r.v[m][kk].load(v + (base_tok + t) * S::DV + 32 * kk + 8 * g);
-      else r.v[m][kk].zero();
+      for (int kk = 0; kk < S::KV; ++kk) r.v[m][kk].zero();
     }
   }
 }
@@ -421,15 +428,33 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
-  ChunkIn<S, TIn> cur;
-  load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, c0 * S::C, T, wave, lane);
-  for (int c = 0; c < nch; ++c) {
+  SeqRsrc rs;
+  rs.k = make_rsrc(k + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.v = make_rsrc(v + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TIn));
+  const int tc0 = (int)(c0 * S::C);
+  // Inputs are prefetched DEPTH chunks ahead in DEPTH register buffers: the loads of
+  // chunk c+DEPTH are in flight while chunk c is processed.  Loads past the leaf
+  // read zeros or unused rows.  (Two buffers measured no faster: the kernel is not
+  // limited by the prefetch distance, and the extra registers cost occupancy.)
+  constexpr int DEPTH = 1;
+  ChunkIn<S, TIn> buf[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, tc0 + i * S::C, wave, lane);
+  auto step = [&](ChunkIn<S, TIn>& cur, int c) {
     stage_chunk<S, TIn, false>(cur, pp, sel, nullptr, nullptr, Wacc, vf_hi, vf_lo, wave, lane);
-    if (c + 1 < nch) load_chunk<S, TIn, false>(cur, nullptr, k, v, base_tok, (c0 + c + 1) * S::C, T, wave, lane);
+    load_chunk<S, TIn, false>(cur, rs, tc0 + (c + DEPTH) * S::C, wave, lane);
     __syncthreads();
     state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);
     __syncthreads();
+  };
+  int c = 0;
+  for (; c + DEPTH <= nch; c += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) step(buf[i], c + i);
   }
+#pragma unroll
+  for (int i = 0; i + 1 < DEPTH; ++i)   // fewer than DEPTH chunks left: static buffer index
+    if (c + i < nch) step(buf[i], c + i);
   // write the leaf state (tile-native layout) and Z
   float* out = ws + (bh * (int64_t)gridDim.x + leaf) * S::E;
 #pragma unroll
@@ -496,17 +521,20 @@ __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int
   st.Z = wave == 0 ? *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + lane * 4) : zero4();
 }
 
-// Vector store of 4 consecutive outputs.
+// Vector store of 4 consecutive outputs through the y buffer resource (stores past
+// the end of the sequence are dropped).
 template <typename TOut> struct Store4;
 template <> struct Store4<float> {
-  static __device__ __forceinline__ void st(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int off, const f32x4& x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
+  }
 };
 template <> struct Store4<bf16> {
-  static __device__ __forceinline__ void st(bf16* p, const f32x4& x) {
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int off, const f32x4& x) {
     bf16x4 b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) b[i] = (bf16)x[i];
-    *reinterpret_cast<bf16x4*>(p) = b;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, b), r, off, 0, 0);
   }
 };
 
@@ -518,8 +546,7 @@ template <> struct Store4<bf16> {
 template <class S, typename TOut>
 __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
                                               const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
-                                              const float* Zs, TOut* __restrict__ y, int64_t base_tok,
-                                              int64_t t0, int64_t T, int lane) {
+                                              const float* Zs, const SeqRsrc& rs, int t0, int lane) {
   const int n = lane & 15, g = lane >> 4;
   const int t = mb * 16 + n;    // token (within chunk) whose fragment column this lane builds
 
@@ -625,17 +652,14 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   den += __shfl_xor(den, 16);
   den += __shfl_xor(den, 32);
   // output gate: y = O / den (0 where the denominator is 0)
-  const int64_t tok = t0 + t;
-  if (tok < T) {
-    const float inv = den != 0.f ? 1.f / den : 0.f;
-    TOut* yrow = y + (base_tok + tok) * S::DV + 4 * g;
+  const float inv = den != 0.f ? 1.f / den : 0.f;
+  const int row = (t0 + t) * S::DV + 4 * g;
 #pragma unroll
-    for (int nb = 0; nb < S::NB; ++nb) {
-      f32x4 o;
+  for (int nb = 0; nb < S::NB; ++nb) {
+    f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = den != 0.f ? O[nb][r] * inv : 0.f;
-      Store4<TOut>::st(yrow + nb * 16, o);
-    }
+    for (int r = 0; r < 4; ++r) o[r] = O[nb][r] * inv;
+    Store4<TOut>::st(rs.y, (row + nb * 16) * (int)sizeof(TOut), o);
   }
 }
 
@@ -676,17 +700,23 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, lane);
   publish_state<S>(st, hx_hi, hx_lo, Zs, wave, lane);
 
+  SeqRsrc rs;
+  rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.k = make_rsrc(k + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.v = make_rsrc(v + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TIn));
+  rs.y = make_rsrc(y + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TOut));
+  const int tc0 = (int)(c0 * S::C);
   ChunkIn<S, TIn> cur;
-  load_chunk<S, TIn, true>(cur, q, k, v, base_tok, c0 * S::C, T, wave, lane);
+  load_chunk<S, TIn, true>(cur, rs, tc0, wave, lane);
   for (int c = 0; c < nch; ++c) {
-    const int64_t t0 = (c0 + c) * S::C;
+    const int t0 = tc0 + c * S::C;
     stage_chunk<S, TIn, true>(cur, pp, sel, Us, Ws, Wacc, vf_hi, vf_lo, wave, lane);
-    if (c + 1 < nch) load_chunk<S, TIn, true>(cur, q, k, v, base_tok, t0 + S::C, T, wave, lane);
+    if (c + 1 < nch) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, wave, lane);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < S::MBW; ++m) {
       const int mb = wave + 4 * m;
-      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, y, base_tok, t0, T, lane);
+      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, rs, t0, lane);
     }
     const bool more = c + 1 < nch;
     if (more) state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);

@@ -84,6 +84,20 @@ __device__ __forceinline__ f32x4 mma(const Op4<SA>& a, const Op4<SB>& b, f32x4 c
   return c;
 }
 
+// ---- buffer (range-checked) memory access ----------------------------------------
+// A raw buffer resource covers one sequence; loads past its end return 0 and
+// stores past it are dropped, so ragged tails need no branches.  Offsets are
+// 32-bit byte offsets (the host limits a sequence to < 2 GiB).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int BUF_OOB = 0x7ffffff0;          // an offset past any sequence: reads 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 // ---- element loads / stores in either storage dtype ------------------------------
 __device__ __forceinline__ float bf16_bits_to_float(u16 b) {
   return __uint_as_float(((uint32_t)b) << 16);

@@ -10,7 +10,7 @@
 // workgroup owns 32 consecutive elements e of one (b, h) and walks the leaves in
 // passes of blockDim.x rows: lane = leaf row, so every lane moves 128 contiguous
 // bytes per pass.  Within a pass the prefix across rows is a log-depth
-// Hillis-Steele scan over the wavefront (lane shuffles, 6 levels) followed by a
+// Hillis-Steele scan over the wavefront (DPP lane shifts, 6 levels) followed by a
 // scan of the per-wave totals through LDS; passes are chained by a carry.  The
 // exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g'.
 #pragma once
@@ -54,14 +54,25 @@ __device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, in
   return true;
 }
 
-__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const float y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+// Wavefront inclusive prefix sum by DPP (log depth, no LDS traffic): Hillis-Steele
+// inside each 16-lane row with row_shr:1,2,4,8, then the row totals are carried
+// with row_bcast:15 (row r-1's last lane into row r, rows 1 and 3) and
+// row_bcast:31 (lane 31 into rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
+  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
   return x;
 }
+// lane i receives lane i-1's value, lane 0 receives 0 (wave_shr:1)
+__device__ __forceinline__ float wave_shift_up1(float x) { return dpp_or_zero<0x138, 0xf>(x); }
 
 // grid (ceil(E/32), B*H), block = 64 * ceil(min(n_leaf, 256)/64) threads.
 __global__ void __launch_bounds__(256)
@@ -110,9 +121,8 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv,
     float ex[SCAN_COLS];
 #pragma unroll
     for (int c = 0; c < SCAN_COLS; ++c) {
-      const float inc = wave_inclusive_scan(x[c], lane);
-      const float up = __shfl_up(inc, 1);
-      ex[c] = lane == 0 ? 0.f : up;
+      const float inc = wave_inclusive_scan(x[c]);
+      ex[c] = wave_shift_up1(inc);
       if (lane == WAVE - 1) wtot[wave][c] = inc;
     }
     __syncthreads();

@@ -109,7 +109,7 @@ def main():
     ap.add_argument("--leaf", type=int, default=0, help="chunks per scan leaf (0 = library default)")
     ap.add_argument("--scan", default="assoc", choices=("assoc", "sequential"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-stride", type=int, default=64)
+    ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()

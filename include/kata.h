@@ -119,10 +119,12 @@ kata_status kata_forward(const kata_forward_desc* desc,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* kata_forward that also records four caller-created hipEvent_t, all on `stream`:
- * events[0] before kata_chunk_state, events[1] before kata_state_scan, events[2]
- * before kata_chunk_intra and events[3] after it, so a caller can time each kernel
- * of the chunked forward on the stream it runs on.  events == NULL behaves exactly
+/* kata_forward that also stamps four caller-created hipEvent_t (created with timing
+ * enabled) from the kernel launches on `stream`: events[0] at the start of
+ * kata_chunk_state, events[1] at the start of kata_state_scan, events[2] at the start
+ * of kata_chunk_intra and events[3] at its end, so a caller can time each kernel of
+ * the chunked forward on the stream it runs on.  The launches record the events
+ * themselves (no extra commands enter the stream).  events == NULL behaves exactly
  * like kata_forward; a NULL element returns KATA_ERR_NULL.  When nothing is launched
  * for the chunked path (B*H == 0 or T == 0) no event is recorded. */
 kata_status kata_forward_timed(const kata_forward_desc* desc,

@@ -158,8 +158,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
 
     Returns y [B,H,T,dv] (out_dtype, default q's dtype), or (y, ST, zT) with the final
     state when return_state.  Outputs and the workspace may be passed in preallocated.
-    events: optional four torch.cuda.Event(enable_timing=True), recorded on the stream
-    before the chunk-state, scan and intra kernels and after the last (kata_forward_timed).
+    events: optional four torch.cuda.Event(enable_timing=True), stamped by the launches with
+    the start of the chunk-state, scan and intra kernels and the end of the last
+    (kata_forward_timed).  An event torch has not created yet is recorded once first.
     """
     B, H, T, d = q.shape
     dv = v.shape[-1]

@@ -8,6 +8,7 @@
 // gist.science summary of "Kernelized Linear Attention", arXiv 2607.17419,
 // section 2.3, and in the paper's abstract).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdlib>
 
@@ -51,8 +52,11 @@ kata_status validate(const kata_forward_desc* d) {
 
 // Concurrent workgroups of kata_chunk_intra on one MI355X (256 compute units): the
 // instance's waves per SIMD (one 4-wave workgroup per SIMD set) limited by its LDS.
+// The LDS that co-resident workgroups can share is taken as 156 KiB: measured on
+// MI355X, three 256-thread workgroups of 52 KiB start together but three of 53 KiB
+// do not (the occupancy query of the runtime still reports three for 53 KiB).
 constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kLdsPerCU = 160 * 1024;
+constexpr int64_t kLdsPerCU = 156 * 1024;
 
 template <int C, int DV, bool SPLIT>
 int64_t intra_slots() {
@@ -140,20 +144,22 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
       allow_smem(kata_chunk_intra<S, TIn, TOut>, S::SMEM) != KATA_OK)
     return KATA_ERR_LAUNCH;
   const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
-  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return KATA_ERR_LAUNCH;
-  hipLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, (const TIn*)k,
-                     (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  // With events, the launches themselves stamp them (hipExtLaunchKernel: start of
+  // each kernel, end of the last), so timing adds no commands to the stream.
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, e0, nullptr, 0,
+                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int threads = (int)(pl.n_leaf >= 256 ? 256 : ((pl.n_leaf + 63) / 64) * 64);
   const dim3 sgrid((unsigned)((pl.E + SCAN_COLS - 1) / SCAN_COLS), (unsigned)bh);
-  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return KATA_ERR_LAUNCH;
-  hipLaunchKernelGGL(kata_state_scan, sgrid, dim3(threads), 0, st, ws, pl.n_leaf, pl.E, S::DV, S0, z0, ST, zT);
+  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(threads), 0, st, e1, nullptr, 0, ws, pl.n_leaf, pl.E,
+                        (int)S::DV, S0, z0, ST, zT);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  if (ev && hipEventRecord(ev[2], st) != hipSuccess) return KATA_ERR_LAUNCH;
-  hipLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, (const TIn*)q,
-                     (const TIn*)k, (const TIn*)v, P, ws, (TOut*)y, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, e2, e3, 0,
+                        (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
+                        (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  if (ev && hipEventRecord(ev[3], st) != hipSuccess) return KATA_ERR_LAUNCH;
   return KATA_OK;
 }
 

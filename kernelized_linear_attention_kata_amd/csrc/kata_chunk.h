@@ -48,18 +48,24 @@ struct Shape {
   static constexpr int HX_BYTES = READ_KB * NB * WAVE * 16;   // H as bf16 readout fragments
   static constexpr int U_BYTES = C * USTR * 4;                // u rows (fp32), W rows likewise
   static constexpr int WACC_BYTES = NMB * WAVE * 16;          // w tiles in accumulator layout
-  static constexpr int Z_BYTES = WAVE * 16;                   // Z (16 x 16) in accumulator layout
+  static constexpr int WZ_BYTES = 2 * NJ * WAVE * 16;         // w tiles as hi/lo bf16 K-block fragments
+  static constexpr int Z_BYTES = WAVE * 16;                   // Z (16 x 16) as hi/lo bf16 A-fragments
+  static constexpr int PF_BYTES = KD * 2 * WAVE * 16;         // P as hi/lo projection B-fragments
   static constexpr int NSPLIT = SPLIT ? 2 : 1;
   static constexpr int OFF_VF = 0;
   static constexpr int OFF_HX = OFF_VF + NSPLIT * VF_BYTES;
   static constexpr int OFF_U = OFF_HX + NSPLIT * HX_BYTES;
   static constexpr int OFF_W = OFF_U + U_BYTES;
   static constexpr int OFF_WACC = OFF_W + U_BYTES;
-  static constexpr int OFF_Z = OFF_WACC + WACC_BYTES;
-  static constexpr int SMEM = OFF_Z + Z_BYTES;
-  // kata_chunk_state needs only the V fragments and the w tiles
+  static constexpr int OFF_WZ = OFF_WACC + WACC_BYTES;
+  static constexpr int OFF_Z = OFF_WZ + WZ_BYTES;
+  static constexpr int OFF_PF = OFF_Z + Z_BYTES;
+  static constexpr int SMEM = OFF_PF + PF_BYTES;
+  // kata_chunk_state needs only the V fragments, the w tiles and the constants
   static constexpr int ST_OFF_WACC = NSPLIT * VF_BYTES;
-  static constexpr int SMEM_STATE = ST_OFF_WACC + WACC_BYTES;
+  static constexpr int ST_OFF_WZ = ST_OFF_WACC + WACC_BYTES;
+  static constexpr int ST_OFF_PF = ST_OFF_WZ + WZ_BYTES;
+  static constexpr int SMEM_STATE = ST_OFF_PF + PF_BYTES;
   // waves per SIMD each kernel is compiled for (register budget 512 / OCC): the
   // largest that fits without spilling on gfx950
   static constexpr int OCC_INTRA = DV <= 16 ? (C == 128 ? 3 : 4) : ((SPLIT || C == 128) ? 2 : 3);
@@ -70,6 +76,8 @@ struct Shape {
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(DV % 16 == 0 && DV <= 128, "dv");
   static_assert(DIN == 16 || DIN % 32 == 0, "d");
+  // three workgroups of the bf16 C = 64, dv = 64 instance share a CU (156 KiB of LDS)
+  static_assert(!(C == 64 && DV == 64 && !SPLIT) || 3 * SMEM <= 156 * 1024, "LDS budget");
 };
 
 // Offsets of an accumulator tile (delta, nb) inside a leaf's workspace block:
@@ -134,12 +142,12 @@ __device__ __forceinline__ bool proj_valid(int g) {
 // Rows at or past T fall outside the buffer and read as zero (no branches, so the
 // compiler can track the outstanding loads of each prefetch buffer exactly).
 template <class S, typename TIn, bool WANT_Q>
-__device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const SeqRsrc& rs, int t0, int wave, int lane) {
+__device__ __forceinline__ void load_chunk(ChunkIn<S, TIn>& r, const SeqRsrc& rs, int t0, int tw, int lane) {
   const int n = lane & 15, g = lane >> 4;
   constexpr int ES = (int)sizeof(TIn);
 #pragma unroll
   for (int m = 0; m < S::MBW; ++m) {
-    const int mb = wave + 4 * m;
+    const int mb = tw + 4 * m;
     if (S::NMB >= 4 * (m + 1) || mb < S::NMB) {       // wave-uniform
       const int t = t0 + mb * 16 + n;
 #pragma unroll
@@ -233,8 +241,10 @@ __device__ __forceinline__ Op8<S::SPLIT> load_vf(const bf16* vf_hi, const bf16* 
 template <class S>
 struct ProjP { Op8<true> f[S::KD]; };
 
+// The P fragments are loop-invariant and live in LDS rather than in registers:
+// Pf[kk][hi/lo][lane], 16 bytes each, written by one wave before the first chunk.
 template <class S>
-__device__ __forceinline__ void load_P(ProjP<S>& pp, const float* __restrict__ P, int h, int lane) {
+__device__ __forceinline__ void write_P(bf16* Pf, const float* __restrict__ P, int h, int lane) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < S::KD; ++kk) {
@@ -242,7 +252,18 @@ __device__ __forceinline__ void load_P(ProjP<S>& pp, const float* __restrict__ P
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       x[i] = proj_valid<S>(g) ? P[((int64_t)h * P_DIM + n) * S::DIN + proj_col<S>(g, kk, i)] : 0.f;
-    pp.f[kk] = make8<true>(x);
+    const Op8<true> f = make8<true>(x);
+    *reinterpret_cast<bf16x8*>(Pf + ((2 * kk) * WAVE + lane) * 8) = f.hi;
+    *reinterpret_cast<bf16x8*>(Pf + ((2 * kk + 1) * WAVE + lane) * 8) = f.lo;
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void read_P(ProjP<S>& pp, const bf16* Pf, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < S::KD; ++kk) {
+    pp.f[kk].hi = *reinterpret_cast<const bf16x8*>(Pf + ((2 * kk) * WAVE + lane) * 8);
+    pp.f[kk].lo = *reinterpret_cast<const bf16x8*>(Pf + ((2 * kk + 1) * WAVE + lane) * 8);
   }
 }
 
@@ -290,21 +311,16 @@ __device__ __forceinline__ float row_plus(float x) {
 // projection tiles of the two 16-token M-blocks of the K-block in accumulator layout
 // (lane (a, g) holds w_{4g+r}[a]); wb0/wb1 the same tiles with the lanes rotated so
 // lane a holds w[(a + d0) % 16]; ROT (a compile-time DPP row rotation) adds the rest
-// of delta = d0 + ROT.  Slots (8, a >= 8) repeat the pairs of a < 8 and are zeroed.
-template <class S, int ROT, bool DELTA8>
+// of delta = d0 + ROT.  The slots (8, a >= 8) repeat the pairs of a < 8; they are
+// accumulated like the others but carry query weight 0 and are never exported.
+template <class S, int ROT>
 __device__ __forceinline__ Op8<S::SPLIT> key_frag(const f32x4& wa0, const f32x4& wa1, const f32x4& wb0,
-                                                  const f32x4& wb1, int lane) {
+                                                  const f32x4& wb1) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[i] = wa0[i] * row_plus<ROT>(wb0[i]);
     x[4 + i] = wa1[i] * row_plus<ROT>(wb1[i]);
-  }
-  if constexpr (DELTA8) {
-    if ((lane & 15) >= 8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    }
   }
   return make8<S::SPLIT>(x);
 }
@@ -315,7 +331,7 @@ struct StateAcc {
   static constexpr int N8 = (S::NB + 3) / 4;   // delta = 8 column blocks per wave (max)
   f32x4 s[2][S::NB];     // delta = wave, wave + 4
   f32x4 s8[N8];          // delta = 8, nb = wave + 4*i
-  f32x4 Z;               // normaliser matrix, wave 0 only: lane (b, g) holds Z[4g+r][b]
+  f32x4 Z;               // normaliser matrix, Z-owning wave only: lane (b, g) holds Z[4g+r][b]
 };
 
 template <class S>
@@ -337,10 +353,11 @@ __device__ __forceinline__ void state_zero(StateAcc<S>& st) {
 // rotation (0, 4 or 8) away.  The z part of the chunk state, sum_s phi(k_s), is
 // vec(Z): the W fragment of a K-block is at the same time the A operand W^T (lane =
 // feature row a) and the B operand W (lane = column b), so one MFMA per K-block
-// updates all 256 entries.
+// updates all 256 entries; the fragment arrives already split into hi/lo bf16 (Wz).
 template <class S>
-__device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc, const bf16* vf_hi,
-                                             const bf16* vf_lo, int wave, int lane) {
+__device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc, const bf16* Wz,
+                                             const bf16* vf_hi, const bf16* vf_lo, int wave, bool zrole,
+                                             int lane) {
   const int rot_lane = (lane & ~15) | ((lane + wave) & 15);
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) {
@@ -352,17 +369,17 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc,
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 0, false>(wa0, wa1, wr0, wr1, lane);     // delta = w
+      const Op8<S::SPLIT> kf = key_frag<S, 0>(wa0, wa1, wr0, wr1);     // delta = w
 #pragma unroll
       for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
     }
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 4, false>(wa0, wa1, wr0, wr1, lane);     // delta = w + 4
+      const Op8<S::SPLIT> kf = key_frag<S, 4>(wa0, wa1, wr0, wr1);     // delta = w + 4
 #pragma unroll
       for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
     }
     if (wave < S::NB) {
-      const Op8<S::SPLIT> kf = key_frag<S, 8, true>(wa0, wa1, wa0, wa1, lane);      // delta = 8
+      const Op8<S::SPLIT> kf = key_frag<S, 8>(wa0, wa1, wa0, wa1);      // delta = 8
 #pragma unroll
       for (int i = 0; i < StateAcc<S>::N8; ++i) {
 #pragma unroll
@@ -370,9 +387,10 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc,
           if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
       }
     }
-    if (wave == 0) {
-      float x[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
-      const Op8<true> wf = make8<true>(x);   // hi/lo: Z feeds the denominator
+    if (zrole) {   // hi/lo: Z feeds the denominator
+      Op8<true> wf;
+      wf.hi = *reinterpret_cast<const bf16x8*>(Wz + (jj * WAVE + lane) * 8);
+      wf.lo = *reinterpret_cast<const bf16x8*>(Wz + ((S::NJ + jj) * WAVE + lane) * 8);
       st.Z = mma<true, true>(wf, wf, st.Z);
     }
   }
@@ -382,16 +400,25 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc,
 // layout, one 16-byte slot per lane), queries into U rows and keys into W rows when
 // WANT_Q, and transpose the wave's V rows into B-fragments.
 template <class S, typename TIn, bool WANT_Q>
-__device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const ProjP<S>& pp, const bf16x8 (&sel)[2],
-                                            float* Us, float* Ws, float* Wacc, bf16* vf_hi, bf16* vf_lo,
-                                            int wave, int lane) {
+__device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const bf16* Pf, const bf16x8 (&sel)[2],
+                                            float* Us, float* Ws, float* Wacc, bf16* Wz, bf16* vf_hi,
+                                            bf16* vf_lo, int tw, int lane) {
   const int n = lane & 15, g = lane >> 4;
+  ProjP<S> pp;
+  read_P<S>(pp, Pf, lane);
 #pragma unroll
   for (int m = 0; m < S::MBW; ++m) {
-    const int mb = wave + 4 * m;
+    const int mb = tw + 4 * m;
     if (mb < S::NMB) {
       const f32x4 w = project_tile<S, TIn>(r.k[m], pp);
       *reinterpret_cast<f32x4*>(Wacc + (mb * WAVE + lane) * 4) = w;
+      {   // hi/lo halves of the Z-update fragment of K-block mb/2 (slots 4*(mb&1) ..)
+        float wv[4] = {w[0], w[1], w[2], w[3]};
+        const Op4<true> wz = make4<true>(wv);
+        const int idx = ((mb >> 1) * WAVE + lane) * 8 + (mb & 1) * 4;
+        *reinterpret_cast<bf16x4*>(Wz + idx) = wz.hi;
+        *reinterpret_cast<bf16x4*>(Wz + S::NJ * WAVE * 8 + idx) = wz.lo;
+      }
       if constexpr (WANT_Q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ws[(mb * 16 + 4 * g + i) * S::USTR + n] = w[i];
@@ -414,6 +441,8 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
   bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
   float* Wacc = reinterpret_cast<float*>(smem + S::ST_OFF_WACC);
+  bf16* Wz = reinterpret_cast<bf16*>(smem + S::ST_OFF_WZ);
+  bf16* Pf = reinterpret_cast<bf16*>(smem + S::ST_OFF_PF);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
@@ -423,8 +452,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
   const int64_t base_tok = bh * T;
 
-  ProjP<S> pp;
-  load_P<S>(pp, P, h, lane);
+  if (wave == 0) write_P<S>(Pf, P, h, lane);
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
@@ -437,14 +465,20 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   // read zeros or unused rows.  (Two buffers measured no faster: the kernel is not
   // limited by the prefetch distance, and the extra registers cost occupancy.)
   constexpr int DEPTH = 1;
+  // Chunks are summed last to first: the sum does not depend on the order, and the
+  // data read last (the leaf's first chunks) is what kata_chunk_intra reads first,
+  // so part of it is still in the last-level cache.  The prefetch past the leaf's
+  // last chunk reads at T, outside the buffer (zeros, no memory traffic).
+  auto chunk_t0 = [&](int c) { return tc0 + (nch - 1 - c) * S::C; };
   ChunkIn<S, TIn> buf[DEPTH];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, tc0 + i * S::C, wave, lane);
+  for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, chunk_t0(i), wave, lane);
+  __syncthreads();   // P fragments written
   auto step = [&](ChunkIn<S, TIn>& cur, int c) {
-    stage_chunk<S, TIn, false>(cur, pp, sel, nullptr, nullptr, Wacc, vf_hi, vf_lo, wave, lane);
-    load_chunk<S, TIn, false>(cur, rs, tc0 + (c + DEPTH) * S::C, wave, lane);
+    stage_chunk<S, TIn, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf_hi, vf_lo, wave, lane);
+    load_chunk<S, TIn, false>(cur, rs, c + DEPTH < nch ? chunk_t0(c + DEPTH) : (int)T, wave, lane);
     __syncthreads();
-    state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);
+    state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, wave == 0, lane);
     __syncthreads();
   };
   int c = 0;
@@ -474,11 +508,26 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
 
 // ---- kata_chunk_intra ------------------------------------------------------------
 
+// Issue priority from the progress through the leaf.  The workgroups that share a CU
+// start together, and at equal priority the oldest wave issues first, so the first
+// workgroup dispatched to a CU runs ahead and the last one finishes alone, at a
+// fraction of the CU's throughput.  Lowering a wave's priority as it passes 50%, 75%
+// and 90% of its leaf lets the ones behind catch up at each step.
+__device__ __forceinline__ void progress_priority(int c, int nch) {
+  const int pm = (1000 * c) / nch;
+  if (pm < 500) __builtin_amdgcn_s_setprio(3);
+  else if (pm < 750) __builtin_amdgcn_s_setprio(2);
+  else if (pm < 900) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Publish the state accumulators as bf16 readout fragments: Hx[kb][nb][lane][slot],
-// delta = 2*kb + slot/4 (delta 8 -> kb 4, slots 0..3); wave 0 publishes Z in fp32.
+// delta = 2*kb + slot/4 (delta 8 -> kb 4, slots 0..3).  The Z owner publishes Z split into
+// hi/lo bf16: Z is symmetric, so its accumulator tile (lane (b, g) holds Z[4g+r][b])
+// is also its 16x16x16 A-fragment (lane (m, g) holds Z[m][4g+i]); Zs[lane] = {hi, lo}.
 template <class S>
-__device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi, bf16* hx_lo, float* Zs,
-                                              int wave, int lane) {
+__device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi, bf16* hx_lo, bf16* Zs,
+                                              int wave, bool zrole, int lane) {
   auto put = [&](int delta, int nb, const f32x4& a) {
     const int idx = (((delta >> 1) * S::NB + nb) * WAVE + lane) * 8 + (delta & 1) * 4;
     bf16x4 hi, lo;
@@ -501,11 +550,21 @@ __device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi
     const int nb = wave + 4 * i;
     if (nb < S::NB) put(8, nb, st.s8[i]);
   }
-  if (wave == 0) *reinterpret_cast<f32x4*>(Zs + lane * 4) = st.Z;
+  if (zrole) {
+    float zv[4] = {st.Z[0], st.Z[1], st.Z[2], st.Z[3]};
+    const Op4<true> z = make4<true>(zv);
+    bf16x8 zz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      zz[i] = z.hi[i];
+      zz[4 + i] = z.lo[i];
+    }
+    *reinterpret_cast<bf16x8*>(Zs + lane * 8) = zz;
+  }
 }
 
 template <class S>
-__device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int wave, int lane) {
+__device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int wave, bool zrole, int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int delta = wave + 4 * j;
@@ -518,7 +577,7 @@ __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int
     const int nb = wave + 4 * i;
     st.s8[i] = (nb < S::NB) ? *reinterpret_cast<const f32x4*>(in + ws_tile_offset<S>(8, nb, lane)) : zero4();
   }
-  st.Z = wave == 0 ? *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + lane * 4) : zero4();
+  st.Z = zrole ? *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + lane * 4) : zero4();
 }
 
 // Vector store of 4 consecutive outputs through the y buffer resource (stores past
@@ -546,7 +605,7 @@ template <> struct Store4<bf16> {
 template <class S, typename TOut>
 __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
                                               const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
-                                              const float* Zs, const SeqRsrc& rs, int t0, int lane) {
+                                              const bf16* Zs, const SeqRsrc& rs, int t0, int lane) {
   const int n = lane & 15, g = lane >> 4;
   const int t = mb * 16 + n;    // token (within chunk) whose fragment column this lane builds
 
@@ -603,10 +662,15 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   // so its accumulator tile is its own A fragment), dotted with u_t[4g..4g+3]
   float den;
   {
-    const f32x4 zt = *reinterpret_cast<const f32x4*>(Zs + lane * 4);
-    float zv[4] = {zt[0], zt[1], zt[2], zt[3]};
+    const bf16x8 zz = *reinterpret_cast<const bf16x8*>(Zs + lane * 8);
+    Op4<true> zf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      zf.hi[i] = zz[i];
+      zf.lo[i] = zz[4 + i];
+    }
     float uv[4] = {Q[0][0], Q[0][1], Q[0][2], Q[0][3]};
-    const f32x4 zu = mma<true, true>(make4<true>(zv), make4<true>(uv), zero4());
+    const f32x4 zu = mma<true, true>(zf, make4<true>(uv), zero4());
     den = zu[0] * Q[0][0] + zu[1] * Q[0][1] + zu[2] * Q[0][2] + zu[3] * Q[0][3];
   }
 
@@ -622,13 +686,15 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
       const f32x4 wb = *reinterpret_cast<const f32x4*>(Ws + (j * 16 + n) * S::USTR + 4 * g);
       float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
       const f32x4 X = mma<S::SPLIT, S::SPLIT>(make4<S::SPLIT>(wbv), uf, zero4());
+      if (j < mb) {   // wave-uniform: only the diagonal tile is masked
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool keep = (j < mb) || (4 * g + r <= n);
-        const float a2 = keep ? X[r] * X[r] : 0.f;
-        A2[j][r] = a2;
-        den += a2;
+        for (int r = 0; r < 4; ++r) A2[j][r] = X[r] * X[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] = (4 * g + r <= n) ? X[r] * X[r] : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) den += A2[j][r];
     }
   }
   // O^T += V^T (A^2 masked)^T: K-block jj = score tiles 2jj (slots 0..3), 2jj+1 (slots 4..7)
@@ -648,11 +714,12 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
     }
   }
 
-  // den(t) = sum over the 4 lane groups of this token's partial sums
-  den += __shfl_xor(den, 16);
-  den += __shfl_xor(den, 32);
-  // output gate: y = O / den (0 where the denominator is 0)
-  const float inv = den != 0.f ? 1.f / den : 0.f;
+  // den(t) = sum over the 4 lane groups of this token's partial sums: each permlane
+  // swap exchanges rows between its two outputs, whose sum is the pair sum in every lane
+  den = row_pair_sum<16>(den);
+  den = row_pair_sum<32>(den);
+  // output gate: y = O / den (0 where the denominator is 0); v_rcp_f32 is within 1 ulp
+  const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
   const int row = (t0 + t) * S::DV + 4 * g;
 #pragma unroll
   for (int nb = 0; nb < S::NB; ++nb) {
@@ -677,7 +744,9 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   float* Us = reinterpret_cast<float*>(smem + S::OFF_U);
   float* Ws = reinterpret_cast<float*>(smem + S::OFF_W);
   float* Wacc = reinterpret_cast<float*>(smem + S::OFF_WACC);
-  float* Zs = reinterpret_cast<float*>(smem + S::OFF_Z);
+  bf16* Wz = reinterpret_cast<bf16*>(smem + S::OFF_WZ);
+  bf16* Zs = reinterpret_cast<bf16*>(smem + S::OFF_Z);
+  bf16* Pf = reinterpret_cast<bf16*>(smem + S::OFF_PF);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
@@ -693,12 +762,15 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
     if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
   }
-  ProjP<S> pp;
-  load_P<S>(pp, P, h, lane);
+  // Roles: wave w takes the M-blocks w, w + 4, ... (token split) and the Z update
+  // goes to wave 0, whose M-block has the least intra-chunk work.
+  const int tw = wave;
+  const bool zrole = wave == 0;
+  if (wave == 0) write_P<S>(Pf, P, h, lane);
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
-  load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, lane);
-  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, lane);
+  load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
 
   SeqRsrc rs;
   rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
@@ -707,21 +779,23 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   rs.y = make_rsrc(y + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TOut));
   const int tc0 = (int)(c0 * S::C);
   ChunkIn<S, TIn> cur;
-  load_chunk<S, TIn, true>(cur, rs, tc0, wave, lane);
+  load_chunk<S, TIn, true>(cur, rs, tc0, tw, lane);
+  __syncthreads();   // P fragments written
   for (int c = 0; c < nch; ++c) {
     const int t0 = tc0 + c * S::C;
-    stage_chunk<S, TIn, true>(cur, pp, sel, Us, Ws, Wacc, vf_hi, vf_lo, wave, lane);
-    if (c + 1 < nch) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, wave, lane);
+    progress_priority(c, nch);
+    stage_chunk<S, TIn, true>(cur, Pf, sel, Us, Ws, Wacc, Wz, vf_hi, vf_lo, tw, lane);
+    if (c + 1 < nch) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, tw, lane);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < S::MBW; ++m) {
-      const int mb = wave + 4 * m;
+      const int mb = tw + 4 * m;
       if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, rs, t0, lane);
     }
     const bool more = c + 1 < nch;
-    if (more) state_update<S>(st, Wacc, vf_hi, vf_lo, wave, lane);
+    if (more) state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, zrole, lane);
     __syncthreads();
-    if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, lane);
+    if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
   }
 }
 

@@ -84,6 +84,23 @@ __device__ __forceinline__ f32x4 mma(const Op4<SA>& a, const Op4<SB>& b, f32x4 c
   return c;
 }
 
+// x + (x of the lane 16 or 32 away, i.e. lane ^ 16 or lane ^ 32) in every lane.
+// v_permlane16_swap / v_permlane32_swap exchange rows between their two operands; fed
+// the same value twice, the two results hold the two halves of each row pair, and
+// their sum is the pair sum whichever half each one holds.
+template <int DIST>
+__device__ __forceinline__ float row_pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  if constexpr (DIST == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    static_assert(DIST == 32, "row pair distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // ---- buffer (range-checked) memory access ----------------------------------------
 // A raw buffer resource covers one sequence; loads past its end return 0 and
 // stores past it are dropped, so ragged tails need no branches.  Offsets are

@@ -21,6 +21,11 @@ stream it launches on) and the CPU oracle timed on a bounded sample of the same
 workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W] [--chunk C] [--no-cpu-baseline]
+    python bench.py --decode     # the recurrent decode step instead (its own JSON line)
+
+The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
+the final-state export), then times 1024 kata_decode_step calls, each of which reads
+and writes the 272.6 MB fp32 state once.
 """
 from __future__ import annotations
 
@@ -106,6 +111,94 @@ def cpu_baseline(case, stride):
     }
 
 
+DECODE_METRIC = ("KATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=16, dv=64), "
+                 "1024 steps after an 8192-token prefill (1 GPU)")
+
+
+def decode_cpu_baseline(dc, budget_s=10.0):
+    """The oracle's decode step on the host over the same streams, steps until budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    N, H, dv = dc.N, dc.H, dc.dv
+    S = np.zeros((N, H, 256, dv))
+    z = np.zeros((N, H, 256))
+    P = dc.P.double().cpu().numpy()
+    steps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and steps < dc.steps:
+        q = O.bf16_bits_to_f64(I.bf16_bits(dc.q[steps]))
+        k = O.bf16_bits_to_f64(I.bf16_bits(dc.k[steps]))
+        v = O.bf16_bits_to_f64(I.bf16_bits(dc.v[steps]))
+        _, S, z = O.decode_reference(S, z, q, k, v, P)
+        steps += 1
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": N * steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle decode step over all {N} streams x {H} heads, first {steps} steps "
+                      f"({dt:.1f} s); the cost per step does not depend on the state's values"}
+
+
+def bench_decode(args):
+    import torch
+    import kernelized_linear_attention_kata_amd as kata
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dc = I.make_decode(device=dev)
+    N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
+    _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
+    S = torch.empty_like(S0)
+    z = torch.empty_like(z0)
+    ys = torch.empty((steps, N, H, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(j):
+        kata.decode_step(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
+
+    S.copy_(S0); z.copy_(z0)
+    settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - settle0 < args.settle_s:
+        for _ in range(16):
+            run(n_settle % steps)
+            n_settle += 1
+        torch.cuda.synchronize()
+    S.copy_(S0); z.copy_(z0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream); e1.record(stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for j in range(steps):
+        run(j)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms_step = total_ms / steps
+    state_bytes = (S.numel() + z.numel()) * 4
+    step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4
+    achieved = step_bytes / (ms_step / 1e3) / 1e9
+    result = {
+        "metric": DECODE_METRIC, "value": N * steps / (total_ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": 0, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 q/k/v, f32 state", "data": "synthetic",
+        "config": {"workload": f"recurrent decode: {N} streams x {H} heads, d=dv={d}, p=16, canonical fp32 "
+                               f"state [{N},{H},256,{dv}] + z, prefill T={T0} by kata_forward, {steps} steps, "
+                               f"every 4th key repeating an earlier one", "streams": N, "heads": H},
+        "roofline": {"bound": "hbm", "kernel": "kata_decode_step", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_step": step_bytes},
+        "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = decode_cpu_baseline(dc)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +212,7 @@ def main():
     ap.add_argument("--scan", default="assoc", choices=("assoc", "sequential"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=16)
+    ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
@@ -138,6 +232,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the sharded path is described in DESIGN.md but not run.", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        bench_decode(args)
+        return
 
     import torch
     import kernelized_linear_attention_kata_amd as kata

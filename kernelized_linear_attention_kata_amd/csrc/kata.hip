@@ -151,10 +151,14 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
   hipExtLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, e0, nullptr, 0,
                         (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  const int threads = (int)(pl.n_leaf >= 256 ? 256 : ((pl.n_leaf + 63) / 64) * 64);
-  const dim3 sgrid((unsigned)((pl.E + SCAN_COLS - 1) / SCAN_COLS), (unsigned)bh);
-  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(threads), 0, st, e1, nullptr, 0, ws, pl.n_leaf, pl.E,
-                        (int)S::DV, S0, z0, ST, zT);
+  // segments per column quad: the smallest power of two with at most SCAN_ROWS leaf
+  // rows each, capped at SCAN_GMAX (more leaves take several passes)
+  int G = 1;
+  while (G < SCAN_GMAX && (int64_t)G * SCAN_ROWS < pl.n_leaf) G *= 2;
+  const int quads = (int)(pl.E / 4);
+  const dim3 sgrid((unsigned)((quads + 256 / G - 1) / (256 / G)), (unsigned)bh);
+  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
+                        (int)S::DV, G, S0, z0, ST, zT);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,

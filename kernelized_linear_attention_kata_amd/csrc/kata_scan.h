@@ -6,20 +6,13 @@
 // state propagation is an associative scan (parallel prefix sum) of depth
 // O(log(T/C)).  The combine operator on states [S | z] is elementwise addition.
 //
-// Layout: ws[bh][leaf][e], e < E = 144*dv + 256 (packed S then Z, see kata_chunk.h).  One
-// workgroup owns 32 consecutive elements e of one (b, h) and walks the leaves in
-// passes of blockDim.x rows: lane = leaf row, so every lane moves 128 contiguous
-// bytes per pass.  Within a pass the prefix across rows is a log-depth
-// Hillis-Steele scan over the wavefront (DPP lane shifts, 6 levels) followed by a
-// scan of the per-wave totals through LDS; passes are chained by a carry.  The
-// exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g'.
+// Layout: ws[bh][leaf][e], e < E = 144*dv + 256 (packed S then Z, see kata_chunk.h).
+// The exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g'.
 #pragma once
 
 #include "kata_common.h"
 
 namespace kata {
-
-constexpr int SCAN_COLS = 32;
 
 // Element e of a leaf block -> canonical feature pair (a, b), value column and
 // whether it is a z entry.  S part: packed slot (delta, a) in accumulator-tile order,
@@ -54,109 +47,88 @@ __device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, in
   return true;
 }
 
-// Wavefront inclusive prefix sum by DPP (log depth, no LDS traffic): Hillis-Steele
-// inside each 16-lane row with row_shr:1,2,4,8, then the row totals are carried
-// with row_bcast:15 (row r-1's last lane into row r, rows 1 and 3) and
-// row_bcast:31 (lane 31 into rows 2 and 3).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_or_zero(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
-}
-__device__ __forceinline__ float wave_inclusive_scan(float x) {
-  x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
-  x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
-  x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
-  x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
-  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
-  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
-  return x;
-}
-// lane i receives lane i-1's value, lane 0 receives 0 (wave_shr:1)
-__device__ __forceinline__ float wave_shift_up1(float x) { return dpp_or_zero<0x138, 0xf>(x); }
+// One thread per 16-byte column quad (4 consecutive elements e) and per segment of
+// leaf rows: a workgroup holds QW = 256/G quads x G segments.  A pass covers G*Lseg
+// rows: segment s takes rows [s*Lseg, (s+1)*Lseg) of the pass, keeps them in
+// registers, and forms its total; the totals of the segments of a quad are combined
+// through LDS (segment s adds those of segments < s to the quad's running carry), and
+// each thread then writes the exclusive prefix of its rows in order.  Passes chain by
+// the carry.  Every element is read and written once, and each wavefront instruction
+// moves 1 KB (QW >= 64) or 16-byte pieces of QW consecutive quads, contiguous in the
+// leaf row.  Depth: Lseg sequential steps per pass plus the combination of G segments.
+constexpr int SCAN_ROWS = 16;    // rows per segment and pass (registers)
+constexpr int SCAN_GMAX = 16;    // segments per quad
 
-// grid (ceil(E/32), B*H), block = 64 * ceil(min(n_leaf, 256)/64) threads.
+// Canonical initial value of element e (upper-triangle entry of S0 / z0), 0 for none.
+__device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const float* S0, const float* z0) {
+  int a, b, col;
+  bool is_z, mirror;
+  if (!packed_to_pair(e, dv, a, b, col, is_z, mirror)) return 0.f;
+  const int64_t pp = (int64_t)P_DIM * P_DIM;
+  const int lo = a < b ? a : b, hi = a < b ? b : a;
+  if (!is_z) return S0 ? S0[(bh * pp + lo * P_DIM + hi) * dv + col] : 0.f;
+  return z0 ? z0[bh * pp + lo * P_DIM + hi] : 0.f;
+}
+
+// grid (ceil((E/4) / (256/G)), B*H), block 256.  E is a multiple of 4.
 __global__ void __launch_bounds__(256)
-kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv,
+kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
                 const float* __restrict__ S0, const float* __restrict__ z0,
                 float* __restrict__ ST, float* __restrict__ zT) {
-  __shared__ float wtot[4][SCAN_COLS];
-  __shared__ float carry[SCAN_COLS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
+  __shared__ f32x4 tot[256];
+  __shared__ f32x4 carry_s[256];
+  const int tid = threadIdx.x;
+  const int QW = 256 / G;
+  const int ql = tid % QW, seg = tid / QW;
   const int64_t bh = blockIdx.y;
-  const int e0 = blockIdx.x * SCAN_COLS;
-  const int64_t pp = (int64_t)P_DIM * P_DIM;
+  const int e0 = (blockIdx.x * QW + ql) * 4;
+  const bool active = e0 < E;
+  float* base = ws + bh * n_leaf * (int64_t)E + e0;
+  const int64_t per_pass = (int64_t)SCAN_ROWS * G;
+  const int lseg = (int)((n_leaf < per_pass ? n_leaf : per_pass) + G - 1) / G;
 
-  if (tid < SCAN_COLS) {
-    float c0 = 0.f;
-    const int e = e0 + tid;
-    int a, b, col;
-    bool is_z, mirror;
-    if (e < E && packed_to_pair(e, dv, a, b, col, is_z, mirror)) {
-      const int lo = a < b ? a : b, hi = a < b ? b : a;   // read the upper triangle
-      if (!is_z && S0) c0 = S0[(bh * pp + lo * P_DIM + hi) * dv + col];
-      if (is_z && z0) c0 = z0[bh * pp + lo * P_DIM + hi];
-    }
-    carry[tid] = c0;
+  f32x4 carry = zero4();   // the quad's running carry, kept by segment 0
+  if (seg == 0 && active) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0);
   }
-  __syncthreads();
-
-  float* base = ws + bh * n_leaf * (int64_t)E;
-  const bool full = (e0 + SCAN_COLS <= E);
-  for (int64_t r0 = 0; r0 < n_leaf; r0 += blockDim.x) {
-    const int64_t row = r0 + tid;
-    const bool rok = row < n_leaf;
-    float x[SCAN_COLS];
-    float* rp = base + row * E + e0;
-    if (rok && full) {
+  for (int64_t r0 = 0; r0 < n_leaf; r0 += (int64_t)lseg * G) {
+    const int64_t rs = r0 + (int64_t)seg * lseg;
+    f32x4 x[SCAN_ROWS];
+    f32x4 tsum = zero4();
 #pragma unroll
-      for (int c = 0; c < SCAN_COLS; c += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(rp + c);
-        x[c] = v[0]; x[c + 1] = v[1]; x[c + 2] = v[2]; x[c + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < SCAN_COLS; ++c) x[c] = (rok && e0 + c < E) ? rp[c] : 0.f;
+    for (int i = 0; i < SCAN_ROWS; ++i) {
+      const bool ok = active && i < lseg && rs + i < n_leaf;
+      x[i] = ok ? *reinterpret_cast<const f32x4*>(base + (rs + i) * E) : zero4();
+      tsum += x[i];
     }
-    float ex[SCAN_COLS];
-#pragma unroll
-    for (int c = 0; c < SCAN_COLS; ++c) {
-      const float inc = wave_inclusive_scan(x[c]);
-      ex[c] = wave_shift_up1(inc);
-      if (lane == WAVE - 1) wtot[wave][c] = inc;
-    }
+    tot[tid] = tsum;
+    if (seg == 0) carry_s[ql] = carry;
     __syncthreads();
+    f32x4 c = carry_s[ql];
+    for (int s2 = 0; s2 < seg; ++s2) c += tot[ql + s2 * QW];
 #pragma unroll
-    for (int c = 0; c < SCAN_COLS; ++c) {
-      float pre = carry[c];
-      for (int w = 0; w < wave; ++w) pre += wtot[w][c];
-      ex[c] += pre;
+    for (int i = 0; i < SCAN_ROWS; ++i) {
+      if (active && i < lseg && rs + i < n_leaf) *reinterpret_cast<f32x4*>(base + (rs + i) * E) = c;
+      c += x[i];
     }
-    if (rok && full) {
-#pragma unroll
-      for (int c = 0; c < SCAN_COLS; c += 4)
-        *reinterpret_cast<f32x4*>(rp + c) = f32x4{ex[c], ex[c + 1], ex[c + 2], ex[c + 3]};
-    } else if (rok) {
-#pragma unroll
-      for (int c = 0; c < SCAN_COLS; ++c)
-        if (e0 + c < E) rp[c] = ex[c];
-    }
-    __syncthreads();
-    if (tid < SCAN_COLS) {
-      float s = carry[tid];
-      for (int w = 0; w < nwaves; ++w) s += wtot[w][tid];
-      carry[tid] = s;
+    if (seg == 0) {
+      f32x4 nc = carry_s[ql];
+      for (int s2 = 0; s2 < G; ++s2) nc += tot[ql + s2 * QW];
+      carry = nc;
     }
     __syncthreads();
   }
 
-  // carry now holds S0 + sum of every leaf state: export in the canonical layout
-  if (tid < SCAN_COLS && (ST || zT)) {
-    const int e = e0 + tid;
-    int a, b, col;
-    bool is_z, mirror;
-    if (e < E && packed_to_pair(e, dv, a, b, col, is_z, mirror)) {
-      const float val = carry[tid];
+  // segment 0 now holds S0 + the sum of every leaf state: export it canonically
+  if (seg == 0 && active && (ST || zT)) {
+    const int64_t pp = (int64_t)P_DIM * P_DIM;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int a, b, col;
+      bool is_z, mirror;
+      if (!packed_to_pair(e0 + i, dv, a, b, col, is_z, mirror)) continue;
+      const float val = carry[i];
       if (!is_z && ST) {
         ST[(bh * pp + a * P_DIM + b) * dv + col] = val;
         if (mirror) ST[(bh * pp + b * P_DIM + a) * dv + col] = val;

@@ -138,6 +138,51 @@ def test_paths_agree():
     assert slice_rel(base[0], yref) <= 2e-2
 
 
+_SCAN_CASE = {}
+
+
+def _scan_case():
+    """T = 32*600 + 7 with chunk 32: 601 chunks per head, a random initial state."""
+    if not _SCAN_CASE:
+        case = I.make_forward("mid", B=1, H=2, T=32 * 600 + 7, seed=21)
+        g = torch.Generator().manual_seed(5)
+        S0 = torch.randn((1, 2, 256, 64), generator=g)
+        S0 = 0.5 * (S0 + S0.view(1, 2, 16, 16, 64).transpose(2, 3).reshape(1, 2, 256, 64))   # symmetric
+        z0 = torch.rand((1, 2, 16, 16), generator=g)
+        z0 = (z0 + z0.transpose(2, 3)).reshape(1, 2, 256)
+        Sr, zr = O.final_state(host64(case.k), host64(case.v), case.P.double().cpu().numpy())
+        _SCAN_CASE.update(case=case, S0=S0, z0=z0, Sref=Sr + S0.double().numpy(), zref=zr + z0.double().numpy())
+        q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
+        y, ST, zT = kata.forward(q, k, v, P, chunk=32, S0=S0.to(DEV), z0=z0.to(DEV), return_state=True,
+                                 out_dtype=torch.float32)
+        _SCAN_CASE.update(ybase=y.double().cpu().numpy(), Sbase=ST.cpu().numpy(), zbase=zT.cpu().numpy())
+    return _SCAN_CASE
+
+
+@pytest.mark.parametrize("leaf", [1, 3, 15, 36, 40, 601])
+def test_scan_leaf_counts(leaf):
+    """Leaf counts 601 (three passes of the scan), 201, 41, 17, 16 and 1 (one to sixteen
+    segments per column).  Against the automatic plan, which groups the same per-token
+    terms into different leaves, only the fp32 summation order differs: S, z and y
+    agree to 1e-5 / 1e-5 / 1e-3.  Against the oracle's S0 + sum: z (hi/lo W) to 1e-5,
+    S (bf16 features) to the bf16 bar."""
+    sc = _scan_case()
+    case = sc["case"]
+    q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
+    y, ST, zT = kata.forward(q, k, v, P, chunk=32, S0=sc["S0"].to(DEV), z0=sc["z0"].to(DEV), return_state=True,
+                             out_dtype=torch.float32, scan_leaf=leaf)
+    torch.cuda.synchronize()
+    eS = slice_rel(ST.cpu().numpy(), sc["Sbase"])
+    ez = slice_rel(zT.cpu().numpy(), sc["zbase"])
+    ey = slice_rel(y.double().cpu().numpy(), sc["ybase"])
+    oS = slice_rel(ST.cpu().numpy(), sc["Sref"])
+    oz = slice_rel(zT.cpu().numpy(), sc["zref"])
+    print(f"[scan leaf={leaf}] vs auto: S {eS:.2e} z {ez:.2e} y {ey:.2e}; vs oracle: S {oS:.2e} z {oz:.2e}",
+          flush=True)
+    assert eS <= 1e-5 and ez <= 1e-5 and ey <= 1e-3
+    assert oS <= TOL["bf16"] and oz <= 1e-5
+
+
 def test_resume_from_state():
     """forward(x1 || x2) on the x2 part equals forward(x2) from the state after x1,
     which is how a sequence split across devices would be joined."""

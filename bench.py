@@ -22,6 +22,7 @@ workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W] [--chunk C] [--no-cpu-baseline]
     python bench.py --decode     # the recurrent decode step instead (its own JSON line)
+    python bench.py --flash      # the flash-style O(T^2) forward on the 340M-layer workload
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -142,6 +143,98 @@ def decode_cpu_baseline(dc, budget_s=10.0):
                       f"({dt:.1f} s); the cost per step does not depend on the state's values"}
 
 
+FLASH_METRIC = ("KATA flash-style O(T^2) causal forward tokens/sec, 340M-layer shape "
+                "B=8 H=16 T=2048 d=dv=64 p=16, bf16 (1 GPU)")
+
+
+def flash_algorithmic_flops(B, H, T, d=64, dv=64, p=16):
+    """Useful flops: per causal pair 2p (score) + 2dv (weighted values) + 2 (denominator);
+    per token and head the two projections 2 * 2pd."""
+    pairs = B * H * T * (T + 1) // 2
+    return pairs * (2 * p + 2 * dv + 2) + B * H * T * 4 * p * d
+
+
+def bench_flash(args):
+    import torch
+    import kernelized_linear_attention_kata_amd as kata
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nb = max(1, args.batches)
+    seed0 = I.WORKLOADS["lm340m"]["seed"]
+    cases = [I.make_forward("lm340m", device=dev, seed=seed0 + b) for b in range(nb)]
+    c0 = cases[0]
+    B, H, T, d, dv = c0.B, c0.H, c0.T, c0.d, c0.dv
+    ws = torch.empty(kata.flash_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        c = cases[i % nb]
+        kata.flash_forward(c.q, c.k, c.v, c.P, y=ys[i % nb], workspace=ws, stream=stream, events=events)
+
+    settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - settle0 < args.settle_s:
+        for _ in range(8):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [t0, t1] + [e for es in evs for e in es]:
+        e.record(stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    flops = flash_algorithmic_flops(B, H, T)
+    attn_flops = flops - B * H * T * 4 * 16 * d
+    achieved = attn_flops / (attn_ms / 1e3) / 1e12
+
+    # the chunked path on the same inputs, for comparison (same settle state)
+    wsc = torch.empty(kata.forward_workspace_bytes(B, H, T, d, dv, 64), dtype=torch.uint8, device=dev)
+    for i in range(5):
+        c = cases[i % nb]
+        kata.forward(c.q, c.k, c.v, c.P, chunk=64, y=ys[i % nb], workspace=wsc, stream=stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        c = cases[i % nb]
+        kata.forward(c.q, c.k, c.v, c.P, chunk=64, y=ys[i % nb], workspace=wsc, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    chunked_ms = t0.elapsed_time(t1) / args.steps
+
+    result = {
+        "metric": FLASH_METRIC, "value": B * T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
+        "config": {"workload": f"flash-style O(T^2) forward (no state), 340M-layer inputs: B={B} H={H} T={T} "
+                               f"d=dv={d} p=16, per-head P, unit-norm keys, bf16",
+                   "global_batch": B, "seq_len": T, "heads": H},
+        "roofline": {"bound": "mfma", "kernel": "kata_flash_attn", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": attn_flops},
+        "kernels": {"kata_flash_prep": {"ms": round(prep_ms, 4)}, "kata_flash_attn": {"ms": round(attn_ms, 4)}},
+        "chunked_path_ms_per_step": round(chunked_ms, 4),
+        "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(c0, args.cpu_stride)
+        result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(result), flush=True)
+
+
 def bench_decode(args):
     import torch
     import kernelized_linear_attention_kata_amd as kata
@@ -213,6 +306,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
+    ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
@@ -235,6 +329,9 @@ def main():
 
     if args.decode:
         bench_decode(args)
+        return
+    if args.flash:
+        bench_flash(args)
         return
 
     import torch

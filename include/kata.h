@@ -136,6 +136,27 @@ kata_status kata_forward_timed(const kata_forward_desc* desc,
                                void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events);
 
+/* Flash-style O(T^2) forward (no state): the first operating point of the
+ * hardware section of the gist.science summary of arXiv 2607.17419 (section 2.3),
+ * the fused kernel behind the 1.6x-over-FlashAttention-2 figure of the paper's
+ * abstract.  Computes the same y as kata_forward with no initial state,
+ *   y_t = sum_{s<=t} (u_t . w_s)^2 v_s / sum_{s<=t} (u_t . w_s)^2   (0 if the sum is 0),
+ * by accumulating masked squared score tiles over all earlier key blocks; no state is
+ * formed or returned.  Supported: p = 16, d = dv = 64, in_dtype BF16, out_dtype F32 or
+ * BF16; desc->chunk, scan and scan_leaf are ignored.  q, k [B,H,T,64], v [B,H,T,64]
+ * bf16, P [H,16,64] f32, y [B,H,T,64] out_dtype, all device memory owned by the caller.
+ * The workspace (kata_flash_workspace_bytes: 192 bytes per token and head, T rounded
+ * up to 256) holds the projected u and w (bf16) and V in MFMA operand order.
+ * events: NULL, or three caller-created hipEvent_t (timing enabled) stamped with the
+ * start of the projection kernel, the start of the attention kernel and its end.
+ * Errors are returned before anything is enqueued; B*H == 0 or T == 0 is a no-op. */
+kata_status kata_flash_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+kata_status kata_flash_forward(const kata_forward_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const float* P, void* y,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events);
+
 /* One recurrent decode step for N independent streams ([TS-1], [ABS]):
  *   S += phi(k) v^T, z += phi(k)   (in place, canonical layout)
  *   y  = S^T phi(q) / (z . phi(q)) (after the update; 0 if the denominator is 0)

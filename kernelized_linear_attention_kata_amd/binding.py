@@ -80,6 +80,11 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_timed.restype = ci
     lib.kata_forward_timed.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                        ctypes.POINTER(vp)]
+    lib.kata_flash_workspace_bytes.restype = ci
+    lib.kata_flash_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_flash_forward.restype = ci
+    lib.kata_flash_forward.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, sz, vp,
+                                       ctypes.POINTER(vp)]
     lib.kata_decode_step.restype = ci
     lib.kata_decode_step.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_feature_map.restype = ci
@@ -212,6 +217,58 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_forward")
     return (y, ST, zT) if return_state else y
+
+
+def flash_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None) -> int:
+    """Workspace bytes of kata_flash_forward for these sizes."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_flash_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_flash_workspace_bytes")
+    return int(n.value)
+
+
+def flash_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, *,
+                  out_dtype: Optional[torch.dtype] = None, y: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
+    """Flash-style O(T^2) forward (kata_flash_forward): the same y as forward() with no
+    initial state, without forming the state.  q, k, v: [B,H,T,64] bf16; P: [H,16,64] fp32.
+    events: optional three torch.cuda.Event(enable_timing=True), stamped with the start of
+    the projection kernel, the start of the attention kernel and its end."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    _check(lib.kata_flash_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_flash_workspace_bytes")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    sh = _stream_handle(stream, dev)
+    evarr = None
+    if events is not None:
+        if len(events) != 3:
+            raise ValueError("events: three torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_flash_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
+    _check(st, "kata_flash_forward")
+    return y
 
 
 def decode_step(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -15,6 +15,7 @@
 #include "../../include/kata.h"
 #include "kata_chunk.h"
 #include "kata_decode.h"
+#include "kata_flash.h"
 #include "kata_scan.h"
 
 using namespace kata;
@@ -201,6 +202,23 @@ kata_status copy_initial_state(const kata_forward_desc* d, const float* S0, cons
   return launch_status();
 }
 
+// The flash-style forward supports bf16 q/k/v with d = dv = 64 and p = 16.
+kata_status validate_flash(const kata_forward_desc* d) {
+  if (!d) return KATA_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0) return KATA_ERR_SHAPE;
+  if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
+  if (d->T > (((int64_t)1 << 31) - 4096) / (FL_DV * 4) - 256) return KATA_ERR_SHAPE;
+  if (d->p != P_DIM || d->d != 64 || d->dv != FL_DV) return KATA_ERR_UNSUPPORTED;
+  if (d->in_dtype != KATA_BF16 || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+int64_t flash_tpad(int64_t T) { return (T + FL_QB - 1) / FL_QB * FL_QB; }
+
+size_t flash_ws_bytes(const kata_forward_desc* d) {
+  return (size_t)(d->B * d->H) * (size_t)flash_ws_elems(flash_tpad(d->T)) * sizeof(bf16);
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +281,48 @@ kata_status kata_forward(const kata_forward_desc* desc, const void* q, const voi
                          const float* P, const float* S0, const float* z0, void* y, float* ST, float* zT,
                          void* workspace, size_t workspace_bytes, void* stream) {
   return kata_forward_timed(desc, q, k, v, P, S0, z0, y, ST, zT, workspace, workspace_bytes, stream, nullptr);
+}
+
+kata_status kata_flash_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {
+  if (!bytes) return KATA_ERR_NULL;
+  const kata_status s = validate_flash(desc);
+  if (s != KATA_OK) return s;
+  *bytes = flash_ws_bytes(desc);
+  return KATA_OK;
+}
+
+kata_status kata_flash_forward(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                               const float* P, void* y, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const* events) {
+  const kata_status s = validate_flash(desc);
+  if (s != KATA_OK) return s;
+  const int64_t bh = desc->B * desc->H;
+  if (bh == 0 || desc->T == 0) return KATA_OK;
+  if (!q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  if (!workspace || workspace_bytes < flash_ws_bytes(desc)) return KATA_ERR_WORKSPACE;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (events) {
+    for (int i = 0; i < 3; ++i) {
+      if (!events[i]) return KATA_ERR_NULL;
+      ev[i] = (hipEvent_t)events[i];
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t tpad = flash_tpad(desc->T);
+  bf16* ws = (bf16*)workspace;
+  hipExtLaunchKernelGGL((kata_flash_prep<bf16>), dim3((unsigned)(tpad / 64), (unsigned)bh), dim3(256), 0, st,
+                        ev[0], nullptr, 0, (const bf16*)q, (const bf16*)k, (const bf16*)v, P, ws, desc->T, tpad,
+                        (int)desc->H);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  if ((tpad / FL_QB) * bh > 0x7fffffff) return KATA_ERR_SHAPE;
+  const dim3 grid((unsigned)((tpad / FL_QB) * bh));
+  if (desc->out_dtype == KATA_F32)
+    hipExtLaunchKernelGGL(kata_flash_attn<float>, grid, dim3(64 * FL_WAVES), 0, st, ev[1], ev[2], 0, (const bf16*)ws,
+                          (float*)y, desc->T, tpad, (int)bh);
+  else
+    hipExtLaunchKernelGGL(kata_flash_attn<bf16>, grid, dim3(64 * FL_WAVES), 0, st, ev[1], ev[2], 0, (const bf16*)ws,
+                          (bf16*)y, desc->T, tpad, (int)bh);
+  return launch_status();
 }
 
 kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,

@@ -142,3 +142,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(Bd, "_LIB", None)
     with pytest.raises(Bd.KataError):
         Bd.load_library()
+
+
+def test_flash_workspace_and_validation():
+    lib = _lib_or_skip()
+    n = ctypes.c_size_t(0)
+    d = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_flash_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    assert n.value == 6 * 1024 * 192          # T rounded up to 256; u, w, V: 192 B per token
+    fake = ctypes.c_void_p(0x1000)
+    for field, value, status in [("d", 16, Bd.KATA_ERR_UNSUPPORTED), ("in_dtype", Bd.KATA_F32, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("p", 8, Bd.KATA_ERR_UNSUPPORTED), ("T", -1, Bd.KATA_ERR_SHAPE),
+                                 ("out_dtype", 9, Bd.KATA_ERR_UNSUPPORTED)]:
+        bad = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        setattr(bad, field, value)
+        assert lib.kata_flash_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == status, field
+        assert lib.kata_flash_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, 1 << 30, None,
+                                      None) == status, field
+    assert lib.kata_flash_forward(ctypes.byref(d), None, fake, fake, fake, fake, fake, 1 << 30, None, None) \
+        == Bd.KATA_ERR_NULL
+    assert lib.kata_flash_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, n.value - 1, None, None) \
+        == Bd.KATA_ERR_WORKSPACE
+    empty = Bd.make_desc(2, 3, 0, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_flash_forward(ctypes.byref(empty), None, None, None, None, None, None, 0, None, None) \
+        == Bd.KATA_OK

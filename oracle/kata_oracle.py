@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the KATA causal forward pass and decode step.
+"""Plain fp64 CPU oracle for the KATA causal forward pass, its gradients and the decode step.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module.  The product path (the
@@ -31,6 +31,11 @@ numerator and phi(q_t) . z0 to the denominator, phi(x) = vec((Px)(Px)^T) in
 the canonical row-major index i*p + j.  The final state is
 S_T = S0 + sum_s phi(k_s) v_s^T, z_T = z0 + sum_s phi(k_s).
 
+The backward (``backward_quadratic``) is the chain rule through this same
+definition: the pages give no backward pass, so the gradient of the forward they
+define is the only reading; it is pinned against finite differences of the
+forward, not against itself.
+
 Readings where the pages leave a step open (each also listed in the design
 notes): the causal sum includes s = t (the convex gate of [TS-2.1] mixes in
 the current value); there is no temperature and no epsilon; a zero
@@ -54,6 +59,7 @@ __all__ = [
     "final_state",
     "recurrence",
     "decode_reference",
+    "backward_quadratic",
 ]
 
 
@@ -243,3 +249,83 @@ def decode_reference(S, z, q, k, v, P):
         ok = den != 0.0
         y[ok, h] = num[ok] / den[ok, None]
     return y, S, z
+
+
+def _sym_mat(x, p):
+    """The symmetric p x p matrix M + M^T of a flattened row-major p*p vector."""
+    m = np.asarray(x, dtype=np.float64).reshape(p, p)
+    return m + m.T
+
+
+def backward_quadratic(q, k, v, P, gy, S0=None, z0=None, gST=None, gzT=None):
+    """Gradients of the causal KATA forward by the chain rule through its O(T^2) definition.
+
+    PARITY NOTE: the pages give no backward pass; the gradient is fixed by the forward
+    definition alone ([TS-1], [TS-2.1], [TS-2.2], [ABS]: the same quantities as
+    ``forward_quadratic`` and ``final_state``).  The scalar being differentiated is
+
+        L = sum_t gy_t . y_t + <gST, S_T> + <gzT, z_T>
+
+    with y, S_T, z_T as in ``forward_quadratic`` / ``final_state`` (the initial state
+    enters through the full feature phi(x) = vec(u u^T), so S0 and z0 are used with
+    every entry).  Inputs as for ``forward_quadratic``; gy [B, H, T, dv]; gST [B, H,
+    p*p, dv] and gzT [B, H, p*p] or None (zero).
+
+    Per head, with u = P q, w = P k, X = u w^T and a = tril(X^2):
+      num_t = sum_s a_ts v_s + phi(u_t)^T S0,  den_t = sum_s a_ts + phi(u_t) . z0
+      gnum_t = gy_t / den_t,  gden_t = -(gy_t . y_t) / den_t   (both 0 where den_t = 0,
+                                                              where y_t is the constant 0)
+      ga_ts = gnum_t . v_s + gden_t   (s <= t),  gX = 2 X o ga
+      du_t = sum_s gX_ts w_s + (M_t + M_t^T) u_t,  M_t = mat(S0 gnum_t + z0 gden_t)
+      dw_s = sum_t gX_ts u_t + (N_s + N_s^T) w_s,  N_s = mat(gST v_s + gzT)
+      dv_s = sum_t a_ts gnum_t + gST^T phi(w_s)
+      dq = du P, dk = dw P, dP = sum over batch rows and tokens of du q^T + dw k^T
+      dS0 = gST + sum_t phi(u_t) gnum_t^T,  dz0 = gzT + sum_t phi(u_t) gden_t
+
+    Returns (dq [B,H,T,d], dk [B,H,T,d], dv [B,H,T,dv], dP [H,p,d], dS0 [B,H,p*p,dv],
+    dz0 [B,H,p*p]), all float64.
+    """
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    gy = np.asarray(gy, dtype=np.float64)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    p = P.shape[1]
+    pp = p * p
+    dq = np.zeros_like(q); dk = np.zeros_like(k); dvv = np.zeros_like(v)
+    dP = np.zeros_like(P)
+    dS0 = np.zeros((B, H, pp, dv)); dz0 = np.zeros((B, H, pp))
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            s0 = np.zeros((pp, dv)) if S0 is None else np.asarray(S0[b, h], dtype=np.float64)
+            zz = np.zeros(pp) if z0 is None else np.asarray(z0[b, h], dtype=np.float64)
+            gs = np.zeros((pp, dv)) if gST is None else np.asarray(gST[b, h], dtype=np.float64)
+            gz = np.zeros(pp) if gzT is None else np.asarray(gzT[b, h], dtype=np.float64)
+            u = project(q[b, h], P[h])
+            w = project(k[b, h], P[h])
+            fu = feature_full(u)
+            fw = feature_full(w)
+            X = u @ w.T
+            a = np.where(causal, X * X, 0.0)
+            num = a @ v[b, h] + fu @ s0
+            den = a.sum(axis=1) + fu @ zz
+            ok = den != 0.0
+            safe = np.where(ok, den, 1.0)
+            y = np.where(ok[:, None], num / safe[:, None], 0.0)
+            gnum = np.where(ok[:, None], gy[b, h] / safe[:, None], 0.0)
+            gden = np.where(ok, -np.einsum("tj,tj->t", gy[b, h], y) / safe, 0.0)
+            ga = np.where(causal, gnum @ v[b, h].T + gden[:, None], 0.0)
+            gX = 2.0 * X * ga
+            du = gX @ w
+            dw = gX.T @ u
+            for t in range(T):
+                du[t] += _sym_mat(s0 @ gnum[t] + zz * gden[t], p) @ u[t]
+                dw[t] += _sym_mat(gs @ v[b, h, t] + gz, p) @ w[t]
+            dvv[b, h] = a.T @ gnum + fw @ gs
+            dq[b, h] = du @ P[h]
+            dk[b, h] = dw @ P[h]
+            dP[h] += du.T @ q[b, h] + dw.T @ k[b, h]
+            dS0[b, h] = gs + fu.T @ gnum
+            dz0[b, h] = gz + fu.T @ gden
+    return dq, dk, dvv, dP, dS0, dz0

@@ -157,6 +157,61 @@ kata_status kata_flash_forward(const kata_forward_desc* desc,
                                void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events);
 
+/* Backward of kata_forward: gradients of q, k, v, P and the initial state for a given
+ * gradient gy of the output y and (optionally) gST, gzT of the final state.  The pages
+ * give no backward pass; it is the derivative of the forward defined above (chain rule):
+ * with num_t, den_t the numerator and denominator of y_t, g_t = gy_t / den_t and
+ * h_t = -(g_t . num_t) / den_t = -(gy_t . y_t) / den_t (both 0 where den_t = 0, where y_t
+ * is the constant 0), and B_ts = 2 (u_t . w_s) (g_t . v_s + h_t) for s <= t,
+ *   du_t = sum_s B_ts w_s + 2 mat(S_t g_t + z_t h_t) u_t        dq = du P
+ *   dw_s = sum_t B_ts u_t + 2 mat(R_s v_s + r_s) w_s            dk = dw P
+ *   dv_s = sum_{t>=s} a_ts g_t + gST^T phi(k_s)                 dP = sum over b, t of du q^T + dw k^T
+ *   dS0 = gST + sum_t phi(q_t) g_t^T,  dz0 = gzT + sum_t phi(q_t) h_t
+ * where S_t, z_t is the forward's prefix state (exclusive of chunk-local tokens, which
+ * enter through B_ts) and R_s, r_s = gST, gzT + sum_{t > chunk of s} phi(q_t) [g_t | h_t]
+ * the backward's suffix state.  It runs in the chunked-state form: the forward's chunk
+ * states and their associative prefix, a walk over the chunks that forms g, h and dq,
+ * the backward's chunk states phi(Q_c)^T [G_c | h_c] and their associative SUFFIX (the
+ * hardware section of the gist.science summary, section 2.3, applied to the reversed
+ * sequence), and a reverse walk that forms dv and dk.
+ *   desc: as for kata_forward; supported p = 16, d = dv = 64, chunk = 64, in_dtype BF16
+ *         (q, k, v, dq, dk, dv), out_dtype F32 or BF16 (gy).  scan / scan_leaf as for
+ *         kata_forward (the leaf plan is the backward's own).
+ *   q, k [B,H,T,64], v [B,H,T,64] bf16; P [H,16,64] f32; S0 [B,H,256,64], z0 [B,H,256] f32
+ *   or both NULL (those of the forward being differentiated);
+ *   gy [B,H,T,64] out_dtype: the gradient of the loss w.r.t. the forward's output y.  y itself
+ *   is not an input: g_t . num_t is formed from the state and score tiles of the walk, so
+ *   the gradient does not inherit the rounding of a stored y;
+ *   gST [B,H,256,64], gzT [B,H,256] f32 or both NULL (zero): gradient w.r.t. the final state;
+ *   dq, dk, dv [B,H,T,64] bf16, dP [H,16,64] f32 (summed over the batch) - written;
+ *   dS0 [B,H,256,64], dz0 [B,H,256] f32 or both NULL - written.  A state is symmetric in
+ *   (i, j), so dS0 / dz0 are returned as the gradient within symmetric states: gST and gzT
+ *   enter through the mean of their mirror entries, and dS0[i*16+j] = dS0[j*16+i].
+ *   workspace: kata_backward_workspace_bytes bytes (device memory owned by the caller).
+ * B*H == 0 or T == 0 writes dP = 0 and dS0, dz0 = gST, gzT (zero when NULL).  Errors are
+ * returned before anything is enqueued.  kata_backward_timed stamps eight caller events
+ * (NULL = none): the starts of the forward chunk-state kernel, the forward scan, the query
+ * walk, the backward chunk-state kernel, the reverse scan, the key walk and the dP
+ * reduction, and the end of the last. */
+kata_status kata_backward_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+kata_status kata_backward(const kata_forward_desc* desc,
+                          const void* q, const void* k, const void* v, const float* P,
+                          const float* S0, const float* z0,
+                          const void* gy,
+                          const float* gST, const float* gzT,
+                          void* dq, void* dk, void* dv, float* dP,
+                          float* dS0, float* dz0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+kata_status kata_backward_timed(const kata_forward_desc* desc,
+                                const void* q, const void* k, const void* v, const float* P,
+                                const float* S0, const float* z0,
+                                const void* gy,
+                                const float* gST, const float* gzT,
+                                void* dq, void* dk, void* dv, float* dP,
+                                float* dS0, float* dz0,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
+
 /* One recurrent decode step for N independent streams ([TS-1], [ABS]):
  *   S += phi(k) v^T, z += phi(k)   (in place, canonical layout)
  *   y  = S^T phi(q) / (z . phi(q)) (after the update; 0 if the denominator is 0)

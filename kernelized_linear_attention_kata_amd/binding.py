@@ -85,6 +85,12 @@ def load_library() -> ctypes.CDLL:
     lib.kata_flash_forward.restype = ci
     lib.kata_flash_forward.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, sz, vp,
                                        ctypes.POINTER(vp)]
+    lib.kata_backward_workspace_bytes.restype = ci
+    lib.kata_backward_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_backward_timed.restype = ci
+    lib.kata_backward_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 16 + [sz, vp, ctypes.POINTER(vp)]
+    lib.kata_backward.restype = ci
+    lib.kata_backward.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 16 + [sz, vp]
     lib.kata_decode_step.restype = ci
     lib.kata_decode_step.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_feature_map.restype = ci
@@ -269,6 +275,88 @@ def flash_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_flash_forward")
     return y
+
+
+def backward_workspace_bytes(B, H, T, d=64, dv=64, chunk=64, in_dtype=torch.bfloat16, out_dtype=None,
+                             scan="assoc", scan_leaf=0) -> int:
+    """Workspace bytes of kata_backward for these sizes."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "kata_backward_workspace_bytes")
+    return int(n.value)
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, gy: torch.Tensor,
+             chunk: int = 64, *, S0: Optional[torch.Tensor] = None,
+             z0: Optional[torch.Tensor] = None, gST: Optional[torch.Tensor] = None,
+             gzT: Optional[torch.Tensor] = None, return_state_grad: bool = False, scan: str = "assoc",
+             scan_leaf: int = 0, workspace: Optional[torch.Tensor] = None, out=None, stream=None, events=None):
+    """Gradients of the KATA causal forward (kata_backward).
+
+    q, k, v: [B,H,T,64] bf16; P: [H,16,64] fp32; gy: the gradient of the loss with respect
+    to the forward's output y, [B,H,T,64] bf16 or fp32 (y itself is not needed); S0, z0:
+    the forward's initial state (or None); gST, gzT: gradient of the final state (or None).  Returns (dq, dk, dv, dP)
+    and, when return_state_grad, (dq, dk, dv, dP, dS0, dz0).  out: optional preallocated
+    (dq, dk, dv, dP).  events: optional eight torch.cuda.Event(enable_timing=True).
+    """
+    B, H, T, d = q.shape
+    dv_ = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv_), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(gy, "gy", (B, H, T, dv_), device=dev)
+    pp = P_DIM * P_DIM
+    for a, b_, n1, n2 in ((S0, z0, "S0", "z0"), (gST, gzT, "gST", "gzT")):
+        if (a is None) != (b_ is None):
+            raise ValueError(f"{n1} and {n2} go together")
+        if a is not None:
+            _need(a, n1, (B, H, pp, dv_), torch.float32, dev)
+            _need(b_, n2, (B, H, pp), torch.float32, dev)
+    desc = make_desc(B, H, T, d, dv_, chunk, _dtype_code(q.dtype), _dtype_code(gy.dtype), scan, scan_leaf)
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    _check(lib.kata_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_backward_workspace_bytes")
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dvv = torch.empty_like(v)
+        dP = torch.empty((H, P_DIM, d), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dvv, dP = out
+        _need(dq, "dq", q.shape, q.dtype, dev)
+        _need(dk, "dk", k.shape, q.dtype, dev)
+        _need(dvv, "dv", v.shape, q.dtype, dev)
+        _need(dP, "dP", (H, P_DIM, d), torch.float32, dev)
+    dS0 = dz0 = None
+    if return_state_grad:
+        dS0 = torch.empty((B, H, pp, dv_), dtype=torch.float32, device=dev)
+        dz0 = torch.empty((B, H, pp), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    sh = _stream_handle(stream, dev)
+    evarr = None
+    if events is not None:
+        if len(events) != 8:
+            raise ValueError("events: eight torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_backward_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(S0), _ptr(z0),
+                                 _ptr(gy), _ptr(gST), _ptr(gzT), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dP),
+                                 _ptr(dS0), _ptr(dz0), _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
+    _check(st, "kata_backward")
+    if return_state_grad:
+        return dq, dk, dvv, dP, dS0, dz0
+    return dq, dk, dvv, dP
 
 
 def decode_step(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

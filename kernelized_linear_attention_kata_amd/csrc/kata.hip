@@ -13,6 +13,7 @@
 #include <cstdlib>
 
 #include "../../include/kata.h"
+#include "kata_bwd.h"
 #include "kata_chunk.h"
 #include "kata_decode.h"
 #include "kata_flash.h"
@@ -86,7 +87,7 @@ int64_t slots_for(const kata_forward_desc* d) {
 // on the descriptor, so the workspace size is reproducible.
 constexpr int64_t kMaxLeaf = 64;
 
-Plan make_plan(const kata_forward_desc* d) {
+Plan make_plan(const kata_forward_desc* d, int64_t slots) {
   Plan p;
   p.n_chunks = (d->T + d->chunk - 1) / d->chunk;
   const int64_t bh = d->B * d->H;
@@ -97,7 +98,6 @@ Plan make_plan(const kata_forward_desc* d) {
   } else if (d->scan_leaf > 0) {
     p.leaf = d->scan_leaf < p.n_chunks ? d->scan_leaf : p.n_chunks;
   } else {
-    const int64_t slots = slots_for(d);
     const int64_t units = bh * p.n_chunks;
     int64_t rounds = (units + slots * kMaxLeaf - 1) / (slots * kMaxLeaf);
     if (rounds < 1) rounds = 1;
@@ -116,6 +116,8 @@ Plan make_plan(const kata_forward_desc* d) {
   p.ws_bytes = (size_t)bh * (size_t)p.n_leaf * (size_t)p.E * sizeof(float);
   return p;
 }
+
+Plan make_plan(const kata_forward_desc* d) { return make_plan(d, slots_for(d)); }
 
 kata_status launch_status() {
   return hipGetLastError() == hipSuccess ? KATA_OK : KATA_ERR_LAUNCH;
@@ -136,6 +138,18 @@ __global__ void kata_copy_or_zero(float* __restrict__ dst, const float* __restri
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// segments per column quad of kata_state_scan: the smallest power of two with at most
+// SCAN_ROWS leaf rows each, capped at SCAN_GMAX (more leaves take several passes)
+int scan_segments(const Plan& pl) {
+  int G = 1;
+  while (G < SCAN_GMAX && (int64_t)G * SCAN_ROWS < pl.n_leaf) G *= 2;
+  return G;
+}
+dim3 scan_grid(const Plan& pl, int G, int64_t bh) {
+  const int quads = (int)(pl.E / 4);
+  return dim3((unsigned)((quads + 256 / G - 1) / (256 / G)), (unsigned)bh);
+}
+
 template <class S, typename TIn, typename TOut>
 kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
                         const void* v, const float* P, const float* S0, const float* z0, void* y,
@@ -152,14 +166,10 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
   hipExtLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, e0, nullptr, 0,
                         (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  // segments per column quad: the smallest power of two with at most SCAN_ROWS leaf
-  // rows each, capped at SCAN_GMAX (more leaves take several passes)
-  int G = 1;
-  while (G < SCAN_GMAX && (int64_t)G * SCAN_ROWS < pl.n_leaf) G *= 2;
-  const int quads = (int)(pl.E / 4);
-  const dim3 sgrid((unsigned)((quads + 256 / G - 1) / (256 / G)), (unsigned)bh);
+  const int G = scan_segments(pl);
+  const dim3 sgrid = scan_grid(pl, G, bh);
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
-                        (int)S::DV, G, S0, z0, ST, zT);
+                        (int)S::DV, G, S0, z0, ST, zT, 0, 0);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
@@ -217,6 +227,100 @@ int64_t flash_tpad(int64_t T) { return (T + FL_QB - 1) / FL_QB * FL_QB; }
 
 size_t flash_ws_bytes(const kata_forward_desc* d) {
   return (size_t)(d->B * d->H) * (size_t)flash_ws_elems(flash_tpad(d->T)) * sizeof(bf16);
+}
+
+// ---- backward ----------------------------------------------------------------------
+// Supported: p = 16, d = dv = 64, chunk 64, bf16 q/k/v (and dq/dk/dv), y and gy in
+// out_dtype.  Concurrent workgroup slots for the leaf plan: two kata_bwd_query
+// workgroups per compute unit (kata_bwd_key, at one 8-wave workgroup per compute unit,
+// then runs the same leaves in two rounds).
+constexpr int64_t kBwdSlots = kComputeUnits * 2;
+
+kata_status validate_bwd(const kata_forward_desc* d) {
+  const kata_status s = validate(d);
+  if (s != KATA_OK) return s;
+  if (d->d != 64 || d->dv != 64 || d->chunk != 64 || d->in_dtype != KATA_BF16) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+struct BwdLayout {
+  Plan pl;
+  size_t off_wsr = 0, off_ghi = 0, off_glo = 0, off_h = 0, off_dpa = 0, off_dpb = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the backward: the forward's leaf prefix states, the backward's leaf
+// suffix states, g as two bf16 planes (hi, lo) and h (per token), and the dP partials
+// of the two chunk walks (one 16 x 64 block per workgroup).
+BwdLayout bwd_layout(const kata_forward_desc* d) {
+  BwdLayout L;
+  L.pl = make_plan(d, kBwdSlots);
+  const size_t bh = (size_t)(d->B * d->H);
+  const size_t tok = bh * (size_t)d->T;
+  const size_t st = bh * (size_t)L.pl.n_leaf * (size_t)L.pl.E * sizeof(float);
+  const size_t dp = bh * (size_t)L.pl.n_leaf * (size_t)BW_DP * sizeof(float);
+  L.off_wsr = align256(st);
+  L.off_ghi = L.off_wsr + align256(st);
+  L.off_glo = L.off_ghi + align256(tok * 64 * 2);
+  L.off_h = L.off_glo + align256(tok * 64 * 2);
+  L.off_dpa = L.off_h + align256(tok * 4);
+  L.off_dpb = L.off_dpa + align256(dp);
+  L.total = L.off_dpb + align256(dp);
+  return L;
+}
+
+template <typename TY>
+kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const void* q, const void* k,
+                         const void* v, const float* P, const float* S0, const float* z0, const void* gy, const float* gST, const float* gzT, void* dq, void* dk, void* dv,
+                         float* dP, float* dS0, float* dz0, unsigned char* wsb, hipStream_t st,
+                         hipEvent_t* ev) {
+  using S = BS;
+  const Plan& pl = L.pl;
+  const int64_t bh = d->B * d->H;
+  if (allow_smem(kata_chunk_state<S, bf16>, S::SMEM_STATE) != KATA_OK ||
+      allow_smem(kata_bwd_query<TY>, QA_SMEM) != KATA_OK || allow_smem(kata_bwd_rstate, RS_SMEM) != KATA_OK ||
+      allow_smem(kata_bwd_key, KB_SMEM) != KATA_OK)
+    return KATA_ERR_LAUNCH;
+  float* wsf = reinterpret_cast<float*>(wsb);
+  float* wsr = reinterpret_cast<float*>(wsb + L.off_wsr);
+  bf16* ghi = reinterpret_cast<bf16*>(wsb + L.off_ghi);
+  bf16* glo = reinterpret_cast<bf16*>(wsb + L.off_glo);
+  float* hb = reinterpret_cast<float*>(wsb + L.off_h);
+  float* dpa = reinterpret_cast<float*>(wsb + L.off_dpa);
+  float* dpb = reinterpret_cast<float*>(wsb + L.off_dpb);
+  hipEvent_t e[8];
+  for (int i = 0; i < 8; ++i) e[i] = ev ? ev[i] : nullptr;
+  const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
+  const int G = scan_segments(pl);
+  const dim3 sgrid = scan_grid(pl, G, bh);
+  const bf16* qb = (const bf16*)q;
+  const bf16* kb = (const bf16*)k;
+  const bf16* vb = (const bf16*)v;
+  // forward prefix states at every leaf start
+  hipExtLaunchKernelGGL((kata_chunk_state<S, bf16>), grid, dim3(256), S::SMEM_STATE, st, e[0], nullptr, 0, kb, vb,
+                        P, wsf, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[1], nullptr, 0, wsf, pl.n_leaf, (int)pl.E, 64, G,
+                        S0, z0, (float*)nullptr, (float*)nullptr, 0, 0);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QA_SMEM, st, e[2], nullptr, 0, qb, kb, vb,
+                        (const TY*)gy, P, (const float*)wsf, ghi, glo, hb, (bf16*)dq, dpa, d->T,
+                        (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL(kata_bwd_rstate, grid, dim3(256), RS_SMEM, st, e[3], nullptr, 0, qb, (const bf16*)ghi,
+                        (const float*)hb, P, wsr, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[4], nullptr, 0, wsr, pl.n_leaf, (int)pl.E, 64, G,
+                        gST, gzT, dS0, dz0, 1, 1);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL(kata_bwd_key, grid, dim3(512), KB_SMEM, st, e[5], nullptr, 0, qb, kb, vb, (const bf16*)ghi,
+                        (const bf16*)glo, (const float*)hb, P, (const float*)wsr, (bf16*)dk, (bf16*)dv, dpb, d->T,
+                        (int)d->H, (int)pl.leaf, pl.n_chunks);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL(kata_bwd_dp_reduce, dim3((unsigned)d->H, 4), dim3(256), 0, st, e[6], e[7], 0,
+                        (const float*)dpa, (const float*)dpb, dP, d->B, (int)d->H, pl.n_leaf);
+  return launch_status();
 }
 
 }  // namespace
@@ -323,6 +427,67 @@ kata_status kata_flash_forward(const kata_forward_desc* desc, const void* q, con
     hipExtLaunchKernelGGL(kata_flash_attn<bf16>, grid, dim3(64 * FL_WAVES), 0, st, ev[1], ev[2], 0, (const bf16*)ws,
                           (bf16*)y, desc->T, tpad, (int)bh);
   return launch_status();
+}
+
+kata_status kata_backward_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {
+  if (!bytes) return KATA_ERR_NULL;
+  const kata_status s = validate_bwd(desc);
+  if (s != KATA_OK) return s;
+  *bytes = bwd_layout(desc).total;
+  return KATA_OK;
+}
+
+kata_status kata_backward_timed(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                                const float* P, const float* S0, const float* z0, const void* gy,
+                                const float* gST, const float* gzT, void* dq, void* dk, void* dv, float* dP,
+                                float* dS0, float* dz0, void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events) {
+  const kata_status s = validate_bwd(desc);
+  if (s != KATA_OK) return s;
+  if ((S0 == nullptr) != (z0 == nullptr)) return KATA_ERR_NULL;
+  if ((gST == nullptr) != (gzT == nullptr)) return KATA_ERR_NULL;
+  if ((dS0 == nullptr) != (dz0 == nullptr)) return KATA_ERR_NULL;
+  if (!dP) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t bh = desc->B * desc->H;
+  const int64_t nP = desc->H * BW_DP;
+  if (bh == 0 || desc->T == 0) {
+    // no token: dP = 0 and the initial state's gradient is the final state's (S_T = S0)
+    if (nP > 0)
+      hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nP + 255) / 256)), dim3(256), 0, st, dP,
+                         (const float*)nullptr, nP);
+    if (bh > 0 && dS0) {
+      const int64_t nS = bh * P_DIM * P_DIM * desc->dv, nz = bh * P_DIM * P_DIM;
+      hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, dS0, gST, nS);
+      hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, dz0, gzT, nz);
+    }
+    return launch_status();
+  }
+  if (!q || !k || !v || !P || !gy || !dq || !dk || !dv) return KATA_ERR_NULL;
+  const BwdLayout L = bwd_layout(desc);
+  if (!workspace || workspace_bytes < L.total) return KATA_ERR_WORKSPACE;
+  if (L.pl.n_leaf > 0x7fffffff) return KATA_ERR_SHAPE;
+  hipEvent_t ev[8];
+  hipEvent_t* evp = nullptr;
+  if (events) {
+    for (int i = 0; i < 8; ++i) {
+      if (!events[i]) return KATA_ERR_NULL;
+      ev[i] = (hipEvent_t)events[i];
+    }
+    evp = ev;
+  }
+  unsigned char* wsb = (unsigned char*)workspace;
+  if (desc->out_dtype == KATA_F32)
+    return run_backward<float>(desc, L, q, k, v, P, S0, z0, gy, gST, gzT, dq, dk, dv, dP, dS0, dz0, wsb, st, evp);
+  return run_backward<bf16>(desc, L, q, k, v, P, S0, z0, gy, gST, gzT, dq, dk, dv, dP, dS0, dz0, wsb, st, evp);
+}
+
+kata_status kata_backward(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                          const float* P, const float* S0, const float* z0, const void* gy,
+                          const float* gST, const float* gzT, void* dq, void* dk, void* dv, float* dP, float* dS0,
+                          float* dz0, void* workspace, size_t workspace_bytes, void* stream) {
+  return kata_backward_timed(desc, q, k, v, P, S0, z0, gy, gST, gzT, dq, dk, dv, dP, dS0, dz0, workspace,
+                             workspace_bytes, stream, nullptr);
 }
 
 kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,

@@ -7,7 +7,8 @@
 // O(log(T/C)).  The combine operator on states [S | z] is elementwise addition.
 //
 // Layout: ws[bh][leaf][e], e < E = 144*dv + 256 (packed S then Z, see kata_chunk.h).
-// The exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g'.
+// The exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g' (or the suffix
+// sum over g' > g in reverse mode).
 #pragma once
 
 #include "kata_common.h"
@@ -59,22 +60,34 @@ __device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, in
 constexpr int SCAN_ROWS = 16;    // rows per segment and pass (registers)
 constexpr int SCAN_GMAX = 16;    // segments per quad
 
-// Canonical initial value of element e (upper-triangle entry of S0 / z0), 0 for none.
-__device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const float* S0, const float* z0) {
+// Canonical initial value of element e, 0 for none: the upper-triangle entry of S0 / z0
+// (sym = false: a state, whose mirror entries are equal), or the mean of the two mirror
+// entries (sym = true: a gradient with respect to a state, whose symmetric part is what
+// acts on the symmetric feature).
+__device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const float* S0, const float* z0,
+                                              bool sym) {
   int a, b, col;
   bool is_z, mirror;
   if (!packed_to_pair(e, dv, a, b, col, is_z, mirror)) return 0.f;
   const int64_t pp = (int64_t)P_DIM * P_DIM;
   const int lo = a < b ? a : b, hi = a < b ? b : a;
-  if (!is_z) return S0 ? S0[(bh * pp + lo * P_DIM + hi) * dv + col] : 0.f;
-  return z0 ? z0[bh * pp + lo * P_DIM + hi] : 0.f;
+  if (!is_z) {
+    if (!S0) return 0.f;
+    const float x = S0[(bh * pp + lo * P_DIM + hi) * dv + col];
+    return sym ? 0.5f * (x + S0[(bh * pp + hi * P_DIM + lo) * dv + col]) : x;
+  }
+  if (!z0) return 0.f;
+  const float x = z0[bh * pp + lo * P_DIM + hi];
+  return sym ? 0.5f * (x + z0[bh * pp + hi * P_DIM + lo]) : x;
 }
 
-// grid (ceil((E/4) / (256/G)), B*H), block 256.  E is a multiple of 4.
+// grid (ceil((E/4) / (256/G)), B*H), block 256.  E is a multiple of 4.  reverse = 1
+// scans the leaves from the last to the first (an exclusive suffix: leaf g receives
+// init + sum_{g' > g} state_g'), as the backward pass needs; sym_init as in scan_initial.
 __global__ void __launch_bounds__(256)
 kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
                 const float* __restrict__ S0, const float* __restrict__ z0,
-                float* __restrict__ ST, float* __restrict__ zT) {
+                float* __restrict__ ST, float* __restrict__ zT, int reverse, int sym_init) {
   __shared__ f32x4 tot[256];
   __shared__ f32x4 carry_s[256];
   const int tid = threadIdx.x;
@@ -86,11 +99,12 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
   float* base = ws + bh * n_leaf * (int64_t)E + e0;
   const int64_t per_pass = (int64_t)SCAN_ROWS * G;
   const int lseg = (int)((n_leaf < per_pass ? n_leaf : per_pass) + G - 1) / G;
+  auto row = [&](int64_t i) { return reverse ? n_leaf - 1 - i : i; };   // scan position -> leaf
 
   f32x4 carry = zero4();   // the quad's running carry, kept by segment 0
   if (seg == 0 && active) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0);
+    for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0, sym_init != 0);
   }
   for (int64_t r0 = 0; r0 < n_leaf; r0 += (int64_t)lseg * G) {
     const int64_t rs = r0 + (int64_t)seg * lseg;
@@ -99,7 +113,7 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
 #pragma unroll
     for (int i = 0; i < SCAN_ROWS; ++i) {
       const bool ok = active && i < lseg && rs + i < n_leaf;
-      x[i] = ok ? *reinterpret_cast<const f32x4*>(base + (rs + i) * E) : zero4();
+      x[i] = ok ? *reinterpret_cast<const f32x4*>(base + row(rs + i) * E) : zero4();
       tsum += x[i];
     }
     tot[tid] = tsum;
@@ -109,7 +123,7 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
     for (int s2 = 0; s2 < seg; ++s2) c += tot[ql + s2 * QW];
 #pragma unroll
     for (int i = 0; i < SCAN_ROWS; ++i) {
-      if (active && i < lseg && rs + i < n_leaf) *reinterpret_cast<f32x4*>(base + (rs + i) * E) = c;
+      if (active && i < lseg && rs + i < n_leaf) *reinterpret_cast<f32x4*>(base + row(rs + i) * E) = c;
       c += x[i];
     }
     if (seg == 0) {

@@ -177,6 +177,23 @@ def make_decode(device="cpu", *, N: Optional[int] = None, H: Optional[int] = Non
                         q0=q0, k0=k0, v0=v0, q=q, k=k, v=v, repeat_src=src)
 
 
+def make_output_grad(B: int, H: int, T: int, dv: int, dtype: str = "bf16", seed: int = 0,
+                     device="cpu") -> torch.Tensor:
+    """A seeded gradient of the loss with respect to y, [B, H, T, dv]: standard normal / 8
+    (the scale of the value inputs), stored in ``dtype`` ("bf16" or "f32")."""
+    g = _gen(1000 + seed, device)
+    return _normal((B, H, T, dv), 1.0 / 8.0, g, device).to(_torch_dtype(dtype))
+
+
+def make_state_grad(B: int, H: int, dv: int, seed: int = 0, device="cpu"):
+    """A seeded gradient (gST, gzT) of the loss with respect to the final state, float32,
+    standard normal / 8 (not symmetric in the feature pair)."""
+    g = _gen(2000 + seed, device)
+    gST = _normal((B, H, P_DIM * P_DIM, dv), 1.0 / 8.0, g, device)
+    gzT = _normal((B, H, P_DIM * P_DIM), 1.0 / 8.0, g, device)
+    return gST, gzT
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw uint16 bit patterns of a bfloat16 tensor, as a numpy array on the host."""
     assert t.dtype == torch.bfloat16

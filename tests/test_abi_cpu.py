@@ -166,3 +166,40 @@ def test_flash_workspace_and_validation():
     empty = Bd.make_desc(2, 3, 0, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
     assert lib.kata_flash_forward(ctypes.byref(empty), None, None, None, None, None, None, 0, None, None) \
         == Bd.KATA_OK
+
+
+def test_backward_workspace_and_validation():
+    lib = _lib_or_skip()
+    n = ctypes.c_size_t(0)
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_backward_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    # 2048 chunks per head, 512 concurrent workgroups -> leaves of 64 chunks, 32 per head:
+    # forward and backward leaf states, g (hi, lo bf16), h (f32), two dP partial sets
+    st = 16 * 32 * (144 * 64 + 256) * 4
+    tok = 16 * 131072
+    assert n.value == 2 * st + 2 * tok * 128 + tok * 4 + 2 * 16 * 32 * 1024 * 4
+    fake = ctypes.c_void_p(0x1000)
+    args15 = [fake] * 15
+    for field, value, status in [("d", 16, Bd.KATA_ERR_UNSUPPORTED), ("chunk", 128, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("in_dtype", Bd.KATA_F32, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("p", 8, Bd.KATA_ERR_UNSUPPORTED), ("T", -1, Bd.KATA_ERR_SHAPE),
+                                 ("out_dtype", 9, Bd.KATA_ERR_UNSUPPORTED)]:
+        bad = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        setattr(bad, field, value)
+        assert lib.kata_backward_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == status, field
+        assert lib.kata_backward(ctypes.byref(bad), *args15, fake, 1 << 40, None) == status, field
+    d = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_backward_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    # pointer pairs go together: S0/z0 (arguments 5, 6), gST/gzT (8, 9), dS0/dz0 (14, 15)
+    for i in (4, 7, 13):
+        a = list(args15)
+        a[i] = None
+        assert lib.kata_backward(ctypes.byref(d), *a, fake, 1 << 40, None) == Bd.KATA_ERR_NULL, i
+    a = list(args15)
+    a[12] = None                       # dP
+    assert lib.kata_backward(ctypes.byref(d), *a, fake, 1 << 40, None) == Bd.KATA_ERR_NULL
+    a = list(args15)
+    a[0] = None                        # q
+    assert lib.kata_backward(ctypes.byref(d), *a, fake, 1 << 40, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_backward(ctypes.byref(d), *args15, fake, n.value - 1, None) == Bd.KATA_ERR_WORKSPACE
+    assert lib.kata_backward(ctypes.byref(d), *args15, None, 1 << 40, None) == Bd.KATA_ERR_WORKSPACE

@@ -23,6 +23,7 @@ workload on the host's cores.
     python bench.py [--steps K] [--warmup W] [--chunk C] [--no-cpu-baseline]
     python bench.py --decode     # the recurrent decode step instead (its own JSON line)
     python bench.py --flash      # the flash-style O(T^2) forward on the 340M-layer workload
+    python bench.py --backward   # the chunked-state backward on the long-context workload
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -292,6 +293,139 @@ def bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+BWD_METRIC = ("KATA causal backward (dq, dk, dv, dP) tokens/sec at T=131072, chunked-state form "
+              "+ % of HBM peak (1 GPU)")
+BWD_KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_bwd_query", "kata_bwd_rstate", "kata_state_scan(rev)",
+               "kata_bwd_key", "kata_bwd_dp_reduce")
+
+
+def bwd_algorithmic_bytes(B, H, T, d, dv, n_leaf, gy_bytes):
+    """Bytes each backward kernel must move per launch under the byte model of the path:
+    its token streams (bf16 q, k, v, dq, dk, dv; gy; g as two bf16 planes and h in f32
+    between the walks) plus the leaf states it reads or writes."""
+    E = 144 * dv + 256
+    states = B * H * n_leaf * E * 4
+    parts = B * H * n_leaf * 16 * d * 4
+    tok = B * H * T
+    g_planes = tok * dv * 2 * 2
+    return {
+        "kata_chunk_state": tok * (d + dv) * 2 + states,
+        "kata_state_scan": 2 * states,
+        "kata_bwd_query": tok * (2 * d + dv) * 2 + tok * dv * gy_bytes + tok * d * 2 + g_planes + tok * 4
+        + states + parts,
+        "kata_bwd_rstate": tok * (d * 2 + dv * 2 + 4) + states,
+        "kata_state_scan(rev)": 2 * states,
+        "kata_bwd_key": tok * (2 * d + dv) * 2 + g_planes + tok * 4 + tok * (d + dv) * 2 + states + parts,
+        "kata_bwd_dp_reduce": 2 * parts + H * 16 * d * 4,
+    }
+
+
+def bwd_cpu_baseline(case, gy, T_sample, heads_sample):
+    """The oracle's O(T^2) backward on the first T_sample tokens of heads_sample heads,
+    extrapolated to the whole workload by its T^2 cost."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    hs = slice(0, heads_sample)
+    q = O.bf16_bits_to_f64(I.bf16_bits(case.q[:, hs, :T_sample]))
+    k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
+    v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
+    g = O.bf16_bits_to_f64(I.bf16_bits(gy[:, hs, :T_sample]))
+    P = case.P[hs].double().cpu().numpy()
+    t0 = time.perf_counter()
+    O.backward_quadratic(q, k, v, P, g)
+    dt = time.perf_counter() - t0
+    scale = (case.T / T_sample) ** 2 * (case.H / heads_sample)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 O(T^2) oracle backward on the first {T_sample} tokens of {heads_sample} of "
+                       f"{case.H} heads, {dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} "
+                       f"by the T^2 cost")}
+
+
+def bench_backward(args):
+    import torch
+    import kernelized_linear_attention_kata_amd as kata
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nb = max(1, args.batches)
+    seed0 = I.WORKLOADS["long"]["seed"]
+    cases = [I.make_forward("long", device=dev, seed=seed0 + b) for b in range(nb)]
+    c0 = cases[0]
+    B, H, T, d, dv = c0.B, c0.H, c0.T, c0.d, c0.dv
+    gys = [I.make_output_grad(B, H, T, dv, seed=seed0 + b, device=dev) for b in range(nb)]
+    ws_bytes = kata.backward_workspace_bytes(B, H, T, d, dv, 64, scan=args.scan, scan_leaf=args.leaf)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [(torch.empty_like(c0.q), torch.empty_like(c0.k), torch.empty_like(c0.v),
+             torch.empty((H, 16, d), dtype=torch.float32, device=dev)) for _ in range(nb)]
+    stream = torch.cuda.current_stream(dev)
+    E = 144 * dv + 256
+    tok = B * H * T
+    # workspace = 2 states + g planes + h + 2 dP partial sets (each block 256-byte aligned)
+    n_leaf = (ws_bytes - 2 * tok * dv * 2 - tok * 4) // (2 * B * H * (E + 16 * d) * 4)
+
+    def step(i, events=None):
+        c = cases[i % nb]
+        kata.backward(c.q, c.k, c.v, c.P, gys[i % nb], scan=args.scan, scan_leaf=args.leaf, workspace=ws,
+                      out=outs[i % nb], stream=stream, events=events)
+
+    settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - settle0 < args.settle_s:
+        for _ in range(4):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - settle0
+    for i in range(args.warmup):
+        step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [t0, t1] + [e for es in evs for e in es]:
+        e.record(stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    per_kernel = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                  for j, name in enumerate(BWD_KERNELS)}
+    abytes = bwd_algorithmic_bytes(B, H, T, d, dv, n_leaf, 2)
+    kernels = {name: {"ms": round(ms, 4), "alg_bytes": abytes[name],
+                      "alg_GBps": round(abytes[name] / (ms / 1e3) / 1e9, 1),
+                      "hbm_frac": round(abytes[name] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for name, ms in per_kernel.items()}
+    dominant = max(per_kernel, key=per_kernel.get)
+    achieved = abytes[dominant] / (per_kernel[dominant] / 1e3) / 1e9
+    step_bytes = sum(abytes.values())
+    result = {
+        "metric": BWD_METRIC, "value": B * T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic ({nb} distinct seeded batches of q, k, v and gy, cycled per step)",
+        "config": {"workload": f"long-context KATA backward: B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v/gy "
+                               f"(dq, dk, dv bf16; dP f32), chunk 64, {args.scan} scans over {n_leaf} leaf "
+                               f"states per head",
+                   "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "step_alg_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+        "kernels": kernels,
+        "source_hash": source_hash(),
+        "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = bwd_cpu_baseline(c0, gys[0], args.bwd_cpu_tokens, 8)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +441,9 @@ def main():
     ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
+    ap.add_argument("--backward", action="store_true", help="time the chunked-state backward instead")
+    ap.add_argument("--bwd-cpu-tokens", type=int, default=16384,
+                    help="prefix length of the oracle's backward sample (CPU baseline of --backward)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
@@ -332,6 +469,9 @@ def main():
         return
     if args.flash:
         bench_flash(args)
+        return
+    if args.backward:
+        bench_backward(args)
         return
 
     import torch

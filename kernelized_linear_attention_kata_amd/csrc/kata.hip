@@ -279,7 +279,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   const Plan& pl = L.pl;
   const int64_t bh = d->B * d->H;
   if (allow_smem(kata_chunk_state<S, bf16>, S::SMEM_STATE) != KATA_OK ||
-      allow_smem(kata_bwd_query<TY>, QA_SMEM) != KATA_OK || allow_smem(kata_bwd_rstate, RS_SMEM) != KATA_OK ||
+      allow_smem(kata_bwd_query<TY>, QaGy<TY>::SMEM) != KATA_OK || allow_smem(kata_bwd_rstate, RS_SMEM) != KATA_OK ||
       allow_smem(kata_bwd_key, KB_SMEM) != KATA_OK)
     return KATA_ERR_LAUNCH;
   float* wsf = reinterpret_cast<float*>(wsb);
@@ -304,7 +304,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[1], nullptr, 0, wsf, pl.n_leaf, (int)pl.E, 64, G,
                         S0, z0, (float*)nullptr, (float*)nullptr, 0, 0);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QA_SMEM, st, e[2], nullptr, 0, qb, kb, vb,
+  hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QaGy<TY>::SMEM, st, e[2], nullptr, 0, qb, kb, vb,
                         (const TY*)gy, P, (const float*)wsf, ghi, glo, hb, (bf16*)dq, dpa, d->T,
                         (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;

@@ -56,9 +56,14 @@ constexpr int QA_OFF_WZ = QA_OFF_WACC + BS::WACC_BYTES;
 constexpr int QA_OFF_HT = QA_OFF_WZ + BS::WZ_BYTES;
 constexpr int QA_OFF_Z = QA_OFF_HT + BW_HT_BYTES;
 constexpr int QA_OFF_PF = QA_OFF_Z + BS::Z_BYTES;
-constexpr int QA_SMEM = QA_OFF_PF + BS::PF_BYTES;
-static_assert(QA_SMEM * 2 <= 156 * 1024, "two query workgroups per CU");
-static_assert(4 * 4 * WAVE * 16 <= BW_HT_BYTES, "dP reduction fits the HT region");
+constexpr int QA_OFF_PT = QA_OFF_PF + BS::PF_BYTES;
+constexpr int QA_OFF_GY = QA_OFF_PT + 4 * 2 * WAVE * 8;
+// gy rows of the chunk (row stride keeps 16-byte alignment and spreads the banks)
+template <typename TY> struct QaGy {
+  static constexpr int STR = sizeof(TY) == 2 ? 72 : 68;
+  static constexpr int SMEM = QA_OFF_GY + BS::C * STR * (int)sizeof(TY);
+};
+static_assert(QaGy<bf16>::SMEM * 2 <= 156 * 1024, "two query workgroups per CU (bf16 gy)");
 
 // kata_bwd_key LDS (bytes)
 constexpr int KB_OFF_HX = 0;
@@ -72,9 +77,10 @@ constexpr int KB_OFF_W = KB_OFF_U + BS::U_BYTES;
 constexpr int KB_OFF_UACC = KB_OFF_W + BS::U_BYTES;
 constexpr int KB_OFF_HS = KB_OFF_UACC + BS::WACC_BYTES;
 constexpr int KB_OFF_PF = KB_OFF_HS + BS::C * 4;
-constexpr int KB_SMEM = KB_OFF_PF + BS::PF_BYTES;
+constexpr int KB_OFF_PT = KB_OFF_PF + BS::PF_BYTES;
+constexpr int KB_SMEM = KB_OFF_PT + 4 * 2 * WAVE * 8;
 static_assert(KB_SMEM <= 156 * 1024, "key workgroup LDS");
-static_assert(4 * 4 * WAVE * 16 <= BS::HX_BYTES, "dP reduction fits the HX region");
+static_assert(4 * 4 * WAVE * 16 <= BS::HX_BYTES && 4 * 4 * WAVE * 16 <= BW_HT_BYTES, "dP reduction fits");
 
 // kata_bwd_rstate LDS (bytes)
 constexpr int RS_OFF_VF = 0;
@@ -134,80 +140,76 @@ __device__ __forceinline__ Op4<true> get_z(const bf16* Zs, int lane) {
 // ---- input-space gradient and the projection's gradient ----------------------------
 
 // P^T as 16x16x16 A-fragments (M = input column within block db, K = projection index):
-// lane (n, g) holds P[4g + i][16 db + n], split hi/lo.
-struct PT4 { Op4<true> f[4]; };
-__device__ __forceinline__ void load_pt(PT4& pt, const float* __restrict__ P, int h, int lane) {
+// lane (n, g) holds P[4g + i][16 db + n], split hi/lo.  Loop-invariant: written to LDS
+// once (PTs[db][hi/lo][lane], 8 bytes each, 4 KiB) and read back per use.
+constexpr int BW_PT_BYTES = 4 * 2 * WAVE * 8;
+__device__ __forceinline__ void write_pt(bf16* PTs, const float* __restrict__ P, int h, int lane) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = P[((int64_t)h * P_DIM + 4 * g + i) * 64 + 16 * db + n];
-    pt.f[db] = make4<true>(x);
+    const Op4<true> f = make4<true>(x);
+    *reinterpret_cast<bf16x4*>(PTs + ((2 * db) * WAVE + lane) * 4) = f.hi;
+    *reinterpret_cast<bf16x4*>(PTs + ((2 * db + 1) * WAVE + lane) * 4) = f.lo;
   }
 }
-
-// Constant fragments: the 16 x 16 identity as a 16x16x16 B-fragment, and the column
-// selectors that transpose 16 input columns of a token-row fragment (see grad_head).
-struct GradConst {
-  bf16x4 eye;
-  bf16x8 hot[2];
-};
-__device__ __forceinline__ GradConst make_grad_const(int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  GradConst c;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c.eye[i] = (bf16)((4 * g + i == n) ? 1.f : 0.f);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c.hot[kk][i] = (bf16)((8 * kk + i == n) ? 1.f : 0.f);
-  }
-  return c;
+__device__ __forceinline__ Op4<true> read_pt(const bf16* PTs, int db, int lane) {
+  Op4<true> f;
+  f.hi = *reinterpret_cast<const bf16x4*>(PTs + ((2 * db) * WAVE + lane) * 4);
+  f.lo = *reinterpret_cast<const bf16x4*>(PTs + ((2 * db + 1) * WAVE + lane) * 4);
+  return f;
 }
-
-struct DPAcc { f32x4 t[4]; };   // lane (a, g) holds dP[a][16 db + 4g + r]
 
 // Given the projected-space gradient of one 16-token block (lane (t, g) holds
 // d_t[4g + r], t = the block's token n): store P^T d_t (input-space gradient, bf16, four
-// consecutive columns per lane per 16-column block) and add d x^T to the dP
-// accumulators.  xr are the block's input rows as loaded for the projection (lane
-// (t, g) holds x_t[16 g + 8 kk + i]).  d^T comes from one identity MFMA per hi/lo half
-// (exact), x^T from column-selector MFMAs (exact), so dP takes one MFMA per half.
-__device__ __forceinline__ void grad_head(const f32x4& d, const PT4& pt, const bf16x8 (&xr)[2],
-                                          const GradConst& gc, __amdgpu_buffer_rsrc_t out, int row_byte,
-                                          DPAcc& acc, int lane) {
-  const int g = lane >> 4;
+// consecutive columns per lane per 16-column block) and add d x^T to this wave's dP
+// accumulators.
+// xr are the block's input rows as loaded for the projection (lane (t, g) holds
+// x_t[16 g + 8 kk + i]).  d^T comes from one identity MFMA per hi/lo half (exact), x^T
+// from column-selector MFMAs (exact), so dP takes one MFMA per half.
+struct DPAcc { f32x4 t[4]; };   // lane (a, g) holds dP[a][16 db + 4g + r]
+
+__device__ __forceinline__ void grad_head(const f32x4& d, const bf16* PTs, const bf16x8 (&xr)[2],
+                                          __amdgpu_buffer_rsrc_t out, int row_byte, DPAcc& acc, int lane) {
+  const int n = lane & 15, g = lane >> 4;
   float dv4[4] = {d[0], d[1], d[2], d[3]};
   const Op4<true> df = make4<true>(dv4);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const f32x4 o = mma<true, true>(pt.f[db], df, zero4());   // lane (t, g): column 16db + 4g + r
+    const f32x4 o = mma<true, true>(read_pt(PTs, db, lane), df, zero4());   // lane (t, g): column 16db + 4g + r
     Store4<bf16>::st(out, row_byte + (16 * db + 4 * g) * 2, o);
   }
   // d^T: C[t][a] = sum_k d_t[k] [k == a]; lane (a, g) then holds d_{4g + r}[a]
-  f32x4 tr = mfma16(df.hi, gc.eye, zero4());
-  tr = mfma16(df.lo, gc.eye, tr);
+  bf16x4 eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = (bf16)((4 * g + i == n) ? 1.f : 0.f);
+  f32x4 tr = mfma16(df.hi, eye, zero4());
+  tr = mfma16(df.lo, eye, tr);
   float tv[4] = {tr[0], tr[1], tr[2], tr[3]};
   const Op4<true> tf = make4<true>(tv);
-  bf16x8 zero8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) zero8[i] = (bf16)0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    // x^T block db: C[t][n'] = x_t[16 db + n'], lane (n', g) holds token 4g + r
+    // x^T block db: C[t][n'] = x_t[16 db + n'], lane (n', g) holds token 4g + r; the
+    // selector picks input column 16 db + n' out of this lane group's 8 columns
     f32x4 xt = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) xt = mfma32(xr[kk], g == db ? gc.hot[kk] : zero8, xt);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 hot;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hot[i] = (bf16)((g == db && 8 * kk + i == n) ? 1.f : 0.f);
+      xt = mfma32(xr[kk], hot, xt);
+    }
     Op4<false> xa;
 #pragma unroll
     for (int i = 0; i < 4; ++i) xa.hi[i] = (bf16)xt[i];
-    acc.t[db] = mma<false, true>(xa, tf, acc.t[db]);       // dP^T[d][a] += sum_t x_t[d] d_t[a]
+    acc.t[db] = mma<false, true>(xa, tf, acc.t[db]);    // lane (a, g): += sum_t x_t[16db + 4g + r] d_t[a]
   }
 }
 
-// Sum the dP accumulators of the 4 waves that hold them (through `red`, 16 KiB of LDS
-// free at this point) and write the workgroup's partial (canonical [a][col]).
+// Sum the dP accumulators of the 4 waves that hold them, in a fixed order (through `red`,
+// 16 KiB of LDS free at this point), and write the workgroup's partial ([a][col]).
 __device__ __forceinline__ void write_dp_partial(const DPAcc& acc, bool holder, int hw, float* red,
                                                  float* __restrict__ out, int tid, int lane) {
   if (holder) {
@@ -266,6 +268,8 @@ __device__ __forceinline__ void ht_contract(f32x4& du, float* gn, const bf16* HT
         if constexpr (GN) *gn += w1 * f[r] * Q[0][r] * up;
       }
     }
+    // keep the fragment reads of at most three diagonals in flight (register pressure)
+    if (delta % 3 == 2) asm volatile("" ::: "memory");
   }
 }
 
@@ -321,6 +325,9 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   bf16* HT = reinterpret_cast<bf16*>(smem + QA_OFF_HT);
   bf16* Zs = reinterpret_cast<bf16*>(smem + QA_OFF_Z);
   bf16* Pf = reinterpret_cast<bf16*>(smem + QA_OFF_PF);
+  bf16* PTs = reinterpret_cast<bf16*>(smem + QA_OFF_PT);
+  TY* gys = reinterpret_cast<TY*>(smem + QA_OFF_GY);
+  constexpr int GYS = QaGy<TY>::STR;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -333,10 +340,7 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   const bool zrole = wave == 0;
 
   if (wave == 0) write_P<S>(Pf, P, h, lane);
-  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
-  PT4 pt;
-  load_pt(pt, P, h, lane);
-  const GradConst gc = make_grad_const(lane);
+  if (wave == 1) write_pt(PTs, P, h, lane);
   StateAcc<S> st;
   load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
   auto publish = [&]() {
@@ -366,20 +370,34 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   DPAcc dpa;
 #pragma unroll
   for (int db = 0; db < 4; ++db) dpa.t[db] = zero4();
-  __syncthreads();   // P fragments and the first HT / Z written
+  __syncthreads();   // P fragments, P^T fragments and the first HT / Z written
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = tc0 + c * S::C;
     progress_priority(c, nch);
-    stage_chunk<S, bf16, true>(cur.c, Pf, sel, Us, Ws, Wacc, Wz, vf, nullptr, wave, lane);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      *reinterpret_cast<bf16x8*>(vr + (wave * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = cur.c.v[0][kk].x;
-    float gyv[2][8];
+    // Lane-derived constants (selectors, masks, addresses) are rebuilt in every chunk
+    // from an opaque copy of the lane index: hoisted out of the loop they would not fit
+    // in registers next to the state and the prefetched inputs, and spilled values come
+    // back from scratch memory with its full latency.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
+    const int n = lane & 15, g = lane >> 4;
+    {
+      const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
+      stage_chunk<S, bf16, true>(cur.c, Pf, sel, Us, Ws, Wacc, Wz, vf, nullptr, wave, lane);
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gyv[kk][i] = cur.gy[kk][i];
+      *reinterpret_cast<bf16x8*>(vr + (wave * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = cur.c.v[0][kk].x;
+      // this lane's gy columns, read back by the same lane once den_t is known
+      TY* gp = gys + (wave * 16 + n) * GYS + 32 * kk + 8 * g;
+      if constexpr (sizeof(TY) == 2) {
+        *reinterpret_cast<bf16x8*>(gp) = cur.gy[kk].x;
+      } else {
+        *reinterpret_cast<f32x4*>(gp) = cur.gy[kk].a;
+        *reinterpret_cast<f32x4*>(gp + 4) = cur.gy[kk].b;
+      }
     }
     const bf16x8 qr[2] = {cur.c.q[0][0].x, cur.c.q[0][1].x};
     if (c + 1 < nch) load_qa<TY>(cur, rs, t0 + S::C, wave, lane);
@@ -417,8 +435,19 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     float gv[2][8];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      const TY* gp = gys + t * GYS + 32 * kk + 8 * g;
+      if constexpr (sizeof(TY) == 2) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(gp);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) gv[kk][i] = gyv[kk][i] * inv;
+        for (int i = 0; i < 8; ++i) gv[kk][i] = (float)x[i] * inv;
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(gp), b = *reinterpret_cast<const f32x4*>(gp + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gv[kk][i] = a[i] * inv;
+          gv[kk][4 + i] = b[i] * inv;
+        }
+      }
     }
     Op8<true> G[2];
 #pragma unroll
@@ -487,7 +516,7 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 #pragma unroll
     for (int r = 0; r < 4; ++r) du[r] += 2.f * hh * zu[r];
 
-    grad_head(du, pt, qr, gc, rs.dq, ((t0 + t) * 64) * 2, dpa, lane);
+    grad_head(du, PTs, qr, rs.dq, ((t0 + t) * 64) * 2, dpa, lane);
 
     const bool more = c + 1 < nch;
     if (more) state_update<S>(st, Wacc, Wz, vf, nullptr, wave, zrole, lane);
@@ -611,6 +640,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
   float* Uacc = reinterpret_cast<float*>(smem + KB_OFF_UACC);
   float* hs = reinterpret_cast<float*>(smem + KB_OFF_HS);
   bf16* Pf = reinterpret_cast<bf16*>(smem + KB_OFF_PF);
+  bf16* PTs = reinterpret_cast<bf16*>(smem + KB_OFF_PT);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int role = wave >> 2, mb = wave & 3;
@@ -628,10 +658,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     *reinterpret_cast<bf16x4*>(hx + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
   }
   if (wave == 0) write_P<S>(Pf, P, h, lane);
-  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
-  PT4 pt;
-  if (role == 1) load_pt(pt, P, h, lane);
-  const GradConst gc = make_grad_const(lane);
+  if (wave == 1) write_pt(PTs, P, h, lane);
 
   KbState st;
   {
@@ -686,7 +713,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
   DPAcc dpa;
 #pragma unroll
   for (int db = 0; db < 4; ++db) dpa.t[db] = zero4();
-  __syncthreads();   // P fragments, hx zeros, first publish
+  __syncthreads();   // P and P^T fragments, hx zeros, first publish
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = chunk_t0(c);
@@ -704,6 +731,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         *reinterpret_cast<bf16x8*>(grh + (mb * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = cur.gg[kk].x;
+      const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
       stage_v<S, bf16>(cur.gg, mb, sel, gf, nullptr, lane);
       if (g == 0) hs[mb * 16 + n] = cur.hv;
     } else {
@@ -847,7 +875,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
       for (int r = 0; r < 4; ++r) dw[r] += 2.f * zw[r];
       const bf16x8 vx[2] = {vcur[0].x, vcur[1].x};
       ht_contract<false>(dw, nullptr, HT, vx, Q, lane);
-      grad_head(dw, pt, xr, gc, r_out, ((t0 + s_loc) * 64) * 2, dpa, lane);
+      grad_head(dw, PTs, xr, r_out, ((t0 + s_loc) * 64) * 2, dpa, lane);
     }
 
     // ---- state update: R += phi(U_c)^T G_c, Zr += U_c^T diag(h_c) U_c ----

@@ -301,21 +301,20 @@ BWD_KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_bwd_query", "kata_bw
 
 def bwd_algorithmic_bytes(B, H, T, d, dv, n_leaf, gy_bytes):
     """Bytes each backward kernel must move per launch under the byte model of the path:
-    its token streams (bf16 q, k, v, dq, dk, dv; gy; g as two bf16 planes and h in f32
-    between the walks) plus the leaf states it reads or writes."""
+    its token streams (bf16 q, k, v, dq, dk, dv; gy; the (1/den, h) f32 pair per token
+    between the walks) plus the leaf states and dP partials it reads or writes."""
     E = 144 * dv + 256
     states = B * H * n_leaf * E * 4
     parts = B * H * n_leaf * 16 * d * 4
     tok = B * H * T
-    g_planes = tok * dv * 2 * 2
+    gy_b = tok * dv * gy_bytes
     return {
         "kata_chunk_state": tok * (d + dv) * 2 + states,
         "kata_state_scan": 2 * states,
-        "kata_bwd_query": tok * (2 * d + dv) * 2 + tok * dv * gy_bytes + tok * d * 2 + g_planes + tok * 4
-        + states + parts,
-        "kata_bwd_rstate": tok * (d * 2 + dv * 2 + 4) + states,
+        "kata_bwd_query": tok * (2 * d + dv) * 2 + gy_b + tok * d * 2 + tok * 8 + states + parts,
+        "kata_bwd_rstate": tok * d * 2 + gy_b + tok * 8 + states,
         "kata_state_scan(rev)": 2 * states,
-        "kata_bwd_key": tok * (2 * d + dv) * 2 + g_planes + tok * 4 + tok * (d + dv) * 2 + states + parts,
+        "kata_bwd_key": tok * (2 * d + dv) * 2 + gy_b + tok * 8 + tok * (d + dv) * 2 + states + parts,
         "kata_bwd_dp_reduce": 2 * parts + H * 16 * d * 4,
     }
 
@@ -366,8 +365,8 @@ def bench_backward(args):
     stream = torch.cuda.current_stream(dev)
     E = 144 * dv + 256
     tok = B * H * T
-    # workspace = 2 states + g planes + h + 2 dP partial sets (each block 256-byte aligned)
-    n_leaf = (ws_bytes - 2 * tok * dv * 2 - tok * 4) // (2 * B * H * (E + 16 * d) * 4)
+    # workspace = 2 states + (1/den, h) pairs + 2 dP partial sets (each block 256-byte aligned)
+    n_leaf = (ws_bytes - tok * 8) // (2 * B * H * (E + 16 * d) * 4)
 
     def step(i, events=None):
         c = cases[i % nb]

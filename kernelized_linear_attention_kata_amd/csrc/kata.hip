@@ -245,14 +245,14 @@ kata_status validate_bwd(const kata_forward_desc* d) {
 
 struct BwdLayout {
   Plan pl;
-  size_t off_wsr = 0, off_ghi = 0, off_glo = 0, off_h = 0, off_dpa = 0, off_dpb = 0, total = 0;
+  size_t off_wsr = 0, off_ih = 0, off_dpa = 0, off_dpb = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of the backward: the forward's leaf prefix states, the backward's leaf
-// suffix states, g as two bf16 planes (hi, lo) and h (per token), and the dP partials
-// of the two chunk walks (one 16 x 64 block per workgroup).
+// suffix states, (1/den_t, h_t) per token, and the dP partials of the two chunk walks
+// (one 16 x 64 block per workgroup).
 BwdLayout bwd_layout(const kata_forward_desc* d) {
   BwdLayout L;
   L.pl = make_plan(d, kBwdSlots);
@@ -261,10 +261,8 @@ BwdLayout bwd_layout(const kata_forward_desc* d) {
   const size_t st = bh * (size_t)L.pl.n_leaf * (size_t)L.pl.E * sizeof(float);
   const size_t dp = bh * (size_t)L.pl.n_leaf * (size_t)BW_DP * sizeof(float);
   L.off_wsr = align256(st);
-  L.off_ghi = L.off_wsr + align256(st);
-  L.off_glo = L.off_ghi + align256(tok * 64 * 2);
-  L.off_h = L.off_glo + align256(tok * 64 * 2);
-  L.off_dpa = L.off_h + align256(tok * 4);
+  L.off_ih = L.off_wsr + align256(st);
+  L.off_dpa = L.off_ih + align256(tok * 8);
   L.off_dpb = L.off_dpa + align256(dp);
   L.total = L.off_dpb + align256(dp);
   return L;
@@ -279,14 +277,12 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   const Plan& pl = L.pl;
   const int64_t bh = d->B * d->H;
   if (allow_smem(kata_chunk_state<S, bf16>, S::SMEM_STATE) != KATA_OK ||
-      allow_smem(kata_bwd_query<TY>, QaGy<TY>::SMEM) != KATA_OK || allow_smem(kata_bwd_rstate, RS_SMEM) != KATA_OK ||
-      allow_smem(kata_bwd_key, KB_SMEM) != KATA_OK)
+      allow_smem(kata_bwd_query<TY>, QaGy<TY>::SMEM) != KATA_OK ||
+      allow_smem(kata_bwd_rstate<TY>, RS_SMEM) != KATA_OK || allow_smem(kata_bwd_key<TY>, KB_SMEM) != KATA_OK)
     return KATA_ERR_LAUNCH;
   float* wsf = reinterpret_cast<float*>(wsb);
   float* wsr = reinterpret_cast<float*>(wsb + L.off_wsr);
-  bf16* ghi = reinterpret_cast<bf16*>(wsb + L.off_ghi);
-  bf16* glo = reinterpret_cast<bf16*>(wsb + L.off_glo);
-  float* hb = reinterpret_cast<float*>(wsb + L.off_h);
+  float* ih = reinterpret_cast<float*>(wsb + L.off_ih);
   float* dpa = reinterpret_cast<float*>(wsb + L.off_dpa);
   float* dpb = reinterpret_cast<float*>(wsb + L.off_dpb);
   hipEvent_t e[8];
@@ -305,17 +301,17 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
                         S0, z0, (float*)nullptr, (float*)nullptr, 0, 0);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QaGy<TY>::SMEM, st, e[2], nullptr, 0, qb, kb, vb,
-                        (const TY*)gy, P, (const float*)wsf, ghi, glo, hb, (bf16*)dq, dpa, d->T,
+                        (const TY*)gy, P, (const float*)wsf, ih, (bf16*)dq, dpa, d->T,
                         (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL(kata_bwd_rstate, grid, dim3(256), RS_SMEM, st, e[3], nullptr, 0, qb, (const bf16*)ghi,
-                        (const float*)hb, P, wsr, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  hipExtLaunchKernelGGL((kata_bwd_rstate<TY>), grid, dim3(256), RS_SMEM, st, e[3], nullptr, 0, qb, (const TY*)gy,
+                        (const float*)ih, P, wsr, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[4], nullptr, 0, wsr, pl.n_leaf, (int)pl.E, 64, G,
                         gST, gzT, dS0, dz0, 1, 1);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL(kata_bwd_key, grid, dim3(512), KB_SMEM, st, e[5], nullptr, 0, qb, kb, vb, (const bf16*)ghi,
-                        (const bf16*)glo, (const float*)hb, P, (const float*)wsr, (bf16*)dk, (bf16*)dv, dpb, d->T,
+  hipExtLaunchKernelGGL((kata_bwd_key<TY>), grid, dim3(512), KB_SMEM, st, e[5], nullptr, 0, qb, kb, vb, (const TY*)gy,
+                        (const float*)ih, P, (const float*)wsr, (bf16*)dk, (bf16*)dv, dpb, d->T,
                         (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_bwd_dp_reduce, dim3((unsigned)d->H, 4), dim3(256), 0, st, e[6], e[7], 0,

@@ -18,7 +18,8 @@
 // (k, [v | 1]).  So the backward is two chunk walks:
 //   kata_bwd_query : forward order over the chunks of a leaf, from the forward's scanned
 //                    prefix state: den, g, h, du -> dq, and the dP share of du q^T;
-//                    writes g (hi/lo bf16 planes) and h for the second walk
+//                    writes 1/den_t and h_t (8 bytes per token) for the later kernels,
+//                    which form g_t = gy_t (1/den_t) again, bit for bit
 //   kata_bwd_rstate: per leaf, sum of phi(U_c)^T [G_c | h_c]   (Z part: U^T diag(h) U)
 //   kata_state_scan: (reverse) exclusive suffix of those leaf states; its total is dS0, dz0
 //   kata_bwd_key   : reverse order over the chunks of a leaf, from the suffix state:
@@ -78,7 +79,8 @@ constexpr int KB_OFF_UACC = KB_OFF_W + BS::U_BYTES;
 constexpr int KB_OFF_HS = KB_OFF_UACC + BS::WACC_BYTES;
 constexpr int KB_OFF_PF = KB_OFF_HS + BS::C * 4;
 constexpr int KB_OFF_PT = KB_OFF_PF + BS::PF_BYTES;
-constexpr int KB_SMEM = KB_OFF_PT + 4 * 2 * WAVE * 8;
+constexpr int KB_OFF_DW = KB_OFF_PT + 4 * 2 * WAVE * 8;
+constexpr int KB_SMEM = KB_OFF_DW + 2 * BS::C * P_DIM * 4;   // dw of two chunks (role 1 -> role 0)
 static_assert(KB_SMEM <= 156 * 1024, "key workgroup LDS");
 static_assert(4 * 4 * WAVE * 16 <= BS::HX_BYTES && 4 * 4 * WAVE * 16 <= BW_HT_BYTES, "dP reduction fits");
 
@@ -234,7 +236,9 @@ __device__ __forceinline__ void write_dp_partial(const DPAcc& acc, bool holder, 
 // x_t[32 kc + 8 g + i]); Q: rotated quads of u_t (Q[m] = u_t[4((g + m) & 3) .. + 3]).
 // With GN, also adds this lane's share of phi(u_t) . (H x_t) (query weights included) to
 // *gn: summed over the lane groups it is x_t . (the inter-chunk part of the numerator).
-template <bool GN>
+// Only the diagonals DLO <= delta < DHI are taken (the contraction may be split
+// between waves).
+template <bool GN, int DLO = 0, int DHI = NDELTA>
 __device__ __forceinline__ void ht_contract(f32x4& du, float* gn, const bf16* HT, const bf16x8 (&xf)[2],
                                             const f32x4 (&Q)[4], int lane) {
   const int n = lane & 15, g = lane >> 4;
@@ -244,7 +248,7 @@ __device__ __forceinline__ void ht_contract(f32x4& du, float* gn, const bf16* HT
     return j < 4 ? Q[m & 3][j] : Q[(m + 1) & 3][j - 4];
   };
 #pragma unroll
-  for (int delta = 0; delta < NDELTA; ++delta) {
+  for (int delta = DLO; delta < DHI; ++delta) {
     f32x4 f = zero4(), f2 = zero4();
     const int lrot = ((n - delta) & 15) + 16 * g;
 #pragma unroll
@@ -283,7 +287,7 @@ struct QaIn {
 
 struct QaRsrc {
   SeqRsrc s;
-  __amdgpu_buffer_rsrc_t gy, ghi, glo, hb, dq;
+  __amdgpu_buffer_rsrc_t gy, ih, dq;
 };
 
 template <typename TY>
@@ -311,8 +315,8 @@ template <typename TY>
 __global__ void __launch_bounds__(256, 2)
 kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                const TY* __restrict__ gy, const float* __restrict__ P,
-               const float* __restrict__ ws, bf16* __restrict__ ghi, bf16* __restrict__ glo,
-               float* __restrict__ hb, bf16* __restrict__ dq, float* __restrict__ dpart, int64_t T, int H,
+               const float* __restrict__ ws, float* __restrict__ ih, bf16* __restrict__ dq,
+               float* __restrict__ dpart, int64_t T, int H,
                int leaf_chunks, int64_t n_chunks) {
   using S = BS;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -360,9 +364,7 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   rs.s.k = make_rsrc(k + base_tok * 64, tb);
   rs.s.v = make_rsrc(v + base_tok * 64, tb);
   rs.gy = make_rsrc(gy + base_tok * 64, T * 64 * (int64_t)sizeof(TY));
-  rs.ghi = make_rsrc(ghi + base_tok * 64, tb);
-  rs.glo = make_rsrc(glo + base_tok * 64, tb);
-  rs.hb = make_rsrc(hb + base_tok, T * 4);
+  rs.ih = make_rsrc(ih + base_tok * 2, T * 8);
   rs.dq = make_rsrc(dq + base_tok * 64, tb);
   const int tc0 = (int)(c0 * S::C);
   QaIn<TY> cur;
@@ -451,12 +453,7 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     }
     Op8<true> G[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      G[kk] = make8<true>(gv[kk]);
-      const int off = ((t0 + t) * 64 + 32 * kk + 8 * g) * 2;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, G[kk].hi), rs.ghi, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, G[kk].lo), rs.glo, off, 0, 0);
-    }
+    for (int kk = 0; kk < 2; ++kk) G[kk] = make8<true>(gv[kk]);
 
     // g_t . v_s for the chunk's s <= t, and its a_ts-weighted sum (intra part of g_t . num_t)
     f32x4 D[4];
@@ -485,7 +482,10 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     gn = row_pair_sum<16>(gn);
     gn = row_pair_sum<32>(gn);
     const float hh = -gn * inv;                          // h_t = -(g_t . num_t) / den_t
-    if (g == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(hh), rs.hb, (t0 + t) * 4, 0, 0);
+    if (g == 0) {
+      const i32x2 ihv = {__float_as_int(inv), __float_as_int(hh)};
+      __builtin_amdgcn_raw_buffer_store_b64(ihv, rs.ih, (t0 + t) * 8, 0, 0);
+    }
 
     // intra-chunk: B_ts = 2 X_ts (g_t . v_s + h_t) for s <= t; du_t += sum_s B_ts w_s
     f32x4 Bm[4];
@@ -531,9 +531,12 @@ kata_bwd_query(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 // grid (n_leaf, B*H), block 256.  Per leaf, sum over its tokens of phi(u_t) [g_t | h_t]:
 // the packed S part accumulates phi(u) g^T exactly as kata_chunk_state accumulates
 // phi(w) v^T (u plays the key, the hi plane of g the value), and the z part is the
-// 16 x 16 matrix sum_t h_t u_t u_t^T.  Layout of ws as for kata_chunk_state.
+// 16 x 16 matrix sum_t h_t u_t u_t^T.  g_t = gy_t (1/den_t) is formed from gy and the
+// (1/den_t, h_t) pairs of kata_bwd_query, as that kernel formed it.  Layout of ws as for
+// kata_chunk_state.
+template <typename TY>
 __global__ void __launch_bounds__(256, 3)
-kata_bwd_rstate(const bf16* __restrict__ q, const bf16* __restrict__ ghi, const float* __restrict__ hb,
+kata_bwd_rstate(const bf16* __restrict__ q, const TY* __restrict__ gy, const float* __restrict__ ih,
                 const float* __restrict__ P, float* __restrict__ ws, int64_t T, int H, int leaf_chunks,
                 int64_t n_chunks) {
   using S = BS;
@@ -557,23 +560,40 @@ kata_bwd_rstate(const bf16* __restrict__ q, const bf16* __restrict__ ghi, const 
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
-  SeqRsrc rs;
-  rs.k = make_rsrc(q + base_tok * 64, T * 64 * 2);
-  rs.v = make_rsrc(ghi + base_tok * 64, T * 64 * 2);
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(hb + base_tok, T * 4);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base_tok * 64, T * 64 * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gy + base_tok * 64, T * 64 * (int64_t)sizeof(TY));
+  const __amdgpu_buffer_rsrc_t rih = make_rsrc(ih + base_tok * 2, T * 8);
+  struct In {
+    Vec8<bf16> x[2];   // q rows, projection column order
+    Vec8<TY> gy[2];    // gy rows, natural column order
+    i32x2 ih;          // (1/den, h) of token n
+  };
+  auto load_in = [&](In& r, int t0) {
+    const int t = t0 + wave * 16 + n;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      r.x[kk].load(rq, (t * 64 + 16 * g + 8 * kk) * 2);
+      r.gy[kk].load(rg, (t * 64 + 32 * kk + 8 * g) * (int)sizeof(TY));
+    }
+    r.ih = __builtin_amdgcn_raw_buffer_load_b64(rih, t * 8, 0, 0);
+  };
   const int tc0 = (int)(c0 * S::C);
-  ChunkIn<S, bf16> cur;
-  load_chunk<S, bf16, false>(cur, rs, tc0, wave, lane);
-  float hv = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rh, (tc0 + wave * 16 + n) * 4, 0, 0));
+  In in;
+  load_in(in, tc0);
   __syncthreads();   // P fragments written
   for (int c = 0; c < nch; ++c) {
     const int t0 = tc0 + c * S::C;
-    stage_chunk<S, bf16, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf, nullptr, wave, lane);
-    if (g == 0) hs[wave * 16 + n] = hv;
-    if (c + 1 < nch) {
-      load_chunk<S, bf16, false>(cur, rs, t0 + S::C, wave, lane);
-      hv = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rh, (t0 + S::C + wave * 16 + n) * 4, 0, 0));
+    ChunkIn<S, bf16> cur;   // u plays the key, the hi part of g the value
+    const float inv = __int_as_float(in.ih[0]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      cur.k[0][kk] = in.x[kk];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cur.v[0][kk].x[i] = (bf16)(in.gy[kk][i] * inv);
     }
+    stage_chunk<S, bf16, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf, nullptr, wave, lane);
+    if (g == 0) hs[wave * 16 + n] = __int_as_float(in.ih[1]);
+    if (c + 1 < nch) load_in(in, t0 + S::C);
     __syncthreads();
     state_update<S>(st, Wacc, Wz, vf, nullptr, wave, false, lane);
     if (wave == 0) {   // Z += U^T diag(h) U, hi/lo operands
@@ -611,19 +631,22 @@ kata_bwd_rstate(const bf16* __restrict__ q, const bf16* __restrict__ ghi, const 
 // ---- kata_bwd_key --------------------------------------------------------------------
 // grid (n_leaf, B*H), block 512 (8 waves).  ws holds each leaf's exclusive SUFFIX of the
 // backward state [R | Zr] (kata_bwd_rstate + reverse kata_state_scan).  Waves 0..3
-// (role 0) compute dv of the 16-token key block mb = wave; waves 4..7 (role 1) compute
-// dw -> dk and the dP share of key block mb = wave - 4.  The state is owned by diagonal:
-// wave w holds delta = w for all column blocks, waves 4..7 also delta = 8 for column
-// block w - 4, wave 0 the z-matrix.  Chunks are walked from the leaf's last to its first.
+// (role 0) compute dv of the 16-token key block mb = wave, waves 4..7 (role 1) dw of key
+// block mb = 7 - wave.  dk = P^T dw and the dP share dw k^T are formed by role 0 one
+// chunk later, from dw handed over in LDS (two buffers), which balances the two roles
+// without another barrier.  The state is owned by diagonal: wave w holds delta = w for
+// all column blocks, waves 4..7 also delta = 8 for column block w - 4, wave 0 the
+// z-matrix.  Chunks are walked from the leaf's last to its first.
 struct KbState {
   f32x4 s[4];
   f32x4 s8;
   f32x4 Z;
 };
 
+template <typename TY>
 __global__ void __launch_bounds__(512, 2)
 kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-             const bf16* __restrict__ ghi, const bf16* __restrict__ glo, const float* __restrict__ hb,
+             const TY* __restrict__ gy, const float* __restrict__ ih,
              const float* __restrict__ P, const float* __restrict__ ws, bf16* __restrict__ dk,
              bf16* __restrict__ dv, float* __restrict__ dpart, int64_t T, int H, int leaf_chunks,
              int64_t n_chunks) {
@@ -641,9 +664,12 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
   float* hs = reinterpret_cast<float*>(smem + KB_OFF_HS);
   bf16* Pf = reinterpret_cast<bf16*>(smem + KB_OFF_PF);
   bf16* PTs = reinterpret_cast<bf16*>(smem + KB_OFF_PT);
+  float* dWs = reinterpret_cast<float*>(smem + KB_OFF_DW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int role = wave >> 2, mb = wave & 3;
+  // key block of the wave: role 0 takes block w, role 1 block 3 - (w - 4), so that each
+  // SIMD (waves w and w + 4) pairs a block with many later query tiles with one with few
+  const int role = wave >> 2, mb = role == 0 ? wave : 3 - (wave & 3);
   const int n = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
@@ -682,64 +708,98 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
   };
   publish();
 
-  // role 0 loads q (-> u) and the hi plane of g (-> G^T fragments, G rows) and h;
-  // role 1 loads k (-> w), v and the lo plane of g.
+  // role 0 loads k (-> w; kept for dk and dP), role 1 q (-> u); both load v, gy and the
+  // (1/den, h) pairs and form g = gy (1/den) as kata_bwd_query did: role 0 stages its hi
+  // part (G^T fragments, G rows) and h, role 1 the lo part (G rows).
   const int64_t tb = T * 64 * 2;
-  const __amdgpu_buffer_rsrc_t r_x = make_rsrc((role == 0 ? q : k) + base_tok * 64, tb);
-  const __amdgpu_buffer_rsrc_t r_g = make_rsrc((role == 0 ? ghi : glo) + base_tok * 64, tb);
+  const __amdgpu_buffer_rsrc_t r_x = make_rsrc((role == 0 ? k : q) + base_tok * 64, tb);
+  const __amdgpu_buffer_rsrc_t r_g = make_rsrc(gy + base_tok * 64, T * 64 * (int64_t)sizeof(TY));
   const __amdgpu_buffer_rsrc_t r_v = make_rsrc(v + base_tok * 64, tb);
-  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(hb + base_tok, T * 4);
-  const __amdgpu_buffer_rsrc_t r_out = make_rsrc((role == 0 ? dv : dk) + base_tok * 64, tb);
+  const __amdgpu_buffer_rsrc_t r_ih = make_rsrc(ih + base_tok * 2, T * 8);
+  const __amdgpu_buffer_rsrc_t r_dv = make_rsrc(dv + base_tok * 64, tb);
+  const __amdgpu_buffer_rsrc_t r_dk = make_rsrc(dk + base_tok * 64, tb);
   struct In {
-    Vec8<bf16> x[2];   // q or k rows, projection column order
-    Vec8<bf16> gg[2];  // g hi or lo rows, natural column order
-    Vec8<bf16> vv[2];  // v rows (role 1), natural column order
-    float hv;          // h of token n (role 0)
+    Vec8<bf16> x[2];   // k or q rows, projection column order
+    Vec8<TY> gg[2];    // gy rows, natural column order
+    Vec8<bf16> vv[2];  // v rows, natural column order
+    i32x2 ih;          // (1/den, h) of token n
   };
   auto load_in = [&](In& r, int t0) {
     const int t = t0 + mb * 16 + n;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       r.x[kk].load(r_x, (t * 64 + 16 * g + 8 * kk) * 2);
-      r.gg[kk].load(r_g, (t * 64 + 32 * kk + 8 * g) * 2);
-      if (role == 1) r.vv[kk].load(r_v, (t * 64 + 32 * kk + 8 * g) * 2);
+      r.gg[kk].load(r_g, (t * 64 + 32 * kk + 8 * g) * (int)sizeof(TY));
+        r.vv[kk].load(r_v, (t * 64 + 32 * kk + 8 * g) * 2);
     }
-    if (role == 0) r.hv = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_h, t * 4, 0, 0));
+    r.ih = __builtin_amdgcn_raw_buffer_load_b64(r_ih, t * 8, 0, 0);
   };
+  DPAcc dpa;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dpa.t[db] = zero4();
+  // role 0: dk = P^T dw and dP += dw k^T for the key block of an earlier chunk; dw is
+  // role 1's part (LDS) plus the part of the state contraction role 0 took itself
+  auto key_grad = [&](int tprev, int buf, const bf16x8 (&krows)[2], const f32x4& own) {
+    const int s_loc = mb * 16 + n;
+    f32x4 dwv = *reinterpret_cast<const f32x4*>(dWs + (buf * S::C + s_loc) * P_DIM + 4 * g);
+    dwv += own;
+    grad_head(dwv, PTs, krows, r_dk, ((tprev + s_loc) * 64) * 2, dpa, lane);
+  };
+  // split of the dw state contraction over the diagonals: role 1 takes delta < KB_DSPLIT
+  constexpr int KB_DSPLIT = 6;
   const int tc0 = (int)(c0 * S::C);
   auto chunk_t0 = [&](int c) { return tc0 + (nch - 1 - c) * S::C; };   // last chunk first
   In cur;
   load_in(cur, chunk_t0(0));
-  DPAcc dpa;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) dpa.t[db] = zero4();
+  bf16x8 kprev[2];   // role 0: k rows of the previous chunk
+  f32x4 dwprev = zero4();   // role 0: its share of the previous chunk's dw
   __syncthreads();   // P and P^T fragments, hx zeros, first publish
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = chunk_t0(c);
     progress_priority(c, nch);
+    // lane-derived constants rebuilt per chunk (not hoisted and spilled), as in the query walk
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
+    const int n = lane & 15, g = lane >> 4;
     // ---- stage ----
     ProjP<S> pp;
     read_P<S>(pp, Pf, lane);
     const f32x4 x = project_tile<S, bf16>(cur.x, pp);      // lane (a, g): x-projection of token 4g + r
-    bf16x8 xr[2] = {cur.x[0].x, cur.x[1].x};
+    const bf16x8 kcur[2] = {cur.x[0].x, cur.x[1].x};
     Vec8<bf16> vcur[2] = {cur.vv[0], cur.vv[1]};
+    Op8<true> gsp[2];   // g = gy (1/den) of this lane's token and columns, hi/lo
+    {
+      const float inv = __int_as_float(cur.ih[0]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float gv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = cur.gg[kk][i] * inv;
+        gsp[kk] = make8<true>(gv);
+      }
+    }
+    const float hcur = __int_as_float(cur.ih[1]);
     if (role == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ws[(mb * 16 + 4 * g + r) * S::USTR + n] = x[r];
+      Vec8<bf16> gh[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        gh[kk].x = gsp[kk].hi;
+        *reinterpret_cast<bf16x8*>(grh + (mb * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = gsp[kk].hi;
+      }
+      const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
+      stage_v<S, bf16>(gh, mb, sel, gf, nullptr, lane);
+      if (g == 0) hs[mb * 16 + n] = hcur;
+    } else {
       *reinterpret_cast<f32x4*>(Uacc + (mb * WAVE + lane) * 4) = x;
 #pragma unroll
       for (int r = 0; r < 4; ++r) Us[(mb * 16 + 4 * g + r) * S::USTR + n] = x[r];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        *reinterpret_cast<bf16x8*>(grh + (mb * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = cur.gg[kk].x;
-      const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
-      stage_v<S, bf16>(cur.gg, mb, sel, gf, nullptr, lane);
-      if (g == 0) hs[mb * 16 + n] = cur.hv;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ws[(mb * 16 + 4 * g + r) * S::USTR + n] = x[r];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        *reinterpret_cast<bf16x8*>(grl + (mb * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = cur.gg[kk].x;
+        *reinterpret_cast<bf16x8*>(grl + (mb * 16 + n) * BW_GSTR + 32 * kk + 8 * g) = gsp[kk].lo;
     }
     if (c + 1 < nch) load_in(cur, chunk_t0(c + 1));
     __syncthreads();
@@ -827,7 +887,14 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
       }
       const int row = ((t0 + s_loc) * 64 + 4 * g) * 2;
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) Store4<bf16>::st(r_out, row + nb * 32, O[nb]);
+      for (int nb = 0; nb < S::NB; ++nb) Store4<bf16>::st(r_dv, row + nb * 32, O[nb]);
+      if (c > 0) key_grad(chunk_t0(c - 1), (c - 1) & 1, kprev, dwprev);
+      kprev[0] = kcur[0];
+      kprev[1] = kcur[1];
+      // this chunk's share of the dw state contraction (diagonals KB_DSPLIT..8)
+      dwprev = zero4();
+      const bf16x8 vx[2] = {vcur[0].x, vcur[1].x};
+      ht_contract<false, KB_DSPLIT, NDELTA>(dwprev, nullptr, HT, vx, Q, lane);
     } else {
       // dw_s = sum_{t >= s} B_ts u_t + 2 (mat(R v_s) + Zr) w_s; dk = P^T dw; dP += dw k^T
       f32x4 Bm[4];
@@ -874,8 +941,8 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
 #pragma unroll
       for (int r = 0; r < 4; ++r) dw[r] += 2.f * zw[r];
       const bf16x8 vx[2] = {vcur[0].x, vcur[1].x};
-      ht_contract<false>(dw, nullptr, HT, vx, Q, lane);
-      grad_head(dw, PTs, xr, r_out, ((t0 + s_loc) * 64) * 2, dpa, lane);
+      ht_contract<false, 0, KB_DSPLIT>(dw, nullptr, HT, vx, Q, lane);
+      *reinterpret_cast<f32x4*>(dWs + ((c & 1) * S::C + s_loc) * P_DIM + 4 * g) = dw;
     }
 
     // ---- state update: R += phi(U_c)^T G_c, Zr += U_c^T diag(h_c) U_c ----
@@ -920,8 +987,10 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
     __syncthreads();
     if (more) publish();
   }
+  // the last chunk's dk (its dw was written before the loop's final barrier)
+  if (role == 0) key_grad(chunk_t0(nch - 1), (nch - 1) & 1, kprev, dwprev);
   float* red = reinterpret_cast<float*>(smem + KB_OFF_HX);   // hx is no longer read
-  write_dp_partial(dpa, role == 1, mb, red, dpart + (bh * (int64_t)gridDim.x + leaf) * BW_DP, tid, lane);
+  write_dp_partial(dpa, role == 0, mb, red, dpart + (bh * (int64_t)gridDim.x + leaf) * BW_DP, tid, lane);
 }
 
 // ---- kata_bwd_dp_reduce --------------------------------------------------------------

@@ -174,10 +174,10 @@ def test_backward_workspace_and_validation():
     d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
     assert lib.kata_backward_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
     # 2048 chunks per head, 512 concurrent workgroups -> leaves of 64 chunks, 32 per head:
-    # forward and backward leaf states, g (hi, lo bf16), h (f32), two dP partial sets
+    # forward and backward leaf states, (1/den, h) per token (f32 pairs), two dP partial sets
     st = 16 * 32 * (144 * 64 + 256) * 4
     tok = 16 * 131072
-    assert n.value == 2 * st + 2 * tok * 128 + tok * 4 + 2 * 16 * 32 * 1024 * 4
+    assert n.value == 2 * st + tok * 8 + 2 * 16 * 32 * 1024 * 4
     fake = ctypes.c_void_p(0x1000)
     args15 = [fake] * 15
     for field, value, status in [("d", 16, Bd.KATA_ERR_UNSUPPORTED), ("chunk", 128, Bd.KATA_ERR_UNSUPPORTED),

@@ -60,6 +60,9 @@ __all__ = [
     "recurrence",
     "decode_reference",
     "backward_quadratic",
+    "forward_decay_quadratic",
+    "final_state_decay",
+    "decode_decay_reference",
 ]
 
 
@@ -329,3 +332,82 @@ def backward_quadratic(q, k, v, P, gy, S0=None, z0=None, gST=None, gzT=None):
             dS0[b, h] = gs + fu.T @ gnum
             dz0[b, h] = gz + fu.T @ gden
     return dq, dk, dvv, dP, dS0, dz0
+
+
+# ---- decay-gated KATA ------------------------------------------------------------------
+#
+# PARITY NOTE (reading): the abstract names "decay gates" among the mechanisms studied
+# with KATA's features but defines none.  The plainest reading, the scalar forget gate of
+# gated linear attention, applied to KATA's state [S | z]:
+#
+#     S_t = gamma_t S_{t-1} + phi(k_t) v_t^T,   z_t = gamma_t z_{t-1} + phi(k_t),
+#     y_t = S_t^T phi(q_t) / (z_t . phi(q_t)),   gamma_t = exp(lam_t), lam_t <= 0,
+#
+# one gate per token and head, the current token undecayed.  Unrolled, the weight of key
+# s in query t is a_ts = (u_t . w_s)^2 exp(Lam_t - Lam_s) with Lam_t = sum_{r<=t} lam_r;
+# an initial state enters with exp(Lam_t).  Numerator and denominator decay alike, so
+# y_t stays a convex combination (the output gate of [TS-2.1]).
+
+
+def forward_decay_quadratic(q, k, v, P, lam, S0=None, z0=None):
+    """Decay-gated causal KATA by its O(T^2) definition (see the reading above).
+
+    q, k: [B, H, T, d]; v: [B, H, T, dv]; P: [H, p, d]; lam: [B, H, T] log-gates (<= 0);
+    S0 [B, H, p*p, dv], z0 [B, H, p*p] or None.  Returns y [B, H, T, dv] float64.
+    """
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    lam = np.asarray(lam, dtype=np.float64)
+    B, H, T, _ = q.shape
+    dv = v.shape[-1]
+    pp = P.shape[1] * P.shape[1]
+    y = np.zeros((B, H, T, dv))
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            u = project(q[b, h], P[h])
+            w = project(k[b, h], P[h])
+            Lam = np.cumsum(lam[b, h])
+            decay = np.where(causal, np.exp(np.where(causal, Lam[:, None] - Lam[None, :], 0.0)), 0.0)
+            a = (u @ w.T) ** 2 * decay
+            num = a @ v[b, h]
+            den = a.sum(axis=1)
+            if S0 is not None:
+                f = feature_full(u) * np.exp(Lam)[:, None]
+                num = num + f @ np.asarray(S0[b, h], dtype=np.float64)
+                den = den + f @ np.asarray(z0[b, h], dtype=np.float64)
+            ok = den != 0.0
+            y[b, h][ok] = num[ok] / den[ok, None]
+    return y
+
+
+def final_state_decay(k, v, P, lam, S0=None, z0=None):
+    """Final state of the decay-gated recurrence:
+    S_T = exp(Lam_T) S0 + sum_s exp(Lam_T - Lam_s) phi(k_s) v_s^T, likewise z_T."""
+    k = np.asarray(k, dtype=np.float64); v = np.asarray(v, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64); lam = np.asarray(lam, dtype=np.float64)
+    B, H, T, _ = k.shape
+    pp = P.shape[1] * P.shape[1]
+    ST = np.zeros((B, H, pp, v.shape[-1]))
+    zT = np.zeros((B, H, pp))
+    for b in range(B):
+        for h in range(H):
+            Lam = np.cumsum(lam[b, h])
+            tot = Lam[-1] if T > 0 else 0.0
+            wgt = np.exp(tot - Lam)                       # [T]
+            f = feature_full(project(k[b, h], P[h]))      # [T, pp]
+            ST[b, h] = (f * wgt[:, None]).T @ v[b, h]
+            zT[b, h] = (f * wgt[:, None]).sum(axis=0)
+            if S0 is not None:
+                ST[b, h] += np.exp(tot) * np.asarray(S0[b, h], dtype=np.float64)
+                zT[b, h] += np.exp(tot) * np.asarray(z0[b, h], dtype=np.float64)
+    return ST, zT
+
+
+def decode_decay_reference(S, z, q, k, v, P, lam):
+    """One decay-gated recurrent decode step for N streams: S' = gamma S + phi(k) v^T,
+    z' = gamma z + phi(k), gamma = exp(lam) [N, H]; y = S'^T phi(q) / (z' . phi(q))."""
+    g = np.exp(np.asarray(lam, dtype=np.float64))
+    S = np.array(S, dtype=np.float64) * g[:, :, None, None]
+    z = np.array(z, dtype=np.float64) * g[:, :, None]
+    return decode_reference(S, z, q, k, v, P)

@@ -212,6 +212,45 @@ kata_status kata_backward_timed(const kata_forward_desc* desc,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);
 
+/* Decay-gated causal forward.  The paper's abstract names "decay gates" among the
+ * mechanisms studied with KATA's features without defining them; the reading taken is
+ * the scalar forget gate of gated linear attention applied to KATA's state [S | z]:
+ *   S_t = gamma_t S_{t-1} + phi(k_t) v_t^T,  z_t = gamma_t z_{t-1} + phi(k_t),
+ *   y_t = S_t^T phi(q_t) / (z_t . phi(q_t)),  gamma_t = exp(lam_t)
+ * with one log-gate lam_t <= 0 per token and head (the current token is not decayed; an
+ * initial state S0, z0 decays like the rest).  Numerator and denominator decay alike, so
+ * the output gate stays convex.  Chunked form ([TS-2.3]): keys weighted by their decay
+ * to the end of the chunk, the inter-chunk prefix by the affine recurrence
+ * H <- exp(L_c) H + chunk state (an associative scan with combine (D_a, S_a) o (D_b, S_b)
+ * = (D_a D_b, D_b S_a + S_b)), and inside the chunk weights (u_t.w_s)^2 exp(l_t - l_s).
+ *   lam [B,H,T] float32 (device); other arguments as for kata_forward.
+ * Supported: p = 16, d = dv = 64, chunk = 64, in_dtype BF16, out_dtype F32 or BF16.
+ * The workspace (kata_forward_decay_workspace_bytes) is kata_forward's plus one float per
+ * leaf.  kata_forward_decay_timed stamps the same four events as kata_forward_timed. */
+kata_status kata_forward_decay_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+kata_status kata_forward_decay(const kata_forward_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const float* P, const float* lam,
+                               const float* S0, const float* z0,
+                               void* y, float* ST, float* zT,
+                               void* workspace, size_t workspace_bytes, void* stream);
+kata_status kata_forward_decay_timed(const kata_forward_desc* desc,
+                                     const void* q, const void* k, const void* v,
+                                     const float* P, const float* lam,
+                                     const float* S0, const float* z0,
+                                     void* y, float* ST, float* zT,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events);
+
+/* One decay-gated recurrent decode step (same reading): S <- gamma S + phi(k) v^T,
+ * z <- gamma z + phi(k), y = S^T phi(q) / (z . phi(q)), gamma = exp(lam), lam [N,H]
+ * float32 (device).  Other arguments and support as for kata_decode_step. */
+kata_status kata_decode_step_decay(int64_t N, int64_t H, int d, int dv, int p,
+                                   kata_dtype in_dtype, kata_dtype out_dtype,
+                                   float* S, float* z,
+                                   const void* q, const void* k, const void* v,
+                                   const float* P, const float* lam, void* y, void* stream);
+
 /* One recurrent decode step for N independent streams ([TS-1], [ABS]):
  *   S += phi(k) v^T, z += phi(k)   (in place, canonical layout)
  *   y  = S^T phi(q) / (z . phi(q)) (after the update; 0 if the denominator is 0)

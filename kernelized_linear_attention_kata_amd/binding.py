@@ -91,6 +91,14 @@ def load_library() -> ctypes.CDLL:
     lib.kata_backward_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 16 + [sz, vp, ctypes.POINTER(vp)]
     lib.kata_backward.restype = ci
     lib.kata_backward.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 16 + [sz, vp]
+    lib.kata_forward_decay_workspace_bytes.restype = ci
+    lib.kata_forward_decay_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_forward_decay_timed.restype = ci
+    lib.kata_forward_decay_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp, ctypes.POINTER(vp)]
+    lib.kata_forward_decay.restype = ci
+    lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
+    lib.kata_decode_step_decay.restype = ci
+    lib.kata_decode_step_decay.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_decode_step.restype = ci
     lib.kata_decode_step.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_feature_map.restype = ci
@@ -223,6 +231,99 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_forward")
     return (y, ST, zT) if return_state else y
+
+
+def forward_decay_workspace_bytes(B, H, T, d=64, dv=64, chunk=64, in_dtype=torch.bfloat16, out_dtype=None,
+                                  scan="assoc", scan_leaf=0) -> int:
+    """Workspace bytes of kata_forward_decay for these sizes."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_forward_decay_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "kata_forward_decay_workspace_bytes")
+    return int(n.value)
+
+
+def forward_decay(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, lam: torch.Tensor,
+                  chunk: int = 64, *, S0: Optional[torch.Tensor] = None, z0: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, return_state: bool = False, scan: str = "assoc",
+                  scan_leaf: int = 0, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None, events=None):
+    """Decay-gated causal forward (kata_forward_decay): S_t = exp(lam_t) S_{t-1} + phi(k_t) v_t^T
+    and z_t likewise.  q, k, v: [B,H,T,64] bf16; P: [H,16,64] fp32; lam: [B,H,T] fp32 (<= 0).
+    Returns y, or (y, ST, zT) when return_state.  events: optional four torch.cuda.Event."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(lam, "lam", (B, H, T), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if (S0 is None) != (z0 is None):
+        raise ValueError("S0 and z0 go together")
+    if S0 is not None:
+        _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        _need(z0, "z0", (B, H, P_DIM * P_DIM), torch.float32, dev)
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(q.dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    _check(lib.kata_forward_decay_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "kata_forward_decay_workspace_bytes")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    ST = zT = None
+    if return_state:
+        ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
+        zT = torch.empty((B, H, P_DIM * P_DIM), dtype=torch.float32, device=dev)
+    sh = _stream_handle(stream, dev)
+    evarr = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_forward_decay_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(lam), _ptr(S0),
+                                      _ptr(z0), _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
+    _check(st, "kata_forward_decay")
+    return (y, ST, zT) if return_state else y
+
+
+def decode_step_decay(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      P: torch.Tensor, lam: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decay-gated recurrent step (kata_decode_step_decay): S <- exp(lam) S + phi(k) v^T,
+    z likewise, in place; lam [N,H] fp32.  Returns y [N,H,dv]."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(S, "S", (N, H, P_DIM * P_DIM, dv), torch.float32, dev)
+    _need(z, "z", (N, H, P_DIM * P_DIM), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(lam, "lam", (N, H), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_decay(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype), _ptr(S),
+                                       _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(lam), _ptr(y),
+                                       _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_decay")
+    return y
 
 
 def flash_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None) -> int:

@@ -150,30 +150,34 @@ dim3 scan_grid(const Plan& pl, int G, int64_t bh) {
   return dim3((unsigned)((quads + 256 / G - 1) / (256 / G)), (unsigned)bh);
 }
 
-template <class S, typename TIn, typename TOut>
+// DECAY: lam [B,H,T] log-decays; dec (B*H*n_leaf floats) receives the leaf decays.
+template <class S, typename TIn, typename TOut, bool DECAY = false>
 kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
                         const void* v, const float* P, const float* S0, const float* z0, void* y,
-                        float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
+                        float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev,
+                        const float* lam = nullptr, float* dec = nullptr) {
   const int64_t bh = d->B * d->H;
-  if (allow_smem(kata_chunk_state<S, TIn>, S::SMEM_STATE) != KATA_OK ||
-      allow_smem(kata_chunk_intra<S, TIn, TOut>, S::SMEM) != KATA_OK)
+  constexpr int smem_state = S::SMEM_STATE + (DECAY ? S::DEC_BYTES : 0);
+  constexpr int smem_intra = S::SMEM + (DECAY ? S::DEC_BYTES : 0);
+  if (allow_smem(kata_chunk_state<S, TIn, DECAY>, smem_state) != KATA_OK ||
+      allow_smem(kata_chunk_intra<S, TIn, TOut, DECAY>, smem_intra) != KATA_OK)
     return KATA_ERR_LAUNCH;
   const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
   // With events, the launches themselves stamp them (hipExtLaunchKernel: start of
   // each kernel, end of the last), so timing adds no commands to the stream.
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn>), grid, dim3(256), S::SMEM_STATE, st, e0, nullptr, 0,
-                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, DECAY>), grid, dim3(256), smem_state, st, e0, nullptr, 0,
+                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks, lam, dec);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int G = scan_segments(pl);
   const dim3 sgrid = scan_grid(pl, G, bh);
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
-                        (int)S::DV, G, S0, z0, ST, zT, 0, 0);
+                        (int)S::DV, G, S0, z0, ST, zT, 0, 0, (const float*)dec);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut>), grid, dim3(256), S::SMEM, st, e2, e3, 0,
+  hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut, DECAY>), grid, dim3(256), smem_intra, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
-                        (int)d->H, (int)pl.leaf, pl.n_chunks);
+                        (int)d->H, (int)pl.leaf, pl.n_chunks, lam);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   return KATA_OK;
 }
@@ -276,7 +280,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   using S = BS;
   const Plan& pl = L.pl;
   const int64_t bh = d->B * d->H;
-  if (allow_smem(kata_chunk_state<S, bf16>, S::SMEM_STATE) != KATA_OK ||
+  if (allow_smem(kata_chunk_state<S, bf16, false>, S::SMEM_STATE) != KATA_OK ||
       allow_smem(kata_bwd_query<TY>, QaGy<TY>::SMEM) != KATA_OK ||
       allow_smem(kata_bwd_rstate<TY>, RS_SMEM) != KATA_OK || allow_smem(kata_bwd_key<TY>, KB_SMEM) != KATA_OK)
     return KATA_ERR_LAUNCH;
@@ -294,11 +298,12 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   const bf16* kb = (const bf16*)k;
   const bf16* vb = (const bf16*)v;
   // forward prefix states at every leaf start
-  hipExtLaunchKernelGGL((kata_chunk_state<S, bf16>), grid, dim3(256), S::SMEM_STATE, st, e[0], nullptr, 0, kb, vb,
-                        P, wsf, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  hipExtLaunchKernelGGL((kata_chunk_state<S, bf16, false>), grid, dim3(256), S::SMEM_STATE, st, e[0], nullptr, 0, kb,
+                        vb, P, wsf, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks, (const float*)nullptr,
+                        (float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[1], nullptr, 0, wsf, pl.n_leaf, (int)pl.E, 64, G,
-                        S0, z0, (float*)nullptr, (float*)nullptr, 0, 0);
+                        S0, z0, (float*)nullptr, (float*)nullptr, 0, 0, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QaGy<TY>::SMEM, st, e[2], nullptr, 0, qb, kb, vb,
                         (const TY*)gy, P, (const float*)wsf, ih, (bf16*)dq, dpa, d->T,
@@ -308,7 +313,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
                         (const float*)ih, P, wsr, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[4], nullptr, 0, wsr, pl.n_leaf, (int)pl.E, 64, G,
-                        gST, gzT, dS0, dz0, 1, 1);
+                        gST, gzT, dS0, dz0, 1, 1, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_bwd_key<TY>), grid, dim3(512), KB_SMEM, st, e[5], nullptr, 0, qb, kb, vb, (const TY*)gy,
                         (const float*)ih, P, (const float*)wsr, (bf16*)dk, (bf16*)dv, dpb, d->T,
@@ -317,6 +322,20 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   hipExtLaunchKernelGGL(kata_bwd_dp_reduce, dim3((unsigned)d->H, 4), dim3(256), 0, st, e[6], e[7], 0,
                         (const float*)dpa, (const float*)dpb, dP, d->B, (int)d->H, pl.n_leaf);
   return launch_status();
+}
+
+// ---- decay-gated forward -----------------------------------------------------------
+// Supported: p = 16, d = dv = 64, chunk 64, bf16 q/k/v, f32 or bf16 y (the plain forward's
+// fast instance).  Workspace: the plain forward's, then one float per leaf (its decay).
+kata_status validate_decay(const kata_forward_desc* d) {
+  const kata_status s = validate(d);
+  if (s != KATA_OK) return s;
+  if (d->d != 64 || d->dv != 64 || d->chunk != 64 || d->in_dtype != KATA_BF16) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+size_t decay_ws_bytes(const Plan& pl, const kata_forward_desc* d) {
+  return align256(pl.ws_bytes) + (size_t)(d->B * d->H) * (size_t)pl.n_leaf * sizeof(float);
 }
 
 }  // namespace
@@ -486,6 +505,84 @@ kata_status kata_backward(const kata_forward_desc* desc, const void* q, const vo
                              workspace_bytes, stream, nullptr);
 }
 
+kata_status kata_forward_decay_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {
+  if (!bytes) return KATA_ERR_NULL;
+  const kata_status s = validate_decay(desc);
+  if (s != KATA_OK) return s;
+  *bytes = decay_ws_bytes(make_plan(desc), desc);
+  return KATA_OK;
+}
+
+kata_status kata_forward_decay_timed(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                                     const float* P, const float* lam, const float* S0, const float* z0, void* y,
+                                     float* ST, float* zT, void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events) {
+  const kata_status s = validate_decay(desc);
+  if (s != KATA_OK) return s;
+  if ((S0 == nullptr) != (z0 == nullptr)) return KATA_ERR_NULL;
+  if ((ST == nullptr) != (zT == nullptr)) return KATA_ERR_NULL;
+  const Plan pl = make_plan(desc);
+  const int64_t bh = desc->B * desc->H;
+  hipStream_t st = (hipStream_t)stream;
+  if (bh == 0) return KATA_OK;
+  if (desc->T == 0) return copy_initial_state(desc, S0, z0, ST, zT, st);
+  if (!q || !k || !v || !P || !lam || !y) return KATA_ERR_NULL;
+  if (!workspace || workspace_bytes < decay_ws_bytes(pl, desc)) return KATA_ERR_WORKSPACE;
+  if (pl.n_leaf > 0x7fffffff) return KATA_ERR_SHAPE;
+  hipEvent_t ev[4];
+  hipEvent_t* evp = nullptr;
+  if (events) {
+    for (int i = 0; i < 4; ++i) {
+      if (!events[i]) return KATA_ERR_NULL;
+      ev[i] = (hipEvent_t)events[i];
+    }
+    evp = ev;
+  }
+  float* ws = (float*)workspace;
+  float* dec = (float*)((unsigned char*)workspace + align256(pl.ws_bytes));
+  using S = Shape<64, 64, 64, false>;
+  if (desc->out_dtype == KATA_F32)
+    return run_forward<S, bf16, float, true>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp, lam, dec);
+  return run_forward<S, bf16, bf16, true>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp, lam, dec);
+}
+
+kata_status kata_forward_decay(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                               const float* P, const float* lam, const float* S0, const float* z0, void* y,
+                               float* ST, float* zT, void* workspace, size_t workspace_bytes, void* stream) {
+  return kata_forward_decay_timed(desc, q, k, v, P, lam, S0, z0, y, ST, zT, workspace, workspace_bytes, stream,
+                                  nullptr);
+}
+
+kata_status kata_decode_step_decay(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                                   kata_dtype out_dtype, float* S, float* z, const void* q, const void* k,
+                                   const void* v, const float* P, const float* lam, void* y, void* stream) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N * H == 0) return KATA_OK;
+  if (N * H > 0x7fffffff) return KATA_ERR_SHAPE;
+  if (!S || !z || !q || !k || !v || !P || !lam || !y) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)(N * H));
+#define KATA_DECODE_D(TI, TO, DVV)                                                                         \
+  hipLaunchKernelGGL((kata::kata_decode_step<TI, TO, DVV, true>), grid, dim3(256), 0, st, S, z, (const TI*)q, \
+                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d, lam)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DECODE_D(float, float, 64);
+    else if (fi) KATA_DECODE_D(float, bf16, 64);
+    else if (fo) KATA_DECODE_D(bf16, float, 64);
+    else KATA_DECODE_D(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DECODE_D(float, float, 16);
+    else if (fi) KATA_DECODE_D(float, bf16, 16);
+    else if (fo) KATA_DECODE_D(bf16, float, 16);
+    else KATA_DECODE_D(bf16, bf16, 16);
+  }
+#undef KATA_DECODE_D
+  return launch_status();
+}
+
 kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
                              kata_dtype out_dtype, float* S, float* z, const void* q, const void* k,
                              const void* v, const float* P, void* y, void* stream) {
@@ -498,8 +595,8 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dt
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)(N * H));
 #define KATA_DECODE(TI, TO, DVV)                                                                     \
-  hipLaunchKernelGGL((kata::kata_decode_step<TI, TO, DVV>), grid, dim3(256), 0, st, S, z, (const TI*)q, \
-                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d)
+  hipLaunchKernelGGL((kata::kata_decode_step<TI, TO, DVV, false>), grid, dim3(256), 0, st, S, z, (const TI*)q, \
+                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d, (const float*)nullptr)
   const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
   if (dv == 64) {
     if (fi && fo) KATA_DECODE(float, float, 64);

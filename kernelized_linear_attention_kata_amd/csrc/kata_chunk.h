@@ -66,6 +66,9 @@ struct Shape {
   static constexpr int ST_OFF_WZ = ST_OFF_WACC + WACC_BYTES;
   static constexpr int ST_OFF_PF = ST_OFF_WZ + WZ_BYTES;
   static constexpr int SMEM_STATE = ST_OFF_PF + PF_BYTES;
+  // decay-gated instances append the chunk's cumulative log-decays and the key weights
+  // of the state update (two floats per token) after the layouts above
+  static constexpr int DEC_BYTES = 2 * C * 4;
   // waves per SIMD each kernel is compiled for (register budget 512 / OCC): the
   // largest that fits without spilling on gfx950
   static constexpr int OCC_INTRA = DV <= 16 ? (C == 128 ? 3 : 4) : ((SPLIT || C == 128) ? 2 : 3);
@@ -77,7 +80,7 @@ struct Shape {
   static_assert(DV % 16 == 0 && DV <= 128, "dv");
   static_assert(DIN == 16 || DIN % 32 == 0, "d");
   // three workgroups of the bf16 C = 64, dv = 64 instance share a CU (156 KiB of LDS)
-  static_assert(!(C == 64 && DV == 64 && !SPLIT) || 3 * SMEM <= 156 * 1024, "LDS budget");
+  static_assert(!(C == 64 && DV == 64 && !SPLIT) || 3 * (SMEM + DEC_BYTES) <= 156 * 1024, "LDS budget");
 };
 
 // Offsets of an accumulator tile (delta, nb) inside a leaf's workspace block:
@@ -396,6 +399,99 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc,
   }
 }
 
+// ---- decay gates ------------------------------------------------------------------
+// Decay-gated state (the abstract's "decay gates", read as a scalar forget gate per token
+// and head): S_t = gamma_t S_{t-1} + phi(k_t) [v_t | 1]^T with gamma_t = exp(lam_t).  Inside
+// a chunk with cumulative log-decay l_t (from the chunk start) and total L_c:
+//   chunk state  = sum_s exp(L_c - l_s) phi(k_s) [v_s | 1]^T     (keys weighted)
+//   prefix       : H <- exp(L_c) H + chunk state                 (affine scan)
+//   readout of t : exp(l_t) phi(q_t)^T H,  tile weights (u_t . w_s)^2 exp(l_t - l_s).
+
+// Chunk-local inclusive prefix of the log-decays: lane l of the wave gets l_l, the sum
+// of lam over tokens t0 .. t0 + l (x = lam of token t0 + l, 0 past the sequence); Lc is
+// the chunk total.  Every wave computes it (one 256-byte load per chunk and wave).
+__device__ __forceinline__ float chunk_cumlog(float x, int lane, float& Lc) {
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const float y = __shfl_up(x, off, WAVE);
+    if (lane >= off) x += y;
+  }
+  Lc = __shfl(x, WAVE - 1, WAVE);
+  return x;
+}
+
+// The state update of a decay-gated chunk: as state_update, with the key features of
+// token s weighted by es[s] (the factor its contribution keeps at the end of the chunk,
+// or of the leaf) and the z-matrix updated by W^T diag(es) W.
+template <class S>
+__device__ __forceinline__ void state_update_decay(StateAcc<S>& st, const float* Wacc, const float* es,
+                                                   const bf16* vf_hi, const bf16* vf_lo, int wave, bool zrole,
+                                                   int lane) {
+  const int g = lane >> 4;
+  const int rot_lane = (lane & ~15) | ((lane + wave) & 15);
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) {
+    const f32x4 wa0 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj) * WAVE + lane) * 4);
+    const f32x4 wa1 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj + 1) * WAVE + lane) * 4);
+    const f32x4 wr0 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj) * WAVE + rot_lane) * 4);
+    const f32x4 wr1 = *reinterpret_cast<const f32x4*>(Wacc + ((2 * jj + 1) * WAVE + rot_lane) * 4);
+    const f32x4 e0 = *reinterpret_cast<const f32x4*>(es + 32 * jj + 4 * g);
+    const f32x4 e1 = *reinterpret_cast<const f32x4*>(es + 32 * jj + 16 + 4 * g);
+    // the weight goes on the plain operand: key feature (a, a + delta) of token s times es[s]
+    f32x4 we0, we1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      we0[i] = wa0[i] * e0[i];
+      we1[i] = wa1[i] * e1[i];
+    }
+    Op8<S::SPLIT> vfr[S::NB];
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
+    {
+      const Op8<S::SPLIT> kf = key_frag<S, 0>(we0, we1, wr0, wr1);     // delta = w
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
+    }
+    {
+      const Op8<S::SPLIT> kf = key_frag<S, 4>(we0, we1, wr0, wr1);     // delta = w + 4
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
+    }
+    if (wave < S::NB) {
+      const Op8<S::SPLIT> kf = key_frag<S, 8>(we0, we1, wa0, wa1);      // delta = 8
+#pragma unroll
+      for (int i = 0; i < StateAcc<S>::N8; ++i) {
+#pragma unroll
+        for (int nb = 0; nb < S::NB; ++nb)
+          if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
+      }
+    }
+    if (zrole) {
+      float ua[8], ue[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ua[r] = wa0[r];
+        ua[4 + r] = wa1[r];
+        ue[r] = we0[r];
+        ue[4 + r] = we1[r];
+      }
+      st.Z = mma<true, true>(make8<true>(ua), make8<true>(ue), st.Z);
+    }
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void state_scale(StateAcc<S>& st, float f) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] *= f;
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) st.s8[i] *= f;
+  st.Z *= f;
+}
+
 // Stage one chunk: project keys (token split) into W tiles in LDS (accumulator
 // layout, one 16-byte slot per lane), queries into U rows and keys into W rows when
 // WANT_Q, and transpose the wave's V rows into B-fragments.
@@ -432,17 +528,21 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const bf16
 }
 
 // ---- kata_chunk_state ----------------------------------------------------------
-// grid (n_leaf, B*H), block 256.  Writes the leaf's summed packed state to ws.
-template <class S, typename TIn>
+// grid (n_leaf, B*H), block 256.  Writes the leaf's summed packed state to ws.  DECAY:
+// lam [B*H, T] log-decays; each token's contribution is weighted by the decay from it to
+// the leaf's end, and the leaf's total decay exp(sum lam) goes to dec[bh * n_leaf + leaf].
+template <class S, typename TIn, bool DECAY = false>
 __global__ void __launch_bounds__(256, S::OCC_STATE)
 kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
-                 float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+                 float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks,
+                 const float* __restrict__ lam, float* __restrict__ dec) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
   bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
   float* Wacc = reinterpret_cast<float*>(smem + S::ST_OFF_WACC);
   bf16* Wz = reinterpret_cast<bf16*>(smem + S::ST_OFF_WZ);
   bf16* Pf = reinterpret_cast<bf16*>(smem + S::ST_OFF_PF);
+  float* es = reinterpret_cast<float*>(smem + S::SMEM_STATE);   // DECAY: key weights
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
@@ -451,6 +551,9 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   const int64_t c0 = leaf * leaf_chunks;
   const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
   const int64_t base_tok = bh * T;
+  __amdgpu_buffer_rsrc_t rl;
+  if constexpr (DECAY) rl = make_rsrc(lam + base_tok, T * 4);
+  float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the leaf's end
 
   if (wave == 0) write_P<S>(Pf, P, h, lane);
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
@@ -473,12 +576,23 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   ChunkIn<S, TIn> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, chunk_t0(i), wave, lane);
+  float lam_next = 0.f;
+  if constexpr (DECAY) lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (chunk_t0(0) + lane) * 4, 0, 0));
   __syncthreads();   // P fragments written
   auto step = [&](ChunkIn<S, TIn>& cur, int c) {
     stage_chunk<S, TIn, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf_hi, vf_lo, wave, lane);
     load_chunk<S, TIn, false>(cur, rs, c + DEPTH < nch ? chunk_t0(c + DEPTH) : (int)T, wave, lane);
+    if constexpr (DECAY) {
+      float Lc;
+      const float l = chunk_cumlog(lam_next, lane, Lc);
+      if (wave == 0) es[lane] = fdec * __expf(Lc - l);
+      fdec *= __expf(Lc);
+      lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rl, ((c + 1 < nch ? chunk_t0(c + 1) : (int)T) + lane) * 4, 0, 0));
+    }
     __syncthreads();
-    state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, wave == 0, lane);
+    if constexpr (DECAY) state_update_decay<S>(st, Wacc, es, vf_hi, vf_lo, wave, wave == 0, lane);
+    else state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, wave == 0, lane);
     __syncthreads();
   };
   int c = 0;
@@ -504,6 +618,9 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
     if (nb < S::NB) *reinterpret_cast<f32x4*>(out + ws_tile_offset<S>(8, nb, lane)) = st.s8[i];
   }
   if (wave == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + lane * 4) = st.Z;
+  if constexpr (DECAY) {
+    if (tid == 0) dec[bh * (int64_t)gridDim.x + leaf] = fdec;
+  }
 }
 
 // ---- kata_chunk_intra ------------------------------------------------------------
@@ -602,10 +719,11 @@ template <> struct Store4<bf16> {
 // feeding the same fragments to the MFMA in swapped operand order: lane (t, g) then
 // holds output columns 16nb + 4g .. 16nb + 4g + 3 of token t, so the denominator of
 // token t is lane-local and y leaves as 4-element vector stores.
-template <class S, typename TOut>
+template <class S, typename TOut, bool DECAY = false>
 __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const float* Ws, const bf16* vf_hi,
                                               const bf16* vf_lo, const bf16* hx_hi, const bf16* hx_lo,
-                                              const bf16* Zs, const SeqRsrc& rs, int t0, int lane) {
+                                              const bf16* Zs, const SeqRsrc& rs, int t0, int lane,
+                                              const float* ls = nullptr) {
   const int n = lane & 15, g = lane >> 4;
   const int t = mb * 16 + n;    // token (within chunk) whose fragment column this lane builds
 
@@ -673,6 +791,15 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
     const f32x4 zu = mma<true, true>(zf, make4<true>(uv), zero4());
     den = zu[0] * Q[0][0] + zu[1] * Q[0][1] + zu[2] * Q[0][2] + zu[3] * Q[0][3];
   }
+  // DECAY: the prefix state reaches token t decayed by exp(l_t)
+  float lt = 0.f;
+  if constexpr (DECAY) {
+    lt = ls[t];
+    const float f = __expf(lt);
+    den *= f;
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) O[nb] *= f;
+  }
 
   // intra-chunk: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds X[s = 4g + r][t]
   const f32x4 ub = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * g);
@@ -692,6 +819,11 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) A2[j][r] = (4 * g + r <= n) ? X[r] * X[r] : 0.f;
+      }
+      if constexpr (DECAY) {   // weight exp(l_t - l_s) of key s = 16j + 4g + r
+        const f32x4 lsv = *reinterpret_cast<const f32x4*>(ls + j * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] *= __expf(fminf(lt - lsv[r], 0.f));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) den += A2[j][r];
@@ -730,12 +862,13 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   }
 }
 
-// grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.
-template <class S, typename TIn, typename TOut>
+// grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.  DECAY:
+// lam [B*H, T] log-decays (see the decay-gate notes above).
+template <class S, typename TIn, typename TOut, bool DECAY = false>
 __global__ void __launch_bounds__(256, S::OCC_INTRA)
 kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                  const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
-                 int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+                 int64_t T, int H, int leaf_chunks, int64_t n_chunks, const float* __restrict__ lam) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
   bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
@@ -747,6 +880,8 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   bf16* Wz = reinterpret_cast<bf16*>(smem + S::OFF_WZ);
   bf16* Zs = reinterpret_cast<bf16*>(smem + S::OFF_Z);
   bf16* Pf = reinterpret_cast<bf16*>(smem + S::OFF_PF);
+  float* ls = reinterpret_cast<float*>(smem + S::SMEM);        // DECAY: cumulative log-decays
+  float* es = ls + S::C;                                         // DECAY: key weights exp(L_c - l_s)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.y;
@@ -755,6 +890,8 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   const int64_t c0 = leaf * leaf_chunks;
   const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
   const int64_t base_tok = bh * T;
+  __amdgpu_buffer_rsrc_t rl;
+  if constexpr (DECAY) rl = make_rsrc(lam + base_tok, T * 4);
 
   // the readout K-block 4 holds delta = 8 in slots 0..3; slots 4..7 stay zero
   for (int i = tid; i < S::NB * WAVE; i += 256) {
@@ -780,20 +917,38 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   const int tc0 = (int)(c0 * S::C);
   ChunkIn<S, TIn> cur;
   load_chunk<S, TIn, true>(cur, rs, tc0, tw, lane);
+  float lam_next = 0.f;
+  if constexpr (DECAY) lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (tc0 + lane) * 4, 0, 0));
   __syncthreads();   // P fragments written
   for (int c = 0; c < nch; ++c) {
     const int t0 = tc0 + c * S::C;
     progress_priority(c, nch);
     stage_chunk<S, TIn, true>(cur, Pf, sel, Us, Ws, Wacc, Wz, vf_hi, vf_lo, tw, lane);
     if (c + 1 < nch) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, tw, lane);
+    float Lc = 0.f;
+    if constexpr (DECAY) {
+      const float l = chunk_cumlog(lam_next, lane, Lc);
+      if (wave == 0) {
+        ls[lane] = l;
+        es[lane] = __expf(Lc - l);
+      }
+      lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (t0 + S::C + lane) * 4, 0, 0));
+    }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < S::MBW; ++m) {
       const int mb = tw + 4 * m;
-      if (mb < S::NMB) chunk_outputs<S, TOut>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, rs, t0, lane);
+      if (mb < S::NMB) chunk_outputs<S, TOut, DECAY>(mb, Us, Ws, vf_hi, vf_lo, hx_hi, hx_lo, Zs, rs, t0, lane, ls);
     }
     const bool more = c + 1 < nch;
-    if (more) state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, zrole, lane);
+    if constexpr (DECAY) {
+      if (more) {
+        state_scale<S>(st, __expf(Lc));
+        state_update_decay<S>(st, Wacc, es, vf_hi, vf_lo, wave, zrole, lane);
+      }
+    } else {
+      if (more) state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, zrole, lane);
+    }
     __syncthreads();
     if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
   }

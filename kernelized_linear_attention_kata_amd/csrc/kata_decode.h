@@ -30,12 +30,14 @@ __device__ __forceinline__ float project_row(const TIn* __restrict__ x, const fl
   return s;   // valid in every lane of the 16-lane group of row a
 }
 
-// grid N*H, block 256.  dv in {16, 64}: each thread owns one 4-column quad.
-template <typename TIn, typename TOut, int DV>
+// grid N*H, block 256.  dv in {16, 64}: each thread owns one 4-column quad.  DECAY: the
+// state is first multiplied by gamma = exp(lam[stream, head]) (decay-gated state:
+// S <- gamma S + phi(k) v^T, z <- gamma z + phi(k)).
+template <typename TIn, typename TOut, int DV, bool DECAY = false>
 __global__ void __launch_bounds__(256)
 kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __restrict__ q,
                  const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
-                 TOut* __restrict__ y, int H, int d) {
+                 TOut* __restrict__ y, int H, int d, const float* __restrict__ lam) {
   constexpr int D = P_DIM * P_DIM;
   constexpr int QPR = DV / 4;               // float4 quads per state row
   constexpr int ROWS_PER_IT = 256 / QPR;    // rows covered per pass of the block
@@ -48,6 +50,8 @@ kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __rest
   const int64_t nh = blockIdx.x;
   const int h = (int)(nh % H);
   const float* Ph = P + (int64_t)h * P_DIM * d;
+  float gam = 1.f;
+  if constexpr (DECAY) gam = __expf(lam[nh]);
 
   const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
   const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
@@ -72,15 +76,20 @@ kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __rest
     f32x4* p = reinterpret_cast<f32x4*>(Sh + row * DV + 4 * c4);
     f32x4 s = *p;
     const float fwr = fw[row], fur = fu[row];
+    if constexpr (DECAY) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] += fwr * vv[i];
+      for (int i = 0; i < 4; ++i) s[i] = gam * s[i] + fwr * vv[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] += fwr * vv[i];
+    }
     *p = s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += fur * s[i];
   }
   // z (one feature per thread) and the denominator
   float* zh = z + nh * D;
-  const float zn = zh[tid] + fw[tid];
+  const float zn = DECAY ? gam * zh[tid] + fw[tid] : zh[tid] + fw[tid];
   zh[tid] = zn;
   float dp = fu[tid] * zn;
 #pragma unroll

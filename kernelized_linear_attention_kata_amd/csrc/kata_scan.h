@@ -84,12 +84,18 @@ __device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const f
 // grid (ceil((E/4) / (256/G)), B*H), block 256.  E is a multiple of 4.  reverse = 1
 // scans the leaves from the last to the first (an exclusive suffix: leaf g receives
 // init + sum_{g' > g} state_g'), as the backward pass needs; sym_init as in scan_initial.
+//
+// dec (decay-gated state, may be NULL): dec[bh * n_leaf + g] is the total decay D_g of leaf
+// g, and the combine becomes affine: the prefix entering leaf g + 1 is D_g * (prefix
+// entering leaf g) + state_g; a segment's total carries the product of its leaves' D.
 __global__ void __launch_bounds__(256)
 kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
                 const float* __restrict__ S0, const float* __restrict__ z0,
-                float* __restrict__ ST, float* __restrict__ zT, int reverse, int sym_init) {
+                float* __restrict__ ST, float* __restrict__ zT, int reverse, int sym_init,
+                const float* __restrict__ dec) {
   __shared__ f32x4 tot[256];
   __shared__ f32x4 carry_s[256];
+  __shared__ float dseg[SCAN_GMAX];
   const int tid = threadIdx.x;
   const int QW = 256 / G;
   const int ql = tid % QW, seg = tid / QW;
@@ -106,29 +112,36 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
 #pragma unroll
     for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0, sym_init != 0);
   }
+  const float* dl = dec ? dec + bh * n_leaf : nullptr;
   for (int64_t r0 = 0; r0 < n_leaf; r0 += (int64_t)lseg * G) {
     const int64_t rs = r0 + (int64_t)seg * lseg;
     f32x4 x[SCAN_ROWS];
+    float dr[SCAN_ROWS];
     f32x4 tsum = zero4();
+    float dprod = 1.f;
 #pragma unroll
     for (int i = 0; i < SCAN_ROWS; ++i) {
-      const bool ok = active && i < lseg && rs + i < n_leaf;
+      const bool in = i < lseg && rs + i < n_leaf;
+      const bool ok = active && in;
       x[i] = ok ? *reinterpret_cast<const f32x4*>(base + row(rs + i) * E) : zero4();
-      tsum += x[i];
+      dr[i] = (dl && in) ? dl[row(rs + i)] : 1.f;
+      tsum = dr[i] * tsum + x[i];
+      dprod *= dr[i];
     }
     tot[tid] = tsum;
+    if (ql == 0) dseg[seg] = dprod;
     if (seg == 0) carry_s[ql] = carry;
     __syncthreads();
     f32x4 c = carry_s[ql];
-    for (int s2 = 0; s2 < seg; ++s2) c += tot[ql + s2 * QW];
+    for (int s2 = 0; s2 < seg; ++s2) c = dseg[s2] * c + tot[ql + s2 * QW];
 #pragma unroll
     for (int i = 0; i < SCAN_ROWS; ++i) {
       if (active && i < lseg && rs + i < n_leaf) *reinterpret_cast<f32x4*>(base + row(rs + i) * E) = c;
-      c += x[i];
+      c = dr[i] * c + x[i];
     }
     if (seg == 0) {
       f32x4 nc = carry_s[ql];
-      for (int s2 = 0; s2 < G; ++s2) nc += tot[ql + s2 * QW];
+      for (int s2 = 0; s2 < G; ++s2) nc = dseg[s2] * nc + tot[ql + s2 * QW];
       carry = nc;
     }
     __syncthreads();

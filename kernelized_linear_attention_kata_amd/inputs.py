@@ -194,6 +194,15 @@ def make_state_grad(B: int, H: int, dv: int, seed: int = 0, device="cpu"):
     return gST, gzT
 
 
+def make_log_decay(B: int, H: int, T: int, seed: int = 0, lo: float = 0.9, hi: float = 1.0,
+                   device="cpu") -> torch.Tensor:
+    """Seeded log-gates lam = log(gamma) [B, H, T] float32 with gamma uniform in [lo, hi]
+    (per token and head), the range of forget gates of gated linear attention."""
+    g = _gen(3000 + seed, device)
+    gam = lo + (hi - lo) * torch.rand((B, H, T), generator=g, device=device, dtype=torch.float32)
+    return torch.log(gam)
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw uint16 bit patterns of a bfloat16 tensor, as a numpy array on the host."""
     assert t.dtype == torch.bfloat16

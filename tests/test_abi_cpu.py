@@ -203,3 +203,32 @@ def test_backward_workspace_and_validation():
     assert lib.kata_backward(ctypes.byref(d), *a, fake, 1 << 40, None) == Bd.KATA_ERR_NULL
     assert lib.kata_backward(ctypes.byref(d), *args15, fake, n.value - 1, None) == Bd.KATA_ERR_WORKSPACE
     assert lib.kata_backward(ctypes.byref(d), *args15, None, 1 << 40, None) == Bd.KATA_ERR_WORKSPACE
+
+
+def test_decay_forward_workspace_and_validation():
+    lib = _lib_or_skip()
+    n = ctypes.c_size_t(0)
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    plain = ctypes.c_size_t(0)
+    assert lib.kata_forward_workspace_bytes(ctypes.byref(d), ctypes.byref(plain)) == Bd.KATA_OK
+    assert lib.kata_forward_decay_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    n_leaf = plain.value // (16 * (144 * 64 + 256) * 4)
+    assert n.value == (plain.value + 255) // 256 * 256 + 16 * n_leaf * 4
+    fake = ctypes.c_void_p(0x1000)
+    for field, value, status in [("d", 16, Bd.KATA_ERR_UNSUPPORTED), ("chunk", 128, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("in_dtype", Bd.KATA_F32, Bd.KATA_ERR_UNSUPPORTED), ("T", -1, Bd.KATA_ERR_SHAPE)]:
+        bad = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        setattr(bad, field, value)
+        assert lib.kata_forward_decay_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == status, field
+        assert lib.kata_forward_decay(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, fake, None, None,
+                                      fake, 1 << 40, None) == status, field
+    good = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_decay(ctypes.byref(good), fake, fake, fake, fake, None, None, None, fake, None, None,
+                                  fake, 1 << 40, None) == Bd.KATA_ERR_NULL          # lam missing
+    assert lib.kata_forward_decay(ctypes.byref(good), fake, fake, fake, fake, fake, fake, None, fake, None, None,
+                                  fake, 1 << 40, None) == Bd.KATA_ERR_NULL          # S0 without z0
+    assert lib.kata_forward_decay(ctypes.byref(good), fake, fake, fake, fake, fake, None, None, fake, None, None,
+                                  fake, 16, None) == Bd.KATA_ERR_WORKSPACE
+    args = [fake] * 7
+    assert lib.kata_decode_step_decay(4, 16, 64, 64, 16, 1, 0, *args[:6], None, fake, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_decode_step_decay(4, 16, 64, 32, 16, 1, 0, *args, fake, None) == Bd.KATA_ERR_UNSUPPORTED

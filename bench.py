@@ -24,6 +24,7 @@ workload on the host's cores.
     python bench.py --decode     # the recurrent decode step instead (its own JSON line)
     python bench.py --flash      # the flash-style O(T^2) forward on the 340M-layer workload
     python bench.py --backward   # the chunked-state backward on the long-context workload
+    python bench.py --decay      # the decay-gated forward on the long-context workload
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -42,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KATA causal fwd tokens/sec at T=131072 + % of MFMA/HBM peak (1 GPU)"
+DECAY_METRIC = "KATA decay-gated causal fwd tokens/sec at T=131072 + % of HBM peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_chunk_intra")
@@ -58,15 +60,19 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes):
-    """Bytes each kernel must move at minimum (per launch), by the byte model of the path."""
+def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False):
+    """Bytes each kernel must move at minimum (per launch), by the byte model of the path
+    (decay: the log-gates, 4 B per token-head, read by the state and intra kernels, and
+    one float per leaf)."""
     E = 144 * dv + 256                    # packed leaf state block (S slots + Z), floats
     states = B * H * n_leaf * E * 4
     tok = B * H * T
+    g = tok * 4 if decay else 0
+    gl = B * H * n_leaf * 4 if decay else 0
     return {
-        "kata_chunk_state": tok * (d + dv) * in_bytes + states,
-        "kata_state_scan": 2 * states + B * H * 256 * (dv + 1) * 4,
-        "kata_chunk_intra": tok * (2 * d + dv) * in_bytes + states + tok * dv * out_bytes,
+        "kata_chunk_state": tok * (d + dv) * in_bytes + states + g + gl,
+        "kata_state_scan": 2 * states + B * H * 256 * (dv + 1) * 4 + gl,
+        "kata_chunk_intra": tok * (2 * d + dv) * in_bytes + states + tok * dv * out_bytes + g,
     }
 
 
@@ -111,6 +117,30 @@ def cpu_baseline(case, stride):
         "seconds": dt,
         "host_cpus": os.cpu_count(),
     }
+
+
+def decay_cpu_baseline(case, lam, T_sample=8192):
+    """The oracle's O(T^2) decay-gated forward on the first T_sample tokens of 2 heads,
+    extrapolated to the whole workload by its T^2 cost."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    hs = slice(0, 2)
+    q = O.bf16_bits_to_f64(I.bf16_bits(case.q[:, hs, :T_sample]))
+    k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
+    v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
+    P = case.P[hs].double().cpu().numpy()
+    lm = lam[:, hs, :T_sample].double().cpu().numpy()
+    t0 = time.perf_counter()
+    O.forward_decay_quadratic(q, k, v, P, lm)
+    dt = time.perf_counter() - t0
+    scale = (case.T / T_sample) ** 2 * (case.H / 2)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 O(T^2) decay-gated oracle on the first {T_sample} tokens of 2 of {case.H} heads, "
+                       f"{dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the T^2 cost")}
 
 
 DECODE_METRIC = ("KATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=16, dv=64), "
@@ -441,6 +471,8 @@ def main():
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
     ap.add_argument("--backward", action="store_true", help="time the chunked-state backward instead")
+    ap.add_argument("--decay", action="store_true",
+                    help="time the decay-gated forward (kata_forward_decay, gates in [0.9, 1]) instead")
     ap.add_argument("--bwd-cpu-tokens", type=int, default=16384,
                     help="prefix length of the oracle's backward sample (CPU baseline of --backward)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -485,7 +517,15 @@ def main():
     case = cases[0]
     B, H, T, d, dv, C = case.B, case.H, case.T, case.d, case.dv, args.chunk
     ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if args.decay:
+        if C != 64:
+            print("bench.py --decay supports chunk 64 only", file=sys.stderr)
+            sys.exit(2)
+        lams = [I.make_log_decay(B, H, T, seed=seed0 + b, device=dev) for b in range(nb)]
+        wsd = kata.forward_decay_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
+        ws = torch.empty(wsd, dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
     ST = torch.empty((B, H, 256, dv), dtype=torch.float32, device=dev)
     zT = torch.empty((B, H, 256), dtype=torch.float32, device=dev)
@@ -495,6 +535,10 @@ def main():
 
     def step(i, events=None):
         c = cases[i % nb]
+        if args.decay:
+            kata.forward_decay(c.q, c.k, c.v, c.P, lams[i % nb], chunk=C, y=ys[i % nb], workspace=ws,
+                               return_state=False, scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events)
+            return
         kata.forward(c.q, c.k, c.v, c.P, chunk=C, y=ys[i % nb], workspace=ws, ST=ST, zT=zT, return_state=True,
                      scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events)
 
@@ -529,7 +573,7 @@ def main():
                   for j, name in enumerate(KERNELS)}
 
     tokens_per_s = B * T / (ms_per_step / 1e3)
-    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2)
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay)
     aflops = algorithmic_flops(B, H, T, d, dv, C)
     dominant = max(per_kernel, key=per_kernel.get)
     kernels = {}
@@ -551,13 +595,13 @@ def main():
         try:
             cnt = json.load(open(COUNTERS_FILE))
             entry = cnt.get("kernels", {}).get(dominant)
-            if cnt.get("source_hash") == src and entry and cnt.get("chunk") == C:
+            if cnt.get("source_hash") == src and entry and cnt.get("chunk") == C and not args.decay:
                 traffic = entry["hbm_bytes_per_launch"]
         except (ValueError, KeyError):
             traffic = None
 
     result = {
-        "metric": METRIC,
+        "metric": DECAY_METRIC if args.decay else METRIC,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -569,8 +613,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
-        "config": {"workload": f"long-context KATA forward: B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, "
-                               f"fp32 P/state, chunk {C}, {args.scan} scan over {n_leaf} leaf states per head",
+        "config": {"workload": (f"long-context KATA forward{' with decay gates in [0.9, 1] (fp32 log-gates)' if args.decay else ''}: "
+                                f"B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, fp32 P/state, chunk {C}, "
+                                f"{args.scan} scan over {n_leaf} leaf states per head"),
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": C, "batches_cycled": nb,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -581,7 +626,7 @@ def main():
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(case, args.cpu_stride)
+        cb = decay_cpu_baseline(case, lams[0], args.cpu_stride) if args.decay else cpu_baseline(case, args.cpu_stride)
         result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(result), flush=True)
 

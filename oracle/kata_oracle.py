@@ -63,6 +63,9 @@ __all__ = [
     "forward_decay_quadratic",
     "final_state_decay",
     "decode_decay_reference",
+    "feature_unit",
+    "delta_recurrence",
+    "delta_decode_reference",
 ]
 
 
@@ -411,3 +414,71 @@ def decode_decay_reference(S, z, q, k, v, P, lam):
     S = np.array(S, dtype=np.float64) * g[:, :, None, None]
     z = np.array(z, dtype=np.float64) * g[:, :, None]
     return decode_reference(S, z, q, k, v, P)
+
+
+# ---- DeltaKATA -------------------------------------------------------------------------
+#
+# PARITY NOTE (reading): the pages name DeltaKATA (KATA with the delta rule; it corrects
+# stale bindings under repeated-key overwrite) without defining it.  The plainest
+# reading: the delta rule of DeltaNet with KATA's rank-one PSD feature normalised to unit
+# norm (as DeltaNet normalises its keys and queries),
+#
+#     phi^(x) = vec(u u^T) / |u|^2,                 u = P x   (|phi^(x)| = 1)
+#     S_t = S_{t-1} + beta_t phi^(k_t) (v_t - S_{t-1}^T phi^(k_t))^T,   beta_t in [0, 1]
+#     y_t = S_t^T phi^(q_t)
+#
+# with no denominator (the delta rule replaces the normalisation); phi^(x) = 0 where u = 0.
+
+
+def feature_unit(u):
+    """phi^(u) = vec(u u^T) / |u|^2 (unit Frobenius norm; 0 for u = 0)."""
+    u = np.asarray(u, dtype=np.float64)
+    n2 = np.sum(u * u, axis=-1, keepdims=True)
+    f = feature_full(u)
+    return np.where(n2 > 0, f / np.where(n2 > 0, n2, 1.0), 0.0)
+
+
+def delta_recurrence(q, k, v, P, beta, S0=None):
+    """DeltaKATA by its token recurrence (see the reading above).
+
+    q, k: [B, H, T, d]; v: [B, H, T, dv]; P: [H, p, d]; beta: [B, H, T]; S0 [B, H, p*p, dv]
+    or None.  Returns (y [B, H, T, dv], S_T [B, H, p*p, dv]).
+    """
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, H, T, _ = q.shape
+    dv = v.shape[-1]
+    pp = P.shape[1] * P.shape[1]
+    y = np.zeros((B, H, T, dv))
+    ST = np.zeros((B, H, pp, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((pp, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            fq = feature_unit(project(q[b, h], P[h]))
+            fk = feature_unit(project(k[b, h], P[h]))
+            for t in range(T):
+                e = v[b, h, t] - S.T @ fk[t]
+                S = S + beta[b, h, t] * np.outer(fk[t], e)
+                y[b, h, t] = S.T @ fq[t]
+            ST[b, h] = S
+    return y, ST
+
+
+def delta_decode_reference(S, q, k, v, P, beta):
+    """One DeltaKATA decode step for N streams: S' = S + beta phi^(k) (v - S^T phi^(k))^T,
+    y = S'^T phi^(q).  S [N, H, p*p, dv]; q, k [N, H, d]; v [N, H, dv]; beta [N, H].
+    Returns (y, S')."""
+    S = np.array(S, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    N, H = q.shape[:2]
+    y = np.zeros(v.shape)
+    for h in range(H):
+        fq = feature_unit(project(q[:, h], P[h]))
+        fk = feature_unit(project(k[:, h], P[h]))
+        e = v[:, h] - np.einsum("nf,nfc->nc", fk, S[:, h])
+        S[:, h] = S[:, h] + beta[:, h, None, None] * fk[:, :, None] * e[:, None, :]
+        y[:, h] = np.einsum("nf,nfc->nc", fq, S[:, h])
+    return y, S

@@ -25,6 +25,7 @@ workload on the host's cores.
     python bench.py --flash      # the flash-style O(T^2) forward on the 340M-layer workload
     python bench.py --backward   # the chunked-state backward on the long-context workload
     python bench.py --decay      # the decay-gated forward on the long-context workload
+    python bench.py --decode --delta   # the DeltaKATA decode step (prefill by its recurrent forward)
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -143,12 +144,15 @@ def decay_cpu_baseline(case, lam, T_sample=8192):
                        f"{dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the T^2 cost")}
 
 
+DELTA_DECODE_METRIC = ("DeltaKATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=16, dv=64), "
+                       "1024 steps after an 8192-token prefill (1 GPU)")
 DECODE_METRIC = ("KATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=16, dv=64), "
                  "1024 steps after an 8192-token prefill (1 GPU)")
 
 
-def decode_cpu_baseline(dc, budget_s=10.0):
-    """The oracle's decode step on the host over the same streams, steps until budget_s."""
+def decode_cpu_baseline(dc, budget_s=10.0, delta=False, betas=None):
+    """The oracle's decode step (or DeltaKATA decode step) on the host over the same
+    streams, steps until budget_s."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -165,12 +169,16 @@ def decode_cpu_baseline(dc, budget_s=10.0):
         q = O.bf16_bits_to_f64(I.bf16_bits(dc.q[steps]))
         k = O.bf16_bits_to_f64(I.bf16_bits(dc.k[steps]))
         v = O.bf16_bits_to_f64(I.bf16_bits(dc.v[steps]))
-        _, S, z = O.decode_reference(S, z, q, k, v, P)
+        if delta:
+            _, S = O.delta_decode_reference(S, q, k, v, P, betas[steps].double().cpu().numpy())
+        else:
+            _, S, z = O.decode_reference(S, z, q, k, v, P)
         steps += 1
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": N * steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle decode step over all {N} streams x {H} heads, first {steps} steps "
+            "sample": f"fp64 oracle {'DeltaKATA ' if delta else ''}decode step over all {N} streams x {H} heads, "
+                      f"first {steps} steps "
                       f"({dt:.1f} s); the cost per step does not depend on the state's values"}
 
 
@@ -273,18 +281,44 @@ def bench_decode(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    delta = bool(args.delta)
     dc = I.make_decode(device=dev)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
-    _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
+    prefill = None
+    if delta:
+        beta0 = I.make_beta(N, H, T0, seed=4, device=dev)
+        betas = I.make_beta(steps, N, H, seed=5, device=dev)
+        pf0, pf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        kata.forward_delta(dc.q0, dc.k0, dc.v0, dc.P, beta0, return_state=True)      # untimed first call
+        pf0.record()
+        _, S0 = kata.forward_delta(dc.q0, dc.k0, dc.v0, dc.P, beta0, return_state=True)
+        pf1.record()
+        torch.cuda.synchronize()
+        pms = pf0.elapsed_time(pf1)
+        pbytes = N * H * (T0 * (2 * d + dv) * 2 + T0 * (dv * 2 + 4) + 256 * dv * 4)
+        prefill = {"kernel": "kata_delta_recurrent", "tokens": N * T0, "ms": round(pms, 3),
+                   "tokens_per_s": N * T0 / (pms / 1e3), "hbm_GBps": round(pbytes / (pms / 1e3) / 1e9, 1)}
+        z0 = None
+    else:
+        _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
     S = torch.empty_like(S0)
-    z = torch.empty_like(z0)
+    z = torch.empty_like(z0) if z0 is not None else None
     ys = torch.empty((steps, N, H, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def run(j):
-        kata.decode_step(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
+    if delta:
+        def run(j):
+            kata.decode_step_delta(S, dc.q[j], dc.k[j], dc.v[j], dc.P, betas[j], y=ys[j], stream=stream)
+    else:
+        def run(j):
+            kata.decode_step(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
 
-    S.copy_(S0); z.copy_(z0)
+    def reset():
+        S.copy_(S0)
+        if z is not None:
+            z.copy_(z0)
+
+    reset()
     settle0 = time.perf_counter()
     n_settle = 0
     while time.perf_counter() - settle0 < args.settle_s:
@@ -292,7 +326,7 @@ def bench_decode(args):
             run(n_settle % steps)
             n_settle += 1
         torch.cuda.synchronize()
-    S.copy_(S0); z.copy_(z0)
+    reset()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream); e1.record(stream)
     torch.cuda.synchronize()
@@ -303,23 +337,29 @@ def bench_decode(args):
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     ms_step = total_ms / steps
-    state_bytes = (S.numel() + z.numel()) * 4
-    step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4
+    state_bytes = S.numel() * 4 + (z.numel() * 4 if z is not None else 0)
+    step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4 + (N * H * 4 if delta else 0)
     achieved = step_bytes / (ms_step / 1e3) / 1e9
+    kernel = "kata_delta_recurrent (T=1, in place)" if delta else "kata_decode_step"
+    workload = (f"recurrent {'DeltaKATA ' if delta else ''}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
+                f"canonical fp32 state [{N},{H},256,{dv}]{'' if delta else ' + z'}, prefill T={T0} by "
+                f"{'kata_forward_delta' if delta else 'kata_forward'}, {steps} steps, every 4th key repeating "
+                f"an earlier one" + (", beta uniform in [0.5, 1]" if delta else ""))
     result = {
-        "metric": DECODE_METRIC, "value": N * steps / (total_ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "metric": DELTA_DECODE_METRIC if delta else DECODE_METRIC, "value": N * steps / (total_ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": 0, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 q/k/v, f32 state", "data": "synthetic",
-        "config": {"workload": f"recurrent decode: {N} streams x {H} heads, d=dv={d}, p=16, canonical fp32 "
-                               f"state [{N},{H},256,{dv}] + z, prefill T={T0} by kata_forward, {steps} steps, "
-                               f"every 4th key repeating an earlier one", "streams": N, "heads": H},
-        "roofline": {"bound": "hbm", "kernel": "kata_decode_step", "achieved": round(achieved, 1),
+        "config": {"workload": workload, "streams": N, "heads": H},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "bytes_per_step": step_bytes},
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
     }
+    if prefill is not None:
+        result["prefill"] = prefill
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = decode_cpu_baseline(dc)
+        result["cpu_baseline"] = decode_cpu_baseline(dc, delta=delta, betas=betas if delta else None)
     print(json.dumps(result), flush=True)
 
 
@@ -469,6 +509,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
+    ap.add_argument("--delta", action="store_true",
+                    help="with --decode: the DeltaKATA decode step (prefill by kata_forward_delta)")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
     ap.add_argument("--backward", action="store_true", help="time the chunked-state backward instead")
     ap.add_argument("--decay", action="store_true",

@@ -263,6 +263,39 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p,
                              const void* q, const void* k, const void* v,
                              const float* P, void* y, void* stream);
 
+/* DeltaKATA.  [TS-4] (repeated-key overwrite) credits the delta-rule variant of KATA with
+ * correcting stale bindings when a key is written again, and [TS-1] / [ABS] name delta
+ * rules among the mechanisms studied with KATA's features; none defines it.  The reading
+ * taken is DeltaNet's delta rule with KATA's feature normalised to unit norm:
+ *   phi^(x) = vec(u u^T) / |u|^2, u = P x     (|phi^(x)| = 1; phi^(x) = 0 where u = 0)
+ *   S_t = S_{t-1} + beta_t phi^(k_t) (v_t - S_{t-1}^T phi^(k_t))^T
+ *   y_t = S_t^T phi^(q_t)                      (no denominator, no z)
+ * beta is taken as given (0 <= beta <= 1 keeps the update a contraction toward v; beta = 1
+ * with a repeated key overwrites its value exactly).
+ *
+ * kata_forward_delta: the causal forward by the token recurrence, the state held on chip
+ * by one workgroup per (batch row, head); it reads q, k, v once and the state once.
+ *   q [B,H,T,d], k [B,H,T,d], v [B,H,T,dv] in_dtype; P [H,p,d] float32;
+ *   beta [B,H,T] float32; S0 [B,H,p*p,dv] float32 initial state or NULL for zero;
+ *   y [B,H,T,dv] out_dtype (written); ST [B,H,p*p,dv] float32 final state or NULL.
+ * desc->chunk, scan and scan_leaf are not used.  No workspace.
+ * Supported: p = 16, (d, dv) = (16, 16) or (64, 64), in/out dtype F32 or BF16,
+ * B*H < 2^31, any T >= 0 (T = 0 writes ST = S0, or 0).  The state is carried in full
+ * (both mirror entries of the symmetric feature are updated alike). */
+kata_status kata_forward_delta(const kata_forward_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const float* P, const float* beta, const float* S0,
+                               void* y, float* ST, void* stream);
+
+/* One DeltaKATA decode step for N independent streams (same reading), in place:
+ *   S <- S + beta phi^(k) (v - S^T phi^(k))^T,  y = S^T phi^(q)  (after the update)
+ *   S [N,H,p*p,dv] float32; q, k [N,H,d], v [N,H,dv] in_dtype; P [H,p,d] float32;
+ *   beta [N,H] float32; y [N,H,dv] out_dtype.  Support as for kata_forward_delta. */
+kata_status kata_decode_step_delta(int64_t N, int64_t H, int d, int dv, int p,
+                                   kata_dtype in_dtype, kata_dtype out_dtype,
+                                   float* S, const void* q, const void* k, const void* v,
+                                   const float* P, const float* beta, void* y, void* stream);
+
 /* Feature layouts for kata_feature_map. */
 typedef enum {
   KATA_FEATURE_FULL = 0,         /* p*p entries, index i*p + j: phi = vec(u u^T)       */

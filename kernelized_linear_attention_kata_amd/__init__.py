@@ -7,8 +7,8 @@ library; the first call of an entry point does, and fails loudly if it is
 missing.
 """
 _BINDING_NAMES = (
-    "KataError", "abi_version", "backward", "backward_workspace_bytes", "decode_step", "decode_step_decay",
-    "forward_decay", "forward_decay_workspace_bytes", "feature_map", "flash_forward", "flash_workspace_bytes",
+    "KataError", "abi_version", "backward", "backward_workspace_bytes", "decode_step", "decode_step_decay", "decode_step_delta",
+    "forward_decay", "forward_decay_workspace_bytes", "forward_delta", "feature_map", "flash_forward", "flash_workspace_bytes",
     "forward", "forward_workspace_bytes", "library_path", "load_library",
 )
 

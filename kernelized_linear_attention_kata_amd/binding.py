@@ -99,6 +99,10 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
     lib.kata_decode_step_decay.restype = ci
     lib.kata_decode_step_decay.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_forward_delta.restype = ci
+    lib.kata_forward_delta.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9
+    lib.kata_decode_step_delta.restype = ci
+    lib.kata_decode_step_delta.argtypes = [i64, i64, ci, ci, ci, ci, ci] + [vp] * 8
     lib.kata_decode_step.restype = ci
     lib.kata_decode_step.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_feature_map.restype = ci
@@ -323,6 +327,61 @@ def decode_step_decay(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torc
                                        _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(lam), _ptr(y),
                                        _stream_handle(stream, dev))
     _check(st, "kata_decode_step_decay")
+    return y
+
+
+def forward_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,
+                  S0: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  return_state: bool = False, y: Optional[torch.Tensor] = None, stream=None):
+    """DeltaKATA causal forward (kata_forward_delta), by the token recurrence with the state on
+    chip: S_t = S_{t-1} + beta_t phi^(k_t) (v_t - S_{t-1}^T phi^(k_t))^T, y_t = S_t^T phi^(q_t),
+    phi^ the unit-normalised feature.  q, k: [B,H,T,d]; v: [B,H,T,dv]; P: [H,16,d] fp32;
+    beta: [B,H,T] fp32; S0: [B,H,256,dv] fp32 or None.  Returns y, or (y, ST) when return_state."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(beta, "beta", (B, H, T), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev) if return_state else None
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    st = _lib().kata_forward_delta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta), _ptr(S0),
+                                   _ptr(y), _ptr(ST), _stream_handle(stream, dev))
+    _check(st, "kata_forward_delta")
+    return (y, ST) if return_state else y
+
+
+def decode_step_delta(S: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
+                      beta: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One DeltaKATA decode step (kata_decode_step_delta), in place on S [N,H,256,dv] fp32;
+    beta [N,H] fp32.  Returns y [N,H,dv]."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(S, "S", (N, H, P_DIM * P_DIM, dv), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_delta(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype), _ptr(S),
+                                       _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta), _ptr(y),
+                                       _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_delta")
     return y
 
 

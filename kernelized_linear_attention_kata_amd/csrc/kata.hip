@@ -16,6 +16,7 @@
 #include "kata_bwd.h"
 #include "kata_chunk.h"
 #include "kata_decode.h"
+#include "kata_delta.h"
 #include "kata_flash.h"
 #include "kata_scan.h"
 
@@ -338,6 +339,30 @@ size_t decay_ws_bytes(const Plan& pl, const kata_forward_desc* d) {
   return align256(pl.ws_bytes) + (size_t)(d->B * d->H) * (size_t)pl.n_leaf * sizeof(float);
 }
 
+// DeltaKATA token recurrence: one workgroup per (sequence, head), T tokens each.
+kata_status launch_delta(int64_t BH, int64_t T, int H, int d, int dv, kata_dtype in_dtype, kata_dtype out_dtype,
+                         const float* S0, float* ST, const void* q, const void* k, const void* v,
+                         const float* beta, const float* P, void* y, hipStream_t st) {
+  const dim3 grid((unsigned)BH);
+#define KATA_DELTA(TI, TO, DVV)                                                                              \
+  hipLaunchKernelGGL((kata::kata_delta_recurrent<TI, TO, DVV>), grid, dim3(256), 0, st, S0, ST, (const TI*)q, \
+                     (const TI*)k, (const TI*)v, beta, P, (TO*)y, H, d, T)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DELTA(float, float, 64);
+    else if (fi) KATA_DELTA(float, bf16, 64);
+    else if (fo) KATA_DELTA(bf16, float, 64);
+    else KATA_DELTA(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DELTA(float, float, 16);
+    else if (fi) KATA_DELTA(float, bf16, 16);
+    else if (fo) KATA_DELTA(bf16, float, 16);
+    else KATA_DELTA(bf16, bf16, 16);
+  }
+#undef KATA_DELTA
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -611,6 +636,37 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dt
   }
 #undef KATA_DECODE
   return launch_status();
+}
+
+kata_status kata_forward_delta(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                               const float* P, const float* beta, const float* S0, void* y, float* ST,
+                               void* stream) {
+  if (!desc) return KATA_ERR_NULL;
+  const kata_forward_desc* d = desc;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0) return KATA_ERR_SHAPE;
+  if (d->p != P_DIM || !((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(d->in_dtype) != KATA_OK || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (d->B > 0 && d->H > 0x7fffffff / d->B) return KATA_ERR_SHAPE;
+  const int64_t BH = d->B * d->H;
+  if (BH == 0) return KATA_OK;
+  if (d->T > ((int64_t)1 << 40)) return KATA_ERR_SHAPE;
+  if (!P) return KATA_ERR_NULL;
+  if (d->T > 0 && (!q || !k || !v || !beta || !y)) return KATA_ERR_NULL;
+  if (d->T == 0 && !ST) return KATA_OK;
+  return launch_delta(BH, d->T, (int)d->H, d->d, d->dv, d->in_dtype, d->out_dtype, S0, ST, q, k, v, beta, P, y,
+                      (hipStream_t)stream);
+}
+
+kata_status kata_decode_step_delta(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                                   kata_dtype out_dtype, float* S, const void* q, const void* k, const void* v,
+                                   const float* P, const float* beta, void* y, void* stream) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N > 0 && H > 0x7fffffff / N) return KATA_ERR_SHAPE;
+  if (N * H == 0) return KATA_OK;
+  if (!S || !q || !k || !v || !P || !beta || !y) return KATA_ERR_NULL;
+  return launch_delta(N * H, 1, (int)H, d, dv, in_dtype, out_dtype, S, S, q, k, v, beta, P, y, (hipStream_t)stream);
 }
 
 kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H, int d, int p,

@@ -203,6 +203,13 @@ def make_log_decay(B: int, H: int, T: int, seed: int = 0, lo: float = 0.9, hi: f
     return torch.log(gam)
 
 
+def make_beta(*shape: int, seed: int = 0, lo: float = 0.5, hi: float = 1.0, device="cpu") -> torch.Tensor:
+    """Seeded delta-rule write strengths beta, float32 uniform in [lo, hi], of the given
+    shape ([B, H, T] for a forward, [N, H] or [steps, N, H] for decode steps)."""
+    g = _gen(4000 + seed, device)
+    return lo + (hi - lo) * torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw uint16 bit patterns of a bfloat16 tensor, as a numpy array on the host."""
     assert t.dtype == torch.bfloat16

@@ -232,3 +232,38 @@ def test_decay_forward_workspace_and_validation():
     args = [fake] * 7
     assert lib.kata_decode_step_decay(4, 16, 64, 64, 16, 1, 0, *args[:6], None, fake, None) == Bd.KATA_ERR_NULL
     assert lib.kata_decode_step_decay(4, 16, 64, 32, 16, 1, 0, *args, fake, None) == Bd.KATA_ERR_UNSUPPORTED
+
+
+def test_delta_forward_and_decode_validation():
+    """DeltaKATA entry points reject bad shapes, dtypes and missing pointers on the host
+    and treat empty work as a no-op (nothing is launched on these paths)."""
+    lib = _lib_or_skip()
+    fake = ctypes.c_void_p(0x1000)
+    for field, value, status in [("d", 32, Bd.KATA_ERR_UNSUPPORTED), ("dv", 16, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("p", 8, Bd.KATA_ERR_UNSUPPORTED), ("in_dtype", 7, Bd.KATA_ERR_UNSUPPORTED),
+                                 ("T", -1, Bd.KATA_ERR_SHAPE), ("B", -2, Bd.KATA_ERR_SHAPE)]:
+        bad = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        setattr(bad, field, value)
+        assert lib.kata_forward_delta(ctypes.byref(bad), fake, fake, fake, fake, fake, None, fake, None,
+                                      None) == status, field
+    good = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_delta(None, fake, fake, fake, fake, fake, None, fake, None, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_forward_delta(ctypes.byref(good), fake, fake, fake, fake, None, None, fake, None,
+                                  None) == Bd.KATA_ERR_NULL                                   # beta missing
+    assert lib.kata_forward_delta(ctypes.byref(good), fake, fake, fake, None, fake, None, fake, None,
+                                  None) == Bd.KATA_ERR_NULL                                   # P missing
+    huge = Bd.make_desc(1 << 20, 1 << 12, 10, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_delta(ctypes.byref(huge), fake, fake, fake, fake, fake, None, fake, None,
+                                  None) == Bd.KATA_ERR_SHAPE                                  # B*H >= 2^31
+    empty = Bd.make_desc(0, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_delta(ctypes.byref(empty), None, None, None, None, None, None, None, None,
+                                  None) == Bd.KATA_OK
+    no_tokens = Bd.make_desc(2, 3, 0, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_delta(ctypes.byref(no_tokens), None, None, None, fake, None, None, None, None,
+                                  None) == Bd.KATA_OK                                         # nothing to write
+    args = [fake] * 6
+    assert lib.kata_decode_step_delta(4, 16, 64, 64, 16, 1, 0, *args[:5], None, fake, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_decode_step_delta(4, 16, 64, 16, 16, 1, 0, *args, fake, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_delta(4, 16, 64, 64, 12, 1, 0, *args, fake, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_delta(-1, 16, 64, 64, 16, 1, 0, *args, fake, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_decode_step_delta(0, 16, 64, 64, 16, 1, 0, *([None] * 6), None, None) == Bd.KATA_OK

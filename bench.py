@@ -51,13 +51,25 @@ KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_chunk_intra")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
+FORWARD_SOURCES = ("kata_common.h", "kata_chunk.h", "kata_scan.h")
+FORWARD_HOST_END = "kata_status validate_flash("
+
+
 def source_hash() -> str:
+    """Hash of what the chunked forward's kernels and their launch plan are built from:
+    the three device headers they live in and the host code of kata.hip up to the first
+    entry point of another path.  Counters recorded under another hash are not reused."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kernelized_linear_attention_kata_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in FORWARD_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
+    with open(os.path.join(csrc, "kata.hip"), "r") as f:
+        host = f.read()
+    cut = host.find(FORWARD_HOST_END)
+    h.update(b"kata.hip")
+    h.update((host[:cut] if cut > 0 else host).encode())
     return h.hexdigest()[:16]
 
 

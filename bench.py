@@ -55,22 +55,36 @@ FORWARD_SOURCES = ("kata_common.h", "kata_chunk.h", "kata_scan.h")
 FORWARD_HOST_END = "kata_status validate_flash("
 
 
-def source_hash() -> str:
+def source_hash(extra=()) -> str:
     """Hash of what the chunked forward's kernels and their launch plan are built from:
     the three device headers they live in and the host code of kata.hip up to the first
-    entry point of another path.  Counters recorded under another hash are not reused."""
+    entry point of another path (plus the headers in ``extra``, and then all of kata.hip,
+    for another path).  Counters recorded under another hash are not reused."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kernelized_linear_attention_kata_amd", "csrc")
-    for name in FORWARD_SOURCES:
+    for name in FORWARD_SOURCES + tuple(extra):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     with open(os.path.join(csrc, "kata.hip"), "r") as f:
         host = f.read()
-    cut = host.find(FORWARD_HOST_END)
+    cut = host.find(FORWARD_HOST_END) if not extra else -1
     h.update(b"kata.hip")
     h.update((host[:cut] if cut > 0 else host).encode())
     return h.hexdigest()[:16]
+
+
+def recorded_traffic(fname: str, src: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from a committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when the summary is missing or was recorded for other kernel sources."""
+    path = os.path.join(ROOT, "profiles", fname)
+    try:
+        cnt = json.load(open(path))
+        if cnt.get("source_hash") != src:
+            return None
+        return cnt["kernels"][kernel]["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False):
@@ -353,6 +367,8 @@ def bench_decode(args):
     step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4 + (N * H * 4 if delta else 0)
     achieved = step_bytes / (ms_step / 1e3) / 1e9
     kernel = "kata_delta_recurrent (T=1, in place)" if delta else "kata_decode_step"
+    src = source_hash(("kata_delta.h",) if delta else ("kata_decode.h",))
+    traffic = recorded_traffic("hbm_counters_decode_delta.json", src, "kata_delta_recurrent") if delta else None
     workload = (f"recurrent {'DeltaKATA ' if delta else ''}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
                 f"canonical fp32 state [{N},{H},256,{dv}]{'' if delta else ' + z'}, prefill T={T0} by "
                 f"{'kata_forward_delta' if delta else 'kata_forward'}, {steps} steps, every 4th key repeating "
@@ -365,7 +381,8 @@ def bench_decode(args):
         "config": {"workload": workload, "streams": N, "heads": H},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_step": step_bytes},
+                     "traffic": traffic, "bytes_per_step": step_bytes},
+        "source_hash": src,
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
     }
     if prefill is not None:
@@ -496,10 +513,11 @@ def bench_backward(args):
                                f"states per head",
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("hbm_counters_backward.json", source_hash(("kata_bwd.h",)), dominant)},
         "step_alg_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
         "kernels": kernels,
-        "source_hash": source_hash(),
+        "source_hash": source_hash(("kata_bwd.h",)),
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
     }
     if not args.no_cpu_baseline:

@@ -19,6 +19,8 @@ Wall with Symmetric Cones", arXiv 2607.17419):
            "Cono PSD"): rank-one PSD feature psi(u) = u u^T, which squares the
            raw inner product; capacity grows with the projection dimension p.
 * [TS-2.3] same summary, section 2.3: chunked form, exact O(T) chunked state.
+* [TS-4]   same summary, section 4 ("Resultados"): the delta-rule variant
+           (DeltaKATA) corrects stale bindings under repeated-key overwrite.
 
 What is computed (plain definition, no blocking beyond bounding memory):
 
@@ -418,8 +420,8 @@ def decode_decay_reference(S, z, q, k, v, P, lam):
 
 # ---- DeltaKATA -------------------------------------------------------------------------
 #
-# PARITY NOTE (reading): the pages name DeltaKATA (KATA with the delta rule; it corrects
-# stale bindings under repeated-key overwrite) without defining it.  The plainest
+# PARITY NOTE (reading): [TS-4] and [ABS] name DeltaKATA (KATA with the delta rule; it
+# corrects stale bindings under repeated-key overwrite) without defining it.  The plainest
 # reading: the delta rule of DeltaNet with KATA's rank-one PSD feature normalised to unit
 # norm (as DeltaNet normalises its keys and queries),
 #

@@ -21,6 +21,8 @@ Wall with Symmetric Cones", arXiv 2607.17419):
 * [TS-2.3] same summary, section 2.3: chunked form, exact O(T) chunked state.
 * [TS-4]   same summary, section 4 ("Resultados"): the delta-rule variant
            (DeltaKATA) corrects stale bindings under repeated-key overwrite.
+* [TS-2.3v] same summary, section 2.3, item "Variantes": KATA-Mg (several PSD
+           factors) and KATA-Sigma-g (summed PSD factors).
 
 What is computed (plain definition, no blocking beyond bounding memory):
 
@@ -68,6 +70,13 @@ __all__ = [
     "feature_unit",
     "delta_recurrence",
     "delta_decode_reference",
+    "factor_projections",
+    "forward_mg_quadratic",
+    "final_state_mg",
+    "recurrence_mg",
+    "forward_sg_quadratic",
+    "final_state_sg",
+    "recurrence_sg",
 ]
 
 
@@ -484,3 +493,172 @@ def delta_decode_reference(S, q, k, v, P, beta):
         S[:, h] = S[:, h] + beta[:, h, None, None] * fk[:, :, None] * e[:, None, :]
         y[:, h] = np.einsum("nf,nfc->nc", fq, S[:, h])
     return y, S
+
+
+# ---- KATA-Mg and KATA-Sigma-g ----------------------------------------------------------
+#
+# PARITY NOTE (reading): [TS-2.3v] names two variants with g PSD factors, "several" (Mg) and
+# "summed" (Sigma-g), trading state size against packing efficiency, without defining
+# them.  With g projections P_1..P_g per head (P [H, g, p, d]) and u_i = P_i q, w_i = P_i k:
+#
+#   Mg      phi(x) = [vec(u_1 u_1^T); ...; vec(u_g u_g^T)]     state g*p*p x dv
+#           a_ts = sum_i (u_i,t . w_i,s)^2
+#   Sigma-g phi(x) = vec(sum_i u_i u_i^T)                      state p*p x dv
+#           a_ts = sum_i sum_j (u_i,t . w_j,s)^2
+#
+# and y_t = sum_s a_ts v_s / sum_s a_ts over s <= t as for KATA (g = 1 is KATA itself in
+# both).  Initial and final states are in the layouts above (Mg: factor-major blocks of
+# p*p rows).
+
+
+def factor_projections(x, P):
+    """u_i = P_i x for every factor: x [..., d], P [g, p, d] -> [g, ..., p]."""
+    x = np.asarray(x, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    return np.stack([x @ P[i].T for i in range(P.shape[0])])
+
+
+def _gate(num, den):
+    return np.where(den[:, None] != 0, num / np.where(den[:, None] != 0, den[:, None], 1.0), 0.0)
+
+
+def forward_mg_quadratic(q, k, v, P, S0=None, z0=None):
+    """KATA-Mg by its O(T^2) definition.  q, k [B,H,T,d]; v [B,H,T,dv]; P [H,g,p,d];
+    S0 [B,H,g*p*p,dv], z0 [B,H,g*p*p] or None.  Returns y [B,H,T,dv]."""
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = q.shape
+    G, p = P.shape[1], P.shape[2]
+    y = np.zeros(v.shape)
+    mask = np.tril(np.ones((T, T))) > 0
+    for b in range(B):
+        for h in range(H):
+            U = factor_projections(q[b, h], P[h])     # [g, T, p]
+            W = factor_projections(k[b, h], P[h])
+            a = np.zeros((T, T))
+            for i in range(G):
+                a += (U[i] @ W[i].T) ** 2
+            a = np.where(mask, a, 0.0)
+            num = a @ v[b, h]
+            den = a.sum(axis=1)
+            if S0 is not None:
+                fq = np.concatenate([feature_full(U[i]) for i in range(G)], axis=1)
+                num = num + fq @ np.asarray(S0[b, h], dtype=np.float64)
+                den = den + fq @ np.asarray(z0[b, h], dtype=np.float64)
+            y[b, h] = _gate(num, den)
+    return y
+
+
+def final_state_mg(k, v, P, S0=None, z0=None):
+    """S_T = S0 + sum_s phi(k_s) v_s^T, z_T = z0 + sum_s phi(k_s) with the concatenated
+    feature of KATA-Mg; [B,H,g*p*p,dv] and [B,H,g*p*p]."""
+    k = np.asarray(k, dtype=np.float64); v = np.asarray(v, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = k.shape
+    G, p = P.shape[1], P.shape[2]
+    S = np.zeros((B, H, G * p * p, v.shape[-1]))
+    z = np.zeros((B, H, G * p * p))
+    for b in range(B):
+        for h in range(H):
+            W = factor_projections(k[b, h], P[h])
+            f = np.concatenate([feature_full(W[i]) for i in range(G)], axis=1)
+            S[b, h] = f.T @ v[b, h]
+            z[b, h] = f.sum(axis=0)
+    if S0 is not None:
+        S = S + S0
+        z = z + z0
+    return S, z
+
+
+def recurrence_mg(q, k, v, P):
+    """KATA-Mg by the token loop over the concatenated state (small inputs)."""
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = q.shape
+    G, p = P.shape[1], P.shape[2]
+    y = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((G * p * p, v.shape[-1]))
+            z = np.zeros(G * p * p)
+            for t in range(T):
+                fk = np.concatenate([np.outer(P[h, i] @ k[b, h, t], P[h, i] @ k[b, h, t]).ravel() for i in range(G)])
+                fq = np.concatenate([np.outer(P[h, i] @ q[b, h, t], P[h, i] @ q[b, h, t]).ravel() for i in range(G)])
+                S += np.outer(fk, v[b, h, t])
+                z += fk
+                den = fq @ z
+                y[b, h, t] = (fq @ S) / den if den != 0 else 0.0
+    return y
+
+
+def _feature_sum(X):
+    """vec(sum_i x_i x_i^T) for X [g, n, p] -> [n, p*p]."""
+    return sum(feature_full(X[i]) for i in range(X.shape[0]))
+
+
+def forward_sg_quadratic(q, k, v, P, S0=None, z0=None):
+    """KATA-Sigma-g by its O(T^2) definition.  P [H,g,p,d]; S0 [B,H,p*p,dv], z0 [B,H,p*p]
+    or None.  Returns y [B,H,T,dv]."""
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = q.shape
+    G = P.shape[1]
+    y = np.zeros(v.shape)
+    mask = np.tril(np.ones((T, T))) > 0
+    for b in range(B):
+        for h in range(H):
+            U = factor_projections(q[b, h], P[h])
+            W = factor_projections(k[b, h], P[h])
+            a = np.zeros((T, T))
+            for i in range(G):
+                for j in range(G):
+                    a += (U[i] @ W[j].T) ** 2
+            a = np.where(mask, a, 0.0)
+            num = a @ v[b, h]
+            den = a.sum(axis=1)
+            if S0 is not None:
+                fq = _feature_sum(U)
+                num = num + fq @ np.asarray(S0[b, h], dtype=np.float64)
+                den = den + fq @ np.asarray(z0[b, h], dtype=np.float64)
+            y[b, h] = _gate(num, den)
+    return y
+
+
+def final_state_sg(k, v, P, S0=None, z0=None):
+    """Final state of KATA-Sigma-g: S_T = S0 + sum_s vec(sum_i w_i w_i^T) v_s^T, z_T likewise."""
+    k = np.asarray(k, dtype=np.float64); v = np.asarray(v, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = k.shape
+    p = P.shape[2]
+    S = np.zeros((B, H, p * p, v.shape[-1]))
+    z = np.zeros((B, H, p * p))
+    for b in range(B):
+        for h in range(H):
+            f = _feature_sum(factor_projections(k[b, h], P[h]))
+            S[b, h] = f.T @ v[b, h]
+            z[b, h] = f.sum(axis=0)
+    if S0 is not None:
+        S = S + S0
+        z = z + z0
+    return S, z
+
+
+def recurrence_sg(q, k, v, P):
+    """KATA-Sigma-g by the token loop over the p*p state (small inputs)."""
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    B, H, T, _ = q.shape
+    G, p = P.shape[1], P.shape[2]
+    y = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((p * p, v.shape[-1]))
+            z = np.zeros(p * p)
+            for t in range(T):
+                Mk = sum(np.outer(P[h, i] @ k[b, h, t], P[h, i] @ k[b, h, t]) for i in range(G))
+                Mq = sum(np.outer(P[h, i] @ q[b, h, t], P[h, i] @ q[b, h, t]) for i in range(G))
+                S += np.outer(Mk.ravel(), v[b, h, t])
+                z += Mk.ravel()
+                den = Mq.ravel() @ z
+                y[b, h, t] = (Mq.ravel() @ S) / den if den != 0 else 0.0
+    return y

@@ -26,6 +26,7 @@ workload on the host's cores.
     python bench.py --backward   # the chunked-state backward on the long-context workload
     python bench.py --decay      # the decay-gated forward on the long-context workload
     python bench.py --decode --delta   # the DeltaKATA decode step (prefill by its recurrent forward)
+    python bench.py --factors 2  # KATA-M2 (two concatenated PSD factors) on the long-context workload
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -44,6 +45,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KATA causal fwd tokens/sec at T=131072 + % of MFMA/HBM peak (1 GPU)"
+MG_METRIC = ("KATA-M{g} (g={g} concatenated PSD factors) causal fwd tokens/sec at T=131072 "
+             "+ % of HBM peak (1 GPU)")
 DECAY_METRIC = "KATA decay-gated causal fwd tokens/sec at T=131072 + % of HBM peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
@@ -87,26 +90,27 @@ def recorded_traffic(fname: str, src: str, kernel: str):
         return None
 
 
-def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False):
+def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False, factors=1):
     """Bytes each kernel must move at minimum (per launch), by the byte model of the path
     (decay: the log-gates, 4 B per token-head, read by the state and intra kernels, and
-    one float per leaf)."""
+    one float per leaf; factors: g leaf states per leaf, the tokens still read once)."""
     E = 144 * dv + 256                    # packed leaf state block (S slots + Z), floats
-    states = B * H * n_leaf * E * 4
+    states = factors * B * H * n_leaf * E * 4
     tok = B * H * T
     g = tok * 4 if decay else 0
     gl = B * H * n_leaf * 4 if decay else 0
     return {
         "kata_chunk_state": tok * (d + dv) * in_bytes + states + g + gl,
-        "kata_state_scan": 2 * states + B * H * 256 * (dv + 1) * 4 + gl,
+        "kata_state_scan": 2 * states + factors * B * H * 256 * (dv + 1) * 4 + gl,
         "kata_chunk_intra": tok * (2 * d + dv) * in_bytes + states + tok * dv * out_bytes + g,
     }
 
 
-def algorithmic_flops(B, H, T, d, dv, C):
-    """Useful flops per launch (136 distinct packed features, causal half of the score tile)."""
+def algorithmic_flops(B, H, T, d, dv, C, factors=1):
+    """Useful flops per launch (136 distinct packed features, causal half of the score tile;
+    every PSD factor does the one-factor work)."""
     D = 136
-    tok = B * H * T
+    tok = B * H * T * factors
     proj = 2 * d * 16
     return {
         "kata_chunk_state": tok * (proj + 2 * D * (dv + 1)),
@@ -146,15 +150,15 @@ def cpu_baseline(case, stride):
     }
 
 
-def decay_cpu_baseline(case, lam, T_sample=8192):
-    """The oracle's O(T^2) decay-gated forward on the first T_sample tokens of 2 heads,
+def decay_cpu_baseline(case, lam, T_sample=16384, heads=8):
+    """The oracle's O(T^2) decay-gated forward on the first T_sample tokens of `heads` heads,
     extrapolated to the whole workload by its T^2 cost."""
     from threadpoolctl import threadpool_info
 
     from oracle import kata_oracle as O
     from kernelized_linear_attention_kata_amd import inputs as I
 
-    hs = slice(0, 2)
+    hs = slice(0, heads)
     q = O.bf16_bits_to_f64(I.bf16_bits(case.q[:, hs, :T_sample]))
     k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
     v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
@@ -163,11 +167,34 @@ def decay_cpu_baseline(case, lam, T_sample=8192):
     t0 = time.perf_counter()
     O.forward_decay_quadratic(q, k, v, P, lm)
     dt = time.perf_counter() - t0
-    scale = (case.T / T_sample) ** 2 * (case.H / 2)
+    scale = (case.T / T_sample) ** 2 * (case.H / heads)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 O(T^2) decay-gated oracle on the first {T_sample} tokens of 2 of {case.H} heads, "
+            "sample": (f"fp64 O(T^2) decay-gated oracle on the first {T_sample} tokens of {heads} of {case.H} heads, "
                        f"{dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the T^2 cost")}
+
+
+def mg_cpu_baseline(case, P, T_sample=16384, heads=8):
+    """The oracle's O(T^2) KATA-Mg forward on the first T_sample tokens of `heads` heads,
+    extrapolated to the whole workload by its T^2 cost."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    hs = slice(0, heads)
+    q = O.bf16_bits_to_f64(I.bf16_bits(case.q[:, hs, :T_sample]))
+    k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
+    v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
+    t0 = time.perf_counter()
+    O.forward_mg_quadratic(q, k, v, P[hs].double().cpu().numpy())
+    dt = time.perf_counter() - t0
+    scale = (case.T / T_sample) ** 2 * (case.H / heads)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 O(T^2) KATA-Mg oracle (g={P.shape[1]}) on the first {T_sample} tokens of {heads} of "
+                       f"{case.H} heads, {dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the "
+                       f"T^2 cost")}
 
 
 DELTA_DECODE_METRIC = ("DeltaKATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=16, dv=64), "
@@ -539,6 +566,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
+    ap.add_argument("--factors", type=int, default=1, choices=(1, 2, 3),
+                    help="KATA-Mg: time kata_forward_factors with this many concatenated PSD factors")
     ap.add_argument("--delta", action="store_true",
                     help="with --decode: the DeltaKATA decode step (prefill by kata_forward_delta)")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
@@ -589,10 +618,15 @@ def main():
     case = cases[0]
     B, H, T, d, dv, C = case.B, case.H, case.T, case.d, case.dv, args.chunk
     ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
-    if args.decay:
-        if C != 64:
-            print("bench.py --decay supports chunk 64 only", file=sys.stderr)
-            sys.exit(2)
+    G = args.factors
+    if (args.decay or G > 1) and C != 64:
+        print("bench.py --decay / --factors support chunk 64 only", file=sys.stderr)
+        sys.exit(2)
+    if G > 1:
+        Ps = [I.make_factor_projections(H, G, d, seed=seed0 + b, device=dev) for b in range(nb)]
+        ws_bytes = kata.forward_factors_workspace_bytes(B, H, T, G) // G
+        ws = torch.empty(G * ws_bytes, dtype=torch.uint8, device=dev)
+    elif args.decay:
         lams = [I.make_log_decay(B, H, T, seed=seed0 + b, device=dev) for b in range(nb)]
         wsd = kata.forward_decay_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
         ws = torch.empty(wsd, dtype=torch.uint8, device=dev)
@@ -607,6 +641,10 @@ def main():
 
     def step(i, events=None):
         c = cases[i % nb]
+        if G > 1:
+            kata.forward_factors(c.q, c.k, c.v, Ps[i % nb], "concat", chunk=C, y=ys[i % nb], workspace=ws,
+                                 stream=stream, events=events)
+            return
         if args.decay:
             kata.forward_decay(c.q, c.k, c.v, c.P, lams[i % nb], chunk=C, y=ys[i % nb], workspace=ws,
                                return_state=False, scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events)
@@ -645,8 +683,8 @@ def main():
                   for j, name in enumerate(KERNELS)}
 
     tokens_per_s = B * T / (ms_per_step / 1e3)
-    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay)
-    aflops = algorithmic_flops(B, H, T, d, dv, C)
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=G)
+    aflops = algorithmic_flops(B, H, T, d, dv, C, factors=G)
     dominant = max(per_kernel, key=per_kernel.get)
     kernels = {}
     for name in KERNELS:
@@ -667,13 +705,13 @@ def main():
         try:
             cnt = json.load(open(COUNTERS_FILE))
             entry = cnt.get("kernels", {}).get(dominant)
-            if cnt.get("source_hash") == src and entry and cnt.get("chunk") == C and not args.decay:
+            if cnt.get("source_hash") == src and entry and cnt.get("chunk") == C and not args.decay and G == 1:
                 traffic = entry["hbm_bytes_per_launch"]
         except (ValueError, KeyError):
             traffic = None
 
     result = {
-        "metric": DECAY_METRIC if args.decay else METRIC,
+        "metric": MG_METRIC.format(g=G) if G > 1 else (DECAY_METRIC if args.decay else METRIC),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -685,7 +723,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
-        "config": {"workload": (f"long-context KATA forward{' with decay gates in [0.9, 1] (fp32 log-gates)' if args.decay else ''}: "
+        "config": {"workload": (f"long-context KATA{f'-M{G}' if G > 1 else ''} forward"
+                                f"{' with decay gates in [0.9, 1] (fp32 log-gates)' if args.decay else ''}"
+                                f"{f' with {G} concatenated PSD factors (P [16,{G},16,64], no state export)' if G > 1 else ''}: "
                                 f"B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, fp32 P/state, chunk {C}, "
                                 f"{args.scan} scan over {n_leaf} leaf states per head"),
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": C, "batches_cycled": nb,
@@ -698,7 +738,12 @@ def main():
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
     }
     if not args.no_cpu_baseline:
-        cb = decay_cpu_baseline(case, lams[0], args.cpu_stride) if args.decay else cpu_baseline(case, args.cpu_stride)
+        if G > 1:
+            cb = mg_cpu_baseline(case, Ps[0])
+        elif args.decay:
+            cb = decay_cpu_baseline(case, lams[0])
+        else:
+            cb = cpu_baseline(case, args.cpu_stride)
         result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(result), flush=True)
 

@@ -263,6 +263,39 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p,
                              const void* q, const void* k, const void* v,
                              const float* P, void* y, void* stream);
 
+/* KATA-Mg and KATA-Sigma-g: g PSD factors per head.  [TS-2.3] (item "Variantes") names
+ * "several PSD factors" (Mg) and "summed PSD factors" (Sigma-g), trading state size
+ * against packing efficiency, and [TS-4] quotes the chunked-state kernel of KATA-M2;
+ * none defines how the factors combine.  Reading taken, with u_i = P_i x, w_i = P_i k:
+ *   KATA_FACTORS_CONCAT (Mg): phi(x) = [vec(u_1 u_1^T); ...; vec(u_g u_g^T)],
+ *       a_ts = sum_i (u_i,t . w_i,s)^2, state g*p*p x dv (the g one-factor states stacked)
+ *   KATA_FACTORS_SUM (Sigma-g): phi(x) = vec(sum_i u_i u_i^T),
+ *       a_ts = sum_i sum_j (u_i,t . w_j,s)^2, state p*p x dv
+ * and y_t = sum_s a_ts v_s / sum_s a_ts as for KATA; g = 1 is KATA in both modes. */
+typedef enum { KATA_FACTORS_CONCAT = 0, KATA_FACTORS_SUM = 1 } kata_factor_mode;
+
+/* Bytes of workspace kata_forward_factors needs (g times the one-factor leaf states). */
+kata_status kata_forward_factors_workspace_bytes(const kata_forward_desc* desc, int g,
+                                                 kata_factor_mode mode, size_t* bytes);
+
+/* The causal forward with g PSD factors in the chunked-state form.
+ *   q, k [B,H,T,d], v [B,H,T,dv] in_dtype; P [H,g,p,d] float32 (factor-major per head);
+ *   S0 [B,H,g*p*p,dv], z0 [B,H,g*p*p] float32 (CONCAT; factor i's rows i*p*p ..) or NULL;
+ *   y [B,H,T,dv]; ST, zT in the layout of S0, z0, or NULL; workspace as returned above.
+ * Supported: g = 1 with everything kata_forward supports (it runs kata_forward); g = 2 or 3
+ * with KATA_FACTORS_CONCAT, d = dv = 64, chunk 64, in_dtype BF16, B*H*g <= 65535.  Other
+ * values return KATA_ERR_UNSUPPORTED.  kata_forward_factors_timed stamps the events of
+ * kata_forward_timed (state pass over the B*H*g factor states, scan, intra pass). */
+kata_status kata_forward_factors(const kata_forward_desc* desc, int g, kata_factor_mode mode,
+                                 const void* q, const void* k, const void* v, const float* P,
+                                 const float* S0, const float* z0, void* y, float* ST, float* zT,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+kata_status kata_forward_factors_timed(const kata_forward_desc* desc, int g, kata_factor_mode mode,
+                                       const void* q, const void* k, const void* v, const float* P,
+                                       const float* S0, const float* z0, void* y, float* ST, float* zT,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       void* const* events);
+
 /* DeltaKATA.  [TS-4] (repeated-key overwrite) credits the delta-rule variant of KATA with
  * correcting stale bindings when a key is written again, and [TS-1] / [ABS] name delta
  * rules among the mechanisms studied with KATA's features; none defines it.  The reading

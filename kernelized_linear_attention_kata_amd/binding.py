@@ -99,6 +99,12 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
     lib.kata_decode_step_decay.restype = ci
     lib.kata_decode_step_decay.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_forward_factors_workspace_bytes.restype = ci
+    lib.kata_forward_factors_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ci, ci, ctypes.POINTER(sz)]
+    lib.kata_forward_factors_timed.restype = ci
+    lib.kata_forward_factors_timed.argtypes = [ctypes.POINTER(ForwardDesc), ci, ci] + [vp] * 10 + [sz, vp, vp]
+    lib.kata_forward_factors.restype = ci
+    lib.kata_forward_factors.argtypes = [ctypes.POINTER(ForwardDesc), ci, ci] + [vp] * 10 + [sz, vp]
     lib.kata_forward_delta.restype = ci
     lib.kata_forward_delta.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9
     lib.kata_decode_step_delta.restype = ci
@@ -328,6 +334,77 @@ def decode_step_decay(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torc
                                        _stream_handle(stream, dev))
     _check(st, "kata_decode_step_decay")
     return y
+
+
+FACTOR_MODES = {"concat": 0, "sum": 1}
+
+
+def forward_factors_workspace_bytes(B, H, T, g, mode="concat", d=64, dv=64, chunk=64, in_dtype=torch.bfloat16,
+                                    out_dtype=None) -> int:
+    """Workspace bytes of kata_forward_factors for these sizes."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_forward_factors_workspace_bytes(ctypes.byref(desc), g, FACTOR_MODES[mode], ctypes.byref(n)),
+           "kata_forward_factors_workspace_bytes")
+    return int(n.value)
+
+
+def forward_factors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, mode: str = "concat",
+                    chunk: int = 64, *, S0: Optional[torch.Tensor] = None, z0: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, return_state: bool = False,
+                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                    events=None):
+    """KATA with g PSD factors per head (kata_forward_factors): mode "concat" (KATA-Mg,
+    a_ts = sum_i (u_i.w_i)^2, state g*256 x dv) or "sum" (KATA-Sigma-g).  P: [H, g, 16, d]
+    fp32.  Returns y, or (y, ST, zT) when return_state (ST [B,H,g*256,dv] for concat)."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    g = P.shape[1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, g, P_DIM, d), torch.float32, dev)
+    rows = (g if mode == "concat" else 1) * P_DIM * P_DIM
+    if (S0 is None) != (z0 is None):
+        raise ValueError("S0 and z0 go together")
+    if S0 is not None:
+        _need(S0, "S0", (B, H, rows, dv), torch.float32, dev)
+        _need(z0, "z0", (B, H, rows), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    _check(lib.kata_forward_factors_workspace_bytes(ctypes.byref(desc), g, FACTOR_MODES[mode], ctypes.byref(n)),
+           "kata_forward_factors_workspace_bytes")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    ST = zT = None
+    if return_state:
+        ST = torch.empty((B, H, rows, dv), dtype=torch.float32, device=dev)
+        zT = torch.empty((B, H, rows), dtype=torch.float32, device=dev)
+    sh = _stream_handle(stream, dev)
+    evarr = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_forward_factors_timed(ctypes.byref(desc), g, FACTOR_MODES[mode], _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(P), _ptr(S0), _ptr(z0), _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
+                                        ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
+    _check(st, "kata_forward_factors")
+    return (y, ST, zT) if return_state else y
 
 
 def forward_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,

@@ -531,7 +531,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const bf16
 // grid (n_leaf, B*H), block 256.  Writes the leaf's summed packed state to ws.  DECAY:
 // lam [B*H, T] log-decays; each token's contribution is weighted by the decay from it to
 // the leaf's end, and the leaf's total decay exp(sum lam) goes to dec[bh * n_leaf + leaf].
-template <class S, typename TIn, bool DECAY = false>
+// G > 1 (KATA-Mg, several concatenated PSD factors): grid (n_leaf, B*H*G), P [H, G, p, d];
+// the workgroup of virtual head vh = bh*G + i builds factor i's state of sequence bh into
+// ws row vh (the state of each factor is that of one-factor KATA with P_i).
+template <class S, typename TIn, bool DECAY = false, int G = 1>
 __global__ void __launch_bounds__(256, S::OCC_STATE)
 kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
                  float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks,
@@ -545,7 +548,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   float* es = reinterpret_cast<float*>(smem + S::SMEM_STATE);   // DECAY: key weights
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = blockIdx.y / G;     // sequence; blockIdx.y is the workspace row
   const int h = (int)(bh % H);
   const int64_t leaf = blockIdx.x;
   const int64_t c0 = leaf * leaf_chunks;
@@ -555,7 +558,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   if constexpr (DECAY) rl = make_rsrc(lam + base_tok, T * 4);
   float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the leaf's end
 
-  if (wave == 0) write_P<S>(Pf, P, h, lane);
+  if (wave == 0) write_P<S>(Pf, P, G == 1 ? h : h * G + (int)(blockIdx.y % G), lane);
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
@@ -604,7 +607,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   for (int i = 0; i + 1 < DEPTH; ++i)   // fewer than DEPTH chunks left: static buffer index
     if (c + i < nch) step(buf[i], c + i);
   // write the leaf state (tile-native layout) and Z
-  float* out = ws + (bh * (int64_t)gridDim.x + leaf) * S::E;
+  float* out = ws + ((int64_t)blockIdx.y * gridDim.x + leaf) * S::E;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int delta = wave + 4 * j;
@@ -619,7 +622,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   }
   if (wave == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + lane * 4) = st.Z;
   if constexpr (DECAY) {
-    if (tid == 0) dec[bh * (int64_t)gridDim.x + leaf] = fdec;
+    if (tid == 0) dec[(int64_t)blockIdx.y * gridDim.x + leaf] = fdec;
   }
 }
 
@@ -862,6 +865,150 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   }
 }
 
+// ---- the same three steps, separated -------------------------------------------------
+// chunk_outputs above fuses, for one PSD factor, the prefix readout, the intra tile and the
+// gate.  With several concatenated PSD factors (KATA-Mg) every factor adds its readout and
+// its intra tile to one output tile and one denominator before the single division, so
+// the steps are also available separately (same arithmetic, same fragment layouts).
+
+// Inter-chunk readout of token t = 16 mb + lane % 16 through the published state:
+// O^T += H^T phi(Q)^T, and den += phi(q_t) . z = u_t^T Z u_t (den = ... when FIRST).
+template <class S, bool FIRST>
+__device__ __forceinline__ void readout_acc(int t, const float* Us, const bf16* hx_hi, const bf16* hx_lo,
+                                            const bf16* Zs, int lane, f32x4 (&O)[S::NB], float& den) {
+  const int g = lane >> 4;
+  // rotated quads of u_t: Q[m] = u_t[4*((g+m)&3) .. +3]
+  f32x4 Q[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) Q[m] = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * ((g + m) & 3));
+  auto u_rot = [&](int delta, int i) -> float {   // u_t[(4g + i + delta) & 15]
+    const int m = delta >> 2, e = delta & 3;
+    const int j = i + e;
+    return j < 4 ? Q[m & 3][j] : Q[(m + 1) & 3][j - 4];
+  };
+  // query-side weights folded into u_a: 1 on the diagonal, 2 off it, and for the
+  // diagonal delta = 8 only the 8 distinct slots a < 8 (lane groups g < 2) count
+  f32x4 ua1 = Q[0], ua2, ua8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ua2[i] = 2.f * Q[0][i];
+    ua8[i] = g < 2 ? ua2[i] : 0.f;
+  }
+#pragma unroll
+  for (int kb = 0; kb < READ_KB; ++kb) {
+    float x[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int delta = 2 * kb + half;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (delta <= 8) {
+          const f32x4& ua = delta == 0 ? ua1 : (delta == 8 ? ua8 : ua2);
+          x[half * 4 + i] = ua[i] * u_rot(delta, i);
+        } else {
+          x[half * 4 + i] = 0.f;
+        }
+      }
+    }
+    const Op8<S::SPLIT> qf = make8<S::SPLIT>(x);
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) {
+      const int idx = ((kb * S::NB + nb) * WAVE + lane) * 8;
+      Op8<S::SPLIT> hf;
+      hf.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
+      if constexpr (S::SPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
+      O[nb] = mma<S::SPLIT, S::SPLIT>(hf, qf, O[nb]);
+    }
+  }
+  // (Z U^T)[4g + r][t] from one 16x16x16 MFMA (Z symmetric, so its accumulator tile is
+  // its own A fragment), dotted with u_t[4g..4g+3]
+  const bf16x8 zz = *reinterpret_cast<const bf16x8*>(Zs + lane * 8);
+  Op4<true> zf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    zf.hi[i] = zz[i];
+    zf.lo[i] = zz[4 + i];
+  }
+  float uv[4] = {Q[0][0], Q[0][1], Q[0][2], Q[0][3]};
+  const f32x4 zu = mma<true, true>(zf, make4<true>(uv), zero4());
+  const float zd = zu[0] * Q[0][0] + zu[1] * Q[0][1] + zu[2] * Q[0][2] + zu[3] * Q[0][3];
+  if constexpr (FIRST) den = zd;
+  else den += zd;
+}
+
+// Intra-chunk part of M-block mb: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds
+// X[s = 4g + r][t]; the masked squares (times exp(l_t - l_s) under DECAY) add to den and,
+// through O^T += V^T (A^2 masked)^T, to the output tile.
+template <class S, bool DECAY>
+__device__ __forceinline__ void intra_acc(int mb, int t, const float* Us, const float* Ws, const bf16* vf_hi,
+                                          const bf16* vf_lo, int lane, float lt, const float* ls,
+                                          f32x4 (&O)[S::NB], float& den) {
+  const int n = lane & 15, g = lane >> 4;
+  const f32x4 ub = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * g);
+  float ubv[4] = {ub[0], ub[1], ub[2], ub[3]};
+  const Op4<S::SPLIT> uf = make4<S::SPLIT>(ubv);
+  f32x4 A2[S::NMB];
+#pragma unroll
+  for (int j = 0; j < S::NMB; ++j) {
+    A2[j] = zero4();
+    if (j <= mb) {
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(Ws + (j * 16 + n) * S::USTR + 4 * g);
+      float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
+      const f32x4 X = mma<S::SPLIT, S::SPLIT>(make4<S::SPLIT>(wbv), uf, zero4());
+      if (j < mb) {   // wave-uniform: only the diagonal tile is masked
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] = X[r] * X[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] = (4 * g + r <= n) ? X[r] * X[r] : 0.f;
+      }
+      if constexpr (DECAY) {   // weight exp(l_t - l_s) of key s = 16j + 4g + r
+        const f32x4 lsv = *reinterpret_cast<const f32x4*>(ls + j * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] *= __expf(fminf(lt - lsv[r], 0.f));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) den += A2[j][r];
+    }
+  }
+  // O^T += V^T (A^2 masked)^T: K-block jj = score tiles 2jj (slots 0..3), 2jj+1 (slots 4..7)
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) {
+    if (2 * jj <= mb) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = A2[2 * jj][i];
+        x[4 + i] = (2 * jj + 1 < S::NMB) ? A2[2 * jj + 1][i] : 0.f;
+      }
+      const Op8<S::SPLIT> af = make8<S::SPLIT>(x);
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb)
+        O[nb] = mma<S::SPLIT, S::SPLIT>(load_vf<S>(vf_hi, vf_lo, jj, nb, lane), af, O[nb]);
+    }
+  }
+}
+
+// Output gate of token t: den summed over the 4 lane groups (each permlane swap
+// exchanges rows between its two outputs, whose sum is the pair sum in every lane),
+// y = O / den (0 where the denominator is 0; v_rcp_f32 is within 1 ulp).
+template <class S, typename TOut>
+__device__ __forceinline__ void gate_store(const f32x4 (&O)[S::NB], float den, const SeqRsrc& rs, int t0, int t,
+                                           int lane) {
+  const int g = lane >> 4;
+  den = row_pair_sum<16>(den);
+  den = row_pair_sum<32>(den);
+  const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
+  const int row = (t0 + t) * S::DV + 4 * g;
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) {
+    f32x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = O[nb][r] * inv;
+    Store4<TOut>::st(rs.y, (row + nb * 16) * (int)sizeof(TOut), o);
+  }
+}
+
 // grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.  DECAY:
 // lam [B*H, T] log-decays (see the decay-gate notes above).
 template <class S, typename TIn, typename TOut, bool DECAY = false>
@@ -951,6 +1098,146 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     }
     __syncthreads();
     if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
+  }
+}
+
+// ---- KATA-Mg: g concatenated PSD factors ----------------------------------------------
+// The feature is [vec(u_1 u_1^T); ...; vec(u_g u_g^T)] with u_i = P_i x (several PSD
+// factors, item "Variantes" of section 2.3 of the gist.science summary; the factors'
+// combination is not defined there and is read as concatenation), so a_ts =
+// sum_i (u_i,t . w_i,s)^2 and the state is the g one-factor states stacked.
+
+// The projections of the chunk's q and k through one factor (stage_chunk without V).
+template <class S, typename TIn>
+__device__ __forceinline__ void stage_proj(const ChunkIn<S, TIn>& r, const bf16* Pf, float* Us, float* Ws,
+                                           float* Wacc, bf16* Wz, int tw, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  ProjP<S> pp;
+  read_P<S>(pp, Pf, lane);
+#pragma unroll
+  for (int m = 0; m < S::MBW; ++m) {
+    const int mb = tw + 4 * m;
+    if (mb < S::NMB) {
+      const f32x4 w = project_tile<S, TIn>(r.k[m], pp);
+      *reinterpret_cast<f32x4*>(Wacc + (mb * WAVE + lane) * 4) = w;
+      {
+        float wv[4] = {w[0], w[1], w[2], w[3]};
+        const Op4<true> wz = make4<true>(wv);
+        const int idx = ((mb >> 1) * WAVE + lane) * 8 + (mb & 1) * 4;
+        *reinterpret_cast<bf16x4*>(Wz + idx) = wz.hi;
+        *reinterpret_cast<bf16x4*>(Wz + S::NJ * WAVE * 8 + idx) = wz.lo;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ws[(mb * 16 + 4 * g + i) * S::USTR + n] = w[i];
+      const f32x4 u = project_tile<S, TIn>(r.q[m], pp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Us[(mb * 16 + 4 * g + i) * S::USTR + n] = u[i];
+    }
+  }
+}
+
+// LDS of the Mg intra kernel: the one-factor layout plus the P fragments of the other
+// factors after it.
+template <class S, int G>
+struct MgLayout {
+  static constexpr int SMEM = S::SMEM + (G - 1) * S::PF_BYTES;
+  static constexpr int PF_ELEMS = S::PF_BYTES / 2;   // bf16 elements per factor's fragments
+};
+
+// grid (n_leaf, B*H), block 256.  ws [B*H*G, n_leaf, E]: row bh*G + i holds factor i's
+// exclusive leaf prefix (kata_chunk_state<..., G> then kata_state_scan over B*H*G rows).
+// Per chunk: V is staged once; then, factor by factor, the projections through P_i are
+// staged, factor i's prefix state is published and read out, its intra tile is added to
+// the same output tile and denominator, and its state is advanced; the gate divides
+// once at the end.  Two barriers per factor and chunk.
+template <class S, typename TIn, typename TOut, int G>
+__global__ void __launch_bounds__(256, 2)
+kata_chunk_intra_mg(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                    const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
+                    int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+  using L = MgLayout<S, G>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
+  bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
+  bf16* hx_hi = reinterpret_cast<bf16*>(smem + S::OFF_HX);
+  bf16* hx_lo = reinterpret_cast<bf16*>(smem + S::OFF_HX + S::HX_BYTES);
+  float* Us = reinterpret_cast<float*>(smem + S::OFF_U);
+  float* Ws = reinterpret_cast<float*>(smem + S::OFF_W);
+  float* Wacc = reinterpret_cast<float*>(smem + S::OFF_WACC);
+  bf16* Wz = reinterpret_cast<bf16*>(smem + S::OFF_WZ);
+  bf16* Zs = reinterpret_cast<bf16*>(smem + S::OFF_Z);
+  bf16* Pf = reinterpret_cast<bf16*>(smem + S::OFF_PF);      // G factors, PF_ELEMS apart
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t leaf = blockIdx.x;
+  const int64_t c0 = leaf * leaf_chunks;
+  const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
+  const int64_t base_tok = bh * T;
+
+  for (int i = tid; i < S::NB * WAVE; i += 256) {   // readout K-block 4, slots 4..7: zero
+    const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
+    *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  }
+  const int tw = wave;
+  const bool zrole = wave == 0;
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) write_P<S>(Pf + i * L::PF_ELEMS, P, h * G + i, lane);
+  }
+  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
+  StateAcc<S> st[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    load_state<S>(st[i], ws + ((bh * G + i) * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+
+  SeqRsrc rs;
+  rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.k = make_rsrc(k + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.v = make_rsrc(v + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TIn));
+  rs.y = make_rsrc(y + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TOut));
+  const int tc0 = (int)(c0 * S::C);
+  ChunkIn<S, TIn> cur;
+  load_chunk<S, TIn, true>(cur, rs, tc0, tw, lane);
+  __syncthreads();   // P fragments written
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = tc0 + c * S::C;
+    const bool more = c + 1 < nch;
+    progress_priority(c, nch);
+    f32x4 O[S::MBW][S::NB];
+    float den[S::MBW];
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m) {
+      den[m] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) O[m][nb] = zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i == 0) stage_chunk<S, TIn, true>(cur, Pf, sel, Us, Ws, Wacc, Wz, vf_hi, vf_lo, tw, lane);
+      else stage_proj<S, TIn>(cur, Pf + i * L::PF_ELEMS, Us, Ws, Wacc, Wz, tw, lane);
+      if (i == G - 1 && more) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, tw, lane);
+      publish_state<S>(st[i], hx_hi, hx_lo, Zs, wave, zrole, lane);
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < S::MBW; ++m) {
+        const int mb = tw + 4 * m;
+        if (mb < S::NMB) {
+          const int t = mb * 16 + (lane & 15);
+          readout_acc<S, false>(t, Us, hx_hi, hx_lo, Zs, lane, O[m], den[m]);
+          intra_acc<S, false>(mb, t, Us, Ws, vf_hi, vf_lo, lane, 0.f, nullptr, O[m], den[m]);
+        }
+      }
+      if (more) state_update<S>(st[i], Wacc, Wz, vf_hi, vf_lo, wave, zrole, lane);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m) {
+      const int mb = tw + 4 * m;
+      if (mb < S::NMB) gate_store<S, TOut>(O[m], den[m], rs, t0, mb * 16 + (lane & 15), lane);
+    }
   }
 }
 

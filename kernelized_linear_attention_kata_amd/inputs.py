@@ -210,6 +210,18 @@ def make_beta(*shape: int, seed: int = 0, lo: float = 0.5, hi: float = 1.0, devi
     return lo + (hi - lo) * torch.rand(shape, generator=g, device=device, dtype=torch.float32)
 
 
+def make_factor_projections(H: int, g: int, d: int = 64, seed: int = 0, per_head: bool = False,
+                            device="cpu") -> torch.Tensor:
+    """Seeded projections of g PSD factors, P [H, g, 16, d] float32 with entries N(0, 1/d)
+    (each factor drawn like the one projection of the one-factor workloads); one set shared
+    by all heads unless per_head."""
+    gen = _gen(5000 + seed, device)
+    std = 1.0 / d ** 0.5
+    if per_head:
+        return _normal((H, g, P_DIM, d), std, gen, device)
+    return _normal((1, g, P_DIM, d), std, gen, device).expand(H, g, P_DIM, d).contiguous()
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw uint16 bit patterns of a bfloat16 tensor, as a numpy array on the host."""
     assert t.dtype == torch.bfloat16

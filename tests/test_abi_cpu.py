@@ -267,3 +267,44 @@ def test_delta_forward_and_decode_validation():
     assert lib.kata_decode_step_delta(4, 16, 64, 64, 12, 1, 0, *args, fake, None) == Bd.KATA_ERR_UNSUPPORTED
     assert lib.kata_decode_step_delta(-1, 16, 64, 64, 16, 1, 0, *args, fake, None) == Bd.KATA_ERR_SHAPE
     assert lib.kata_decode_step_delta(0, 16, 64, 64, 16, 1, 0, *([None] * 6), None, None) == Bd.KATA_OK
+
+
+def test_factor_forward_workspace_and_validation():
+    """kata_forward_factors: g = 1 is the plain forward (same workspace), g = 2, 3 with the
+    concatenated factors need g times the one-factor leaf states; unsupported shapes,
+    modes and factor counts are rejected on the host."""
+    lib = _lib_or_skip()
+    n = ctypes.c_size_t(0)
+    plain = ctypes.c_size_t(0)
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_forward_workspace_bytes(ctypes.byref(d), ctypes.byref(plain)) == Bd.KATA_OK
+    assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), 1, 0, ctypes.byref(n)) == Bd.KATA_OK
+    assert n.value == plain.value
+    assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), 1, 1, ctypes.byref(n)) == Bd.KATA_OK
+    assert n.value == plain.value
+    E = 144 * 64 + 256
+    for g in (2, 3):
+        assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), g, 0, ctypes.byref(n)) == Bd.KATA_OK
+        per = n.value // g
+        assert n.value == g * per and per % (16 * E * 4) == 0
+    fake = ctypes.c_void_p(0x1000)
+    for g, mode, status in [(0, 0, Bd.KATA_ERR_SHAPE), (4, 0, Bd.KATA_ERR_UNSUPPORTED), (2, 2, Bd.KATA_ERR_UNSUPPORTED)]:
+        assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), g, mode, ctypes.byref(n)) == status
+    for fields in [{"d": 16, "dv": 16}, {"chunk": 128}, {"in_dtype": Bd.KATA_F32}]:
+        bad = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        for field, value in fields.items():
+            setattr(bad, field, value)
+        assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(bad), 2, 0, ctypes.byref(n)) == \
+            Bd.KATA_ERR_UNSUPPORTED, fields
+        # one factor is plain KATA, which supports these
+        assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(bad), 1, 0, ctypes.byref(n)) == Bd.KATA_OK
+    big = Bd.make_desc(1, 40000, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(big), 2, 0, ctypes.byref(n)) == Bd.KATA_ERR_SHAPE
+    good = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    args = [fake] * 4
+    assert lib.kata_forward_factors(ctypes.byref(good), 2, 0, *args, fake, None, fake, None, None, fake,
+                                    16, None) == Bd.KATA_ERR_NULL                      # S0 without z0
+    assert lib.kata_forward_factors(ctypes.byref(good), 2, 0, *args, None, None, fake, None, None, fake,
+                                    16, None) == Bd.KATA_ERR_WORKSPACE
+    assert lib.kata_forward_factors(ctypes.byref(good), 2, 0, fake, fake, fake, None, None, None, fake, None,
+                                    None, fake, 1 << 40, None) == Bd.KATA_ERR_NULL      # P missing

@@ -47,6 +47,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KATA causal fwd tokens/sec at T=131072 + % of MFMA/HBM peak (1 GPU)"
 MG_METRIC = ("KATA-M{g} (g={g} concatenated PSD factors) causal fwd tokens/sec at T=131072 "
              "+ % of HBM peak (1 GPU)")
+SG_METRIC = ("KATA-Sigma{g} (g={g} summed PSD factors) causal fwd tokens/sec at T=131072 "
+             "+ % of HBM peak (1 GPU)")
 DECAY_METRIC = "KATA decay-gated causal fwd tokens/sec at T=131072 + % of HBM peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
@@ -106,17 +108,18 @@ def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False, 
     }
 
 
-def algorithmic_flops(B, H, T, d, dv, C, factors=1):
+def algorithmic_flops(B, H, T, d, dv, C, factors=1, cross=False):
     """Useful flops per launch (136 distinct packed features, causal half of the score tile;
-    every PSD factor does the one-factor work)."""
+    every PSD factor does the one-factor work; cross: the summed factors' g*g score tiles)."""
     D = 136
     tok = B * H * T * factors
     proj = 2 * d * 16
+    tiles = factors if cross else 1
     return {
         "kata_chunk_state": tok * (proj + 2 * D * (dv + 1)),
         "kata_state_scan": 0,
         "kata_chunk_intra": tok * (2 * proj + 2 * D * (dv + 1) + 2 * D * (dv + 1)
-                                   + (C + 1) * (16 + dv + 1)),
+                                   + tiles * (C + 1) * (16 + dv + 1)),
     }
 
 
@@ -174,9 +177,9 @@ def decay_cpu_baseline(case, lam, T_sample=16384, heads=8):
                        f"{dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the T^2 cost")}
 
 
-def mg_cpu_baseline(case, P, T_sample=16384, heads=8):
-    """The oracle's O(T^2) KATA-Mg forward on the first T_sample tokens of `heads` heads,
-    extrapolated to the whole workload by its T^2 cost."""
+def mg_cpu_baseline(case, P, T_sample=16384, heads=8, summed=False):
+    """The oracle's O(T^2) KATA-Mg (or, summed, KATA-Sigma-g) forward on the first T_sample
+    tokens of `heads` heads, extrapolated to the whole workload by its T^2 cost."""
     from threadpoolctl import threadpool_info
 
     from oracle import kata_oracle as O
@@ -187,12 +190,13 @@ def mg_cpu_baseline(case, P, T_sample=16384, heads=8):
     k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
     v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
     t0 = time.perf_counter()
-    O.forward_mg_quadratic(q, k, v, P[hs].double().cpu().numpy())
+    (O.forward_sg_quadratic if summed else O.forward_mg_quadratic)(q, k, v, P[hs].double().cpu().numpy())
     dt = time.perf_counter() - t0
     scale = (case.T / T_sample) ** 2 * (case.H / heads)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 O(T^2) KATA-Mg oracle (g={P.shape[1]}) on the first {T_sample} tokens of {heads} of "
+            "sample": (f"fp64 O(T^2) KATA-{'Sigma-g' if summed else 'Mg'} oracle (g={P.shape[1]}) on the first "
+                       f"{T_sample} tokens of {heads} of "
                        f"{case.H} heads, {dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} by the "
                        f"T^2 cost")}
 
@@ -568,6 +572,8 @@ def main():
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
     ap.add_argument("--factors", type=int, default=1, choices=(1, 2, 3),
                     help="KATA-Mg: time kata_forward_factors with this many concatenated PSD factors")
+    ap.add_argument("--factor-mode", default="concat", choices=("concat", "sum"),
+                    help="with --factors: concatenated (KATA-Mg) or summed (KATA-Sigma-g) factors")
     ap.add_argument("--delta", action="store_true",
                     help="with --decode: the DeltaKATA decode step (prefill by kata_forward_delta)")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
@@ -624,8 +630,9 @@ def main():
         sys.exit(2)
     if G > 1:
         Ps = [I.make_factor_projections(H, G, d, seed=seed0 + b, device=dev) for b in range(nb)]
-        ws_bytes = kata.forward_factors_workspace_bytes(B, H, T, G) // G
-        ws = torch.empty(G * ws_bytes, dtype=torch.uint8, device=dev)
+        wsf = kata.forward_factors_workspace_bytes(B, H, T, G, args.factor_mode)
+        ws_bytes = wsf // G if args.factor_mode == "concat" else wsf
+        ws = torch.empty(wsf, dtype=torch.uint8, device=dev)
     elif args.decay:
         lams = [I.make_log_decay(B, H, T, seed=seed0 + b, device=dev) for b in range(nb)]
         wsd = kata.forward_decay_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
@@ -642,7 +649,7 @@ def main():
     def step(i, events=None):
         c = cases[i % nb]
         if G > 1:
-            kata.forward_factors(c.q, c.k, c.v, Ps[i % nb], "concat", chunk=C, y=ys[i % nb], workspace=ws,
+            kata.forward_factors(c.q, c.k, c.v, Ps[i % nb], args.factor_mode, chunk=C, y=ys[i % nb], workspace=ws,
                                  stream=stream, events=events)
             return
         if args.decay:
@@ -683,8 +690,11 @@ def main():
                   for j, name in enumerate(KERNELS)}
 
     tokens_per_s = B * T / (ms_per_step / 1e3)
-    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=G)
-    aflops = algorithmic_flops(B, H, T, d, dv, C, factors=G)
+    sg = G > 1 and args.factor_mode == "sum"
+    fac_word = "summed" if sg else "concatenated"
+    fac_note = f" with {G} {fac_word} PSD factors (P [16,{G},16,64], no state export)" if G > 1 else ""
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=1 if sg else G)
+    aflops = algorithmic_flops(B, H, T, d, dv, C, factors=G, cross=sg)
     dominant = max(per_kernel, key=per_kernel.get)
     kernels = {}
     for name in KERNELS:
@@ -711,7 +721,8 @@ def main():
             traffic = None
 
     result = {
-        "metric": MG_METRIC.format(g=G) if G > 1 else (DECAY_METRIC if args.decay else METRIC),
+        "metric": ((SG_METRIC if sg else MG_METRIC).format(g=G) if G > 1
+                   else (DECAY_METRIC if args.decay else METRIC)),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -723,9 +734,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
-        "config": {"workload": (f"long-context KATA{f'-M{G}' if G > 1 else ''} forward"
+        "config": {"workload": (f"long-context KATA{(f'-Sigma{G}' if sg else f'-M{G}') if G > 1 else ''} forward"
                                 f"{' with decay gates in [0.9, 1] (fp32 log-gates)' if args.decay else ''}"
-                                f"{f' with {G} concatenated PSD factors (P [16,{G},16,64], no state export)' if G > 1 else ''}: "
+                                f"{fac_note}: "
                                 f"B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, fp32 P/state, chunk {C}, "
                                 f"{args.scan} scan over {n_leaf} leaf states per head"),
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": C, "batches_cycled": nb,
@@ -739,7 +750,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         if G > 1:
-            cb = mg_cpu_baseline(case, Ps[0])
+            cb = mg_cpu_baseline(case, Ps[0], summed=sg)
         elif args.decay:
             cb = decay_cpu_baseline(case, lams[0])
         else:

@@ -363,17 +363,16 @@ kata_status launch_delta(int64_t BH, int64_t T, int H, int d, int dv, kata_dtype
   return launch_status();
 }
 
-// ---- KATA-Mg (several concatenated PSD factors) ------------------------------------------
-// Supported for g > 1: p = 16, d = dv = 64, chunk 64, bf16 q/k/v, f32 or bf16 y, g <= 3,
-// KATA_FACTORS_CONCAT.  g = 1 is one-factor KATA in both modes and runs the plain forward
-// (P [H,1,p,d] is P [H,p,d]).  Workspace: g times the one-factor leaf states.
+// ---- KATA-Mg / KATA-Sigma-g (several PSD factors, concatenated or summed) ----------------
+// Supported for g > 1: p = 16, d = dv = 64, chunk 64, bf16 q/k/v, f32 or bf16 y, g <= 3.
+// g = 1 is one-factor KATA in both modes and runs the plain forward (P [H,1,p,d] is
+// P [H,p,d]).  Workspace: CONCAT g times the one-factor leaf states, SUM the one-factor's.
 constexpr int kMaxFactors = 3;
 
-template <int G>
-int64_t mg_slots() {
-  using S = Shape<64, 64, 64, false>;
-  const int64_t by_lds = kLdsPerCU / kata::MgLayout<S, G>::SMEM;
-  const int64_t per_cu = by_lds < 2 ? by_lds : 2;
+template <int SMEM>
+int64_t slots_by_lds() {
+  const int64_t by_lds = kLdsPerCU / SMEM;
+  const int64_t per_cu = by_lds < 2 ? by_lds : 2;   // the factor kernels run at most 2 per CU
   return kComputeUnits * (per_cu < 1 ? 1 : per_cu);
 }
 
@@ -383,15 +382,18 @@ kata_status validate_factors(const kata_forward_desc* d, int g, kata_factor_mode
   if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
   if (g < 1) return KATA_ERR_SHAPE;
   if (g == 1) return KATA_OK;
-  if (mode != KATA_FACTORS_CONCAT || g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
+  if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
   if (d->d != 64 || d->dv != 64 || d->chunk != 64 || d->in_dtype != KATA_BF16) return KATA_ERR_UNSUPPORTED;
   if (d->B * d->H * g > 65535) return KATA_ERR_SHAPE;
   return KATA_OK;
 }
 
-Plan factors_plan(const kata_forward_desc* d, int g) {
+Plan factors_plan(const kata_forward_desc* d, int g, kata_factor_mode mode) {
+  using S = Shape<64, 64, 64, false>;
   if (g <= 1) return make_plan(d);
-  Plan p = make_plan(d, g == 2 ? mg_slots<2>() : mg_slots<3>());
+  if (mode == KATA_FACTORS_SUM)
+    return make_plan(d, g == 2 ? slots_by_lds<kata::SgLayout<S, 2>::SMEM>() : slots_by_lds<kata::SgLayout<S, 3>::SMEM>());
+  Plan p = make_plan(d, g == 2 ? slots_by_lds<kata::MgLayout<S, 2>::SMEM>() : slots_by_lds<kata::MgLayout<S, 3>::SMEM>());
   p.ws_bytes *= (size_t)g;
   return p;
 }
@@ -419,6 +421,33 @@ kata_status run_forward_mg(const kata_forward_desc* d, const Plan& pl, const voi
   hipExtLaunchKernelGGL((kata_chunk_intra_mg<S, TIn, TOut, G>), dim3((unsigned)pl.n_leaf, (unsigned)bh), dim3(256),
                         smem_intra, st, e2, e3, 0, (const TIn*)q, (const TIn*)k, (const TIn*)v, P,
                         (const float*)ws, (TOut*)y, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
+  return launch_status();
+}
+
+template <class S, typename TIn, typename TOut, int G>
+kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const void* q, const void* k,
+                           const void* v, const float* P, const float* S0, const float* z0, void* y,
+                           float* ST, float* zT, float* ws, hipStream_t st, hipEvent_t* ev) {
+  const int64_t bh = d->B * d->H;
+  constexpr int smem_state = kata::SgStateLayout<S, G>::SMEM;
+  constexpr int smem_intra = kata::SgLayout<S, G>::SMEM;
+  if (allow_smem(kata_chunk_state<S, TIn, false, G, true>, smem_state) != KATA_OK ||
+      allow_smem(kata_chunk_intra_sg<S, TIn, TOut, G>, smem_intra) != KATA_OK)
+    return KATA_ERR_LAUNCH;
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+  const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
+  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, false, G, true>), grid, dim3(256), smem_state, st, e0, nullptr, 0,
+                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks,
+                        (const float*)nullptr, (float*)nullptr);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  const int segs = scan_segments(pl);
+  hipExtLaunchKernelGGL(kata_state_scan, scan_grid(pl, segs, bh), dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf,
+                        (int)pl.E, (int)S::DV, segs, S0, z0, ST, zT, 0, 0, (const float*)nullptr);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL((kata_chunk_intra_sg<S, TIn, TOut, G>), grid, dim3(256), smem_intra, st, e2, e3, 0,
+                        (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
+                        (int)d->H, (int)pl.leaf, pl.n_chunks);
   return launch_status();
 }
 
@@ -733,7 +762,7 @@ kata_status kata_forward_factors_workspace_bytes(const kata_forward_desc* desc, 
   if (!bytes) return KATA_ERR_NULL;
   const kata_status s = validate_factors(desc, g, mode);
   if (s != KATA_OK) return s;
-  *bytes = factors_plan(desc, g).ws_bytes;
+  *bytes = factors_plan(desc, g, mode).ws_bytes;
   return KATA_OK;
 }
 
@@ -747,13 +776,13 @@ kata_status kata_forward_factors_timed(const kata_forward_desc* desc, int g, kat
     return kata_forward_timed(desc, q, k, v, P, S0, z0, y, ST, zT, workspace, workspace_bytes, stream, events);
   if ((S0 == nullptr) != (z0 == nullptr)) return KATA_ERR_NULL;
   if ((ST == nullptr) != (zT == nullptr)) return KATA_ERR_NULL;
-  const Plan pl = factors_plan(desc, g);
+  const Plan pl = factors_plan(desc, g, mode);
   const int64_t bh = desc->B * desc->H;
   hipStream_t st = (hipStream_t)stream;
   if (bh == 0) return KATA_OK;
-  if (desc->T == 0) {   // the state export of g stacked factors is the one-factor export of B*H*g rows
+  if (desc->T == 0) {   // CONCAT: the export of g stacked factor states is that of B*H*g rows
     kata_forward_desc dd = *desc;
-    dd.H = desc->H * g;
+    if (mode == KATA_FACTORS_CONCAT) dd.H = desc->H * g;
     return copy_initial_state(&dd, S0, z0, ST, zT, st);
   }
   if (!q || !k || !v || !P || !y) return KATA_ERR_NULL;
@@ -771,6 +800,13 @@ kata_status kata_forward_factors_timed(const kata_forward_desc* desc, int g, kat
   float* ws = (float*)workspace;
   using S = Shape<64, 64, 64, false>;
   const bool fo = desc->out_dtype == KATA_F32;
+  if (mode == KATA_FACTORS_SUM) {
+    if (g == 2)
+      return fo ? run_forward_sg<S, bf16, float, 2>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp)
+                : run_forward_sg<S, bf16, bf16, 2>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);
+    return fo ? run_forward_sg<S, bf16, float, 3>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp)
+              : run_forward_sg<S, bf16, bf16, 3>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);
+  }
   if (g == 2)
     return fo ? run_forward_mg<S, bf16, float, 2>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp)
               : run_forward_mg<S, bf16, bf16, 2>(desc, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, evp);

@@ -534,7 +534,39 @@ __device__ __forceinline__ void stage_chunk(const ChunkIn<S, TIn>& r, const bf16
 // G > 1 (KATA-Mg, several concatenated PSD factors): grid (n_leaf, B*H*G), P [H, G, p, d];
 // the workgroup of virtual head vh = bh*G + i builds factor i's state of sequence bh into
 // ws row vh (the state of each factor is that of one-factor KATA with P_i).
-template <class S, typename TIn, bool DECAY = false, int G = 1>
+// G > 1 with SUMG (KATA-Sigma-g, summed PSD factors): grid (n_leaf, B*H); the workgroup adds
+// the key features of all G factors into the same accumulators (their state is the sum of
+// the factor states), so k and v are read once; the extra factors' key tiles and P
+// fragments sit after the one-factor LDS (SgStateLayout).
+template <class S, int G>
+struct SgStateLayout {
+  static constexpr int XB = S::WACC_BYTES + S::WZ_BYTES + S::PF_BYTES;   // per extra factor
+  static constexpr int SMEM = S::SMEM_STATE + (G - 1) * XB;
+  static __device__ __forceinline__ int off(int i) { return S::SMEM_STATE + (i - 1) * XB; }
+};
+
+// The key projections of one more factor (stage_chunk's key part, without V).
+template <class S, typename TIn>
+__device__ __forceinline__ void stage_keys(const ChunkIn<S, TIn>& r, const bf16* Pf, float* Wacc, bf16* Wz, int tw,
+                                           int lane) {
+  ProjP<S> pp;
+  read_P<S>(pp, Pf, lane);
+#pragma unroll
+  for (int m = 0; m < S::MBW; ++m) {
+    const int mb = tw + 4 * m;
+    if (mb < S::NMB) {
+      const f32x4 w = project_tile<S, TIn>(r.k[m], pp);
+      *reinterpret_cast<f32x4*>(Wacc + (mb * WAVE + lane) * 4) = w;
+      float wv[4] = {w[0], w[1], w[2], w[3]};
+      const Op4<true> wz = make4<true>(wv);
+      const int idx = ((mb >> 1) * WAVE + lane) * 8 + (mb & 1) * 4;
+      *reinterpret_cast<bf16x4*>(Wz + idx) = wz.hi;
+      *reinterpret_cast<bf16x4*>(Wz + S::NJ * WAVE * 8 + idx) = wz.lo;
+    }
+  }
+}
+
+template <class S, typename TIn, bool DECAY = false, int G = 1, bool SUMG = false>
 __global__ void __launch_bounds__(256, S::OCC_STATE)
 kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
                  float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks,
@@ -548,7 +580,9 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   float* es = reinterpret_cast<float*>(smem + S::SMEM_STATE);   // DECAY: key weights
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.y / G;     // sequence; blockIdx.y is the workspace row
+  static_assert(!(DECAY && G > 1), "decay gates with one PSD factor only");
+  constexpr int VG = SUMG ? 1 : G;        // workspace rows per sequence
+  const int64_t bh = blockIdx.y / VG;    // sequence; blockIdx.y is the workspace row
   const int h = (int)(bh % H);
   const int64_t leaf = blockIdx.x;
   const int64_t c0 = leaf * leaf_chunks;
@@ -558,7 +592,15 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   if constexpr (DECAY) rl = make_rsrc(lam + base_tok, T * 4);
   float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the leaf's end
 
-  if (wave == 0) write_P<S>(Pf, P, G == 1 ? h : h * G + (int)(blockIdx.y % G), lane);
+  if (wave == 0) write_P<S>(Pf, P, G == 1 ? h : (SUMG ? h * G : h * G + (int)(blockIdx.y % G)), lane);
+  if constexpr (SUMG) {
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 1; i < G; ++i)
+        write_P<S>(reinterpret_cast<bf16*>(smem + SgStateLayout<S, G>::off(i) + S::WACC_BYTES + S::WZ_BYTES), P,
+                   h * G + i, lane);
+    }
+  }
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
   StateAcc<S> st;
   state_zero<S>(st);
@@ -584,6 +626,14 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   __syncthreads();   // P fragments written
   auto step = [&](ChunkIn<S, TIn>& cur, int c) {
     stage_chunk<S, TIn, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf_hi, vf_lo, wave, lane);
+    if constexpr (SUMG) {
+#pragma unroll
+      for (int i = 1; i < G; ++i) {
+        unsigned char* xb = smem + SgStateLayout<S, G>::off(i);
+        stage_keys<S, TIn>(cur, reinterpret_cast<const bf16*>(xb + S::WACC_BYTES + S::WZ_BYTES),
+                           reinterpret_cast<float*>(xb), reinterpret_cast<bf16*>(xb + S::WACC_BYTES), wave, lane);
+      }
+    }
     load_chunk<S, TIn, false>(cur, rs, c + DEPTH < nch ? chunk_t0(c + DEPTH) : (int)T, wave, lane);
     if constexpr (DECAY) {
       float Lc;
@@ -596,6 +646,14 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
     __syncthreads();
     if constexpr (DECAY) state_update_decay<S>(st, Wacc, es, vf_hi, vf_lo, wave, wave == 0, lane);
     else state_update<S>(st, Wacc, Wz, vf_hi, vf_lo, wave, wave == 0, lane);
+    if constexpr (SUMG) {
+#pragma unroll
+      for (int i = 1; i < G; ++i) {
+        unsigned char* xb = smem + SgStateLayout<S, G>::off(i);
+        state_update<S>(st, reinterpret_cast<const float*>(xb), reinterpret_cast<const bf16*>(xb + S::WACC_BYTES),
+                        vf_hi, vf_lo, wave, wave == 0, lane);
+      }
+    }
     __syncthreads();
   };
   int c = 0;
@@ -1238,6 +1296,129 @@ kata_chunk_intra_mg(const TIn* __restrict__ q, const TIn* __restrict__ k, const 
       const int mb = tw + 4 * m;
       if (mb < S::NMB) gate_store<S, TOut>(O[m], den[m], rs, t0, mb * 16 + (lane & 15), lane);
     }
+  }
+}
+
+// ---- KATA-Sigma-g: g summed PSD factors -------------------------------------------------
+// The feature is vec(sum_i u_i u_i^T) (summed PSD factors, item "Variantes" of section 2.3
+// of the gist.science summary; read as the sum of the rank-one factors), so the state is
+// one p*p x dv state (the sum of the factor states), the readout is sum_i phi(u_i)^T H, the
+// denominator's state part sum_i u_i^T Z u_i, and a_ts = sum_i sum_j (u_i,t . w_j,s)^2.
+
+// LDS of the Sigma-g intra kernel: the one-factor layout, then per extra factor its u and
+// w rows, key tiles, hi/lo key fragments and P fragments.
+template <class S, int G>
+struct SgLayout {
+  static constexpr int XB = 2 * S::U_BYTES + S::WACC_BYTES + S::WZ_BYTES + S::PF_BYTES;
+  static constexpr int SMEM = S::SMEM + (G - 1) * XB;
+  static __device__ __forceinline__ int off(int i) { return S::SMEM + (i - 1) * XB; }
+};
+
+// grid (n_leaf, B*H), block 256.  ws [B*H, n_leaf, E]: the exclusive leaf prefix of the
+// summed state (kata_chunk_state<..., G, true> then kata_state_scan).  Per chunk: V and the
+// projections of all factors are staged, the state (published at the end of the previous
+// chunk) is read out through every factor's query feature, the g*g score tiles of all
+// factor pairs are added, the gate divides, and every factor's keys update the state.
+template <class S, typename TIn, typename TOut, int G>
+__global__ void __launch_bounds__(256, 2)
+kata_chunk_intra_sg(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                    const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
+                    int64_t T, int H, int leaf_chunks, int64_t n_chunks) {
+  using L = SgLayout<S, G>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
+  bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
+  bf16* hx_hi = reinterpret_cast<bf16*>(smem + S::OFF_HX);
+  bf16* hx_lo = reinterpret_cast<bf16*>(smem + S::OFF_HX + S::HX_BYTES);
+  bf16* Zs = reinterpret_cast<bf16*>(smem + S::OFF_Z);
+  float* Us[G];
+  float* Ws[G];
+  float* Wacc[G];
+  bf16* Wz[G];
+  bf16* Pf[G];
+  Us[0] = reinterpret_cast<float*>(smem + S::OFF_U);
+  Ws[0] = reinterpret_cast<float*>(smem + S::OFF_W);
+  Wacc[0] = reinterpret_cast<float*>(smem + S::OFF_WACC);
+  Wz[0] = reinterpret_cast<bf16*>(smem + S::OFF_WZ);
+  Pf[0] = reinterpret_cast<bf16*>(smem + S::OFF_PF);
+#pragma unroll
+  for (int i = 1; i < G; ++i) {
+    unsigned char* xb = smem + L::off(i);
+    Us[i] = reinterpret_cast<float*>(xb);
+    Ws[i] = reinterpret_cast<float*>(xb + S::U_BYTES);
+    Wacc[i] = reinterpret_cast<float*>(xb + 2 * S::U_BYTES);
+    Wz[i] = reinterpret_cast<bf16*>(xb + 2 * S::U_BYTES + S::WACC_BYTES);
+    Pf[i] = reinterpret_cast<bf16*>(xb + 2 * S::U_BYTES + S::WACC_BYTES + S::WZ_BYTES);
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t leaf = blockIdx.x;
+  const int64_t c0 = leaf * leaf_chunks;
+  const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
+  const int64_t base_tok = bh * T;
+
+  for (int i = tid; i < S::NB * WAVE; i += 256) {   // readout K-block 4, slots 4..7: zero
+    const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
+    *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  }
+  const int tw = wave;
+  const bool zrole = wave == 0;
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) write_P<S>(Pf[i], P, h * G + i, lane);
+  }
+  const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
+  StateAcc<S> st;
+  load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
+
+  SeqRsrc rs;
+  rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.k = make_rsrc(k + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
+  rs.v = make_rsrc(v + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TIn));
+  rs.y = make_rsrc(y + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TOut));
+  const int tc0 = (int)(c0 * S::C);
+  ChunkIn<S, TIn> cur;
+  load_chunk<S, TIn, true>(cur, rs, tc0, tw, lane);
+  __syncthreads();   // P fragments written
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = tc0 + c * S::C;
+    const bool more = c + 1 < nch;
+    progress_priority(c, nch);
+    stage_chunk<S, TIn, true>(cur, Pf[0], sel, Us[0], Ws[0], Wacc[0], Wz[0], vf_hi, vf_lo, tw, lane);
+#pragma unroll
+    for (int i = 1; i < G; ++i) stage_proj<S, TIn>(cur, Pf[i], Us[i], Ws[i], Wacc[i], Wz[i], tw, lane);
+    if (more) load_chunk<S, TIn, true>(cur, rs, t0 + S::C, tw, lane);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m) {
+      const int mb = tw + 4 * m;
+      if (mb < S::NMB) {
+        const int t = mb * 16 + (lane & 15);
+        f32x4 O[S::NB];
+#pragma unroll
+        for (int nb = 0; nb < S::NB; ++nb) O[nb] = zero4();
+        float den = 0.f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) readout_acc<S, false>(t, Us[i], hx_hi, hx_lo, Zs, lane, O, den);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+            intra_acc<S, false>(mb, t, Us[i], Ws[j], vf_hi, vf_lo, lane, 0.f, nullptr, O, den);
+        }
+        gate_store<S, TOut>(O, den, rs, t0, t, lane);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) state_update<S>(st, Wacc[i], Wz[i], vf_hi, vf_lo, wave, zrole, lane);
+    }
+    __syncthreads();
+    if (more) publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
   }
 }
 

@@ -287,8 +287,11 @@ def test_factor_forward_workspace_and_validation():
         assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), g, 0, ctypes.byref(n)) == Bd.KATA_OK
         per = n.value // g
         assert n.value == g * per and per % (16 * E * 4) == 0
+        assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), g, 1, ctypes.byref(n)) == Bd.KATA_OK
+        assert n.value % (16 * E * 4) == 0 and n.value < g * per        # Sigma-g: one summed state
     fake = ctypes.c_void_p(0x1000)
-    for g, mode, status in [(0, 0, Bd.KATA_ERR_SHAPE), (4, 0, Bd.KATA_ERR_UNSUPPORTED), (2, 2, Bd.KATA_ERR_UNSUPPORTED)]:
+    for g, mode, status in [(0, 0, Bd.KATA_ERR_SHAPE), (4, 0, Bd.KATA_ERR_UNSUPPORTED), (4, 1, Bd.KATA_ERR_UNSUPPORTED),
+                            (2, 2, Bd.KATA_ERR_UNSUPPORTED)]:
         assert lib.kata_forward_factors_workspace_bytes(ctypes.byref(d), g, mode, ctypes.byref(n)) == status
     for fields in [{"d": 16, "dv": 16}, {"chunk": 128}, {"in_dtype": Bd.KATA_F32}]:
         bad = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)

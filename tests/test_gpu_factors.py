@@ -143,3 +143,119 @@ def test_mg_long_prefix_and_final_state():
     print(f"[mg long] y prefix {ey:.3e} S_T {eS:.3e} z_T {ez:.3e}", flush=True)
     assert ey <= TOL and eS <= TOL and ez <= TOL
     assert torch.all(torch.isfinite(y.float()))
+
+
+# ---- KATA-Sigma-g (summed PSD factors) ----------------------------------------------------
+
+def run_sg(case, P, **kw):
+    q, k, v = (t.to(DEV) for t in (case.q, case.k, case.v))
+    out = kata.forward_factors(q, k, v, P.to(DEV), "sum", **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("g", [2, 3])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300, 1000])
+def test_sg_against_oracle(g, T):
+    case = I.make_forward("mid", B=2, H=3, T=T, seed=100 + T)
+    P = I.make_factor_projections(3, g, seed=50 + T + g, per_head=True)
+    y = run_sg(case, P, out_dtype=torch.float32).double().cpu().numpy()
+    ref = O.forward_sg_quadratic(host64(case.q), host64(case.k), host64(case.v), P.double().numpy())
+    e = row_rel(y, ref)
+    print(f"[sg g={g} T={T}] rel y {e:.3e}", flush=True)
+    assert e <= TOL
+
+
+def test_sg_state_in_and_out():
+    g = 2
+    P = I.make_factor_projections(2, g, seed=101, per_head=True)
+    pre = I.make_forward("mid", B=2, H=2, T=150, seed=101)
+    S0, z0 = O.final_state_sg(host64(pre.k), host64(pre.v), P.double().numpy())
+    case = I.make_forward("mid", B=2, H=2, T=700, seed=102)
+    S0t, z0t = torch.from_numpy(S0).float().to(DEV), torch.from_numpy(z0).float().to(DEV)
+    y, ST, zT = run_sg(case, P, S0=S0t, z0=z0t, return_state=True)
+    args = (host64(case.q), host64(case.k), host64(case.v), P.double().numpy())
+    ref = O.forward_sg_quadratic(*args, S0, z0)
+    Sref, zref = O.final_state_sg(*args[1:], S0, z0)
+    ey = row_rel(y.double().cpu().numpy(), ref)
+    eS = slice_rel(ST.double().cpu().numpy(), Sref)
+    ez = slice_rel(zT.double().cpu().numpy(), zref)
+    print(f"[sg state] y {ey:.3e} S_T {eS:.3e} z_T {ez:.3e}", flush=True)
+    assert ey <= TOL and eS <= TOL and ez <= TOL
+
+
+def test_sg_state_is_sum_of_factor_states():
+    """The Sigma-g state equals the sum of the g one-factor states (same data)."""
+    g = 3
+    case = I.make_forward("mid", B=1, H=4, T=2000, seed=103)
+    P = I.make_factor_projections(4, g, seed=103, per_head=True)
+    _, ST, zT = run_sg(case, P, out_dtype=torch.float32, return_state=True)
+    q, k, v = (t.to(DEV) for t in (case.q, case.k, case.v))
+    S_sum = torch.zeros_like(ST)
+    z_sum = torch.zeros_like(zT)
+    for i in range(g):
+        _, S1, z1 = kata.forward(q, k, v, P[:, i].contiguous().to(DEV), chunk=64, return_state=True)
+        S_sum += S1
+        z_sum += z1
+    torch.cuda.synchronize()
+    eS = float((ST.double() - S_sum.double()).norm() / S_sum.double().norm())
+    ez = float((zT.double() - z_sum.double()).norm() / z_sum.double().norm())
+    assert eS <= 1e-5 and ez <= 1e-5, (eS, ez)
+
+
+def test_sg_factor_mixing_invariance():
+    """y depends on the factors only through sum_i P_i^T P_i-type products: mixing the
+    factors by an orthogonal g x g matrix leaves y unchanged (the cross terms must be
+    right for this to hold)."""
+    g = 2
+    case = I.make_forward("mid", B=1, H=2, T=1500, seed=104)
+    P = I.make_factor_projections(2, g, seed=104, per_head=True)
+    c, s_ = np.cos(0.7), np.sin(0.7)
+    R = torch.tensor([[c, -s_], [s_, c]], dtype=torch.float32)
+    Pm = torch.einsum("ji,hjab->hiab", R, P).contiguous()
+    y = run_sg(case, P, out_dtype=torch.float32)
+    ym = run_sg(case, Pm, out_dtype=torch.float32)
+    e = float((y.double() - ym.double()).norm() / y.double().norm())
+    print(f"[sg mixing] {e:.2e}", flush=True)
+    assert e <= 5e-3
+
+
+def test_sg_equal_factors_is_one_factor():
+    """g equal factors give weights g^2 (u.w)^2, which the gate cancels."""
+    case = I.make_forward("mid", B=2, H=2, T=1500, seed=105)
+    P1 = I.make_factor_projections(2, 1, seed=105, per_head=True)
+    P = P1.expand(2, 2, 16, 64).contiguous()
+    y = run_sg(case, P, out_dtype=torch.float32)
+    q, k, v = (t.to(DEV) for t in (case.q, case.k, case.v))
+    y1 = kata.forward(q, k, v, P1[:, 0].contiguous().to(DEV), chunk=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    e = float((y.double() - y1.double()).norm() / y1.double().norm())
+    print(f"[sg equal factors] {e:.2e}", flush=True)
+    assert e <= 1e-3
+
+
+def test_sg_lm340m_workload():
+    case = I.make_forward("lm340m", B=2, H=4, T=512, seed=106)
+    P = I.make_factor_projections(4, 2, seed=106, per_head=True)
+    y = run_sg(case, P).double().cpu().numpy()
+    ref = O.forward_sg_quadratic(host64(case.q), host64(case.k), host64(case.v), P.double().numpy())
+    e = row_rel(y, ref)
+    print(f"[sg lm340m] rel y {e:.3e}", flush=True)
+    assert e <= TOL
+
+
+def test_sg_long_prefix_and_final_state():
+    T = 131072
+    case = I.make_forward("long", T=T, seed=107)
+    P = I.make_factor_projections(16, 2, seed=107)
+    y, ST, zT = run_sg(case, P, return_state=True)
+    m = 2048
+    ref = O.forward_sg_quadratic(host64(case.q[:, :, :m]), host64(case.k[:, :, :m]), host64(case.v[:, :, :m]),
+                                 P.double().numpy())
+    ey = row_rel(y[:, :, :m].double().cpu().numpy(), ref)
+    Sref, zref = O.final_state_sg(host64(case.k), host64(case.v), P.double().numpy())
+    eS = slice_rel(ST.double().cpu().numpy(), Sref)
+    ez = slice_rel(zT.double().cpu().numpy(), zref)
+    print(f"[sg long] y prefix {ey:.3e} S_T {eS:.3e} z_T {ez:.3e}", flush=True)
+    assert ey <= TOL and eS <= TOL and ez <= TOL
+    assert torch.all(torch.isfinite(y.float()))

@@ -711,7 +711,11 @@ def main():
     achieved = abytes[dominant] / (per_kernel[dominant] / 1e3) / 1e9
     traffic = None
     src = source_hash()
-    if os.path.exists(COUNTERS_FILE):
+    if G > 1:
+        # the factor paths' host code lies past the forward's part of kata.hip: hash all of it
+        traffic = recorded_traffic(f"hbm_counters_{'sigma' if sg else 'm'}{G}.json",
+                                   source_hash(("kata_chunk.h",)), dominant)
+    elif os.path.exists(COUNTERS_FILE):
         try:
             cnt = json.load(open(COUNTERS_FILE))
             entry = cnt.get("kernels", {}).get(dominant)

@@ -26,6 +26,7 @@ workload on the host's cores.
     python bench.py --backward   # the chunked-state backward on the long-context workload
     python bench.py --decay      # the decay-gated forward on the long-context workload
     python bench.py --decode --delta   # the DeltaKATA decode step (prefill by its recurrent forward)
+    python bench.py --delta      # the DeltaKATA forward, chunked form, on the long-context workload
     python bench.py --factors 2  # KATA-M2 (two concatenated PSD factors) on the long-context workload
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
@@ -423,6 +424,124 @@ def bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+DELTA_FWD_METRIC = ("DeltaKATA causal fwd tokens/sec at T=131072, chunked (WY) form (1 GPU)")
+
+
+def delta_cpu_baseline(case, beta, T_sample=16384, heads=2):
+    """The oracle's DeltaKATA token recurrence on the first T_sample tokens of `heads` heads,
+    extrapolated linearly (the recurrence costs the same per token)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    hs = slice(0, heads)
+    q = O.bf16_bits_to_f64(I.bf16_bits(case.q[:, hs, :T_sample]))
+    k = O.bf16_bits_to_f64(I.bf16_bits(case.k[:, hs, :T_sample]))
+    v = O.bf16_bits_to_f64(I.bf16_bits(case.v[:, hs, :T_sample]))
+    t0 = time.perf_counter()
+    O.delta_recurrence(q, k, v, case.P[hs].double().cpu().numpy(), beta[:, hs, :T_sample].double().cpu().numpy())
+    dt = time.perf_counter() - t0
+    scale = (case.T / T_sample) * (case.H / heads)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": case.B * case.T / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 DeltaKATA token-recurrence oracle on the first {T_sample} tokens of {heads} of "
+                       f"{case.H} heads, {dt:.1f} s measured; whole-workload time extrapolated x{scale:.0f} "
+                       f"(linear in T)")}
+
+
+def bench_delta_forward(args):
+    """DeltaKATA forward on the long-context workload: the chunked form timed per kernel
+    (events from the launches), the token-recurrent form timed once beside it."""
+    import torch
+    import kernelized_linear_attention_kata_amd as kata
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nb = max(1, args.batches)
+    seed0 = I.WORKLOADS["long"]["seed"]
+    cases = [I.make_forward("long", device=dev, seed=seed0 + b) for b in range(nb)]
+    betas = [I.make_beta(c.B, c.H, c.T, seed=seed0 + b, device=dev) for b, c in enumerate(cases)]
+    case = cases[0]
+    B, H, T, d, dv = case.B, case.H, case.T, case.d, case.dv
+    wsb = kata.forward_delta_chunked_workspace_bytes(B, H, T, d, dv)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        c = cases[i % nb]
+        kata.forward_delta_chunked(c.q, c.k, c.v, c.P, betas[i % nb], y=ys[i % nb], workspace=ws, stream=stream,
+                                   events=events)
+
+    settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - settle0 < args.settle_s:
+        step(n_settle)
+        n_settle += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [t_start, t_end] + [e for es in evs for e in es]:
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    walk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    # the token-recurrent form once, for comparison
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    kata.forward_delta(case.q, case.k, case.v, case.P, betas[0], y=ys[0], stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    rec_ms = r0.elapsed_time(r1)
+    tok = B * H * T
+    n_chunks = (T + 63) // 64
+    prep_bytes = tok * (2 * d * 2 + 4) + tok * 2 * 16 * 4 + B * H * n_chunks * 64 * 64 * 4
+    walk_bytes = tok * (2 * 16 * 4 + dv * 2 + 4 + dv * 2) + B * H * n_chunks * 64 * 64 * 4
+    # useful walk flops per chunk and 16-column block: K^S and Q^S (2 x 64x256x16), T X (64x64x16),
+    # the causal score tile (64x64x16 / 2) times E (64x64x16 / 2), K^^T E (256x64x16); x2 per MAC
+    walk_flops = B * H * n_chunks * (dv // 16) * 2 * (2 * 64 * 256 * 16 + 64 * 64 * 16 + 64 * 64 * 16 + 256 * 64 * 16)
+    walk_tflops = walk_flops / (walk_ms / 1e3) / 1e12
+    result = {
+        "metric": DELTA_FWD_METRIC, "value": B * T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 q/k/v/y, f32 state (hi/lo bf16 MFMA products)",
+        "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
+        "config": {"workload": (f"long-context DeltaKATA forward: B={B} H={H} T={T} d=dv={d} p=16, beta uniform in "
+                                f"[0.5, 1], chunk 64 ({n_chunks} chunks per head walked in order by {dv // 16} "
+                                f"workgroups per head)"),
+                   "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
+        "roofline": {"bound": "mfma", "kernel": "kata_delta_chunk", "achieved": round(walk_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(walk_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+                     "traffic": None, "note": ("the walk is a dependency chain over the chunks of one sequence with "
+                                               f"{B * H * (dv // 16)} workgroups: bound by per-chunk latency, "
+                                               "not by either peak")},
+        "kernels": {"kata_delta_prep": {"ms": round(prep_ms, 4), "alg_bytes": prep_bytes,
+                                        "alg_GBps": round(prep_bytes / (prep_ms / 1e3) / 1e9, 1)},
+                    "kata_delta_chunk": {"ms": round(walk_ms, 4), "alg_bytes": walk_bytes,
+                                         "alg_GBps": round(walk_bytes / (walk_ms / 1e3) / 1e9, 1),
+                                         "alg_TFLOPs": round(walk_tflops, 2),
+                                         "us_per_chunk": round(walk_ms * 1e3 / n_chunks, 3)}},
+        "recurrent_form": {"kernel": "kata_delta_recurrent", "ms": round(rec_ms, 3),
+                           "tokens_per_s": B * T / (rec_ms / 1e3)},
+        "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = delta_cpu_baseline(case, betas[0])
+    print(json.dumps(result), flush=True)
+
+
+
 BWD_METRIC = ("KATA causal backward (dq, dk, dv, dP) tokens/sec at T=131072, chunked-state form "
               "+ % of HBM peak (1 GPU)")
 BWD_KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_bwd_query", "kata_bwd_rstate", "kata_state_scan(rev)",
@@ -575,7 +694,8 @@ def main():
     ap.add_argument("--factor-mode", default="concat", choices=("concat", "sum"),
                     help="with --factors: concatenated (KATA-Mg) or summed (KATA-Sigma-g) factors")
     ap.add_argument("--delta", action="store_true",
-                    help="with --decode: the DeltaKATA decode step (prefill by kata_forward_delta)")
+                    help="the DeltaKATA forward (chunked form) on the long-context workload; with --decode the "
+                         "DeltaKATA decode step (prefill by kata_forward_delta)")
     ap.add_argument("--flash", action="store_true", help="time the flash-style O(T^2) forward instead")
     ap.add_argument("--backward", action="store_true", help="time the chunked-state backward instead")
     ap.add_argument("--decay", action="store_true",
@@ -604,6 +724,9 @@ def main():
 
     if args.decode:
         bench_decode(args)
+        return
+    if args.delta:
+        bench_delta_forward(args)
         return
     if args.flash:
         bench_flash(args)

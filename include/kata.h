@@ -320,6 +320,30 @@ kata_status kata_forward_delta(const kata_forward_desc* desc,
                                const float* P, const float* beta, const float* S0,
                                void* y, float* ST, void* stream);
 
+/* DeltaKATA causal forward in the chunked (WY) form, for few long sequences: chunks of 64
+ * tokens; per chunk T = (I + tril(diag(beta) K^K^^T, -1))^{-1} over the chunk's unit key
+ * features K^ (formed for all chunks in parallel), then, walking the chunks in order,
+ * E = T diag(beta)(V - K^ S), Y = Q^ S + (Q^K^^T o M) E (M: s <= t), S += K^^T E.  Same
+ * definition and arguments as kata_forward_delta (exactly equal up to rounding), plus a
+ * device workspace of kata_forward_delta_chunked_workspace_bytes bytes (normalised
+ * projections and T per chunk: 9 KiB per 64 tokens and head), owned by the caller.
+ * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S).
+ * Supported: p = 16, (d, dv) = (16, 16) or (64, 64), desc->chunk = 64, in/out dtype F32
+ * or BF16, B*H <= 65535.  kata_forward_delta_chunked_timed stamps three caller-created
+ * events: start of the per-chunk pass, start and end of the walk. */
+kata_status kata_forward_delta_chunked_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+kata_status kata_forward_delta_chunked(const kata_forward_desc* desc,
+                                       const void* q, const void* k, const void* v,
+                                       const float* P, const float* beta, const float* S0,
+                                       void* y, float* ST, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+kata_status kata_forward_delta_chunked_timed(const kata_forward_desc* desc,
+                                             const void* q, const void* k, const void* v,
+                                             const float* P, const float* beta, const float* S0,
+                                             void* y, float* ST, void* workspace,
+                                             size_t workspace_bytes, void* stream,
+                                             void* const* events);
+
 /* One DeltaKATA decode step for N independent streams (same reading), in place:
  *   S <- S + beta phi^(k) (v - S^T phi^(k))^T,  y = S^T phi^(q)  (after the update)
  *   S [N,H,p*p,dv] float32; q, k [N,H,d], v [N,H,dv] in_dtype; P [H,p,d] float32;

@@ -8,7 +8,8 @@ missing.
 """
 _BINDING_NAMES = (
     "KataError", "abi_version", "backward", "backward_workspace_bytes", "decode_step", "decode_step_decay", "decode_step_delta",
-    "forward_decay", "forward_decay_workspace_bytes", "forward_delta", "forward_factors",
+    "forward_decay", "forward_decay_workspace_bytes", "forward_delta", "forward_delta_chunked",
+    "forward_delta_chunked_workspace_bytes", "forward_factors",
     "forward_factors_workspace_bytes", "feature_map", "flash_forward", "flash_workspace_bytes",
     "forward", "forward_workspace_bytes", "library_path", "load_library",
 )

@@ -105,6 +105,12 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_factors_timed.argtypes = [ctypes.POINTER(ForwardDesc), ci, ci] + [vp] * 10 + [sz, vp, vp]
     lib.kata_forward_factors.restype = ci
     lib.kata_forward_factors.argtypes = [ctypes.POINTER(ForwardDesc), ci, ci] + [vp] * 10 + [sz, vp]
+    lib.kata_forward_delta_chunked_workspace_bytes.restype = ci
+    lib.kata_forward_delta_chunked_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_forward_delta_chunked_timed.restype = ci
+    lib.kata_forward_delta_chunked_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9 + [sz, vp, vp]
+    lib.kata_forward_delta_chunked.restype = ci
+    lib.kata_forward_delta_chunked.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9 + [sz, vp]
     lib.kata_forward_delta.restype = ci
     lib.kata_forward_delta.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9
     lib.kata_decode_step_delta.restype = ci
@@ -434,6 +440,65 @@ def forward_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     st = _lib().kata_forward_delta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta), _ptr(S0),
                                    _ptr(y), _ptr(ST), _stream_handle(stream, dev))
     _check(st, "kata_forward_delta")
+    return (y, ST) if return_state else y
+
+
+def forward_delta_chunked_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None) -> int:
+    """Workspace bytes of kata_forward_delta_chunked for these sizes."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    n = ctypes.c_size_t(0)
+    _check(_lib().kata_forward_delta_chunked_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "kata_forward_delta_chunked_workspace_bytes")
+    return int(n.value)
+
+
+def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,
+                          S0: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                          return_state: bool = False, y: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+    """DeltaKATA causal forward in the chunked form (kata_forward_delta_chunked); same
+    definition and arguments as forward_delta.  events: optional three torch.cuda.Event
+    (start of the per-chunk pass, start and end of the walk)."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(beta, "beta", (B, H, T), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    _check(lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "kata_forward_delta_chunked_workspace_bytes")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if workspace is None:
+        workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev) if return_state else None
+    evarr = None
+    if events is not None:
+        if len(events) != 3:
+            raise ValueError("events: three torch.cuda.Event objects")
+        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+        for e in events:
+            if e.cuda_event == 0:
+                e.record(s_obj)
+        evarr = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib.kata_forward_delta_chunked_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta),
+                                              _ptr(S0), _ptr(y), _ptr(ST), _ptr(workspace),
+                                              ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                              _stream_handle(stream, dev), evarr)
+    _check(st, "kata_forward_delta_chunked")
     return (y, ST) if return_state else y
 
 

@@ -451,6 +451,54 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
   return launch_status();
 }
 
+// ---- chunked DeltaKATA ---------------------------------------------------------------------
+// Workspace: u^, w^ [B*H, n_chunks*64, 16] and T [B*H, n_chunks, 64, 64], float32, each
+// block 256-byte aligned.
+struct DeltaChunkLayout {
+  int64_t n_chunks = 0;
+  size_t off_w = 0, off_t = 0, total = 0;
+};
+
+DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
+  DeltaChunkLayout L;
+  const int64_t bh = d->B * d->H;
+  L.n_chunks = (d->T + kata::DC - 1) / kata::DC;
+  const size_t uw = (size_t)bh * (size_t)L.n_chunks * kata::DC * P_DIM * sizeof(float);
+  L.off_w = align256(uw);
+  L.off_t = L.off_w + align256(uw);
+  L.total = L.off_t + (size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * sizeof(float);
+  return L;
+}
+
+kata_status validate_delta_chunked(const kata_forward_desc* d) {
+  if (!d) return KATA_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0) return KATA_ERR_SHAPE;
+  if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
+  if (d->T > ((int64_t)1 << 40)) return KATA_ERR_SHAPE;
+  if (d->p != P_DIM || !((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (d->chunk != kata::DC) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(d->in_dtype) != KATA_OK || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+template <typename TIn, typename TOut, int DV>
+kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout& L, const void* q, const void* k,
+                              const void* v, const float* P, const float* beta, const float* S0, void* y,
+                              float* ST, unsigned char* ws, hipStream_t st, hipEvent_t* ev) {
+  const int64_t bh = d->B * d->H;
+  float* U = (float*)ws;
+  float* W = (float*)(ws + L.off_w);
+  float* Tm = (float*)(ws + L.off_t);
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr, e2 = ev ? ev[2] : nullptr;
+  hipExtLaunchKernelGGL((kata::kata_delta_prep<TIn, DV>), dim3((unsigned)L.n_chunks, (unsigned)bh), dim3(256), 0,
+                        st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tm, d->T, (int)d->H);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(256),
+                        0, st, e1, e2, 0, (const float*)U, (const float*)W, (const float*)Tm, (const TIn*)v, beta,
+                        S0, ST, (TOut*)y, d->T, L.n_chunks);
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -820,6 +868,66 @@ kata_status kata_forward_factors(const kata_forward_desc* desc, int g, kata_fact
                                  void* stream) {
   return kata_forward_factors_timed(desc, g, mode, q, k, v, P, S0, z0, y, ST, zT, workspace, workspace_bytes,
                                     stream, nullptr);
+}
+
+kata_status kata_forward_delta_chunked_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {
+  if (!bytes) return KATA_ERR_NULL;
+  const kata_status s = validate_delta_chunked(desc);
+  if (s != KATA_OK) return s;
+  *bytes = delta_chunk_layout(desc).total;
+  return KATA_OK;
+}
+
+kata_status kata_forward_delta_chunked_timed(const kata_forward_desc* desc, const void* q, const void* k,
+                                             const void* v, const float* P, const float* beta, const float* S0,
+                                             void* y, float* ST, void* workspace, size_t workspace_bytes,
+                                             void* stream, void* const* events) {
+  const kata_status s = validate_delta_chunked(desc);
+  if (s != KATA_OK) return s;
+  const int64_t bh = desc->B * desc->H;
+  if (bh == 0) return KATA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (desc->T == 0) {   // no tokens: ST = S0 (or 0)
+    if (!ST) return KATA_OK;
+    const int64_t nS = bh * P_DIM * P_DIM * desc->dv;
+    hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, ST, S0, nS);
+    return launch_status();
+  }
+  if (!q || !k || !v || !P || !beta || !y) return KATA_ERR_NULL;
+  const DeltaChunkLayout L = delta_chunk_layout(desc);
+  if (!workspace || workspace_bytes < L.total) return KATA_ERR_WORKSPACE;
+  if (L.n_chunks > 0x7fffffff) return KATA_ERR_SHAPE;
+  hipEvent_t ev[3];
+  hipEvent_t* evp = nullptr;
+  if (events) {
+    for (int i = 0; i < 3; ++i) {
+      if (!events[i]) return KATA_ERR_NULL;
+      ev[i] = (hipEvent_t)events[i];
+    }
+    evp = ev;
+  }
+  unsigned char* ws = (unsigned char*)workspace;
+  const bool fi = desc->in_dtype == KATA_F32, fo = desc->out_dtype == KATA_F32;
+#define KATA_DCH(TI, TO, DVV) \
+  return run_delta_chunked<TI, TO, DVV>(desc, L, q, k, v, P, beta, S0, y, ST, ws, st, evp)
+  if (desc->dv == 64) {
+    if (fi && fo) KATA_DCH(float, float, 64);
+    if (fi) KATA_DCH(float, bf16, 64);
+    if (fo) KATA_DCH(bf16, float, 64);
+    KATA_DCH(bf16, bf16, 64);
+  }
+  if (fi && fo) KATA_DCH(float, float, 16);
+  if (fi) KATA_DCH(float, bf16, 16);
+  if (fo) KATA_DCH(bf16, float, 16);
+  KATA_DCH(bf16, bf16, 16);
+#undef KATA_DCH
+}
+
+kata_status kata_forward_delta_chunked(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                                       const float* P, const float* beta, const float* S0, void* y, float* ST,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return kata_forward_delta_chunked_timed(desc, q, k, v, P, beta, S0, y, ST, workspace, workspace_bytes, stream,
+                                          nullptr);
 }
 
 kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H, int d, int p,

@@ -169,4 +169,373 @@ kata_delta_recurrent(const float* S0, float* ST, const TIn* __restrict__ q, cons
   }
 }
 
+// ---- chunked DeltaKATA forward ----------------------------------------------------------
+// The chunked form of the delta rule (the WY / UT form of chunked DeltaNet): with the
+// chunk's unit key features K^ (C x 256), query features Q^, write strengths beta and
+//   A = I + tril(diag(beta) K^ K^^T, -1),   T = A^{-1}      (unit lower triangular)
+// the chunk's corrections are E = T diag(beta) (V - K^ S), and
+//   Y = Q^ S + (Q^ K^^T o M) E   (M: s <= t),      S <- S + K^^T E.
+// K^ K^^T and Q^ K^^T are cos^2 tiles of the 16-dim normalised projections, so the
+// features are only built for the contractions with S.  T depends on the chunk's keys
+// alone, so kata_delta_prep forms it (and the normalised projections) for all chunks in
+// parallel; kata_delta_chunk then walks the chunks of one sequence in order.  The value
+// columns of S are independent (E's column block j needs S's column block j only), so
+// a sequence's walk is split over dv/16 workgroups, one per 16-column block.
+constexpr int DC = 64;          // chunk length of the chunked delta forward
+
+// One element through a range-checked buffer (0 past its end), as float.
+template <typename TIn> __device__ __forceinline__ float buf_elem(__amdgpu_buffer_rsrc_t r, int idx);
+template <> __device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, int idx) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0));
+}
+template <> __device__ __forceinline__ float buf_elem<bf16>(__amdgpu_buffer_rsrc_t r, int idx) {
+  return bf16_bits_to_float((u16)__builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0));
+}
+constexpr int DC_TSTR = 68;     // LDS row stride of T (floats), breaks bank alignment of rows
+
+// grid (n_chunks, B*H), block 256.  Writes for every token of the chunk u^ = Pq/|Pq| and
+// w^ = Pk/|Pk| (0 where the projection is 0, and past T) to Uo, Wo [B*H, n_chunks*64, 16],
+// and T of the chunk (64 x 64, row-major) to Tm [B*H, n_chunks, 64, 64].
+// Projection: the 4 threads of a token each take 16 input columns (two 16-byte loads of q
+// and of k), form the partial dot products of all 16 rows of P (staged in LDS) and sum
+// them with two lane shuffles.  Inversion: one column of T per lane of wave 0, the sum
+// over s split into 4 interleaved partial sums to shorten the dependency chain.
+template <typename TIn, int DIN>
+__global__ void __launch_bounds__(256)
+kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
+                const float* __restrict__ P, float* __restrict__ Uo, float* __restrict__ Wo,
+                float* __restrict__ Tm, int64_t T, int H) {
+  constexpr int d = DIN;
+  __shared__ __align__(16) float Ps[P_DIM][64 + 4];
+  __shared__ __align__(16) float ws[DC][P_DIM];
+  __shared__ __align__(16) float G[DC][DC + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t n_chunks = gridDim.x;
+  for (int i = tid; i < P_DIM * d; i += 256) Ps[i / d][i % d] = P[(int64_t)h * P_DIM * d + i];
+  const int tl = tid >> 2, qq = tid & 3;           // token of the chunk, quarter of the columns
+  const int64_t t = c * DC + tl;
+  const bool live = t < T;
+  constexpr int cw = d >> 2;                       // columns per quarter (16 or 4)
+  float xq[16], xk[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    xq[i] = 0.f;
+    xk[i] = 0.f;
+  }
+  if (live) {
+    const TIn* qr = q + (bh * T + t) * d + qq * cw;
+    const TIn* kr = k + (bh * T + t) * d + qq * cw;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < cw) {
+        xq[i] = Elem<TIn>::load(qr, i);
+        xk[i] = Elem<TIn>::load(kr, i);
+      }
+    }
+  }
+  __syncthreads();   // P staged
+  float u[P_DIM], w[P_DIM];
+#pragma unroll
+  for (int a = 0; a < P_DIM; ++a) {
+    float su = 0.f, sw = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < cw) {
+        const float pv = Ps[a][qq * cw + i];
+        su += pv * xq[i];
+        sw += pv * xk[i];
+      }
+    }
+    su += __shfl_xor(su, 1); su += __shfl_xor(su, 2);
+    sw += __shfl_xor(sw, 1); sw += __shfl_xor(sw, 2);
+    u[a] = su;
+    w[a] = sw;
+  }
+  float nu = 0.f, nw = 0.f;
+#pragma unroll
+  for (int a = 0; a < P_DIM; ++a) {
+    nu += u[a] * u[a];
+    nw += w[a] * w[a];
+  }
+  const float iu = nu > 0.f ? 1.f / sqrtf(nu) : 0.f;
+  const float iw = nw > 0.f ? 1.f / sqrtf(nw) : 0.f;
+  f32x4 uh, wh;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uh[i] = u[4 * qq + i] * iu;   // this thread writes components 4qq .. 4qq+3
+    wh[i] = w[4 * qq + i] * iw;
+  }
+  const int64_t row = (bh * n_chunks + c) * DC + tl;
+  *reinterpret_cast<f32x4*>(Uo + row * P_DIM + 4 * qq) = uh;
+  *reinterpret_cast<f32x4*>(Wo + row * P_DIM + 4 * qq) = wh;
+  *reinterpret_cast<f32x4*>(&ws[tl][4 * qq]) = wh;
+  __syncthreads();
+  // G[t][s] = beta_t (w^_t . w^_s)^2 for s < t: thread (t = tl, s = 16 qq .. 16 qq + 15)
+  {
+    const float bt = live ? beta[bh * T + t] : 0.f;
+    f32x4 wt[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) wt[m] = *reinterpret_cast<const f32x4*>(&ws[tl][4 * m]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sidx = 16 * qq + i;
+      float dp = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 wsv = *reinterpret_cast<const f32x4*>(&ws[sidx][4 * m]);
+        dp += wt[m][0] * wsv[0] + wt[m][1] * wsv[1] + wt[m][2] * wsv[2] + wt[m][3] * wsv[3];
+      }
+      G[tl][sidx] = sidx < tl ? bt * dp * dp : 0.f;
+    }
+  }
+  __syncthreads();
+  // T = (I + G)^{-1} by forward substitution, one column per lane of wave 0:
+  // x_t = [t == j] - sum_{s < t} G[t][s] x_s, all columns in lockstep (G reads broadcast).
+  if (wave == 0) {
+    float x[DC];
+#pragma unroll
+    for (int tt = 0; tt < DC; ++tt) {
+      float acc[4] = {tt == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < tt; s4 += 4) {
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(&G[tt][s4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s4 + e < tt) acc[e] -= gv[e] * x[s4 + e];
+      }
+      x[tt] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    float* out = Tm + ((bh * n_chunks + c) * DC) * DC;
+#pragma unroll
+    for (int tt = 0; tt < DC; ++tt) out[tt * DC + lane] = x[tt];
+  }
+}
+
+// grid (dv/16, B*H), block 256 (4 waves; wave w owns the 16-token block w of every chunk
+// and the state rows 64w .. 64w+63 of the column block).  Walks the chunks in order:
+//   publish S (bf16 B-fragments, K = feature) | R = V - K^ S, Pq = Q^ S |
+//   X = diag(beta) R | E = T X | Y = Pq + (Q^K^^T o M) E, S += K^^T E.
+// Token-K fragments use the permuted order of the accumulator tiles: slot i < 4 of
+// K-block kk, lane group g is token 32kk + 4g + i, slot 4 + i is token 32kk + 16 + 4g + i
+// (the same permutation for the feature-K fragments of S and K^), so accumulator tiles
+// are stored as fragments with one 8-byte store per lane.  Precision: the state, the
+// corrections X and E, T and the 16-dim cosine tiles are hi/lo bf16 operands (~16
+// significant bits: these are where sums cancel); the 256-entry feature fragments
+// (products of unit-vector components) are hi/lo only for fp32 inputs (SPLIT) and single
+// bf16 for bf16 inputs, as the one-factor kernels round their features.
+// S0/ST [B*H, 256, dv] (nullable; S0 == ST allowed), y [B*H, T, dv].
+template <typename TIn, typename TOut, int DV>
+__global__ void __launch_bounds__(256)
+kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const float* __restrict__ Tm,
+                 const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
+                 TOut* __restrict__ y, int64_t T, int64_t n_chunks) {
+  constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
+  constexpr int NS = 2;                      // state / X / E fragments: always hi / lo
+  __shared__ __align__(16) float Us[DC][P_DIM];
+  __shared__ __align__(16) float Wsm[DC][P_DIM];
+  __shared__ __align__(16) float Tl[DC][DC_TSTR];
+  __shared__ __align__(16) bf16 SB[NS][8][WAVE][8];    // S as B-fragments (hi [, lo])
+  __shared__ __align__(16) bf16 XB[NS][2][WAVE][8];    // diag(beta) R
+  __shared__ __align__(16) bf16 EB[NS][2][WAVE][8];    // E
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int j = blockIdx.x;                           // value column block
+  const int64_t bh = blockIdx.y;
+  const int mb = wave;                                // 16-token block of this wave
+  const int col = 16 * j + n;                         // value column of this lane
+  // v and beta of this sequence through range-checked buffers: rows past T read 0
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * T * DV, T * DV * (int64_t)sizeof(TIn));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + bh * T, T * 4);
+
+  auto put = [&](auto& dst, int kk, int slot, const float (&x)[4]) {   // dst [NS][K-blocks][WAVE][8]
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = (bf16)x[r];
+      lo[r] = (bf16)(x[r] - (float)hi[r]);
+    }
+    *reinterpret_cast<bf16x4*>(&dst[0][kk][lane][slot]) = hi;
+    *reinterpret_cast<bf16x4*>(&dst[1][kk][lane][slot]) = lo;
+  };
+  auto frag = [&](const auto& src, int kk) {
+    Op8<true> f;
+    f.hi = *reinterpret_cast<const bf16x8*>(&src[0][kk][lane][0]);
+    f.lo = *reinterpret_cast<const bf16x8*>(&src[1][kk][lane][0]);
+    return f;
+  };
+
+  // state tiles: tile qd of this wave holds features f = 16 (4 wave + qd) + 4g + r, column col
+  f32x4 Sacc[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = 16 * (4 * wave + qd) + 4 * g + r;
+      Sacc[qd][r] = S0 ? S0[(bh * P_DIM * P_DIM + f) * DV + col] : 0.f;
+    }
+  }
+
+  // per-chunk inputs, prefetched one chunk ahead into registers
+  f32x4 pu, pw, pt[4];
+  float pv[4], pb[4];
+  auto fetch = [&](int64_t c) {
+    const int64_t rbase = (bh * n_chunks + c) * DC;
+    pu = *reinterpret_cast<const f32x4*>(Uh + rbase * P_DIM + 4 * tid);
+    pw = *reinterpret_cast<const f32x4*>(Wh + rbase * P_DIM + 4 * tid);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pt[i] = *reinterpret_cast<const f32x4*>(Tm + rbase * DC + 4 * (tid + 256 * i));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
+      pv[r] = buf_elem<TIn>(rv, t * DV + col);
+      pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
+    }
+  };
+  if (n_chunks > 0) fetch(0);
+
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    // ---- stage: inputs to LDS, S to B-fragments
+    *reinterpret_cast<f32x4*>(&Us[0][0] + 4 * tid) = pu;
+    *reinterpret_cast<f32x4*>(&Wsm[0][0] + 4 * tid) = pw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * (tid + 256 * i);
+      *reinterpret_cast<f32x4*>(&Tl[e / DC][e % DC]) = pt[i];
+    }
+    float vv[4], bb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      vv[r] = pv[r];
+      bb[r] = pb[r];
+    }
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int tile = 4 * wave + qd;
+      const float sx[4] = {Sacc[qd][0], Sacc[qd][1], Sacc[qd][2], Sacc[qd][3]};
+      put(SB, tile >> 1, (tile & 1) * 4, sx);
+    }
+    __syncthreads();
+    if (c + 1 < n_chunks) fetch(c + 1);
+
+    // ---- R = V - K^ S, Pq = Q^ S for tokens 16 mb + n (A rows), K = feature
+    const int tt = 16 * mb + n;
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&Wsm[tt][4 * g]);   // components 4g .. 4g+3
+    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&Us[tt][4 * g]);
+    f32x4 accR = zero4(), accQ = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      // slot i < 4: feature (2kk, 4g+i); slot 4+i: feature (2kk+1, 4g+i)
+      const f32x2 wa = *reinterpret_cast<const f32x2*>(&Wsm[tt][2 * kk]);
+      const f32x2 ua = *reinterpret_cast<const f32x2*>(&Us[tt][2 * kk]);
+      float xk[8], xq[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[i] = wa[0] * w4[i];
+        xk[4 + i] = wa[1] * w4[i];
+        xq[i] = ua[0] * u4[i];
+        xq[4 + i] = ua[1] * u4[i];
+      }
+      const Op8<true> sb = frag(SB, kk);
+      accR = mma<SPLIT, true>(make8<SPLIT>(xk), sb, accR);
+      accQ = mma<SPLIT, true>(make8<SPLIT>(xq), sb, accQ);
+    }
+    // accumulator lane (n, g) holds token 16 mb + 4g + r, column col
+    {
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = bb[r] * (vv[r] - accR[r]);
+      put(XB, mb >> 1, (mb & 1) * 4, x);
+    }
+    __syncthreads();
+
+    // ---- E = T X for tokens 16 mb + n (A rows of T), K = token
+    f32x4 accE = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const f32x4 t0v = *reinterpret_cast<const f32x4*>(&Tl[tt][32 * kk + 4 * g]);
+      const f32x4 t1v = *reinterpret_cast<const f32x4*>(&Tl[tt][32 * kk + 16 + 4 * g]);
+      float xt[8] = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
+      accE = mma<true, true>(make8<true>(xt), frag(XB, kk), accE);
+    }
+    {
+      const float ex[4] = {accE[0], accE[1], accE[2], accE[3]};
+      put(EB, mb >> 1, (mb & 1) * 4, ex);
+    }
+    __syncthreads();
+
+    // ---- Y = Pq + (Q^ K^^T o M) E.  Score tile of key block sb against this query block:
+    // X = W^_sb U^_mb^T (K = 16), lane (t = n, g) holds s = 16 sb + 4g + r: (u^_t . w^_s)^2.
+    f32x4 accY = accQ;
+    {
+      float ubv[4] = {u4[0], u4[1], u4[2], u4[3]};
+      const Op4<true> uf = make4<true>(ubv);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (2 * kk <= mb) {
+          float xa[8];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int sb = 2 * kk + hb;
+            if (sb <= mb) {
+              const f32x4 wb = *reinterpret_cast<const f32x4*>(&Wsm[16 * sb + n][4 * g]);
+              float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
+              const f32x4 X = mma<true, true>(make4<true>(wbv), uf, zero4());
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                xa[4 * hb + r] = (sb < mb || 4 * g + r <= n) ? X[r] * X[r] : 0.f;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) xa[4 * hb + r] = 0.f;
+            }
+          }
+          // A = score rows t (lane n) over key tokens s (K, permuted order), B = E (K = s):
+          // lane (n, g) keeps column col and tokens 4g + r, as accQ does
+          accY = mma<SPLIT, true>(make8<SPLIT>(xa), frag(EB, kk), accY);
+        }
+      }
+    }
+    // ---- S += K^^T E: tile qd holds features f = 16 a + b with a = 4 wave + qd; as an A
+    // operand its row n is b = n, so slot i of K-block kk carries w^_s[a] w^_s[n] of token s
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Op8<true> eb = frag(EB, kk);
+      f32x4 wsl[8];
+      float wn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sidx = 32 * kk + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+        wsl[i] = *reinterpret_cast<const f32x4*>(&Wsm[sidx][4 * wave]);
+        wn[i] = Wsm[sidx][n];
+      }
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        float xa[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[i] = wsl[i][qd] * wn[i];
+        Sacc[qd] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[qd]);
+      }
+    }
+    // ---- y (accumulator lane (n, g): token 16 mb + 4g + r, column col)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = c * DC + 16 * mb + 4 * g + r;
+      if (t < T) Elem<TOut>::store(y, (bh * T + t) * DV + col, accY[r]);
+    }
+    __syncthreads();
+  }
+  if (ST) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * (4 * wave + qd) + 4 * g + r;
+        ST[(bh * P_DIM * P_DIM + f) * DV + col] = Sacc[qd][r];
+      }
+    }
+  }
+}
+
 }  // namespace kata

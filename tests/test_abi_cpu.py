@@ -311,3 +311,29 @@ def test_factor_forward_workspace_and_validation():
                                     16, None) == Bd.KATA_ERR_WORKSPACE
     assert lib.kata_forward_factors(ctypes.byref(good), 2, 0, fake, fake, fake, None, None, None, fake, None,
                                     None, fake, 1 << 40, None) == Bd.KATA_ERR_NULL      # P missing
+
+
+def test_delta_chunked_workspace_and_validation():
+    lib = _lib_or_skip()
+    n = ctypes.c_size_t(0)
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    chunks = 131072 // 64
+    uw = 16 * chunks * 64 * 16 * 4
+    assert n.value == 2 * uw + 16 * chunks * 64 * 64 * 4          # u^, w^ and T per chunk
+    fake = ctypes.c_void_p(0x1000)
+    for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),
+                           ({"p": 8}, Bd.KATA_ERR_UNSUPPORTED), ({"T": -1}, Bd.KATA_ERR_SHAPE),
+                           ({"B": 70000}, Bd.KATA_ERR_SHAPE)]:
+        bad = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+        for f, val in fields.items():
+            setattr(bad, f, val)
+        assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == status, fields
+    good = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    args = [fake] * 4
+    assert lib.kata_forward_delta_chunked(ctypes.byref(good), *args, None, None, fake, None, fake, 1 << 40,
+                                          None) == Bd.KATA_ERR_NULL                     # beta missing
+    assert lib.kata_forward_delta_chunked(ctypes.byref(good), *args, fake, None, fake, None, fake, 16,
+                                          None) == Bd.KATA_ERR_WORKSPACE
+    empty = Bd.make_desc(0, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
+    assert lib.kata_forward_delta_chunked(ctypes.byref(empty), *([None] * 8), None, 0, None) == Bd.KATA_OK

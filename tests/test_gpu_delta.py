@@ -29,6 +29,16 @@ def row_rel(got, ref):
     return float(np.max(np.linalg.norm(got - ref, axis=-1) / np.where(den == 0, 1.0, den)))
 
 
+def slice_rel(got, ref):
+    """Normwise relative error per (b, h) slice, max over slices (the reading of
+    "relative error" the one-factor tests use)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    g = g.reshape(g.shape[0] * g.shape[1], -1)
+    r = r.reshape(r.shape[0] * r.shape[1], -1)
+    return float(np.max(np.linalg.norm(g - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)))
+
+
 def to_dev(*ts):
     return [t.to(DEV) for t in ts]
 
@@ -195,4 +205,104 @@ def test_delta_long_prefix_and_final_state():
                                case.P[heads].double().numpy(), beta[:, heads].double().numpy())
     eS = row_rel(ST[:, heads].double().cpu().numpy().reshape(2, -1), Sr.reshape(2, -1))
     print(f"[delta long] y prefix {ey:.3e} S_T {eS:.3e}", flush=True)
+    assert ey <= TOL_BF16 and eS <= TOL_BF16
+
+
+# ---- chunked form (kata_forward_delta_chunked) ------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 300])
+def test_delta_chunked_against_oracle_bf16(T):
+    case = I.make_forward("mid", B=2, H=3, T=T, seed=180 + T)
+    beta = I.make_beta(2, 3, T, seed=100 + T)
+    q, k, v, P, b = to_dev(case.q, case.k, case.v, case.P, beta)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, out_dtype=torch.float32, return_state=True)
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                                beta.double().numpy())
+    ey = row_rel(y.double().cpu().numpy(), yr)
+    sy, sS = slice_rel(y.cpu().numpy(), yr), slice_rel(ST.cpu().numpy(), Sr)
+    print(f"[delta chunked bf16 T={T}] rel y rows {ey:.3e} slices {sy:.3e} S_T {sS:.3e}", flush=True)
+    assert ey <= TOL_BF16
+    # bf16 inputs: the feature fragments are rounded to bf16 once (the state, T and the
+    # corrections stay hi/lo), the precision class of the one-factor chunked forward
+    assert sy <= 5e-3 and sS <= 5e-3
+
+
+def test_delta_chunked_tiny_fp32_with_state():
+    case = I.make_forward("tiny", seed=181)
+    B, H, T = case.q.shape[:3]
+    beta = I.make_beta(B, H, T, seed=181, lo=0.0, hi=1.0)
+    S0 = torch.randn((B, H, 256, 16), generator=torch.Generator().manual_seed(181)) / 4
+    q, k, v, P, b, S0d = to_dev(case.q, case.k, case.v, case.P, beta, S0)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, S0=S0d, return_state=True)
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                                beta.double().numpy(), S0.double().numpy())
+    ey = row_rel(y.double().cpu().numpy(), yr)
+    sy, sS = slice_rel(y.cpu().numpy(), yr), slice_rel(ST.cpu().numpy(), Sr)
+    print(f"[delta chunked tiny fp32] rel y rows {ey:.3e} slices {sy:.3e} S_T {sS:.3e}", flush=True)
+    assert sy <= TOL_F32 and sS <= TOL_F32 and ey <= 1e-3
+
+
+def test_delta_chunked_overwrite_and_zero_keys():
+    """Repeated keys with beta = 1 inside one chunk and across chunks, plus zero keys and
+    queries (features 0): against the oracle."""
+    T = 200
+    g = torch.Generator().manual_seed(182)
+    k = torch.randn((1, 2, T, 64), generator=g) / 8
+    k[:, :, 40] = k[:, :, 10]
+    k[:, :, 150] = k[:, :, 10]
+    k[:, :, 70] = 0.0
+    q = torch.randn((1, 2, T, 64), generator=g) / 8
+    q[:, :, 90] = 0.0
+    v = torch.randn((1, 2, T, 64), generator=g) / 8
+    P = torch.randn((2, 16, 64), generator=g) / 8
+    b = torch.ones((1, 2, T))
+    qd, kd, vd, Pd, bd = to_dev(q, k, v, P, b)
+    y = kata.forward_delta_chunked(qd, kd, vd, Pd, bd)
+    torch.cuda.synchronize()
+    yr, _ = O.delta_recurrence(q.double().numpy(), k.double().numpy(), v.double().numpy(), P.double().numpy(),
+                               b.double().numpy())
+    e = row_rel(y.double().cpu().numpy(), yr)
+    se = slice_rel(y.float().cpu().numpy(), yr)
+    print(f"[delta chunked overwrite] rel y rows {e:.3e} slices {se:.3e}", flush=True)
+    assert e <= TOL_BF16 and se <= 5e-3   # bf16 output
+    assert torch.all(y[:, :, 90] == 0)
+
+
+def test_delta_chunked_equals_recurrent_lm340m():
+    """The chunked and the token-recurrent kernels on the 340M-layer inputs (bf16 in, f32 out)."""
+    case = I.make_forward("lm340m", B=2, H=16, T=2048, seed=183)
+    beta = I.make_beta(2, 16, 2048, seed=183)
+    q, k, v, P, b = to_dev(case.q, case.k, case.v, case.P, beta)
+    y1, S1 = kata.forward_delta_chunked(q, k, v, P, b, out_dtype=torch.float32, return_state=True)
+    y2, S2 = kata.forward_delta(q, k, v, P, b, out_dtype=torch.float32, return_state=True)
+    torch.cuda.synchronize()
+    ey = row_rel(y1.double().cpu().numpy().reshape(-1, 64), y2.double().cpu().numpy().reshape(-1, 64))
+    sy, sS = slice_rel(y1.cpu().numpy(), y2.cpu().numpy()), slice_rel(S1.cpu().numpy(), S2.cpu().numpy())
+    print(f"[delta chunked vs recurrent lm340m] y rows {ey:.3e} slices {sy:.3e} S {sS:.3e}", flush=True)
+    assert ey <= TOL_BF16 and sy <= 5e-3 and sS <= 5e-3
+
+
+def test_delta_chunked_long_prefix_and_final_state():
+    """The long-context shape (B=1, H=16, T=131072) in the launch configuration the
+    benchmark uses: the first 2048 tokens of two heads and their final states against the
+    oracle."""
+    T = 131072
+    case = I.make_forward("long", T=T, seed=184)
+    beta = I.make_beta(1, 16, T, seed=184)
+    q, k, v, P, b = to_dev(case.q, case.k, case.v, case.P, beta)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(y.float()))
+    m = 2048
+    heads = [0, 15]
+    yr, _ = O.delta_recurrence(host64(case.q[:, heads, :m]), host64(case.k[:, heads, :m]),
+                               host64(case.v[:, heads, :m]), case.P[heads].double().numpy(),
+                               beta[:, heads, :m].double().numpy())
+    ey = row_rel(y[:, heads, :m].double().cpu().numpy(), yr)
+    _, Sr = O.delta_recurrence(host64(case.q[:, heads]), host64(case.k[:, heads]), host64(case.v[:, heads]),
+                               case.P[heads].double().numpy(), beta[:, heads].double().numpy())
+    eS = row_rel(ST[:, heads].double().cpu().numpy().reshape(2, -1), Sr.reshape(2, -1))
+    print(f"[delta chunked long] y prefix {ey:.3e} S_T {eS:.3e}", flush=True)
     assert ey <= TOL_BF16 and eS <= TOL_BF16

@@ -452,8 +452,8 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
 }
 
 // ---- chunked DeltaKATA ---------------------------------------------------------------------
-// Workspace: u^, w^ [B*H, n_chunks*64, 16] and T [B*H, n_chunks, 64, 64], float32, each
-// block 256-byte aligned.
+// Workspace: u^, w^ [B*H, n_chunks*64, 16] float32 and T per chunk as hi/lo bf16 matrix-core
+// fragments (64 x 64 x 2 bf16 per chunk), each block 256-byte aligned.
 struct DeltaChunkLayout {
   int64_t n_chunks = 0;
   size_t off_w = 0, off_t = 0, total = 0;
@@ -466,7 +466,7 @@ DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   const size_t uw = (size_t)bh * (size_t)L.n_chunks * kata::DC * P_DIM * sizeof(float);
   L.off_w = align256(uw);
   L.off_t = L.off_w + align256(uw);
-  L.total = L.off_t + (size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * sizeof(float);
+  L.total = L.off_t + (size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * 2 * sizeof(bf16);
   return L;
 }
 
@@ -488,13 +488,13 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   const int64_t bh = d->B * d->H;
   float* U = (float*)ws;
   float* W = (float*)(ws + L.off_w);
-  float* Tm = (float*)(ws + L.off_t);
+  bf16* Tf = (bf16*)(ws + L.off_t);
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr, e2 = ev ? ev[2] : nullptr;
   hipExtLaunchKernelGGL((kata::kata_delta_prep<TIn, DV>), dim3((unsigned)L.n_chunks, (unsigned)bh), dim3(256), 0,
-                        st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tm, d->T, (int)d->H);
+                        st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tf, d->T, (int)d->H);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(256),
-                        0, st, e1, e2, 0, (const float*)U, (const float*)W, (const float*)Tm, (const TIn*)v, beta,
+                        0, st, e1, e2, 0, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
                         S0, ST, (TOut*)y, d->T, L.n_chunks);
   return launch_status();
 }

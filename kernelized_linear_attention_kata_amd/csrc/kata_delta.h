@@ -191,11 +191,13 @@ template <> __device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsr
 template <> __device__ __forceinline__ float buf_elem<bf16>(__amdgpu_buffer_rsrc_t r, int idx) {
   return bf16_bits_to_float((u16)__builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0));
 }
-constexpr int DC_TSTR = 68;     // LDS row stride of T (floats), breaks bank alignment of rows
 
 // grid (n_chunks, B*H), block 256.  Writes for every token of the chunk u^ = Pq/|Pq| and
 // w^ = Pk/|Pk| (0 where the projection is 0, and past T) to Uo, Wo [B*H, n_chunks*64, 16],
-// and T of the chunk (64 x 64, row-major) to Tm [B*H, n_chunks, 64, 64].
+// and T of the chunk to Tf [B*H, n_chunks, 4, 2, 64, 2, 8] bf16, already in the form the
+// walk feeds the matrix cores: for query block mb, token K-block kk and lane (n, g), the 8
+// entries T[16 mb + n][s] of the lane's K slots (permuted token order, see the walk) as
+// hi and lo bf16 halves.
 // Projection: the 4 threads of a token each take 16 input columns (two 16-byte loads of q
 // and of k), form the partial dot products of all 16 rows of P (staged in LDS) and sum
 // them with two lane shuffles.  Inversion: one column of T per lane of wave 0, the sum
@@ -204,7 +206,7 @@ template <typename TIn, int DIN>
 __global__ void __launch_bounds__(256)
 kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
                 const float* __restrict__ P, float* __restrict__ Uo, float* __restrict__ Wo,
-                float* __restrict__ Tm, int64_t T, int H) {
+                bf16* __restrict__ Tf, int64_t T, int H) {
   constexpr int d = DIN;
   __shared__ __align__(16) float Ps[P_DIM][64 + 4];
   __shared__ __align__(16) float ws[DC][P_DIM];
@@ -307,9 +309,25 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
       }
       x[tt] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
-    float* out = Tm + ((bh * n_chunks + c) * DC) * DC;
+    // T back into LDS (over G, which is no longer read) for the fragment transpose
 #pragma unroll
-    for (int tt = 0; tt < DC; ++tt) out[tt * DC + lane] = x[tt];
+    for (int tt = 0; tt < DC; ++tt) G[tt][lane] = x[tt];
+  }
+  __syncthreads();
+  // fragments: thread handles (mb, kk, lane') for two of the 4 x 2 x 64 combinations
+  bf16* out = Tf + (bh * n_chunks + c) * (DC * DC * 2);
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int idx = tid + 256 * rep;          // = (mb * 2 + kk) * 64 + lane'
+    const int lf = idx & 63, kk = (idx >> 6) & 1, mb = idx >> 7;
+    const int nn = lf & 15, gg = lf >> 4;
+    const int row = 16 * mb + nn;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&G[row][32 * kk + 4 * gg]);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(&G[row][32 * kk + 16 + 4 * gg]);
+    const float xv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const Op8<true> f = make8<true>(xv);
+    *reinterpret_cast<bf16x8*>(out + idx * 16) = f.hi;
+    *reinterpret_cast<bf16x8*>(out + idx * 16 + 8) = f.lo;
   }
 }
 
@@ -328,14 +346,13 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 // S0/ST [B*H, 256, dv] (nullable; S0 == ST allowed), y [B*H, T, dv].
 template <typename TIn, typename TOut, int DV>
 __global__ void __launch_bounds__(256)
-kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const float* __restrict__ Tm,
+kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
                  TOut* __restrict__ y, int64_t T, int64_t n_chunks) {
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
   constexpr int NS = 2;                      // state / X / E fragments: always hi / lo
   __shared__ __align__(16) float Us[DC][P_DIM];
   __shared__ __align__(16) float Wsm[DC][P_DIM];
-  __shared__ __align__(16) float Tl[DC][DC_TSTR];
   __shared__ __align__(16) bf16 SB[NS][8][WAVE][8];    // S as B-fragments (hi [, lo])
   __shared__ __align__(16) bf16 XB[NS][2][WAVE][8];    // diag(beta) R
   __shared__ __align__(16) bf16 EB[NS][2][WAVE][8];    // E
@@ -378,38 +395,42 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     }
   }
 
-  // per-chunk inputs, prefetched one chunk ahead into registers
-  f32x4 pu, pw, pt[4];
-  float pv[4], pb[4];
-  auto fetch = [&](int64_t c) {
+  // per-chunk inputs, prefetched two chunks ahead into two register sets (the chunk loop
+  // is unrolled by two so each set has a static name); T arrives as this wave's own hi/lo
+  // A-fragments (two K-blocks)
+  struct Inputs {
+    f32x4 pu, pw;
+    Op8<true> pt[2];
+    float pv[4], pb[4];
+  };
+  auto fetch = [&](Inputs& in, int64_t c) {
     const int64_t rbase = (bh * n_chunks + c) * DC;
-    pu = *reinterpret_cast<const f32x4*>(Uh + rbase * P_DIM + 4 * tid);
-    pw = *reinterpret_cast<const f32x4*>(Wh + rbase * P_DIM + 4 * tid);
+    in.pu = *reinterpret_cast<const f32x4*>(Uh + rbase * P_DIM + 4 * tid);
+    in.pw = *reinterpret_cast<const f32x4*>(Wh + rbase * P_DIM + 4 * tid);
+    const bf16* tf = Tf + (bh * n_chunks + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pt[i] = *reinterpret_cast<const f32x4*>(Tm + rbase * DC + 4 * (tid + 256 * i));
+    for (int kk = 0; kk < 2; ++kk) {
+      in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
+      in.pt[kk].lo = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16 + 8);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
-      pv[r] = buf_elem<TIn>(rv, t * DV + col);
-      pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
+      in.pv[r] = buf_elem<TIn>(rv, t * DV + col);
+      in.pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
     }
   };
-  if (n_chunks > 0) fetch(0);
 
-  for (int64_t c = 0; c < n_chunks; ++c) {
+  auto step = [&](Inputs& in, int64_t c) {
     // ---- stage: inputs to LDS, S to B-fragments
-    *reinterpret_cast<f32x4*>(&Us[0][0] + 4 * tid) = pu;
-    *reinterpret_cast<f32x4*>(&Wsm[0][0] + 4 * tid) = pw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * (tid + 256 * i);
-      *reinterpret_cast<f32x4*>(&Tl[e / DC][e % DC]) = pt[i];
-    }
+    *reinterpret_cast<f32x4*>(&Us[0][0] + 4 * tid) = in.pu;
+    *reinterpret_cast<f32x4*>(&Wsm[0][0] + 4 * tid) = in.pw;
+    const Op8<true> tfr[2] = {in.pt[0], in.pt[1]};
     float vv[4], bb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      vv[r] = pv[r];
-      bb[r] = pb[r];
+      vv[r] = in.pv[r];
+      bb[r] = in.pb[r];
     }
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
@@ -418,8 +439,7 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
       put(SB, tile >> 1, (tile & 1) * 4, sx);
     }
     __syncthreads();
-    if (c + 1 < n_chunks) fetch(c + 1);
-
+    if (c + 2 < n_chunks) fetch(in, c + 2);
     // ---- R = V - K^ S, Pq = Q^ S for tokens 16 mb + n (A rows), K = feature
     const int tt = 16 * mb + n;
     const f32x4 w4 = *reinterpret_cast<const f32x4*>(&Wsm[tt][4 * g]);   // components 4g .. 4g+3
@@ -454,12 +474,7 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     // ---- E = T X for tokens 16 mb + n (A rows of T), K = token
     f32x4 accE = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const f32x4 t0v = *reinterpret_cast<const f32x4*>(&Tl[tt][32 * kk + 4 * g]);
-      const f32x4 t1v = *reinterpret_cast<const f32x4*>(&Tl[tt][32 * kk + 16 + 4 * g]);
-      float xt[8] = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
-      accE = mma<true, true>(make8<true>(xt), frag(XB, kk), accE);
-    }
+    for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(tfr[kk], frag(XB, kk), accE);
     {
       const float ex[4] = {accE[0], accE[1], accE[2], accE[3]};
       put(EB, mb >> 1, (mb & 1) * 4, ex);
@@ -525,7 +540,17 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
       if (t < T) Elem<TOut>::store(y, (bh * T + t) * DV + col, accY[r]);
     }
     __syncthreads();
+  };
+
+  Inputs ia, ib;
+  if (n_chunks > 0) fetch(ia, 0);
+  if (n_chunks > 1) fetch(ib, 1);
+  int64_t c = 0;
+  for (; c + 1 < n_chunks; c += 2) {
+    step(ia, c);
+    step(ib, c + 1);
   }
+  if (c < n_chunks) step(ia, c);
   if (ST) {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {

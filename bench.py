@@ -427,7 +427,7 @@ def bench_decode(args):
 DELTA_FWD_METRIC = ("DeltaKATA causal fwd tokens/sec at T=131072, chunked (WY) form (1 GPU)")
 
 
-def delta_cpu_baseline(case, beta, T_sample=16384, heads=2):
+def delta_cpu_baseline(case, beta, T_sample=65536, heads=8):
     """The oracle's DeltaKATA token recurrence on the first T_sample tokens of `heads` heads,
     extrapolated linearly (the recurrence costs the same per token)."""
     from threadpoolctl import threadpool_info

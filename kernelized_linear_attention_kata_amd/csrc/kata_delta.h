@@ -359,8 +359,19 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int j = blockIdx.x;                           // value column block
-  const int64_t bh = blockIdx.y;
+  // The dv/16 workgroups of a sequence read the same u^, w^ and T.  Workgroups go to the
+  // 8 XCDs (each with its own L2) round-robin by linear id, so when B*H is a multiple of 8
+  // the ids are remapped to place all column blocks of a sequence on one XCD:
+  // id = 8 slot + xcd, sequence = xcd + 8 (slot / NBLK), column block = slot % NBLK.
+  constexpr int NBLK = DV / 16;
+  int j = blockIdx.x;                                 // value column block
+  int64_t bh = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {
+    const int64_t id = (int64_t)blockIdx.y * NBLK + blockIdx.x;
+    const int64_t xcd = id & 7, slot = id >> 3;
+    bh = xcd + 8 * (slot / NBLK);
+    j = (int)(slot % NBLK);
+  }
   const int mb = wave;                                // 16-token block of this wave
   const int col = 16 * j + n;                         // value column of this lane
   // v and beta of this sequence through range-checked buffers: rows past T read 0

@@ -719,7 +719,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the sharded path is described in DESIGN.md but not run.", file=sys.stderr)
+              "sequences and heads shard across GPUs without exchange and one long sequence by carrying "
+              "the state (the resume form), but no multi-GPU run is made here.", file=sys.stderr)
         sys.exit(2)
 
     if args.decode:

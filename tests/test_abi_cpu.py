@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "kata.h")
 
 def _lib_or_skip():
     if not os.path.exists(Bd.library_path()):
-        pytest.skip("libkata.so not built (run __graft_entry__.build())")
+        pytest.skip("libkata.so not built (python -m kernelized_linear_attention_kata_amd.build)")
     return Bd.load_library()
 
 

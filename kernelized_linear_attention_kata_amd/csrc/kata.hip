@@ -493,7 +493,7 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   hipExtLaunchKernelGGL((kata::kata_delta_prep<TIn, DV>), dim3((unsigned)L.n_chunks, (unsigned)bh), dim3(256), 0,
                         st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tf, d->T, (int)d->H);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(256),
+  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(512),
                         0, st, e1, e2, 0, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
                         S0, ST, (TOut*)y, d->T, L.n_chunks);
   return launch_status();

@@ -331,10 +331,14 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   }
 }
 
-// grid (dv/16, B*H), block 256 (4 waves; wave w owns the 16-token block w of every chunk
-// and the state rows 64w .. 64w+63 of the column block).  Walks the chunks in order:
-//   publish S (bf16 B-fragments, K = feature) | R = V - K^ S, Pq = Q^ S |
-//   X = diag(beta) R | E = T X | Y = Pq + (Q^K^^T o M) E, S += K^^T E.
+// grid (dv/16, B*H), block 512: 8 waves in two roles that share the staged fragments.
+//  * state waves (0..3): wave w owns the 16-token block w of every chunk and the state rows
+//    64w .. 64w+63 of the column block; per chunk R = V - K^ S, X = diag(beta) R, E = T X,
+//    S += K^^T E - the chain from one chunk's state to the next;
+//  * output waves (4..7): wave 4 + m computes, for token block m, Q^ S, the causal score
+//    tiles (Q^ K^^T o M) and y = Q^ S + (Q^ K^^T o M) E, off that chain.
+// Each SIMD runs one wave of each role, so the output work overlaps the state chain.
+// Four barriers per chunk: S and the inputs staged | X written | E written | chunk done.
 // Token-K fragments use the permuted order of the accumulator tiles: slot i < 4 of
 // K-block kk, lane group g is token 32kk + 4g + i, slot 4 + i is token 32kk + 16 + 4g + i
 // (the same permutation for the feature-K fragments of S and K^), so accumulator tiles
@@ -345,19 +349,20 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 // bf16 for bf16 inputs, as the one-factor kernels round their features.
 // S0/ST [B*H, 256, dv] (nullable; S0 == ST allowed), y [B*H, T, dv].
 template <typename TIn, typename TOut, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
                  TOut* __restrict__ y, int64_t T, int64_t n_chunks) {
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
-  constexpr int NS = 2;                      // state / X / E fragments: always hi / lo
   __shared__ __align__(16) float Us[DC][P_DIM];
   __shared__ __align__(16) float Wsm[DC][P_DIM];
-  __shared__ __align__(16) bf16 SB[NS][8][WAVE][8];    // S as B-fragments (hi [, lo])
-  __shared__ __align__(16) bf16 XB[NS][2][WAVE][8];    // diag(beta) R
-  __shared__ __align__(16) bf16 EB[NS][2][WAVE][8];    // E
+  __shared__ __align__(16) bf16 SB[2][8][WAVE][8];     // S as B-fragments, hi / lo
+  __shared__ __align__(16) bf16 XB[2][2][WAVE][8];     // diag(beta) R
+  __shared__ __align__(16) bf16 EB[2][2][WAVE][8];     // E
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool state_role = wave < 4;
+  const int mb = wave & 3;                            // 16-token block of this wave
   const int n = lane & 15, g = lane >> 4;
   // The dv/16 workgroups of a sequence read the same u^, w^ and T.  Workgroups go to the
   // 8 XCDs (each with its own L2) round-robin by linear id, so when B*H is a multiple of 8
@@ -372,13 +377,12 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     bh = xcd + 8 * (slot / NBLK);
     j = (int)(slot % NBLK);
   }
-  const int mb = wave;                                // 16-token block of this wave
   const int col = 16 * j + n;                         // value column of this lane
   // v and beta of this sequence through range-checked buffers: rows past T read 0
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * T * DV, T * DV * (int64_t)sizeof(TIn));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + bh * T, T * 4);
 
-  auto put = [&](auto& dst, int kk, int slot, const float (&x)[4]) {   // dst [NS][K-blocks][WAVE][8]
+  auto put = [&](auto& dst, int kk, int slot, const float (&x)[4]) {   // dst [2][K-blocks][WAVE][8]
     bf16x4 hi, lo;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -395,47 +399,47 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     return f;
   };
 
-  // state tiles: tile qd of this wave holds features f = 16 (4 wave + qd) + 4g + r, column col
+  // state tiles (state waves): tile qd holds features f = 16 (4 wave + qd) + 4g + r, column col
   f32x4 Sacc[4];
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int f = 16 * (4 * wave + qd) + 4 * g + r;
-      Sacc[qd][r] = S0 ? S0[(bh * P_DIM * P_DIM + f) * DV + col] : 0.f;
+      const int f = 16 * (4 * mb + qd) + 4 * g + r;
+      Sacc[qd][r] = (S0 && state_role) ? S0[(bh * P_DIM * P_DIM + f) * DV + col] : 0.f;
     }
   }
 
   // per-chunk inputs, prefetched two chunks ahead into two register sets (the chunk loop
-  // is unrolled by two so each set has a static name); T arrives as this wave's own hi/lo
-  // A-fragments (two K-blocks)
+  // is unrolled by two so each set has a static name).  Threads 0..255 stage u^, threads
+  // 256..511 w^; the state waves also take T (their own hi/lo A-fragments), v and beta.
   struct Inputs {
-    f32x4 pu, pw;
+    f32x4 puw;
     Op8<true> pt[2];
     float pv[4], pb[4];
   };
   auto fetch = [&](Inputs& in, int64_t c) {
     const int64_t rbase = (bh * n_chunks + c) * DC;
-    in.pu = *reinterpret_cast<const f32x4*>(Uh + rbase * P_DIM + 4 * tid);
-    in.pw = *reinterpret_cast<const f32x4*>(Wh + rbase * P_DIM + 4 * tid);
-    const bf16* tf = Tf + (bh * n_chunks + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
+    in.puw = *reinterpret_cast<const f32x4*>((state_role ? Uh : Wh) + rbase * P_DIM + 4 * (tid & 255));
+    if (state_role) {
+      const bf16* tf = Tf + (bh * n_chunks + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
-      in.pt[kk].lo = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16 + 8);
-    }
+      for (int kk = 0; kk < 2; ++kk) {
+        in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
+        in.pt[kk].lo = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16 + 8);
+      }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
-      in.pv[r] = buf_elem<TIn>(rv, t * DV + col);
-      in.pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
+      for (int r = 0; r < 4; ++r) {
+        const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
+        in.pv[r] = buf_elem<TIn>(rv, t * DV + col);
+        in.pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
+      }
     }
   };
 
   auto step = [&](Inputs& in, int64_t c) {
     // ---- stage: inputs to LDS, S to B-fragments
-    *reinterpret_cast<f32x4*>(&Us[0][0] + 4 * tid) = in.pu;
-    *reinterpret_cast<f32x4*>(&Wsm[0][0] + 4 * tid) = in.pw;
+    *reinterpret_cast<f32x4*>((state_role ? &Us[0][0] : &Wsm[0][0]) + 4 * (tid & 255)) = in.puw;
     const Op8<true> tfr[2] = {in.pt[0], in.pt[1]};
     float vv[4], bb[4];
 #pragma unroll
@@ -443,112 +447,110 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
       vv[r] = in.pv[r];
       bb[r] = in.pb[r];
     }
+    if (state_role) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int tile = 4 * wave + qd;
-      const float sx[4] = {Sacc[qd][0], Sacc[qd][1], Sacc[qd][2], Sacc[qd][3]};
-      put(SB, tile >> 1, (tile & 1) * 4, sx);
+      for (int qd = 0; qd < 4; ++qd) {
+        const int tile = 4 * mb + qd;
+        const float sx[4] = {Sacc[qd][0], Sacc[qd][1], Sacc[qd][2], Sacc[qd][3]};
+        put(SB, tile >> 1, (tile & 1) * 4, sx);
+      }
     }
     __syncthreads();
     if (c + 2 < n_chunks) fetch(in, c + 2);
-    // ---- R = V - K^ S, Pq = Q^ S for tokens 16 mb + n (A rows), K = feature
+
+    // ---- R = V - K^ S (state waves) or Q^ S (output waves), tokens 16 mb + n, K = feature
     const int tt = 16 * mb + n;
-    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&Wsm[tt][4 * g]);   // components 4g .. 4g+3
-    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&Us[tt][4 * g]);
-    f32x4 accR = zero4(), accQ = zero4();
+    const float* xs = state_role ? &Wsm[tt][0] : &Us[tt][0];
+    const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + 4 * g);   // components 4g .. 4g+3
+    f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       // slot i < 4: feature (2kk, 4g+i); slot 4+i: feature (2kk+1, 4g+i)
-      const f32x2 wa = *reinterpret_cast<const f32x2*>(&Wsm[tt][2 * kk]);
-      const f32x2 ua = *reinterpret_cast<const f32x2*>(&Us[tt][2 * kk]);
-      float xk[8], xq[8];
+      const f32x2 xa = *reinterpret_cast<const f32x2*>(xs + 2 * kk);
+      float xf[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xk[i] = wa[0] * w4[i];
-        xk[4 + i] = wa[1] * w4[i];
-        xq[i] = ua[0] * u4[i];
-        xq[4 + i] = ua[1] * u4[i];
+        xf[i] = xa[0] * x4[i];
+        xf[4 + i] = xa[1] * x4[i];
       }
-      const Op8<true> sb = frag(SB, kk);
-      accR = mma<SPLIT, true>(make8<SPLIT>(xk), sb, accR);
-      accQ = mma<SPLIT, true>(make8<SPLIT>(xq), sb, accQ);
+      acc = mma<SPLIT, true>(make8<SPLIT>(xf), frag(SB, kk), acc);
     }
     // accumulator lane (n, g) holds token 16 mb + 4g + r, column col
-    {
+    Op8<SPLIT> sc[2];   // output waves: causal score tiles as A-fragments (K-block kk)
+    if (state_role) {
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = bb[r] * (vv[r] - accR[r]);
+      for (int r = 0; r < 4; ++r) x[r] = bb[r] * (vv[r] - acc[r]);
       put(XB, mb >> 1, (mb & 1) * 4, x);
+    } else {
+      // score tile of key block sb against this query block: X = W^_sb U^_mb^T (K = 16),
+      // lane (t = n, g) holds s = 16 sb + 4g + r: (u^_t . w^_s)^2, masked s <= t
+      float ubv[4] = {x4[0], x4[1], x4[2], x4[3]};
+      const Op4<true> uf = make4<true>(ubv);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float xa[8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int sb = 2 * kk + hb;
+          if (sb <= mb) {
+            const f32x4 wb = *reinterpret_cast<const f32x4*>(&Wsm[16 * sb + n][4 * g]);
+            float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
+            const f32x4 X = mma<true, true>(make4<true>(wbv), uf, zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xa[4 * hb + r] = (sb < mb || 4 * g + r <= n) ? X[r] * X[r] : 0.f;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xa[4 * hb + r] = 0.f;
+          }
+        }
+        sc[kk] = make8<SPLIT>(xa);
+      }
     }
     __syncthreads();
 
-    // ---- E = T X for tokens 16 mb + n (A rows of T), K = token
-    f32x4 accE = zero4();
+    // ---- E = T X (state waves), tokens 16 mb + n (A rows of T), K = token
+    if (state_role) {
+      f32x4 accE = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(tfr[kk], frag(XB, kk), accE);
-    {
+      for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(tfr[kk], frag(XB, kk), accE);
       const float ex[4] = {accE[0], accE[1], accE[2], accE[3]};
       put(EB, mb >> 1, (mb & 1) * 4, ex);
     }
     __syncthreads();
 
-    // ---- Y = Pq + (Q^ K^^T o M) E.  Score tile of key block sb against this query block:
-    // X = W^_sb U^_mb^T (K = 16), lane (t = n, g) holds s = 16 sb + 4g + r: (u^_t . w^_s)^2.
-    f32x4 accY = accQ;
-    {
-      float ubv[4] = {u4[0], u4[1], u4[2], u4[3]};
-      const Op4<true> uf = make4<true>(ubv);
+    if (state_role) {
+      // ---- S += K^^T E: tile qd holds features f = 16 a + b with a = 4 mb + qd; as an A
+      // operand its row n is b = n, so slot i of K-block kk carries w^_s[a] w^_s[n] of token s
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (2 * kk <= mb) {
+        const Op8<true> eb = frag(EB, kk);
+        f32x4 wsl[8];
+        float wn[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int sidx = 32 * kk + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+          wsl[i] = *reinterpret_cast<const f32x4*>(&Wsm[sidx][4 * mb]);
+          wn[i] = Wsm[sidx][n];
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
           float xa[8];
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int sb = 2 * kk + hb;
-            if (sb <= mb) {
-              const f32x4 wb = *reinterpret_cast<const f32x4*>(&Wsm[16 * sb + n][4 * g]);
-              float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
-              const f32x4 X = mma<true, true>(make4<true>(wbv), uf, zero4());
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                xa[4 * hb + r] = (sb < mb || 4 * g + r <= n) ? X[r] * X[r] : 0.f;
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) xa[4 * hb + r] = 0.f;
-            }
-          }
-          // A = score rows t (lane n) over key tokens s (K, permuted order), B = E (K = s):
-          // lane (n, g) keeps column col and tokens 4g + r, as accQ does
-          accY = mma<SPLIT, true>(make8<SPLIT>(xa), frag(EB, kk), accY);
+          for (int i = 0; i < 8; ++i) xa[i] = wsl[i][qd] * wn[i];
+          Sacc[qd] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[qd]);
         }
       }
-    }
-    // ---- S += K^^T E: tile qd holds features f = 16 a + b with a = 4 wave + qd; as an A
-    // operand its row n is b = n, so slot i of K-block kk carries w^_s[a] w^_s[n] of token s
+    } else {
+      // ---- y = Q^ S + (Q^ K^^T o M) E: A = score rows t over key tokens s, B = E (K = s)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const Op8<true> eb = frag(EB, kk);
-      f32x4 wsl[8];
-      float wn[8];
+      for (int kk = 0; kk < 2; ++kk)
+        if (2 * kk <= mb) acc = mma<SPLIT, true>(sc[kk], frag(EB, kk), acc);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sidx = 32 * kk + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
-        wsl[i] = *reinterpret_cast<const f32x4*>(&Wsm[sidx][4 * wave]);
-        wn[i] = Wsm[sidx][n];
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = c * DC + 16 * mb + 4 * g + r;
+        if (t < T) Elem<TOut>::store(y, (bh * T + t) * DV + col, acc[r]);
       }
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        float xa[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xa[i] = wsl[i][qd] * wn[i];
-        Sacc[qd] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[qd]);
-      }
-    }
-    // ---- y (accumulator lane (n, g): token 16 mb + 4g + r, column col)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = c * DC + 16 * mb + 4 * g + r;
-      if (t < T) Elem<TOut>::store(y, (bh * T + t) * DV + col, accY[r]);
     }
     __syncthreads();
   };
@@ -562,12 +564,12 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     step(ib, c + 1);
   }
   if (c < n_chunks) step(ia, c);
-  if (ST) {
+  if (ST && state_role) {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int f = 16 * (4 * wave + qd) + 4 * g + r;
+        const int f = 16 * (4 * mb + qd) + 4 * g + r;
         ST[(bh * P_DIM * P_DIM + f) * DV + col] = Sacc[qd][r];
       }
     }

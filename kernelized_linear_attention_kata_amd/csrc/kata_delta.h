@@ -555,7 +555,7 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     __syncthreads();
   };
 
-  Inputs ia, ib;
+  Inputs ia{}, ib{};   // zeroed: the output waves load only puw and never read the rest
   if (n_chunks > 0) fetch(ia, 0);
   if (n_chunks > 1) fetch(ib, 1);
   int64_t c = 0;

@@ -77,6 +77,7 @@ __all__ = [
     "forward_sg_quadratic",
     "final_state_sg",
     "recurrence_sg",
+    "decode_factors_reference",
 ]
 
 
@@ -662,3 +663,31 @@ def recurrence_sg(q, k, v, P):
                 den = Mq.ravel() @ z
                 y[b, h, t] = (Mq.ravel() @ S) / den if den != 0 else 0.0
     return y
+
+
+def decode_factors_reference(S, z, q, k, v, P, mode):
+    """One decode step of KATA-Mg (mode "concat") or KATA-Sigma-g (mode "sum") for N
+    streams: the token's feature is folded into the state, then read out (as the one-factor
+    step).  S [N,H,R,dv], z [N,H,R] with R = g*p*p (concat, factor-major) or p*p (sum);
+    q, k [N,H,d]; v [N,H,dv]; P [H,g,p,d].  Returns (y, S', z')."""
+    S = np.array(S, dtype=np.float64)
+    z = np.array(z, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64); k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64); P = np.asarray(P, dtype=np.float64)
+    N, H = q.shape[:2]
+    y = np.zeros(v.shape)
+    for h in range(H):
+        U = factor_projections(q[:, h], P[h])      # [g, N, p]
+        W = factor_projections(k[:, h], P[h])
+        if mode == "concat":
+            fq = np.concatenate([feature_full(U[i]) for i in range(U.shape[0])], axis=1)
+            fk = np.concatenate([feature_full(W[i]) for i in range(W.shape[0])], axis=1)
+        else:
+            fq = _feature_sum(U)
+            fk = _feature_sum(W)
+        S[:, h] += fk[:, :, None] * v[:, h, None, :]
+        z[:, h] += fk
+        num = np.einsum("nf,nfc->nc", fq, S[:, h])
+        den = np.einsum("nf,nf->n", fq, z[:, h])
+        y[:, h] = np.where(den[:, None] != 0, num / np.where(den[:, None] != 0, den[:, None], 1.0), 0.0)
+    return y, S, z

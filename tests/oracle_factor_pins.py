@@ -148,3 +148,20 @@ def pin_final_states():
                 zm_r += fcat; zs_r += fsum
             res += [rel(Sm[b, h], Sm_r), rel(Ss[b, h], Ss_r), rel(zm[b, h], zm_r), rel(zs[b, h], zs_r)]
     return max(res)
+
+
+def pin_decode_steps(mode):
+    """Decode steps from the final state of a prefix reproduce the forward over the whole
+    sequence at the decoded tokens (the state is the whole history)."""
+    q, k, v, P = fcase(12, B=2, T=12)
+    m = 7
+    fin = O.final_state_mg if mode == "concat" else O.final_state_sg
+    fwd = O.forward_mg_quadratic if mode == "concat" else O.forward_sg_quadratic
+    S, z = fin(k[:, :, :m], v[:, :, :m], P)
+    yfull = fwd(q, k, v, P)
+    worst = 0.0
+    for t in range(m, q.shape[2]):
+        yt, S, z = O.decode_factors_reference(S, z, q[:, :, t], k[:, :, t], v[:, :, t], P, mode)
+        worst = max(worst, rel(yt, yfull[:, :, t]))
+    Sf, zf = fin(k, v, P)
+    return max(worst, rel(S, Sf), rel(z, zf))

@@ -85,3 +85,19 @@ def test_mg_pins_catch(kind):
 @pytest.mark.parametrize("kind", SG_MUTANTS)
 def test_sg_pins_catch(kind):
     assert pins.failing(pins.PINS_SG, _weights_mutant(kind)), kind
+
+
+@pytest.mark.parametrize("mode", ["concat", "sum"])
+def test_decode_factors_pin(mode):
+    assert pins.pin_decode_steps(mode) <= 1e-12
+
+
+def test_decode_factors_mode_matters():
+    """The two decode modes differ once g > 1 (and the sum mode keeps the one-factor state size)."""
+    q, k, v, P = pins.fcase(13, B=1, T=5)
+    Sm, zm = O.final_state_mg(k, v, P)
+    Ss, zs = O.final_state_sg(k, v, P)
+    assert Sm.shape[2] == 2 * Ss.shape[2]
+    ym, _, _ = O.decode_factors_reference(Sm, zm, q[:, :, 0], k[:, :, 0], v[:, :, 0], P, "concat")
+    ys, _, _ = O.decode_factors_reference(Ss, zs, q[:, :, 0], k[:, :, 0], v[:, :, 0], P, "sum")
+    assert pins.rel(ym, ys) > 1e-3

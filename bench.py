@@ -208,7 +208,7 @@ DECODE_METRIC = ("KATA decode tokens/sec: 256 streams x 16 heads, fp32 state (p=
                  "1024 steps after an 8192-token prefill (1 GPU)")
 
 
-def decode_cpu_baseline(dc, budget_s=10.0, delta=False, betas=None):
+def decode_cpu_baseline(dc, budget_s=10.0, delta=False, betas=None, factors=None):
     """The oracle's decode step (or DeltaKATA decode step) on the host over the same
     streams, steps until budget_s."""
     import numpy as np
@@ -218,9 +218,10 @@ def decode_cpu_baseline(dc, budget_s=10.0, delta=False, betas=None):
     from kernelized_linear_attention_kata_amd import inputs as I
 
     N, H, dv = dc.N, dc.H, dc.dv
-    S = np.zeros((N, H, 256, dv))
-    z = np.zeros((N, H, 256))
-    P = dc.P.double().cpu().numpy()
+    rows = 256 * (factors[0].shape[1] if factors is not None and factors[1] == "concat" else 1)
+    S = np.zeros((N, H, rows, dv))
+    z = np.zeros((N, H, rows))
+    P = (factors[0] if factors is not None else dc.P).double().cpu().numpy()
     steps = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s and steps < dc.steps:
@@ -229,13 +230,16 @@ def decode_cpu_baseline(dc, budget_s=10.0, delta=False, betas=None):
         v = O.bf16_bits_to_f64(I.bf16_bits(dc.v[steps]))
         if delta:
             _, S = O.delta_decode_reference(S, q, k, v, P, betas[steps].double().cpu().numpy())
+        elif factors is not None:
+            _, S, z = O.decode_factors_reference(S, z, q, k, v, P, factors[1])
         else:
             _, S, z = O.decode_reference(S, z, q, k, v, P)
         steps += 1
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": N * steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle {'DeltaKATA ' if delta else ''}decode step over all {N} streams x {H} heads, "
+            "sample": f"fp64 oracle {'DeltaKATA ' if delta else ('factor ' if factors is not None else '')}decode step "
+                      f"over all {N} streams x {H} heads, "
                       f"first {steps} steps "
                       f"({dt:.1f} s); the cost per step does not depend on the state's values"}
 
@@ -340,6 +344,11 @@ def bench_decode(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     delta = bool(args.delta)
+    G = args.factors
+    fmode = args.factor_mode
+    if delta and G > 1:
+        print("bench.py --decode takes --delta or --factors, not both", file=sys.stderr)
+        sys.exit(2)
     dc = I.make_decode(device=dev)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
     prefill = None
@@ -357,6 +366,9 @@ def bench_decode(args):
         prefill = {"kernel": "kata_delta_recurrent", "tokens": N * T0, "ms": round(pms, 3),
                    "tokens_per_s": N * T0 / (pms / 1e3), "hbm_GBps": round(pbytes / (pms / 1e3) / 1e9, 1)}
         z0 = None
+    elif G > 1:
+        PF = I.make_factor_projections(H, G, d, seed=4, device=dev)
+        _, S0, z0 = kata.forward_factors(dc.q0, dc.k0, dc.v0, PF, fmode, return_state=True)
     else:
         _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
     S = torch.empty_like(S0)
@@ -367,6 +379,9 @@ def bench_decode(args):
     if delta:
         def run(j):
             kata.decode_step_delta(S, dc.q[j], dc.k[j], dc.v[j], dc.P, betas[j], y=ys[j], stream=stream)
+    elif G > 1:
+        def run(j):
+            kata.decode_step_factors(S, z, dc.q[j], dc.k[j], dc.v[j], PF, fmode, y=ys[j], stream=stream)
     else:
         def run(j):
             kata.decode_step(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
@@ -398,15 +413,22 @@ def bench_decode(args):
     state_bytes = S.numel() * 4 + (z.numel() * 4 if z is not None else 0)
     step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4 + (N * H * 4 if delta else 0)
     achieved = step_bytes / (ms_step / 1e3) / 1e9
-    kernel = "kata_delta_recurrent (T=1, in place)" if delta else "kata_decode_step"
+    kernel = ("kata_delta_recurrent (T=1, in place)" if delta
+              else ("kata_decode_step_factors" if G > 1 else "kata_decode_step"))
     src = source_hash(("kata_delta.h",) if delta else ("kata_decode.h",))
+    fname = {"concat": f"KATA-M{G} ", "sum": f"KATA-Sigma{G} "}[fmode] if G > 1 else ""
     traffic = recorded_traffic("hbm_counters_decode_delta.json", src, "kata_delta_recurrent") if delta else None
-    workload = (f"recurrent {'DeltaKATA ' if delta else ''}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
-                f"canonical fp32 state [{N},{H},256,{dv}]{'' if delta else ' + z'}, prefill T={T0} by "
-                f"{'kata_forward_delta' if delta else 'kata_forward'}, {steps} steps, every 4th key repeating "
-                f"an earlier one" + (", beta uniform in [0.5, 1]" if delta else ""))
+    rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
+    prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
+    workload = (f"recurrent {'DeltaKATA ' if delta else fname}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
+                f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}, prefill T={T0} by "
+                f"{prefill_fn}, {steps} steps, every 4th key repeating an earlier one"
+                + (", beta uniform in [0.5, 1]" if delta else "")
+                + (f", {G} PSD factors per head (P [16,{G},16,64])" if G > 1 else ""))
     result = {
-        "metric": DELTA_DECODE_METRIC if delta else DECODE_METRIC, "value": N * steps / (total_ms / 1e3),
+        "metric": (DELTA_DECODE_METRIC if delta else
+                   (DECODE_METRIC.replace("KATA decode", f"{fname.strip()} decode", 1) if G > 1 else DECODE_METRIC)),
+        "value": N * steps / (total_ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": 0, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 q/k/v, f32 state", "data": "synthetic",
@@ -420,7 +442,8 @@ def bench_decode(args):
     if prefill is not None:
         result["prefill"] = prefill
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = decode_cpu_baseline(dc, delta=delta, betas=betas if delta else None)
+        result["cpu_baseline"] = decode_cpu_baseline(dc, delta=delta, betas=betas if delta else None,
+                                                     factors=(PF, fmode) if G > 1 else None)
     print(json.dumps(result), flush=True)
 
 

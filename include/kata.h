@@ -296,6 +296,18 @@ kata_status kata_forward_factors_timed(const kata_forward_desc* desc, int g, kat
                                        void* workspace, size_t workspace_bytes, void* stream,
                                        void* const* events);
 
+/* One decode step of KATA-Mg / KATA-Sigma-g (same reading as kata_forward_factors) for N
+ * independent streams, in place: the token's feature (concatenated: one 256-row block per
+ * factor; summed: one block) is folded into (S, z), then y = S^T phi(q) / (z . phi(q)).
+ *   S [N,H,R,dv], z [N,H,R] float32 with R = g*p*p (CONCAT, factor-major) or p*p (SUM);
+ *   q, k [N,H,d], v [N,H,dv] in_dtype; P [H,g,p,d] float32; y [N,H,dv] out_dtype.
+ * Supported: g = 1 (runs kata_decode_step), g = 2 or 3; p = 16; (d, dv) = (16, 16) or
+ * (64, 64); in/out dtype F32 or BF16. */
+kata_status kata_decode_step_factors(int64_t N, int64_t H, int d, int dv, int p, int g,
+                                     kata_factor_mode mode, kata_dtype in_dtype, kata_dtype out_dtype,
+                                     float* S, float* z, const void* q, const void* k, const void* v,
+                                     const float* P, void* y, void* stream);
+
 /* DeltaKATA.  [TS-4] (repeated-key overwrite) credits the delta-rule variant of KATA with
  * correcting stale bindings when a key is written again, and [TS-1] / [ABS] name delta
  * rules among the mechanisms studied with KATA's features; none defines it.  The reading

@@ -7,7 +7,7 @@ library; the first call of an entry point does, and fails loudly if it is
 missing.
 """
 _BINDING_NAMES = (
-    "KataError", "abi_version", "backward", "backward_workspace_bytes", "decode_step", "decode_step_decay", "decode_step_delta",
+    "KataError", "abi_version", "backward", "backward_workspace_bytes", "decode_step", "decode_step_decay", "decode_step_delta", "decode_step_factors",
     "forward_decay", "forward_decay_workspace_bytes", "forward_delta", "forward_delta_chunked",
     "forward_delta_chunked_workspace_bytes", "forward_factors",
     "forward_factors_workspace_bytes", "feature_map", "flash_forward", "flash_workspace_bytes",

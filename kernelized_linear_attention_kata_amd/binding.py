@@ -111,6 +111,8 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_delta_chunked_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9 + [sz, vp, vp]
     lib.kata_forward_delta_chunked.restype = ci
     lib.kata_forward_delta_chunked.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9 + [sz, vp]
+    lib.kata_decode_step_factors.restype = ci
+    lib.kata_decode_step_factors.argtypes = [i64, i64, ci, ci, ci, ci, ci, ci, ci] + [vp] * 8
     lib.kata_forward_delta.restype = ci
     lib.kata_forward_delta.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 9
     lib.kata_decode_step_delta.restype = ci
@@ -411,6 +413,33 @@ def forward_factors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.
                                         ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_forward_factors")
     return (y, ST, zT) if return_state else y
+
+
+def decode_step_factors(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        P: torch.Tensor, mode: str = "concat", *, out_dtype: torch.dtype = torch.float32,
+                        y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One KATA-Mg ("concat") / KATA-Sigma-g ("sum") decode step (kata_decode_step_factors),
+    in place on S [N,H,R,dv], z [N,H,R] (R = g*256 for concat, 256 for sum); P [H,g,16,d]."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    g = P.shape[1]
+    dev = q.device
+    rows = (g if mode == "concat" else 1) * P_DIM * P_DIM
+    _need(S, "S", (N, H, rows, dv), torch.float32, dev)
+    _need(z, "z", (N, H, rows), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, g, P_DIM, d), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_factors(N, H, d, dv, P_DIM, g, FACTOR_MODES[mode], _dtype_code(q.dtype),
+                                         _dtype_code(out_dtype), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(P), _ptr(y), _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_factors")
+    return y
 
 
 def forward_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,

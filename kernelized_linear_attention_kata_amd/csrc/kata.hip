@@ -499,6 +499,31 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   return launch_status();
 }
 
+// KATA-Mg / Sigma-g decode step: one workgroup per (stream, head).
+template <int G, bool SUMG>
+kata_status launch_decode_factors(int64_t NH, int H, int d, int dv, kata_dtype in_dtype, kata_dtype out_dtype,
+                                  float* S, float* z, const void* q, const void* k, const void* v, const float* P,
+                                  void* y, hipStream_t st) {
+  const dim3 grid((unsigned)NH);
+#define KATA_DF(TI, TO, DVV)                                                                                   \
+  hipLaunchKernelGGL((kata::kata_decode_step_factors<TI, TO, DVV, G, SUMG>), grid, dim3(256), 0, st, S, z,      \
+                     (const TI*)q, (const TI*)k, (const TI*)v, P, (TO*)y, H, d)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DF(float, float, 64);
+    else if (fi) KATA_DF(float, bf16, 64);
+    else if (fo) KATA_DF(bf16, float, 64);
+    else KATA_DF(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DF(float, float, 16);
+    else if (fi) KATA_DF(float, bf16, 16);
+    else if (fo) KATA_DF(bf16, float, 16);
+    else KATA_DF(bf16, bf16, 16);
+  }
+#undef KATA_DF
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -928,6 +953,27 @@ kata_status kata_forward_delta_chunked(const kata_forward_desc* desc, const void
                                        void* workspace, size_t workspace_bytes, void* stream) {
   return kata_forward_delta_chunked_timed(desc, q, k, v, P, beta, S0, y, ST, workspace, workspace_bytes, stream,
                                           nullptr);
+}
+
+kata_status kata_decode_step_factors(int64_t N, int64_t H, int d, int dv, int p, int g, kata_factor_mode mode,
+                                     kata_dtype in_dtype, kata_dtype out_dtype, float* S, float* z, const void* q,
+                                     const void* k, const void* v, const float* P, void* y, void* stream) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0 || g < 1) return KATA_ERR_SHAPE;
+  if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
+  if (g == 1) return kata_decode_step(N, H, d, dv, p, in_dtype, out_dtype, S, z, q, k, v, P, y, stream);
+  if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N > 0 && H > 0x7fffffff / N) return KATA_ERR_SHAPE;
+  if (N * H == 0) return KATA_OK;
+  if (!S || !z || !q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const bool sum = mode == KATA_FACTORS_SUM;
+  if (g == 2)
+    return sum ? launch_decode_factors<2, true>(N * H, (int)H, d, dv, in_dtype, out_dtype, S, z, q, k, v, P, y, st)
+               : launch_decode_factors<2, false>(N * H, (int)H, d, dv, in_dtype, out_dtype, S, z, q, k, v, P, y, st);
+  return sum ? launch_decode_factors<3, true>(N * H, (int)H, d, dv, in_dtype, out_dtype, S, z, q, k, v, P, y, st)
+             : launch_decode_factors<3, false>(N * H, (int)H, d, dv, in_dtype, out_dtype, S, z, q, k, v, P, y, st);
 }
 
 kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H, int d, int p,

@@ -113,6 +113,112 @@ kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __rest
   }
 }
 
+// One decode step of KATA-Mg (several concatenated PSD factors) or KATA-Sigma-g (summed
+// factors): the item "Variantes" of section 2.3 of the gist.science summary, read as the
+// forward's kata_forward_factors reads it.  grid N*H, block 256.  P [H, G, p, d].
+//  * concat: state S [N,H,G*256,dv], z [N,H,G*256], factor-major; every factor's feature
+//    updates its own block and the read-out sums over the blocks (one division);
+//  * SUMG: state [N,H,256,dv]; the features are summed over the factors first, then the
+//    step is the one-factor one.
+// The state is streamed once in and once out, as in kata_decode_step.
+template <typename TIn, typename TOut, int DV, int G, bool SUMG>
+__global__ void __launch_bounds__(256)
+kata_decode_step_factors(float* __restrict__ S, float* __restrict__ z, const TIn* __restrict__ q,
+                         const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
+                         TOut* __restrict__ y, int H, int d) {
+  constexpr int D = P_DIM * P_DIM;
+  constexpr int NF = SUMG ? 1 : G;          // feature (and state) blocks
+  constexpr int QPR = DV / 4;
+  constexpr int ROWS_PER_IT = 256 / QPR;
+  constexpr int NIT = D / ROWS_PER_IT;
+  __shared__ float su[G][P_DIM], sw[G][P_DIM];
+  __shared__ float fu[NF][D], fw[NF][D];
+  __shared__ float red[4][DV];
+  __shared__ float dred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nh = blockIdx.x;
+  const int h = (int)(nh % H);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float* Ph = P + ((int64_t)h * G + i) * P_DIM * d;
+    const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
+    const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
+    if ((tid & 15) == 0) {
+      su[i][tid >> 4] = u;
+      sw[i][tid >> 4] = w;
+    }
+  }
+  __syncthreads();
+  {
+    const int a = tid >> 4, b = tid & 15;
+    if constexpr (SUMG) {
+      float xu = 0.f, xw = 0.f;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        xu += su[i][a] * su[i][b];
+        xw += sw[i][a] * sw[i][b];
+      }
+      fu[0][tid] = xu;
+      fw[0][tid] = xw;
+    } else {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        fu[i][tid] = su[i][a] * su[i][b];
+        fw[i][tid] = sw[i][a] * sw[i][b];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int c4 = tid % QPR;
+  f32x4 vv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vv[i] = (float)v[nh * DV + 4 * c4 + i];
+  float* Sh = S + nh * (int64_t)(NF * D) * DV;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll 4
+    for (int it = 0; it < NIT; ++it) {
+      const int row = it * ROWS_PER_IT + tid / QPR;
+      f32x4* p = reinterpret_cast<f32x4*>(Sh + (f * D + row) * DV + 4 * c4);
+      f32x4 s = *p;
+      const float fwr = fw[f][row], fur = fu[f][row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] += fwr * vv[i];
+      *p = s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += fur * s[i];
+    }
+  }
+  float* zh = z + nh * (int64_t)(NF * D);
+  float dp = 0.f;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const float zn = zh[f * D + tid] + fw[f][tid];
+    zh[f * D + tid] = zn;
+    dp += fu[f][tid] * zn;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dp += __shfl_xor(dp, off);
+#pragma unroll
+  for (int off = 32; off >= QPR; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+  }
+  if (lane < QPR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * lane + i] = acc[i];
+  }
+  if (lane == 0) dred[wave] = dp;
+  __syncthreads();
+  if (tid < DV) {
+    const float num = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float den = dred[0] + dred[1] + dred[2] + dred[3];
+    Elem<TOut>::store(y, nh * DV + tid, den != 0.f ? num / den : 0.f);
+  }
+}
+
 // Debug feature map: grid n*H, block 256.  layout 0 = full (256), 1 = packed key
 // side (144), 2 = packed query side (144).
 template <typename TIn>

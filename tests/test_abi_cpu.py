@@ -337,3 +337,15 @@ def test_delta_chunked_workspace_and_validation():
                                           None) == Bd.KATA_ERR_WORKSPACE
     empty = Bd.make_desc(0, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
     assert lib.kata_forward_delta_chunked(ctypes.byref(empty), *([None] * 8), None, 0, None) == Bd.KATA_OK
+
+
+def test_decode_factors_validation():
+    lib = _lib_or_skip()
+    fake = ctypes.c_void_p(0x1000)
+    ptrs = [fake] * 7                    # S, z, q, k, v, P, y
+    assert lib.kata_decode_step_factors(4, 16, 64, 64, 16, 4, 0, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_factors(4, 16, 64, 64, 16, 0, 0, 1, 0, *ptrs, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_decode_step_factors(4, 16, 64, 64, 16, 2, 5, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_factors(4, 16, 64, 32, 16, 2, 0, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_factors(4, 16, 64, 64, 16, 2, 1, 1, 0, *ptrs[:6], None, None) == Bd.KATA_ERR_NULL
+    assert lib.kata_decode_step_factors(0, 16, 64, 64, 16, 3, 0, 1, 0, *([None] * 7), None) == Bd.KATA_OK

@@ -259,3 +259,60 @@ def test_sg_long_prefix_and_final_state():
     print(f"[sg long] y prefix {ey:.3e} S_T {eS:.3e} z_T {ez:.3e}", flush=True)
     assert ey <= TOL and eS <= TOL and ez <= TOL
     assert torch.all(torch.isfinite(y.float()))
+
+
+# ---- decode steps (kata_decode_step_factors) --------------------------------------------
+
+@pytest.mark.parametrize("mode", ["concat", "sum"])
+@pytest.mark.parametrize("g", [2, 3])
+def test_factor_decode_against_oracle_and_forward(mode, g):
+    """Prefill by the chunked factor forward (state export), then decode steps: each step
+    against the oracle's step from the same state, and against the forward over the whole
+    sequence."""
+    N, H, T0, steps = 3, 2, 150, 5
+    case = I.make_forward("mid", B=N, H=H, T=T0 + steps, seed=130 + g)
+    P = I.make_factor_projections(H, g, seed=130 + g, per_head=True).to(DEV)
+    q, k, v = (t.to(DEV) for t in (case.q, case.k, case.v))
+    yfull = kata.forward_factors(q, k, v, P, mode, out_dtype=torch.float32)
+    _, S, z = kata.forward_factors(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                                   P, mode, return_state=True)
+    torch.cuda.synchronize()
+    Sh, zh = S.double().cpu().numpy(), z.double().cpu().numpy()
+    Ph = P.double().cpu().numpy()
+    for j in range(steps):
+        t = T0 + j
+        qs, ks, vs = (x[:, :, t].contiguous() for x in (q, k, v))
+        yj = kata.decode_step_factors(S, z, qs, ks, vs, P, mode)
+        torch.cuda.synchronize()
+        yr, Sh, zh = O.decode_factors_reference(Sh, zh, host64(qs.cpu()), host64(ks.cpu()), host64(vs.cpu()), Ph,
+                                                mode)
+        e1 = row_rel(yj.double().cpu().numpy(), yr)
+        e2 = row_rel(yj.double().cpu().numpy(), yfull[:, :, t].double().cpu().numpy())
+        print(f"[factor decode {mode} g={g} step {j}] vs oracle {e1:.2e} vs forward {e2:.2e}", flush=True)
+        assert e1 <= 1e-5 and e2 <= TOL, (j, e1, e2)
+    eS = slice_rel(S.double().cpu().numpy(), Sh)
+    assert eS <= 1e-5
+
+
+def test_factor_decode_workload_sampled():
+    """The decode workload's shape (256 streams x 16 heads) with two concatenated factors:
+    one step from a seeded state, sampled streams against the oracle's step."""
+    dc = I.make_decode(T_prefill=1, steps=1, seed=131)
+    N, H = dc.N, dc.H
+    P = I.make_factor_projections(H, 2, seed=131).to(DEV)
+    g = torch.Generator().manual_seed(131)
+    S = (torch.rand((N, H, 512, 64), generator=g) / 8).to(DEV)
+    z = (torch.rand((N, H, 512), generator=g) + 0.5).to(DEV)
+    S0, z0 = S.double().cpu().numpy(), z.double().cpu().numpy()
+    qs, ks, vs = (x[0].to(DEV) for x in (dc.q, dc.k, dc.v))
+    y = kata.decode_step_factors(S, z, qs, ks, vs, P, "concat")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(131)
+    sel = [(0, 0), (N - 1, H - 1)] + [tuple(x) for x in rng.integers(0, [N, H], size=(4, 2))]
+    for n, h in sel:
+        yr, Sr, zr = O.decode_factors_reference(S0[n:n + 1, h:h + 1], z0[n:n + 1, h:h + 1],
+                                                host64(dc.q[0, n:n + 1, h:h + 1]), host64(dc.k[0, n:n + 1, h:h + 1]),
+                                                host64(dc.v[0, n:n + 1, h:h + 1]), P[h:h + 1].double().cpu().numpy(),
+                                                "concat")
+        assert row_rel(y[n:n + 1, h:h + 1].double().cpu().numpy(), yr) <= 1e-5
+        assert slice_rel(S[n:n + 1, h:h + 1].double().cpu().numpy(), Sr) <= 1e-6

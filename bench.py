@@ -80,6 +80,27 @@ def source_hash(extra=()) -> str:
     return h.hexdigest()[:16]
 
 
+# Headers each bench mode's kernels live in; the mode's counters are keyed by their hash
+# together with all of kata.hip (the forward keeps its narrower hash, see source_hash).
+PATH_HEADERS = {"decay": ("kata_chunk.h",), "backward": ("kata_bwd.h",), "flash": ("kata_flash.h",),
+                "delta": ("kata_delta.h",), "decode": ("kata_decode.h",), "decode_delta": ("kata_delta.h",)}
+
+
+def path_hash(mode: str) -> str:
+    if mode == "forward":
+        return source_hash()
+    if mode.startswith(("m", "sigma")):
+        return source_hash(("kata_chunk.h",))
+    if mode.startswith("decode_"):
+        return source_hash(PATH_HEADERS.get(mode, ("kata_decode.h",)))
+    return source_hash(PATH_HEADERS[mode])
+
+
+def mode_traffic(mode: str, kernel: str):
+    """Recorded HBM bytes per launch of ``kernel`` for a bench mode (None if not current)."""
+    return recorded_traffic(f"hbm_counters_{mode}.json", path_hash(mode), kernel)
+
+
 def recorded_traffic(fname: str, src: str, kernel: str):
     """HBM bytes per launch of ``kernel`` from a committed FETCH_SIZE/WRITE_SIZE summary,
     or None when the summary is missing or was recorded for other kernel sources."""
@@ -325,8 +346,9 @@ def bench_flash(args):
                    "global_batch": B, "seq_len": T, "heads": H},
         "roofline": {"bound": "mfma", "kernel": "kata_flash_attn", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": attn_flops},
+                     "traffic": mode_traffic("flash", "kata_flash_attn"), "flops_per_launch": attn_flops},
         "kernels": {"kata_flash_prep": {"ms": round(prep_ms, 4)}, "kata_flash_attn": {"ms": round(attn_ms, 4)}},
+        "mode": "flash", "source_hash": path_hash("flash"),
         "chunked_path_ms_per_step": round(chunked_ms, 4),
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
     }
@@ -415,9 +437,11 @@ def bench_decode(args):
     achieved = step_bytes / (ms_step / 1e3) / 1e9
     kernel = ("kata_delta_recurrent (T=1, in place)" if delta
               else ("kata_decode_step_factors" if G > 1 else "kata_decode_step"))
-    src = source_hash(("kata_delta.h",) if delta else ("kata_decode.h",))
     fname = {"concat": f"KATA-M{G} ", "sum": f"KATA-Sigma{G} "}[fmode] if G > 1 else ""
-    traffic = recorded_traffic("hbm_counters_decode_delta.json", src, "kata_delta_recurrent") if delta else None
+    mode = ("decode_delta" if delta else
+            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode"))
+    src = path_hash(mode)
+    traffic = mode_traffic(mode, kernel.split(" ")[0])
     rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
     prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
     workload = (f"recurrent {'DeltaKATA ' if delta else fname}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
@@ -436,7 +460,7 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_step": step_bytes},
-        "source_hash": src,
+        "mode": mode, "source_hash": src,
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
     }
     if prefill is not None:
@@ -546,7 +570,8 @@ def bench_delta_forward(args):
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
         "roofline": {"bound": "mfma", "kernel": "kata_delta_chunk", "achieved": round(walk_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(walk_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
-                     "traffic": None, "note": ("the walk is a dependency chain over the chunks of one sequence with "
+                     "traffic": mode_traffic("delta", "kata_delta_chunk"),
+                     "note": ("the walk is a dependency chain over the chunks of one sequence with "
                                                f"{B * H * (dv // 16)} workgroups: bound by per-chunk latency, "
                                                "not by either peak")},
         "kernels": {"kata_delta_prep": {"ms": round(prep_ms, 4), "alg_bytes": prep_bytes,
@@ -555,6 +580,7 @@ def bench_delta_forward(args):
                                          "alg_GBps": round(walk_bytes / (walk_ms / 1e3) / 1e9, 1),
                                          "alg_TFLOPs": round(walk_tflops, 2),
                                          "us_per_chunk": round(walk_ms * 1e3 / n_chunks, 3)}},
+        "mode": "delta", "source_hash": path_hash("delta"),
         "recurrent_form": {"kernel": "kata_delta_recurrent", "ms": round(rec_ms, 3),
                            "tokens_per_s": B * T / (rec_ms / 1e3)},
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
@@ -687,10 +713,10 @@ def bench_backward(args):
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("hbm_counters_backward.json", source_hash(("kata_bwd.h",)), dominant)},
+                     "traffic": mode_traffic("backward", dominant)},
         "step_alg_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
         "kernels": kernels,
-        "source_hash": source_hash(("kata_bwd.h",)),
+        "mode": "backward", "source_hash": path_hash("backward"),
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
     }
     if not args.no_cpu_baseline:
@@ -857,11 +883,10 @@ def main():
         }
     achieved = abytes[dominant] / (per_kernel[dominant] / 1e3) / 1e9
     traffic = None
-    src = source_hash()
-    if G > 1:
-        # the factor paths' host code lies past the forward's part of kata.hip: hash all of it
-        traffic = recorded_traffic(f"hbm_counters_{'sigma' if sg else 'm'}{G}.json",
-                                   source_hash(("kata_chunk.h",)), dominant)
+    mode = (f"{'sigma' if sg else 'm'}{G}" if G > 1 else ("decay" if args.decay else "forward"))
+    src = path_hash(mode)
+    if mode != "forward":
+        traffic = mode_traffic(mode, dominant) if C == 64 else None
     elif os.path.exists(COUNTERS_FILE):
         try:
             cnt = json.load(open(COUNTERS_FILE))
@@ -895,7 +920,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": kernels,
-        "source_hash": src,
+        "mode": mode, "source_hash": src,
         "wall_s_timed": round(wall, 4),
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
     }

@@ -120,3 +120,65 @@ def test_delta_chunked_many_sequences_against_recurrent():
     # y_t = S_t^T phi^(q_t) can cancel to near 0 in single rows, so the per-row ratio is
     # ill-posed (as for gradients): slice-normwise error, every row within 2e-2 of its slice RMS
     assert sy <= 5e-3 and guard <= 2e-2 and eS <= 5e-3
+
+
+def test_forward_at_the_largest_batch_times_heads():
+    """B*H = 65535 sequences (the largest the grid takes), T = 70 (a full chunk and a ragged
+    one), fp32 d = dv = 16: sampled sequences against the oracle."""
+    B, H, T = 65535, 1, 70
+    g = torch.Generator().manual_seed(140)
+    q = (torch.randn((B, H, T, 16), generator=g) / 4)
+    k = (torch.randn((B, H, T, 16), generator=g) / 4)
+    v = (torch.randn((B, H, T, 16), generator=g) / 4)
+    P = torch.randn((H, 16, 16), generator=g) / 4
+    y, ST, zT = kata.forward(q.to(DEV), k.to(DEV), v.to(DEV), P.to(DEV), chunk=64, return_state=True)
+    torch.cuda.synchronize()
+    from oracle import kata_oracle as O
+    rng = np.random.default_rng(140)
+    for b in [0, B - 1] + list(rng.integers(0, B, 6)):
+        ref = O.forward_quadratic(q[b:b + 1].double().numpy(), k[b:b + 1].double().numpy(),
+                                  v[b:b + 1].double().numpy(), P.double().numpy())
+        got = y[b:b + 1].double().cpu().numpy()
+        e = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        Sr, zr = O.final_state(k[b:b + 1].double().numpy(), v[b:b + 1].double().numpy(), P.double().numpy())
+        eS = np.linalg.norm(ST[b:b + 1].double().cpu().numpy() - Sr) / np.linalg.norm(Sr)
+        assert e <= 1e-4 and eS <= 1e-4, (b, e, eS)
+
+
+def test_decode_step_beyond_65535_workgroups():
+    """N*H = 67200 streams (a 1-D grid past 65535), dv = 16, each with a valid KATA state
+    (the sum of phi(k) v^T over 4 seeded keys): sampled streams' steps against a float64
+    evaluation of the same update on the host."""
+    N, H, d = 4200, 16, 16
+    g = torch.Generator().manual_seed(141)
+    P = torch.randn((H, 16, d), generator=g) / 4
+
+    def feat(x):   # phi(x) = vec(u u^T), u = P_h x, for x [..., H, d]
+        u = torch.einsum("had,...hd->...ha", P, x)
+        return (u[..., :, None] * u[..., None, :]).flatten(-2)
+
+    k0 = torch.randn((4, N, H, d), generator=g) / 4
+    v0 = torch.randn((4, N, H, d), generator=g) / 4
+    f0 = feat(k0)                                            # [4, N, H, 256]
+    S = torch.einsum("jnhf,jnhc->nhfc", f0, v0).contiguous()
+    z = f0.sum(0).contiguous()
+    q, k, v = (torch.randn((N, H, d), generator=g) / 4 for _ in range(3))
+    Sd, zd = S.to(DEV), z.to(DEV)
+    y = kata.decode_step(Sd, zd, q.to(DEV), k.to(DEV), v.to(DEV), P.to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(141)
+    idx = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 300)]))
+    Pd = P.double()
+    u = torch.einsum("had,nhd->nha", Pd, q[idx].double())
+    w = torch.einsum("had,nhd->nha", Pd, k[idx].double())
+    fu = (u[..., :, None] * u[..., None, :]).flatten(2)
+    fw = (w[..., :, None] * w[..., None, :]).flatten(2)
+    S2 = S[idx].double() + fw[..., None] * v[idx].double()[:, :, None, :]
+    z2 = z[idx].double() + fw
+    yr = torch.einsum("nhf,nhfc->nhc", fu, S2) / torch.einsum("nhf,nhf->nh", fu, z2)[..., None]
+    yg = y[torch.as_tensor(idx, device=DEV)].double().cpu()
+    Sg = Sd[torch.as_tensor(idx, device=DEV)].double().cpu()
+    e = float(((yg - yr).norm(dim=-1) / yr.norm(dim=-1)).max())
+    eS = float(((Sg - S2).flatten(2).norm(dim=-1) / S2.flatten(2).norm(dim=-1)).max())
+    print(f"[decode 67200 streams] y {e:.2e} S {eS:.2e}", flush=True)
+    assert e <= 1e-5 and eS <= 1e-6

@@ -18,7 +18,10 @@ reach their working level, and a handful of warmup steps (a few ms) is not enoug
 Prints ONE JSON line with the metric, a roofline entry for the dominant kernel
 (its duration measured live with HIP events recorded by the library on the
 stream it launches on) and the CPU oracle timed on a bounded sample of the same
-workload on the host's cores.
+workload on the host's cores.  In the K timed steps only the dominant kernel's launch
+stamps events (each stamping launch adds a few microseconds of dispatch gap); the
+per-kernel breakdown comes from a pass of K steps before them in which every launch
+stamps one.
 
     python bench.py [--steps K] [--warmup W] [--chunk C] [--no-cpu-baseline]
     python bench.py --decode     # the recurrent decode step instead (its own JSON line)
@@ -55,6 +58,49 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_chunk_intra")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def time_steps(torch, step, stream, steps, n_events, stamp):
+    """Run exactly `steps` calls step(i, events) on `stream` between two device
+    synchronisations.  Only the events at the indices in `stamp` reach the launches (the
+    rest are None): each launch that stamps an event costs a few microseconds of dispatch
+    gap, so the timed steps stamp only the dominant kernel.  Returns (ms per step, wall
+    seconds, the per-step event lists)."""
+    evs = [[torch.cuda.Event(enable_timing=True) if j in stamp else None for j in range(n_events)]
+           for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [t0, t1] + [e for es in evs for e in es if e is not None]:
+        e.record(stream)     # torch creates the HIP event on its first record: do it before timing
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0, evs
+
+
+def mean_interval(evs, a, b):
+    return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
+
+
+def kernel_breakdown(torch, step, stream, steps, names):
+    """Per-kernel times from a pass before the timed steps in which every launch stamps its
+    start (and the last its end): start to start of the next launch, so each includes the
+    dispatch gap after it.  The pass picks the dominant kernel; value and roofline come
+    from the timed steps."""
+    n = len(names) + 1
+    _, _, evs = time_steps(torch, step, stream, steps, n, range(n))
+    return {name: mean_interval(evs, j, j + 1) for j, name in enumerate(names)}
+
+
+def timed_dominant(torch, step, stream, steps, names, dominant):
+    """The timed steps: (ms per step, wall seconds, the dominant kernel's mean duration in
+    ms, measured on the same steps from the events its launch stamps)."""
+    j = names.index(dominant)
+    ms_step, wall, evs = time_steps(torch, step, stream, steps, len(names) + 1, (j, j + 1))
+    return ms_step, wall, mean_interval(evs, j, j + 1)
 
 
 FORWARD_SOURCES = ("kata_common.h", "kata_chunk.h", "kata_scan.h")
@@ -305,19 +351,10 @@ def bench_flash(args):
         torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    names = ("kata_flash_prep", "kata_flash_attn")
+    prep_ms = kernel_breakdown(torch, step, stream, args.steps, names)["kata_flash_prep"]
+    ms_step, _, attn_ms = timed_dominant(torch, step, stream, args.steps, names, "kata_flash_attn")
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for e in [t0, t1] + [e for es in evs for e in es]:
-        e.record(stream)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     flops = flash_algorithmic_flops(B, H, T)
     attn_flops = flops - B * H * T * 4 * 16 * d
     achieved = attn_flops / (attn_ms / 1e3) / 1e12
@@ -531,19 +568,9 @@ def bench_delta_forward(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for e in [t_start, t_end] + [e for es in evs for e in es]:
-        e.record(stream)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    walk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    names = ("kata_delta_prep", "kata_delta_chunk")
+    prep_ms = kernel_breakdown(torch, step, stream, args.steps, names)["kata_delta_prep"]
+    ms_step, _, walk_ms = timed_dominant(torch, step, stream, args.steps, names, "kata_delta_chunk")
     # the token-recurrent form once, for comparison
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     r0.record(stream)
@@ -681,26 +708,16 @@ def bench_backward(args):
     settle_s = time.perf_counter() - settle0
     for i in range(args.warmup):
         step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for e in [t0, t1] + [e for es in evs for e in es]:
-        e.record(stream)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    per_kernel = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-                  for j, name in enumerate(BWD_KERNELS)}
+    per_kernel = kernel_breakdown(torch, step, stream, args.steps, BWD_KERNELS)
+    dominant = max(per_kernel, key=per_kernel.get)
+    ms_step, _, dom_ms = timed_dominant(torch, step, stream, args.steps, BWD_KERNELS, dominant)
     abytes = bwd_algorithmic_bytes(B, H, T, d, dv, n_leaf, 2)
     kernels = {name: {"ms": round(ms, 4), "alg_bytes": abytes[name],
                       "alg_GBps": round(abytes[name] / (ms / 1e3) / 1e9, 1),
                       "hbm_frac": round(abytes[name] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
                for name, ms in per_kernel.items()}
-    dominant = max(per_kernel, key=per_kernel.get)
-    achieved = abytes[dominant] / (per_kernel[dominant] / 1e3) / 1e9
+    kernels[dominant]["ms_timed_steps"] = round(dom_ms, 4)
+    achieved = abytes[dominant] / (dom_ms / 1e3) / 1e9
     step_bytes = sum(abytes.values())
     result = {
         "metric": BWD_METRIC, "value": B * T / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
@@ -844,23 +861,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    for e in [t_start, t_end] + [e for es in evs for e in es]:
-        e.record(stream)     # torch creates the HIP event on its first record: do it before timing
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    per_kernel = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-                  for j, name in enumerate(KERNELS)}
+    per_kernel = kernel_breakdown(torch, step, stream, args.steps, KERNELS)
+    dominant = max(per_kernel, key=per_kernel.get)
+    ms_per_step, wall, dom_ms = timed_dominant(torch, step, stream, args.steps, KERNELS, dominant)
+    total_ms = ms_per_step * args.steps
 
     tokens_per_s = B * T / (ms_per_step / 1e3)
     sg = G > 1 and args.factor_mode == "sum"
@@ -868,7 +872,6 @@ def main():
     fac_note = f" with {G} {fac_word} PSD factors (P [16,{G},16,64], no state export)" if G > 1 else ""
     abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=1 if sg else G)
     aflops = algorithmic_flops(B, H, T, d, dv, C, factors=G, cross=sg)
-    dominant = max(per_kernel, key=per_kernel.get)
     kernels = {}
     for name in KERNELS:
         ms = per_kernel[name]
@@ -881,7 +884,8 @@ def main():
             "alg_bytes": abytes[name],
             "alg_flops": aflops[name],
         }
-    achieved = abytes[dominant] / (per_kernel[dominant] / 1e3) / 1e9
+    kernels[dominant]["ms_timed_steps"] = round(dom_ms, 4)
+    achieved = abytes[dominant] / (dom_ms / 1e3) / 1e9
     traffic = None
     mode = (f"{'sigma' if sg else 'm'}{G}" if G > 1 else ("decay" if args.decay else "forward"))
     src = path_hash(mode)

@@ -125,8 +125,10 @@ kata_status kata_forward(const kata_forward_desc* desc,
  * of kata_chunk_intra and events[3] at its end, so a caller can time each kernel of
  * the chunked forward on the stream it runs on.  The launches record the events
  * themselves (no extra commands enter the stream).  events == NULL behaves exactly
- * like kata_forward; a NULL element returns KATA_ERR_NULL.  When nothing is launched
- * for the chunked path (B*H == 0 or T == 0) no event is recorded. */
+ * like kata_forward.  A NULL element is not stamped: every stamped launch costs a few
+ * microseconds of dispatch gap, so a caller timing one kernel passes only its two.
+ * When nothing is launched (B*H == 0 or T == 0) no event is recorded.  The same rule
+ * holds for every *_timed entry point below. */
 kata_status kata_forward_timed(const kata_forward_desc* desc,
                                const void* q, const void* k, const void* v,
                                const float* P,

@@ -185,6 +185,23 @@ def forward_workspace_bytes(B, H, T, d, dv, chunk, in_dtype=torch.bfloat16, out_
     return int(n.value)
 
 
+
+def _event_array(events, n: int, stream, dev):
+    """The C array of hipEvent_t handles for a *_timed entry point, or None.
+
+    events: None, or n torch.cuda.Event(enable_timing=True) objects, any of which may be
+    None (that stamp is skipped).  torch creates the HIP event lazily on its first
+    record, so an event without one is recorded once first on the launch stream."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"events: {n} torch.cuda.Event objects (or None)")
+    s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
+    for e in events:
+        if e is not None and e.cuda_event == 0:
+            e.record(s_obj)
+    return (ctypes.c_void_p * n)(*[ctypes.c_void_p(None if e is None else e.cuda_event) for e in events])
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, chunk: int = 64, *,
             S0: Optional[torch.Tensor] = None, z0: Optional[torch.Tensor] = None,
             out_dtype: Optional[torch.dtype] = None, return_state: bool = False, scan: str = "assoc",
@@ -235,15 +252,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
     else:
         ST = zT = None
     sh = _stream_handle(stream, dev)
-    evarr = None
-    if events is not None:
-        if len(events) != 4:
-            raise ValueError("events: four torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:      # torch creates the HIP event lazily on first record
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 4, stream, dev)
     st = lib.kata_forward_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(S0), _ptr(z0),
                                 _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
@@ -302,15 +311,7 @@ def forward_decay(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
         ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
         zT = torch.empty((B, H, P_DIM * P_DIM), dtype=torch.float32, device=dev)
     sh = _stream_handle(stream, dev)
-    evarr = None
-    if events is not None:
-        if len(events) != 4:
-            raise ValueError("events: four torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 4, stream, dev)
     st = lib.kata_forward_decay_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(lam), _ptr(S0),
                                       _ptr(z0), _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
                                       ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
@@ -399,15 +400,7 @@ def forward_factors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.
         ST = torch.empty((B, H, rows, dv), dtype=torch.float32, device=dev)
         zT = torch.empty((B, H, rows), dtype=torch.float32, device=dev)
     sh = _stream_handle(stream, dev)
-    evarr = None
-    if events is not None:
-        if len(events) != 4:
-            raise ValueError("events: four torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 4, stream, dev)
     st = lib.kata_forward_factors_timed(ctypes.byref(desc), g, FACTOR_MODES[mode], _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(P), _ptr(S0), _ptr(z0), _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
                                         ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
@@ -514,15 +507,7 @@ def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: 
     elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
         raise ValueError("workspace too small")
     ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev) if return_state else None
-    evarr = None
-    if events is not None:
-        if len(events) != 3:
-            raise ValueError("events: three torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 3, stream, dev)
     st = lib.kata_forward_delta_chunked_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta),
                                               _ptr(S0), _ptr(y), _ptr(ST), _ptr(workspace),
                                               ctypes.c_size_t(workspace.numel() * workspace.element_size()),
@@ -593,15 +578,7 @@ def flash_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
         raise ValueError("workspace too small")
     sh = _stream_handle(stream, dev)
-    evarr = None
-    if events is not None:
-        if len(events) != 3:
-            raise ValueError("events: three torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 3, stream, dev)
     st = lib.kata_flash_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y), _ptr(workspace),
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_flash_forward")
@@ -671,15 +648,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
     elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
         raise ValueError("workspace too small")
     sh = _stream_handle(stream, dev)
-    evarr = None
-    if events is not None:
-        if len(events) != 8:
-            raise ValueError("events: eight torch.cuda.Event objects")
-        s_obj = stream if stream is not None else torch.cuda.current_stream(dev)
-        for e in events:
-            if e.cuda_event == 0:
-                e.record(s_obj)
-        evarr = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    evarr = _event_array(events, 8, stream, dev)
     st = lib.kata_backward_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(S0), _ptr(z0),
                                  _ptr(gy), _ptr(gST), _ptr(gzT), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dP),
                                  _ptr(dS0), _ptr(dz0), _ptr(workspace),

@@ -569,7 +569,6 @@ kata_status kata_forward_timed(const kata_forward_desc* desc, const void* q, con
   hipEvent_t* evp = nullptr;
   if (events) {
     for (int i = 0; i < 4; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
     evp = ev;
@@ -608,7 +607,6 @@ kata_status kata_flash_forward(const kata_forward_desc* desc, const void* q, con
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   if (events) {
     for (int i = 0; i < 3; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
   }
@@ -672,7 +670,6 @@ kata_status kata_backward_timed(const kata_forward_desc* desc, const void* q, co
   hipEvent_t* evp = nullptr;
   if (events) {
     for (int i = 0; i < 8; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
     evp = ev;
@@ -719,7 +716,6 @@ kata_status kata_forward_decay_timed(const kata_forward_desc* desc, const void* 
   hipEvent_t* evp = nullptr;
   if (events) {
     for (int i = 0; i < 4; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
     evp = ev;
@@ -865,7 +861,6 @@ kata_status kata_forward_factors_timed(const kata_forward_desc* desc, int g, kat
   hipEvent_t* evp = nullptr;
   if (events) {
     for (int i = 0; i < 4; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
     evp = ev;
@@ -926,7 +921,6 @@ kata_status kata_forward_delta_chunked_timed(const kata_forward_desc* desc, cons
   hipEvent_t* evp = nullptr;
   if (events) {
     for (int i = 0; i < 3; ++i) {
-      if (!events[i]) return KATA_ERR_NULL;
       ev[i] = (hipEvent_t)events[i];
     }
     evp = ev;

@@ -352,7 +352,7 @@ def bench_flash(args):
     for i in range(args.warmup):
         step(i)
     names = ("kata_flash_prep", "kata_flash_attn")
-    prep_ms = kernel_breakdown(torch, step, stream, args.steps, names)["kata_flash_prep"]
+    split = kernel_breakdown(torch, step, stream, args.steps, names)
     ms_step, _, attn_ms = timed_dominant(torch, step, stream, args.steps, names, "kata_flash_attn")
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     flops = flash_algorithmic_flops(B, H, T)
@@ -384,7 +384,8 @@ def bench_flash(args):
         "roofline": {"bound": "mfma", "kernel": "kata_flash_attn", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": mode_traffic("flash", "kata_flash_attn"), "flops_per_launch": attn_flops},
-        "kernels": {"kata_flash_prep": {"ms": round(prep_ms, 4)}, "kata_flash_attn": {"ms": round(attn_ms, 4)}},
+        "kernels": {"kata_flash_prep": {"ms": round(split["kata_flash_prep"], 4)},
+                    "kata_flash_attn": {"ms": round(split["kata_flash_attn"], 4), "ms_timed_steps": round(attn_ms, 4)}},
         "mode": "flash", "source_hash": path_hash("flash"),
         "chunked_path_ms_per_step": round(chunked_ms, 4),
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},
@@ -569,7 +570,8 @@ def bench_delta_forward(args):
         step(i)
     torch.cuda.synchronize()
     names = ("kata_delta_prep", "kata_delta_chunk")
-    prep_ms = kernel_breakdown(torch, step, stream, args.steps, names)["kata_delta_prep"]
+    split = kernel_breakdown(torch, step, stream, args.steps, names)
+    prep_ms = split["kata_delta_prep"]
     ms_step, _, walk_ms = timed_dominant(torch, step, stream, args.steps, names, "kata_delta_chunk")
     # the token-recurrent form once, for comparison
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -603,7 +605,8 @@ def bench_delta_forward(args):
                                                "not by either peak")},
         "kernels": {"kata_delta_prep": {"ms": round(prep_ms, 4), "alg_bytes": prep_bytes,
                                         "alg_GBps": round(prep_bytes / (prep_ms / 1e3) / 1e9, 1)},
-                    "kata_delta_chunk": {"ms": round(walk_ms, 4), "alg_bytes": walk_bytes,
+                    "kata_delta_chunk": {"ms": round(split["kata_delta_chunk"], 4), "ms_timed_steps": round(walk_ms, 4),
+                                         "alg_bytes": walk_bytes,
                                          "alg_GBps": round(walk_bytes / (walk_ms / 1e3) / 1e9, 1),
                                          "alg_TFLOPs": round(walk_tflops, 2),
                                          "us_per_chunk": round(walk_ms * 1e3 / n_chunks, 3)}},

@@ -478,10 +478,13 @@ def forward_delta_chunked_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.b
 def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,
                           S0: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                           return_state: bool = False, y: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+                          workspace: Optional[torch.Tensor] = None, ST: Optional[torch.Tensor] = None,
+                          stream=None, events=None):
     """DeltaKATA causal forward in the chunked form (kata_forward_delta_chunked); same
-    definition and arguments as forward_delta.  events: optional three torch.cuda.Event
-    (start of the per-chunk pass, start and end of the walk)."""
+    definition and arguments as forward_delta.  ST: optional preallocated final state
+    [B,H,256,dv] fp32 (implies return_state; may be S0 itself, updated in place).
+    events: optional three torch.cuda.Event (start of the per-chunk pass, start and end
+    of the walk)."""
     B, H, T, d = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -506,7 +509,11 @@ def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: 
         workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
     elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < n.value:
         raise ValueError("workspace too small")
-    ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev) if return_state else None
+    if ST is not None:
+        _need(ST, "ST", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        return_state = True
+    elif return_state:
+        ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
     evarr = _event_array(events, 3, stream, dev)
     st = lib.kata_forward_delta_chunked_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta),
                                               _ptr(S0), _ptr(y), _ptr(ST), _ptr(workspace),

@@ -22,7 +22,7 @@
 // buffers so no third barrier is needed.  The state is read once and written once.
 #pragma once
 
-#include "kata_common.h"
+#include "kata_chunk.h"   // kata_common.h, and row_plus (DPP row rotation)
 
 namespace kata {
 
@@ -192,6 +192,19 @@ template <> __device__ __forceinline__ float buf_elem<bf16>(__amdgpu_buffer_rsrc
   return bf16_bits_to_float((u16)__builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0));
 }
 
+// The raw bits of one element (0 past the buffer's end), and their value: a prefetch keeps
+// the bits and converts them where they are used, so the load is not waited for at issue.
+template <typename TIn> __device__ __forceinline__ uint32_t buf_bits(__amdgpu_buffer_rsrc_t r, int idx);
+template <> __device__ __forceinline__ uint32_t buf_bits<float>(__amdgpu_buffer_rsrc_t r, int idx) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0);
+}
+template <> __device__ __forceinline__ uint32_t buf_bits<bf16>(__amdgpu_buffer_rsrc_t r, int idx) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0);
+}
+template <typename TIn> __device__ __forceinline__ float bits_value(uint32_t b) {
+  return __uint_as_float(sizeof(TIn) == 2 ? b << 16 : b);
+}
+
 // grid (n_chunks, B*H), block 256.  Writes for every token of the chunk u^ = Pq/|Pq| and
 // w^ = Pk/|Pk| (0 where the projection is 0, and past T) to Uo, Wo [B*H, n_chunks*64, 16],
 // and T of the chunk to Tf [B*H, n_chunks, 4, 2, 64, 2, 8] bf16, already in the form the
@@ -331,23 +344,39 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   }
 }
 
+// Packed state.  Every update adds phi^(k) e^T with phi^(k) = vec(u u^T)/|u|^2 a
+// symmetric 16 x 16 matrix, and every read S^T phi^(x) sees only the symmetric part of S
+// (phi^(x) is symmetric).  The walk therefore keeps that part in the packed circulant
+// order of the one-factor kernels: slot (delta, a) = 16 delta + a stands for the pair
+// {a, (a + delta) mod 16}, delta = 0..8 (for delta = 8 the slots a >= 8 repeat a < 8).
+// Writes add the packed feature w_a w_(a+delta) unweighted; reads weight it by 1 on the
+// diagonal, 2 off it, and 0 for the repeated slots, so the packed inner product equals
+// the full one.  That is 144 rows instead of 256 (136 distinct): the state contractions
+// shrink from 8 to 5 K-blocks and from 16 to 9 state tiles.  The walk starts from the
+// symmetric part of S0 and exports ST = S0 + (packed change) at both entries of each
+// pair, so S0's antisymmetric part, which no read sees, reaches ST unchanged (and a walk
+// that writes nothing returns S0 bit for bit).
+//
 // grid (dv/16, B*H), block 512: 8 waves in two roles that share the staged fragments.
-//  * state waves (0..3): wave w owns the 16-token block w of every chunk and the state rows
-//    64w .. 64w+63 of the column block; per chunk R = V - K^ S, X = diag(beta) R, E = T X,
-//    S += K^^T E - the chain from one chunk's state to the next;
+//  * state waves (0..3): wave w owns the 16-token block w of every chunk and the packed
+//    state tiles delta = w and w + 4 (wave 0 also delta = 8) of the column block; per chunk
+//    R = V - K^ S, X = diag(beta) R, E = T X, S += K^^T E - the chain from one chunk's
+//    state to the next;
 //  * output waves (4..7): wave 4 + m computes, for token block m, Q^ S, the causal score
 //    tiles (Q^ K^^T o M) and y = Q^ S + (Q^ K^^T o M) E, off that chain.
 // Each SIMD runs one wave of each role, so the output work overlaps the state chain.
 // Four barriers per chunk: S and the inputs staged | X written | E written | chunk done.
 // Token-K fragments use the permuted order of the accumulator tiles: slot i < 4 of
 // K-block kk, lane group g is token 32kk + 4g + i, slot 4 + i is token 32kk + 16 + 4g + i
-// (the same permutation for the feature-K fragments of S and K^), so accumulator tiles
-// are stored as fragments with one 8-byte store per lane.  Precision: the state, the
-// corrections X and E, T and the 16-dim cosine tiles are hi/lo bf16 operands (~16
-// significant bits: these are where sums cancel); the 256-entry feature fragments
-// (products of unit-vector components) are hi/lo only for fp32 inputs (SPLIT) and single
-// bf16 for bf16 inputs, as the one-factor kernels round their features.
+// (and slot i < 4 of the feature K-block kk is (2kk, 4g + i), slot 4 + i is
+// (2kk + 1, 4g + i)), so accumulator tiles are stored as fragments with one 8-byte store
+// per lane.  Precision: the state, the corrections X and E, T and the 16-dim cosine tiles
+// are hi/lo bf16 operands (~16 significant bits: these are where sums cancel); the
+// packed feature fragments (products of unit-vector components) are hi/lo only for fp32
+// inputs (SPLIT) and single bf16 for bf16 inputs, as the one-factor kernels round theirs.
 // S0/ST [B*H, 256, dv] (nullable; S0 == ST allowed), y [B*H, T, dv].
+constexpr int DKB = 5;   // feature K-blocks of the packed state: delta pairs (0,1) .. (8, 9 = none)
+
 template <typename TIn, typename TOut, int DV>
 __global__ void __launch_bounds__(512)
 kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const bf16* __restrict__ Tf,
@@ -356,7 +385,7 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
   __shared__ __align__(16) float Us[DC][P_DIM];
   __shared__ __align__(16) float Wsm[DC][P_DIM];
-  __shared__ __align__(16) bf16 SB[2][8][WAVE][8];     // S as B-fragments, hi / lo
+  __shared__ __align__(16) bf16 SB[2][DKB][WAVE][8];   // packed S as B-fragments, hi / lo
   __shared__ __align__(16) bf16 XB[2][2][WAVE][8];     // diag(beta) R
   __shared__ __align__(16) bf16 EB[2][2][WAVE][8];     // E
   const int tid = threadIdx.x, lane = tid & 63;
@@ -399,15 +428,26 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     return f;
   };
 
-  // state tiles (state waves): tile qd holds features f = 16 (4 wave + qd) + 4g + r, column col
-  f32x4 Sacc[4];
+  // Packed state tiles (state waves): tile jt is diagonal dl(jt) = w, w + 4, and 8 (wave 0
+  // only); lane (n, g) holds slots (dl, a = 4g + r), column col.  sym0 gives the symmetric
+  // part of S0 at the lane's pair {a, b} (full row indices 16 a + b and 16 b + a).
+  const bool own8 = state_role && wave == 0;
+  auto dl = [&](int jt) { return jt == 2 ? 8 : wave + 4 * jt; };
+  auto s0_at = [&](int a, int b) { return S0[(bh * P_DIM * P_DIM + 16 * a + b) * DV + col]; };
+  auto sym0 = [&](int a, int b) { return 0.5f * (s0_at(a, b) + s0_at(b, a)); };
+  f32x4 Sacc[3];
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
+  for (int jt = 0; jt < 3; ++jt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int f = 16 * (4 * mb + qd) + 4 * g + r;
-      Sacc[qd][r] = (S0 && state_role) ? S0[(bh * P_DIM * P_DIM + f) * DV + col] : 0.f;
+      const int a = 4 * g + r, b = (a + dl(jt)) & 15;
+      Sacc[jt][r] = (S0 && state_role && (jt < 2 || own8)) ? sym0(a, b) : 0.f;
     }
+  }
+  // the K-block 4 slots 4..7 stand for delta = 9, which does not exist: zero once
+  if (tid < 2 * WAVE) {
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    *reinterpret_cast<bf16x4*>(&SB[tid >> 6][DKB - 1][lane][4]) = z;
   }
 
   // per-chunk inputs, prefetched two chunks ahead into two register sets (the chunk loop
@@ -416,7 +456,8 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
   struct Inputs {
     f32x4 puw;
     Op8<true> pt[2];
-    float pv[4], pb[4];
+    uint32_t pv[4];   // raw bits of v (converted at use)
+    float pb[4];
   };
   auto fetch = [&](Inputs& in, int64_t c) {
     const int64_t rbase = (bh * n_chunks + c) * DC;
@@ -431,121 +472,139 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
-        in.pv[r] = buf_elem<TIn>(rv, t * DV + col);
+        in.pv[r] = buf_bits<TIn>(rv, t * DV + col);
         in.pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
       }
     }
   };
 
+  const int rot = (lane & ~15) | ((n + wave) & 15);   // lane of the row rotated by w
+
   auto step = [&](Inputs& in, int64_t c) {
-    // ---- stage: inputs to LDS, S to B-fragments
+    // ---- stage: inputs to LDS, packed S to B-fragments (K-block dl / 2, half dl % 2)
     *reinterpret_cast<f32x4*>((state_role ? &Us[0][0] : &Wsm[0][0]) + 4 * (tid & 255)) = in.puw;
     const Op8<true> tfr[2] = {in.pt[0], in.pt[1]};
     float vv[4], bb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      vv[r] = in.pv[r];
+      vv[r] = bits_value<TIn>(in.pv[r]);
       bb[r] = in.pb[r];
     }
     if (state_role) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int tile = 4 * mb + qd;
-        const float sx[4] = {Sacc[qd][0], Sacc[qd][1], Sacc[qd][2], Sacc[qd][3]};
-        put(SB, tile >> 1, (tile & 1) * 4, sx);
+      for (int jt = 0; jt < 3; ++jt) {
+        if (jt < 2 || own8) {
+          const int d = dl(jt);
+          const float sx[4] = {Sacc[jt][0], Sacc[jt][1], Sacc[jt][2], Sacc[jt][3]};
+          put(SB, d >> 1, (d & 1) * 4, sx);
+        }
       }
     }
     __syncthreads();
     if (c + 2 < n_chunks) fetch(in, c + 2);
 
-    // ---- R = V - K^ S (state waves) or Q^ S (output waves), tokens 16 mb + n, K = feature
+    // ---- R = V - K^ S (state waves) or Q^ S (output waves), tokens 16 mb + n, K = packed
+    // slot.  xr[m] = components 4g + 4m .. 4g + 4m + 3 (mod 16) of the token's projection,
+    // so component (4g + i + delta) mod 16 is xr[(i + delta) / 4 % 4][(i + delta) % 4].
     const int tt = 16 * mb + n;
     const float* xs = state_role ? &Wsm[tt][0] : &Us[tt][0];
-    const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + 4 * g);   // components 4g .. 4g+3
+    f32x4 xr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const f32x4*>(xs + ((4 * g + 4 * m) & 15));
+    auto comp = [&](int e) { return xr[(e >> 2) & 3][e & 3]; };
+    const float w8 = g < 2 ? 2.f : 0.f;                // read weight of slot (8, 4g + i)
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      // slot i < 4: feature (2kk, 4g+i); slot 4+i: feature (2kk+1, 4g+i)
-      const f32x2 xa = *reinterpret_cast<const f32x2*>(xs + 2 * kk);
+    for (int kk = 0; kk < DKB; ++kk) {
+      const int d0 = 2 * kk, d1 = 2 * kk + 1;
+      const float wt0 = d0 == 0 ? 1.f : (d0 == 8 ? w8 : 2.f);
+      const float wt1 = d1 == 9 ? 0.f : 2.f;
       float xf[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xf[i] = xa[0] * x4[i];
-        xf[4 + i] = xa[1] * x4[i];
+        xf[i] = comp(i) * comp(i + d0) * wt0;
+        xf[4 + i] = comp(i) * comp(i + d1) * wt1;
       }
       acc = mma<SPLIT, true>(make8<SPLIT>(xf), frag(SB, kk), acc);
     }
     // accumulator lane (n, g) holds token 16 mb + 4g + r, column col
-    Op8<SPLIT> sc[2];   // output waves: causal score tiles as A-fragments (K-block kk)
     if (state_role) {
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = bb[r] * (vv[r] - acc[r]);
       put(XB, mb >> 1, (mb & 1) * 4, x);
-    } else {
-      // score tile of key block sb against this query block: X = W^_sb U^_mb^T (K = 16),
-      // lane (t = n, g) holds s = 16 sb + 4g + r: (u^_t . w^_s)^2, masked s <= t
-      float ubv[4] = {x4[0], x4[1], x4[2], x4[3]};
-      const Op4<true> uf = make4<true>(ubv);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float xa[8];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int sb = 2 * kk + hb;
-          if (sb <= mb) {
-            const f32x4 wb = *reinterpret_cast<const f32x4*>(&Wsm[16 * sb + n][4 * g]);
-            float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
-            const f32x4 X = mma<true, true>(make4<true>(wbv), uf, zero4());
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xa[4 * hb + r] = (sb < mb || 4 * g + r <= n) ? X[r] * X[r] : 0.f;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xa[4 * hb + r] = 0.f;
-          }
-        }
-        sc[kk] = make8<SPLIT>(xa);
-      }
     }
+    // output waves: the causal score tiles of key K-block kk against this query block as an
+    // A-fragment, built off the state chain (kk = 0 beside E = T X, kk = 1 beside the state
+    // update).  X = W^_sb U^_mb^T (K = 16), lane (t = n, g) holds s = 16 sb + 4g + r:
+    // (u^_t . w^_s)^2, masked s <= t.
+    auto score_frag = [&](int kk) {
+      const float ubv[4] = {xr[0][0], xr[0][1], xr[0][2], xr[0][3]};
+      const Op4<true> uf = make4<true>(ubv);
+      float xa[8];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int sb = 2 * kk + hb;
+        if (sb <= mb) {
+          const f32x4 wb = *reinterpret_cast<const f32x4*>(&Wsm[16 * sb + n][4 * g]);
+          float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
+          const f32x4 X = mma<true, true>(make4<true>(wbv), uf, zero4());
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xa[4 * hb + r] = (sb < mb || 4 * g + r <= n) ? X[r] * X[r] : 0.f;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xa[4 * hb + r] = 0.f;
+        }
+      }
+      return make8<SPLIT>(xa);
+    };
     __syncthreads();
 
     // ---- E = T X (state waves), tokens 16 mb + n (A rows of T), K = token
+    Op8<SPLIT> sc0;
     if (state_role) {
       f32x4 accE = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(tfr[kk], frag(XB, kk), accE);
       const float ex[4] = {accE[0], accE[1], accE[2], accE[3]};
       put(EB, mb >> 1, (mb & 1) * 4, ex);
+    } else {
+      sc0 = score_frag(0);
     }
     __syncthreads();
 
     if (state_role) {
-      // ---- S += K^^T E: tile qd holds features f = 16 a + b with a = 4 mb + qd; as an A
-      // operand its row n is b = n, so slot i of K-block kk carries w^_s[a] w^_s[n] of token s
+      // ---- S += K^^T E on the owned diagonals: as an A operand, row n of tile delta is
+      // slot (delta, a = n), so slot i of K-block kk carries w^_s[n] w^_s[(n + delta) % 16]
+      // of token s.  wn: component n; wr: component (n + w) % 16 (a rotated LDS read), so
+      // delta = w is wn wr, delta = w + 4 rotates wr by 4 lanes, delta = 8 rotates wn by 8.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const Op8<true> eb = frag(EB, kk);
-        f32x4 wsl[8];
-        float wn[8];
+        float wn[8], wr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int sidx = 32 * kk + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
-          wsl[i] = *reinterpret_cast<const f32x4*>(&Wsm[sidx][4 * mb]);
           wn[i] = Wsm[sidx][n];
+          wr[i] = Wsm[sidx][rot & 15];
         }
+        float xa[8];
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          float xa[8];
+        for (int i = 0; i < 8; ++i) xa[i] = wn[i] * wr[i];
+        Sacc[0] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[0]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) xa[i] = wsl[i][qd] * wn[i];
-          Sacc[qd] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[qd]);
+        for (int i = 0; i < 8; ++i) xa[i] = wn[i] * row_plus<4>(wr[i]);
+        Sacc[1] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[1]);
+        if (own8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xa[i] = wn[i] * row_plus<8>(wn[i]);
+          Sacc[2] = mma<SPLIT, true>(make8<SPLIT>(xa), eb, Sacc[2]);
         }
       }
     } else {
       // ---- y = Q^ S + (Q^ K^^T o M) E: A = score rows t over key tokens s, B = E (K = s)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        if (2 * kk <= mb) acc = mma<SPLIT, true>(sc[kk], frag(EB, kk), acc);
+      acc = mma<SPLIT, true>(sc0, frag(EB, 0), acc);
+      if (mb >= 2) acc = mma<SPLIT, true>(score_frag(1), frag(EB, 1), acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = c * DC + 16 * mb + 4 * g + r;
@@ -564,13 +623,27 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     step(ib, c + 1);
   }
   if (c < n_chunks) step(ia, c);
+  // ST = S0 + the change of the packed state, at both entries (a, b) and (b, a) of each
+  // pair, written by the one lane that owns its slot (for delta = 8 the lanes a < 8).  That
+  // lane is also the only reader of these S0 entries, so S0 == ST is safe.
   if (ST && state_role) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
+    for (int jt = 0; jt < 3; ++jt) {
+      if (jt < 2 || own8) {
+        const int d = dl(jt);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * (4 * mb + qd) + 4 * g + r;
-        ST[(bh * P_DIM * P_DIM + f) * DV + col] = Sacc[qd][r];
+        for (int r = 0; r < 4; ++r) {
+          const int a = 4 * g + r, b = (a + d) & 15;
+          if (d == 8 && a >= 8) continue;
+          float sab = 0.f, sba = 0.f, ch = Sacc[jt][r];
+          if (S0) {
+            sab = s0_at(a, b);
+            sba = s0_at(b, a);
+            ch -= 0.5f * (sab + sba);
+          }
+          ST[(bh * P_DIM * P_DIM + 16 * a + b) * DV + col] = sab + ch;
+          if (d != 0) ST[(bh * P_DIM * P_DIM + 16 * b + a) * DV + col] = sba + ch;
+        }
       }
     }
   }

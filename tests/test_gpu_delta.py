@@ -244,6 +244,27 @@ def test_delta_chunked_tiny_fp32_with_state():
     assert sy <= TOL_F32 and sS <= TOL_F32 and ey <= 1e-3
 
 
+def test_delta_chunked_beta_zero_keeps_state_exactly():
+    """beta = 0 in the chunked form: every correction E is zero, so S_T equals S0 bit for
+    bit, including S0's antisymmetric part (the packed walk carries it to S_T unchanged),
+    also when S_T overwrites S0 in place; y_t = S0^T phi^(q_t) against the oracle."""
+    case = I.make_forward("mid", B=1, H=2, T=200, seed=84)
+    S0 = torch.randn((1, 2, 256, 64), generator=torch.Generator().manual_seed(84))
+    q, k, v, P, S0d = to_dev(case.q, case.k, case.v, case.P, S0)
+    b = torch.zeros((1, 2, 200), device=DEV)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, S0=S0d, out_dtype=torch.float32, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ST.cpu(), S0)
+    inplace = S0d.clone()
+    kata.forward_delta_chunked(q, k, v, P, b, S0=inplace, out_dtype=torch.float32, ST=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace.cpu(), S0)
+    yr, _ = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                               np.zeros((1, 2, 200)), S0.double().numpy())
+    # y reads the state through the bf16-rounded packed query features: the chunked bf16 bound
+    assert slice_rel(y.cpu().numpy(), yr) <= 5e-3 and row_rel(y.double().cpu().numpy(), yr) <= 2e-2
+
+
 def test_delta_chunked_overwrite_and_zero_keys():
     """Repeated keys with beta = 1 inside one chunk and across chunks, plus zero keys and
     queries (features 0): against the oracle."""

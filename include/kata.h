@@ -341,10 +341,14 @@ kata_status kata_forward_delta(const kata_forward_desc* desc,
  * definition and arguments as kata_forward_delta (exactly equal up to rounding), plus a
  * device workspace of kata_forward_delta_chunked_workspace_bytes bytes (normalised
  * projections and T per chunk: 9 KiB per 64 tokens and head), owned by the caller.
- * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S).
- * Supported: p = 16, (d, dv) = (16, 16) or (64, 64), desc->chunk = 64, in/out dtype F32
- * or BF16, B*H <= 65535.  kata_forward_delta_chunked_timed stamps three caller-created
- * events: start of the per-chunk pass, start and end of the walk. */
+ * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S) and
+ * keeps the state's symmetric part packed (the antisymmetric part of S0, which no read
+ * sees, reaches ST unchanged).  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),
+ * desc->chunk = 64, in/out dtype F32 or BF16, B*H <= 65535, and a sequence of q, k, v
+ * or y under 2 GiB at 4 bytes per element (T * max(d, dv) * 4 < 2^31 - 4096, less 256
+ * tokens; else KATA_ERR_SHAPE: the walk addresses a sequence with 32-bit offsets).
+ * kata_forward_delta_chunked_timed stamps three caller-created events: start of the
+ * per-chunk pass, start and end of the walk. */
 kata_status kata_forward_delta_chunked_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
 kata_status kata_forward_delta_chunked(const kata_forward_desc* desc,
                                        const void* q, const void* k, const void* v,

@@ -474,7 +474,9 @@ kata_status validate_delta_chunked(const kata_forward_desc* d) {
   if (!d) return KATA_ERR_NULL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0) return KATA_ERR_SHAPE;
   if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
-  if (d->T > ((int64_t)1 << 40)) return KATA_ERR_SHAPE;
+  // the walk reads a sequence's v (and beta) with 32-bit byte offsets, as the chunked forward
+  const int64_t widest = (int64_t)(d->d > d->dv ? d->d : d->dv) * 4;
+  if (d->T > (((int64_t)1 << 31) - 4096) / widest - 256) return KATA_ERR_SHAPE;
   if (d->p != P_DIM || !((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
   if (d->chunk != kata::DC) return KATA_ERR_UNSUPPORTED;
   if (check_dtype(d->in_dtype) != KATA_OK || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;

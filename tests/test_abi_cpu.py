@@ -324,7 +324,10 @@ def test_delta_chunked_workspace_and_validation():
     fake = ctypes.c_void_p(0x1000)
     for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),
                            ({"p": 8}, Bd.KATA_ERR_UNSUPPORTED), ({"T": -1}, Bd.KATA_ERR_SHAPE),
-                           ({"B": 70000}, Bd.KATA_ERR_SHAPE)]:
+                           ({"B": 70000}, Bd.KATA_ERR_SHAPE),
+                           # a sequence of v addressed with 32-bit offsets: T * 64 * 4 < 2^31 - 4096, less 256
+                           ({"T": ((1 << 31) - 4096) // 256 - 255}, Bd.KATA_ERR_SHAPE),
+                           ({"T": ((1 << 31) - 4096) // 256 - 256}, Bd.KATA_OK)]:
         bad = Bd.make_desc(2, 3, 100, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
         for f, val in fields.items():
             setattr(bad, f, val)

@@ -29,6 +29,7 @@ stamps one.
     python bench.py --backward   # the chunked-state backward on the long-context workload
     python bench.py --decay      # the decay-gated forward on the long-context workload
     python bench.py --decode --delta   # the DeltaKATA decode step (prefill by its recurrent forward)
+    python bench.py --decode --packed  # the decode step on the packed symmetric state (136 rows)
     python bench.py --delta      # the DeltaKATA forward, chunked form, on the long-context workload
     python bench.py --factors 2  # KATA-M2 (two concatenated PSD factors) on the long-context workload
 
@@ -406,8 +407,12 @@ def bench_decode(args):
     delta = bool(args.delta)
     G = args.factors
     fmode = args.factor_mode
+    packed = bool(args.packed)
     if delta and G > 1:
         print("bench.py --decode takes --delta or --factors, not both", file=sys.stderr)
+        sys.exit(2)
+    if packed and (delta or G > 1):
+        print("bench.py --decode --packed is the one-factor additive step only", file=sys.stderr)
         sys.exit(2)
     dc = I.make_decode(device=dev)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
@@ -431,6 +436,8 @@ def bench_decode(args):
         _, S0, z0 = kata.forward_factors(dc.q0, dc.k0, dc.v0, PF, fmode, return_state=True)
     else:
         _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
+        if packed:        # the export has equal mirror rows: packing it is exact
+            S0, z0 = kata.state_pack(S0, z0)
     S = torch.empty_like(S0)
     z = torch.empty_like(z0) if z0 is not None else None
     ys = torch.empty((steps, N, H, dv), dtype=torch.float32, device=dev)
@@ -442,6 +449,9 @@ def bench_decode(args):
     elif G > 1:
         def run(j):
             kata.decode_step_factors(S, z, dc.q[j], dc.k[j], dc.v[j], PF, fmode, y=ys[j], stream=stream)
+    elif packed:
+        def run(j):
+            kata.decode_step_packed(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
     else:
         def run(j):
             kata.decode_step(S, z, dc.q[j], dc.k[j], dc.v[j], dc.P, y=ys[j], stream=stream)
@@ -474,16 +484,20 @@ def bench_decode(args):
     step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4 + (N * H * 4 if delta else 0)
     achieved = step_bytes / (ms_step / 1e3) / 1e9
     kernel = ("kata_delta_recurrent (T=1, in place)" if delta
-              else ("kata_decode_step_factors" if G > 1 else "kata_decode_step"))
+              else ("kata_decode_step_factors" if G > 1
+                    else ("kata_decode_step_packed" if packed else "kata_decode_step")))
     fname = {"concat": f"KATA-M{G} ", "sum": f"KATA-Sigma{G} "}[fmode] if G > 1 else ""
     mode = ("decode_delta" if delta else
-            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode"))
+            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1
+             else ("decode_packed" if packed else "decode")))
     src = path_hash(mode)
     traffic = mode_traffic(mode, kernel.split(" ")[0])
     rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
     prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
+    state_desc = (f"packed symmetric fp32 state [{N},{H},136,{dv}] + z (kata_state_pack of the export)" if packed
+                  else f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}")
     workload = (f"recurrent {'DeltaKATA ' if delta else fname}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
-                f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}, prefill T={T0} by "
+                f"{state_desc}, prefill T={T0} by "
                 f"{prefill_fn}, {steps} steps, every 4th key repeating an earlier one"
                 + (", beta uniform in [0.5, 1]" if delta else "")
                 + (f", {G} PSD factors per head (P [16,{G},16,64])" if G > 1 else ""))
@@ -762,6 +776,8 @@ def main():
                     help="KATA-Mg: time kata_forward_factors with this many concatenated PSD factors")
     ap.add_argument("--factor-mode", default="concat", choices=("concat", "sum"),
                     help="with --factors: concatenated (KATA-Mg) or summed (KATA-Sigma-g) factors")
+    ap.add_argument("--packed", action="store_true",
+                    help="with --decode: the step on the packed symmetric state (kata_decode_step_packed)")
     ap.add_argument("--delta", action="store_true",
                     help="the DeltaKATA forward (chunked form) on the long-context workload; with --decode the "
                          "DeltaKATA decode step (prefill by kata_forward_delta)")

@@ -244,6 +244,38 @@ kata_status kata_forward_decay_timed(const kata_forward_desc* desc,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
 
+/* The packed symmetric state: phi(k) = vec(w w^T) is symmetric, so every state the
+ * decode steps or kata_forward produce has equal mirror rows (a, b) and (b, a) of S and z,
+ * and every read phi(q) . S sees only their sum.  The packed layout keeps one row per
+ * pair {a, b}: KATA_PACKED_ROWS = 136 rows, row 16 delta + a (delta = 0..7, a = 0..15)
+ * and row 128 + a (delta = 8, a = 0..7) for the pair {a, (a + delta) mod 16} (p = 16):
+ * the slots of the packed feature layouts of kata_feature_map without their 8 zero slots.
+ * Sp [n, 136, dv], zp [n, 136] float32 device memory owned by the caller.
+ *   kata_state_pack:   Sp row of {a, b} = (S[16a+b] + S[16b+a]) / 2 (exact where the
+ *                      mirror rows are equal; a read sees only their sum, which this
+ *                      keeps); zp likewise.  n = number of (stream, head) states.
+ *   kata_state_unpack: both S[16a+b] and S[16b+a] = Sp row of {a, b}; z likewise.
+ * z and zp are both NULL (S only) or both given.  dv = 16 or 64.  The calls are enqueued
+ * on `stream`; S and Sp must not overlap. */
+#define KATA_PACKED_ROWS 136
+kata_status kata_state_pack(int64_t n, int dv, const float* S, const float* z, float* Sp, float* zp,
+                            void* stream);
+kata_status kata_state_unpack(int64_t n, int dv, const float* Sp, const float* zp, float* S, float* z,
+                              void* stream);
+
+/* kata_decode_step on the packed state ([TS-1], [ABS]; packed as above):
+ *   Sp += phi_p(k) v^T, zp += phi_p(k),  phi_p(k)[row of {a, b}] = w_a w_b
+ *   y = sum_r c_r phi_p(q)[r] Sp[r] / sum_r c_r phi_p(q)[r] zp[r],  c_r = 1 on the
+ *       diagonal (a = b), 2 off it (a pair stands for two mirror rows)
+ * which equals kata_decode_step on the unpacked state, with 136 instead of 256 rows
+ * read and written per head.  Sp [N,H,136,dv], zp [N,H,136] float32 in place; other
+ * arguments, support and errors as for kata_decode_step. */
+kata_status kata_decode_step_packed(int64_t N, int64_t H, int d, int dv, int p,
+                                    kata_dtype in_dtype, kata_dtype out_dtype,
+                                    float* Sp, float* zp,
+                                    const void* q, const void* k, const void* v,
+                                    const float* P, void* y, void* stream);
+
 /* One decay-gated recurrent decode step (same reading): S <- gamma S + phi(k) v^T,
  * z <- gamma z + phi(k), y = S^T phi(q) / (z . phi(q)), gamma = exp(lam), lam [N,H]
  * float32 (device).  Other arguments and support as for kata_decode_step. */

@@ -22,6 +22,7 @@ FEATURE_LAYOUTS = {"full": 0, "packed_key": 1, "packed_query": 2}
 ABI_VERSION = 1
 P_DIM = 16
 N_PACKED = 9 * P_DIM
+PACKED_ROWS = 136      # rows of the packed symmetric state (the first 136 packed feature slots)
 
 
 class KataError(RuntimeError):
@@ -97,6 +98,12 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_decay_timed.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp, ctypes.POINTER(vp)]
     lib.kata_forward_decay.restype = ci
     lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
+    lib.kata_decode_step_packed.restype = ci
+    lib.kata_decode_step_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_state_pack.restype = ci
+    lib.kata_state_pack.argtypes = [i64, ci, vp, vp, vp, vp, vp]
+    lib.kata_state_unpack.restype = ci
+    lib.kata_state_unpack.argtypes = [i64, ci, vp, vp, vp, vp, vp]
     lib.kata_decode_step_decay.restype = ci
     lib.kata_decode_step_decay.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kata_forward_factors_workspace_bytes.restype = ci
@@ -687,6 +694,81 @@ def decode_step(S: torch.Tensor, z: torch.Tensor, q: torch.Tensor, k: torch.Tens
                                  _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y),
                                  _stream_handle(stream, dev))
     _check(st, "kata_decode_step")
+    return y
+
+
+def state_pack(S: torch.Tensor, z: Optional[torch.Tensor] = None, *, Sp: Optional[torch.Tensor] = None,
+               zp: Optional[torch.Tensor] = None, stream=None):
+    """Canonical state S [..., 256, dv] (and z [..., 256]) to the packed symmetric layout
+    Sp [..., 136, dv] (zp [..., 136]) (kata_state_pack): one row per pair {a, b}, the mean
+    of its two mirror rows.  Returns Sp, or (Sp, zp) when z is given."""
+    lead, dv = tuple(S.shape[:-2]), S.shape[-1]
+    dev = S.device
+    _need(S, "S", lead + (P_DIM * P_DIM, dv), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", lead + (P_DIM * P_DIM,), torch.float32, dev)
+    n = 1
+    for x in lead:
+        n *= x
+    if Sp is None:
+        Sp = torch.empty(lead + (PACKED_ROWS, dv), dtype=torch.float32, device=dev)
+    _need(Sp, "Sp", lead + (PACKED_ROWS, dv), torch.float32, dev)
+    if z is not None:
+        if zp is None:
+            zp = torch.empty(lead + (PACKED_ROWS,), dtype=torch.float32, device=dev)
+        _need(zp, "zp", lead + (PACKED_ROWS,), torch.float32, dev)
+    _check(_lib().kata_state_pack(n, dv, _ptr(S), _ptr(z), _ptr(Sp), _ptr(zp if z is not None else None),
+                                  _stream_handle(stream, dev)), "kata_state_pack")
+    return (Sp, zp) if z is not None else Sp
+
+
+def state_unpack(Sp: torch.Tensor, zp: Optional[torch.Tensor] = None, *, S: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, stream=None):
+    """Packed symmetric state Sp [..., 136, dv] (and zp) back to the canonical layout
+    (kata_state_unpack): both mirror rows of each pair.  Returns S, or (S, z)."""
+    lead, dv = tuple(Sp.shape[:-2]), Sp.shape[-1]
+    dev = Sp.device
+    _need(Sp, "Sp", lead + (PACKED_ROWS, dv), torch.float32, dev)
+    if zp is not None:
+        _need(zp, "zp", lead + (PACKED_ROWS,), torch.float32, dev)
+    n = 1
+    for x in lead:
+        n *= x
+    if S is None:
+        S = torch.empty(lead + (P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
+    _need(S, "S", lead + (P_DIM * P_DIM, dv), torch.float32, dev)
+    if zp is not None:
+        if z is None:
+            z = torch.empty(lead + (P_DIM * P_DIM,), dtype=torch.float32, device=dev)
+        _need(z, "z", lead + (P_DIM * P_DIM,), torch.float32, dev)
+    _check(_lib().kata_state_unpack(n, dv, _ptr(Sp), _ptr(zp), _ptr(S), _ptr(z if zp is not None else None),
+                                    _stream_handle(stream, dev)), "kata_state_unpack")
+    return (S, z) if zp is not None else S
+
+
+def decode_step_packed(Sp: torch.Tensor, zp: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       P: torch.Tensor, *, out_dtype: torch.dtype = torch.float32, y: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """One recurrent step on the packed state (kata_decode_step_packed): Sp [N,H,136,dv],
+    zp [N,H,136] updated in place; returns y [N,H,dv], equal to decode_step's on the
+    unpacked state."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(Sp, "Sp", (N, H, PACKED_ROWS, dv), torch.float32, dev)
+    _need(zp, "zp", (N, H, PACKED_ROWS), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_packed(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype), _ptr(Sp),
+                                        _ptr(zp), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y),
+                                        _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_packed")
     return y
 
 

@@ -797,6 +797,61 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dt
   return launch_status();
 }
 
+kata_status kata_decode_step_packed(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                                    kata_dtype out_dtype, float* Sp, float* zp, const void* q, const void* k,
+                                    const void* v, const float* P, void* y, void* stream) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N > 0 && H > 0x7fffffff / N) return KATA_ERR_SHAPE;
+  if (N * H == 0) return KATA_OK;
+  if (!Sp || !zp || !q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)(N * H));
+#define KATA_DECODE_P(TI, TO, DVV)                                                                       \
+  hipLaunchKernelGGL((kata::kata_decode_step_packed<TI, TO, DVV>), grid, dim3(256), 0, st, Sp, zp, (const TI*)q, \
+                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DECODE_P(float, float, 64);
+    else if (fi) KATA_DECODE_P(float, bf16, 64);
+    else if (fo) KATA_DECODE_P(bf16, float, 64);
+    else KATA_DECODE_P(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DECODE_P(float, float, 16);
+    else if (fi) KATA_DECODE_P(float, bf16, 16);
+    else if (fo) KATA_DECODE_P(bf16, float, 16);
+    else KATA_DECODE_P(bf16, bf16, 16);
+  }
+#undef KATA_DECODE_P
+  return launch_status();
+}
+
+kata_status kata_state_pack(int64_t n, int dv, const float* S, const float* z, float* Sp, float* zp, void* stream) {
+  if (n < 0) return KATA_ERR_SHAPE;
+  if (dv != 16 && dv != 64) return KATA_ERR_UNSUPPORTED;
+  if (n > 0x7fffffff / kata::DPK) return KATA_ERR_SHAPE;
+  if ((z == nullptr) != (zp == nullptr)) return KATA_ERR_NULL;
+  if (n == 0) return KATA_OK;
+  if (!S || !Sp) return KATA_ERR_NULL;
+  hipLaunchKernelGGL(kata::kata_state_pack, dim3((unsigned)(n * kata::DPK)), dim3(64), 0, (hipStream_t)stream, S, z,
+                     Sp, zp, dv);
+  return launch_status();
+}
+
+kata_status kata_state_unpack(int64_t n, int dv, const float* Sp, const float* zp, float* S, float* z,
+                              void* stream) {
+  if (n < 0) return KATA_ERR_SHAPE;
+  if (dv != 16 && dv != 64) return KATA_ERR_UNSUPPORTED;
+  if (n > 0x7fffffff / (P_DIM * P_DIM)) return KATA_ERR_SHAPE;
+  if ((z == nullptr) != (zp == nullptr)) return KATA_ERR_NULL;
+  if (n == 0) return KATA_OK;
+  if (!S || !Sp) return KATA_ERR_NULL;
+  hipLaunchKernelGGL(kata::kata_state_unpack, dim3((unsigned)(n * P_DIM * P_DIM)), dim3(64), 0, (hipStream_t)stream,
+                     Sp, zp, S, z, dv);
+  return launch_status();
+}
+
 kata_status kata_forward_delta(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
                                const float* P, const float* beta, const float* S0, void* y, float* ST,
                                void* stream) {

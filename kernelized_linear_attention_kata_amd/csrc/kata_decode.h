@@ -113,6 +113,129 @@ kata_decode_step(float* __restrict__ S, float* __restrict__ z, const TIn* __rest
   }
 }
 
+// ---- packed state ------------------------------------------------------------------
+// Every update adds phi(k) = vec(w w^T), a symmetric 16 x 16 matrix, so a state built by
+// the steps (or exported by kata_forward) has equal mirror rows (a, b) and (b, a), and
+// every read phi(q) . S sees only their sum.  The packed layout keeps one row per pair
+// {a, b}, in the circulant order of the chunked kernels: row 16 delta + a (delta = 0..7,
+// a = 0..15) and row 128 + a (delta = 8, a = 0..7) stand for the pair {a, (a + delta) mod 16}:
+// 136 rows instead of 256, so a step moves 1.88x fewer bytes.
+constexpr int DPK = 136;
+__host__ __device__ constexpr int packed_delta(int r) { return r < 128 ? r >> 4 : 8; }
+__host__ __device__ constexpr int packed_a(int r) { return r < 128 ? r & 15 : r - 128; }
+
+// grid N*H, block 256.  The packed step: Sp += phi_p(k) v^T, zp += phi_p(k) with
+// phi_p(k)[r] = w_a w_b, then y = sum_r c_r phi_p(q)[r] Sp[r] / sum_r c_r phi_p(q)[r] zp[r]
+// with c_r = 1 on the diagonal (delta = 0) and 2 off it (each pair stands for two mirror
+// rows of the canonical state).  Equal to kata_decode_step on the canonical state.
+template <typename TIn, typename TOut, int DV>
+__global__ void __launch_bounds__(256)
+kata_decode_step_packed(float* __restrict__ S, float* __restrict__ z, const TIn* __restrict__ q,
+                        const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
+                        TOut* __restrict__ y, int H, int d) {
+  constexpr int QPR = DV / 4;               // float4 quads per state row
+  constexpr int ROWS_PER_IT = 256 / QPR;    // rows covered per pass of the block
+  constexpr int NIT = (DPK + ROWS_PER_IT - 1) / ROWS_PER_IT;
+  __shared__ float su[P_DIM], sw[P_DIM];
+  __shared__ float fu[DPK], fw[DPK];
+  __shared__ float red[4][DV];
+  __shared__ float dred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nh = blockIdx.x;
+  const int h = (int)(nh % H);
+  const float* Ph = P + (int64_t)h * P_DIM * d;
+
+  const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
+  const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
+  if ((tid & 15) == 0) { su[tid >> 4] = u; sw[tid >> 4] = w; }
+  __syncthreads();
+  if (tid < DPK) {
+    const int dl = packed_delta(tid), a = packed_a(tid), b = (a + dl) & 15;
+    fu[tid] = (dl == 0 ? 1.f : 2.f) * su[a] * su[b];
+    fw[tid] = sw[a] * sw[b];
+  }
+  __syncthreads();
+
+  const int c4 = tid % QPR;
+  f32x4 vv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vv[i] = (float)v[nh * DV + 4 * c4 + i];
+  float* Sh = S + nh * (int64_t)DPK * DV;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int row = it * ROWS_PER_IT + tid / QPR;
+    if (row < DPK) {
+      f32x4* ptr = reinterpret_cast<f32x4*>(Sh + row * DV + 4 * c4);
+      f32x4 sv = *ptr;
+      const float fwr = fw[row], fur = fu[row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] += fwr * vv[i];
+      *ptr = sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += fur * sv[i];
+    }
+  }
+  float dp = 0.f;
+  if (tid < DPK) {
+    float* zh = z + nh * DPK;
+    const float zn = zh[tid] + fw[tid];
+    zh[tid] = zn;
+    dp = fu[tid] * zn;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dp += __shfl_xor(dp, off);
+#pragma unroll
+  for (int off = 32; off >= QPR; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+  }
+  if (lane < QPR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * lane + i] = acc[i];
+  }
+  if (lane == 0) dred[wave] = dp;
+  __syncthreads();
+  if (tid < DV) {
+    const float num = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float den = dred[0] + dred[1] + dred[2] + dred[3];
+    Elem<TOut>::store(y, nh * DV + tid, den != 0.f ? num / den : 0.f);
+  }
+}
+
+// grid n*DPK, block 64 (thread c: value column c < dv).  Canonical -> packed: row r of
+// the pair {a, b} takes (S[16a + b] + S[16b + a]) / 2 (exact when the mirror rows are
+// equal, as they are for every state the steps or kata_forward produce); z likewise.
+__global__ void __launch_bounds__(64)
+kata_state_pack(const float* __restrict__ S, const float* __restrict__ z, float* __restrict__ Sp,
+                float* __restrict__ zp, int dv) {
+  const int r = (int)(blockIdx.x % DPK), c = threadIdx.x;
+  const int64_t n = blockIdx.x / DPK;
+  const int dl = packed_delta(r), a = packed_a(r), b = (a + dl) & 15;
+  const int64_t f1 = 16 * a + b, f2 = 16 * b + a;
+  const float* Sn = S + n * (int64_t)(P_DIM * P_DIM) * dv;
+  if (c < dv) Sp[(n * DPK + r) * dv + c] = 0.5f * (Sn[f1 * dv + c] + Sn[f2 * dv + c]);
+  if (z && c == 0) zp[n * DPK + r] = 0.5f * (z[n * (P_DIM * P_DIM) + f1] + z[n * (P_DIM * P_DIM) + f2]);
+}
+
+// grid n*256, block 64.  Packed -> canonical: both mirror rows (a, b) and (b, a) take the
+// pair's row.
+__global__ void __launch_bounds__(64)
+kata_state_unpack(const float* __restrict__ Sp, const float* __restrict__ zp, float* __restrict__ S,
+                  float* __restrict__ z, int dv) {
+  const int f = (int)(blockIdx.x & 255), c = threadIdx.x;
+  const int64_t n = blockIdx.x >> 8;
+  const int a = f >> 4, b = f & 15;
+  const int dab = (b - a) & 15;
+  // the pair's row: distance dab <= 8 from a (for 8, a < 8 holds the pair), else from b
+  int r;
+  if (dab <= 7) r = 16 * dab + a;
+  else if (dab == 8) r = 128 + (a & 7);
+  else r = 16 * (16 - dab) + b;
+  if (c < dv) S[(n * (P_DIM * P_DIM) + f) * dv + c] = Sp[(n * DPK + r) * dv + c];
+  if (z && c == 0) z[n * (P_DIM * P_DIM) + f] = zp[n * DPK + r];
+}
+
 // One decode step of KATA-Mg (several concatenated PSD factors) or KATA-Sigma-g (summed
 // factors): the item "Variantes" of section 2.3 of the gist.science summary, read as the
 // forward's kata_forward_factors reads it.  grid N*H, block 256.  P [H, G, p, d].

@@ -342,6 +342,29 @@ def test_delta_chunked_workspace_and_validation():
     assert lib.kata_forward_delta_chunked(ctypes.byref(empty), *([None] * 8), None, 0, None) == Bd.KATA_OK
 
 
+def test_packed_state_validation():
+    """kata_decode_step_packed, kata_state_pack, kata_state_unpack: every argument error is
+    returned before anything is enqueued (no GPU needed)."""
+    lib = _lib_or_skip()
+    fake = ctypes.c_void_p(0x1000)
+    ptrs = [fake] * 7                    # Sp, zp, q, k, v, P, y
+    assert lib.kata_decode_step_packed(-1, 16, 64, 64, 16, 1, 0, *ptrs, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_decode_step_packed(4, 16, 64, 64, 8, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_packed(4, 16, 64, 32, 16, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_packed(4, 16, 64, 64, 16, 3, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
+    assert lib.kata_decode_step_packed(4, 16, 64, 64, 16, 1, 0, None, *ptrs[1:], None) == Bd.KATA_ERR_NULL
+    assert lib.kata_decode_step_packed(1 << 20, 1 << 12, 64, 64, 16, 1, 0, *ptrs, None) == Bd.KATA_ERR_SHAPE
+    assert lib.kata_decode_step_packed(0, 16, 64, 64, 16, 1, 0, *([None] * 7), None) == Bd.KATA_OK
+    for fn in (lib.kata_state_pack, lib.kata_state_unpack):
+        assert fn(-1, 64, fake, fake, fake, fake, None) == Bd.KATA_ERR_SHAPE
+        assert fn(4, 32, fake, fake, fake, fake, None) == Bd.KATA_ERR_UNSUPPORTED
+        assert fn(4, 64, fake, None, fake, fake, None) == Bd.KATA_ERR_NULL      # z without zp
+        assert fn(4, 64, None, None, fake, None, None) == Bd.KATA_ERR_NULL
+        assert fn(1 << 30, 64, fake, None, fake, None, None) == Bd.KATA_ERR_SHAPE
+        assert fn(0, 64, None, None, None, None, None) == Bd.KATA_OK
+    assert Bd.PACKED_ROWS == 136
+
+
 def test_decode_factors_validation():
     lib = _lib_or_skip()
     fake = ctypes.c_void_p(0x1000)

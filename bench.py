@@ -411,8 +411,8 @@ def bench_decode(args):
     if delta and G > 1:
         print("bench.py --decode takes --delta or --factors, not both", file=sys.stderr)
         sys.exit(2)
-    if packed and (delta or G > 1):
-        print("bench.py --decode --packed is the one-factor additive step only", file=sys.stderr)
+    if packed and delta:
+        print("bench.py --decode --packed: the additive steps only (not --delta)", file=sys.stderr)
         sys.exit(2)
     dc = I.make_decode(device=dev)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
@@ -434,6 +434,10 @@ def bench_decode(args):
     elif G > 1:
         PF = I.make_factor_projections(H, G, d, seed=4, device=dev)
         _, S0, z0 = kata.forward_factors(dc.q0, dc.k0, dc.v0, PF, fmode, return_state=True)
+        if packed:        # each factor block packed as a state of its own
+            nb = G if fmode == "concat" else 1
+            S0, z0 = kata.state_pack(S0.reshape(N, H * nb, 256, dv), z0.reshape(N, H * nb, 256))
+            S0, z0 = S0.reshape(N, H, nb * 136, dv), z0.reshape(N, H, nb * 136)
     else:
         _, S0, z0 = kata.forward(dc.q0, dc.k0, dc.v0, dc.P, chunk=64, return_state=True)
         if packed:        # the export has equal mirror rows: packing it is exact
@@ -446,6 +450,9 @@ def bench_decode(args):
     if delta:
         def run(j):
             kata.decode_step_delta(S, dc.q[j], dc.k[j], dc.v[j], dc.P, betas[j], y=ys[j], stream=stream)
+    elif G > 1 and packed:
+        def run(j):
+            kata.decode_step_factors_packed(S, z, dc.q[j], dc.k[j], dc.v[j], PF, fmode, y=ys[j], stream=stream)
     elif G > 1:
         def run(j):
             kata.decode_step_factors(S, z, dc.q[j], dc.k[j], dc.v[j], PF, fmode, y=ys[j], stream=stream)
@@ -484,18 +491,18 @@ def bench_decode(args):
     step_bytes = 2 * state_bytes + N * H * (2 * d + dv) * 2 + N * H * dv * 4 + (N * H * 4 if delta else 0)
     achieved = step_bytes / (ms_step / 1e3) / 1e9
     kernel = ("kata_delta_recurrent (T=1, in place)" if delta
-              else ("kata_decode_step_factors" if G > 1
-                    else ("kata_decode_step_packed" if packed else "kata_decode_step")))
+              else ("kata_decode_step_packed" if packed
+                    else ("kata_decode_step_factors" if G > 1 else "kata_decode_step")))
     fname = {"concat": f"KATA-M{G} ", "sum": f"KATA-Sigma{G} "}[fmode] if G > 1 else ""
     mode = ("decode_delta" if delta else
-            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1
-             else ("decode_packed" if packed else "decode")))
+            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode")
+            + ("_packed" if packed else ""))
     src = path_hash(mode)
     traffic = mode_traffic(mode, kernel.split(" ")[0])
     rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
     prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
-    state_desc = (f"packed symmetric fp32 state [{N},{H},136,{dv}] + z (kata_state_pack of the export)" if packed
-                  else f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}")
+    state_desc = (f"packed symmetric fp32 state [{N},{H},{rows * 136 // 256},{dv}] + z (kata_state_pack of the "
+                  f"export)" if packed else f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}")
     workload = (f"recurrent {'DeltaKATA ' if delta else fname}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
                 f"{state_desc}, prefill T={T0} by "
                 f"{prefill_fn}, {steps} steps, every 4th key repeating an earlier one"

@@ -276,6 +276,15 @@ kata_status kata_decode_step_packed(int64_t N, int64_t H, int d, int dv, int p,
                                     const void* q, const void* k, const void* v,
                                     const float* P, void* y, void* stream);
 
+/* kata_decode_step_decay on the packed state: Sp <- gamma Sp + phi_p(k) v^T,
+ * zp <- gamma zp + phi_p(k), gamma = exp(lam) (lam [N,H] float32), then the packed read.
+ * Other arguments, support and errors as for kata_decode_step_decay. */
+kata_status kata_decode_step_decay_packed(int64_t N, int64_t H, int d, int dv, int p,
+                                          kata_dtype in_dtype, kata_dtype out_dtype,
+                                          float* Sp, float* zp,
+                                          const void* q, const void* k, const void* v,
+                                          const float* P, const float* lam, void* y, void* stream);
+
 /* One decay-gated recurrent decode step (same reading): S <- gamma S + phi(k) v^T,
  * z <- gamma z + phi(k), y = S^T phi(q) / (z . phi(q)), gamma = exp(lam), lam [N,H]
  * float32 (device).  Other arguments and support as for kata_decode_step. */
@@ -341,6 +350,16 @@ kata_status kata_decode_step_factors(int64_t N, int64_t H, int d, int dv, int p,
                                      kata_factor_mode mode, kata_dtype in_dtype, kata_dtype out_dtype,
                                      float* S, float* z, const void* q, const void* k, const void* v,
                                      const float* P, void* y, void* stream);
+
+/* kata_decode_step_factors on packed states (layout as for kata_decode_step_packed):
+ * concat: Sp [N,H,g*136,dv], zp [N,H,g*136], factor-major (each block is the packed form
+ * of that factor's canonical block; pack it with kata_state_pack over N*H*g states);
+ * sum: Sp [N,H,136,dv], zp [N,H,136].  Same step, arguments, support and errors as
+ * kata_decode_step_factors; g = 1 is kata_decode_step_packed. */
+kata_status kata_decode_step_factors_packed(int64_t N, int64_t H, int d, int dv, int p, int g,
+                                            kata_factor_mode mode, kata_dtype in_dtype, kata_dtype out_dtype,
+                                            float* Sp, float* zp, const void* q, const void* k, const void* v,
+                                            const float* P, void* y, void* stream);
 
 /* DeltaKATA.  [TS-4] (repeated-key overwrite) credits the delta-rule variant of KATA with
  * correcting stale bindings when a key is written again, and [TS-1] / [ABS] name delta

@@ -100,6 +100,10 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
     lib.kata_decode_step_packed.restype = ci
     lib.kata_decode_step_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_decode_step_decay_packed.restype = ci
+    lib.kata_decode_step_decay_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci] + [vp] * 9
+    lib.kata_decode_step_factors_packed.restype = ci
+    lib.kata_decode_step_factors_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci, ci, ci] + [vp] * 8
     lib.kata_state_pack.restype = ci
     lib.kata_state_pack.argtypes = [i64, ci, vp, vp, vp, vp, vp]
     lib.kata_state_unpack.restype = ci
@@ -769,6 +773,59 @@ def decode_step_packed(Sp: torch.Tensor, zp: torch.Tensor, q: torch.Tensor, k: t
                                         _ptr(zp), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y),
                                         _stream_handle(stream, dev))
     _check(st, "kata_decode_step_packed")
+    return y
+
+
+def decode_step_decay_packed(Sp: torch.Tensor, zp: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             P: torch.Tensor, lam: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                             y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_step_decay on the packed state (kata_decode_step_decay_packed); lam [N,H] fp32."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(Sp, "Sp", (N, H, PACKED_ROWS, dv), torch.float32, dev)
+    _need(zp, "zp", (N, H, PACKED_ROWS), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(lam, "lam", (N, H), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_decay_packed(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                              _ptr(Sp), _ptr(zp), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(lam),
+                                              _ptr(y), _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_decay_packed")
+    return y
+
+
+def decode_step_factors_packed(Sp: torch.Tensor, zp: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                               v: torch.Tensor, P: torch.Tensor, mode: str = "concat", *,
+                               out_dtype: torch.dtype = torch.float32, y: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """decode_step_factors on packed states (kata_decode_step_factors_packed): P [H,g,16,d];
+    Sp [N,H,g*136,dv], zp [N,H,g*136] ("concat") or [N,H,136,...] ("sum")."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    g = P.shape[1]
+    dev = q.device
+    rows = PACKED_ROWS * (g if mode == "concat" else 1)
+    _need(Sp, "Sp", (N, H, rows, dv), torch.float32, dev)
+    _need(zp, "zp", (N, H, rows), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, g, P_DIM, d), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_factors_packed(N, H, d, dv, P_DIM, g, FACTOR_MODES[mode], _dtype_code(q.dtype),
+                                                _dtype_code(out_dtype), _ptr(Sp), _ptr(zp), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(P), _ptr(y), _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_factors_packed")
     return y
 
 

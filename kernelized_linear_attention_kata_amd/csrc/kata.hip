@@ -526,6 +526,41 @@ kata_status launch_decode_factors(int64_t NH, int H, int d, int dv, kata_dtype i
   return launch_status();
 }
 
+// The decode step on the packed symmetric state (kata_decode_step_packed): one-factor,
+// decay-gated (DECAY) or several PSD factors (G > 1, concatenated or SUMG).
+template <int G, bool SUMG, bool DECAY>
+kata_status launch_decode_packed(int64_t NH, int H, int d, int dv, kata_dtype in_dtype, kata_dtype out_dtype,
+                                 float* Sp, float* zp, const void* q, const void* k, const void* v, const float* P,
+                                 const float* lam, void* y, hipStream_t st) {
+  const dim3 grid((unsigned)NH);
+#define KATA_DP(TI, TO, DVV)                                                                                      \
+  hipLaunchKernelGGL((kata::kata_decode_step_packed<TI, TO, DVV, G, SUMG, DECAY>), grid, dim3(256), 0, st, Sp, zp, \
+                     (const TI*)q, (const TI*)k, (const TI*)v, P, (TO*)y, H, d, lam)
+  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
+  if (dv == 64) {
+    if (fi && fo) KATA_DP(float, float, 64);
+    else if (fi) KATA_DP(float, bf16, 64);
+    else if (fo) KATA_DP(bf16, float, 64);
+    else KATA_DP(bf16, bf16, 64);
+  } else {
+    if (fi && fo) KATA_DP(float, float, 16);
+    else if (fi) KATA_DP(float, bf16, 16);
+    else if (fo) KATA_DP(bf16, float, 16);
+    else KATA_DP(bf16, bf16, 16);
+  }
+#undef KATA_DP
+  return launch_status();
+}
+
+// Shared checks of the decode entry points: sizes, supported shapes and dtypes.
+kata_status validate_decode(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype, kata_dtype out_dtype) {
+  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
+  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
+  if (N > 0 && H > 0x7fffffff / N) return KATA_ERR_SHAPE;
+  return KATA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -800,31 +835,42 @@ kata_status kata_decode_step(int64_t N, int64_t H, int d, int dv, int p, kata_dt
 kata_status kata_decode_step_packed(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
                                     kata_dtype out_dtype, float* Sp, float* zp, const void* q, const void* k,
                                     const void* v, const float* P, void* y, void* stream) {
-  if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
-  if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
-  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
-  if (N > 0 && H > 0x7fffffff / N) return KATA_ERR_SHAPE;
-  if (N * H == 0) return KATA_OK;
+  const kata_status s = validate_decode(N, H, d, dv, p, in_dtype, out_dtype);
+  if (s != KATA_OK || N * H == 0) return s;
+  if (!Sp || !zp || !q || !k || !v || !P || !y) return KATA_ERR_NULL;
+  return launch_decode_packed<1, false, false>(N * H, (int)H, d, dv, in_dtype, out_dtype, Sp, zp, q, k, v, P,
+                                               nullptr, y, (hipStream_t)stream);
+}
+
+kata_status kata_decode_step_decay_packed(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                                          kata_dtype out_dtype, float* Sp, float* zp, const void* q, const void* k,
+                                          const void* v, const float* P, const float* lam, void* y, void* stream) {
+  const kata_status s = validate_decode(N, H, d, dv, p, in_dtype, out_dtype);
+  if (s != KATA_OK || N * H == 0) return s;
+  if (!Sp || !zp || !q || !k || !v || !P || !lam || !y) return KATA_ERR_NULL;
+  return launch_decode_packed<1, false, true>(N * H, (int)H, d, dv, in_dtype, out_dtype, Sp, zp, q, k, v, P, lam,
+                                              y, (hipStream_t)stream);
+}
+
+kata_status kata_decode_step_factors_packed(int64_t N, int64_t H, int d, int dv, int p, int g,
+                                            kata_factor_mode mode, kata_dtype in_dtype, kata_dtype out_dtype,
+                                            float* Sp, float* zp, const void* q, const void* k, const void* v,
+                                            const float* P, void* y, void* stream) {
+  if (g < 1) return KATA_ERR_SHAPE;
+  if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
+  if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
+  const kata_status s = validate_decode(N, H, d, dv, p, in_dtype, out_dtype);
+  if (s != KATA_OK || N * H == 0) return s;
   if (!Sp || !zp || !q || !k || !v || !P || !y) return KATA_ERR_NULL;
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((unsigned)(N * H));
-#define KATA_DECODE_P(TI, TO, DVV)                                                                       \
-  hipLaunchKernelGGL((kata::kata_decode_step_packed<TI, TO, DVV>), grid, dim3(256), 0, st, Sp, zp, (const TI*)q, \
-                     (const TI*)k, (const TI*)v, P, (TO*)y, (int)H, d)
-  const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
-  if (dv == 64) {
-    if (fi && fo) KATA_DECODE_P(float, float, 64);
-    else if (fi) KATA_DECODE_P(float, bf16, 64);
-    else if (fo) KATA_DECODE_P(bf16, float, 64);
-    else KATA_DECODE_P(bf16, bf16, 64);
-  } else {
-    if (fi && fo) KATA_DECODE_P(float, float, 16);
-    else if (fi) KATA_DECODE_P(float, bf16, 16);
-    else if (fo) KATA_DECODE_P(bf16, float, 16);
-    else KATA_DECODE_P(bf16, bf16, 16);
-  }
-#undef KATA_DECODE_P
-  return launch_status();
+  const int64_t NH = N * H;
+  const bool sum = mode == KATA_FACTORS_SUM;
+#define KATA_DFP(GG, SS) \
+  launch_decode_packed<GG, SS, false>(NH, (int)H, d, dv, in_dtype, out_dtype, Sp, zp, q, k, v, P, nullptr, y, st)
+  if (g == 1) return KATA_DFP(1, false);
+  if (g == 2) return sum ? KATA_DFP(2, true) : KATA_DFP(2, false);
+  return sum ? KATA_DFP(3, true) : KATA_DFP(3, false);
+#undef KATA_DFP
 }
 
 kata_status kata_state_pack(int64_t n, int dv, const float* S, const float* z, float* Sp, float* zp, void* stream) {

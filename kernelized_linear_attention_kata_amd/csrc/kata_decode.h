@@ -128,31 +128,54 @@ __host__ __device__ constexpr int packed_a(int r) { return r < 128 ? r & 15 : r 
 // phi_p(k)[r] = w_a w_b, then y = sum_r c_r phi_p(q)[r] Sp[r] / sum_r c_r phi_p(q)[r] zp[r]
 // with c_r = 1 on the diagonal (delta = 0) and 2 off it (each pair stands for two mirror
 // rows of the canonical state).  Equal to kata_decode_step on the canonical state.
-template <typename TIn, typename TOut, int DV>
+// DECAY: the state is first multiplied by gamma = exp(lam[stream, head]), as in
+// kata_decode_step<..., DECAY>.  G > 1 (P [H, G, p, d]): KATA-Mg (G packed blocks,
+// factor-major, each updated by its factor's feature) or SUMG (KATA-Sigma-g: one packed
+// block, the features summed over the factors), as in kata_decode_step_factors.
+template <typename TIn, typename TOut, int DV, int G = 1, bool SUMG = false, bool DECAY = false>
 __global__ void __launch_bounds__(256)
 kata_decode_step_packed(float* __restrict__ S, float* __restrict__ z, const TIn* __restrict__ q,
                         const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
-                        TOut* __restrict__ y, int H, int d) {
+                        TOut* __restrict__ y, int H, int d, const float* __restrict__ lam) {
+  static_assert(!(DECAY && G > 1), "decay gates with one PSD factor only");
+  constexpr int NF = SUMG ? 1 : G;          // packed state blocks
+  constexpr int ROWS = NF * DPK;
   constexpr int QPR = DV / 4;               // float4 quads per state row
   constexpr int ROWS_PER_IT = 256 / QPR;    // rows covered per pass of the block
-  constexpr int NIT = (DPK + ROWS_PER_IT - 1) / ROWS_PER_IT;
-  __shared__ float su[P_DIM], sw[P_DIM];
-  __shared__ float fu[DPK], fw[DPK];
+  constexpr int NIT = (ROWS + ROWS_PER_IT - 1) / ROWS_PER_IT;
+  __shared__ float su[G][P_DIM], sw[G][P_DIM];
+  __shared__ float fu[ROWS], fw[ROWS];
   __shared__ float red[4][DV];
   __shared__ float dred[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nh = blockIdx.x;
   const int h = (int)(nh % H);
-  const float* Ph = P + (int64_t)h * P_DIM * d;
-
-  const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
-  const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
-  if ((tid & 15) == 0) { su[tid >> 4] = u; sw[tid >> 4] = w; }
+  float gam = 1.f;
+  if constexpr (DECAY) gam = __expf(lam[nh]);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float* Ph = P + ((int64_t)h * G + i) * P_DIM * d;
+    const float u = project_row<TIn>(q + nh * d, Ph, d, tid);
+    const float w = project_row<TIn>(k + nh * d, Ph, d, tid);
+    if ((tid & 15) == 0) {
+      su[i][tid >> 4] = u;
+      sw[i][tid >> 4] = w;
+    }
+  }
   __syncthreads();
-  if (tid < DPK) {
-    const int dl = packed_delta(tid), a = packed_a(tid), b = (a + dl) & 15;
-    fu[tid] = (dl == 0 ? 1.f : 2.f) * su[a] * su[b];
-    fw[tid] = sw[a] * sw[b];
+  for (int r = tid; r < ROWS; r += 256) {
+    const int blk = r / DPK, rr = r - blk * DPK;
+    const int dl = packed_delta(rr), a = packed_a(rr), b = (a + dl) & 15;
+    float xu = 0.f, xw = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (SUMG || i == blk) {
+        xu += su[i][a] * su[i][b];
+        xw += sw[i][a] * sw[i][b];
+      }
+    }
+    fu[r] = (dl == 0 ? 1.f : 2.f) * xu;
+    fw[r] = xw;
   }
   __syncthreads();
 
@@ -160,28 +183,28 @@ kata_decode_step_packed(float* __restrict__ S, float* __restrict__ z, const TIn*
   f32x4 vv;
 #pragma unroll
   for (int i = 0; i < 4; ++i) vv[i] = (float)v[nh * DV + 4 * c4 + i];
-  float* Sh = S + nh * (int64_t)DPK * DV;
+  float* Sh = S + nh * (int64_t)ROWS * DV;
   f32x4 acc = zero4();
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int row = it * ROWS_PER_IT + tid / QPR;
-    if (row < DPK) {
+    if (row < ROWS) {
       f32x4* ptr = reinterpret_cast<f32x4*>(Sh + row * DV + 4 * c4);
       f32x4 sv = *ptr;
       const float fwr = fw[row], fur = fu[row];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] += fwr * vv[i];
+      for (int i = 0; i < 4; ++i) sv[i] = (DECAY ? gam * sv[i] : sv[i]) + fwr * vv[i];
       *ptr = sv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += fur * sv[i];
     }
   }
   float dp = 0.f;
-  if (tid < DPK) {
-    float* zh = z + nh * DPK;
-    const float zn = zh[tid] + fw[tid];
-    zh[tid] = zn;
-    dp = fu[tid] * zn;
+  float* zh = z + nh * (int64_t)ROWS;
+  for (int r = tid; r < ROWS; r += 256) {
+    const float zn = (DECAY ? gam * zh[r] : zh[r]) + fw[r];
+    zh[r] = zn;
+    dp += fu[r] * zn;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) dp += __shfl_xor(dp, off);

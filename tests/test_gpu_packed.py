@@ -144,6 +144,68 @@ def test_packed_decode_workload_sampled():
     assert slice_rel(zu.cpu().numpy(), z.cpu().numpy()) <= 1e-6
 
 
+def _sym_blocks(N, H, blocks, dv, g):
+    """Random canonical states with equal mirror rows: [N, H, blocks*256, dv] and z."""
+    S, z = symmetric_state(N, H * blocks, dv, g)
+    return S.reshape(N, H, blocks * 256, dv), z.reshape(N, H, blocks * 256)
+
+
+def _tokens(N, H, d, g, dt=torch.bfloat16):
+    return [(torch.randn((N, H, d), generator=g) / 8).to(dt) for _ in range(3)]
+
+
+def test_packed_decay_step_against_oracle_and_canonical():
+    g = torch.Generator().manual_seed(94)
+    N, H, d = 5, 3, 64
+    S, z = symmetric_state(N, H, d, g)
+    q, k, v = _tokens(N, H, d, g)
+    P = torch.randn((H, 16, d), generator=g) / d ** 0.5
+    lam = torch.log(torch.rand((N, H), generator=g) * 0.1 + 0.9)
+    dq, dk, dvv, dP, dlam = (x.to(DEV) for x in (q, k, v, P, lam))
+    Sp, zp = kata.state_pack(S.to(DEV), z.to(DEV))
+    yp = kata.decode_step_decay_packed(Sp, zp, dq, dk, dvv, dP, dlam)
+    Sc, zc = S.to(DEV), z.to(DEV)
+    yc = kata.decode_step_decay(Sc, zc, dq, dk, dvv, dP, dlam)
+    Su, zu = kata.state_unpack(Sp, zp)
+    torch.cuda.synchronize()
+    yr, Sr, zr = O.decode_decay_reference(S.double().numpy(), z.double().numpy(), host64(q), host64(k), host64(v),
+                                          P.double().numpy(), lam.double().numpy())
+    assert slice_rel(yp.double().cpu().numpy()[:, :, None], yr[:, :, None]) <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sr) <= 1e-6 and slice_rel(zu.cpu().numpy(), zr) <= 1e-6
+    # the canonical step sums 256 terms, the packed one 136, of a state whose sums cancel
+    # in part: the two y agree to the oracle's decode bound
+    assert slice_rel(yp.double().cpu().numpy()[:, :, None], yc.double().cpu().numpy()[:, :, None]) <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sc.cpu().numpy()) <= 1e-6
+
+
+@pytest.mark.parametrize("mode,G", [("concat", 2), ("concat", 3), ("sum", 2), ("sum", 3)])
+def test_packed_factor_step_against_oracle_and_canonical(mode, G):
+    g = torch.Generator().manual_seed(95 + G)
+    N, H, d = 4, 3, 64
+    blocks = G if mode == "concat" else 1
+    S, z = _sym_blocks(N, H, blocks, d, g)
+    q, k, v = _tokens(N, H, d, g)
+    P = torch.randn((H, G, 16, d), generator=g) / d ** 0.5
+    dq, dk, dvv, dP = (x.to(DEV) for x in (q, k, v, P))
+    # a concatenated state is G canonical blocks: pack them as N*H*G states
+    Sp, zp = kata.state_pack(S.to(DEV).reshape(N, H * blocks, 256, d), z.to(DEV).reshape(N, H * blocks, 256))
+    Sp, zp = Sp.reshape(N, H, blocks * 136, d), zp.reshape(N, H, blocks * 136)
+    yp = kata.decode_step_factors_packed(Sp, zp, dq, dk, dvv, dP, mode)
+    Sc, zc = S.to(DEV), z.to(DEV)
+    yc = kata.decode_step_factors(Sc, zc, dq, dk, dvv, dP, mode)
+    Su, zu = kata.state_unpack(Sp.reshape(N, H * blocks, 136, d), zp.reshape(N, H * blocks, 136))
+    torch.cuda.synchronize()
+    Su, zu = Su.reshape(N, H, blocks * 256, d), zu.reshape(N, H, blocks * 256)
+    yr, Sr, zr = O.decode_factors_reference(S.double().numpy(), z.double().numpy(), host64(q), host64(k),
+                                            host64(v), P.double().numpy(), mode)
+    ey = slice_rel(yp.double().cpu().numpy()[:, :, None], yr[:, :, None])
+    print(f"[packed factors {mode} g={G}] rel y {ey:.2e}", flush=True)
+    assert ey <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sr) <= 1e-6 and slice_rel(zu.cpu().numpy(), zr) <= 1e-6
+    assert slice_rel(yp.double().cpu().numpy()[:, :, None], yc.double().cpu().numpy()[:, :, None]) <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sc.cpu().numpy()) <= 1e-6
+
+
 def test_packed_empty_is_a_no_op():
     Sp = torch.zeros((0, 4, 136, 64), device=DEV)
     zp = torch.zeros((0, 4, 136), device=DEV)

@@ -130,7 +130,8 @@ def source_hash(extra=()) -> str:
 # Headers each bench mode's kernels live in; the mode's counters are keyed by their hash
 # together with all of kata.hip (the forward keeps its narrower hash, see source_hash).
 PATH_HEADERS = {"decay": ("kata_chunk.h",), "backward": ("kata_bwd.h",), "flash": ("kata_flash.h",),
-                "delta": ("kata_delta.h",), "decode": ("kata_decode.h",), "decode_delta": ("kata_delta.h",)}
+                "delta": ("kata_delta.h",), "decode": ("kata_decode.h",), "decode_delta": ("kata_delta.h",),
+                "decode_delta_packed": ("kata_delta.h", "kata_decode.h")}
 
 
 def path_hash(mode: str) -> str:
@@ -411,9 +412,6 @@ def bench_decode(args):
     if delta and G > 1:
         print("bench.py --decode takes --delta or --factors, not both", file=sys.stderr)
         sys.exit(2)
-    if packed and delta:
-        print("bench.py --decode --packed: the additive steps only (not --delta)", file=sys.stderr)
-        sys.exit(2)
     dc = I.make_decode(device=dev)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
     prefill = None
@@ -427,6 +425,8 @@ def bench_decode(args):
         pf1.record()
         torch.cuda.synchronize()
         pms = pf0.elapsed_time(pf1)
+        if packed:        # the delta-rule export has equal mirror rows: packing it is exact
+            S0 = kata.state_pack(S0)
         pbytes = N * H * (T0 * (2 * d + dv) * 2 + T0 * (dv * 2 + 4) + 256 * dv * 4)
         prefill = {"kernel": "kata_delta_recurrent", "tokens": N * T0, "ms": round(pms, 3),
                    "tokens_per_s": N * T0 / (pms / 1e3), "hbm_GBps": round(pbytes / (pms / 1e3) / 1e9, 1)}
@@ -447,7 +447,10 @@ def bench_decode(args):
     ys = torch.empty((steps, N, H, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if delta:
+    if delta and packed:
+        def run(j):
+            kata.decode_step_delta_packed(S, dc.q[j], dc.k[j], dc.v[j], dc.P, betas[j], y=ys[j], stream=stream)
+    elif delta:
         def run(j):
             kata.decode_step_delta(S, dc.q[j], dc.k[j], dc.v[j], dc.P, betas[j], y=ys[j], stream=stream)
     elif G > 1 and packed:
@@ -495,14 +498,14 @@ def bench_decode(args):
                     else ("kata_decode_step_factors" if G > 1 else "kata_decode_step")))
     fname = {"concat": f"KATA-M{G} ", "sum": f"KATA-Sigma{G} "}[fmode] if G > 1 else ""
     mode = ("decode_delta" if delta else
-            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode")
-            + ("_packed" if packed else ""))
+            (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode")) + ("_packed" if packed else "")
     src = path_hash(mode)
     traffic = mode_traffic(mode, kernel.split(" ")[0])
     rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
     prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
-    state_desc = (f"packed symmetric fp32 state [{N},{H},{rows * 136 // 256},{dv}] + z (kata_state_pack of the "
-                  f"export)" if packed else f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}")
+    state_desc = (f"packed symmetric fp32 state [{N},{H},{rows * 136 // 256},{dv}]{'' if delta else ' + z'} "
+                  f"(kata_state_pack of the export)" if packed
+                  else f"canonical fp32 state [{N},{H},{rows},{dv}]{'' if delta else ' + z'}")
     workload = (f"recurrent {'DeltaKATA ' if delta else fname}decode: {N} streams x {H} heads, d=dv={d}, p=16, "
                 f"{state_desc}, prefill T={T0} by "
                 f"{prefill_fn}, {steps} steps, every 4th key repeating an earlier one"

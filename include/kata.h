@@ -422,6 +422,17 @@ kata_status kata_decode_step_delta(int64_t N, int64_t H, int d, int dv, int p,
                                    float* S, const void* q, const void* k, const void* v,
                                    const float* P, const float* beta, void* y, void* stream);
 
+/* kata_decode_step_delta on the packed symmetric state (layout as for
+ * kata_decode_step_packed; pack with kata_state_pack, z NULL): every update adds
+ * beta phi^(k) e^T with phi^(k) symmetric, so the packed step writes a pair's row with
+ * the unweighted feature and reads it with weight 2 off the diagonal.
+ * Sp [N,H,136,dv] float32 in place; other arguments, support and errors as for
+ * kata_decode_step_delta. */
+kata_status kata_decode_step_delta_packed(int64_t N, int64_t H, int d, int dv, int p,
+                                          kata_dtype in_dtype, kata_dtype out_dtype,
+                                          float* Sp, const void* q, const void* k, const void* v,
+                                          const float* P, const float* beta, void* y, void* stream);
+
 /* Feature layouts for kata_feature_map. */
 typedef enum {
   KATA_FEATURE_FULL = 0,         /* p*p entries, index i*p + j: phi = vec(u u^T)       */

@@ -12,7 +12,8 @@ _BINDING_NAMES = (
     "forward_delta_chunked_workspace_bytes", "forward_factors",
     "forward_factors_workspace_bytes", "feature_map", "flash_forward", "flash_workspace_bytes",
     "forward", "forward_workspace_bytes", "library_path", "load_library",
-    "decode_step_packed", "decode_step_decay_packed", "decode_step_factors_packed", "state_pack", "state_unpack",
+    "decode_step_packed", "decode_step_decay_packed", "decode_step_delta_packed", "decode_step_factors_packed",
+    "state_pack", "state_unpack",
     "PACKED_ROWS",
 )
 

@@ -100,6 +100,8 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_decay.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 11 + [sz, vp]
     lib.kata_decode_step_packed.restype = ci
     lib.kata_decode_step_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kata_decode_step_delta_packed.restype = ci
+    lib.kata_decode_step_delta_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci] + [vp] * 8
     lib.kata_decode_step_decay_packed.restype = ci
     lib.kata_decode_step_decay_packed.argtypes = [i64, i64, ci, ci, ci, ci, ci] + [vp] * 9
     lib.kata_decode_step_factors_packed.restype = ci
@@ -773,6 +775,31 @@ def decode_step_packed(Sp: torch.Tensor, zp: torch.Tensor, q: torch.Tensor, k: t
                                         _ptr(zp), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(y),
                                         _stream_handle(stream, dev))
     _check(st, "kata_decode_step_packed")
+    return y
+
+
+def decode_step_delta_packed(Sp: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
+                             beta: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                             y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_step_delta on the packed state (kata_decode_step_delta_packed): Sp [N,H,136,dv]
+    updated in place; beta [N,H] fp32.  Returns y [N,H,dv]."""
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(Sp, "Sp", (N, H, PACKED_ROWS, dv), torch.float32, dev)
+    _need(q, "q", (N, H, d), device=dev)
+    _need(k, "k", (N, H, d), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (N, H, dv), out_dtype, dev)
+    st = _lib().kata_decode_step_delta_packed(N, H, d, dv, P_DIM, _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                              _ptr(Sp), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(beta), _ptr(y),
+                                              _stream_handle(stream, dev))
+    _check(st, "kata_decode_step_delta_packed")
     return y
 
 

@@ -340,12 +340,14 @@ size_t decay_ws_bytes(const Plan& pl, const kata_forward_desc* d) {
 }
 
 // DeltaKATA token recurrence: one workgroup per (sequence, head), T tokens each.
+// PACKED: the state in the packed symmetric layout (kata_decode_step_delta_packed)
+template <bool PACKED = false>
 kata_status launch_delta(int64_t BH, int64_t T, int H, int d, int dv, kata_dtype in_dtype, kata_dtype out_dtype,
                          const float* S0, float* ST, const void* q, const void* k, const void* v,
                          const float* beta, const float* P, void* y, hipStream_t st) {
   const dim3 grid((unsigned)BH);
-#define KATA_DELTA(TI, TO, DVV)                                                                              \
-  hipLaunchKernelGGL((kata::kata_delta_recurrent<TI, TO, DVV>), grid, dim3(256), 0, st, S0, ST, (const TI*)q, \
+#define KATA_DELTA(TI, TO, DVV)                                                                                      \
+  hipLaunchKernelGGL((kata::kata_delta_recurrent<TI, TO, DVV, PACKED>), grid, dim3(256), 0, st, S0, ST, (const TI*)q, \
                      (const TI*)k, (const TI*)v, beta, P, (TO*)y, H, d, T)
   const bool fi = in_dtype == KATA_F32, fo = out_dtype == KATA_F32;
   if (dv == 64) {
@@ -927,6 +929,16 @@ kata_status kata_decode_step_delta(int64_t N, int64_t H, int d, int dv, int p, k
   if (N * H == 0) return KATA_OK;
   if (!S || !q || !k || !v || !P || !beta || !y) return KATA_ERR_NULL;
   return launch_delta(N * H, 1, (int)H, d, dv, in_dtype, out_dtype, S, S, q, k, v, beta, P, y, (hipStream_t)stream);
+}
+
+kata_status kata_decode_step_delta_packed(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype,
+                                          kata_dtype out_dtype, float* Sp, const void* q, const void* k,
+                                          const void* v, const float* P, const float* beta, void* y, void* stream) {
+  const kata_status s = validate_decode(N, H, d, dv, p, in_dtype, out_dtype);
+  if (s != KATA_OK || N * H == 0) return s;
+  if (!Sp || !q || !k || !v || !P || !beta || !y) return KATA_ERR_NULL;
+  return launch_delta<true>(N * H, 1, (int)H, d, dv, in_dtype, out_dtype, Sp, Sp, q, k, v, beta, P, y,
+                            (hipStream_t)stream);
 }
 
 kata_status kata_forward_factors_workspace_bytes(const kata_forward_desc* desc, int g, kata_factor_mode mode,

@@ -23,27 +23,33 @@
 #pragma once
 
 #include "kata_chunk.h"   // kata_common.h, and row_plus (DPP row rotation)
+#include "kata_decode.h"  // the packed state rows (DPK, packed_delta, packed_a)
 
 namespace kata {
 
-template <int DV>
+// PACKED: the state in the packed symmetric layout of kata_decode_step_packed (136 rows,
+// one per pair {a, b}): every delta-rule update adds beta phi^(k) e^T with phi^(k)
+// symmetric, and the reads S^T phi^(x) see only the sum of the mirror rows, so the step
+// updates a pair's row with the unweighted feature and reads it with weight 2 off the
+// diagonal.
+template <int DV, bool PACKED = false>
 struct DeltaLayout {
-  static constexpr int D = P_DIM * P_DIM;
+  static constexpr int D = PACKED ? DPK : P_DIM * P_DIM;
   static constexpr int QPR = DV / 4;     // float4 quads per state row
   static constexpr int RPI = 256 / QPR;  // rows covered by the block per register quad
-  static constexpr int NIT = D / RPI;    // register quads per thread
+  static constexpr int NIT = (D + RPI - 1) / RPI;   // register quads per thread (last one partial)
   static_assert(DV == 16 || DV == 64, "dv 16 or 64");
 };
 
 // grid B*H, block 256.  S0 (nullable) is read before anything is written and ST
 // (nullable) written at the end, so S0 == ST (an in-place decode step) is allowed.
 // q, k [B*H, T, d]; v [B*H, T, DV]; beta [B*H, T]; y [B*H, T, DV].
-template <typename TIn, typename TOut, int DV>
+template <typename TIn, typename TOut, int DV, bool PACKED = false>
 __global__ void __launch_bounds__(256)
 kata_delta_recurrent(const float* S0, float* ST, const TIn* __restrict__ q, const TIn* __restrict__ k,
                      const TIn* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ P,
                      TOut* __restrict__ y, int H, int d, int64_t T) {
-  using L = DeltaLayout<DV>;
+  using L = DeltaLayout<DV, PACKED>;
   __shared__ __align__(16) float su[2][P_DIM];
   __shared__ __align__(16) float sw[2][P_DIM];
   __shared__ __align__(16) float red[2][2][4][DV];
@@ -63,7 +69,7 @@ kata_delta_recurrent(const float* S0, float* ST, const TIn* __restrict__ q, cons
 #pragma unroll
   for (int it = 0; it < L::NIT; ++it) {
     const int row = it * L::RPI + r0;
-    s[it] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + row * DV + 4 * c4) : zero4();
+    s[it] = (S0 && row < L::D) ? *reinterpret_cast<const f32x4*>(S0 + sbase + row * DV + 4 * c4) : zero4();
   }
 
   for (int64_t t = 0; t < T; ++t) {
@@ -113,12 +119,23 @@ kata_delta_recurrent(const float* S0, float* ST, const TIn* __restrict__ q, cons
 #pragma unroll
     for (int it = 0; it < L::NIT; ++it) {
       const int row = it * L::RPI + r0;
-      const int a = row >> 4, b = row & 15;
-      fk[it] = sw[buf][a] * sw[buf][b] * iw;
-      const float fq = su[buf][a] * su[buf][b] * iu;
+      int a, b;
+      float c = 1.f;                   // read weight of the row
+      if constexpr (PACKED) {
+        const bool live = row < L::D;  // the rows past the packed state (last quad) read as zero
+        const int dl = live ? packed_delta(row) : 0;
+        a = live ? packed_a(row) : 0;
+        b = (a + dl) & 15;
+        c = live ? (dl == 0 ? 1.f : 2.f) : 0.f;
+      } else {
+        a = row >> 4;
+        b = row & 15;
+      }
+      fk[it] = (PACKED && row >= L::D) ? 0.f : sw[buf][a] * sw[buf][b] * iw;
+      const float fq = su[buf][a] * su[buf][b] * iu * c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ak[i] += fk[it] * s[it][i];
+        ak[i] += c * fk[it] * s[it][i];
         aq[i] += fq * s[it][i];
       }
     }
@@ -164,7 +181,7 @@ kata_delta_recurrent(const float* S0, float* ST, const TIn* __restrict__ q, cons
 #pragma unroll
     for (int it = 0; it < L::NIT; ++it) {
       const int row = it * L::RPI + r0;
-      *reinterpret_cast<f32x4*>(ST + sbase + row * DV + 4 * c4) = s[it];
+      if (row < L::D) *reinterpret_cast<f32x4*>(ST + sbase + row * DV + 4 * c4) = s[it];
     }
   }
 }

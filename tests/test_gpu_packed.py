@@ -206,6 +206,38 @@ def test_packed_factor_step_against_oracle_and_canonical(mode, G):
     assert slice_rel(Su.cpu().numpy(), Sc.cpu().numpy()) <= 1e-6
 
 
+def test_packed_delta_step_against_oracle_and_canonical():
+    """The DeltaKATA decode step on the packed state, from a kata_forward_delta export
+    (packed exactly: its mirror rows are equal), over ten steps: against
+    kata_decode_step_delta on the canonical export, and against the oracle's delta steps
+    from the oracle's own recurrence over the same prefix."""
+    case = I.make_forward("mid", B=3, H=2, T=60, seed=97)
+    beta = I.make_beta(3, 2, 60, seed=97)
+    q, k, v, P, b = (t.to(DEV) for t in (case.q, case.k, case.v, case.P, beta))
+    pre = slice(0, 50)
+    _, S = kata.forward_delta(q[:, :, pre].contiguous(), k[:, :, pre].contiguous(), v[:, :, pre].contiguous(), P,
+                              b[:, :, pre].contiguous(), return_state=True)
+    Sp = kata.state_pack(S)
+    torch.cuda.synchronize()
+    assert torch.equal(kata.state_unpack(Sp), S)
+    q64, k64, v64, P64 = host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy()
+    b64 = beta.double().numpy()
+    _, Sref = O.delta_recurrence(q64[:, :, pre], k64[:, :, pre], v64[:, :, pre], P64, b64[:, :, pre])
+    for t in range(50, 60):
+        qt, kt, vt = (x[:, :, t].contiguous() for x in (q, k, v))
+        bt = b[:, :, t].contiguous()
+        yc = kata.decode_step_delta(S, qt, kt, vt, P, bt)
+        yp = kata.decode_step_delta_packed(Sp, qt, kt, vt, P, bt)
+        torch.cuda.synchronize()
+        yr, Sref = O.delta_decode_reference(Sref, q64[:, :, t], k64[:, :, t], v64[:, :, t], P64, b64[:, :, t])
+        assert slice_rel(yp.double().cpu().numpy()[:, :, None], yc.double().cpu().numpy()[:, :, None]) <= 1e-4
+        assert slice_rel(yp.double().cpu().numpy()[:, :, None], yr[:, :, None]) <= 1e-3
+    Su = kata.state_unpack(Sp)
+    torch.cuda.synchronize()
+    assert slice_rel(Su.cpu().numpy(), S.cpu().numpy()) <= 1e-5
+    assert slice_rel(Su.cpu().numpy(), Sref) <= 1e-3
+
+
 def test_packed_empty_is_a_no_op():
     Sp = torch.zeros((0, 4, 136, 64), device=DEV)
     zp = torch.zeros((0, 4, 136), device=DEV)

@@ -43,6 +43,18 @@ int main(void) {
                          NULL) == KATA_OK);
   CHECK(kata_decode_step_delta(0, 16, 64, 64, 16, KATA_BF16, KATA_F32, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                                NULL) == KATA_OK);
+  /* the packed symmetric state: no-ops on empty input, argument errors before any device call */
+  CHECK(KATA_PACKED_ROWS == 136);
+  CHECK(kata_state_pack(0, 64, NULL, NULL, NULL, NULL, NULL) == KATA_OK);
+  CHECK(kata_state_unpack(4, 32, NULL, NULL, NULL, NULL, NULL) == KATA_ERR_UNSUPPORTED);
+  CHECK(kata_decode_step_packed(0, 16, 64, 64, 16, KATA_BF16, KATA_F32, NULL, NULL, NULL, NULL, NULL, NULL,
+                                NULL, NULL) == KATA_OK);
+  CHECK(kata_decode_step_decay_packed(4, 16, 64, 64, 8, KATA_BF16, KATA_F32, NULL, NULL, NULL, NULL, NULL, NULL,
+                                      NULL, NULL, NULL) == KATA_ERR_UNSUPPORTED);
+  CHECK(kata_decode_step_delta_packed(-1, 16, 64, 64, 16, KATA_BF16, KATA_F32, NULL, NULL, NULL, NULL, NULL,
+                                      NULL, NULL, NULL) == KATA_ERR_SHAPE);
+  CHECK(kata_decode_step_factors_packed(4, 16, 64, 64, 16, 4, KATA_FACTORS_SUM, KATA_BF16, KATA_F32, NULL, NULL,
+                                        NULL, NULL, NULL, NULL, NULL, NULL) == KATA_ERR_UNSUPPORTED);
   if (fails == 0) printf("kata.h from C: ok\n");
   return fails == 0 ? 0 : 1;
 }

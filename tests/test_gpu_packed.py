@@ -154,9 +154,10 @@ def _tokens(N, H, d, g, dt=torch.bfloat16):
     return [(torch.randn((N, H, d), generator=g) / 8).to(dt) for _ in range(3)]
 
 
-def test_packed_decay_step_against_oracle_and_canonical():
+@pytest.mark.parametrize("d", [64, 16])
+def test_packed_decay_step_against_oracle_and_canonical(d):
     g = torch.Generator().manual_seed(94)
-    N, H, d = 5, 3, 64
+    N, H = 5, 3
     S, z = symmetric_state(N, H, d, g)
     q, k, v = _tokens(N, H, d, g)
     P = torch.randn((H, 16, d), generator=g) / d ** 0.5
@@ -178,10 +179,11 @@ def test_packed_decay_step_against_oracle_and_canonical():
     assert slice_rel(Su.cpu().numpy(), Sc.cpu().numpy()) <= 1e-6
 
 
-@pytest.mark.parametrize("mode,G", [("concat", 2), ("concat", 3), ("sum", 2), ("sum", 3)])
-def test_packed_factor_step_against_oracle_and_canonical(mode, G):
+@pytest.mark.parametrize("mode,G,d", [("concat", 2, 64), ("concat", 3, 64), ("sum", 2, 64), ("sum", 3, 64),
+                                      ("concat", 2, 16), ("sum", 3, 16)])
+def test_packed_factor_step_against_oracle_and_canonical(mode, G, d):
     g = torch.Generator().manual_seed(95 + G)
-    N, H, d = 4, 3, 64
+    N, H = 4, 3
     blocks = G if mode == "concat" else 1
     S, z = _sym_blocks(N, H, blocks, d, g)
     q, k, v = _tokens(N, H, d, g)
@@ -236,6 +238,32 @@ def test_packed_delta_step_against_oracle_and_canonical():
     torch.cuda.synchronize()
     assert slice_rel(Su.cpu().numpy(), S.cpu().numpy()) <= 1e-5
     assert slice_rel(Su.cpu().numpy(), Sref) <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 16])
+def test_packed_delta_step_from_a_given_state(d):
+    """One DeltaKATA step on the packed state from a symmetric fp32 state built on the
+    host (for d = dv = 16 the last register quad of every thread lies past the 136 rows),
+    against the oracle's delta step and against kata_decode_step_delta."""
+    g = torch.Generator().manual_seed(98)
+    N, H = 5, 3
+    S, _ = symmetric_state(N, H, d, g)
+    q, k, v = _tokens(N, H, d, g)
+    P = torch.randn((H, 16, d), generator=g) / d ** 0.5
+    beta = torch.rand((N, H), generator=g) * 0.5 + 0.5
+    dq, dk, dvv, dP, db = (x.to(DEV) for x in (q, k, v, P, beta))
+    Sp = kata.state_pack(S.to(DEV))
+    yp = kata.decode_step_delta_packed(Sp, dq, dk, dvv, dP, db)
+    Sc = S.to(DEV)
+    yc = kata.decode_step_delta(Sc, dq, dk, dvv, dP, db)
+    Su = kata.state_unpack(Sp)
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_decode_reference(S.double().numpy(), host64(q), host64(k), host64(v), P.double().numpy(),
+                                      beta.double().numpy())
+    assert slice_rel(yp.double().cpu().numpy()[:, :, None], yr[:, :, None]) <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sr) <= 1e-6
+    assert slice_rel(yp.double().cpu().numpy()[:, :, None], yc.double().cpu().numpy()[:, :, None]) <= 1e-4
+    assert slice_rel(Su.cpu().numpy(), Sc.cpu().numpy()) <= 1e-6
 
 
 def test_packed_empty_is_a_no_op():

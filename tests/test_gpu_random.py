@@ -1,0 +1,232 @@
+"""Randomised-shape parity: seeded draws of batch, heads, length, head width, input dtype,
+chunk size and an initial state carried over from a prefix, each path against the
+oracle at the bars of the fixed-shape tests.
+
+Per draw: the chunked forward (y and the final state), the decay-gated forward, both
+factor modes, the backward (bf16, d = 64, C = 64, the shapes those paths take), the
+chunked DeltaKATA forward, and two packed decode steps from the prefix's state.
+
+Conditioning.  The output gate divides by den_t = sum_s (u_t.w_s)^2 (the prefix's keys
+included, through z0).  A bf16 feature rounds each term by about 2^-9 of
+|u_t|^2 |w_s|^2, so where den_t is a tiny fraction of sum_s |u_t|^2 |w_s|^2 (a query
+nearly orthogonal to every key) y_t is set by rounding on any path that stores bf16
+features, and no relative bound holds for it.  The exception is a single key, where
+y_t = v_s for any nonzero weight.  A draw in which some query with two or more keys has
+den_t below 1e-2 of that sum is rejected on the host, from the seeded inputs alone, and
+drawn again; the packed decode draws are checked the same way.  At T = 1 the DeltaKATA
+output is beta (u.w)^2 / (|u|^2 |w|^2) v: one squared cosine, compared as an absolute
+error on the scale beta |v|.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import kernelized_linear_attention_kata_amd as kata
+from kernelized_linear_attention_kata_amd import inputs as I
+from oracle import kata_oracle as O
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NDRAWS = 12
+MIN_RATIO = 1e-2
+
+
+def host64(t):
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(I.bf16_bits(t))
+    return t.detach().double().cpu().numpy()
+
+
+def slice_rel(got, ref):
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    g = g.reshape(g.shape[0] * g.shape[1], -1)
+    r = r.reshape(r.shape[0] * r.shape[1], -1)
+    den = np.linalg.norm(r, axis=1)
+    return float(np.max(np.linalg.norm(g - r, axis=1) / np.where(den == 0, 1.0, den)))
+
+
+def _draw(i, attempt, bf16_only):
+    r = np.random.default_rng([9000 + i, attempt, int(bf16_only)])
+    d = 64 if bf16_only else int(r.choice([16, 64]))
+    dtype = "bf16" if bf16_only else str(r.choice(["f32", "bf16"]))
+    chunk = 64 if bf16_only else int(r.choice([32, 64, 128]))
+    B, H = int(r.integers(1, 4)), int(r.integers(1, 5))
+    T = int(r.choice([1, 2, 17, 63, 64, 65, 127, 200, 333]))
+    T0 = int(r.choice([0, 17, 48]))
+    name = "tiny" if d == 16 else "mid"
+    seed = int(r.integers(1 << 30))
+    case = I.make_forward(name, B=B, H=H, T=T, seed=seed, dtype=dtype)
+    pre = I.make_forward(name, B=B, H=H, T=T0, seed=seed + 1, dtype=dtype) if T0 else None
+    return case, pre, chunk
+
+
+def draw(i, bf16_only=False):
+    """Draw i: a forward case, the prefix that builds its initial state (or None) and a
+    chunk size.  bf16_only keeps to the shapes of the decay, factor and backward paths
+    (d = 64, bf16 inputs, C = 64).  Ill-conditioned draws are rejected and redrawn."""
+    for attempt in range(64):
+        case, pre, chunk = _draw(i, attempt, bf16_only)
+        if gate_ratio(case, pre) >= MIN_RATIO:
+            return case, pre, chunk
+    raise RuntimeError(f"no well-conditioned draw for {i}")
+
+
+def prefix_state(case, pre):
+    if pre is None:
+        return None, None
+    S0, z0 = O.final_state(host64(pre.k), host64(pre.v), case.P.double().numpy())
+    return torch.from_numpy(S0).float(), torch.from_numpy(z0).float()
+
+
+def gate_ratio(case, pre):
+    """min over queries with two or more keys of den_t / sum_s |u_t|^2 |w_s|^2."""
+    P = case.P.double().numpy()
+    q, k = host64(case.q), host64(case.k)
+    n0 = 0 if pre is None else pre.T
+    k0 = host64(pre.k) if pre is not None else None
+    t = np.arange(case.T)
+    worst = np.inf
+    for b in range(case.B):
+        for h in range(case.H):
+            U = q[b, h] @ P[h].T
+            W = k[b, h] if k0 is None else np.concatenate([k0[b, h], k[b, h]])
+            W = W @ P[h].T
+            den = np.cumsum((U @ W.T) ** 2, axis=1)[t, n0 + t]
+            scale = (U * U).sum(1) * np.cumsum((W * W).sum(1))[n0 + t]
+            live = (n0 + t + 1 >= 2) & (scale > 0)
+            if live.any():
+                worst = min(worst, float(np.min(den[live] / scale[live])))
+    return worst
+
+
+def test_draws_span_the_shapes():
+    """The draws (host only): well-conditioned, and between them both head widths, both
+    input dtypes, every chunk size, runs with and without a prefix, and a one-token run."""
+    draws = [draw(i) for i in range(NDRAWS)]
+    assert all(gate_ratio(c, p) >= MIN_RATIO for c, p, _ in draws)
+    assert {c.d for c, _, _ in draws} == {16, 64}
+    assert {c.dtype for c, _, _ in draws} == {"f32", "bf16"}
+    assert {ch for _, _, ch in draws} == {32, 64, 128}
+    assert {p is None for _, p, _ in draws} == {True, False}
+    assert any(c.T == 1 for c, _, _ in draws)
+    for i in range(NDRAWS):
+        c, p, ch = draw(i, bf16_only=True)
+        assert (c.d, c.dtype, ch) == (64, "bf16", 64) and gate_ratio(c, p) >= MIN_RATIO
+
+
+def to_dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_forward(i):
+    case, pre, chunk = draw(i)
+    S0, z0 = prefix_state(case, pre)
+    q, k, v, P = to_dev(case.q, case.k, case.v, case.P)
+    y, ST, zT = kata.forward(q, k, v, P, chunk, S0=None if S0 is None else S0.to(DEV),
+                             z0=None if z0 is None else z0.to(DEV), return_state=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qh, kh, vh, Ph = host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy()
+    S0h = None if S0 is None else S0.double().numpy()
+    z0h = None if z0 is None else z0.double().numpy()
+    yr = O.forward_quadratic(qh, kh, vh, Ph, S0h, z0h)
+    Sr, zr = O.final_state(kh, vh, Ph, S0h, z0h)
+    ey, eS, ez = slice_rel(y.cpu().numpy(), yr), slice_rel(ST.cpu().numpy(), Sr), slice_rel(zT.cpu().numpy(), zr)
+    print(f"[draw {i}: B={case.B} H={case.H} T={case.T} d={case.d} {case.dtype} C={chunk} "
+          f"prefix={0 if pre is None else pre.T}] y {ey:.2e} S {eS:.2e} z {ez:.2e}", flush=True)
+    tol = TOL[case.dtype]
+    assert ey <= tol and eS <= tol and ez <= tol
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_decay_factors_backward(i):
+    case, pre, _ = draw(i, bf16_only=True)
+    S0, z0 = prefix_state(case, pre)
+    q, k, v, P = to_dev(case.q, case.k, case.v, case.P)
+    qh, kh, vh, Ph = host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy()
+    S0h = None if S0 is None else S0.double().numpy()
+    z0h = None if z0 is None else z0.double().numpy()
+    S0d = None if S0 is None else S0.to(DEV)
+    z0d = None if z0 is None else z0.to(DEV)
+    tag = f"[draw {i}: B={case.B} H={case.H} T={case.T} prefix={0 if pre is None else pre.T}]"
+
+    lam = I.make_log_decay(case.B, case.H, case.T, seed=i)
+    yd = kata.forward_decay(q, k, v, P, lam.to(DEV), 64, S0=S0d, z0=z0d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ed = slice_rel(yd.cpu().numpy(), O.forward_decay_quadratic(qh, kh, vh, Ph, lam.double().numpy(), S0h, z0h))
+
+    g = 2 + i % 2
+    Pg = I.make_factor_projections(case.H, g, 64, seed=i)
+    ef = {}
+    for mode, fn in (("concat", O.forward_mg_quadratic), ("sum", O.forward_sg_quadratic)):
+        yf = kata.forward_factors(q, k, v, Pg.to(DEV), mode, 64, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ef[mode] = slice_rel(yf.cpu().numpy(), fn(qh, kh, vh, Pg.double().numpy()))
+
+    gy = I.make_output_grad(case.B, case.H, case.T, 64, seed=i)
+    dq, dk, dv, _ = kata.backward(q, k, v, P, gy.to(DEV), 64, S0=S0d, z0=z0d)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.backward_quadratic(qh, kh, vh, Ph, host64(gy), S0h, z0h)[:3]
+    eg = {"dv": slice_rel(dv.float().cpu().numpy(), rv)}
+    if case.T + (0 if pre is None else pre.T) > 1:   # one token: y = v for any q, k, so dq = dk = 0
+        eg["dq"] = slice_rel(dq.float().cpu().numpy(), rq)
+        eg["dk"] = slice_rel(dk.float().cpu().numpy(), rk)
+    print(f"{tag} decay {ed:.2e} Mg {ef['concat']:.2e} Sg {ef['sum']:.2e} (g={g}) "
+          + " ".join(f"{n} {e:.2e}" for n, e in eg.items()), flush=True)
+    assert ed <= TOL["bf16"] and max(ef.values()) <= TOL["bf16"] and max(eg.values()) <= TOL["bf16"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_delta_chunked(i):
+    case, _, _ = draw(i)
+    q, k, v, P = to_dev(case.q, case.k, case.v, case.P)
+    beta = I.make_beta(case.B, case.H, case.T, seed=i)
+    y = kata.forward_delta_chunked(q, k, v, P, beta.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, _ = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                               beta.double().numpy())
+    yg = y.double().cpu().numpy()
+    if case.T == 1:
+        scale = np.linalg.norm(beta.double().numpy()[..., None] * host64(case.v), axis=-1)
+        e = float(np.max(np.linalg.norm(yg - yr, axis=-1) / scale))
+        bound = 4e-3 if case.dtype == "bf16" else 1e-4
+    else:
+        e = slice_rel(yg, yr)
+        bound = 5e-3 if case.dtype == "bf16" else TOL["f32"]
+    print(f"[draw {i}: B={case.B} H={case.H} T={case.T} d={case.d} {case.dtype}] delta y {e:.2e}", flush=True)
+    assert e <= bound
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_packed_decode(i):
+    """Two packed steps from a prefix state (17 or 48 tokens), y and the unpacked state."""
+    case, _, _ = draw(i)
+    r = np.random.default_rng(9700 + i)
+    N, H, d = int(r.integers(1, 41)), case.H, case.d
+    T0 = int(r.choice([17, 48]))
+    pre = I.make_forward(case.name, B=N, H=H, T=T0, seed=9800 + i, dtype=case.dtype)
+    step = I.make_forward(case.name, B=N, H=H, T=2, seed=9900 + i, dtype="bf16")
+    P = case.P
+    assert gate_ratio(dataclasses.replace(step, P=P), pre) >= MIN_RATIO
+    Sr, zr = O.final_state(host64(pre.k), host64(pre.v), P.double().numpy())
+    Sp, zp = kata.state_pack(torch.from_numpy(Sr).float().to(DEV), torch.from_numpy(zr).float().to(DEV))
+    for s in range(2):
+        qs, ks, vs = (x[:, :, s].contiguous() for x in (step.q, step.k, step.v))
+        y = kata.decode_step_packed(Sp, zp, *to_dev(qs, ks, vs, P))
+        torch.cuda.synchronize()
+        yr, Sr, zr = O.decode_reference(Sr, zr, host64(qs), host64(ks), host64(vs), P.double().numpy())
+        ey = slice_rel(y.cpu().numpy()[None], yr[None])
+        print(f"[draw {i}: N={N} H={H} d={d} prefix={T0} step {s}] y {ey:.2e}", flush=True)
+        assert ey <= TOL["bf16"]
+    S, z = kata.state_unpack(Sp, zp)
+    torch.cuda.synchronize()
+    eS, ez = slice_rel(S.cpu().numpy(), Sr), slice_rel(z.cpu().numpy(), zr)
+    print(f"[draw {i}] state S {eS:.2e} z {ez:.2e}", flush=True)
+    assert eS <= TOL["f32"] and ez <= TOL["f32"]

@@ -3,8 +3,10 @@ chunk size and an initial state carried over from a prefix, each path against th
 oracle at the bars of the fixed-shape tests.
 
 Per draw: the chunked forward (y and the final state), the decay-gated forward, both
-factor modes, the backward (bf16, d = 64, C = 64, the shapes those paths take), the
-chunked DeltaKATA forward, and two packed decode steps from the prefix's state.
+factor modes, the backward and the flash forward (bf16, d = 64, C = 64, the shapes those
+paths take), the chunked and the token-recurrent DeltaKATA forward, and two decode
+steps (KATA and DeltaKATA on the canonical state, KATA on the packed one) from states
+the oracle builds over a prefix.
 
 Conditioning.  The output gate divides by den_t = sum_s (u_t.w_s)^2 (the prefix's keys
 included, through z0).  A bf16 feature rounds each term by about 2^-9 of
@@ -48,7 +50,7 @@ def slice_rel(got, ref):
     return float(np.max(np.linalg.norm(g - r, axis=1) / np.where(den == 0, 1.0, den)))
 
 
-def _draw(i, attempt, bf16_only):
+def _draw(i, attempt, bf16_only, prefix=True):
     r = np.random.default_rng([9000 + i, attempt, int(bf16_only)])
     d = 64 if bf16_only else int(r.choice([16, 64]))
     dtype = "bf16" if bf16_only else str(r.choice(["f32", "bf16"]))
@@ -59,16 +61,17 @@ def _draw(i, attempt, bf16_only):
     name = "tiny" if d == 16 else "mid"
     seed = int(r.integers(1 << 30))
     case = I.make_forward(name, B=B, H=H, T=T, seed=seed, dtype=dtype)
-    pre = I.make_forward(name, B=B, H=H, T=T0, seed=seed + 1, dtype=dtype) if T0 else None
+    pre = I.make_forward(name, B=B, H=H, T=T0, seed=seed + 1, dtype=dtype) if T0 and prefix else None
     return case, pre, chunk
 
 
-def draw(i, bf16_only=False):
+def draw(i, bf16_only=False, prefix=True):
     """Draw i: a forward case, the prefix that builds its initial state (or None) and a
-    chunk size.  bf16_only keeps to the shapes of the decay, factor and backward paths
-    (d = 64, bf16 inputs, C = 64).  Ill-conditioned draws are rejected and redrawn."""
+    chunk size.  bf16_only keeps to the shapes of the decay, factor, backward and flash
+    paths (d = 64, bf16 inputs, C = 64); prefix=False draws no prefix (a path without an
+    initial state).  Ill-conditioned draws are rejected and redrawn."""
     for attempt in range(64):
-        case, pre, chunk = _draw(i, attempt, bf16_only)
+        case, pre, chunk = _draw(i, attempt, bf16_only, prefix)
         if gate_ratio(case, pre) >= MIN_RATIO:
             return case, pre, chunk
     raise RuntimeError(f"no well-conditioned draw for {i}")
@@ -115,6 +118,24 @@ def test_draws_span_the_shapes():
     for i in range(NDRAWS):
         c, p, ch = draw(i, bf16_only=True)
         assert (c.d, c.dtype, ch) == (64, "bf16", 64) and gate_ratio(c, p) >= MIN_RATIO
+        c, p, _ = draw(i, bf16_only=True, prefix=False)
+        assert p is None and gate_ratio(c, None) >= MIN_RATIO
+    for i in range(NDRAWS):
+        _, N, _, pre, step = decode_draw(i)
+        assert gate_ratio(step, pre) >= MIN_RATIO
+
+
+def decode_draw(i):
+    """Decode draw i: N streams with the heads, width and projection of forward draw i,
+    a 17- or 48-token prefix that builds the state, and two bf16 step tokens (the step
+    case carries the draw's projection, so gate_ratio applies to it)."""
+    case, _, _ = draw(i)
+    r = np.random.default_rng(9700 + i)
+    N, H = int(r.integers(1, 41)), case.H
+    T0 = int(r.choice([17, 48]))
+    pre = I.make_forward(case.name, B=N, H=H, T=T0, seed=9800 + i, dtype=case.dtype)
+    step = I.make_forward(case.name, B=N, H=H, T=2, seed=9900 + i, dtype="bf16")
+    return case, N, H, pre, dataclasses.replace(step, P=case.P)
 
 
 def to_dev(*ts):
@@ -207,14 +228,8 @@ def test_random_delta_chunked(i):
 @pytest.mark.parametrize("i", range(NDRAWS))
 def test_random_packed_decode(i):
     """Two packed steps from a prefix state (17 or 48 tokens), y and the unpacked state."""
-    case, _, _ = draw(i)
-    r = np.random.default_rng(9700 + i)
-    N, H, d = int(r.integers(1, 41)), case.H, case.d
-    T0 = int(r.choice([17, 48]))
-    pre = I.make_forward(case.name, B=N, H=H, T=T0, seed=9800 + i, dtype=case.dtype)
-    step = I.make_forward(case.name, B=N, H=H, T=2, seed=9900 + i, dtype="bf16")
-    P = case.P
-    assert gate_ratio(dataclasses.replace(step, P=P), pre) >= MIN_RATIO
+    case, N, H, pre, step = decode_draw(i)
+    d, T0, P = case.d, pre.T, case.P
     Sr, zr = O.final_state(host64(pre.k), host64(pre.v), P.double().numpy())
     Sp, zp = kata.state_pack(torch.from_numpy(Sr).float().to(DEV), torch.from_numpy(zr).float().to(DEV))
     for s in range(2):
@@ -230,3 +245,78 @@ def test_random_packed_decode(i):
     eS, ez = slice_rel(S.cpu().numpy(), Sr), slice_rel(z.cpu().numpy(), zr)
     print(f"[draw {i}] state S {eS:.2e} z {ez:.2e}", flush=True)
     assert eS <= TOL["f32"] and ez <= TOL["f32"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_flash(i):
+    """The flash-style forward (bf16, d = dv = 64, no initial state) on draw i's shape."""
+    case, _, _ = draw(i, bf16_only=True, prefix=False)
+    q, k, v, P = to_dev(case.q, case.k, case.v, case.P)
+    y = kata.flash_forward(q, k, v, P, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr = O.forward_quadratic(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy())
+    e = slice_rel(y.cpu().numpy(), yr)
+    print(f"[draw {i}: B={case.B} H={case.H} T={case.T}] flash y {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_delta_recurrent(i):
+    """The token-recurrent DeltaKATA forward, from the state the oracle's recurrence
+    leaves after draw i's prefix (none without one): y and the final state."""
+    case, pre, _ = draw(i)
+    Ph = case.P.double().numpy()
+    beta = I.make_beta(case.B, case.H, case.T, seed=100 + i)
+    S0 = None
+    if pre is not None:
+        b0 = I.make_beta(case.B, case.H, pre.T, seed=200 + i)
+        _, S0n = O.delta_recurrence(host64(pre.q), host64(pre.k), host64(pre.v), Ph, b0.double().numpy())
+        S0 = torch.from_numpy(S0n).float()
+    q, k, v, P = to_dev(case.q, case.k, case.v, case.P)
+    y, ST = kata.forward_delta(q, k, v, P, beta.to(DEV), S0=None if S0 is None else S0.to(DEV), return_state=True,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), Ph, beta.double().numpy(),
+                                None if S0 is None else S0.double().numpy())
+    yg = y.double().cpu().numpy()
+    if case.T == 1 and S0 is None:   # one squared cosine: absolute error on the scale beta |v|
+        scale = np.linalg.norm(beta.double().numpy()[..., None] * host64(case.v), axis=-1)
+        ey = float(np.max(np.linalg.norm(yg - yr, axis=-1) / scale))
+    else:
+        ey = slice_rel(yg, yr)
+    eS = slice_rel(ST.cpu().numpy(), Sr)
+    print(f"[draw {i}: B={case.B} H={case.H} T={case.T} d={case.d} {case.dtype} "
+          f"prefix={0 if pre is None else pre.T}] delta recurrent y {ey:.2e} S {eS:.2e}", flush=True)
+    tol = TOL[case.dtype]
+    assert ey <= tol and eS <= tol
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(NDRAWS))
+def test_random_canonical_decode(i):
+    """Two KATA and two DeltaKATA decode steps on the canonical 256-row state, from prefix
+    states built by the oracle: y and the state after the steps."""
+    case, N, H, pre, step = decode_draw(i)
+    Ph = case.P.double().numpy()
+    Sr, zr = O.final_state(host64(pre.k), host64(pre.v), Ph)
+    b0 = I.make_beta(N, H, pre.T, seed=300 + i)
+    _, Dr = O.delta_recurrence(host64(pre.q), host64(pre.k), host64(pre.v), Ph, b0.double().numpy())
+    S, z, D = (torch.from_numpy(x).float().to(DEV) for x in (Sr, zr, Dr))
+    Sr, zr, Dr = S.double().cpu().numpy(), z.double().cpu().numpy(), D.double().cpu().numpy()
+    betas = I.make_beta(2, N, H, seed=400 + i)
+    for s in range(2):
+        qs, ks, vs = (x[:, :, s].contiguous() for x in (step.q, step.k, step.v))
+        qd, kd, vd, Pd = to_dev(qs, ks, vs, case.P)
+        y = kata.decode_step(S, z, qd, kd, vd, Pd)
+        yd = kata.decode_step_delta(D, qd, kd, vd, Pd, betas[s].to(DEV))
+        torch.cuda.synchronize()
+        yr, Sr, zr = O.decode_reference(Sr, zr, host64(qs), host64(ks), host64(vs), Ph)
+        ydr, Dr = O.delta_decode_reference(Dr, host64(qs), host64(ks), host64(vs), Ph, betas[s].double().numpy())
+        ey, ed = slice_rel(y.cpu().numpy()[None], yr[None]), slice_rel(yd.cpu().numpy()[None], ydr[None])
+        print(f"[draw {i}: N={N} H={H} d={case.d} prefix={pre.T} step {s}] y {ey:.2e} delta y {ed:.2e}", flush=True)
+        assert ey <= TOL["bf16"] and ed <= TOL["bf16"]
+    eS, ez, eD = slice_rel(S.cpu().numpy(), Sr), slice_rel(z.cpu().numpy(), zr), slice_rel(D.cpu().numpy(), Dr)
+    print(f"[draw {i}] state S {eS:.2e} z {ez:.2e} delta S {eD:.2e}", flush=True)
+    assert eS <= TOL["f32"] and ez <= TOL["f32"] and eD <= TOL["f32"]

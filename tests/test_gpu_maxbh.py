@@ -1,0 +1,136 @@
+"""Every d = 64 path at the largest batch x heads its grid takes (65535 sequences; the
+concatenated factors' g state rows per sequence count against the same limit), T = 70
+(a full 64-token chunk and a ragged one), bf16 inputs.
+
+The leaf states, the backward's workspace (about 5.5 GB here) and the token streams run
+far past 2^31 bytes, so every offset into them must be 64-bit.  Sampled sequences (the
+first, the last and random ones) are checked against the oracle; samples whose gate is
+ill-conditioned (some query's den_t below 1e-2 of sum_s |u_t|^2 |w_s|^2, where bf16
+rounding decides y on any path) are passed over on the host before the GPU runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kernelized_linear_attention_kata_amd as kata
+from kernelized_linear_attention_kata_amd import inputs as I
+from oracle import kata_oracle as O
+from tests.test_gpu_random import MIN_RATIO, host64, slice_rel
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BH, T = 65535, 70
+TOL = 2e-2
+
+
+def ratio(q, k, Pq, Pk, pairs, C=None):
+    """min over queries with two or more keys of den_t / sum |u_t|^2 |w_s|^2 for one
+    sequence (q, k [T, d]), with query and key projections Pq[i], Pk[j] over the factor
+    pairs (i, j) the path sums and causal weights C [T, T] (ones if None)."""
+    n = q.shape[0]
+    C = np.tril(np.ones((n, n)) if C is None else C)
+    den = np.zeros(n)
+    scale = np.zeros(n)
+    for i, j in pairs:
+        U, W = q @ Pq[i].T, k @ Pk[j].T
+        den += (C * (U @ W.T) ** 2).sum(1)
+        scale += (C * np.outer((U * U).sum(1), (W * W).sum(1))).sum(1)
+    live = np.arange(n) >= 1
+    return float(np.min(den[live] / np.maximum(scale[live], 1e-300)))
+
+
+def pick(case, b_list, ok, count=8):
+    """The first ``count`` candidate sequences whose gate passes ``ok`` (host only)."""
+    out = []
+    for b in b_list:
+        if b not in out and ok(host64(case.q[b:b + 1])[0, 0], host64(case.k[b:b + 1])[0, 0], b):
+            out.append(b)
+        if len(out) == count:
+            return out
+    raise AssertionError("too few well-conditioned samples")
+
+
+@pytest.fixture(scope="module")
+def big():
+    case = I.make_forward("mid", B=BH, H=1, T=T, seed=150)
+    gy = I.make_output_grad(BH, 1, T, 64, seed=150)
+    rng = np.random.default_rng(150)
+    cand = [0, BH - 1, BH // 2 - 1] + [int(x) for x in rng.integers(0, BH, 60)]
+    P = case.P.double().numpy()
+    plain = pick(case, cand, lambda q, k, b: ratio(q, k, P, P, [(0, 0)]) >= MIN_RATIO)
+    dev = tuple(t.to(DEV) for t in (case.q, case.k, case.v, case.P, gy))
+    return case, gy, cand, plain, dev
+
+
+def seq(case, b):
+    return (host64(case.q[b:b + 1]), host64(case.k[b:b + 1]), host64(case.v[b:b + 1]), case.P.double().numpy())
+
+
+def test_decay_at_the_largest_batch(big):
+    case, _, cand, _, (q, k, v, P, _) = big
+    lam = I.make_log_decay(BH, 1, T, seed=151)
+    Ph = case.P.double().numpy()
+
+    def decayed(qh, kh, b):
+        L = np.cumsum(lam[b, 0].double().numpy())
+        return ratio(qh, kh, Ph, Ph, [(0, 0)], np.exp(np.minimum(L[:, None] - L[None, :], 0.0))) >= MIN_RATIO
+    samples = pick(case, cand, decayed)
+    y = kata.forward_decay(q, k, v, P, lam.to(DEV), 64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in samples:
+        qh, kh, vh, Ph = seq(case, b)
+        e = slice_rel(y[b:b + 1].cpu().numpy(), O.forward_decay_quadratic(qh, kh, vh, Ph, lam[b:b + 1].double().numpy()))
+        print(f"[decay BH={BH} seq {b}] y {e:.2e}", flush=True)
+        assert e <= TOL
+
+
+def test_flash_at_the_largest_batch(big):
+    case, _, _, samples, (q, k, v, P, _) = big
+    y = kata.flash_forward(q, k, v, P, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in samples:
+        e = slice_rel(y[b:b + 1].cpu().numpy(), O.forward_quadratic(*seq(case, b)))
+        print(f"[flash BH={BH} seq {b}] y {e:.2e}", flush=True)
+        assert e <= TOL
+
+
+def test_backward_at_the_largest_batch(big):
+    case, gy, _, samples, (q, k, v, P, gyd) = big
+    dq, dk, dv, _ = kata.backward(q, k, v, P, gyd, 64)
+    torch.cuda.synchronize()
+    for b in samples:
+        ref = O.backward_quadratic(*seq(case, b), host64(gy[b:b + 1]))
+        errs = [slice_rel(g[b:b + 1].float().cpu().numpy(), r) for g, r in zip((dq, dk, dv), ref[:3])]
+        print(f"[backward BH={BH} seq {b}] dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}", flush=True)
+        assert max(errs) <= TOL
+
+
+def test_delta_chunked_at_the_largest_batch(big):
+    case, _, _, samples, (q, k, v, P, _) = big
+    beta = I.make_beta(BH, 1, T, seed=152)
+    y = kata.forward_delta_chunked(q, k, v, P, beta.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in samples:
+        yr, _ = O.delta_recurrence(*seq(case, b), beta[b:b + 1].double().numpy())
+        e = slice_rel(y[b:b + 1].cpu().numpy(), yr)
+        print(f"[delta chunked BH={BH} seq {b}] y {e:.2e}", flush=True)
+        assert e <= 5e-3
+
+
+@pytest.mark.parametrize("mode", ["concat", "sum"])
+def test_factors_at_the_largest_batch(big, mode):
+    """g = 2 over 32767 sequences: 65534 factor state rows for the concatenated form."""
+    case, _, cand, _, (q, k, v, _, _) = big
+    n = BH // 2
+    Pg = I.make_factor_projections(1, 2, 64, seed=153)
+    Pf = Pg[0].double().numpy()
+    pairs = [(0, 0), (1, 1)] if mode == "concat" else [(0, 0), (0, 1), (1, 0), (1, 1)]
+    samples = pick(case, [b for b in cand if b < n], lambda qh, kh, b: ratio(qh, kh, Pf, Pf, pairs) >= MIN_RATIO)
+    y = kata.forward_factors(q[:n], k[:n], v[:n], Pg.to(DEV), mode, 64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    fn = O.forward_mg_quadratic if mode == "concat" else O.forward_sg_quadratic
+    for b in samples:
+        qh, kh, vh, _ = seq(case, b)
+        e = slice_rel(y[b:b + 1].cpu().numpy(), fn(qh, kh, vh, Pg.double().numpy()))
+        print(f"[factors {mode} BH={n} seq {b}] y {e:.2e}", flush=True)
+        assert e <= TOL

@@ -190,10 +190,27 @@ def test_random_decay_factors_backward(i):
         ef[mode] = slice_rel(yf.cpu().numpy(), fn(qh, kh, vh, Pg.double().numpy()))
 
     gy = I.make_output_grad(case.B, case.H, case.T, 64, seed=i)
-    dq, dk, dv, _ = kata.backward(q, k, v, P, gy.to(DEV), 64, S0=S0d, z0=z0d)
-    torch.cuda.synchronize()
-    rq, rk, rv = O.backward_quadratic(qh, kh, vh, Ph, host64(gy), S0h, z0h)[:3]
-    eg = {"dv": slice_rel(dv.float().cpu().numpy(), rv)}
+    if pre is None:
+        dq, dk, dv, _ = kata.backward(q, k, v, P, gy.to(DEV), 64)
+        torch.cuda.synchronize()
+        rq, rk, rv = O.backward_quadratic(qh, kh, vh, Ph, host64(gy))[:3]
+        eg = {}
+    else:   # from a prefix state, with a gradient of the final state too
+        gST, gzT = I.make_state_grad(case.B, case.H, 64, seed=i)
+        dq, dk, dv, _, dS0, dz0 = kata.backward(q, k, v, P, gy.to(DEV), 64, S0=S0d, z0=z0d, gST=gST.to(DEV),
+                                                gzT=gzT.to(DEV), return_state_grad=True)
+        torch.cuda.synchronize()
+        ref = O.backward_quadratic(qh, kh, vh, Ph, host64(gy), S0h, z0h, gST.double().numpy(), gzT.double().numpy())
+        rq, rk, rv = ref[:3]
+        # the state enters through a symmetric feature, so only the symmetric part of the
+        # oracle's state gradient is defined by the path's outputs
+        rS = ref[4].reshape(case.B, case.H, 16, 16, 64)
+        rz = ref[5].reshape(case.B, case.H, 16, 16)
+        symS = 0.5 * (rS + rS.transpose(0, 1, 3, 2, 4))
+        symz = 0.5 * (rz + rz.transpose(0, 1, 3, 2))
+        eg = {"dS0": slice_rel(dS0.double().cpu().numpy().reshape(symS.shape), symS),
+              "dz0": slice_rel(dz0.double().cpu().numpy().reshape(symz.shape), symz)}
+    eg["dv"] = slice_rel(dv.float().cpu().numpy(), rv)
     if case.T + (0 if pre is None else pre.T) > 1:   # one token: y = v for any q, k, so dq = dk = 0
         eg["dq"] = slice_rel(dq.float().cpu().numpy(), rq)
         eg["dk"] = slice_rel(dk.float().cpu().numpy(), rk)

@@ -3,7 +3,8 @@ chunk size and an initial state carried over from a prefix, each path against th
 oracle at the bars of the fixed-shape tests.
 
 Per draw: the chunked forward (y and the final state), the decay-gated forward, both
-factor modes, the backward and the flash forward (bf16, d = 64, C = 64, the shapes those
+factor modes, the backward (with a final-state gradient and the initial state's gradient
+on draws with a prefix) and the flash forward (bf16, d = 64, C = 64, the shapes those
 paths take), the chunked and the token-recurrent DeltaKATA forward, and two decode
 steps (KATA and DeltaKATA on the canonical state, KATA on the packed one) from states
 the oracle builds over a prefix.

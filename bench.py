@@ -32,6 +32,8 @@ stamps one.
     python bench.py --decode --packed  # the decode step on the packed symmetric state (136 rows)
     python bench.py --delta      # the DeltaKATA forward, chunked form, on the long-context workload
     python bench.py --factors 2  # KATA-M2 (two concatenated PSD factors) on the long-context workload
+    python bench.py --workload mid     # the forward on the mid workload (B=4 H=8 T=4096), warm and flushed
+    python bench.py --workload lm340m  # the forward on the 340M-layer workload (B=8 H=16 T=2048)
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads
@@ -135,7 +137,7 @@ PATH_HEADERS = {"decay": ("kata_chunk.h",), "backward": ("kata_bwd.h",), "flash"
 
 
 def path_hash(mode: str) -> str:
-    if mode == "forward":
+    if mode in ("forward", "forward_precise", "mid", "lm340m"):
         return source_hash()
     if mode.startswith(("m", "sigma")):
         return source_hash(("kata_chunk.h",))
@@ -651,6 +653,144 @@ BWD_KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_bwd_query", "kata_bw
                "kata_bwd_key", "kata_bwd_dp_reduce")
 
 
+WORKLOAD_METRIC = "KATA causal fwd tokens/sec, {what} (1 GPU)"
+WORKLOAD_WHAT = {
+    "mid": "mid workload B=4 H=8 T=4096 d=dv=64 p=16 bf16, chunk 64, + % of HBM peak",
+    "lm340m": ("340M-LM-shaped attention layer B=8 H=16 T=2048 d=dv=64 p=16 bf16 (per-head P, unit keys), "
+               "chunk 64, + % of HBM peak"),
+}
+FLUSH_BYTES = 512 << 20
+
+
+def bench_workload(args):
+    """The chunked forward on the mid or the 340M-layer workload.  Their inputs and leaf
+    states (about 80 MB and 130 MB per step) fit in the 256 MB last-level cache, so each is
+    timed twice: warm (one batch repeated, everything cache-resident) and flushed (a 512 MB
+    read-modify-write of a scratch tensor before every step, so the step starts from HBM).
+    Each flushed step is timed from the start of its first kernel to the end of its last
+    (events the launches stamp), which leaves the flush out.  value and roofline are the
+    flushed ones; the warm figures come beside them."""
+    import torch
+    import kernelized_linear_attention_kata_amd as kata
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nb = max(1, args.batches)
+    seed0 = I.WORKLOADS[args.workload]["seed"]
+    cases = [I.make_forward(args.workload, device=dev, seed=seed0 + b) for b in range(nb)]
+    case = cases[0]
+    B, H, T, d, dv, C = case.B, case.H, case.T, case.d, case.dv, 64
+    ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    ST = torch.empty((B, H, 256, dv), dtype=torch.float32, device=dev)
+    zT = torch.empty((B, H, 256), dtype=torch.float32, device=dev)
+    n_leaf = ws_bytes // (B * H * (144 * dv + 256) * 4)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None, c=None):
+        c = cases[i % nb] if c is None else c
+        kata.forward(c.q, c.k, c.v, c.P, chunk=C, y=ys[i % nb], workspace=ws, ST=ST, zT=zT, return_state=True,
+                     stream=stream, events=events)
+
+    settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - settle0 < args.settle_s:
+        for _ in range(8):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # warm: one batch repeated
+    warm_step = lambda i, events=None: step(0, events)
+    warm_kernels = kernel_breakdown(torch, warm_step, stream, args.steps, KERNELS)
+    warm_ms, wall_warm, _ = time_steps(torch, warm_step, stream, args.steps, len(KERNELS) + 1, ())
+
+    # flushed: every step after a 512 MB read-modify-write, all launches stamped
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    for es in evs:
+        for e in es:
+            e.record(stream)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.add_(1.0)
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    flushed_ms = mean_interval(evs, 0, len(KERNELS))
+    flushed_kernels = {name: mean_interval(evs, j, j + 1) for j, name in enumerate(KERNELS)}
+    dominant = max(flushed_kernels, key=flushed_kernels.get)
+
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2)
+    aflops = algorithmic_flops(B, H, T, d, dv, C)
+    kernels = {}
+    for name in KERNELS:
+        ms, wms = flushed_kernels[name], warm_kernels[name]
+        kernels[name] = {"ms": round(ms, 4), "ms_warm": round(wms, 4),
+                         "alg_GBps": round(abytes[name] / (ms / 1e3) / 1e9, 1),
+                         "hbm_frac": round(abytes[name] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_TFLOPs": round(aflops[name] / (ms / 1e3) / 1e12, 2),
+                         "mfma_frac": round(aflops[name] / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "alg_bytes": abytes[name], "alg_flops": aflops[name]}
+    achieved = abytes[dominant] / (flushed_kernels[dominant] / 1e3) / 1e9
+    mode = args.workload
+    result = {
+        "metric": WORKLOAD_METRIC.format(what=WORKLOAD_WHAT[args.workload]),
+        "value": B * T / (flushed_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": flushed_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": (f"synthetic ({nb} distinct seeded batches cycled in the flushed steps; one batch in the warm "
+                 "steps)"),
+        "config": {"workload": (f"{args.workload} KATA forward: B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, "
+                                f"fp32 P/state, chunk {C}, assoc scan over {n_leaf} leaf states per sequence; "
+                                "each step after a 512 MB cache flush (warm: no flush, one batch)"),
+                   "global_batch": B, "seq_len": T, "heads": H, "chunk": C, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": mode_traffic(mode, dominant)},
+        "warm": {"value": B * T / (warm_ms / 1e3), "ms_per_step": warm_ms,
+                 "dominant_GBps": round(abytes[dominant] / (warm_kernels[dominant] / 1e3) / 1e9, 1)},
+        "kernels": kernels,
+        "mode": mode, "source_hash": path_hash(mode),
+        "wall_s_timed": round(wall + wall_warm, 4),
+    }
+    if not args.no_cpu_baseline:
+        cb = full_cpu_baseline(case)
+        result["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(result), flush=True)
+
+
+def full_cpu_baseline(case):
+    """The fp64 O(T^2) oracle over the whole workload (every row of every head)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as O
+    from kernelized_linear_attention_kata_amd import inputs as I
+
+    q, k, v = (O.bf16_bits_to_f64(I.bf16_bits(t)) for t in (case.q, case.k, case.v))
+    P = case.P.double().cpu().numpy()
+    t0 = time.perf_counter()
+    O.forward_quadratic(q, k, v, P)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": case.B * case.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 O(T^2) oracle over the whole workload ({case.B} x {case.H} sequences of {case.T} "
+                      f"tokens), {dt:.1f} s"}
+
+
 def bwd_algorithmic_bytes(B, H, T, d, dv, n_leaf, gy_bytes):
     """Bytes each backward kernel must move per launch under the byte model of the path:
     its token streams (bf16 q, k, v, dq, dk, dv; gy; the (1/den, h) f32 pair per token
@@ -777,8 +917,12 @@ def main():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup (clock ramp of an idle GPU)")
     ap.add_argument("--chunk", type=int, default=64, choices=(32, 64, 128))
+    ap.add_argument("--workload", default="long", choices=("long", "mid", "lm340m"),
+                    help="the chunked forward on the mid or the 340M-layer workload instead (warm and flushed)")
     ap.add_argument("--leaf", type=int, default=0, help="chunks per scan leaf (0 = library default)")
     ap.add_argument("--scan", default="assoc", choices=("assoc", "sequential"))
+    ap.add_argument("--precise", action="store_true",
+                    help="the KATA_BF16_HILO compute type (hi/lo feature and state operands)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=16)
     ap.add_argument("--decode", action="store_true", help="time the recurrent decode step instead")
@@ -830,6 +974,9 @@ def main():
     if args.backward:
         bench_backward(args)
         return
+    if args.workload != "long":
+        bench_workload(args)
+        return
 
     import torch
     import kernelized_linear_attention_kata_amd as kata
@@ -842,8 +989,12 @@ def main():
     cases = [I.make_forward("long", device=dev, chunk=args.chunk, seed=seed0 + b) for b in range(nb)]
     case = cases[0]
     B, H, T, d, dv, C = case.B, case.H, case.T, case.d, case.dv, args.chunk
-    ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf)
+    ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf,
+                                            precise=args.precise)
     G = args.factors
+    if args.precise and (args.decay or G > 1):
+        print("bench.py --precise applies to the plain forward", file=sys.stderr)
+        sys.exit(2)
     if (args.decay or G > 1) and C != 64:
         print("bench.py --decay / --factors support chunk 64 only", file=sys.stderr)
         sys.exit(2)
@@ -876,7 +1027,7 @@ def main():
                                return_state=False, scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events)
             return
         kata.forward(c.q, c.k, c.v, c.P, chunk=C, y=ys[i % nb], workspace=ws, ST=ST, zT=zT, return_state=True,
-                     scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events)
+                     scan=args.scan, scan_leaf=args.leaf, stream=stream, events=events, precise=args.precise)
 
     settle0 = time.perf_counter()
     n_settle = 0
@@ -916,10 +1067,13 @@ def main():
     kernels[dominant]["ms_timed_steps"] = round(dom_ms, 4)
     achieved = abytes[dominant] / (dom_ms / 1e3) / 1e9
     traffic = None
-    mode = (f"{'sigma' if sg else 'm'}{G}" if G > 1 else ("decay" if args.decay else "forward"))
+    mode = (f"{'sigma' if sg else 'm'}{G}" if G > 1
+            else ("decay" if args.decay else ("forward_precise" if args.precise else "forward")))
     src = path_hash(mode)
     if mode != "forward":
         traffic = mode_traffic(mode, dominant) if C == 64 else None
+        if mode == "forward_precise":
+            traffic = None
     elif os.path.exists(COUNTERS_FILE):
         try:
             cnt = json.load(open(COUNTERS_FILE))
@@ -944,6 +1098,7 @@ def main():
         "dtype": "bf16",
         "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
         "config": {"workload": (f"long-context KATA{(f'-Sigma{G}' if sg else f'-M{G}') if G > 1 else ''} forward"
+                                f"{' (KATA_BF16_HILO: hi/lo feature and state operands)' if args.precise else ''}"
                                 f"{' with decay gates in [0.9, 1] (fp32 log-gates)' if args.decay else ''}"
                                 f"{fac_note}: "
                                 f"B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, fp32 P/state, chunk {C}, "

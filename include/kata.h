@@ -35,10 +35,17 @@
  *    calls and are safe to call from several host threads.
  *  - State layout ("canonical"): S [.., p*p, dv] and z [.., p*p] float32 with
  *    feature index i*p + j, i.e. S holds sum phi(k) v^T with phi = vec(w w^T).
- *    The state is symmetric in (i, j); where the library READS a caller state
- *    (S0/z0) it reads the entries with i <= j and takes the mirror entries as equal.
+ *    phi(k) = vec(w w^T) is symmetric, and so is every state built from it.  Every entry
+ *    point reads a caller's state through its symmetric part: the mean of the mirror
+ *    entries (i, j) and (j, i), which is the entry itself, bit for bit, for the states
+ *    this library produces.  kata_forward, kata_forward_decay and kata_forward_factors
+ *    export ST, zT as that symmetric part plus the tokens' contribution (for T = 0: the
+ *    symmetric part of S0, z0).  The decode steps and the DeltaKATA entry points add
+ *    their symmetric updates to the caller's state, so an antisymmetric part a caller
+ *    puts in passes through them unchanged and never reaches y.
  *  - Supported in this version: p = 16; (d, dv) = (16, 16) or (64, 64);
- *    chunk in {32, 64, 128}; in_dtype F32 or BF16; any T >= 0 (a ragged last
+ *    chunk in {32, 64, 128}; in_dtype F32 or BF16 (kata_forward also BF16_HILO);
+ *    out_dtype F32 or BF16; any T >= 0 (a ragged last
  *    chunk is handled); B*H <= 65535.  Other values return KATA_ERR_UNSUPPORTED.
  */
 #ifndef KATA_H
@@ -62,14 +69,40 @@ typedef enum {
   KATA_ERR_LAUNCH = 5        /* a kernel launch failed                          */
 } kata_status;
 
-typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype;
+/* Storage (and compute) type of tensors.
+ *  KATA_F32, KATA_BF16: float32 / bfloat16 storage.  With float32 q, k, v every matrix-core
+ *    operand is a hi/lo pair of bf16 (about 16 significant bits).  With bfloat16 q, k, v the
+ *    projections u = Pq, w = Pk enter the score tiles as hi/lo pairs and the features
+ *    phi(k), phi(q) and the published state H are single bf16 (8 significant bits).
+ *  KATA_BF16_HILO (in_dtype of kata_forward only): bfloat16
+ *    storage like KATA_BF16, but phi(k), phi(q) and H also enter the matrix cores as hi/lo
+ *    pairs.  For output gates that are far from well conditioned while keys are read
+ *    through a state: where den_t = sum_s (u_t.w_s)^2 is a small fraction of
+ *    sum_s |u_t|^2 |w_s|^2 (a query nearly orthogonal to keys of earlier chunks or of the
+ *    initial state), the single-bf16 readout phi(q_t)^T H loses y_t to rounding, while
+ *    this mode keeps it to the bf16 bar for fractions down to about 1e-3.  It takes about
+ *    1.45x the time of KATA_BF16 on the long-context shape (twice the state LDS, so two
+ *    workgroups per compute unit instead of three, and three matrix-core products per
+ *    readout and two per state update instead of one).  Other entry points reject it. */
+typedef enum { KATA_F32 = 0, KATA_BF16 = 1, KATA_BF16_HILO = 2 } kata_dtype;
 
-/* How the inter-chunk state prefix is formed.
- *  KATA_SCAN_ASSOC: chunk states are summed over leaves of `scan_leaf` chunks,
- *    the leaf sums are combined by a log-depth (wavefront shuffle + LDS)
- *    associative prefix, and each chunk's prefix inside a leaf is completed by a
- *    running sum kept on chip ([TS-2.3], [ABS]: associative scan over chunk
- *    states, depth O(log(T/C))).  scan_leaf = 1 materialises every chunk state.
+/* How the inter-chunk state prefix is formed ([TS-2.3], [ABS]: an associative scan over
+ * the chunk states replaces the chunk-after-chunk recurrence; the combine is +).
+ *  KATA_SCAN_ASSOC: a reduce-then-scan.  The chunks are grouped into leaves of L =
+ *    `scan_leaf` consecutive chunks (0: chosen by the library so the leaves fill the GPU
+ *    in whole rounds, e.g. L = 43, 48 leaves per sequence, at T = 131072, C = 64).
+ *    (1) Every leaf's chunk states are summed, all leaves in parallel.  (2) The leaf sums
+ *    get an exclusive prefix: each thread keeps up to 16 consecutive leaf rows of one
+ *    16-byte column quad in registers and sums them in order, the totals of up to 16
+ *    such segments are combined through LDS, and sequences of more than 256 leaves take
+ *    several such passes chained by a carry.  (3) Inside each leaf, the pass that forms
+ *    the outputs completes every chunk's prefix with a running sum kept on chip, walking
+ *    the leaf's chunks in order.  The sequential depth is therefore L chunk steps inside a
+ *    leaf plus at most 16 + 16 combine steps per 256 leaves: O(L + n_leaf / 16), not a
+ *    log-depth tree; with the library's choice of L it is about sqrt of the work per
+ *    GPU round.  A log-depth combine of the leaf sums measured 1.5x slower at these leaf
+ *    counts.  scan_leaf = 1 writes and scans every chunk state (the literal chunk-level
+ *    scan, depth 16 per pass plus the segment combine).
  *  KATA_SCAN_SEQUENTIAL: one leaf per sequence - the chunk states are propagated
  *    strictly chunk after chunk (depth O(T/C)), the matched sequential baseline
  *    the pages compare the scan against ([ABS]). */
@@ -147,8 +180,9 @@ kata_status kata_forward_timed(const kata_forward_desc* desc,
  * formed or returned.  Supported: p = 16, d = dv = 64, in_dtype BF16, out_dtype F32 or
  * BF16; desc->chunk, scan and scan_leaf are ignored.  q, k [B,H,T,64], v [B,H,T,64]
  * bf16, P [H,16,64] f32, y [B,H,T,64] out_dtype, all device memory owned by the caller.
- * The workspace (kata_flash_workspace_bytes: 192 bytes per token and head, T rounded
- * up to 256) holds the projected u and w (bf16) and V in MFMA operand order.
+ * The workspace (kata_flash_workspace_bytes: 256 bytes per token and head, T rounded
+ * up to 256) holds the projected u and w (each as a hi/lo pair of bf16, so the squared
+ * scores keep about 16 significant bits) and V in MFMA operand order.
  * events: NULL, or three caller-created hipEvent_t (timing enabled) stamped with the
  * start of the projection kernel, the start of the attention kernel and its end.
  * Errors are returned before anything is enqueued; B*H == 0 or T == 0 is a no-op. */

@@ -16,7 +16,7 @@ import torch
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 
 KATA_OK, KATA_ERR_NULL, KATA_ERR_SHAPE, KATA_ERR_UNSUPPORTED, KATA_ERR_WORKSPACE, KATA_ERR_LAUNCH = range(6)
-KATA_F32, KATA_BF16 = 0, 1
+KATA_F32, KATA_BF16, KATA_BF16_HILO = 0, 1, 2
 KATA_SCAN_ASSOC, KATA_SCAN_SEQUENTIAL = 0, 1
 FEATURE_LAYOUTS = {"full": 0, "packed_key": 1, "packed_query": 2}
 ABI_VERSION = 1
@@ -189,10 +189,20 @@ def make_desc(B, H, T, d, dv, chunk, in_dtype, out_dtype, scan="assoc", scan_lea
                        scan_leaf=scan_leaf)
 
 
+def _in_code(dtype: torch.dtype, precise: bool) -> int:
+    """in_dtype code of q, k, v; precise (bf16 only) selects KATA_BF16_HILO."""
+    code = _dtype_code(dtype)
+    if precise:
+        if code != KATA_BF16:
+            raise KataError(KATA_ERR_UNSUPPORTED, "precise=True applies to bfloat16 inputs")
+        return KATA_BF16_HILO
+    return code
+
+
 def forward_workspace_bytes(B, H, T, d, dv, chunk, in_dtype=torch.bfloat16, out_dtype=None,
-                            scan="assoc", scan_leaf=0) -> int:
+                            scan="assoc", scan_leaf=0, precise=False) -> int:
     out_dtype = in_dtype if out_dtype is None else out_dtype
-    desc = make_desc(B, H, T, d, dv, chunk, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    desc = make_desc(B, H, T, d, dv, chunk, _in_code(in_dtype, precise), _dtype_code(out_dtype), scan, scan_leaf)
     n = ctypes.c_size_t(0)
     _check(_lib().kata_forward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_forward_workspace_bytes")
     return int(n.value)
@@ -220,8 +230,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
             out_dtype: Optional[torch.dtype] = None, return_state: bool = False, scan: str = "assoc",
             scan_leaf: int = 0, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             ST: Optional[torch.Tensor] = None, zT: Optional[torch.Tensor] = None, stream=None,
-            events=None):
+            events=None, precise: bool = False):
     """KATA causal forward (kata_forward).  q, k: [B,H,T,d]; v: [B,H,T,dv]; P: [H,16,d] fp32.
+
+    precise (bf16 q, k, v): the KATA_BF16_HILO compute type, hi/lo feature and state
+    operands for ill-conditioned output gates (about 1.45x the time).
 
     Returns y [B,H,T,dv] (out_dtype, default q's dtype), or (y, ST, zT) with the final
     state when return_state.  Outputs and the workspace may be passed in preallocated.
@@ -237,7 +250,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
     _need(v, "v", (B, H, T, dv), q.dtype, dev)
     _need(P, "P", (H, P_DIM, d), torch.float32, dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    ic, oc = _dtype_code(q.dtype), _dtype_code(out_dtype)
+    ic, oc = _in_code(q.dtype, precise), _dtype_code(out_dtype)
     if (S0 is None) != (z0 is None):
         raise ValueError("S0 and z0 go together")
     if S0 is not None:

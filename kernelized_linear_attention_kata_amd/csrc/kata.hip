@@ -11,6 +11,7 @@
 #include <hip/hip_ext.h>
 
 #include <cstdlib>
+#include <cstring>
 
 #include "../../include/kata.h"
 #include "kata_bwd.h"
@@ -32,8 +33,25 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-kata_status check_dtype(kata_dtype t) {
-  return (t == KATA_F32 || t == KATA_BF16) ? KATA_OK : KATA_ERR_UNSUPPORTED;
+// The enum arguments come from C callers, who may pass any int.  Loading an out-of-range
+// value as the C++ enum type is undefined, so arguments are validated from their bits
+// (read as an int, never as the enum) before any other use.
+template <typename E>
+int bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+kata_status check_dtype(const kata_dtype& t) {
+  const int v = bits(t);
+  return (v == KATA_F32 || v == KATA_BF16) ? KATA_OK : KATA_ERR_UNSUPPORTED;
+}
+
+bool valid_mode(const kata_factor_mode& m) {
+  const int v = bits(m);
+  return v == KATA_FACTORS_CONCAT || v == KATA_FACTORS_SUM;
 }
 
 kata_status validate(const kata_forward_desc* d) {
@@ -48,8 +66,10 @@ kata_status validate(const kata_forward_desc* d) {
   if (d->p != P_DIM) return KATA_ERR_UNSUPPORTED;
   if (!((d->d == 16 && d->dv == 16) || (d->d == 64 && d->dv == 64))) return KATA_ERR_UNSUPPORTED;
   if (!(d->chunk == 32 || d->chunk == 64 || d->chunk == 128)) return KATA_ERR_UNSUPPORTED;
-  if (check_dtype(d->in_dtype) != KATA_OK || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
-  if (d->scan != KATA_SCAN_ASSOC && d->scan != KATA_SCAN_SEQUENTIAL) return KATA_ERR_UNSUPPORTED;
+  if ((check_dtype(d->in_dtype) != KATA_OK && bits(d->in_dtype) != KATA_BF16_HILO) ||
+      check_dtype(d->out_dtype) != KATA_OK)
+    return KATA_ERR_UNSUPPORTED;
+  if (bits(d->scan) != KATA_SCAN_ASSOC && bits(d->scan) != KATA_SCAN_SEQUENTIAL) return KATA_ERR_UNSUPPORTED;
   return KATA_OK;
 }
 
@@ -61,9 +81,9 @@ kata_status validate(const kata_forward_desc* d) {
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kLdsPerCU = 156 * 1024;
 
-template <int C, int DV, bool SPLIT>
+template <int C, int DV, bool SPLIT, bool PREC = false>
 int64_t intra_slots() {
-  using S = Shape<C, DV, DV, SPLIT>;
+  using S = Shape<C, DV, DV, SPLIT, PREC>;
   const int64_t by_lds = kLdsPerCU / S::SMEM;
   const int64_t per_cu = by_lds < S::OCC_INTRA ? by_lds : S::OCC_INTRA;
   return kComputeUnits * (per_cu < 1 ? 1 : per_cu);
@@ -71,6 +91,13 @@ int64_t intra_slots() {
 
 int64_t slots_for(const kata_forward_desc* d) {
   const bool split = d->in_dtype == KATA_F32;
+  if (d->in_dtype == KATA_BF16_HILO) {
+    if (d->dv == 16)
+      return d->chunk == 32 ? intra_slots<32, 16, false, true>()
+                            : (d->chunk == 64 ? intra_slots<64, 16, false, true>() : intra_slots<128, 16, false, true>());
+    return d->chunk == 32 ? intra_slots<32, 64, false, true>()
+                          : (d->chunk == 64 ? intra_slots<64, 64, false, true>() : intra_slots<128, 64, false, true>());
+  }
   if (d->dv == 16) {
     if (d->chunk == 32) return split ? intra_slots<32, 16, true>() : intra_slots<32, 16, false>();
     if (d->chunk == 64) return split ? intra_slots<64, 16, true>() : intra_slots<64, 16, false>();
@@ -139,6 +166,26 @@ __global__ void kata_copy_or_zero(float* __restrict__ dst, const float* __restri
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// dst = the symmetric part of a state (or of a state gradient) src [n_blocks, p*p, cols]:
+// entry (i, j, c) is the mean of src's entries (i, j, c) and (j, i, c), 0 when src is NULL.
+// A symmetric src is copied bit for bit (0.5 * (x + x) = x).  This is how every entry point
+// reads a caller's state, so the state exported for zero tokens is the one a token is
+// added to.
+__global__ void kata_sym_copy_or_zero(float* __restrict__ dst, const float* __restrict__ src, int64_t n, int cols) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  if (!src) {
+    dst[e] = 0.f;
+    return;
+  }
+  const int c = (int)(e % cols);
+  const int64_t f = e / cols;
+  const int64_t blk = f / (P_DIM * P_DIM);
+  const int ij = (int)(f % (P_DIM * P_DIM));
+  const int i = ij / P_DIM, j = ij % P_DIM;
+  dst[e] = 0.5f * (src[e] + src[((blk * P_DIM + j) * P_DIM + i) * cols + c]);
+}
+
 // segments per column quad of kata_state_scan: the smallest power of two with at most
 // SCAN_ROWS leaf rows each, capped at SCAN_GMAX (more leaves take several passes)
 int scan_segments(const Plan& pl) {
@@ -174,7 +221,7 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
   const int G = scan_segments(pl);
   const dim3 sgrid = scan_grid(pl, G, bh);
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
-                        (int)S::DV, G, S0, z0, ST, zT, 0, 0, (const float*)dec);
+                        (int)S::DV, G, S0, z0, ST, zT, 0, (const float*)dec);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut, DECAY>), grid, dim3(256), smem_intra, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
@@ -192,6 +239,11 @@ kata_status dispatch_dtypes(const kata_forward_desc* d, const Plan& pl, const vo
     if (d->out_dtype == KATA_F32) return run_forward<S, float, float>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
     return run_forward<S, float, bf16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
   }
+  if (d->in_dtype == KATA_BF16_HILO) {
+    using SP = Shape<C, DIN, DV, false, true>;
+    if (d->out_dtype == KATA_F32) return run_forward<SP, bf16, float>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+    return run_forward<SP, bf16, bf16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
+  }
   using S = Shape<C, DIN, DV, false>;
   if (d->out_dtype == KATA_F32) return run_forward<S, bf16, float>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
   return run_forward<S, bf16, bf16>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
@@ -205,14 +257,16 @@ kata_status dispatch_dims(const kata_forward_desc* d, const Plan& pl, const void
   return dispatch_dtypes<C, 64, 64>(d, pl, q, k, v, P, S0, z0, y, ST, zT, ws, st, ev);
 }
 
-// The state export when there are no tokens: ST = S0 (or 0), zT = z0 (or 0).
+// The state export when there are no tokens: ST, zT = the symmetric part of S0, z0 (or 0),
+// the state as every entry point reads it.
 kata_status copy_initial_state(const kata_forward_desc* d, const float* S0, const float* z0, float* ST,
                                float* zT, hipStream_t st) {
   const int64_t nS = d->B * d->H * P_DIM * P_DIM * d->dv;
   const int64_t nz = d->B * d->H * P_DIM * P_DIM;
   if (ST) {
-    hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, ST, S0, nS);
-    hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, zT, z0, nz);
+    hipLaunchKernelGGL(kata_sym_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, ST, S0, nS,
+                       d->dv);
+    hipLaunchKernelGGL(kata_sym_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, zT, z0, nz, 1);
   }
   return launch_status();
 }
@@ -222,7 +276,10 @@ kata_status validate_flash(const kata_forward_desc* d) {
   if (!d) return KATA_ERR_NULL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d <= 0 || d->dv <= 0 || d->p <= 0) return KATA_ERR_SHAPE;
   if (d->B > 65535 || d->H > 65535 || d->B * d->H > 65535) return KATA_ERR_SHAPE;
-  if (d->T > (((int64_t)1 << 31) - 4096) / (FL_DV * 4) - 256) return KATA_ERR_SHAPE;
+  // a sequence's workspace (flash_ws_elems bf16 per padded token) and its y rows are
+  // addressed with 32-bit byte offsets
+  const int64_t per_tok = (int64_t)(4 * P_DIM + FL_DV) * 2 > FL_DV * 4 ? (4 * P_DIM + FL_DV) * 2 : FL_DV * 4;
+  if (d->T > (((int64_t)1 << 31) - 4096) / per_tok - 256) return KATA_ERR_SHAPE;
   if (d->p != P_DIM || d->d != 64 || d->dv != FL_DV) return KATA_ERR_UNSUPPORTED;
   if (d->in_dtype != KATA_BF16 || check_dtype(d->out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
   return KATA_OK;
@@ -304,7 +361,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
                         (float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[1], nullptr, 0, wsf, pl.n_leaf, (int)pl.E, 64, G,
-                        S0, z0, (float*)nullptr, (float*)nullptr, 0, 0, (const float*)nullptr);
+                        S0, z0, (float*)nullptr, (float*)nullptr, 0, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_bwd_query<TY>), grid, dim3(256), QaGy<TY>::SMEM, st, e[2], nullptr, 0, qb, kb, vb,
                         (const TY*)gy, P, (const float*)wsf, ih, (bf16*)dq, dpa, d->T,
@@ -314,7 +371,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
                         (const float*)ih, P, wsr, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[4], nullptr, 0, wsr, pl.n_leaf, (int)pl.E, 64, G,
-                        gST, gzT, dS0, dz0, 1, 1, (const float*)nullptr);
+                        gST, gzT, dS0, dz0, 1, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_bwd_key<TY>), grid, dim3(512), KB_SMEM, st, e[5], nullptr, 0, qb, kb, vb, (const TY*)gy,
                         (const float*)ih, P, (const float*)wsr, (bf16*)dk, (bf16*)dv, dpb, d->T,
@@ -378,10 +435,10 @@ int64_t slots_by_lds() {
   return kComputeUnits * (per_cu < 1 ? 1 : per_cu);
 }
 
-kata_status validate_factors(const kata_forward_desc* d, int g, kata_factor_mode mode) {
+kata_status validate_factors(const kata_forward_desc* d, int g, const kata_factor_mode& mode) {
   const kata_status s = validate(d);
   if (s != KATA_OK) return s;
-  if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
+  if (!valid_mode(mode)) return KATA_ERR_UNSUPPORTED;
   if (g < 1) return KATA_ERR_SHAPE;
   if (g == 1) return KATA_OK;
   if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
@@ -390,7 +447,7 @@ kata_status validate_factors(const kata_forward_desc* d, int g, kata_factor_mode
   return KATA_OK;
 }
 
-Plan factors_plan(const kata_forward_desc* d, int g, kata_factor_mode mode) {
+Plan factors_plan(const kata_forward_desc* d, int g, const kata_factor_mode& mode) {
   using S = Shape<64, 64, 64, false>;
   if (g <= 1) return make_plan(d);
   if (mode == KATA_FACTORS_SUM)
@@ -418,7 +475,7 @@ kata_status run_forward_mg(const kata_forward_desc* d, const Plan& pl, const voi
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int segs = scan_segments(pl);
   hipExtLaunchKernelGGL(kata_state_scan, scan_grid(pl, segs, bh * G), dim3(256), 0, st, e1, nullptr, 0, ws,
-                        pl.n_leaf, (int)pl.E, (int)S::DV, segs, S0, z0, ST, zT, 0, 0, (const float*)nullptr);
+                        pl.n_leaf, (int)pl.E, (int)S::DV, segs, S0, z0, ST, zT, 0, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_chunk_intra_mg<S, TIn, TOut, G>), dim3((unsigned)pl.n_leaf, (unsigned)bh), dim3(256),
                         smem_intra, st, e2, e3, 0, (const TIn*)q, (const TIn*)k, (const TIn*)v, P,
@@ -445,7 +502,7 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int segs = scan_segments(pl);
   hipExtLaunchKernelGGL(kata_state_scan, scan_grid(pl, segs, bh), dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf,
-                        (int)pl.E, (int)S::DV, segs, S0, z0, ST, zT, 0, 0, (const float*)nullptr);
+                        (int)pl.E, (int)S::DV, segs, S0, z0, ST, zT, 0, (const float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata_chunk_intra_sg<S, TIn, TOut, G>), grid, dim3(256), smem_intra, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
@@ -555,7 +612,8 @@ kata_status launch_decode_packed(int64_t NH, int H, int d, int dv, kata_dtype in
 }
 
 // Shared checks of the decode entry points: sizes, supported shapes and dtypes.
-kata_status validate_decode(int64_t N, int64_t H, int d, int dv, int p, kata_dtype in_dtype, kata_dtype out_dtype) {
+kata_status validate_decode(int64_t N, int64_t H, int d, int dv, int p, const kata_dtype& in_dtype,
+                            const kata_dtype& out_dtype) {
   if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0) return KATA_ERR_SHAPE;
   if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
   if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
@@ -570,7 +628,7 @@ extern "C" {
 int kata_abi_version(void) { return KATA_ABI_VERSION; }
 
 const char* kata_status_string(kata_status s) {
-  switch (s) {
+  switch (bits(s)) {
     case KATA_OK: return "KATA_OK";
     case KATA_ERR_NULL: return "KATA_ERR_NULL: a required pointer is NULL";
     case KATA_ERR_SHAPE: return "KATA_ERR_SHAPE: invalid or inconsistent size";
@@ -696,8 +754,9 @@ kata_status kata_backward_timed(const kata_forward_desc* desc, const void* q, co
                          (const float*)nullptr, nP);
     if (bh > 0 && dS0) {
       const int64_t nS = bh * P_DIM * P_DIM * desc->dv, nz = bh * P_DIM * P_DIM;
-      hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, dS0, gST, nS);
-      hipLaunchKernelGGL(kata_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, dz0, gzT, nz);
+      hipLaunchKernelGGL(kata_sym_copy_or_zero, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, dS0, gST, nS,
+                         desc->dv);
+      hipLaunchKernelGGL(kata_sym_copy_or_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, dz0, gzT, nz, 1);
     }
     return launch_status();
   }
@@ -859,7 +918,7 @@ kata_status kata_decode_step_factors_packed(int64_t N, int64_t H, int d, int dv,
                                             float* Sp, float* zp, const void* q, const void* k, const void* v,
                                             const float* P, void* y, void* stream) {
   if (g < 1) return KATA_ERR_SHAPE;
-  if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
+  if (!valid_mode(mode)) return KATA_ERR_UNSUPPORTED;
   if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
   const kata_status s = validate_decode(N, H, d, dv, p, in_dtype, out_dtype);
   if (s != KATA_OK || N * H == 0) return s;
@@ -1068,7 +1127,8 @@ kata_status kata_decode_step_factors(int64_t N, int64_t H, int d, int dv, int p,
                                      kata_dtype in_dtype, kata_dtype out_dtype, float* S, float* z, const void* q,
                                      const void* k, const void* v, const float* P, void* y, void* stream) {
   if (N < 0 || H < 0 || d <= 0 || dv <= 0 || p <= 0 || g < 1) return KATA_ERR_SHAPE;
-  if (mode != KATA_FACTORS_CONCAT && mode != KATA_FACTORS_SUM) return KATA_ERR_UNSUPPORTED;
+  if (!valid_mode(mode)) return KATA_ERR_UNSUPPORTED;
+  if (check_dtype(in_dtype) != KATA_OK || check_dtype(out_dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
   if (g == 1) return kata_decode_step(N, H, d, dv, p, in_dtype, out_dtype, S, z, q, k, v, P, y, stream);
   if (g > kMaxFactors) return KATA_ERR_UNSUPPORTED;
   if (p != P_DIM || !((d == 16 && dv == 16) || (d == 64 && dv == 64))) return KATA_ERR_UNSUPPORTED;
@@ -1090,7 +1150,8 @@ kata_status kata_feature_map(const void* x, const float* P, int64_t n, int64_t H
   if (n < 0 || H < 0 || d <= 0 || p <= 0) return KATA_ERR_SHAPE;
   if (p != P_DIM || !(d == 16 || d == 64)) return KATA_ERR_UNSUPPORTED;
   if (check_dtype(dtype) != KATA_OK) return KATA_ERR_UNSUPPORTED;
-  if (layout != KATA_FEATURE_FULL && layout != KATA_FEATURE_PACKED_KEY && layout != KATA_FEATURE_PACKED_QUERY)
+  const int lv = bits(layout);
+  if (lv != KATA_FEATURE_FULL && lv != KATA_FEATURE_PACKED_KEY && lv != KATA_FEATURE_PACKED_QUERY)
     return KATA_ERR_UNSUPPORTED;
   if (n * H == 0) return KATA_OK;
   if (n * H > 0x7fffffff) return KATA_ERR_SHAPE;

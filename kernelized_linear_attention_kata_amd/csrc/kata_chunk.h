@@ -30,12 +30,17 @@
 namespace kata {
 
 // Compile-time shape of one kernel instance.
-template <int C_, int DIN_, int DV_, bool SPLIT_>
+// SPLIT (fp32 inputs): every operand hi/lo bf16, V included.  PREC (bf16 inputs): the
+// feature operands phi(k), phi(q) and the published state H hi/lo (V, exact in bf16, and
+// the squared scores stay single): the readout phi(q)^T H of a query whose denominator is
+// a small fraction of sum_s |u|^2 |w_s|^2 then keeps about 16 significant bits instead of 8.
+template <int C_, int DIN_, int DV_, bool SPLIT_, bool PREC_ = false>
 struct Shape {
   static constexpr int C = C_;          // chunk length (32, 64, 128)
   static constexpr int DIN = DIN_;      // q/k head dim (16 or 64)
   static constexpr int DV = DV_;        // value head dim (16 or 64)
   static constexpr bool SPLIT = SPLIT_; // fp32 inputs: hi/lo bf16 operands
+  static constexpr bool FSPLIT = SPLIT_ || PREC_;   // hi/lo features and published state
   static constexpr int NB = DV / 16;    // value column blocks
   static constexpr int NMB = C / 16;    // 16-token M-blocks per chunk
   static constexpr int NJ = C / 32;     // 32-token K-blocks per chunk
@@ -51,10 +56,11 @@ struct Shape {
   static constexpr int WZ_BYTES = 2 * NJ * WAVE * 16;         // w tiles as hi/lo bf16 K-block fragments
   static constexpr int Z_BYTES = WAVE * 16;                   // Z (16 x 16) as hi/lo bf16 A-fragments
   static constexpr int PF_BYTES = KD * 2 * WAVE * 16;         // P as hi/lo projection B-fragments
-  static constexpr int NSPLIT = SPLIT ? 2 : 1;
+  static constexpr int NSPLIT = SPLIT ? 2 : 1;      // planes of V
+  static constexpr int NFSPLIT = FSPLIT ? 2 : 1;    // planes of H
   static constexpr int OFF_VF = 0;
   static constexpr int OFF_HX = OFF_VF + NSPLIT * VF_BYTES;
-  static constexpr int OFF_U = OFF_HX + NSPLIT * HX_BYTES;
+  static constexpr int OFF_U = OFF_HX + NFSPLIT * HX_BYTES;
   static constexpr int OFF_W = OFF_U + U_BYTES;
   static constexpr int OFF_WACC = OFF_W + U_BYTES;
   static constexpr int OFF_WZ = OFF_WACC + WACC_BYTES;
@@ -71,7 +77,7 @@ struct Shape {
   static constexpr int DEC_BYTES = 2 * C * 4;
   // waves per SIMD each kernel is compiled for (register budget 512 / OCC): the
   // largest that fits without spilling on gfx950
-  static constexpr int OCC_INTRA = DV <= 16 ? (C == 128 ? 3 : 4) : ((SPLIT || C == 128) ? 2 : 3);
+  static constexpr int OCC_INTRA = DV <= 16 ? (C == 128 ? 3 : 4) : ((FSPLIT || C == 128) ? 2 : 3);
   static constexpr int OCC_STATE = DV <= 16 ? 4 : (SPLIT ? 2 : 3);
   // workspace block per leaf: packed S in accumulator-tile order, then the 16 x 16
   // normaliser matrix Z = sum w w^T (z = vec(Z)) as one accumulator tile
@@ -80,7 +86,7 @@ struct Shape {
   static_assert(DV % 16 == 0 && DV <= 128, "dv");
   static_assert(DIN == 16 || DIN % 32 == 0, "d");
   // three workgroups of the bf16 C = 64, dv = 64 instance share a CU (156 KiB of LDS)
-  static_assert(!(C == 64 && DV == 64 && !SPLIT) || 3 * (SMEM + DEC_BYTES) <= 156 * 1024, "LDS budget");
+  static_assert(!(C == 64 && DV == 64 && !FSPLIT) || 3 * (SMEM + DEC_BYTES) <= 156 * 1024, "LDS budget");
 };
 
 // Offsets of an accumulator tile (delta, nb) inside a leaf's workspace block:
@@ -317,15 +323,15 @@ __device__ __forceinline__ float row_plus(float x) {
 // of delta = d0 + ROT.  The slots (8, a >= 8) repeat the pairs of a < 8; they are
 // accumulated like the others but carry query weight 0 and are never exported.
 template <class S, int ROT>
-__device__ __forceinline__ Op8<S::SPLIT> key_frag(const f32x4& wa0, const f32x4& wa1, const f32x4& wb0,
-                                                  const f32x4& wb1) {
+__device__ __forceinline__ Op8<S::FSPLIT> key_frag(const f32x4& wa0, const f32x4& wa1, const f32x4& wb0,
+                                                   const f32x4& wb1) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[i] = wa0[i] * row_plus<ROT>(wb0[i]);
     x[4 + i] = wa1[i] * row_plus<ROT>(wb1[i]);
   }
-  return make8<S::SPLIT>(x);
+  return make8<S::FSPLIT>(x);
 }
 
 // Feature-split ownership of the packed state accumulators.
@@ -372,22 +378,22 @@ __device__ __forceinline__ void state_update(StateAcc<S>& st, const float* Wacc,
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 0>(wa0, wa1, wr0, wr1);     // delta = w
+      const Op8<S::FSPLIT> kf = key_frag<S, 0>(wa0, wa1, wr0, wr1);     // delta = w
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
+      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
     }
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 4>(wa0, wa1, wr0, wr1);     // delta = w + 4
+      const Op8<S::FSPLIT> kf = key_frag<S, 4>(wa0, wa1, wr0, wr1);     // delta = w + 4
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
+      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
     }
     if (wave < S::NB) {
-      const Op8<S::SPLIT> kf = key_frag<S, 8>(wa0, wa1, wa0, wa1);      // delta = 8
+      const Op8<S::FSPLIT> kf = key_frag<S, 8>(wa0, wa1, wa0, wa1);      // delta = 8
 #pragma unroll
       for (int i = 0; i < StateAcc<S>::N8; ++i) {
 #pragma unroll
         for (int nb = 0; nb < S::NB; ++nb)   // static register index: nb == wave + 4i
-          if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
+          if (nb == wave + 4 * i) st.s8[i] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
       }
     }
     if (zrole) {   // hi/lo: Z feeds the denominator
@@ -448,22 +454,22 @@ __device__ __forceinline__ void state_update_decay(StateAcc<S>& st, const float*
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) vfr[nb] = load_vf<S>(vf_hi, vf_lo, jj, nb, lane);
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 0>(we0, we1, wr0, wr1);     // delta = w
+      const Op8<S::FSPLIT> kf = key_frag<S, 0>(we0, we1, wr0, wr1);     // delta = w
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
+      for (int nb = 0; nb < S::NB; ++nb) st.s[0][nb] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s[0][nb]);
     }
     {
-      const Op8<S::SPLIT> kf = key_frag<S, 4>(we0, we1, wr0, wr1);     // delta = w + 4
+      const Op8<S::FSPLIT> kf = key_frag<S, 4>(we0, we1, wr0, wr1);     // delta = w + 4
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
+      for (int nb = 0; nb < S::NB; ++nb) st.s[1][nb] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s[1][nb]);
     }
     if (wave < S::NB) {
-      const Op8<S::SPLIT> kf = key_frag<S, 8>(we0, we1, wa0, wa1);      // delta = 8
+      const Op8<S::FSPLIT> kf = key_frag<S, 8>(we0, we1, wa0, wa1);      // delta = 8
 #pragma unroll
       for (int i = 0; i < StateAcc<S>::N8; ++i) {
 #pragma unroll
         for (int nb = 0; nb < S::NB; ++nb)
-          if (nb == wave + 4 * i) st.s8[i] = mma<S::SPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
+          if (nb == wave + 4 * i) st.s8[i] = mma<S::FSPLIT, S::SPLIT>(kf, vfr[nb], st.s8[i]);
       }
     }
     if (zrole) {
@@ -712,10 +718,10 @@ __device__ __forceinline__ void publish_state(const StateAcc<S>& st, bf16* hx_hi
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       hi[i] = (bf16)a[i];
-      if constexpr (S::SPLIT) lo[i] = (bf16)(a[i] - (float)hi[i]);
+      if constexpr (S::FSPLIT) lo[i] = (bf16)(a[i] - (float)hi[i]);
     }
     *reinterpret_cast<bf16x4*>(hx_hi + idx) = hi;
-    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = lo;
+    if constexpr (S::FSPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = lo;
   };
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -775,6 +781,19 @@ template <> struct Store4<bf16> {
   }
 };
 
+// Score-tile operand: four consecutive fp32 projection entries (u_t or w_s, from their
+// LDS rows) as a hi/lo bf16 pair.  The score X = u.w feeds the weight X^2, and where X is
+// a small fraction eps of |u| |w| (a query nearly orthogonal to its keys) single bf16
+// operands give X^2 a relative error of about 2^-8 / eps, so a few such weights decide
+// y_t.  With hi/lo operands (three MFMAs instead of one on a K = 16 tile) the error of X
+// drops to about 2^-16 |u| |w|.  The denominator sums the fp32 squares; the value MFMA
+// takes them as bf16, a relative rounding of each (non-negative) weight.
+__device__ __forceinline__ Op4<true> score_operand(const float* row4) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(row4);
+  float xv[4] = {x[0], x[1], x[2], x[3]};
+  return make4<true>(xv);
+}
+
 // Readout + intra tile + gate for one 16-token M-block mb of the chunk; writes y.
 // Everything is computed transposed, O^T = H^T phi(Q)^T + V^T (A o A o M)^T, by
 // feeding the same fragments to the MFMA in swapped operand order: lane (t, g) then
@@ -827,14 +846,14 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
         }
       }
     }
-    const Op8<S::SPLIT> qf = make8<S::SPLIT>(x);
+    const Op8<S::FSPLIT> qf = make8<S::FSPLIT>(x);
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) {
       const int idx = ((kb * S::NB + nb) * WAVE + lane) * 8;
-      Op8<S::SPLIT> hf;
+      Op8<S::FSPLIT> hf;
       hf.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
-      if constexpr (S::SPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
-      O[nb] = mma<S::SPLIT, S::SPLIT>(hf, qf, O[nb]);
+      if constexpr (S::FSPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
+      O[nb] = mma<S::FSPLIT, S::FSPLIT>(hf, qf, O[nb]);
     }
   }
   // phi(q_t) . z = u_t^T Z u_t: (Z U^T)[4g + r][t] from one 16x16x16 MFMA (Z symmetric,
@@ -862,18 +881,17 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
     for (int nb = 0; nb < S::NB; ++nb) O[nb] *= f;
   }
 
-  // intra-chunk: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds X[s = 4g + r][t]
-  const f32x4 ub = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * g);
-  float ubv[4] = {ub[0], ub[1], ub[2], ub[3]};
-  const Op4<S::SPLIT> uf = make4<S::SPLIT>(ubv);
+  // intra-chunk: X_j = W_j U_mb^T (16x16, K = p), lane (t, g) holds X[s = 4g + r][t].
+  // u and w enter as hi/lo bf16 pairs for every input dtype: a weight (u.w)^2 of a query
+  // nearly orthogonal to a key is a small difference of large products, and single bf16
+  // operands would leave it an error of about 2^-8 |u| |w| (see score_operand)
+  const Op4<true> uf = score_operand(Us + t * S::USTR + 4 * g);
   f32x4 A2[S::NMB];
 #pragma unroll
   for (int j = 0; j < S::NMB; ++j) {
     A2[j] = zero4();
     if (j <= mb) {
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(Ws + (j * 16 + n) * S::USTR + 4 * g);
-      float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
-      const f32x4 X = mma<S::SPLIT, S::SPLIT>(make4<S::SPLIT>(wbv), uf, zero4());
+      const f32x4 X = mma<true, true>(score_operand(Ws + (j * 16 + n) * S::USTR + 4 * g), uf, zero4());
       if (j < mb) {   // wave-uniform: only the diagonal tile is masked
 #pragma unroll
         for (int r = 0; r < 4; ++r) A2[j][r] = X[r] * X[r];
@@ -968,14 +986,14 @@ __device__ __forceinline__ void readout_acc(int t, const float* Us, const bf16* 
         }
       }
     }
-    const Op8<S::SPLIT> qf = make8<S::SPLIT>(x);
+    const Op8<S::FSPLIT> qf = make8<S::FSPLIT>(x);
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) {
       const int idx = ((kb * S::NB + nb) * WAVE + lane) * 8;
-      Op8<S::SPLIT> hf;
+      Op8<S::FSPLIT> hf;
       hf.hi = *reinterpret_cast<const bf16x8*>(hx_hi + idx);
-      if constexpr (S::SPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
-      O[nb] = mma<S::SPLIT, S::SPLIT>(hf, qf, O[nb]);
+      if constexpr (S::FSPLIT) hf.lo = *reinterpret_cast<const bf16x8*>(hx_lo + idx);
+      O[nb] = mma<S::FSPLIT, S::FSPLIT>(hf, qf, O[nb]);
     }
   }
   // (Z U^T)[4g + r][t] from one 16x16x16 MFMA (Z symmetric, so its accumulator tile is
@@ -1002,17 +1020,13 @@ __device__ __forceinline__ void intra_acc(int mb, int t, const float* Us, const 
                                           const bf16* vf_lo, int lane, float lt, const float* ls,
                                           f32x4 (&O)[S::NB], float& den) {
   const int n = lane & 15, g = lane >> 4;
-  const f32x4 ub = *reinterpret_cast<const f32x4*>(Us + t * S::USTR + 4 * g);
-  float ubv[4] = {ub[0], ub[1], ub[2], ub[3]};
-  const Op4<S::SPLIT> uf = make4<S::SPLIT>(ubv);
+  const Op4<true> uf = score_operand(Us + t * S::USTR + 4 * g);   // hi/lo, as in chunk_outputs
   f32x4 A2[S::NMB];
 #pragma unroll
   for (int j = 0; j < S::NMB; ++j) {
     A2[j] = zero4();
     if (j <= mb) {
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(Ws + (j * 16 + n) * S::USTR + 4 * g);
-      float wbv[4] = {wb[0], wb[1], wb[2], wb[3]};
-      const f32x4 X = mma<S::SPLIT, S::SPLIT>(make4<S::SPLIT>(wbv), uf, zero4());
+      const f32x4 X = mma<true, true>(score_operand(Ws + (j * 16 + n) * S::USTR + 4 * g), uf, zero4());
       if (j < mb) {   // wave-uniform: only the diagonal tile is masked
 #pragma unroll
         for (int r = 0; r < 4; ++r) A2[j][r] = X[r] * X[r];
@@ -1102,7 +1116,7 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   for (int i = tid; i < S::NB * WAVE; i += 256) {
     const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
     *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::FSPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
   }
   // Roles: wave w takes the M-blocks w, w + 4, ... (token split) and the Z update
   // goes to wave 0, whose M-block has the least intra-chunk work.
@@ -1237,7 +1251,7 @@ kata_chunk_intra_mg(const TIn* __restrict__ q, const TIn* __restrict__ k, const 
   for (int i = tid; i < S::NB * WAVE; i += 256) {   // readout K-block 4, slots 4..7: zero
     const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
     *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::FSPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
   }
   const int tw = wave;
   const bool zrole = wave == 0;
@@ -1362,7 +1376,7 @@ kata_chunk_intra_sg(const TIn* __restrict__ q, const TIn* __restrict__ k, const 
   for (int i = tid; i < S::NB * WAVE; i += 256) {   // readout K-block 4, slots 4..7: zero
     const int idx = ((4 * S::NB) * WAVE + i) * 8 + 4;
     *reinterpret_cast<bf16x4*>(hx_hi + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    if constexpr (S::SPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    if constexpr (S::FSPLIT) *reinterpret_cast<bf16x4*>(hx_lo + idx) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
   }
   const int tw = wave;
   const bool zrole = wave == 0;

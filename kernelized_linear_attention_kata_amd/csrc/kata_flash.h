@@ -11,13 +11,19 @@
 // of the weights).
 //
 // Two kernels:
-//  * kata_flash_prep  (grid T_pad/64 x B*H): u = P q, w = P k (bf16) and V, regrouped
-//    into MFMA operand order and written once per token to a workspace.
+//  * kata_flash_prep  (grid T_pad/64 x B*H): u = P q, w = P k (as hi/lo bf16 pairs) and
+//    V, regrouped into MFMA operand order and written once per token to a workspace.
 //  * kata_flash_attn  (T_pad/256 * B*H workgroups, XCD-aware order): 8 waves x
 //    32 queries; 64-key blocks of w and V fragments copied into an LDS ring.  Per
-//    32-key tile: X^T = W U^T (one 32x32x16 MFMA, K = p), squared and masked on the
-//    VALU, then O^T += V^T (X^2)^T (32x32x16 MFMAs, K = 16 keys).  Lane l holds output
-//    columns of query l%32, so the denominator needs one lane-pair sum.
+//    32-key tile: X^T = W U^T (three 32x32x16 MFMAs, K = p, hi/lo operands), squared and
+//    masked on the VALU, then O^T += V^T (X^2)^T (32x32x16 MFMAs, K = 16 keys).  Lane l
+//    holds output columns of query l%32, so the denominator needs one lane-pair sum.
+//
+// Precision: the weight (u.w)^2 of a query nearly orthogonal to a key is a small
+// difference of large products; with u and w as single bf16 its error would be about
+// 2^-8 |u| |w| |u.w|, which decides y_t where the denominator is a small fraction of
+// sum_s |u_t|^2 |w_s|^2.  The hi/lo pairs (hi*hi + hi*lo + lo*hi) bring the error of u.w
+// to about 2^-16 |u| |w|.
 #pragma once
 
 #include "kata_chunk.h"
@@ -39,14 +45,16 @@ __device__ __forceinline__ f32x16 mfma3232(const bf16x8& a, const bf16x8& b, con
 // B lane l holds column l%32, k = 8*(l/32) + i; C lane l holds column l%32 and rows
 // 8*(i/4) + 4*(l/32) + i%4, i = 0..15).  Workspace of one (b, h) sequence, T_pad = T
 // rounded up to FL_QB, rows past T zero:
-//  * U  [T_pad][16] bf16: u_t; a query lane reads u_t[8h .. 8h+7] (B operand of the score).
-//  * Wf [T_pad/32][64 lanes][8] bf16: the A operand of the score tile of 32 keys, lane l
-//    holding w_{32x + l%32}[8h .. 8h+7], h = l/32 (lane-contiguous, conflict-free reads).
+//  * U  [2][T_pad][16] bf16: u_t as hi (plane 0) and lo = bf16(u - hi) (plane 1); a query
+//    lane reads u_t[8h .. 8h+7] of both (B operands of the score).
+//  * Wf [2][T_pad/32][64 lanes][8] bf16: hi and lo planes of the A operand of the score
+//    tile of 32 keys, lane l holding w_{32x + l%32}[8h .. 8h+7], h = l/32
+//    (lane-contiguous, conflict-free reads).
 //  * Vf [T_pad/16][2][64 lanes][8] bf16: the A operand V^T of the value MFMA for the
 //    16-key group kappa and the 32-column tile ct: lane l (column 32ct + l%32, h = l/32)
 //    holds v at keys 16kappa + 4h + i and 16kappa + 8 + 4h + i (i = 0..3), the order in
 //    which the score accumulator hands its squared entries to the value MFMA.
-__host__ __device__ constexpr int64_t flash_ws_elems(int64_t tpad) { return tpad * (2 * P_DIM + FL_DV); }
+__host__ __device__ constexpr int64_t flash_ws_elems(int64_t tpad) { return tpad * (4 * P_DIM + FL_DV); }
 
 // ---- kata_flash_prep -----------------------------------------------------------
 // One 64-token chunk per workgroup, wave w projects tokens 16w..16w+15; V goes
@@ -83,9 +91,9 @@ kata_flash_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn*
     *reinterpret_cast<bf16x8*>(&vs[16 * wave + n][32 * kk + 8 * g]) = r.v[0][kk].x;
 
   bf16* base = ws + bh * flash_ws_elems(tpad);
-  bf16* Ub = base;
-  bf16* Wf = base + tpad * P_DIM;
-  bf16* Vf = base + 2 * tpad * P_DIM;
+  bf16* Ub = base;                          // hi plane; the lo plane follows at + tpad * P_DIM
+  bf16* Wf = base + 2 * tpad * P_DIM;       // hi plane; the lo plane follows at + tpad * P_DIM
+  bf16* Vf = base + 4 * tpad * P_DIM;
   const int tok = t0 + 16 * wave + n;        // this lane's token in the transposed tiles
   // u^T, w^T tiles: P (A operand, lane (a, g)) times q^T / k^T (B operand, lane (t, g)):
   // lane (t, g) receives u_t[4g .. 4g+3]
@@ -101,10 +109,14 @@ kata_flash_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn*
   {
     float uv[4] = {u[0], u[1], u[2], u[3]};
     float wv[4] = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<bf16x4*>(Ub + (int64_t)tok * P_DIM + 4 * g) = make4<false>(uv).hi;
+    const Op4<true> us = make4<true>(uv), ws4 = make4<true>(wv);
+    const int64_t ui = (int64_t)tok * P_DIM + 4 * g;
+    *reinterpret_cast<bf16x4*>(Ub + ui) = us.hi;
+    *reinterpret_cast<bf16x4*>(Ub + tpad * P_DIM + ui) = us.lo;
     // features 4g..4g+3 of key tok: lane (tok%32) + 32*(g/2) of its 32-key tile, slots 4*(g%2)..
     const int64_t wi = (((int64_t)(tok >> 5) * WAVE + (tok & 31) + 32 * (g >> 1)) * 8) + 4 * (g & 1);
-    *reinterpret_cast<bf16x4*>(Wf + wi) = make4<false>(wv).hi;
+    *reinterpret_cast<bf16x4*>(Wf + wi) = ws4.hi;
+    *reinterpret_cast<bf16x4*>(Wf + tpad * P_DIM + wi) = ws4.lo;
   }
   __syncthreads();
   // value fragments: 4 key groups x 2 column tiles of the chunk, 2 per thread
@@ -127,14 +139,14 @@ kata_flash_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn*
 // ---- kata_flash_attn -----------------------------------------------------------
 // Key blocks are copied straight from the workspace into an LDS ring of FL_RING
 // buffers by buffer_load ... lds (no registers), FL_RING - 1 blocks ahead of use.  A
-// buffer is [Wf block: 2 tiles x 64 lanes x 16 B = 2 KB | Vf block: 4 groups x 2 tiles
-// x 64 lanes x 16 B = 8 KB | 6 KB pad], sixteen 1 KB pieces: every wave copies pieces
-// w and w + 8 (the pad pieces read past the workspace: zeros, no traffic), so each
-// wave has exactly FL_DMA_PER_WAVE loads per block in flight and waits for a block
-// with an exact vmcnt.
+// buffer is [Wf hi block: 2 tiles x 64 lanes x 16 B = 2 KB | Wf lo block: 2 KB | Vf
+// block: 4 groups x 2 tiles x 64 lanes x 16 B = 8 KB | 4 KB pad], sixteen 1 KB pieces:
+// every wave copies pieces w and w + 8 (the pad pieces read past the workspace: zeros,
+// no traffic), so each wave has exactly FL_DMA_PER_WAVE loads per block in flight and
+// waits for a block with an exact vmcnt.
 constexpr int FL_W_BYTES = FL_KB * P_DIM * 2;
 constexpr int FL_V_BYTES = FL_KB * FL_DV * 2;
-constexpr int FL_PIECES = 16;   // 1 KB pieces per buffer (10 used, 6 read as zeros)
+constexpr int FL_PIECES = 16;   // 1 KB pieces per buffer (12 used, 4 read as zeros)
 constexpr int FL_BUF_BYTES = FL_PIECES * 1024;
 // Two buffers (the copy of block kb + 1 runs during block kb) measured fastest with
 // eight waves: 32 KB per workgroup, three workgroups per CU, 6 waves per SIMD.
@@ -149,7 +161,7 @@ typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_s_waitcnt(((N) & 0xf) | (((N) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
 template <typename TOut>
-__global__ void __launch_bounds__(64 * FL_WAVES)
+__global__ void __launch_bounds__(64 * FL_WAVES, 6)
 kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, int64_t tpad, int nbh) {
   __shared__ __align__(16) unsigned char sm[FL_RING * FL_BUF_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -173,18 +185,20 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
   }
   const int qb = nqb - 1 - qi;
   const bf16* base = ws + bh * flash_ws_elems(tpad);
-  const int w_off = (int)(tpad * P_DIM * 2);          // byte offsets inside the workspace
-  const int v_off = (int)(2 * tpad * P_DIM * 2);
+  const int w_off = (int)(2 * tpad * P_DIM * 2);      // byte offsets inside the workspace:
+  const int wlo_off = (int)(3 * tpad * P_DIM * 2);    // W hi and lo planes, then V
+  const int v_off = (int)(4 * tpad * P_DIM * 2);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(base, flash_ws_elems(tpad) * 2);
 
   const int q0 = qb * FL_QB + 32 * wave;             // this wave's 32 queries
   const int tq = q0 + c32;                           // this lane's query
   const bf16x8 ub = *reinterpret_cast<const bf16x8*>(base + (int64_t)tq * P_DIM + 8 * hh);
+  const bf16x8 ubl = *reinterpret_cast<const bf16x8*>(base + (tpad + tq) * P_DIM + 8 * hh);
   // the u loads must complete here, before any ring copy is in flight: consumed by an
   // (empty) asm statement, they get their wait at this point; otherwise the loads sink
   // below the first copies and their wait, at the first use of u in the loop, covers
   // every copy in flight
-  asm volatile("" ::"v"(ub));
+  asm volatile("" ::"v"(ub), "v"(ubl));
   f32x16 O[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -199,7 +213,8 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
     for (int i = 0; i < FL_DMA_PER_WAVE; ++i) {
       const int c = wave + FL_WAVES * i;               // 1 KB piece of the buffer
       const int src = c < 2 ? w_off + kb * FL_W_BYTES + c * 1024
-                    : (c < 10 ? v_off + kb * FL_V_BYTES + (c - 2) * 1024 : BUF_OOB);
+                    : (c < 4 ? wlo_off + kb * FL_W_BYTES + (c - 2) * 1024
+                             : (c < 12 ? v_off + kb * FL_V_BYTES + (c - 4) * 1024 : BUF_OOB));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_void*)(dst + c * 1024), 16,
                                                src >= BUF_OOB ? BUF_OOB : src + lane * 16, 0, 0, 0);
     }
@@ -218,7 +233,8 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
     asm volatile("s_barrier" ::: "memory");
     if (kb + FL_RING - 1 < nkb) dma(kb + FL_RING - 1);
     const bf16* Wl = reinterpret_cast<const bf16*>(sm + (kb % FL_RING) * FL_BUF_BYTES);
-    const bf16* Vl = Wl + FL_KB * P_DIM;
+    const bf16* Wlo = Wl + FL_KB * P_DIM;
+    const bf16* Vl = Wl + 2 * FL_KB * P_DIM;
     const int s_blk = kb * FL_KB;
     if (s_blk > q0 + 31) continue;                   // wave-uniform: every key after every query
     const bool full = s_blk + FL_KB - 1 <= q0;       // no key after any query of the wave
@@ -227,6 +243,7 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
       const int s0 = s_blk + 32 * x;
       if (!full && s0 > q0 + 31) continue;           // wave-uniform
       const bf16x8 wf = *reinterpret_cast<const bf16x8*>(Wl + (x * WAVE + lane) * 8);
+      const bf16x8 wfl = *reinterpret_cast<const bf16x8*>(Wlo + (x * WAVE + lane) * 8);
       bf16x8 vf[2][2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -236,7 +253,8 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
       f32x16 zero16;
 #pragma unroll
       for (int i = 0; i < 16; ++i) zero16[i] = 0.f;
-      const f32x16 X = mfma3232(wf, ub, zero16);     // lane: keys s0 + 8(i/4) + 4hh + i%4 of query tq
+      // lane: keys s0 + 8(i/4) + 4hh + i%4 of query tq; hi*hi + hi*lo + lo*hi
+      const f32x16 X = mfma3232(wfl, ub, mfma3232(wf, ubl, mfma3232(wf, ub, zero16)));
       float a2[16];
       if (full || s0 + 31 <= q0) {
 #pragma unroll

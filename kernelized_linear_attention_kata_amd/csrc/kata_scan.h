@@ -2,9 +2,17 @@
 // states, in place, plus the inclusive total exported as the final state.
 //
 // The hardware section of the gist.science summary of "Kernelized Linear Attention"
-// (arXiv 2607.17419, section 2.3) and the paper's abstract state that the inter-chunk
-// state propagation is an associative scan (parallel prefix sum) of depth
-// O(log(T/C)).  The combine operator on states [S | z] is elementwise addition.
+// (arXiv 2607.17419, section 2.3) and the paper's abstract give the inter-chunk state
+// propagation as an associative scan (a parallel prefix sum, log depth in T/C) in place
+// of the chunk-after-chunk recurrence.  The combine operator on states [S | z] is
+// elementwise addition.  What ships is a reduce-then-scan over leaves of L chunks: the
+// leaf sums (kata_chunk_state) get their exclusive prefix here by a segmented scan (up
+// to 16 rows summed in order per thread, up to 16 segment totals combined through LDS,
+// passes of 256 leaves chained by a carry), and the pass that forms the outputs
+// completes each chunk's prefix inside its leaf with a running sum.  Sequential depth:
+// L chunk steps plus at most 32 combine steps per 256 leaves, i.e. O(L + n_leaf/16), not
+// O(log(T/C)); at the leaf counts the library picks (tens per sequence) a log-depth
+// combine of the leaf sums measured 1.5x slower than this one.
 //
 // Layout: ws[bh][leaf][e], e < E = 144*dv + 256 (packed S then Z, see kata_chunk.h).
 // The exclusive prefix written for leaf g is S0 + sum_{g' < g} state_g' (or the suffix
@@ -60,30 +68,26 @@ __device__ __forceinline__ bool packed_to_pair(int e, int dv, int& a, int& b, in
 constexpr int SCAN_ROWS = 16;    // rows per segment and pass (registers)
 constexpr int SCAN_GMAX = 16;    // segments per quad
 
-// Canonical initial value of element e, 0 for none: the upper-triangle entry of S0 / z0
-// (sym = false: a state, whose mirror entries are equal), or the mean of the two mirror
-// entries (sym = true: a gradient with respect to a state, whose symmetric part is what
-// acts on the symmetric feature).
-__device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const float* S0, const float* z0,
-                                              bool sym) {
+// Canonical initial value of element e, 0 for none: the mean of the two mirror entries of
+// S0 / z0 (i.e. the symmetric part of the caller's state, or of a gradient with respect to
+// a state; only the symmetric part acts on the symmetric feature).  For the symmetric
+// states this library produces the mean is the entry itself, bit for bit.
+__device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const float* S0, const float* z0) {
   int a, b, col;
   bool is_z, mirror;
   if (!packed_to_pair(e, dv, a, b, col, is_z, mirror)) return 0.f;
   const int64_t pp = (int64_t)P_DIM * P_DIM;
-  const int lo = a < b ? a : b, hi = a < b ? b : a;
   if (!is_z) {
     if (!S0) return 0.f;
-    const float x = S0[(bh * pp + lo * P_DIM + hi) * dv + col];
-    return sym ? 0.5f * (x + S0[(bh * pp + hi * P_DIM + lo) * dv + col]) : x;
+    return 0.5f * (S0[(bh * pp + a * P_DIM + b) * dv + col] + S0[(bh * pp + b * P_DIM + a) * dv + col]);
   }
   if (!z0) return 0.f;
-  const float x = z0[bh * pp + lo * P_DIM + hi];
-  return sym ? 0.5f * (x + z0[bh * pp + hi * P_DIM + lo]) : x;
+  return 0.5f * (z0[bh * pp + a * P_DIM + b] + z0[bh * pp + b * P_DIM + a]);
 }
 
 // grid (ceil((E/4) / (256/G)), B*H), block 256.  E is a multiple of 4.  reverse = 1
 // scans the leaves from the last to the first (an exclusive suffix: leaf g receives
-// init + sum_{g' > g} state_g'), as the backward pass needs; sym_init as in scan_initial.
+// init + sum_{g' > g} state_g'), as the backward pass needs; init as in scan_initial.
 //
 // dec (decay-gated state, may be NULL): dec[bh * n_leaf + g] is the total decay D_g of leaf
 // g, and the combine becomes affine: the prefix entering leaf g + 1 is D_g * (prefix
@@ -91,8 +95,7 @@ __device__ __forceinline__ float scan_initial(int e, int dv, int64_t bh, const f
 __global__ void __launch_bounds__(256)
 kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
                 const float* __restrict__ S0, const float* __restrict__ z0,
-                float* __restrict__ ST, float* __restrict__ zT, int reverse, int sym_init,
-                const float* __restrict__ dec) {
+                float* __restrict__ ST, float* __restrict__ zT, int reverse, const float* __restrict__ dec) {
   __shared__ f32x4 tot[256];
   __shared__ f32x4 carry_s[256];
   __shared__ float dseg[SCAN_GMAX];
@@ -110,7 +113,7 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
   f32x4 carry = zero4();   // the quad's running carry, kept by segment 0
   if (seg == 0 && active) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0, sym_init != 0);
+    for (int i = 0; i < 4; ++i) carry[i] = scan_initial(e0 + i, dv, bh, S0, z0);
   }
   const float* dl = dec ? dec + bh * n_leaf : nullptr;
   for (int64_t r0 = 0; r0 < n_leaf; r0 += (int64_t)lseg * G) {

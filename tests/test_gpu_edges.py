@@ -1,13 +1,27 @@
 """Edge cases of the entry points beyond the one-factor forward (whose own edge cases are in
-test_gpu_parity.py): sequences with no tokens export the initial state unchanged, empty
-batches return without work, all-zero query rows give y = 0, and the chunked DeltaKATA at
-many sequences (its workgroup remap) against the recurrent kernel."""
+test_gpu_parity.py): sequences with no tokens export the initial state as every entry
+point reads it (its symmetric part; DeltaKATA carries the state unchanged), empty batches
+return without work, all-zero query rows give y = 0, the chunked DeltaKATA at many
+sequences (its workgroup remap) against the recurrent kernel, and a caller state that is
+not symmetric read alike by the forward over no token, the forward over one token and the
+decode step."""
 import numpy as np
 import pytest
 import torch
 
 import kernelized_linear_attention_kata_amd as kata
 from kernelized_linear_attention_kata_amd import inputs as I
+from oracle import kata_oracle as O
+
+
+def sym_state(S):
+    """The symmetric part of canonical states [..., blocks*256, cols] or z [..., blocks*256]:
+    entry (i, j) of each 256-row block is the mean of (i, j) and (j, i)."""
+    if S.dim() >= 2 and S.shape[-1] != 256 and S.shape[-2] % 256 == 0:
+        x = S.reshape(*S.shape[:-2], S.shape[-2] // 256, 16, 16, S.shape[-1])
+        return (0.5 * (x + x.transpose(-3, -2))).reshape(S.shape)
+    x = S.reshape(*S.shape[:-1], S.shape[-1] // 256, 16, 16)
+    return (0.5 * (x + x.transpose(-2, -1))).reshape(S.shape)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -27,7 +41,7 @@ def test_decay_no_tokens_keeps_state():
     y, ST, zT = kata.forward_decay(q, k, v, P, lam, S0=S0, z0=z0, return_state=True)
     torch.cuda.synchronize()
     assert y.shape == (B, H, 0, 64)
-    assert torch.equal(ST, S0) and torch.equal(zT, z0)
+    assert torch.equal(ST, sym_state(S0)) and torch.equal(zT, sym_state(z0))
 
 
 @pytest.mark.parametrize("mode,rows", [("concat", 2 * 256), ("sum", 256)])
@@ -39,7 +53,7 @@ def test_factors_no_tokens_keep_state(mode, rows):
     z0 = torch.rand((B, H, rows), device=DEV)
     y, ST, zT = kata.forward_factors(q, k, v, P, mode, S0=S0, z0=z0, return_state=True)
     torch.cuda.synchronize()
-    assert torch.equal(ST, S0) and torch.equal(zT, z0)
+    assert torch.equal(ST, sym_state(S0)) and torch.equal(zT, sym_state(z0))
     _, ST, zT = kata.forward_factors(q, k, v, P, mode, return_state=True)
     torch.cuda.synchronize()
     assert torch.all(ST == 0) and torch.all(zT == 0)
@@ -147,38 +161,69 @@ def test_forward_at_the_largest_batch_times_heads():
 
 def test_decode_step_beyond_65535_workgroups():
     """N*H = 67200 streams (a 1-D grid past 65535), dv = 16, each with a valid KATA state
-    (the sum of phi(k) v^T over 4 seeded keys): sampled streams' steps against a float64
-    evaluation of the same update on the host."""
+    (the oracle's final state over 4 seeded keys): sampled streams' steps against the
+    oracle's decode step."""
     N, H, d = 4200, 16, 16
     g = torch.Generator().manual_seed(141)
     P = torch.randn((H, 16, d), generator=g) / 4
-
-    def feat(x):   # phi(x) = vec(u u^T), u = P_h x, for x [..., H, d]
-        u = torch.einsum("had,...hd->...ha", P, x)
-        return (u[..., :, None] * u[..., None, :]).flatten(-2)
-
-    k0 = torch.randn((4, N, H, d), generator=g) / 4
-    v0 = torch.randn((4, N, H, d), generator=g) / 4
-    f0 = feat(k0)                                            # [4, N, H, 256]
-    S = torch.einsum("jnhf,jnhc->nhfc", f0, v0).contiguous()
-    z = f0.sum(0).contiguous()
+    k0 = torch.randn((N, H, 4, d), generator=g) / 4
+    v0 = torch.randn((N, H, 4, d), generator=g) / 4
+    Sn, zn = O.final_state(k0.double().numpy(), v0.double().numpy(), P.double().numpy())
+    S, z = torch.from_numpy(Sn).float(), torch.from_numpy(zn).float()
     q, k, v = (torch.randn((N, H, d), generator=g) / 4 for _ in range(3))
     Sd, zd = S.to(DEV), z.to(DEV)
     y = kata.decode_step(Sd, zd, q.to(DEV), k.to(DEV), v.to(DEV), P.to(DEV))
     torch.cuda.synchronize()
     rng = np.random.default_rng(141)
     idx = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 300)]))
-    Pd = P.double()
-    u = torch.einsum("had,nhd->nha", Pd, q[idx].double())
-    w = torch.einsum("had,nhd->nha", Pd, k[idx].double())
-    fu = (u[..., :, None] * u[..., None, :]).flatten(2)
-    fw = (w[..., :, None] * w[..., None, :]).flatten(2)
-    S2 = S[idx].double() + fw[..., None] * v[idx].double()[:, :, None, :]
-    z2 = z[idx].double() + fw
-    yr = torch.einsum("nhf,nhfc->nhc", fu, S2) / torch.einsum("nhf,nhf->nh", fu, z2)[..., None]
-    yg = y[torch.as_tensor(idx, device=DEV)].double().cpu()
-    Sg = Sd[torch.as_tensor(idx, device=DEV)].double().cpu()
-    e = float(((yg - yr).norm(dim=-1) / yr.norm(dim=-1)).max())
-    eS = float(((Sg - S2).flatten(2).norm(dim=-1) / S2.flatten(2).norm(dim=-1)).max())
+    yr, S2, z2 = O.decode_reference(S[idx].double().numpy(), z[idx].double().numpy(), q[idx].double().numpy(),
+                                    k[idx].double().numpy(), v[idx].double().numpy(), P.double().numpy())
+    yg = y[torch.as_tensor(idx, device=DEV)].double().cpu().numpy()
+    Sg = Sd[torch.as_tensor(idx, device=DEV)].double().cpu().numpy()
+    e = float((np.linalg.norm(yg - yr, axis=-1) / np.linalg.norm(yr, axis=-1)).max())
+    eS = float((np.linalg.norm((Sg - S2).reshape(len(idx), H, -1), axis=-1)
+                / np.linalg.norm(S2.reshape(len(idx), H, -1), axis=-1)).max())
     print(f"[decode 67200 streams] y {e:.2e} S {eS:.2e}", flush=True)
     assert e <= 1e-5 and eS <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_asymmetric_initial_state(dtype):
+    """A caller state that is not symmetric in the feature pair (i, j): every entry point
+    reads its symmetric part.  The forward over no token exports that part exactly, the
+    forward over one token exports it plus the token's phi(k) v^T (symmetric), and the
+    decode step from the same state with the same token gives the same y, against the
+    oracle; the decode step keeps the antisymmetric part in place."""
+    name, d = ("mid", 64) if dtype == "bf16" else ("tiny", 16)
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    case = I.make_forward(name, B=2, H=3, T=1, seed=160, dtype=dtype)
+    g = torch.Generator().manual_seed(160)
+    S0 = torch.randn((2, 3, 256, d), generator=g) / 8              # no symmetry
+    z0 = torch.rand((2, 3, 256), generator=g) + 0.5
+    q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
+    S0d, z0d = S0.to(DEV), z0.to(DEV)
+    e0 = [torch.empty((2, 3, 0, d), dtype=q.dtype, device=DEV) for _ in range(3)]
+    _, ST0, zT0 = kata.forward(*e0, P, 32, S0=S0d, z0=z0d, return_state=True)
+    y1, ST1, zT1 = kata.forward(q, k, v, P, 32, S0=S0d, z0=z0d, return_state=True, out_dtype=torch.float32)
+    Sdec, zdec = S0d.clone(), z0d.clone()
+    yd = kata.decode_step(Sdec, zdec, q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(), P)
+    torch.cuda.synchronize()
+    assert torch.equal(ST0, sym_state(S0d)) and torch.equal(zT0, sym_state(z0d))
+    # the export writes one value to both mirror entries of S; z's mirror entries come from
+    # products whose terms pair up differently and agree to rounding
+    assert torch.equal(ST1, sym_state(ST1))
+    assert float((zT1 - sym_state(zT1)).abs().max()) <= 1e-6 * float(zT1.abs().max())
+    qh, kh, vh = (O.bf16_bits_to_f64(I.bf16_bits(t)) if dtype == "bf16" else t.double().numpy()
+                  for t in (case.q, case.k, case.v))
+    Ph = case.P.double().numpy()
+    yr = O.forward_quadratic(qh, kh, vh, Ph, S0.double().numpy(), z0.double().numpy())
+    Sr, zr = O.final_state(kh, vh, Ph, sym_state(S0).double().numpy(), sym_state(z0).double().numpy())
+    rel = lambda a, b: float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+    ey, eyd = rel(y1.cpu().numpy(), yr), rel(yd.cpu().numpy(), yr[:, :, 0])
+    eS, ez = rel(ST1.cpu().numpy(), Sr), rel(zT1.cpu().numpy(), zr)
+    # the decode step adds phi(k) v^T to the caller's state as it is
+    Sdr, zdr = O.final_state(kh, vh, Ph, S0.double().numpy(), z0.double().numpy())
+    eSd, ezd = rel(Sdec.cpu().numpy(), Sdr), rel(zdec.cpu().numpy(), zdr)
+    print(f"[asymmetric S0 {dtype}] y forward {ey:.2e} decode {eyd:.2e}; ST {eS:.2e} zT {ez:.2e}; "
+          f"decode S {eSd:.2e} z {ezd:.2e}", flush=True)
+    assert max(ey, eyd, eS, ez) <= tol and max(eSd, ezd) <= 1e-5

@@ -104,15 +104,32 @@ def test_workload_lm340m():
     check_case(I.make_forward("lm340m", device=DEV))
 
 
+def leaf_starts(B, H, T, chunk):
+    """First token of every leaf after the first in the library's own leaf plan, read back
+    from the workspace size (B*H*n_leaf blocks of 144*64 + 256 floats)."""
+    ws = kata.forward_workspace_bytes(B, H, T, 64, 64, chunk)
+    n_leaf = ws // (B * H * (144 * 64 + 256) * 4)
+    n_chunks = -(-T // chunk)
+    leaf = -(-n_chunks // n_leaf)
+    assert -(-n_chunks // leaf) == n_leaf
+    return [j * leaf * chunk for j in range(1, n_leaf)]
+
+
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_workload_long_sampled(chunk):
-    """T = 131072: y checked on sampled query rows (first/last rows, chunk and leaf
-    boundaries, random rows); the final state in full."""
+    """T = 131072: y checked on sampled query rows (first/last rows, chunk boundaries, the
+    last token of every leaf and the first two of the next, random rows); the final state
+    in full."""
     case = I.make_forward("long", device=DEV)
     T = case.T
     r = np.random.default_rng(5)
+    starts = leaf_starts(case.B, case.H, T, chunk)
+    if chunk == 64:
+        assert starts[:2] == [2752, 5504]          # 48 leaves of 43 chunks per head
+    edges = np.concatenate([[s - 1, s, s + 1] for s in starts])
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128, 4095, 4096, T // 2, T - 2, T - 1],
-                                     r.integers(0, T, 40)]))
+                                     edges, r.integers(0, T, 40)]))
+    print(f"[long C={chunk}] {len(starts) + 1} leaves per head, {len(rows)} sampled rows", flush=True)
     check_case(case, chunk, rows=rows)
 
 
@@ -281,7 +298,11 @@ def test_empty_sequence_copies_initial_state():
     y, ST, zT = kata.forward(q, q, q, P, chunk=64, S0=S0, z0=z0, return_state=True)
     torch.cuda.synchronize()
     assert y.shape == (B, H, 0, 64)
-    assert torch.equal(ST, S0) and torch.equal(zT, z0)
+    # the state as every entry point reads it: the mean of the mirror entries (i, j), (j, i)
+    Sm = S0.view(B, H, 16, 16, 64)
+    zm = z0.view(B, H, 16, 16)
+    assert torch.equal(ST, (0.5 * (Sm + Sm.transpose(2, 3))).reshape(B, H, 256, 64))
+    assert torch.equal(zT, (0.5 * (zm + zm.transpose(2, 3))).reshape(B, H, 256))
     y, ST, zT = kata.forward(q, q, q, P, chunk=64, return_state=True)
     torch.cuda.synchronize()
     assert torch.all(ST == 0) and torch.all(zT == 0)
@@ -302,23 +323,26 @@ def test_many_heads_and_batches():
 
 
 def test_initial_state_symmetric_read():
-    """A caller state is read from its i <= j entries (mirror entries assumed equal)."""
+    """A caller state is read through its symmetric part, the mean of the mirror entries:
+    swapping every mirror pair of S0 and z0 leaves y bit for bit unchanged, and a state
+    with an antisymmetric part added gives the oracle's y (the readout phi(q)^T S0 sees
+    only the symmetric part)."""
     case = I.make_forward("mid", B=1, H=2, T=150, seed=15)
     kh, vh = host64(case.k), host64(case.v)
     Ph = case.P.double().cpu().numpy()
     S0, z0 = O.final_state(kh[:, :, :40], vh[:, :, :40], Ph)
+    g = np.random.default_rng(15)
+    A = g.standard_normal(S0.shape).reshape(1, 2, 16, 16, 64)
+    S0 = S0 + (A - A.transpose(0, 1, 3, 2, 4)).reshape(S0.shape) * np.abs(S0).max()   # not symmetric
+    a = g.standard_normal(z0.shape).reshape(1, 2, 16, 16)
+    z0 = z0 + (a - a.transpose(0, 1, 3, 2)).reshape(z0.shape) * np.abs(z0).max()
     S0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
     z0 = torch.tensor(z0, dtype=torch.float32, device=DEV)
     q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
     y1 = kata.forward(q, k, v, P, chunk=64, S0=S0, z0=z0, out_dtype=torch.float32)
-    # scramble the lower triangle: the result must not change
-    idx = torch.arange(256, device=DEV)
-    lower = (idx // 16) > (idx % 16)
-    S0b = S0.clone()
-    S0b[:, :, lower] = 123.0
-    z0b = z0.clone()
-    z0b[:, :, lower] = -7.0
-    y2 = kata.forward(q, k, v, P, chunk=64, S0=S0b, z0=z0b, out_dtype=torch.float32)
+    S0t = S0.view(1, 2, 16, 16, 64).transpose(2, 3).reshape(1, 2, 256, 64).contiguous()
+    z0t = z0.view(1, 2, 16, 16).transpose(2, 3).reshape(1, 2, 256).contiguous()
+    y2 = kata.forward(q, k, v, P, chunk=64, S0=S0t, z0=z0t, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     qh = host64(case.q)

@@ -10,15 +10,13 @@ steps (KATA and DeltaKATA on the canonical state, KATA on the packed one) from s
 the oracle builds over a prefix.
 
 Conditioning.  The output gate divides by den_t = sum_s (u_t.w_s)^2 (the prefix's keys
-included, through z0).  A bf16 feature rounds each term by about 2^-9 of
-|u_t|^2 |w_s|^2, so where den_t is a tiny fraction of sum_s |u_t|^2 |w_s|^2 (a query
-nearly orthogonal to every key) y_t is set by rounding on any path that stores bf16
-features, and no relative bound holds for it.  The exception is a single key, where
-y_t = v_s for any nonzero weight.  A draw in which some query with two or more keys has
-den_t below 1e-2 of that sum is rejected on the host, from the seeded inputs alone, and
-drawn again; the packed decode draws are checked the same way.  At T = 1 the DeltaKATA
-output is beta (u.w)^2 / (|u|^2 |w|^2) v: one squared cosine, compared as an absolute
-error on the scale beta |v|.
+included, through z0).  Where den_t is a small fraction r_t of sum_s |u_t|^2 |w_s|^2 (a
+query nearly orthogonal to the few keys it sees), y_t rests on weights that are small
+differences of large products.  Every draw is taken as drawn, whatever its conditioning:
+the score tiles take u and w as hi/lo bf16 pairs, so the weights keep about 16 significant
+bits, and test_draws_span_the_shapes checks that ill-conditioned draws (r_t below 1e-2) are
+among them.  Gates built to be far worse (r_t near 1e-5) are in test_gpu_conditioning.py.  At T = 1 the DeltaKATA output is beta (u.w)^2 / (|u|^2 |w|^2) v:
+one squared cosine, compared as an absolute error on the scale beta |v|.
 """
 import dataclasses
 
@@ -33,7 +31,6 @@ from oracle import kata_oracle as O
 DEV = "cuda:0"
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 NDRAWS = 12
-MIN_RATIO = 1e-2
 
 
 def host64(t):
@@ -70,12 +67,8 @@ def draw(i, bf16_only=False, prefix=True):
     """Draw i: a forward case, the prefix that builds its initial state (or None) and a
     chunk size.  bf16_only keeps to the shapes of the decay, factor, backward and flash
     paths (d = 64, bf16 inputs, C = 64); prefix=False draws no prefix (a path without an
-    initial state).  Ill-conditioned draws are rejected and redrawn."""
-    for attempt in range(64):
-        case, pre, chunk = _draw(i, attempt, bf16_only, prefix)
-        if gate_ratio(case, pre) >= MIN_RATIO:
-            return case, pre, chunk
-    raise RuntimeError(f"no well-conditioned draw for {i}")
+    initial state).  No draw is rejected, however ill-conditioned its gate."""
+    return _draw(i, 0, bf16_only, prefix)
 
 
 def prefix_state(case, pre):
@@ -107,10 +100,10 @@ def gate_ratio(case, pre):
 
 
 def test_draws_span_the_shapes():
-    """The draws (host only): well-conditioned, and between them both head widths, both
-    input dtypes, every chunk size, runs with and without a prefix, and a one-token run."""
+    """The draws (host only): between them both head widths, both input dtypes, every chunk
+    size, runs with and without a prefix, a one-token run, and ill-conditioned gates (the
+    draws a bar on the conditioning would have rejected are taken as drawn)."""
     draws = [draw(i) for i in range(NDRAWS)]
-    assert all(gate_ratio(c, p) >= MIN_RATIO for c, p, _ in draws)
     assert {c.d for c, _, _ in draws} == {16, 64}
     assert {c.dtype for c, _, _ in draws} == {"f32", "bf16"}
     assert {ch for _, _, ch in draws} == {32, 64, 128}
@@ -118,12 +111,12 @@ def test_draws_span_the_shapes():
     assert any(c.T == 1 for c, _, _ in draws)
     for i in range(NDRAWS):
         c, p, ch = draw(i, bf16_only=True)
-        assert (c.d, c.dtype, ch) == (64, "bf16", 64) and gate_ratio(c, p) >= MIN_RATIO
+        assert (c.d, c.dtype, ch) == (64, "bf16", 64)
         c, p, _ = draw(i, bf16_only=True, prefix=False)
-        assert p is None and gate_ratio(c, None) >= MIN_RATIO
-    for i in range(NDRAWS):
-        _, N, _, pre, step = decode_draw(i)
-        assert gate_ratio(step, pre) >= MIN_RATIO
+        assert p is None
+    ratios = [gate_ratio(c, p) for c, p, _ in draws] + [gate_ratio(*draw(i, True)[:2]) for i in range(NDRAWS)]
+    assert min(ratios) < 5e-3, min(ratios)
+    assert sum(r < 1e-2 for r in ratios) >= 3, sorted(ratios)[:5]
 
 
 def decode_draw(i):

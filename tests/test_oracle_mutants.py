@@ -63,3 +63,36 @@ def test_reference_mutant_is_clean():
 @pytest.mark.parametrize("kind", MUTANTS)
 def test_pins_catch_mutant(kind):
     assert pins.failing_pins(_mutant(kind)), f"no pin caught mutant {kind}"
+
+
+def _weights_mutant(kind):
+    """A copy of the oracle's weights with one planted mistake."""
+    def weights(q, k, P):
+        u = np.asarray(q, dtype=np.float64) @ np.asarray(P, dtype=np.float64).T
+        w = np.asarray(k, dtype=np.float64) @ np.asarray(P, dtype=np.float64).T
+        dot = (u @ u.T) if kind == "q_for_k" else u @ w.T
+        a = {"no_square": np.abs(dot), "raw_dot": dot, "cubed": np.abs(dot) ** 3}.get(kind, dot ** 2)
+        if kind == "strict_causal":
+            return np.tril(a, -1)
+        if kind == "anti_causal":
+            return np.triu(a)
+        return np.tril(a)
+    return weights
+
+
+WEIGHT_MUTANTS = ["no_square", "raw_dot", "cubed", "q_for_k", "strict_causal", "anti_causal"]
+
+
+@pytest.mark.parametrize("kind", WEIGHT_MUTANTS)
+def test_weight_pins_catch_mutant(kind, monkeypatch):
+    """The golden-scalar and normalised-row pins of O.weights fail on each planted mistake."""
+    from tests import test_oracle_pins as tp
+    monkeypatch.setattr(O, "weights", _weights_mutant(kind))
+    caught = 0
+    for check in (tp.test_weights_golden_scalar, tp.test_weights_normalised_rows_are_the_forward):
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except AssertionError:
+            caught += 1
+    assert caught, f"no weights pin caught mutant {kind}"

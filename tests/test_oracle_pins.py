@@ -71,6 +71,25 @@ def test_weights_nonnegative_and_causal():
     assert np.all(np.diag(a) > 0.0)
 
 
+def test_weights_golden_scalar():
+    """The hand-derived weights of the p = d = 1 example (tests/golden/scalar_p1.json):
+    a_ts = (P q_t * P k_s)^2 row by row, so |u.w| or u.w in place of the square, a strict
+    or reversed mask, or the query used for the key all fail."""
+    g = json.load(open(os.path.join(pins.GOLDEN, "scalar_p1.json")))
+    T = len(g["q"])
+    a = O.weights(np.array(g["q"]).reshape(T, 1), np.array(g["k"]).reshape(T, 1), np.array(g["P"]))
+    assert np.array_equal(a, np.array(g["a"]))
+
+
+def test_weights_normalised_rows_are_the_forward():
+    """Rows of the weights normalised to sum 1, times V, give the forward's y, which its own
+    pins fix independently (convex gate, brute-force recurrence, hand-derived values)."""
+    q, k, v, P = pins.rand_case(22, T=40, d=6, p=5, dv=3)
+    a = O.weights(q[0, 0], k[0, 0], P[0])
+    y = (a @ v[0, 0]) / a.sum(1, keepdims=True)
+    assert pins.rel(y, O.forward_quadratic(q, k, v, P)[0, 0]) < 1e-12
+
+
 def test_final_state_brute_force():
     """S_T = sum_s phi(k_s) v_s^T by explicit per-token outer products ([TS-1])."""
     q, k, v, P = pins.rand_case(21, B=2, H=2, T=9, d=5, p=3, dv=4)

@@ -66,7 +66,9 @@ typedef enum {
   KATA_ERR_SHAPE = 2,        /* a size is negative / inconsistent / too large   */
   KATA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (p, d, dv, chunk, dtype) */
   KATA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
-  KATA_ERR_LAUNCH = 5        /* a kernel launch failed                          */
+  KATA_ERR_LAUNCH = 5,       /* a kernel launch failed                          */
+  KATA_ERR_SCRATCH = 6       /* kata_forward_noalloc: the problem needs more scratch
+                                than its fixed device buffer holds                */
 } kata_status;
 
 /* Storage (and compute) type of tensors.
@@ -74,7 +76,7 @@ typedef enum {
  *    operand is a hi/lo pair of bf16 (about 16 significant bits).  With bfloat16 q, k, v the
  *    projections u = Pq, w = Pk enter the score tiles as hi/lo pairs and the features
  *    phi(k), phi(q) and the published state H are single bf16 (8 significant bits).
- *  KATA_BF16_HILO (in_dtype of kata_forward only): bfloat16
+ *  KATA_BF16_HILO (in_dtype of kata_forward and kata_forward_noalloc only): bfloat16
  *    storage like KATA_BF16, but phi(k), phi(q) and H also enter the matrix cores as hi/lo
  *    pairs.  For output gates that are far from well conditioned while keys are read
  *    through a state: where den_t = sum_s (u_t.w_s)^2 is a small fraction of
@@ -170,6 +172,32 @@ kata_status kata_forward_timed(const kata_forward_desc* desc,
                                float* ST, float* zT,
                                void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events);
+
+/* kata_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops and harnesses that forbid hipMalloc.  It computes exactly
+ * what kata_forward computes, with the same kernels, leaf plan and arguments (results are
+ * bit for bit those of kata_forward), but takes no workspace: the leaf states live in a
+ * device array inside the library, KATA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, set up
+ * when the library is first used on that GPU and held until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *   Limit: kata_forward_workspace_bytes(desc) must be at most KATA_NOALLOC_SCRATCH_BYTES,
+ *   else KATA_ERR_SCRATCH is returned before anything is enqueued (the long-context,
+ *   mid-size and 340M-layer shapes need 27 to 29 MiB; B*H = 4096 sequences of 8192
+ *   tokens need 465 MB and are rejected).
+ *   Concurrency: every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents (nothing in it needs clearing: every leaf state is written before it
+ *   is read).  Calls whose work overlaps on one GPU (different streams, or host threads
+ *   enqueueing concurrently without ordering) race on it and give undefined results;
+ *   calls ordered on one stream are safe.
+ * Other arguments, layouts, ownership and errors as for kata_forward. */
+#define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kata_status kata_forward_noalloc(const kata_forward_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const float* P,
+                                 const float* S0, const float* z0,
+                                 void* y,
+                                 float* ST, float* zT,
+                                 void* stream);
 
 /* Flash-style O(T^2) forward (no state): the first operating point of the
  * hardware section of the gist.science summary of arXiv 2607.17419 (section 2.3),

@@ -15,7 +15,9 @@ import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 
-KATA_OK, KATA_ERR_NULL, KATA_ERR_SHAPE, KATA_ERR_UNSUPPORTED, KATA_ERR_WORKSPACE, KATA_ERR_LAUNCH = range(6)
+KATA_OK, KATA_ERR_NULL, KATA_ERR_SHAPE, KATA_ERR_UNSUPPORTED, KATA_ERR_WORKSPACE, KATA_ERR_LAUNCH, \
+    KATA_ERR_SCRATCH = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20     # KATA_NOALLOC_SCRATCH_BYTES
 KATA_F32, KATA_BF16, KATA_BF16_HILO = 0, 1, 2
 KATA_SCAN_ASSOC, KATA_SCAN_SEQUENTIAL = 0, 1
 FEATURE_LAYOUTS = {"full": 0, "packed_key": 1, "packed_query": 2}
@@ -81,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     lib.kata_forward_timed.restype = ci
     lib.kata_forward_timed.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                        ctypes.POINTER(vp)]
+    lib.kata_forward_noalloc.restype = ci
+    lib.kata_forward_noalloc.argtypes = [ctypes.POINTER(ForwardDesc)] + [vp] * 10
     lib.kata_flash_workspace_bytes.restype = ci
     lib.kata_flash_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
     lib.kata_flash_forward.restype = ci
@@ -283,6 +287,47 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, 
                                 _ptr(y), _ptr(ST), _ptr(zT), _ptr(workspace),
                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), sh, evarr)
     _check(st, "kata_forward")
+    return (y, ST, zT) if return_state else y
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, chunk: int = 64, *,
+                    S0: Optional[torch.Tensor] = None, z0: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, return_state: bool = False, scan: str = "assoc",
+                    scan_leaf: int = 0, y: Optional[torch.Tensor] = None, ST: Optional[torch.Tensor] = None,
+                    zT: Optional[torch.Tensor] = None, stream=None, precise: bool = False):
+    """kata_forward_noalloc: the forward of ``forward`` with the library's fixed scratch
+    buffer as workspace (no device memory passed in or allocated by the call).  With y (and
+    ST, zT when return_state) passed in, this function allocates nothing either."""
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (B, H, T, d), device=dev)
+    _need(k, "k", (B, H, T, d), q.dtype, dev)
+    _need(v, "v", (B, H, T, dv), q.dtype, dev)
+    _need(P, "P", (H, P_DIM, d), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if (S0 is None) != (z0 is None):
+        raise ValueError("S0 and z0 go together")
+    if S0 is not None:
+        _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        _need(z0, "z0", (B, H, P_DIM * P_DIM), torch.float32, dev)
+    desc = make_desc(B, H, T, d, dv, chunk, _in_code(q.dtype, precise), _dtype_code(out_dtype), scan, scan_leaf)
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", (B, H, T, dv), out_dtype, dev)
+    if return_state:
+        if ST is None:
+            ST = torch.empty((B, H, P_DIM * P_DIM, dv), dtype=torch.float32, device=dev)
+        if zT is None:
+            zT = torch.empty((B, H, P_DIM * P_DIM), dtype=torch.float32, device=dev)
+        _need(ST, "ST", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
+        _need(zT, "zT", (B, H, P_DIM * P_DIM), torch.float32, dev)
+    else:
+        ST = zT = None
+    st = _lib().kata_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(S0), _ptr(z0),
+                                     _ptr(y), _ptr(ST), _ptr(zT), _stream_handle(stream, dev))
+    _check(st, "kata_forward_noalloc")
     return (y, ST, zT) if return_state else y
 
 

@@ -12,6 +12,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kata.h"
 #include "kata_bwd.h"
@@ -149,6 +150,30 @@ Plan make_plan(const kata_forward_desc* d) { return make_plan(d, slots_for(d)); 
 
 kata_status launch_status() {
   return hipGetLastError() == hipSuccess ? KATA_OK : KATA_ERR_LAUNCH;
+}
+
+// ---- the scratch buffer of kata_forward_noalloc -------------------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory, so kernels get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+__device__ __align__(256) unsigned char scratch[KATA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or nullptr on failure.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 // Kernels whose LDS footprint exceeds the default 64 KiB dynamic limit need the
@@ -635,6 +660,9 @@ const char* kata_status_string(kata_status s) {
     case KATA_ERR_UNSUPPORTED: return "KATA_ERR_UNSUPPORTED: p, d, dv, chunk, dtype or scan mode not supported";
     case KATA_ERR_WORKSPACE: return "KATA_ERR_WORKSPACE: workspace missing or too small";
     case KATA_ERR_LAUNCH: return "KATA_ERR_LAUNCH: a kernel launch failed";
+    case KATA_ERR_SCRATCH:
+      return "KATA_ERR_SCRATCH: the problem needs more than the KATA_NOALLOC_SCRATCH_BYTES (64 MiB) scratch buffer "
+             "of kata_forward_noalloc";
   }
   return "KATA: unknown status";
 }
@@ -682,6 +710,22 @@ kata_status kata_forward(const kata_forward_desc* desc, const void* q, const voi
                          const float* P, const float* S0, const float* z0, void* y, float* ST, float* zT,
                          void* workspace, size_t workspace_bytes, void* stream) {
   return kata_forward_timed(desc, q, k, v, P, S0, z0, y, ST, zT, workspace, workspace_bytes, stream, nullptr);
+}
+
+kata_status kata_forward_noalloc(const kata_forward_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* P, const float* S0, const float* z0, void* y, float* ST, float* zT,
+                                 void* stream) {
+  kata_status s = validate(desc);
+  if (s != KATA_OK) return s;
+  if ((S0 == nullptr) != (z0 == nullptr)) return KATA_ERR_NULL;
+  if ((ST == nullptr) != (zT == nullptr)) return KATA_ERR_NULL;
+  const Plan pl = make_plan(desc);
+  if (pl.ws_bytes > KATA_NOALLOC_SCRATCH_BYTES) return KATA_ERR_SCRATCH;
+  if (desc->B * desc->H == 0) return KATA_OK;
+  if (desc->T > 0 && (!q || !k || !v || !P || !y)) return KATA_ERR_NULL;
+  void* ws = nullptr;
+  if (desc->T > 0 && !(ws = scratch_address())) return KATA_ERR_LAUNCH;
+  return kata_forward_timed(desc, q, k, v, P, S0, z0, y, ST, zT, ws, KATA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 kata_status kata_flash_workspace_bytes(const kata_forward_desc* desc, size_t* bytes) {

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 def test_abi_version_and_status_strings():
     lib = _lib_or_skip()
     assert lib.kata_abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert lib.kata_status_string(s).decode().startswith("KATA_")
     assert b"unknown" in lib.kata_status_string(99)
 
@@ -375,3 +375,20 @@ def test_decode_factors_validation():
     assert lib.kata_decode_step_factors(4, 16, 64, 32, 16, 2, 0, 1, 0, *ptrs, None) == Bd.KATA_ERR_UNSUPPORTED
     assert lib.kata_decode_step_factors(4, 16, 64, 64, 16, 2, 1, 1, 0, *ptrs[:6], None, None) == Bd.KATA_ERR_NULL
     assert lib.kata_decode_step_factors(0, 16, 64, 64, 16, 3, 0, 1, 0, *([None] * 7), None) == Bd.KATA_OK
+
+
+def test_noalloc_refuses_sizes_past_its_buffer():
+    """kata_forward_noalloc: 4096 sequences of 8192 tokens need 465 MB of leaf states, more
+    than its 64 MiB scratch buffer: KATA_ERR_SCRATCH before anything runs (no pointers are
+    read, no device is touched); a shape that fits passes that check and then asks for its
+    tensors (KATA_ERR_NULL here, with none given)."""
+    lib = _lib_or_skip()
+    d = Bd.make_desc(256, 16, 8192, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    st, n = _ws(d)
+    assert st == 0 and n > Bd.NOALLOC_SCRATCH_BYTES
+    nulls = [None] * 9
+    assert lib.kata_forward_noalloc(ctypes.byref(d), *nulls, None) == Bd.KATA_ERR_SCRATCH
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    st, n = _ws(d)
+    assert st == 0 and 0 < n <= Bd.NOALLOC_SCRATCH_BYTES
+    assert lib.kata_forward_noalloc(ctypes.byref(d), *nulls, None) == Bd.KATA_ERR_NULL

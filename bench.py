@@ -414,7 +414,7 @@ def bench_decode(args):
     if delta and G > 1:
         print("bench.py --decode takes --delta or --factors, not both", file=sys.stderr)
         sys.exit(2)
-    dc = I.make_decode(device=dev)
+    dc = I.make_decode(device=dev, N=args.streams, T_prefill=args.prefill)
     N, H, d, dv, T0, steps = dc.N, dc.H, dc.d, dc.dv, dc.T_prefill, dc.steps
     prefill = None
     if delta:
@@ -502,7 +502,8 @@ def bench_decode(args):
     mode = ("decode_delta" if delta else
             (f"decode_{'m' if fmode == 'concat' else 'sigma'}{G}" if G > 1 else "decode")) + ("_packed" if packed else "")
     src = path_hash(mode)
-    traffic = mode_traffic(mode, kernel.split(" ")[0])
+    # recorded counters are for the decode workload itself (256 streams)
+    traffic = mode_traffic(mode, kernel.split(" ")[0]) if N == 256 else None
     rows = 256 * (G if (G > 1 and fmode == "concat") else 1)
     prefill_fn = "kata_forward_delta" if delta else ("kata_forward_factors" if G > 1 else "kata_forward")
     state_desc = (f"packed symmetric fp32 state [{N},{H},{rows * 136 // 256},{dv}]{'' if delta else ' + z'} "
@@ -515,7 +516,8 @@ def bench_decode(args):
                 + (f", {G} PSD factors per head (P [16,{G},16,64])" if G > 1 else ""))
     result = {
         "metric": (DELTA_DECODE_METRIC if delta else
-                   (DECODE_METRIC.replace("KATA decode", f"{fname.strip()} decode", 1) if G > 1 else DECODE_METRIC)),
+                   (DECODE_METRIC.replace("KATA decode", f"{fname.strip()} decode", 1) if G > 1 else DECODE_METRIC)
+                   ).replace("256 streams", f"{N} streams").replace("8192-token", f"{T0}-token"),
         "value": N * steps / (total_ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": 0, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -930,6 +932,12 @@ def main():
                     help="KATA-Mg: time kata_forward_factors with this many concatenated PSD factors")
     ap.add_argument("--factor-mode", default="concat", choices=("concat", "sum"),
                     help="with --factors: concatenated (KATA-Mg) or summed (KATA-Sigma-g) factors")
+    ap.add_argument("--streams", type=int, default=None,
+                    help="with --decode: streams (default 256, the decode workload's); 1024 makes the state "
+                         "4.3x the 256 MB last-level cache")
+    ap.add_argument("--prefill", type=int, default=None,
+                    help="with --decode: prefill tokens per stream (default 8192; the step's cost does not "
+                         "depend on it)")
     ap.add_argument("--packed", action="store_true",
                     help="with --decode: the step on the packed symmetric state (kata_decode_step_packed)")
     ap.add_argument("--delta", action="store_true",

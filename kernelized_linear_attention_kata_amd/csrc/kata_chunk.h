@@ -794,6 +794,44 @@ __device__ __forceinline__ Op4<true> score_operand(const float* row4) {
   return make4<true>(xv);
 }
 
+// The gated output row of token t: lane (t, g) holds O[nb][r] = column 16nb + 4g + r.
+// bf16 rows go out as two 16-byte stores per lane: for each pair of column blocks
+// (nb, nb + 1) one v_permlane16_swap per element between the lanes g and g ^ 1 (the two
+// 16-lane rows of each 32-lane half) leaves the even lane columns 4g .. 4g + 7 of block nb
+// and the odd lane columns 16 + 4(g - 1) .. 16 + 4g + 3 of block nb + 1, i.e. eight
+// consecutive columns per lane (8-byte stores of four columns take about 5% longer for
+// the whole intra pass).  Other shapes store the four columns of each block directly.
+template <typename T> struct IsBf16 { static constexpr bool value = false; };
+template <> struct IsBf16<bf16> { static constexpr bool value = true; };
+
+template <class S, typename TOut>
+__device__ __forceinline__ void store_row(const f32x4 (&O)[S::NB], float inv, __amdgpu_buffer_rsrc_t ry,
+                                          int row0, int g) {
+  if constexpr (IsBf16<TOut>::value && S::NB % 2 == 0) {
+#pragma unroll
+    for (int p = 0; p < S::NB / 2; ++p) {
+      bf16x8 out;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(O[2 * p][r] * inv),
+                                                         __float_as_uint(O[2 * p + 1][r] * inv), false, false);
+        out[r] = (bf16)__uint_as_float(sw[0]);
+        out[4 + r] = (bf16)__uint_as_float(sw[1]);
+      }
+      const int col = 32 * p + 8 * (g >> 1) + 16 * (g & 1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, out), ry, (row0 + col) * 2, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = O[nb][r] * inv;
+      Store4<TOut>::st(ry, (row0 + nb * 16 + 4 * g) * (int)sizeof(TOut), o);
+    }
+  }
+}
+
 // Readout + intra tile + gate for one 16-token M-block mb of the chunk; writes y.
 // Everything is computed transposed, O^T = H^T phi(Q)^T + V^T (A o A o M)^T, by
 // feeding the same fragments to the MFMA in swapped operand order: lane (t, g) then
@@ -931,14 +969,7 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   den = row_pair_sum<32>(den);
   // output gate: y = O / den (0 where the denominator is 0); v_rcp_f32 is within 1 ulp
   const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-  const int row = (t0 + t) * S::DV + 4 * g;
-#pragma unroll
-  for (int nb = 0; nb < S::NB; ++nb) {
-    f32x4 o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = O[nb][r] * inv;
-    Store4<TOut>::st(rs.y, (row + nb * 16) * (int)sizeof(TOut), o);
-  }
+  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, g);
 }
 
 // ---- the same three steps, separated -------------------------------------------------
@@ -1071,14 +1102,7 @@ __device__ __forceinline__ void gate_store(const f32x4 (&O)[S::NB], float den, c
   den = row_pair_sum<16>(den);
   den = row_pair_sum<32>(den);
   const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-  const int row = (t0 + t) * S::DV + 4 * g;
-#pragma unroll
-  for (int nb = 0; nb < S::NB; ++nb) {
-    f32x4 o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = O[nb][r] * inv;
-    Store4<TOut>::st(rs.y, (row + nb * 16) * (int)sizeof(TOut), o);
-  }
+  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, g);
 }
 
 // grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.  DECAY:

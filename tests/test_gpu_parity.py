@@ -446,3 +446,17 @@ def test_decode_matches_chunked_forward():
     # from bf16-rounded features (fp32 accumulation): agreement to the bf16 bar
     assert slice_rel(S.cpu().numpy(), ST.cpu().numpy()) <= 2e-2
     assert slice_rel(z.cpu().numpy(), zT.cpu().numpy()) <= 2e-2
+
+
+@pytest.mark.parametrize("name,T,chunk", [("mid", 200, 64), ("mid", 333, 32), ("mid", 77, 128), ("tiny", 130, 64),
+                                          ("mid", 4096, 64)])
+def test_bf16_output_is_the_rounded_fp32_output(name, T, chunk):
+    """y stored as bf16 is exactly the fp32 y rounded to nearest even: both leave the same
+    gated tile, and the bf16 rows (written two 16-byte pieces per lane after a lane-pair
+    exchange) must land every column of every token in its place, ragged tails included."""
+    case = I.make_forward(name, B=2, H=3, T=T, seed=170, dtype="bf16")
+    q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
+    y32 = kata.forward(q, k, v, P, chunk=chunk, out_dtype=torch.float32)
+    y16 = kata.forward(q, k, v, P, chunk=chunk, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y32.to(torch.bfloat16))

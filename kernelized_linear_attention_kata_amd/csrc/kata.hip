@@ -241,7 +241,7 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, DECAY>), grid, dim3(256), smem_state, st, e0, nullptr, 0,
-                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks, lam, dec);
+                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, pl.leaf * S::C, lam, dec);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int G = scan_segments(pl);
   const dim3 sgrid = scan_grid(pl, G, bh);
@@ -382,8 +382,7 @@ kata_status run_backward(const kata_forward_desc* d, const BwdLayout& L, const v
   const bf16* vb = (const bf16*)v;
   // forward prefix states at every leaf start
   hipExtLaunchKernelGGL((kata_chunk_state<S, bf16, false>), grid, dim3(256), S::SMEM_STATE, st, e[0], nullptr, 0, kb,
-                        vb, P, wsf, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks, (const float*)nullptr,
-                        (float*)nullptr);
+                        vb, P, wsf, d->T, (int)d->H, pl.leaf * S::C, (const float*)nullptr, (float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e[1], nullptr, 0, wsf, pl.n_leaf, (int)pl.E, 64, G,
                         S0, z0, (float*)nullptr, (float*)nullptr, 0, (const float*)nullptr);
@@ -496,7 +495,7 @@ kata_status run_forward_mg(const kata_forward_desc* d, const Plan& pl, const voi
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, false, G>), dim3((unsigned)pl.n_leaf, (unsigned)(bh * G)),
                         dim3(256), smem_state, st, e0, nullptr, 0, (const TIn*)k, (const TIn*)v, P, ws, d->T,
-                        (int)d->H, (int)pl.leaf, pl.n_chunks, (const float*)nullptr, (float*)nullptr);
+                        (int)d->H, pl.leaf * S::C, (const float*)nullptr, (float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int segs = scan_segments(pl);
   hipExtLaunchKernelGGL(kata_state_scan, scan_grid(pl, segs, bh * G), dim3(256), 0, st, e1, nullptr, 0, ws,
@@ -522,7 +521,7 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   const dim3 grid((unsigned)pl.n_leaf, (unsigned)bh);
   hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, false, G, true>), grid, dim3(256), smem_state, st, e0, nullptr, 0,
-                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, (int)pl.leaf, pl.n_chunks,
+                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, pl.leaf * S::C,
                         (const float*)nullptr, (float*)nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   const int segs = scan_segments(pl);

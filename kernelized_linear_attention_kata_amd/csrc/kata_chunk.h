@@ -575,7 +575,7 @@ __device__ __forceinline__ void stage_keys(const ChunkIn<S, TIn>& r, const bf16*
 template <class S, typename TIn, bool DECAY = false, int G = 1, bool SUMG = false>
 __global__ void __launch_bounds__(256, S::OCC_STATE)
 kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ P,
-                 float* __restrict__ ws, int64_t T, int H, int leaf_chunks, int64_t n_chunks,
+                 float* __restrict__ ws, int64_t T, int H, int64_t part_tokens,
                  const float* __restrict__ lam, float* __restrict__ dec) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
@@ -590,13 +590,15 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   constexpr int VG = SUMG ? 1 : G;        // workspace rows per sequence
   const int64_t bh = blockIdx.y / VG;    // sequence; blockIdx.y is the workspace row
   const int h = (int)(bh % H);
-  const int64_t leaf = blockIdx.x;
-  const int64_t c0 = leaf * leaf_chunks;
-  const int nch = (int)min<int64_t>(leaf_chunks, n_chunks - c0);
-  const int64_t base_tok = bh * T;
+  const int64_t part = blockIdx.x;
+  // the part's tokens [tb, tb + len) of the sequence; loads past them read zeros
+  const int64_t tb = min<int64_t>(part * part_tokens, T);
+  const int len = (int)(min<int64_t>(tb + part_tokens, T) - tb);
+  const int nch = (len + S::C - 1) / S::C;
+  const int64_t base_tok = bh * T + tb;
   __amdgpu_buffer_rsrc_t rl;
-  if constexpr (DECAY) rl = make_rsrc(lam + base_tok, T * 4);
-  float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the leaf's end
+  if constexpr (DECAY) rl = make_rsrc(lam + base_tok, (int64_t)len * 4);
+  float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the part's end
 
   if (wave == 0) write_P<S>(Pf, P, G == 1 ? h : (SUMG ? h * G : h * G + (int)(blockIdx.y % G)), lane);
   if constexpr (SUMG) {
@@ -611,19 +613,18 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   StateAcc<S> st;
   state_zero<S>(st);
   SeqRsrc rs;
-  rs.k = make_rsrc(k + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
-  rs.v = make_rsrc(v + base_tok * S::DV, T * S::DV * (int64_t)sizeof(TIn));
-  const int tc0 = (int)(c0 * S::C);
+  rs.k = make_rsrc(k + base_tok * S::DIN, (int64_t)len * S::DIN * (int64_t)sizeof(TIn));
+  rs.v = make_rsrc(v + base_tok * S::DV, (int64_t)len * S::DV * (int64_t)sizeof(TIn));
   // Inputs are prefetched DEPTH chunks ahead in DEPTH register buffers: the loads of
   // chunk c+DEPTH are in flight while chunk c is processed.  Loads past the leaf
   // read zeros or unused rows.  (Two buffers measured no faster: the kernel is not
   // limited by the prefetch distance, and the extra registers cost occupancy.)
   constexpr int DEPTH = 1;
   // Chunks are summed last to first: the sum does not depend on the order, and the
-  // data read last (the leaf's first chunks) is what kata_chunk_intra reads first,
-  // so part of it is still in the last-level cache.  The prefetch past the leaf's
-  // last chunk reads at T, outside the buffer (zeros, no memory traffic).
-  auto chunk_t0 = [&](int c) { return tc0 + (nch - 1 - c) * S::C; };
+  // data read last (the part's first chunks) is what kata_chunk_intra reads first,
+  // so some of it is still in the last-level cache.  The prefetch past the part's
+  // last chunk reads at len, outside the buffer (zeros, no memory traffic).
+  auto chunk_t0 = [&](int c) { return (nch - 1 - c) * S::C; };
   ChunkIn<S, TIn> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, chunk_t0(i), wave, lane);
@@ -640,14 +641,14 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
                            reinterpret_cast<float*>(xb), reinterpret_cast<bf16*>(xb + S::WACC_BYTES), wave, lane);
       }
     }
-    load_chunk<S, TIn, false>(cur, rs, c + DEPTH < nch ? chunk_t0(c + DEPTH) : (int)T, wave, lane);
+    load_chunk<S, TIn, false>(cur, rs, c + DEPTH < nch ? chunk_t0(c + DEPTH) : len, wave, lane);
     if constexpr (DECAY) {
       float Lc;
       const float l = chunk_cumlog(lam_next, lane, Lc);
       if (wave == 0) es[lane] = fdec * __expf(Lc - l);
       fdec *= __expf(Lc);
       lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rl, ((c + 1 < nch ? chunk_t0(c + 1) : (int)T) + lane) * 4, 0, 0));
+          rl, ((c + 1 < nch ? chunk_t0(c + 1) : len) + lane) * 4, 0, 0));
     }
     __syncthreads();
     if constexpr (DECAY) state_update_decay<S>(st, Wacc, es, vf_hi, vf_lo, wave, wave == 0, lane);
@@ -670,8 +671,8 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
 #pragma unroll
   for (int i = 0; i + 1 < DEPTH; ++i)   // fewer than DEPTH chunks left: static buffer index
     if (c + i < nch) step(buf[i], c + i);
-  // write the leaf state (tile-native layout) and Z
-  float* out = ws + ((int64_t)blockIdx.y * gridDim.x + leaf) * S::E;
+  // write the part's state (tile-native layout) and Z
+  float* out = ws + ((int64_t)blockIdx.y * gridDim.x + part) * S::E;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int delta = wave + 4 * j;
@@ -686,7 +687,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   }
   if (wave == 0) *reinterpret_cast<f32x4*>(out + DPACK * S::DV + lane * 4) = st.Z;
   if constexpr (DECAY) {
-    if (tid == 0) dec[(int64_t)blockIdx.y * gridDim.x + leaf] = fdec;
+    if (tid == 0) dec[(int64_t)blockIdx.y * gridDim.x + part] = fdec;
   }
 }
 
@@ -764,12 +765,20 @@ __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int
   st.Z = zrole ? *reinterpret_cast<const f32x4*>(in + DPACK * S::DV + lane * 4) : zero4();
 }
 
+// y is written once and not read again by the pass, so its stores are non-temporal
+// (cache policy NT): the lines go out to memory instead of staying dirty in the caches,
+// where the next pass (the state pass of the next batch, in a stream of forwards) would
+// have to write them back while it streams its own reads.  Measured on the long shape,
+// the state pass that follows takes 102 us instead of 125 us; the intra pass itself
+// takes about 4 us longer.
+constexpr int Y_STORE_POLICY = 2;   // NT
+
 // Vector store of 4 consecutive outputs through the y buffer resource (stores past
 // the end of the sequence are dropped).
 template <typename TOut> struct Store4;
 template <> struct Store4<float> {
   static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int off, const f32x4& x) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, Y_STORE_POLICY);
   }
 };
 template <> struct Store4<bf16> {
@@ -777,7 +786,7 @@ template <> struct Store4<bf16> {
     bf16x4 b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) b[i] = (bf16)x[i];
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, b), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, b), r, off, 0, Y_STORE_POLICY);
   }
 };
 
@@ -795,21 +804,25 @@ __device__ __forceinline__ Op4<true> score_operand(const float* row4) {
 }
 
 // The gated output row of token t: lane (t, g) holds O[nb][r] = column 16nb + 4g + r.
-// bf16 rows go out as two 16-byte stores per lane: for each pair of column blocks
-// (nb, nb + 1) one v_permlane16_swap per element between the lanes g and g ^ 1 (the two
-// 16-lane rows of each 32-lane half) leaves the even lane columns 4g .. 4g + 7 of block nb
-// and the odd lane columns 16 + 4(g - 1) .. 16 + 4g + 3 of block nb + 1, i.e. eight
-// consecutive columns per lane (8-byte stores of four columns take about 5% longer for
-// the whole intra pass).  Other shapes store the four columns of each block directly.
+// bf16 rows of 64 columns (128 bytes, one cache line) go out in whole lines: for each
+// pair of column blocks (nb, nb + 1) one v_permlane16_swap per element between the lanes
+// g and g ^ 1 (the two 16-lane rows of each 32-lane half) leaves the even lane columns
+// 4g .. 4g + 7 of block nb and the odd lane columns 16 + 4(g - 1) .. 16 + 4g + 3 of
+// block nb + 1, i.e. eight consecutive columns per lane; a DPP exchange between the
+// lanes t and t ^ 8 of each 16-lane row then gives each of the two 16-byte stores eight
+// whole token rows (tokens 0..7 of the M-block, then 8..15).  Stores of half lines take
+// about 4% longer for the whole intra pass with the NT policy.  Other shapes store the
+// four columns of each block directly.
 template <typename T> struct IsBf16 { static constexpr bool value = false; };
 template <> struct IsBf16<bf16> { static constexpr bool value = true; };
 
 template <class S, typename TOut>
 __device__ __forceinline__ void store_row(const f32x4 (&O)[S::NB], float inv, __amdgpu_buffer_rsrc_t ry,
-                                          int row0, int g) {
-  if constexpr (IsBf16<TOut>::value && S::NB % 2 == 0) {
+                                          int row0, int t, int g) {
+  if constexpr (IsBf16<TOut>::value && S::NB == 4) {
+    i32x4 half[2];   // columns 32p + 8(g >> 1) + 16(g & 1) .. + 7 of token t
 #pragma unroll
-    for (int p = 0; p < S::NB / 2; ++p) {
+    for (int p = 0; p < 2; ++p) {
       bf16x8 out;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -818,9 +831,23 @@ __device__ __forceinline__ void store_row(const f32x4 (&O)[S::NB], float inv, __
         out[r] = (bf16)__uint_as_float(sw[0]);
         out[4 + r] = (bf16)__uint_as_float(sw[1]);
       }
-      const int col = 32 * p + 8 * (g >> 1) + 16 * (g & 1);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, out), ry, (row0 + col) * 2, 0, 0);
+      half[p] = __builtin_bit_cast(i32x4, out);
     }
+    // lane t < 8 keeps columns 0..31 of token t and takes columns 0..31 of token t + 8;
+    // lane t >= 8 takes columns 32..63 of token t - 8 and keeps columns 32..63 of token t
+    // (DPP row_ror:8 swaps the two 8-lane halves of each 16-lane row)
+    const bool lo = (t & 15) < 8;
+    i32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rcv = __builtin_amdgcn_update_dpp(0, lo ? half[1][i] : half[0][i], 0x128, 0xf, 0xf, false);
+      a[i] = lo ? half[0][i] : rcv;
+      b[i] = lo ? rcv : half[1][i];
+    }
+    const int col = (lo ? 0 : 32) + 8 * (g >> 1) + 16 * (g & 1);
+    const int rowa = row0 - (lo ? 0 : 8 * S::DV);   // token t & ~8, then t | 8
+    __builtin_amdgcn_raw_buffer_store_b128(a, ry, (rowa + col) * 2, 0, Y_STORE_POLICY);
+    __builtin_amdgcn_raw_buffer_store_b128(b, ry, (rowa + 8 * S::DV + col) * 2, 0, Y_STORE_POLICY);
   } else {
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) {
@@ -969,7 +996,7 @@ __device__ __forceinline__ void chunk_outputs(int mb, const float* Us, const flo
   den = row_pair_sum<32>(den);
   // output gate: y = O / den (0 where the denominator is 0); v_rcp_f32 is within 1 ulp
   const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, g);
+  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, t, g);
 }
 
 // ---- the same three steps, separated -------------------------------------------------
@@ -1102,7 +1129,7 @@ __device__ __forceinline__ void gate_store(const f32x4 (&O)[S::NB], float den, c
   den = row_pair_sum<16>(den);
   den = row_pair_sum<32>(den);
   const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, g);
+  store_row<S, TOut>(O, inv, rs.y, (t0 + t) * S::DV, t, g);
 }
 
 // grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.  DECAY:

@@ -63,14 +63,17 @@ KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_chunk_intra")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
-def time_steps(torch, step, stream, steps, n_events, stamp):
+def time_steps(torch, step, stream, steps, n_events, stamp, every=1):
     """Run exactly `steps` calls step(i, events) on `stream` between two device
     synchronisations.  Only the events at the indices in `stamp` reach the launches (the
-    rest are None): each launch that stamps an event costs a few microseconds of dispatch
-    gap, so the timed steps stamp only the dominant kernel.  Returns (ms per step, wall
-    seconds, the per-step event lists)."""
-    evs = [[torch.cuda.Event(enable_timing=True) if j in stamp else None for j in range(n_events)]
-           for _ in range(steps)]
+    rest are None), and only on the steps i with i % every == 0: each launch that stamps an
+    event costs a few microseconds of dispatch gap (on the long forward, stamping the
+    intra launch's start and end on every step measured 0.342 ms per step against 0.331 ms
+    with no stamp).  Returns (ms per step, wall seconds, the event lists of the stamped
+    steps)."""
+    stamped = [i % every == 0 for i in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) if (j in stamp and stamped[i]) else None for j in range(n_events)]
+           for i in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for e in [t0, t1] + [e for es in evs for e in es if e is not None]:
         e.record(stream)     # torch creates the HIP event on its first record: do it before timing
@@ -81,7 +84,7 @@ def time_steps(torch, step, stream, steps, n_events, stamp):
         step(i, evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0, evs
+    return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0, [es for i, es in enumerate(evs) if stamped[i]]
 
 
 def mean_interval(evs, a, b):
@@ -98,11 +101,17 @@ def kernel_breakdown(torch, step, stream, steps, names):
     return {name: mean_interval(evs, j, j + 1) for j, name in enumerate(names)}
 
 
+# In the timed steps the dominant kernel's launch stamps its own start and end on every
+# STAMP_EVERY-th step (steps 0, 4, 8, ...: 5 of the default 20), and the roofline takes the
+# mean duration of those launches; the other steps run without events.
+STAMP_EVERY = 4
+
+
 def timed_dominant(torch, step, stream, steps, names, dominant):
     """The timed steps: (ms per step, wall seconds, the dominant kernel's mean duration in
-    ms, measured on the same steps from the events its launch stamps)."""
+    ms, measured on the stamped ones of the same steps from the events its launch stamps)."""
     j = names.index(dominant)
-    ms_step, wall, evs = time_steps(torch, step, stream, steps, len(names) + 1, (j, j + 1))
+    ms_step, wall, evs = time_steps(torch, step, stream, steps, len(names) + 1, (j, j + 1), STAMP_EVERY)
     return ms_step, wall, mean_interval(evs, j, j + 1)
 
 
@@ -713,21 +722,36 @@ def bench_workload(args):
     warm_kernels = kernel_breakdown(torch, warm_step, stream, args.steps, KERNELS)
     warm_ms, wall_warm, _ = time_steps(torch, warm_step, stream, args.steps, len(KERNELS) + 1, ())
 
-    # flushed: every step after a 512 MB read-modify-write, all launches stamped
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
-    for es in evs:
-        for e in es:
-            e.record(stream)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        flush.add_(1.0)
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    flushed_ms = mean_interval(evs, 0, len(KERNELS))
+    # flushed: every step after a 512 MB read-modify-write (outside the events).  Three
+    # passes, each stamping only what it measures (a stamped launch costs a few us of
+    # dispatch gap): all launches for the per-kernel breakdown; the state pass's start and
+    # the intra pass's end for the step time (no stamp between them); the dominant
+    # kernel's start and end for its duration.
+    n_ev = len(KERNELS) + 1
+
+    def flushed_pass(stamp):
+        evs = [[torch.cuda.Event(enable_timing=True) if j in stamp else None for j in range(n_ev)]
+               for _ in range(args.steps)]
+        for es in evs:
+            for e in es:
+                if e is not None:
+                    e.record(stream)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            flush.add_(1.0)
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        return evs, time.perf_counter() - w0
+
+    evs, _ = flushed_pass(range(n_ev))
     flushed_kernels = {name: mean_interval(evs, j, j + 1) for j, name in enumerate(KERNELS)}
     dominant = max(flushed_kernels, key=flushed_kernels.get)
+    evs, wall = flushed_pass((0, n_ev - 1))
+    flushed_ms = mean_interval(evs, 0, n_ev - 1)
+    jd = KERNELS.index(dominant)
+    evs, _ = flushed_pass((jd, jd + 1))
+    dominant_ms = mean_interval(evs, jd, jd + 1)
 
     abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2)
     aflops = algorithmic_flops(B, H, T, d, dv, C)
@@ -740,7 +764,8 @@ def bench_workload(args):
                          "alg_TFLOPs": round(aflops[name] / (ms / 1e3) / 1e12, 2),
                          "mfma_frac": round(aflops[name] / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                          "alg_bytes": abytes[name], "alg_flops": aflops[name]}
-    achieved = abytes[dominant] / (flushed_kernels[dominant] / 1e3) / 1e9
+    kernels[dominant]["ms_timed_steps"] = round(dominant_ms, 4)
+    achieved = abytes[dominant] / (dominant_ms / 1e3) / 1e9
     mode = args.workload
     result = {
         "metric": WORKLOAD_METRIC.format(what=WORKLOAD_WHAT[args.workload]),

@@ -252,19 +252,41 @@ struct ProjP { Op8<true> f[S::KD]; };
 
 // The P fragments are loop-invariant and live in LDS rather than in registers:
 // Pf[kk][hi/lo][lane], 16 bytes each, written by one wave before the first chunk.
+// In two halves, so a kernel can issue the reads of P, then its first input loads, and
+// only then wait for P (the two latencies overlap): read_P_rows takes this lane's entries
+// of P into registers, store_P writes them as fragments.
 template <class S>
-__device__ __forceinline__ void write_P(bf16* Pf, const float* __restrict__ P, int h, int lane) {
+struct PRows { float x[S::KD][8]; };
+
+template <class S>
+__device__ __forceinline__ void read_P_rows(PRows<S>& r, const float* __restrict__ P, int h, int lane) {
   const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < S::KD; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r.x[kk][i] = proj_valid<S>(g) ? P[((int64_t)h * P_DIM + n) * S::DIN + proj_col<S>(g, kk, i)] : 0.f;
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void store_P(bf16* Pf, const PRows<S>& r, int lane) {
 #pragma unroll
   for (int kk = 0; kk < S::KD; ++kk) {
     float x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      x[i] = proj_valid<S>(g) ? P[((int64_t)h * P_DIM + n) * S::DIN + proj_col<S>(g, kk, i)] : 0.f;
+    for (int i = 0; i < 8; ++i) x[i] = r.x[kk][i];
     const Op8<true> f = make8<true>(x);
     *reinterpret_cast<bf16x8*>(Pf + ((2 * kk) * WAVE + lane) * 8) = f.hi;
     *reinterpret_cast<bf16x8*>(Pf + ((2 * kk + 1) * WAVE + lane) * 8) = f.lo;
   }
+}
+
+template <class S>
+__device__ __forceinline__ void write_P(bf16* Pf, const float* __restrict__ P, int h, int lane) {
+  PRows<S> r;
+  read_P_rows<S>(r, P, h, lane);
+  store_P<S>(Pf, r, lane);
 }
 
 template <class S>
@@ -600,7 +622,9 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   if constexpr (DECAY) rl = make_rsrc(lam + base_tok, (int64_t)len * 4);
   float fdec = 1.f;   // DECAY: decay from the end of the current chunk to the part's end
 
-  if (wave == 0) write_P<S>(Pf, P, G == 1 ? h : (SUMG ? h * G : h * G + (int)(blockIdx.y % G)), lane);
+  // P is read before the first chunk's loads and written to LDS after them (see store_P)
+  PRows<S> prow;
+  read_P_rows<S>(prow, P, G == 1 ? h : (SUMG ? h * G : h * G + (int)(blockIdx.y % G)), lane);
   if constexpr (SUMG) {
     if (wave == 0) {
 #pragma unroll
@@ -630,6 +654,7 @@ kata_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v, const flo
   for (int i = 0; i < DEPTH; ++i) load_chunk<S, TIn, false>(buf[i], rs, chunk_t0(i), wave, lane);
   float lam_next = 0.f;
   if constexpr (DECAY) lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (chunk_t0(0) + lane) * 4, 0, 0));
+  if (wave == 0) store_P<S>(Pf, prow, lane);
   __syncthreads();   // P fragments written
   auto step = [&](ChunkIn<S, TIn>& cur, int c) {
     stage_chunk<S, TIn, false>(cur, Pf, sel, nullptr, nullptr, Wacc, Wz, vf_hi, vf_lo, wave, lane);
@@ -1173,11 +1198,14 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   // goes to wave 0, whose M-block has the least intra-chunk work.
   const int tw = wave;
   const bool zrole = wave == 0;
-  if (wave == 0) write_P<S>(Pf, P, h, lane);
   const bf16x8 sel[2] = {column_selector(0, lane), column_selector(1, lane)};
+  // P, the leaf's prefix state and the first chunk's inputs are loaded in this order before
+  // any of them is waited for, so the three latencies overlap (loads complete in issue
+  // order: P is waited for with the state and chunk loads still in flight, and so on).
+  PRows<S> prow;
+  read_P_rows<S>(prow, P, h, lane);
   StateAcc<S> st;
   load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
-  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
 
   SeqRsrc rs;
   rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));
@@ -1187,6 +1215,8 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   const int tc0 = (int)(c0 * S::C);
   ChunkIn<S, TIn> cur;
   load_chunk<S, TIn, true>(cur, rs, tc0, tw, lane);
+  if (wave == 0) store_P<S>(Pf, prow, lane);
+  publish_state<S>(st, hx_hi, hx_lo, Zs, wave, zrole, lane);
   float lam_next = 0.f;
   if constexpr (DECAY) lam_next = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (tc0 + lane) * 4, 0, 0));
   __syncthreads();   // P fragments written

@@ -104,7 +104,12 @@ kata_state_scan(float* __restrict__ ws, int64_t n_leaf, int E, int dv, int G,
   const int ql = tid % QW, seg = tid / QW;
   const int64_t bh = blockIdx.y;
   const int e0 = (blockIdx.x * QW + ql) * 4;
-  const bool active = e0 < E;
+  // The quads of the unused packed slots (delta = 8, a >= 8: lanes 32..63 of the delta = 8
+  // tiles) are read with query weight 0 by the forward kernels, which is all they are
+  // used for, so the forward scan leaves them as the state pass wrote them (finite leaf
+  // sums); the reverse scan of the backward does them all.
+  const bool unused = !reverse && e0 < DPACK * dv && (e0 >> 8) >= 8 * (dv / 16) && (e0 & 255) >= 128;
+  const bool active = e0 < E && !unused;
   float* base = ws + bh * n_leaf * (int64_t)E + e0;
   const int64_t per_pass = (int64_t)SCAN_ROWS * G;
   const int lseg = (int)((n_leaf < per_pass ? n_leaf : per_pass) + G - 1) / G;

@@ -38,8 +38,9 @@ def lib():
 def test_forward_bytes_match_tensor_and_workspace_sizes(chunk):
     """The long-context workload: the state pass reads k and v and writes the leaf
     states; the intra pass reads q, k, v and the scanned leaf states and writes y; the
-    scan reads and writes the leaf states and writes the final state (S, z).  The leaf
-    states are exactly the library's forward workspace."""
+    scan reads and writes the leaf states but for their 8 * dv unused packed slots
+    (delta = 8, a >= 8) and writes the final state (S, z).  The leaf states are exactly
+    the library's forward workspace."""
     kata = lib()
     B, H, T, d, dv = 1, 16, 131072, 64, 64
     ws = kata.forward_workspace_bytes(B, H, T, d, dv, chunk)
@@ -52,7 +53,8 @@ def test_forward_bytes_match_tensor_and_workspace_sizes(chunk):
     final = nbytes(B, H, 256, dv, dtype=torch.float32) + nbytes(B, H, 256, dtype=torch.float32)
     assert got["kata_chunk_state"] == nbytes(B, H, T, d) + nbytes(B, H, T, dv) + ws
     assert got["kata_chunk_intra"] == qkv + ws + y
-    assert got["kata_state_scan"] == 2 * ws + final
+    unused = B * H * n_leaf * 8 * dv * 4
+    assert got["kata_state_scan"] == 2 * (ws - unused) + final
 
 
 def test_decay_and_factor_bytes():

@@ -60,7 +60,6 @@ DECAY_METRIC = "KATA decay-gated causal fwd tokens/sec at T=131072 + % of HBM pe
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 KERNELS = ("kata_chunk_state", "kata_state_scan", "kata_chunk_intra")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
 def time_steps(torch, step, stream, steps, n_events, stamp, every=1):
@@ -146,7 +145,7 @@ PATH_HEADERS = {"decay": ("kata_chunk.h",), "backward": ("kata_bwd.h",), "flash"
 
 
 def path_hash(mode: str) -> str:
-    if mode in ("forward", "forward_precise", "mid", "lm340m"):
+    if mode in ("forward", "forward_precise", "forward_seq", "mid", "lm340m"):
         return source_hash()
     if mode.startswith(("m", "sigma")):
         return source_hash(("kata_chunk.h",))
@@ -157,7 +156,8 @@ def path_hash(mode: str) -> str:
 
 def mode_traffic(mode: str, kernel: str):
     """Recorded HBM bytes per launch of ``kernel`` for a bench mode (None if not current)."""
-    return recorded_traffic(f"hbm_counters_{mode}.json", path_hash(mode), kernel)
+    fname = "hbm_counters.json" if mode == "forward" else f"hbm_counters_{mode}.json"
+    return recorded_traffic(fname, path_hash(mode), kernel)
 
 
 def recorded_traffic(fname: str, src: str, kernel: str):
@@ -1104,20 +1104,12 @@ def main():
     achieved = abytes[dominant] / (dom_ms / 1e3) / 1e9
     traffic = None
     mode = (f"{'sigma' if sg else 'm'}{G}" if G > 1
-            else ("decay" if args.decay else ("forward_precise" if args.precise else "forward")))
+            else ("decay" if args.decay else ("forward_precise" if args.precise else
+                                              ("forward_seq" if args.scan == "sequential" else "forward"))))
     src = path_hash(mode)
-    if mode != "forward":
-        traffic = mode_traffic(mode, dominant) if C == 64 else None
-        if mode == "forward_precise":
-            traffic = None
-    elif os.path.exists(COUNTERS_FILE):
-        try:
-            cnt = json.load(open(COUNTERS_FILE))
-            entry = cnt.get("kernels", {}).get(dominant)
-            if cnt.get("source_hash") == src and entry and cnt.get("chunk") == C and not args.decay and G == 1:
-                traffic = entry["hbm_bytes_per_launch"]
-        except (ValueError, KeyError):
-            traffic = None
+    # counters are recorded on the default plan (chunk 64, the library's leaf size)
+    if C == 64 and args.leaf == 0:
+        traffic = mode_traffic(mode, dominant)
 
     result = {
         "metric": ((SG_METRIC if sg else MG_METRIC).format(g=G) if G > 1

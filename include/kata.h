@@ -453,7 +453,9 @@ kata_status kata_forward_delta(const kata_forward_desc* desc,
  * E = T diag(beta)(V - K^ S), Y = Q^ S + (Q^K^^T o M) E (M: s <= t), S += K^^T E.  Same
  * definition and arguments as kata_forward_delta (exactly equal up to rounding), plus a
  * device workspace of kata_forward_delta_chunked_workspace_bytes bytes (normalised
- * projections and T per chunk: 9 KiB per 64 tokens and head), owned by the caller.
+ * projections and T per chunk: 9 KiB per 64 tokens and head; and one int per walk
+ * workgroup that keeps a sequence's workgroups within a few chunks of each other, so they
+ * share their inputs in L2), owned by the caller; calls that overlap on one workspace race.
  * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S) and
  * keeps the state's symmetric part packed (the antisymmetric part of S0, which no read
  * sees, reaches ST unchanged).  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),

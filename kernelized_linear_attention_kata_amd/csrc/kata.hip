@@ -539,9 +539,11 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
 // fragments (64 x 64 x 2 bf16 per chunk), each block 256-byte aligned.
 struct DeltaChunkLayout {
   int64_t n_chunks = 0;
-  size_t off_w = 0, off_t = 0, total = 0;
+  size_t off_w = 0, off_t = 0, off_prog = 0, total = 0;
 };
 
+// u^, w^ (fp32), T (hi/lo bf16 fragments), then the walk's progress counters (one int per
+// column-block workgroup).
 DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   DeltaChunkLayout L;
   const int64_t bh = d->B * d->H;
@@ -549,7 +551,8 @@ DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   const size_t uw = (size_t)bh * (size_t)L.n_chunks * kata::DC * P_DIM * sizeof(float);
   L.off_w = align256(uw);
   L.off_t = L.off_w + align256(uw);
-  L.total = L.off_t + (size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * 2 * sizeof(bf16);
+  L.off_prog = L.off_t + align256((size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * 2 * sizeof(bf16));
+  L.total = L.off_prog + (size_t)bh * (size_t)(d->dv / 16) * sizeof(int);
   return L;
 }
 
@@ -574,12 +577,13 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   float* U = (float*)ws;
   float* W = (float*)(ws + L.off_w);
   bf16* Tf = (bf16*)(ws + L.off_t);
+  int* prog = (int*)(ws + L.off_prog);
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr, e2 = ev ? ev[2] : nullptr;
   hipExtLaunchKernelGGL((kata::kata_delta_prep<TIn, DV>), dim3((unsigned)L.n_chunks, (unsigned)bh), dim3(256), 0,
-                        st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tf, d->T, (int)d->H);
+                        st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tf, prog, d->T, (int)d->H);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(512),
-                        0, st, e1, e2, 0, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
+                        0, st, e1, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
                         S0, ST, (TOut*)y, d->T, L.n_chunks);
   return launch_status();
 }

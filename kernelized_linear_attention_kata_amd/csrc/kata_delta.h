@@ -227,7 +227,8 @@ template <typename TIn> __device__ __forceinline__ float bits_value(uint32_t b) 
 // and T of the chunk to Tf [B*H, n_chunks, 4, 2, 64, 2, 8] bf16, already in the form the
 // walk feeds the matrix cores: for query block mb, token K-block kk and lane (n, g), the 8
 // entries T[16 mb + n][s] of the lane's K slots (permuted token order, see the walk) as
-// hi and lo bf16 halves.
+// hi and lo bf16 halves.  The first chunk's workgroup of each sequence also zeroes that
+// sequence's progress counters prog[bh][d/16] for the walk (dv = d).
 // Projection: the 4 threads of a token each take 16 input columns (two 16-byte loads of q
 // and of k), form the partial dot products of all 16 rows of P (staged in LDS) and sum
 // them with two lane shuffles.  Inversion: one column of T per lane of wave 0, the sum
@@ -236,7 +237,7 @@ template <typename TIn, int DIN>
 __global__ void __launch_bounds__(256)
 kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
                 const float* __restrict__ P, float* __restrict__ Uo, float* __restrict__ Wo,
-                bf16* __restrict__ Tf, int64_t T, int H) {
+                bf16* __restrict__ Tf, int* __restrict__ prog, int64_t T, int H) {
   constexpr int d = DIN;
   __shared__ __align__(16) float Ps[P_DIM][64 + 4];
   __shared__ __align__(16) float ws[DC][P_DIM];
@@ -246,6 +247,7 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   const int h = (int)(bh % H);
   const int64_t n_chunks = gridDim.x;
   for (int i = tid; i < P_DIM * d; i += 256) Ps[i / d][i % d] = P[(int64_t)h * P_DIM * d + i];
+  if (c == 0 && tid < DIN / 16) prog[bh * (DIN / 16) + tid] = 0;   // the walk's progress counters (dv = d)
   const int tl = tid >> 2, qq = tid & 3;           // token of the chunk, quarter of the columns
   const int64_t t = c * DC + tl;
   const bool live = t < T;
@@ -396,7 +398,8 @@ constexpr int DKB = 5;   // feature K-blocks of the packed state: delta pairs (0
 
 template <typename TIn, typename TOut, int DV>
 __global__ void __launch_bounds__(512)
-kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, const bf16* __restrict__ Tf,
+kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const float* __restrict__ Wh,
+                 const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
                  TOut* __restrict__ y, int64_t T, int64_t n_chunks) {
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
@@ -631,15 +634,43 @@ kata_delta_chunk(const float* __restrict__ Uh, const float* __restrict__ Wh, con
     __syncthreads();
   };
 
+  // Progress coupling of the NBLK column-block workgroups of a sequence.  They read the
+  // same u^, w^ and T of every chunk from their XCD's L2; left alone they drift apart over
+  // the chunks, and a workgroup far behind the first misses in L2 and reads them again from
+  // memory (1.45-1.56x the algorithmic bytes).  Every COUPLE_EVERY chunks a workgroup
+  // publishes its progress, and while it is more than COUPLE_LAG chunks ahead of the
+  // slowest workgroup of its sequence it sleeps and polls again, at most COUPLE_POLLS
+  // times.  The wait only orders memory traffic (results do not depend on it), and the
+  // poll bound ends it even if a partner never ran.
+  constexpr int COUPLE_EVERY = 32, COUPLE_LAG = 32, COUPLE_POLLS = 2048;
+  int* myprog = prog + bh * NBLK;
+  auto couple = [&](int64_t cc) {
+    if (tid == 0) {
+      __hip_atomic_store(myprog + j, (int)cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int it = 0; it < COUPLE_POLLS; ++it) {
+        int slowest = (int)cc;
+#pragma unroll
+        for (int o = 0; o < NBLK; ++o)
+          slowest = min(slowest, __hip_atomic_load(myprog + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (cc - slowest <= COUPLE_LAG) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    __syncthreads();
+  };
+
   Inputs ia{}, ib{};   // zeroed: the output waves load only puw and never read the rest
   if (n_chunks > 0) fetch(ia, 0);
   if (n_chunks > 1) fetch(ib, 1);
   int64_t c = 0;
   for (; c + 1 < n_chunks; c += 2) {
+    if (c % COUPLE_EVERY == 0) couple(c);
     step(ia, c);
     step(ib, c + 1);
   }
   if (c < n_chunks) step(ia, c);
+  if (tid == 0)   // done: nobody waits for this workgroup any more
+    __hip_atomic_store(myprog + j, (int)(n_chunks + COUPLE_LAG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // ST = S0 + the change of the packed state, at both entries (a, b) and (b, a) of each
   // pair, written by the one lane that owns its slot (for delta = 8 the lanes a < 8).  That
   // lane is also the only reader of these S0 entries, so S0 == ST is safe.

@@ -320,7 +320,8 @@ def test_delta_chunked_workspace_and_validation():
     assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
     chunks = 131072 // 64
     uw = 16 * chunks * 64 * 16 * 4
-    assert n.value == 2 * uw + 16 * chunks * 64 * 64 * 4          # u^, w^ and T per chunk
+    # u^, w^ and T per chunk, then one progress counter per column-block workgroup of the walk
+    assert n.value == 2 * uw + 16 * chunks * 64 * 64 * 4 + 16 * (64 // 16) * 4
     fake = ctypes.c_void_p(0x1000)
     for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),
                            ({"p": 8}, Bd.KATA_ERR_UNSUPPORTED), ({"T": -1}, Bd.KATA_ERR_SHAPE),

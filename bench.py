@@ -173,19 +173,30 @@ def recorded_traffic(fname: str, src: str, kernel: str):
         return None
 
 
-def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False, factors=1):
+def algorithmic_bytes(B, H, T, d, dv, n_leaf, in_bytes, out_bytes, decay=False, factors=1, scan=True):
     """Bytes each kernel must move at minimum (per launch), by the byte model of the path
     (decay: the log-gates, 4 B per token-head, read by the state and intra kernels, and
-    one float per leaf; factors: g leaf states per leaf, the tokens still read once)."""
+    one float per leaf; factors: g leaf states per leaf, the tokens still read once).
+    scan=False: the plan runs no scan (kata_forward_plan's scanned = 0); the intra pass's
+    workgroup of leaf g reads the states of leaves 0 .. g-1 and the last one writes the
+    final state."""
     E = 144 * dv + 256                    # packed leaf state block (S slots + Z), floats
     states = factors * B * H * n_leaf * E * 4
     scanned = factors * B * H * n_leaf * (E - 8 * dv) * 4   # the forward scan skips the 8 * dv unused slots
+    final = factors * B * H * 256 * (dv + 1) * 4
     tok = B * H * T
     g = tok * 4 if decay else 0
     gl = B * H * n_leaf * 4 if decay else 0
+    if not scan:
+        return {
+            "kata_chunk_state": tok * (d + dv) * in_bytes + states,
+            "kata_state_scan": 0,
+            "kata_chunk_intra": (tok * (2 * d + dv) * in_bytes + tok * dv * out_bytes
+                                 + B * H * (n_leaf * (n_leaf - 1) // 2) * E * 4 + final),
+        }
     return {
         "kata_chunk_state": tok * (d + dv) * in_bytes + states + g + gl,
-        "kata_state_scan": 2 * scanned + factors * B * H * 256 * (dv + 1) * 4 + gl,
+        "kata_state_scan": 2 * scanned + final + gl,
         "kata_chunk_intra": tok * (2 * d + dv) * in_bytes + states + tok * dv * out_bytes + g,
     }
 
@@ -694,12 +705,13 @@ def bench_workload(args):
     cases = [I.make_forward(args.workload, device=dev, seed=seed0 + b) for b in range(nb)]
     case = cases[0]
     B, H, T, d, dv, C = case.B, case.H, case.T, case.d, case.dv, 64
-    ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C)
+    ws_bytes = kata.forward_workspace_bytes(B, H, T, d, dv, C, scan_leaf=args.leaf)
+    plan = kata.forward_plan(B, H, T, d, dv, C, scan_leaf=args.leaf)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
     ST = torch.empty((B, H, 256, dv), dtype=torch.float32, device=dev)
     zT = torch.empty((B, H, 256), dtype=torch.float32, device=dev)
-    n_leaf = ws_bytes // (B * H * (144 * dv + 256) * 4)
+    n_leaf = plan["n_leaf"]
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -707,7 +719,7 @@ def bench_workload(args):
     def step(i, events=None, c=None):
         c = cases[i % nb] if c is None else c
         kata.forward(c.q, c.k, c.v, c.P, chunk=C, y=ys[i % nb], workspace=ws, ST=ST, zT=zT, return_state=True,
-                     stream=stream, events=events)
+                     scan_leaf=args.leaf, stream=stream, events=events)
 
     settle0 = time.perf_counter()
     n_settle = 0
@@ -756,7 +768,7 @@ def bench_workload(args):
     evs, _ = flushed_pass((jd, jd + 1))
     dominant_ms = mean_interval(evs, jd, jd + 1)
 
-    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2)
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, scan=plan["scanned"])
     aflops = algorithmic_flops(B, H, T, d, dv, C)
     kernels = {}
     for name in KERNELS:
@@ -785,12 +797,13 @@ def bench_workload(args):
         "data": (f"synthetic ({nb} distinct seeded batches cycled in the flushed steps; one batch in the warm "
                  "steps)"),
         "config": {"workload": (f"{args.workload} KATA forward: B={B} H={H} T={T} d=dv={d} p=16, bf16 q/k/v, "
-                                f"fp32 P/state, chunk {C}, assoc scan over {n_leaf} leaf states per sequence; "
+                                f"fp32 P/state, chunk {C}, {n_leaf} leaves per sequence "
+                                f"({'assoc scan' if plan['scanned'] else 'prefixes summed in the intra pass, no scan'}); "
                                 "each step after a 512 MB read that flushes the caches (warm: no flush, one batch)"),
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": C, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": mode_traffic(mode, dominant)},
+                     "traffic": mode_traffic(mode, dominant) if args.leaf == 0 else None},
         "warm": {"value": B * T / (warm_ms / 1e3), "ms_per_step": warm_ms,
                  "dominant_GBps": round(abytes[dominant] / (warm_kernels[dominant] / 1e3) / 1e9, 1)},
         "kernels": kernels,
@@ -1086,7 +1099,11 @@ def main():
     sg = G > 1 and args.factor_mode == "sum"
     fac_word = "summed" if sg else "concatenated"
     fac_note = f" with {G} {fac_word} PSD factors (P [16,{G},16,64], no state export)" if G > 1 else ""
-    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=1 if sg else G)
+    scanned = True
+    if G == 1 and not args.decay:
+        scanned = kata.forward_plan(B, H, T, d, dv, C, scan=args.scan, scan_leaf=args.leaf,
+                                    precise=args.precise)["scanned"]
+    abytes = algorithmic_bytes(B, H, T, d, dv, n_leaf, 2, 2, decay=args.decay, factors=1 if sg else G, scan=scanned)
     aflops = algorithmic_flops(B, H, T, d, dv, C, factors=G, cross=sg)
     kernels = {}
     for name in KERNELS:

@@ -104,7 +104,10 @@ typedef enum { KATA_F32 = 0, KATA_BF16 = 1, KATA_BF16_HILO = 2 } kata_dtype;
  *    log-depth tree; with the library's choice of L it is about sqrt of the work per
  *    GPU round.  A log-depth combine of the leaf sums measured 1.5x slower at these leaf
  *    counts.  scan_leaf = 1 writes and scans every chunk state (the literal chunk-level
- *    scan, depth 16 per pass plus the segment combine).
+ *    scan, depth 16 per pass plus the segment combine).  When the library's own plan
+ *    (scan_leaf = 0) has at most 8 leaves per sequence (many short sequences), step (2)
+ *    is folded into step (3): the output pass's workgroup of leaf g adds the sums of
+ *    leaves 0 .. g-1 itself (depth up to 7 leaf additions) and no separate scan runs.
  *  KATA_SCAN_SEQUENTIAL: one leaf per sequence - the chunk states are propagated
  *    strictly chunk after chunk (depth O(T/C)), the matched sequential baseline
  *    the pages compare the scan against ([ABS]). */
@@ -131,9 +134,18 @@ int kata_abi_version(void);
 const char* kata_status_string(kata_status s);
 
 /* Bytes of device workspace kata_forward needs for `desc` (written to *bytes).
- * The workspace holds the per-leaf chunk states and, after the call, their
- * exclusive prefixes: B*H*n_leaf blocks of (ceil-packed) state, float32. */
+ * The workspace holds the per-leaf chunk states, B*H*n_leaf blocks of (ceil-packed)
+ * state, float32, and after the call their exclusive prefixes; when the plan folds the
+ * prefix into the output pass (see KATA_SCAN_ASSOC) it still holds the leaf sums. */
 kata_status kata_forward_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+
+/* The leaf plan kata_forward (and kata_forward_noalloc) uses for `desc` (KATA_SCAN_ASSOC,
+ * [TS-2.3]): *n_leaf leaves per sequence of *leaf_chunks chunks each (the last may be
+ * shorter; 0 leaves when T == 0), and *scanned = 1 when a separate scan forms the leaf
+ * prefixes, 0 when the output pass adds the earlier leaves itself.  Any output pointer
+ * may be NULL.  Pure host computation from the descriptor; the same validation as
+ * kata_forward_workspace_bytes. */
+kata_status kata_forward_plan(const kata_forward_desc* desc, int64_t* n_leaf, int64_t* leaf_chunks, int* scanned);
 
 /* Causal KATA forward over whole sequences in the exact chunked-state form
  * ([TS-2.3], [ABS]; definition in the header comment).
@@ -156,8 +168,9 @@ kata_status kata_forward(const kata_forward_desc* desc,
 
 /* kata_forward that also stamps four caller-created hipEvent_t (created with timing
  * enabled) from the kernel launches on `stream`: events[0] at the start of
- * kata_chunk_state, events[1] at the start of kata_state_scan, events[2] at the start
- * of kata_chunk_intra and events[3] at its end, so a caller can time each kernel of
+ * kata_chunk_state, events[1] at the start of kata_state_scan (or, when the plan runs no
+ * scan, at the end of kata_chunk_state), events[2] at the start of kata_chunk_intra and
+ * events[3] at its end, so a caller can time each kernel of
  * the chunked forward on the stream it runs on.  The launches record the events
  * themselves (no extra commands enter the stream).  events == NULL behaves exactly
  * like kata_forward.  A NULL element is not stamped: every stamped launch costs a few

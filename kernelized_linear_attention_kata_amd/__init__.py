@@ -11,7 +11,7 @@ _BINDING_NAMES = (
     "forward_decay", "forward_decay_workspace_bytes", "forward_delta", "forward_delta_chunked",
     "forward_delta_chunked_workspace_bytes", "forward_factors",
     "forward_factors_workspace_bytes", "feature_map", "flash_forward", "flash_workspace_bytes",
-    "forward", "forward_noalloc", "forward_workspace_bytes", "library_path", "load_library", "NOALLOC_SCRATCH_BYTES",
+    "forward", "forward_noalloc", "forward_plan", "forward_workspace_bytes", "library_path", "load_library", "NOALLOC_SCRATCH_BYTES",
     "decode_step_packed", "decode_step_decay_packed", "decode_step_delta_packed", "decode_step_factors_packed",
     "state_pack", "state_unpack",
     "PACKED_ROWS",

@@ -78,6 +78,9 @@ def load_library() -> ctypes.CDLL:
     lib.kata_status_string.argtypes = [ci]
     lib.kata_forward_workspace_bytes.restype = ci
     lib.kata_forward_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_forward_plan.restype = ci
+    lib.kata_forward_plan.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ci)]
     lib.kata_forward.restype = ci
     lib.kata_forward.argtypes = [ctypes.POINTER(ForwardDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kata_forward_timed.restype = ci
@@ -211,6 +214,17 @@ def forward_workspace_bytes(B, H, T, d, dv, chunk, in_dtype=torch.bfloat16, out_
     _check(_lib().kata_forward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "kata_forward_workspace_bytes")
     return int(n.value)
 
+
+
+def forward_plan(B, H, T, d, dv, chunk, in_dtype=torch.bfloat16, out_dtype=None, scan="assoc", scan_leaf=0,
+                 precise=False) -> dict:
+    """The leaf plan of forward(): {"n_leaf", "leaf_chunks", "scanned"} (kata_forward_plan)."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, chunk, _in_code(in_dtype, precise), _dtype_code(out_dtype), scan, scan_leaf)
+    n, leaf, sc = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int(0)
+    _check(_lib().kata_forward_plan(ctypes.byref(desc), ctypes.byref(n), ctypes.byref(leaf), ctypes.byref(sc)),
+           "kata_forward_plan")
+    return {"n_leaf": int(n.value), "leaf_chunks": int(leaf.value), "scanned": bool(sc.value)}
 
 
 def _event_array(events, n: int, stream, dev):

@@ -30,6 +30,7 @@ struct Plan {
   int64_t n_chunks = 0;
   int64_t leaf = 1;        // chunks per leaf
   int64_t n_leaf = 0;
+  bool direct = false;     // plain forward: no scan, the intra pass sums the earlier leaves
   int E = 0;               // floats per leaf state block
   size_t ws_bytes = 0;
 };
@@ -112,13 +113,37 @@ int64_t slots_for(const kata_forward_desc* d) {
 // Leaf size: SEQUENTIAL = the whole sequence; ASSOC = the caller's value, else the
 // smallest number of leaves that fills the concurrent workgroup slots of the intra
 // kernel in whole rounds (leaves of at most kMaxLeaf chunks), so no round runs
-// partly empty and the scanned state tensor stays small.  The choice depends only
-// on the descriptor, so the workspace size is reproducible.
+// partly empty and the scanned state tensor stays small.  Where the leaf states would
+// then move more than a quarter of the bytes of the tokens (every leaf state is written,
+// scanned and read back: four passes of 37.9 KB at dv = 64), as for many short sequences,
+// the plan fills one workgroup fewer per compute unit: on the 340M-layer shape (B=8, H=16,
+// T=2048) 4 leaves of 8 chunks per sequence took 64.5 us per step against 71.7 us for
+// 6 leaves of 5-6 chunks, on the mid shape (B=4, H=8, T=4096) 16 leaves of 4 chunks
+// 40.0 us against 42.7 us for 22 leaves of 3, while the long shape (the states 11% of the
+// token bytes) keeps its plan.  The choice depends only on the descriptor, so the
+// workspace size is reproducible.
 constexpr int64_t kMaxLeaf = 64;
+constexpr int64_t kDirectMaxLeaves = 8;
+
+int64_t leaf_for_slots(int64_t n_chunks, int64_t bh, int64_t slots) {
+  const int64_t units = bh * n_chunks;
+  int64_t rounds = (units + slots * kMaxLeaf - 1) / (slots * kMaxLeaf);
+  if (rounds < 1) rounds = 1;
+  const int64_t leaves_per_bh = (rounds * slots + bh - 1) / bh;      // want >= this many
+  int64_t leaf = (n_chunks + leaves_per_bh - 1) / leaves_per_bh;
+  if (leaf < 1) leaf = 1;
+  if (leaf > n_chunks) leaf = n_chunks;
+  // fewer leaves than slots per round would idle compute units: shrink the leaf
+  while (leaf > 1 && bh * ((n_chunks + leaf - 1) / leaf) < rounds * slots &&
+         bh * ((n_chunks + leaf - 2) / (leaf - 1)) <= rounds * slots)
+    --leaf;
+  return leaf;
+}
 
 Plan make_plan(const kata_forward_desc* d, int64_t slots) {
   Plan p;
   p.n_chunks = (d->T + d->chunk - 1) / d->chunk;
+  p.E = DPACK * d->dv + P_DIM * P_DIM;
   const int64_t bh = d->B * d->H;
   if (p.n_chunks == 0 || bh == 0) {
     p.leaf = 1;
@@ -127,22 +152,23 @@ Plan make_plan(const kata_forward_desc* d, int64_t slots) {
   } else if (d->scan_leaf > 0) {
     p.leaf = d->scan_leaf < p.n_chunks ? d->scan_leaf : p.n_chunks;
   } else {
-    const int64_t units = bh * p.n_chunks;
-    int64_t rounds = (units + slots * kMaxLeaf - 1) / (slots * kMaxLeaf);
-    if (rounds < 1) rounds = 1;
-    const int64_t leaves_per_bh = (rounds * slots + bh - 1) / bh;      // want >= this many
-    int64_t leaf = (p.n_chunks + leaves_per_bh - 1) / leaves_per_bh;
-    if (leaf < 1) leaf = 1;
-    if (leaf > p.n_chunks) leaf = p.n_chunks;
-    // fewer leaves than slots per round would idle compute units: shrink the leaf
-    while (leaf > 1 && bh * ((p.n_chunks + leaf - 1) / leaf) < rounds * slots &&
-           bh * ((p.n_chunks + leaf - 2) / (leaf - 1)) <= rounds * slots)
-      --leaf;
-    p.leaf = leaf;
+    p.leaf = leaf_for_slots(p.n_chunks, bh, slots);
+    const int64_t per_cu = slots / kComputeUnits;
+    if (per_cu >= 3) {
+      const int in_bytes = bits(d->in_dtype) == KATA_F32 ? 4 : 2, out_bytes = bits(d->out_dtype) == KATA_F32 ? 4 : 2;
+      const double tokens = (double)bh * (double)d->T * ((2.0 * d->d + d->dv) * in_bytes + d->dv * out_bytes);
+      const double states = 4.0 * (double)bh * (double)((p.n_chunks + p.leaf - 1) / p.leaf) * p.E * sizeof(float);
+      if (states > 0.25 * tokens) p.leaf = leaf_for_slots(p.n_chunks, bh, kComputeUnits * (per_cu - 1));
+    }
   }
   p.n_leaf = p.n_chunks == 0 ? 0 : (p.n_chunks + p.leaf - 1) / p.leaf;
-  p.E = DPACK * d->dv + P_DIM * P_DIM;
   p.ws_bytes = (size_t)bh * (size_t)p.n_leaf * (size_t)p.E * sizeof(float);
+  // With few leaves per sequence (many short sequences) a separate scan costs more than
+  // it saves: the intra pass's workgroup of leaf g adds the states of leaves 0 .. g-1 itself
+  // (at most kDirectMaxLeaves - 1 blocks of 37.9 KB, read from the caches they were just
+  // written to) and the last one exports the final state.  Only for the plan the library
+  // picks, so a caller's explicit scan_leaf keeps the scanned workspace.
+  p.direct = d->scan == KATA_SCAN_ASSOC && d->scan_leaf == 0 && p.n_leaf > 0 && p.n_leaf <= kDirectMaxLeaves;
   return p;
 }
 
@@ -240,17 +266,22 @@ kata_status run_forward(const kata_forward_desc* d, const Plan& pl, const void* 
   // each kernel, end of the last), so timing adds no commands to the stream.
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, DECAY>), grid, dim3(256), smem_state, st, e0, nullptr, 0,
-                        (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, pl.leaf * S::C, lam, dec);
+  const bool direct = pl.direct && !DECAY;
+  // direct: no scan; events[1] is stamped by the state pass's end instead of the scan's start
+  hipExtLaunchKernelGGL((kata_chunk_state<S, TIn, DECAY>), grid, dim3(256), smem_state, st, e0, direct ? e1 : nullptr,
+                        0, (const TIn*)k, (const TIn*)v, P, ws, d->T, (int)d->H, pl.leaf * S::C, lam, dec);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  const int G = scan_segments(pl);
-  const dim3 sgrid = scan_grid(pl, G, bh);
-  hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
-                        (int)S::DV, G, S0, z0, ST, zT, 0, (const float*)dec);
-  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  if (!direct) {
+    const int G = scan_segments(pl);
+    const dim3 sgrid = scan_grid(pl, G, bh);
+    hipExtLaunchKernelGGL(kata_state_scan, sgrid, dim3(256), 0, st, e1, nullptr, 0, ws, pl.n_leaf, (int)pl.E,
+                          (int)S::DV, G, S0, z0, ST, zT, 0, (const float*)dec);
+    if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  }
   hipExtLaunchKernelGGL((kata_chunk_intra<S, TIn, TOut, DECAY>), grid, dim3(256), smem_intra, st, e2, e3, 0,
                         (const TIn*)q, (const TIn*)k, (const TIn*)v, P, (const float*)ws, (TOut*)y, d->T,
-                        (int)d->H, (int)pl.leaf, pl.n_chunks, lam);
+                        (int)d->H, (int)pl.leaf, pl.n_chunks, lam, direct ? 1 : 0, direct ? S0 : nullptr,
+                        direct ? z0 : nullptr, direct ? ST : nullptr, direct ? zT : nullptr);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   return KATA_OK;
 }
@@ -675,6 +706,16 @@ kata_status kata_forward_workspace_bytes(const kata_forward_desc* desc, size_t* 
   const kata_status s = validate(desc);
   if (s != KATA_OK) return s;
   *bytes = make_plan(desc).ws_bytes;
+  return KATA_OK;
+}
+
+kata_status kata_forward_plan(const kata_forward_desc* desc, int64_t* n_leaf, int64_t* leaf_chunks, int* scanned) {
+  const kata_status s = validate(desc);
+  if (s != KATA_OK) return s;
+  const Plan pl = make_plan(desc);
+  if (n_leaf) *n_leaf = pl.n_leaf;
+  if (leaf_chunks) *leaf_chunks = pl.leaf;
+  if (scanned) *scanned = pl.direct ? 0 : 1;
   return KATA_OK;
 }
 

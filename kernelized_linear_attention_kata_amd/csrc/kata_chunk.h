@@ -26,6 +26,7 @@
 #pragma once
 
 #include "kata_common.h"
+#include "kata_scan.h"
 
 namespace kata {
 
@@ -798,6 +799,50 @@ __device__ __forceinline__ void load_state(StateAcc<S>& st, const float* in, int
 // takes about 4 us longer.
 constexpr int Y_STORE_POLICY = 2;   // NT
 
+// Element index e (in the leaf block of the workspace) of accumulator element r of the
+// tile (delta, nb) that this lane holds.
+template <class S>
+__device__ __forceinline__ int acc_elem(int delta, int nb, int lane, int r) {
+  return ws_tile_offset<S>(delta, nb, lane) + r;
+}
+
+// Sets every accumulator element this wave holds (its diagonals, its delta = 8 column
+// blocks, and Z for the Z owner) to fn(e, value), e its element index.
+template <class S, typename F>
+__device__ __forceinline__ void for_state_elems(StateAcc<S>& st, int wave, bool zrole, int lane, F&& fn) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.s[j][nb][r] = fn(acc_elem<S>(wave + 4 * j, nb, lane, r), st.s[j][nb][r]);
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) {
+    const int nb = wave + 4 * i;
+    if (nb < S::NB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.s8[i][r] = fn(acc_elem<S>(8, nb, lane, r), st.s8[i][r]);
+    }
+  }
+  if (zrole) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.Z[r] = fn(DPACK * S::DV + lane * 4 + r, st.Z[r]);
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void state_add(StateAcc<S>& st, const StateAcc<S>& t) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb) st.s[j][nb] += t.s[j][nb];
+  }
+#pragma unroll
+  for (int i = 0; i < StateAcc<S>::N8; ++i) st.s8[i] += t.s8[i];
+  st.Z += t.Z;
+}
+
 // Vector store of 4 consecutive outputs through the y buffer resource (stores past
 // the end of the sequence are dropped).
 template <typename TOut> struct Store4;
@@ -1159,11 +1204,18 @@ __device__ __forceinline__ void gate_store(const f32x4 (&O)[S::NB], float den, c
 
 // grid (n_leaf, B*H), block 256.  ws holds each leaf's exclusive prefix state.  DECAY:
 // lam [B*H, T] log-decays (see the decay-gate notes above).
+// direct (not with DECAY): ws holds the leaf states themselves (no scan ran), and the
+// workgroup of leaf g forms its prefix as the symmetric part of S0/z0 (or 0) plus the
+// states of leaves 0 .. g-1; the workgroup of the last leaf also adds its own leaf's
+// state to that prefix and exports the sum, the final state, to ST/zT (when not NULL) as
+// the scan would, before its chunks (the stores drain while it works).
 template <class S, typename TIn, typename TOut, bool DECAY = false>
 __global__ void __launch_bounds__(256, S::OCC_INTRA)
 kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                  const float* __restrict__ P, const float* __restrict__ ws, TOut* __restrict__ y,
-                 int64_t T, int H, int leaf_chunks, int64_t n_chunks, const float* __restrict__ lam) {
+                 int64_t T, int H, int leaf_chunks, int64_t n_chunks, const float* __restrict__ lam,
+                 int direct, const float* __restrict__ S0, const float* __restrict__ z0, float* __restrict__ ST,
+                 float* __restrict__ zT) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* vf_hi = reinterpret_cast<bf16*>(smem + S::OFF_VF);
   bf16* vf_lo = reinterpret_cast<bf16*>(smem + S::OFF_VF + S::VF_BYTES);
@@ -1205,7 +1257,36 @@ kata_chunk_intra(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   PRows<S> prow;
   read_P_rows<S>(prow, P, h, lane);
   StateAcc<S> st;
-  load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+  if (!DECAY && direct) {
+    state_zero<S>(st);
+    if (S0) for_state_elems<S>(st, wave, zrole, lane, [&](int e, float) { return scan_initial(e, S::DV, bh, S0, z0); });
+    for (int64_t g = 0; g < leaf; ++g) {
+      StateAcc<S> t;
+      load_state<S>(t, ws + (bh * (int64_t)gridDim.x + g) * S::E, wave, zrole, lane);
+      state_add<S>(st, t);
+    }
+    if (ST && leaf + 1 == (int64_t)gridDim.x) {   // S0 + every leaf: the canonical final state
+      StateAcc<S> t;
+      load_state<S>(t, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+      state_add<S>(t, st);
+      const int64_t pp = (int64_t)P_DIM * P_DIM;
+      for_state_elems<S>(t, wave, zrole, lane, [&](int e, float x) {
+        int a, b, col;
+        bool is_z, mirror;
+        if (packed_to_pair(e, S::DV, a, b, col, is_z, mirror)) {
+          if (!is_z) {
+            ST[(bh * pp + a * P_DIM + b) * S::DV + col] = x;
+            if (mirror) ST[(bh * pp + b * P_DIM + a) * S::DV + col] = x;
+          } else {
+            zT[bh * pp + a * P_DIM + b] = x;
+          }
+        }
+        return x;
+      });
+    }
+  } else {
+    load_state<S>(st, ws + (bh * (int64_t)gridDim.x + leaf) * S::E, wave, zrole, lane);
+  }
 
   SeqRsrc rs;
   rs.q = make_rsrc(q + base_tok * S::DIN, T * S::DIN * (int64_t)sizeof(TIn));

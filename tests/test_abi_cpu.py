@@ -393,3 +393,29 @@ def test_noalloc_refuses_sizes_past_its_buffer():
     st, n = _ws(d)
     assert st == 0 and 0 < n <= Bd.NOALLOC_SCRATCH_BYTES
     assert lib.kata_forward_noalloc(ctypes.byref(d), *nulls, None) == Bd.KATA_ERR_NULL
+
+
+def test_forward_plan():
+    """kata_forward_plan reports the leaf plan the forward uses: its leaf count matches the
+    workspace size, the long shape keeps 48 leaves of 43 chunks with a scan, many short
+    sequences get one workgroup fewer per compute unit and no separate scan (at most 8
+    leaves), an explicit scan_leaf always scans, and NULL outputs are allowed."""
+    lib = _lib_or_skip()
+    E = 144 * 64 + 256
+    n, leaf, sc = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int(0)
+    cases = [((1, 16, 131072, 0), (48, 43, 1)), ((4, 8, 4096, 0), (16, 4, 1)), ((8, 16, 2048, 0), (4, 8, 0)),
+             ((8, 16, 2048, 8), (4, 8, 1)), ((2, 3, 200, 0), (4, 1, 0)), ((1, 1, 0, 0), (0, 1, 1))]
+    for (B, H, T, sl), want in cases:
+        d = Bd.make_desc(B, H, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "assoc", sl)
+        assert lib.kata_forward_plan(ctypes.byref(d), ctypes.byref(n), ctypes.byref(leaf), ctypes.byref(sc)) == Bd.KATA_OK
+        assert (n.value, leaf.value, sc.value) == want, (B, H, T, sl)
+        ws = ctypes.c_size_t(0)
+        assert lib.kata_forward_workspace_bytes(ctypes.byref(d), ctypes.byref(ws)) == Bd.KATA_OK
+        assert ws.value == B * H * n.value * E * 4
+    d = Bd.make_desc(1, 16, 131072, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16, "sequential")
+    assert lib.kata_forward_plan(ctypes.byref(d), ctypes.byref(n), None, ctypes.byref(sc)) == Bd.KATA_OK
+    assert n.value == 1 and sc.value == 1
+    assert lib.kata_forward_plan(ctypes.byref(d), None, None, None) == Bd.KATA_OK
+    assert lib.kata_forward_plan(None, ctypes.byref(n), None, None) == Bd.KATA_ERR_NULL
+    bad = Bd.make_desc(1, 16, 131072, 32, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    assert lib.kata_forward_plan(ctypes.byref(bad), ctypes.byref(n), None, None) == Bd.KATA_ERR_UNSUPPORTED

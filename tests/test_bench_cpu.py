@@ -91,3 +91,16 @@ def test_backward_bytes_match_workspace():
                + nbytes(B, H, T, 2, dtype=torch.float32)                            # (1/den, h)
                + nbytes(B, H, T, d) + nbytes(B, H, T, dv))                          # dk, dv
     assert got["kata_bwd_key"] == streams + states + parts
+
+
+def test_bytes_without_a_scan():
+    """When the plan runs no scan, the intra pass reads the earlier leaves' states (leaf g
+    reads g of them) and writes the final state; the scan moves nothing."""
+    B, H, T, d, dv, n = 8, 16, 2048, 64, 64, 4
+    got = bench.algorithmic_bytes(B, H, T, d, dv, n, 2, 2, scan=False)
+    E = 144 * dv + 256
+    final = nbytes(B, H, 256, dv, dtype=torch.float32) + nbytes(B, H, 256, dtype=torch.float32)
+    tokens = nbytes(B, H, T, d) * 2 + nbytes(B, H, T, dv) * 2
+    assert got["kata_state_scan"] == 0
+    assert got["kata_chunk_intra"] == tokens + B * H * (0 + 1 + 2 + 3) * E * 4 + final
+    assert got["kata_chunk_state"] == nbytes(B, H, T, d) + nbytes(B, H, T, dv) + B * H * n * E * 4

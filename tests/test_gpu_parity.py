@@ -287,6 +287,67 @@ def test_scan_exclusive_prefix(leaf):
             assert np.linalg.norm(z - zr[0, 0]) / max(np.linalg.norm(zr), 1e-30) <= 1e-2 if t_end else np.all(z == 0)
 
 
+@pytest.mark.parametrize("B,H,T,initial", [(8, 16, 549, False), (8, 16, 549, True), (4, 32, 2048, True),
+                                             (16, 8, 40, False), (2, 3, 200, True)])
+def test_prefix_in_the_intra_pass_agrees_with_the_scan(B, H, T, initial):
+    """With at most 8 leaves per sequence the library's plan runs no scan: the intra pass's
+    workgroup of leaf g adds the leaf sums of 0 .. g-1 (and the symmetric part of S0) and the
+    last one exports S_T, z_T.  The same leaves through the scan (an explicit scan_leaf)
+    give the same y and final state up to summation order, both match the oracle, and the
+    workspace of the scanned call holds prefixes while the other holds the leaf sums."""
+    case = I.make_forward("lm340m", B=B, H=H, T=T, seed=40 + T)
+    q, k, v, P = (t.to(DEV) for t in (case.q, case.k, case.v, case.P))
+    E = 144 * 64 + 256
+    nbytes = kata.forward_workspace_bytes(B, H, T, 64, 64, 64)
+    n_leaf = nbytes // (B * H * E * 4)
+    n_chunks = -(-T // 64)
+    leaf = -(-n_chunks // n_leaf)
+    assert -(-n_chunks // leaf) == n_leaf and n_leaf <= 8
+    kw = {}
+    if initial:
+        kh, vh = host64(case.k), host64(case.v)
+        Ph = case.P.double().cpu().numpy()
+        S0, z0 = O.final_state(kh[:, :, : T // 3], vh[:, :, : T // 3], Ph)
+        g = np.random.default_rng(T)
+        A = g.standard_normal(S0.shape).reshape(B, H, 16, 16, 64)
+        S0 = S0 + 0.3 * (A - A.transpose(0, 1, 3, 2, 4)).reshape(S0.shape) * np.abs(S0).max()   # not symmetric
+        kw = dict(S0=torch.tensor(S0, dtype=torch.float32, device=DEV),
+                  z0=torch.tensor(z0, dtype=torch.float32, device=DEV))
+    ws_d = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws_s = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    yd, Sd, zd = kata.forward(q, k, v, P, chunk=64, workspace=ws_d, return_state=True, out_dtype=torch.float32, **kw)
+    ys, Ss, zs = kata.forward(q, k, v, P, chunk=64, scan_leaf=leaf, workspace=ws_s, return_state=True,
+                              out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    ey = slice_rel(yd.double().cpu().numpy(), ys.double().cpu().numpy())
+    eS = slice_rel(Sd.cpu().numpy(), Ss.cpu().numpy())
+    ez = slice_rel(zd.cpu().numpy(), zs.cpu().numpy())
+    print(f"[B={B} H={H} T={T} n_leaf={n_leaf} S0={initial}] direct vs scan: y {ey:.2e} S {eS:.2e} z {ez:.2e}")
+    assert ey <= 2e-3 and eS <= 1e-5 and ez <= 1e-5, (ey, eS, ez)
+    # against the oracle
+    qh, kh, vh = host64(case.q), host64(case.k), host64(case.v)
+    Ph = case.P.double().cpu().numpy()
+    rows = np.unique(np.linspace(0, T - 1, 24).astype(int))
+    o = {kk: vv.double().cpu().numpy() for kk, vv in kw.items()}
+    yr = O.forward_quadratic(qh, kh, vh, Ph, rows=rows, **o)
+    if initial:   # the export carries the symmetric part of S0 (the only part a read sees)
+        S0h = o["S0"].reshape(B, H, 16, 16, 64)
+        o["S0"] = (0.5 * (S0h + S0h.transpose(0, 1, 3, 2, 4))).reshape(B, H, 256, 64)
+        z0h = o["z0"].reshape(B, H, 16, 16)
+        o["z0"] = (0.5 * (z0h + z0h.transpose(0, 1, 3, 2))).reshape(B, H, 256)
+    Sr, zr = O.final_state(kh, vh, Ph, **o)
+    assert slice_rel(yd.double().cpu().numpy()[:, :, rows], yr) <= 2e-2
+    assert slice_rel(Sd.cpu().numpy(), Sr) <= 2e-2 and slice_rel(zd.cpu().numpy(), zr) <= 2e-2
+    # the scanned workspace holds exclusive prefixes (leaf 0's is the initial state, or 0),
+    # the other the leaf sums: they agree on leaf 0 only when there is no initial state
+    Wd = ws_d.view(torch.float32).cpu().numpy().reshape(B * H, n_leaf, E)
+    Ws = ws_s.view(torch.float32).cpu().numpy().reshape(B * H, n_leaf, E)
+    S1, _ = unpack_leaf(Ws[0, 1 if n_leaf > 1 else 0], 64)
+    Sl, _ = unpack_leaf(Wd[0, 0], 64)
+    if n_leaf > 1 and not initial:
+        assert np.allclose(S1, Sl, rtol=1e-5, atol=1e-6 * np.abs(Sl).max())
+
+
 # ---- edge cases ------------------------------------------------------------------------
 
 def test_empty_sequence_copies_initial_state():

@@ -222,7 +222,7 @@ kata_status kata_forward_noalloc(const kata_forward_desc* desc,
  * BF16; desc->chunk, scan and scan_leaf are ignored.  q, k [B,H,T,64], v [B,H,T,64]
  * bf16, P [H,16,64] f32, y [B,H,T,64] out_dtype, all device memory owned by the caller.
  * The workspace (kata_flash_workspace_bytes: 256 bytes per token and head, T rounded
- * up to 256) holds the projected u and w (each as a hi/lo pair of bf16, so the squared
+ * up to 128) holds the projected u and w (each as a hi/lo pair of bf16, so the squared
  * scores keep about 16 significant bits) and V in MFMA operand order.
  * events: NULL, or three caller-created hipEvent_t (timing enabled) stamped with the
  * start of the projection kernel, the start of the attention kernel and its end.

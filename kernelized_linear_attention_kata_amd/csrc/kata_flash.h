@@ -13,7 +13,7 @@
 // Two kernels:
 //  * kata_flash_prep  (grid T_pad/64 x B*H): u = P q, w = P k (as hi/lo bf16 pairs) and
 //    V, regrouped into MFMA operand order and written once per token to a workspace.
-//  * kata_flash_attn  (T_pad/256 * B*H workgroups, XCD-aware order): 8 waves x
+//  * kata_flash_attn  (T_pad/128 * B*H workgroups, XCD-aware order): 4 waves x
 //    32 queries; 64-key blocks of w and V fragments copied into an LDS ring.  Per
 //    32-key tile: X^T = W U^T (three 32x32x16 MFMAs, K = p, hi/lo operands), squared and
 //    masked on the VALU, then O^T += V^T (X^2)^T (32x32x16 MFMAs, K = 16 keys).  Lane l
@@ -30,7 +30,7 @@
 
 namespace kata {
 
-constexpr int FL_WAVES = 8;                // waves per workgroup, 32 queries each
+constexpr int FL_WAVES = 4;                // waves per workgroup, 32 queries each
 constexpr int FL_QB = 32 * FL_WAVES;       // queries per workgroup
 constexpr int FL_KB = 64;       // keys per staged block
 constexpr int FL_DV = 64;
@@ -141,15 +141,16 @@ kata_flash_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn*
 // buffers by buffer_load ... lds (no registers), FL_RING - 1 blocks ahead of use.  A
 // buffer is [Wf hi block: 2 tiles x 64 lanes x 16 B = 2 KB | Wf lo block: 2 KB | Vf
 // block: 4 groups x 2 tiles x 64 lanes x 16 B = 8 KB | 4 KB pad], sixteen 1 KB pieces:
-// every wave copies pieces w and w + 8 (the pad pieces read past the workspace: zeros,
-// no traffic), so each wave has exactly FL_DMA_PER_WAVE loads per block in flight and
-// waits for a block with an exact vmcnt.
+// wave w copies pieces w, w + 4, w + 8 and w + 12 (the pad pieces read past the
+// workspace: zeros, no traffic), so each wave has exactly FL_DMA_PER_WAVE loads per block
+// in flight and waits for a block with an exact vmcnt.
 constexpr int FL_W_BYTES = FL_KB * P_DIM * 2;
 constexpr int FL_V_BYTES = FL_KB * FL_DV * 2;
 constexpr int FL_PIECES = 16;   // 1 KB pieces per buffer (12 used, 4 read as zeros)
 constexpr int FL_BUF_BYTES = FL_PIECES * 1024;
-// Two buffers (the copy of block kb + 1 runs during block kb) measured fastest with
-// eight waves: 32 KB per workgroup, three workgroups per CU, 6 waves per SIMD.
+// Two buffers (the copy of block kb + 1 runs during block kb): 32 KB per workgroup, five
+// workgroups of four waves per CU (all 160 KB of LDS), 5 waves per SIMD.  Three
+// workgroups of eight waves (6 waves per SIMD) measured 3% slower.
 constexpr int FL_RING = 2;
 constexpr int FL_DMA_PER_WAVE = FL_PIECES / FL_WAVES;
 
@@ -161,7 +162,7 @@ typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_s_waitcnt(((N) & 0xf) | (((N) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
 template <typename TOut>
-__global__ void __launch_bounds__(64 * FL_WAVES, 6)
+__global__ void __launch_bounds__(64 * FL_WAVES, 5)
 kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, int64_t tpad, int nbh) {
   __shared__ __align__(16) unsigned char sm[FL_RING * FL_BUF_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;

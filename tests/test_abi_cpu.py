@@ -149,7 +149,7 @@ def test_flash_workspace_and_validation():
     n = ctypes.c_size_t(0)
     d = Bd.make_desc(2, 3, 1000, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_F32)
     assert lib.kata_flash_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
-    assert n.value == 6 * 1024 * 256          # T rounded up to 256; u, w hi/lo, V: 256 B per token
+    assert n.value == 6 * 1024 * 256          # T rounded up to 128; u, w hi/lo, V: 256 B per token
     fake = ctypes.c_void_p(0x1000)
     for field, value, status in [("d", 16, Bd.KATA_ERR_UNSUPPORTED), ("in_dtype", Bd.KATA_F32, Bd.KATA_ERR_UNSUPPORTED),
                                  ("p", 8, Bd.KATA_ERR_UNSUPPORTED), ("T", -1, Bd.KATA_ERR_SHAPE),

@@ -140,19 +140,22 @@ kata_flash_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn*
 // Key blocks are copied straight from the workspace into an LDS ring of FL_RING
 // buffers by buffer_load ... lds (no registers), FL_RING - 1 blocks ahead of use.  A
 // buffer is [Wf hi block: 2 tiles x 64 lanes x 16 B = 2 KB | Wf lo block: 2 KB | Vf
-// block: 4 groups x 2 tiles x 64 lanes x 16 B = 8 KB | 4 KB pad], sixteen 1 KB pieces:
-// wave w copies pieces w, w + 4, w + 8 and w + 12 (the pad pieces read past the
-// workspace: zeros, no traffic), so each wave has exactly FL_DMA_PER_WAVE loads per block
-// in flight and waits for a block with an exact vmcnt.
+// block: 4 groups x 2 tiles x 64 lanes x 16 B = 8 KB], twelve 1 KB pieces: wave w copies
+// pieces w, w + 4 and w + 8, so each wave has exactly FL_DMA_PER_WAVE loads per block in
+// flight and waits for a block with an exact vmcnt.
 constexpr int FL_W_BYTES = FL_KB * P_DIM * 2;
 constexpr int FL_V_BYTES = FL_KB * FL_DV * 2;
-constexpr int FL_PIECES = 16;   // 1 KB pieces per buffer (12 used, 4 read as zeros)
+constexpr int FL_PIECES = 12;   // 1 KB pieces per buffer
 constexpr int FL_BUF_BYTES = FL_PIECES * 1024;
-// Two buffers (the copy of block kb + 1 runs during block kb): 32 KB per workgroup, five
-// workgroups of four waves per CU (all 160 KB of LDS), 5 waves per SIMD.  Three
-// workgroups of eight waves (6 waves per SIMD) measured 3% slower.
+// Two buffers (the copy of block kb + 1 runs during block kb): 24 KB per workgroup, five
+// workgroups of four waves per CU (5 waves per SIMD, the register budget).  Measured
+// against it: three workgroups of eight waves (6 waves per SIMD) 3% slower; 16 KB buffers
+// whose last 4 KB were copies read past the workspace (zeros), so that eight waves had
+// equal shares, 6% slower; three 12 KB buffers at four workgroups per CU, 4% slower.
 constexpr int FL_RING = 2;
 constexpr int FL_DMA_PER_WAVE = FL_PIECES / FL_WAVES;
+static_assert(FL_PIECES % FL_WAVES == 0 && FL_PIECES * 1024 == 2 * FL_W_BYTES + FL_V_BYTES,
+              "every wave copies the same number of pieces, which cover the block");
 
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -140,7 +140,7 @@ def source_hash(extra=()) -> str:
 # Headers each bench mode's kernels live in; the mode's counters are keyed by their hash
 # together with all of kata.hip (the forward keeps its narrower hash, see source_hash).
 PATH_HEADERS = {"decay": ("kata_chunk.h",), "backward": ("kata_bwd.h",), "flash": ("kata_flash.h",),
-                "delta": ("kata_delta.h",), "decode": ("kata_decode.h",), "decode_delta": ("kata_delta.h",),
+                "delta": ("kata_delta.h",), "delta_seq": ("kata_delta.h",), "decode": ("kata_decode.h",), "decode_delta": ("kata_delta.h",),
                 "decode_delta_packed": ("kata_delta.h", "kata_decode.h")}
 
 
@@ -599,7 +599,8 @@ def bench_delta_forward(args):
     betas = [I.make_beta(c.B, c.H, c.T, seed=seed0 + b, device=dev) for b, c in enumerate(cases)]
     case = cases[0]
     B, H, T, d, dv = case.B, case.H, case.T, case.d, case.dv
-    wsb = kata.forward_delta_chunked_workspace_bytes(B, H, T, d, dv)
+    plan = kata.forward_delta_chunked_plan(B, H, T, d, dv, scan=args.scan, scan_leaf=args.leaf)
+    wsb = kata.forward_delta_chunked_workspace_bytes(B, H, T, d, dv, scan=args.scan, scan_leaf=args.leaf)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     ys = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
     stream = torch.cuda.current_stream(dev)
@@ -607,7 +608,7 @@ def bench_delta_forward(args):
     def step(i, events=None):
         c = cases[i % nb]
         kata.forward_delta_chunked(c.q, c.k, c.v, c.P, betas[i % nb], y=ys[i % nb], workspace=ws, stream=stream,
-                                   events=events)
+                                   events=events, scan=args.scan, scan_leaf=args.leaf)
 
     settle0 = time.perf_counter()
     n_settle = 0
@@ -631,6 +632,14 @@ def bench_delta_forward(args):
     rec_ms = r0.elapsed_time(r1)
     tok = B * H * T
     n_chunks = (T + 63) // 64
+    nseg, seg_chunks = plan["segments"], plan["segment_chunks"]
+    dmode = "delta_seq" if args.scan == "sequential" else "delta"
+    if nseg > 1:
+        walk_how = (f"each head's walk cut into {nseg} segments of {seg_chunks} chunks: the segments' affine maps "
+                    f"({(dv + 144) // 16} column blocks each) side by side, their chain, then the segments' walks "
+                    f"side by side, {B * H * nseg * (dv // 16)} workgroups")
+    else:
+        walk_how = f"{n_chunks} chunks per head walked in order by {dv // 16} workgroups per head"
     prep_bytes = tok * (2 * d * 2 + 4) + tok * 2 * 16 * 4 + B * H * n_chunks * 64 * 64 * 4
     walk_bytes = tok * (2 * 16 * 4 + dv * 2 + 4 + dv * 2) + B * H * n_chunks * 64 * 64 * 4
     # useful walk flops per chunk and 16-column block: K^S and Q^S (2 x 64x256x16), T X (64x64x16),
@@ -643,15 +652,14 @@ def bench_delta_forward(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 q/k/v/y, f32 state (hi/lo bf16 MFMA products)",
         "data": f"synthetic ({nb} distinct seeded batches, cycled per step)",
         "config": {"workload": (f"long-context DeltaKATA forward: B={B} H={H} T={T} d=dv={d} p=16, beta uniform in "
-                                f"[0.5, 1], chunk 64 ({n_chunks} chunks per head walked in order by {dv // 16} "
-                                f"workgroups per head)"),
+                                f"[0.5, 1], chunk 64 ({walk_how})"),
                    "global_batch": B, "seq_len": T, "heads": H, "chunk": 64, "batches_cycled": nb},
         "roofline": {"bound": "mfma", "kernel": "kata_delta_chunk", "achieved": round(walk_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(walk_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
-                     "traffic": mode_traffic("delta", "kata_delta_chunk"),
-                     "note": ("the walk is a dependency chain over the chunks of one sequence with "
-                                               f"{B * H * (dv // 16)} workgroups: bound by per-chunk latency, "
-                                               "not by either peak")},
+                     "traffic": (mode_traffic(dmode, "kata_delta_chunk") if args.leaf == 0 else None),
+                     "note": ("useful flops of the walk (the one-walk form's work; segment maps not counted); "
+                              "the walk is a dependency chain over the chunks of a segment: bound by per-chunk "
+                              "latency, not by either peak")},
         "kernels": {"kata_delta_prep": {"ms": round(prep_ms, 4), "alg_bytes": prep_bytes,
                                         "alg_GBps": round(prep_bytes / (prep_ms / 1e3) / 1e9, 1)},
                     "kata_delta_chunk": {"ms": round(split["kata_delta_chunk"], 4), "ms_timed_steps": round(walk_ms, 4),
@@ -659,7 +667,8 @@ def bench_delta_forward(args):
                                          "alg_GBps": round(walk_bytes / (walk_ms / 1e3) / 1e9, 1),
                                          "alg_TFLOPs": round(walk_tflops, 2),
                                          "us_per_chunk": round(walk_ms * 1e3 / n_chunks, 3)}},
-        "mode": "delta", "source_hash": path_hash("delta"),
+        "mode": dmode, "source_hash": path_hash(dmode),
+        "plan": plan,
         "recurrent_form": {"kernel": "kata_delta_recurrent", "ms": round(rec_ms, 3),
                            "tokens_per_s": B * T / (rec_ms / 1e3)},
         "settle": {"seconds": round(time.perf_counter() - settle0, 3), "steps": n_settle},

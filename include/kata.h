@@ -466,18 +466,31 @@ kata_status kata_forward_delta(const kata_forward_desc* desc,
  * E = T diag(beta)(V - K^ S), Y = Q^ S + (Q^K^^T o M) E (M: s <= t), S += K^^T E.  Same
  * definition and arguments as kata_forward_delta (exactly equal up to rounding), plus a
  * device workspace of kata_forward_delta_chunked_workspace_bytes bytes (normalised
- * projections and T per chunk: 9 KiB per 64 tokens and head; and one int per walk
- * workgroup that keeps a sequence's workgroups within a few chunks of each other, so they
- * share their inputs in L2), owned by the caller; calls that overlap on one workspace race.
+ * projections and T per chunk: 9 KiB per 64 tokens and head; one int per walk workgroup
+ * that keeps a sequence's workgroups within a few chunks of each other, so they share
+ * their inputs in L2; and with segments, below, 144 x (dv + 144) + 256 x dv floats per
+ * segment), owned by the caller; calls that overlap on one workspace race.
  * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S) and
  * keeps the state's symmetric part packed (the antisymmetric part of S0, which no read
- * sees, reaches ST unchanged).  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),
+ * sees, reaches ST unchanged).  Segments: the chunk transition is affine in S, so with few
+ * sequences the walk is cut into segments (kata_forward_delta_chunked_plan): each
+ * segment's map S_end = M S_start + b is formed side by side (M from the packed unit
+ * vectors), the maps are chained into every segment's start state, and the segments'
+ * walks run side by side.  desc->scan_leaf > 0 sets the chunks per segment and
+ * KATA_SCAN_SEQUENTIAL one walk per sequence; 0 lets the library choose.  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),
  * desc->chunk = 64, in/out dtype F32 or BF16, B*H <= 65535, and a sequence of q, k, v
  * or y under 2 GiB at 4 bytes per element (T * max(d, dv) * 4 < 2^31 - 4096, less 256
  * tokens; else KATA_ERR_SHAPE: the walk addresses a sequence with 32-bit offsets).
  * kata_forward_delta_chunked_timed stamps three caller-created events: start of the
  * per-chunk pass, start and end of the walk. */
 kata_status kata_forward_delta_chunked_workspace_bytes(const kata_forward_desc* desc, size_t* bytes);
+/* The walk plan kata_forward_delta_chunked uses for `desc`: each sequence's walk cut into
+ * *segments segments of *segment_chunks chunks of 64 tokens (the last may be shorter; one
+ * segment of all chunks when the walks already fill the GPU or under
+ * KATA_SCAN_SEQUENTIAL).  Any output pointer may be NULL.  Pure host computation from the
+ * descriptor; the same validation as kata_forward_delta_chunked_workspace_bytes. */
+kata_status kata_forward_delta_chunked_plan(const kata_forward_desc* desc, int64_t* segments,
+                                            int64_t* segment_chunks);
 kata_status kata_forward_delta_chunked(const kata_forward_desc* desc,
                                        const void* q, const void* k, const void* v,
                                        const float* P, const float* beta, const float* S0,

@@ -78,6 +78,9 @@ def load_library() -> ctypes.CDLL:
     lib.kata_status_string.argtypes = [ci]
     lib.kata_forward_workspace_bytes.restype = ci
     lib.kata_forward_workspace_bytes.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(sz)]
+    lib.kata_forward_delta_chunked_plan.restype = ci
+    lib.kata_forward_delta_chunked_plan.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(ctypes.c_int64),
+                                                    ctypes.POINTER(ctypes.c_int64)]
     lib.kata_forward_plan.restype = ci
     lib.kata_forward_plan.argtypes = [ctypes.POINTER(ForwardDesc), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ci)]
@@ -550,26 +553,40 @@ def forward_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     return (y, ST) if return_state else y
 
 
-def forward_delta_chunked_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None) -> int:
-    """Workspace bytes of kata_forward_delta_chunked for these sizes."""
+def forward_delta_chunked_workspace_bytes(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None,
+                                          scan="assoc", scan_leaf=0) -> int:
+    """Workspace bytes of kata_forward_delta_chunked for these sizes (and segment plan)."""
     out_dtype = in_dtype if out_dtype is None else out_dtype
-    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
     n = ctypes.c_size_t(0)
     _check(_lib().kata_forward_delta_chunked_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
            "kata_forward_delta_chunked_workspace_bytes")
     return int(n.value)
 
 
+def forward_delta_chunked_plan(B, H, T, d=64, dv=64, in_dtype=torch.bfloat16, out_dtype=None, scan="assoc",
+                               scan_leaf=0) -> dict:
+    """The walk plan of forward_delta_chunked(): {"segments", "segment_chunks"}
+    (kata_forward_delta_chunked_plan)."""
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(in_dtype), _dtype_code(out_dtype), scan, scan_leaf)
+    n, per = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib().kata_forward_delta_chunked_plan(ctypes.byref(desc), ctypes.byref(n), ctypes.byref(per)),
+           "kata_forward_delta_chunked_plan")
+    return {"segments": int(n.value), "segment_chunks": int(per.value)}
+
+
 def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, beta: torch.Tensor, *,
                           S0: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                           return_state: bool = False, y: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, ST: Optional[torch.Tensor] = None,
-                          stream=None, events=None):
+                          scan: str = "assoc", scan_leaf: int = 0, stream=None, events=None):
     """DeltaKATA causal forward in the chunked form (kata_forward_delta_chunked); same
     definition and arguments as forward_delta.  ST: optional preallocated final state
     [B,H,256,dv] fp32 (implies return_state; may be S0 itself, updated in place).
-    events: optional three torch.cuda.Event (start of the per-chunk pass, start and end
-    of the walk)."""
+    scan_leaf: chunks per walk segment (0 = the library's plan); scan="sequential": one
+    walk per sequence.  events: optional three torch.cuda.Event (start of the per-chunk
+    pass, start and end of the walk)."""
     B, H, T, d = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -581,7 +598,7 @@ def forward_delta_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: 
     if S0 is not None:
         _need(S0, "S0", (B, H, P_DIM * P_DIM, dv), torch.float32, dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    desc = make_desc(B, H, T, d, dv, 64, _dtype_code(q.dtype), _dtype_code(out_dtype), scan, scan_leaf)
     lib = _lib()
     n = ctypes.c_size_t(0)
     _check(lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),

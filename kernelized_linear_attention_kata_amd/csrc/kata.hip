@@ -570,20 +570,50 @@ kata_status run_forward_sg(const kata_forward_desc* d, const Plan& pl, const voi
 // fragments (64 x 64 x 2 bf16 per chunk), each block 256-byte aligned.
 struct DeltaChunkLayout {
   int64_t n_chunks = 0;
-  size_t off_w = 0, off_t = 0, off_prog = 0, total = 0;
+  int64_t nseg = 1, seg_chunks = 0;   // segments of a sequence's walk, chunks per segment
+  size_t off_w = 0, off_t = 0, off_prog = 0, off_aff = 0, off_s0 = 0, total = 0;
 };
 
+// Segments.  A sequence's walk runs on dv/16 workgroups, one per CU; with few sequences
+// most CUs idle and the walk takes the chunk count times one chunk's dependency chain.
+// Cut into segments, the segments' affine maps are formed side by side, chained in a short
+// pass, and the segments' walks run side by side.  The library segments where the walks
+// fill fewer than a quarter of the workgroup slots (4 per CU): nseg = 1024 / (B*H*dv/16),
+// at least 16 chunks per segment.  desc->scan_leaf > 0 sets the chunks per segment, and
+// KATA_SCAN_SEQUENTIAL one walk per sequence.
+int64_t delta_segments(const kata_forward_desc* d, int64_t n_chunks, int64_t* seg_chunks) {
+  const int64_t walks = d->B * d->H * (d->dv / 16);
+  int64_t per = n_chunks;
+  if (d->scan == KATA_SCAN_SEQUENTIAL || n_chunks == 0) {
+    per = n_chunks;
+  } else if (d->scan_leaf > 0) {
+    per = d->scan_leaf < n_chunks ? d->scan_leaf : n_chunks;
+  } else if (walks > 0 && walks < kComputeUnits * 4) {
+    int64_t want = (kComputeUnits * 4) / walks;
+    if (want > n_chunks / 16) want = n_chunks / 16;
+    if (want > 1) per = (n_chunks + want - 1) / want;
+  }
+  if (per < 1) per = 1;
+  *seg_chunks = per;
+  return n_chunks == 0 ? 1 : (n_chunks + per - 1) / per;   // no empty segment
+}
+
 // u^, w^ (fp32), T (hi/lo bf16 fragments), then the walk's progress counters (one int per
-// column-block workgroup).
+// column-block workgroup); with segments, their affine maps [B*H*nseg, 144, dv + 144] and
+// start states [B*H*nseg, 256, dv] (fp32).
 DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   DeltaChunkLayout L;
   const int64_t bh = d->B * d->H;
   L.n_chunks = (d->T + kata::DC - 1) / kata::DC;
+  L.nseg = delta_segments(d, L.n_chunks, &L.seg_chunks);
   const size_t uw = (size_t)bh * (size_t)L.n_chunks * kata::DC * P_DIM * sizeof(float);
   L.off_w = align256(uw);
   L.off_t = L.off_w + align256(uw);
   L.off_prog = L.off_t + align256((size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * 2 * sizeof(bf16));
-  L.total = L.off_prog + (size_t)bh * (size_t)(d->dv / 16) * sizeof(int);
+  L.off_aff = L.off_prog + align256((size_t)bh * (size_t)(d->dv / 16) * sizeof(int));
+  const size_t nw = L.nseg > 1 ? (size_t)bh * (size_t)L.nseg : 0;
+  L.off_s0 = L.off_aff + align256(nw * DPACK * (size_t)(d->dv + DPACK) * sizeof(float));
+  L.total = L.off_s0 + nw * P_DIM * P_DIM * (size_t)d->dv * sizeof(float);
   return L;
 }
 
@@ -613,9 +643,29 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   hipExtLaunchKernelGGL((kata::kata_delta_prep<TIn, DV>), dim3((unsigned)L.n_chunks, (unsigned)bh), dim3(256), 0,
                         st, e0, nullptr, 0, (const TIn*)q, (const TIn*)k, beta, P, U, W, Tf, prog, d->T, (int)d->H);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(512),
-                        0, st, e1, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
-                        S0, ST, (TOut*)y, d->T, L.n_chunks);
+  if (L.nseg == 1) {
+    hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh),
+                          dim3(512), 0, st, e1, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf,
+                          (const TIn*)v, beta, S0, ST, (TOut*)y, d->T, L.n_chunks, 1, L.n_chunks, (float*)nullptr);
+    return launch_status();
+  }
+  // segments: their affine maps side by side, the chain of start states, their walks
+  float* aff = (float*)(ws + L.off_aff);
+  float* S0seg = (float*)(ws + L.off_s0);
+  const unsigned nw = (unsigned)(bh * L.nseg);
+  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV, true>), dim3((unsigned)((DV + DPACK) / 16), nw),
+                        dim3(256), 0, st, e1, nullptr, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf,
+                        (const TIn*)v, beta, (const float*)nullptr, (float*)nullptr, (TOut*)nullptr, d->T,
+                        L.n_chunks, (int)L.nseg, L.seg_chunks, aff);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  if (allow_smem(kata::kata_delta_seg_combine<DV>, kata::SEG_COMBINE_SMEM) != KATA_OK) return KATA_ERR_LAUNCH;
+  hipLaunchKernelGGL((kata::kata_delta_seg_combine<DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(kata::SEG_THREADS),
+                     kata::SEG_COMBINE_SMEM, st, (const float*)aff, S0, S0seg, ST, (int)L.nseg);
+  if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
+  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), nw), dim3(512), 0, st,
+                        nullptr, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
+                        (const float*)S0seg, (float*)nullptr, (TOut*)y, d->T, L.n_chunks, (int)L.nseg, L.seg_chunks,
+                        (float*)nullptr);
   return launch_status();
 }
 
@@ -1157,6 +1207,16 @@ kata_status kata_forward_delta_chunked_workspace_bytes(const kata_forward_desc* 
   const kata_status s = validate_delta_chunked(desc);
   if (s != KATA_OK) return s;
   *bytes = delta_chunk_layout(desc).total;
+  return KATA_OK;
+}
+
+kata_status kata_forward_delta_chunked_plan(const kata_forward_desc* desc, int64_t* segments,
+                                            int64_t* segment_chunks) {
+  const kata_status s = validate_delta_chunked(desc);
+  if (s != KATA_OK) return s;
+  const DeltaChunkLayout L = delta_chunk_layout(desc);
+  if (segments) *segments = L.nseg;
+  if (segment_chunks) *segment_chunks = L.seg_chunks;
   return KATA_OK;
 }
 

@@ -394,14 +394,26 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 // packed feature fragments (products of unit-vector components) are hi/lo only for fp32
 // inputs (SPLIT) and single bf16 for bf16 inputs, as the one-factor kernels round theirs.
 // S0/ST [B*H, 256, dv] (nullable; S0 == ST allowed), y [B*H, T, dv].
+//
+// Segments (nseg > 1).  Walk w = blockIdx.y (after the XCD remap) covers the chunks
+// [(w % nseg) seg_chunks, + seg_chunks) of sequence w / nseg, and S0 is that walk's start
+// state, [B*H*nseg, 256, dv] (ST unused).  The chunk transition is affine in S,
+// S <- (I - K^^T T diag(beta) K^) S + K^^T T diag(beta) V, so a segment maps its start
+// state to S_end = M S_start + b.  AFFINE walks (state waves only, 256 threads) compute
+// that map: the value columns from a zero start (b), and DPACK more columns with V = 0
+// that start from the packed unit vectors (column DV + i starts as slot i; M's column i),
+// and write the packed result, aff [B*H*nseg, DPACK, DV + DPACK].
+// kata_delta_seg_combine then chains the maps into every segment's start state, and the
+// segments' walks (y) run side by side instead of one after another.
 constexpr int DKB = 5;   // feature K-blocks of the packed state: delta pairs (0,1) .. (8, 9 = none)
 
-template <typename TIn, typename TOut, int DV>
-__global__ void __launch_bounds__(512)
+template <typename TIn, typename TOut, int DV, bool AFFINE = false>
+__global__ void __launch_bounds__(AFFINE ? 256 : 512, AFFINE ? 4 : 1)
 kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const float* __restrict__ Wh,
                  const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
-                 TOut* __restrict__ y, int64_t T, int64_t n_chunks) {
+                 TOut* __restrict__ y, int64_t T, int64_t n_chunks, int nseg, int64_t seg_chunks,
+                 float* __restrict__ aff) {
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
   __shared__ __align__(16) float Us[DC][P_DIM];
   __shared__ __align__(16) float Wsm[DC][P_DIM];
@@ -410,26 +422,34 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   __shared__ __align__(16) bf16 EB[2][2][WAVE][8];     // E
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool state_role = wave < 4;
+  const bool state_role = AFFINE || wave < 4;
   const int mb = wave & 3;                            // 16-token block of this wave
   const int n = lane & 15, g = lane >> 4;
   // The dv/16 workgroups of a sequence read the same u^, w^ and T.  Workgroups go to the
   // 8 XCDs (each with its own L2) round-robin by linear id, so when B*H is a multiple of 8
   // the ids are remapped to place all column blocks of a sequence on one XCD:
   // id = 8 slot + xcd, sequence = xcd + 8 (slot / NBLK), column block = slot % NBLK.
-  constexpr int NBLK = DV / 16;
+  constexpr int NCOL = AFFINE ? DV + DPACK : DV;    // state columns of the walk
+  constexpr int NBLK = NCOL / 16;
   int j = blockIdx.x;                                 // value column block
-  int64_t bh = blockIdx.y;
+  int64_t bw = blockIdx.y;                            // walk: (sequence, segment)
   if ((gridDim.y & 7) == 0) {
     const int64_t id = (int64_t)blockIdx.y * NBLK + blockIdx.x;
     const int64_t xcd = id & 7, slot = id >> 3;
-    bh = xcd + 8 * (slot / NBLK);
+    bw = xcd + 8 * (slot / NBLK);
     j = (int)(slot % NBLK);
   }
-  const int col = 16 * j + n;                         // value column of this lane
-  // v and beta of this sequence through range-checked buffers: rows past T read 0
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * T * DV, T * DV * (int64_t)sizeof(TIn));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + bh * T, T * 4);
+  const int64_t bh = bw / nseg;                       // sequence
+  const int64_t c0 = (bw % nseg) * seg_chunks;        // its first chunk
+  const int64_t nch = min<int64_t>(seg_chunks, n_chunks - c0);   // chunks of this walk
+  const int64_t tok0 = c0 * DC;
+  const bool couple_on = !AFFINE && nseg == 1;        // progress coupling: whole-sequence walks
+  constexpr int PF = AFFINE ? 1 : 2;                  // chunks of input prefetch
+  const int col = 16 * j + n;                         // state column of this lane
+  const bool vcols = !AFFINE || j < DV / 16;          // (workgroup-uniform) a value column block
+  // v and beta of this walk's tokens through range-checked buffers: rows past T read 0
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (bh * T + tok0) * DV, (T - tok0) * DV * (int64_t)sizeof(TIn));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + bh * T + tok0, (T - tok0) * 4);
 
   auto put = [&](auto& dst, int kk, int slot, const float (&x)[4]) {   // dst [2][K-blocks][WAVE][8]
     bf16x4 hi, lo;
@@ -453,7 +473,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   // part of S0 at the lane's pair {a, b} (full row indices 16 a + b and 16 b + a).
   const bool own8 = state_role && wave == 0;
   auto dl = [&](int jt) { return jt == 2 ? 8 : wave + 4 * jt; };
-  auto s0_at = [&](int a, int b) { return S0[(bh * P_DIM * P_DIM + 16 * a + b) * DV + col]; };
+  auto s0_at = [&](int a, int b) { return S0[(bw * P_DIM * P_DIM + 16 * a + b) * DV + col]; };
   auto sym0 = [&](int a, int b) { return 0.5f * (s0_at(a, b) + s0_at(b, a)); };
   f32x4 Sacc[3];
 #pragma unroll
@@ -461,7 +481,10 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int a = 4 * g + r, b = (a + dl(jt)) & 15;
-      Sacc[jt][r] = (S0 && state_role && (jt < 2 || own8)) ? sym0(a, b) : 0.f;
+      if constexpr (AFFINE)   // value columns from 0, column DV + i from packed slot i
+        Sacc[jt][r] = ((jt < 2 || own8) && col >= DV && 16 * dl(jt) + a == col - DV) ? 1.f : 0.f;
+      else
+        Sacc[jt][r] = (S0 && state_role && (jt < 2 || own8)) ? sym0(a, b) : 0.f;
     }
   }
   // the K-block 4 slots 4..7 stand for delta = 9, which does not exist: zero once
@@ -470,9 +493,11 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     *reinterpret_cast<bf16x4*>(&SB[tid >> 6][DKB - 1][lane][4]) = z;
   }
 
-  // per-chunk inputs, prefetched two chunks ahead into two register sets (the chunk loop
-  // is unrolled by two so each set has a static name).  Threads 0..255 stage u^, threads
-  // 256..511 w^; the state waves also take T (their own hi/lo A-fragments), v and beta.
+  // per-chunk inputs, prefetched PF chunks ahead into PF register sets (for two, the chunk
+  // loop is unrolled by two so each set has a static name).  The AFFINE walks prefetch one
+  // chunk ahead: one register set less keeps four of them on a CU.  Threads 0..255 stage u^, threads
+  // 256..511 w^ (AFFINE: threads 0..255 w^, no u^); the state waves also take T (their own
+  // hi/lo A-fragments), v and beta.
   struct Inputs {
     f32x4 puw;
     Op8<true> pt[2];
@@ -480,10 +505,10 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     float pb[4];
   };
   auto fetch = [&](Inputs& in, int64_t c) {
-    const int64_t rbase = (bh * n_chunks + c) * DC;
-    in.puw = *reinterpret_cast<const f32x4*>((state_role ? Uh : Wh) + rbase * P_DIM + 4 * (tid & 255));
+    const int64_t rbase = (bh * n_chunks + c0 + c) * DC;
+    in.puw = *reinterpret_cast<const f32x4*>(((AFFINE || !state_role) ? Wh : Uh) + rbase * P_DIM + 4 * (tid & 255));
     if (state_role) {
-      const bf16* tf = Tf + (bh * n_chunks + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
+      const bf16* tf = Tf + (bh * n_chunks + c0 + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
@@ -492,7 +517,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
-        in.pv[r] = buf_bits<TIn>(rv, t * DV + col);
+        in.pv[r] = vcols ? buf_bits<TIn>(rv, t * DV + col) : 0u;
         in.pb[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * 4, 0, 0));
       }
     }
@@ -502,7 +527,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
 
   auto step = [&](Inputs& in, int64_t c) {
     // ---- stage: inputs to LDS, packed S to B-fragments (K-block dl / 2, half dl % 2)
-    *reinterpret_cast<f32x4*>((state_role ? &Us[0][0] : &Wsm[0][0]) + 4 * (tid & 255)) = in.puw;
+    *reinterpret_cast<f32x4*>(((AFFINE || !state_role) ? &Wsm[0][0] : &Us[0][0]) + 4 * (tid & 255)) = in.puw;
     const Op8<true> tfr[2] = {in.pt[0], in.pt[1]};
     float vv[4], bb[4];
 #pragma unroll
@@ -521,7 +546,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
       }
     }
     __syncthreads();
-    if (c + 2 < n_chunks) fetch(in, c + 2);
+    if (c + PF < nch) fetch(in, c + PF);
 
     // ---- R = V - K^ S (state waves) or Q^ S (output waves), tokens 16 mb + n, K = packed
     // slot.  xr[m] = components 4g + 4m .. 4g + 4m + 3 (mod 16) of the token's projection,
@@ -627,7 +652,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
       if (mb >= 2) acc = mma<SPLIT, true>(score_frag(1), frag(EB, 1), acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = c * DC + 16 * mb + 4 * g + r;
+        const int64_t t = tok0 + c * DC + 16 * mb + 4 * g + r;
         if (t < T) Elem<TOut>::store(y, (bh * T + t) * DV + col, acc[r]);
       }
     }
@@ -643,7 +668,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   // times.  The wait only orders memory traffic (results do not depend on it), and the
   // poll bound ends it even if a partner never ran.
   constexpr int COUPLE_EVERY = 32, COUPLE_LAG = 32, COUPLE_POLLS = 2048;
-  int* myprog = prog + bh * NBLK;
+  int* myprog = prog + bh * NBLK;   // (only whole-sequence walks couple: bw == bh there)
   auto couple = [&](int64_t cc) {
     if (tid == 0) {
       __hip_atomic_store(myprog + j, (int)cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -660,17 +685,33 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   };
 
   Inputs ia{}, ib{};   // zeroed: the output waves load only puw and never read the rest
-  if (n_chunks > 0) fetch(ia, 0);
-  if (n_chunks > 1) fetch(ib, 1);
-  int64_t c = 0;
-  for (; c + 1 < n_chunks; c += 2) {
-    if (c % COUPLE_EVERY == 0) couple(c);
-    step(ia, c);
-    step(ib, c + 1);
+  if (nch > 0) fetch(ia, 0);
+  if constexpr (PF == 1) {
+    for (int64_t c = 0; c < nch; ++c) step(ia, c);
+  } else {
+    if (nch > 1) fetch(ib, 1);
+    int64_t c = 0;
+    for (; c + 1 < nch; c += 2) {
+      if (couple_on && c % COUPLE_EVERY == 0) couple(c);
+      step(ia, c);
+      step(ib, c + 1);
+    }
+    if (c < nch) step(ia, c);
   }
-  if (c < n_chunks) step(ia, c);
-  if (tid == 0)   // done: nobody waits for this workgroup any more
-    __hip_atomic_store(myprog + j, (int)(n_chunks + COUPLE_LAG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (couple_on && tid == 0)   // done: nobody waits for this workgroup any more
+    __hip_atomic_store(myprog + j, (int)(nch + COUPLE_LAG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (AFFINE) {
+    // the packed state of every owned slot (the repeated delta = 8 slots too), column col
+#pragma unroll
+    for (int jt = 0; jt < 3; ++jt) {
+      if (jt < 2 || own8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          aff[(bw * DPACK + 16 * dl(jt) + 4 * g + r) * NCOL + col] = Sacc[jt][r];
+      }
+    }
+    return;
+  }
   // ST = S0 + the change of the packed state, at both entries (a, b) and (b, a) of each
   // pair, written by the one lane that owns its slot (for delta = 8 the lanes a < 8).  That
   // lane is also the only reader of these S0 entries, so S0 == ST is safe.
@@ -696,5 +737,108 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     }
   }
 }
+
+// grid (dv/16, B*H), block SEG_THREADS: the start state of every segment of a sequence
+// from the segments' affine maps (kata_delta_chunk<..., AFFINE>), in order:
+//   S_0 = the symmetric part of S0 (or 0),  S_{s+1} = M_s S_s + b_s   (packed, fp32),
+// written canonically (both mirror entries of each pair hold the packed value, which is
+// what the walk's initial read takes) to S0seg [B*H*nseg, 256, dv] for the segments'
+// walks; the final S_nseg is exported to ST as the whole-sequence walk exports it
+// (S0 + the packed change, at both entries, so S0's antisymmetric part passes through).
+// Per segment M_s (144 x 144) is staged in LDS (loaded into registers one segment ahead);
+// thread (rg, c) forms rows rg + 36 m (m < 4) of column c, four K entries per LDS read.
+__device__ __forceinline__ int pair_slot(int a, int b) {   // packed slot of the pair {a, b}
+  int dlt = (b - a) & 15, aa = a;
+  if (dlt > 8) {
+    dlt = 16 - dlt;
+    aa = b;
+  } else if (dlt == 8) {
+    aa = a < b ? a : b;                                   // the used slot of delta = 8
+  }
+  return 16 * dlt + aa;
+}
+
+constexpr int SEG_MSTR = DPACK + 4;           // LDS row stride of M (floats)
+constexpr int SEG_RG = 36;                    // row groups: rows rg + 36 m, m < 4
+constexpr int SEG_THREADS = SEG_RG * 16;      // 576: nine waves
+constexpr int SEG_PIECES = DPACK * (DPACK / 4) / SEG_THREADS;   // 16-byte pieces of M per thread (9)
+static_assert(SEG_RG * 4 == DPACK && SEG_PIECES * SEG_THREADS == DPACK * (DPACK / 4), "combine layout");
+
+template <int DV>
+__global__ void __launch_bounds__(SEG_THREADS)
+kata_delta_seg_combine(const float* __restrict__ aff, const float* S0, float* __restrict__ S0seg, float* ST,
+                       int nseg) {
+  constexpr int NCOL = DV + DPACK;
+  extern __shared__ __align__(16) float cmb[];
+  float* Ms = cmb;                                  // [DPACK][SEG_MSTR]
+  float* Sp = cmb + DPACK * SEG_MSTR;               // [16][DPACK]: column-major packed state
+  const int tid = threadIdx.x;
+  const int j = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int rg = tid >> 4, c = tid & 15;
+  auto s0_at = [&](int a, int b, int cc) { return S0[(bh * P_DIM * P_DIM + 16 * a + b) * DV + 16 * j + cc]; };
+  for (int e = tid; e < DPACK * 16; e += SEG_THREADS) {
+    const int slot = e >> 4, cc = e & 15;
+    const int a = slot & 15, b = (a + (slot >> 4)) & 15;
+    Sp[cc * DPACK + slot] = S0 ? 0.5f * (s0_at(a, b, cc) + s0_at(b, a, cc)) : 0.f;
+  }
+  f32x4 mreg[SEG_PIECES];
+  float breg[4];
+  auto load_map = [&](int sg) {
+    const float* blk = aff + (bh * nseg + sg) * DPACK * NCOL;
+#pragma unroll
+    for (int r = 0; r < SEG_PIECES; ++r) {
+      const int e = tid + SEG_THREADS * r;
+      mreg[r] = *reinterpret_cast<const f32x4*>(blk + (e / (DPACK / 4)) * NCOL + DV + 4 * (e % (DPACK / 4)));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) breg[m] = blk[(rg + SEG_RG * m) * NCOL + 16 * j + c];   // b
+  };
+  load_map(0);
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int64_t bw = bh * nseg + sg;
+#pragma unroll
+    for (int r = 0; r < SEG_PIECES; ++r) {
+      const int e = tid + SEG_THREADS * r;
+      *reinterpret_cast<f32x4*>(Ms + (e / (DPACK / 4)) * SEG_MSTR + 4 * (e % (DPACK / 4))) = mreg[r];
+    }
+    float acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = breg[m];
+    __syncthreads();   // M staged; the previous step's state written
+    if (sg + 1 < nseg) load_map(sg + 1);
+    for (int e = tid; e < 256 * 16; e += SEG_THREADS) {   // this segment's start state
+      const int ab = e >> 4, cc = e & 15;
+      S0seg[(bw * 256 + ab) * DV + 16 * j + cc] = Sp[cc * DPACK + pair_slot(ab >> 4, ab & 15)];
+    }
+    for (int k = 0; k < DPACK; k += 4) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(Sp + c * DPACK + k);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(Ms + (rg + SEG_RG * m) * SEG_MSTR + k);
+        acc[m] += mv[0] * sv[0] + mv[1] * sv[1] + mv[2] * sv[2] + mv[3] * sv[3];
+      }
+    }
+    __syncthreads();   // every thread has read the state and M
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Sp[c * DPACK + rg + SEG_RG * m] = acc[m];
+  }
+  __syncthreads();
+  if (ST) {   // one thread per pair a <= b and column writes both entries (S0 == ST allowed)
+    for (int e = tid; e < 256 * 16; e += SEG_THREADS) {
+      const int ab = e >> 4, cc = e & 15, a = ab >> 4, b = ab & 15;
+      if (a > b) continue;
+      float sab = 0.f, sba = 0.f, ch = Sp[cc * DPACK + pair_slot(a, b)];
+      if (S0) {
+        sab = s0_at(a, b, cc);
+        sba = s0_at(b, a, cc);
+        ch -= 0.5f * (sab + sba);
+      }
+      ST[(bh * P_DIM * P_DIM + 16 * a + b) * DV + 16 * j + cc] = sab + ch;
+      if (a != b) ST[(bh * P_DIM * P_DIM + 16 * b + a) * DV + 16 * j + cc] = sba + ch;
+    }
+  }
+}
+constexpr int SEG_COMBINE_SMEM = (DPACK * SEG_MSTR + 16 * DPACK) * 4;
 
 }  // namespace kata

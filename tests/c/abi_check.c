@@ -30,6 +30,11 @@ int main(void) {
   CHECK(kata_forward_factors_workspace_bytes(&d, 2, KATA_FACTORS_CONCAT, &bytes) == KATA_OK && bytes > 0);
   CHECK(kata_forward_factors_workspace_bytes(&d, 2, KATA_FACTORS_SUM, &bytes) == KATA_OK && bytes > 0);
   CHECK(kata_forward_delta_chunked_workspace_bytes(&d, &bytes) == KATA_OK && bytes > 0);
+  {
+    int64_t segs = 0, seg_chunks = 0;
+    CHECK(kata_forward_delta_chunked_plan(&d, &segs, &seg_chunks) == KATA_OK && segs >= 1 && seg_chunks >= 1);
+    CHECK(kata_forward_delta_chunked_plan(&d, NULL, NULL) == KATA_OK);
+  }
   CHECK(kata_forward_workspace_bytes(NULL, &bytes) == KATA_ERR_NULL);
   CHECK(kata_forward_workspace_bytes(&d, NULL) == KATA_ERR_NULL);
   d.p = 8;

@@ -320,8 +320,35 @@ def test_delta_chunked_workspace_and_validation():
     assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
     chunks = 131072 // 64
     uw = 16 * chunks * 64 * 16 * 4
-    # u^, w^ and T per chunk, then one progress counter per column-block workgroup of the walk
-    assert n.value == 2 * uw + 16 * chunks * 64 * 64 * 4 + 16 * (64 // 16) * 4
+
+    def align(x):
+        return (x + 255) // 256 * 256
+    # u^, w^ and T per chunk, then one progress counter per column-block workgroup of the walk;
+    # 16 sequences fill 64 of 1024 workgroup slots, so the plan cuts each walk into 16
+    # segments of 128 chunks: their affine maps (144 x (64 + 144) floats) and start states
+    # (256 x 64 floats)
+    head = 2 * uw + 16 * chunks * 64 * 64 * 4 + align(16 * (64 // 16) * 4)
+    assert n.value == head + 16 * 16 * 144 * (64 + 144) * 4 + 16 * 16 * 256 * 64 * 4
+    # one walk per sequence: no segment blocks
+    d.scan = Bd.KATA_SCAN_SEQUENTIAL
+    assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    assert n.value == head
+    # explicit segments of 100 chunks: 21 per sequence, the last of 48 chunks
+    d.scan, d.scan_leaf = Bd.KATA_SCAN_ASSOC, 100
+    assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
+    assert n.value == head + 16 * 21 * 144 * 208 * 4 + 16 * 21 * 256 * 64 * 4
+    segs, per = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.kata_forward_delta_chunked_plan(ctypes.byref(d), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
+    assert (segs.value, per.value) == (21, 100)
+    d.scan_leaf = 0
+    assert lib.kata_forward_delta_chunked_plan(ctypes.byref(d), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
+    assert (segs.value, per.value) == (16, 128)
+    # 256 x 16 sequences already fill the GPU: one walk each; few chunks: at least 16 per segment
+    for B, T, want in [(256, 8192, (1, 128)), (1, 64 * 40, (2, 20)), (1, 64 * 31, (1, 31))]:
+        e = Bd.make_desc(B, 16, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+        assert lib.kata_forward_delta_chunked_plan(ctypes.byref(e), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
+        assert (segs.value, per.value) == want, (B, T)
+    assert lib.kata_forward_delta_chunked_plan(None, None, None) == Bd.KATA_ERR_NULL
     fake = ctypes.c_void_p(0x1000)
     for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),
                            ({"p": 8}, Bd.KATA_ERR_UNSUPPORTED), ({"T": -1}, Bd.KATA_ERR_SHAPE),

@@ -305,6 +305,67 @@ def test_delta_chunked_equals_recurrent_lm340m():
     assert ey <= TOL_BF16 and sy <= 5e-3 and sS <= 5e-3
 
 
+@pytest.mark.parametrize("dtype,leaf", [("f32", 1), ("f32", 3), ("bf16", 1), ("bf16", 2), ("bf16", 4)])
+def test_delta_chunked_segments_against_oracle(dtype, leaf):
+    """Segmented walks (scan_leaf chunks per segment; the last segment ragged where the
+    chunk count does not divide): each segment's affine map S_end = M S_start + b, their
+    chain, and the segments' walks side by side, against the oracle's recurrence and the
+    one-walk-per-sequence form, with an asymmetric initial state (its antisymmetric part
+    reaches S_T unchanged) and the final state."""
+    if dtype == "f32":
+        case = I.make_forward("tiny", seed=190 + leaf)
+        B, H, T = case.q.shape[:3]
+        dv = 16
+    else:
+        B, H, T, dv = 2, 3, 300 + 37 * leaf, 64
+        case = I.make_forward("mid", B=B, H=H, T=T, seed=190 + leaf)
+    beta = I.make_beta(B, H, T, seed=190 + leaf, lo=0.0, hi=1.0)
+    S0 = torch.randn((B, H, 256, dv), generator=torch.Generator().manual_seed(190 + leaf)) / 4
+    q, k, v, P, b, S0d = to_dev(case.q, case.k, case.v, case.P, beta, S0)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, S0=S0d, out_dtype=torch.float32, return_state=True,
+                                       scan_leaf=leaf)
+    y1, S1 = kata.forward_delta_chunked(q, k, v, P, b, S0=S0d, out_dtype=torch.float32, return_state=True,
+                                        scan="sequential")
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                                beta.double().numpy(), S0.double().numpy())
+    ey = row_rel(y.double().cpu().numpy(), yr)
+    sy, sS = slice_rel(y.cpu().numpy(), yr), slice_rel(ST.cpu().numpy(), Sr)
+    dy, dS = slice_rel(y.cpu().numpy(), y1.cpu().numpy()), slice_rel(ST.cpu().numpy(), S1.cpu().numpy())
+    St = ST.cpu().reshape(B, H, 16, 16, dv)
+    A0 = S0.reshape(B, H, 16, 16, dv)
+    eA = float((St - St.transpose(2, 3) - (A0 - A0.transpose(2, 3))).abs().max())
+    print(f"[delta segments {dtype} leaf={leaf}] rel y rows {ey:.3e} slices {sy:.3e} S_T {sS:.3e}; "
+          f"vs one walk y {dy:.3e} S {dS:.3e}; antisymmetric part {eA:.1e}", flush=True)
+    if dtype == "f32":
+        assert sy <= TOL_F32 and sS <= TOL_F32 and ey <= 1e-3
+    else:
+        assert ey <= TOL_BF16 and sy <= 5e-3 and sS <= 5e-3
+    assert dy <= 5e-3 and dS <= 5e-3
+    assert eA <= 1e-5 * float(A0.abs().max())
+
+
+def test_delta_chunked_segments_beta_zero_keep_state_exactly():
+    """beta = 0 with one-chunk segments: every map is the identity with b = 0 in exact
+    arithmetic (no correction is formed), so the chain hands every segment S0's symmetric
+    part and S_T equals S0 bit for bit, also in place."""
+    case = I.make_forward("mid", B=1, H=2, T=200, seed=85)
+    S0 = torch.randn((1, 2, 256, 64), generator=torch.Generator().manual_seed(85))
+    q, k, v, P, S0d = to_dev(case.q, case.k, case.v, case.P, S0)
+    b = torch.zeros((1, 2, 200), device=DEV)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, S0=S0d, out_dtype=torch.float32, return_state=True,
+                                       scan_leaf=1)
+    torch.cuda.synchronize()
+    assert torch.equal(ST.cpu(), S0)
+    inplace = S0d.clone()
+    kata.forward_delta_chunked(q, k, v, P, b, S0=inplace, out_dtype=torch.float32, ST=inplace, scan_leaf=1)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace.cpu(), S0)
+    yr, _ = O.delta_recurrence(host64(case.q), host64(case.k), host64(case.v), case.P.double().numpy(),
+                               np.zeros((1, 2, 200)), S0.double().numpy())
+    assert slice_rel(y.cpu().numpy(), yr) <= 5e-3 and row_rel(y.double().cpu().numpy(), yr) <= 2e-2
+
+
 def test_delta_chunked_long_prefix_and_final_state():
     """The long-context shape (B=1, H=16, T=131072) in the launch configuration the
     benchmark uses: the first 2048 tokens of two heads and their final states against the
@@ -322,8 +383,12 @@ def test_delta_chunked_long_prefix_and_final_state():
                                host64(case.v[:, heads, :m]), case.P[heads].double().numpy(),
                                beta[:, heads, :m].double().numpy())
     ey = row_rel(y[:, heads, :m].double().cpu().numpy(), yr)
-    _, Sr = O.delta_recurrence(host64(case.q[:, heads]), host64(case.k[:, heads]), host64(case.v[:, heads]),
-                               case.P[heads].double().numpy(), beta[:, heads].double().numpy())
+    yall, Sr = O.delta_recurrence(host64(case.q[:, heads]), host64(case.k[:, heads]), host64(case.v[:, heads]),
+                                  case.P[heads].double().numpy(), beta[:, heads].double().numpy())
     eS = row_rel(ST[:, heads].double().cpu().numpy().reshape(2, -1), Sr.reshape(2, -1))
-    print(f"[delta chunked long] y prefix {ey:.3e} S_T {eS:.3e}", flush=True)
-    assert ey <= TOL_BF16 and eS <= TOL_BF16
+    # rows in later segments of the library's plan (16 segments of 8192 tokens here),
+    # around a segment boundary and at the end
+    rows = np.r_[8192 * 7 - 64: 8192 * 7 + 64, T - 512: T]
+    eL = row_rel(y[:, heads][:, :, rows].double().cpu().numpy(), yall[:, :, rows])
+    print(f"[delta chunked long] y prefix {ey:.3e} later rows {eL:.3e} S_T {eS:.3e}", flush=True)
+    assert ey <= TOL_BF16 and eL <= TOL_BF16 and eS <= TOL_BF16

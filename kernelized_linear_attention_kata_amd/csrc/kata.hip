@@ -579,8 +579,10 @@ struct DeltaChunkLayout {
 // Cut into segments, the segments' affine maps are formed side by side, chained in a short
 // pass, and the segments' walks run side by side.  The library segments where the walks
 // fill fewer than a quarter of the workgroup slots (4 per CU): nseg = 1024 / (B*H*dv/16),
-// at least 16 chunks per segment.  desc->scan_leaf > 0 sets the chunks per segment, and
-// KATA_SCAN_SEQUENTIAL one walk per sequence.
+// at most kDeltaMaxSegments (the chain visits the segments in order, about 10 us each)
+// and at least 16 chunks per segment.  desc->scan_leaf > 0 sets the chunks per segment,
+// and KATA_SCAN_SEQUENTIAL one walk per sequence.
+constexpr int64_t kDeltaMaxSegments = 32;
 int64_t delta_segments(const kata_forward_desc* d, int64_t n_chunks, int64_t* seg_chunks) {
   const int64_t walks = d->B * d->H * (d->dv / 16);
   int64_t per = n_chunks;
@@ -590,6 +592,7 @@ int64_t delta_segments(const kata_forward_desc* d, int64_t n_chunks, int64_t* se
     per = d->scan_leaf < n_chunks ? d->scan_leaf : n_chunks;
   } else if (walks > 0 && walks < kComputeUnits * 4) {
     int64_t want = (kComputeUnits * 4) / walks;
+    if (want > kDeltaMaxSegments) want = kDeltaMaxSegments;
     if (want > n_chunks / 16) want = n_chunks / 16;
     if (want > 1) per = (n_chunks + want - 1) / want;
   }

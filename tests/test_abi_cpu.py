@@ -344,10 +344,12 @@ def test_delta_chunked_workspace_and_validation():
     assert lib.kata_forward_delta_chunked_plan(ctypes.byref(d), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
     assert (segs.value, per.value) == (16, 128)
     # 256 x 16 sequences already fill the GPU: one walk each; few chunks: at least 16 per segment
-    for B, T, want in [(256, 8192, (1, 128)), (1, 64 * 40, (2, 20)), (1, 64 * 31, (1, 31))]:
-        e = Bd.make_desc(B, 16, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+    # one sequence: at most 32 segments (the chain visits them in order)
+    for B, H, T, want in [(256, 16, 8192, (1, 128)), (1, 16, 64 * 40, (2, 20)), (1, 16, 64 * 31, (1, 31)),
+                          (1, 1, 131072, (32, 64))]:
+        e = Bd.make_desc(B, H, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
         assert lib.kata_forward_delta_chunked_plan(ctypes.byref(e), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
-        assert (segs.value, per.value) == want, (B, T)
+        assert (segs.value, per.value) == want, (B, H, T)
     assert lib.kata_forward_delta_chunked_plan(None, None, None) == Bd.KATA_ERR_NULL
     fake = ctypes.c_void_p(0x1000)
     for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),

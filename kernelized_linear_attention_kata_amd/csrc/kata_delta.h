@@ -242,6 +242,7 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   __shared__ __align__(16) float Ps[P_DIM][64 + 4];
   __shared__ __align__(16) float ws[DC][P_DIM];
   __shared__ __align__(16) float G[DC][DC + 4];
+  __shared__ float bs[DC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x, bh = blockIdx.y;
   const int h = (int)(bh % H);
@@ -305,45 +306,93 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   *reinterpret_cast<f32x4*>(Uo + row * P_DIM + 4 * qq) = uh;
   *reinterpret_cast<f32x4*>(Wo + row * P_DIM + 4 * qq) = wh;
   *reinterpret_cast<f32x4*>(&ws[tl][4 * qq]) = wh;
+  if (qq == 0) bs[tl] = live ? beta[bh * T + t] : 0.f;
   __syncthreads();
-  // G[t][s] = beta_t (w^_t . w^_s)^2 for s < t: thread (t = tl, s = 16 qq .. 16 qq + 15)
-  {
-    const float bt = live ? beta[bh * T + t] : 0.f;
-    f32x4 wt[4];
+  // 16 x 16 blocks of the chunk's 64 x 64 matrices on the fp32 matrix cores
+  // (v_mfma_f32_16x16x4_f32, wave64: A lane l holds A[l%16][k = l/16], B lane l holds
+  // B[k = l/16][l%16], D lane l holds D[4(l/16) + i][l%16], i = 0..3).
+  const int m16 = lane & 15, k4 = lane >> 4;
+  // G[t][s] = beta_t (w^_t . w^_s)^2 for s < t, the ten blocks (bt, bs), bt >= bs, over the
+  // four waves (the blocks above the diagonal are not read as G)
+  for (int tile = wave; tile < 10; tile += 4) {
+    const int bt = tile < 1 ? 0 : (tile < 3 ? 1 : (tile < 6 ? 2 : 3));
+    const int bsb = tile - bt * (bt + 1) / 2;
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int m = 0; m < 4; ++m) wt[m] = *reinterpret_cast<const f32x4*>(&ws[tl][4 * m]);
+    for (int kk = 0; kk < 4; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ws[16 * bt + m16][4 * kk + k4], ws[16 * bsb + m16][4 * kk + k4],
+                                                 acc, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int sidx = 16 * qq + i;
-      float dp = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 wsv = *reinterpret_cast<const f32x4*>(&ws[sidx][4 * m]);
-        dp += wt[m][0] * wsv[0] + wt[m][1] * wsv[1] + wt[m][2] * wsv[2] + wt[m][3] * wsv[3];
-      }
-      G[tl][sidx] = sidx < tl ? bt * dp * dp : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int tr = 16 * bt + 4 * k4 + i, sc = 16 * bsb + m16;
+      G[tr][sc] = sc < tr ? bs[tr] * acc[i] * acc[i] : 0.f;
     }
   }
   __syncthreads();
-  // T = (I + G)^{-1} by forward substitution, one column per lane of wave 0:
-  // x_t = [t == j] - sum_{s < t} G[t][s] x_s, all columns in lockstep (G reads broadcast).
+  // T = (I + G)^{-1} by blocks (I + G is unit lower triangular).  Diagonal blocks by forward
+  // substitution, one column per lane of wave 0 (lane (b, c): column c of block b), written
+  // over their G blocks.  Then T_ij = -T_ii (sum_{k = j}^{i-1} G_ik T_kj) for i - j = 1, 2, 3
+  // on the matrix cores; T_ij (i > j) is kept in block (j, i) above the diagonal, which G
+  // does not use, until the last level.
   if (wave == 0) {
-    float x[DC];
+    const int b = lane >> 4, cc = lane & 15;
+    float x[16];
 #pragma unroll
-    for (int tt = 0; tt < DC; ++tt) {
-      float acc[4] = {tt == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 16; ++r) {
+      float acc0 = r == cc ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int s4 = 0; s4 < tt; s4 += 4) {
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(&G[tt][s4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (s4 + e < tt) acc[e] -= gv[e] * x[s4 + e];
+      for (int s2 = 0; s2 < r; ++s2) {
+        if (s2 & 1) acc1 -= G[16 * b + r][16 * b + s2] * x[s2];
+        else acc0 -= G[16 * b + r][16 * b + s2] * x[s2];
       }
-      x[tt] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      x[r] = acc0 + acc1;
     }
-    // T back into LDS (over G, which is no longer read) for the fragment transpose
 #pragma unroll
-    for (int tt = 0; tt < DC; ++tt) G[tt][lane] = x[tt];
+    for (int r = 0; r < 16; ++r) G[16 * b + r][16 * b + cc] = x[r];
+  }
+  __syncthreads();
+  // element (r, c) of block matrix X_ij: G_ij (i > j) at [16i + r][16j + c]; T_ij (i > j) at
+  // [16j + r][16i + c]; T_ii at [16i + r][16i + c]
+  auto gref = [&](int i, int j, int r, int c) -> float& { return G[16 * i + r][16 * j + c]; };
+  auto tref = [&](int i, int j, int r, int c) -> float& {
+    return i > j ? G[16 * j + r][16 * i + c] : G[16 * i + r][16 * i + c];
+  };
+  for (int lev = 1; lev < 4; ++lev) {
+    const int i = lev + wave, j = wave;           // wave w: block (w + lev, w)
+    if (i < 4) {
+      f32x4 xacc = zero4();
+      for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          xacc = __builtin_amdgcn_mfma_f32_16x16x4f32(gref(i, kb, m16, 4 * kk + k4), tref(kb, j, 4 * kk + k4, m16),
+                                                      xacc, 0, 0, 0);
+      }
+      // X as the B operand: lane l needs X[4kk + l/16][l%16], held by lane 16kk + l%16 in its
+      // accumulator entry l/16
+      f32x4 tacc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int src = (16 * kk + m16) * 4;
+        float xb = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(xacc[e])));
+          xb = e == k4 ? v : xb;
+        }
+        tacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tref(i, i, m16, 4 * kk + k4), xb, tacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tref(i, j, 4 * k4 + e, m16) = -tacc[e];
+    }
+    __syncthreads();
+  }
+  // T_ij (i > j) from block (j, i) to block (i, j); block (j, i) becomes 0
+  for (int e = tid; e < 6 * 256; e += 256) {
+    const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+    const int i = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3), j = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+    const float v = G[16 * j + r][16 * i + cc];
+    G[16 * i + r][16 * j + cc] = v;
+    G[16 * j + r][16 * i + cc] = 0.f;
   }
   __syncthreads();
   // fragments: thread handles (mb, kk, lane') for two of the 4 x 2 x 64 combinations

@@ -635,7 +635,7 @@ def bench_delta_forward(args):
     nseg, seg_chunks = plan["segments"], plan["segment_chunks"]
     dmode = "delta_seq" if args.scan == "sequential" else "delta"
     if nseg > 1:
-        walk_how = (f"each head's walk cut into {nseg} segments of {seg_chunks} chunks: the segments' affine maps "
+        walk_how = (f"each head's walk cut into {nseg} segments of {seg_chunks} chunks: the affine maps of all but the last segment "
                     f"({(dv + 144) // 16} column blocks each) side by side, their chain, then the segments' walks "
                     f"side by side, {B * H * nseg * (dv // 16)} workgroups")
     else:

@@ -468,16 +468,19 @@ kata_status kata_forward_delta(const kata_forward_desc* desc,
  * device workspace of kata_forward_delta_chunked_workspace_bytes bytes (normalised
  * projections and T per chunk: 9 KiB per 64 tokens and head; one int per walk workgroup
  * that keeps a sequence's workgroups within a few chunks of each other, so they share
- * their inputs in L2; and with segments, below, 144 x (dv + 144) + 256 x dv floats per
- * segment), owned by the caller; calls that overlap on one workspace race.
+ * their inputs in L2; and with segments, below, 256 x dv floats per segment and
+ * 144 x (dv + 144) per segment but the last of each sequence), owned by the caller; calls
+ * that overlap on one workspace race.
  * The walk of a sequence is split over dv/16 workgroups (value-column blocks of S) and
  * keeps the state's symmetric part packed (the antisymmetric part of S0, which no read
  * sees, reaches ST unchanged).  Segments: the chunk transition is affine in S, so with few
  * sequences the walk is cut into segments (kata_forward_delta_chunked_plan): each
  * segment's map S_end = M S_start + b is formed side by side (M from the packed unit
- * vectors), the maps are chained into every segment's start state, and the segments'
- * walks run side by side.  desc->scan_leaf > 0 sets the chunks per segment and
- * KATA_SCAN_SEQUENTIAL one walk per sequence; 0 lets the library choose.  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),
+ * vectors; not for the last segment, whose walk exports ST, nor M for the first without
+ * S0), the maps are chained into every segment's start state, and the segments' walks run
+ * side by side.  desc->scan_leaf > 0 sets the chunks per segment and
+ * KATA_SCAN_SEQUENTIAL one walk per sequence; 0 lets the library choose.  Either way the
+ * plan keeps B*H*segments <= 65535 (longer segments where scan_leaf asks for more).  Supported: p = 16, (d, dv) = (16, 16) or (64, 64),
  * desc->chunk = 64, in/out dtype F32 or BF16, B*H <= 65535, and a sequence of q, k, v
  * or y under 2 GiB at 4 bytes per element (T * max(d, dv) * 4 < 2^31 - 4096, less 256
  * tokens; else KATA_ERR_SHAPE: the walk addresses a sequence with 32-bit offsets).

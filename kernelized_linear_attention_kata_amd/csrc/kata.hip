@@ -581,10 +581,12 @@ struct DeltaChunkLayout {
 // fill fewer than a quarter of the workgroup slots (4 per CU): nseg = 1024 / (B*H*dv/16),
 // at most kDeltaMaxSegments (the chain visits the segments in order, about 10 us each)
 // and at least 16 chunks per segment.  desc->scan_leaf > 0 sets the chunks per segment,
-// and KATA_SCAN_SEQUENTIAL one walk per sequence.
+// and KATA_SCAN_SEQUENTIAL one walk per sequence.  Either way B*H*nseg stays within the
+// 65535 workgroup rows of a launch (the segments' walks are its rows).
 constexpr int64_t kDeltaMaxSegments = 32;
 int64_t delta_segments(const kata_forward_desc* d, int64_t n_chunks, int64_t* seg_chunks) {
-  const int64_t walks = d->B * d->H * (d->dv / 16);
+  const int64_t bh = d->B * d->H;
+  const int64_t walks = bh * (d->dv / 16);
   int64_t per = n_chunks;
   if (d->scan == KATA_SCAN_SEQUENTIAL || n_chunks == 0) {
     per = n_chunks;
@@ -597,13 +599,18 @@ int64_t delta_segments(const kata_forward_desc* d, int64_t n_chunks, int64_t* se
     if (want > 1) per = (n_chunks + want - 1) / want;
   }
   if (per < 1) per = 1;
+  if (bh > 0) {   // at most 65535 / (B*H) segments per sequence
+    const int64_t most = 65535 / bh;
+    if ((n_chunks + per - 1) / per > most) per = (n_chunks + most - 1) / most;
+  }
   *seg_chunks = per;
   return n_chunks == 0 ? 1 : (n_chunks + per - 1) / per;   // no empty segment
 }
 
 // u^, w^ (fp32), T (hi/lo bf16 fragments), then the walk's progress counters (one int per
-// column-block workgroup); with segments, their affine maps [B*H*nseg, 144, dv + 144] and
-// start states [B*H*nseg, 256, dv] (fp32).
+// column-block workgroup); with segments, the affine maps of all but the last segment of
+// each sequence [B*H*(nseg - 1), 144, dv + 144] and every segment's start state
+// [B*H*nseg, 256, dv] (fp32).
 DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   DeltaChunkLayout L;
   const int64_t bh = d->B * d->H;
@@ -615,7 +622,8 @@ DeltaChunkLayout delta_chunk_layout(const kata_forward_desc* d) {
   L.off_prog = L.off_t + align256((size_t)bh * (size_t)L.n_chunks * kata::DC * kata::DC * 2 * sizeof(bf16));
   L.off_aff = L.off_prog + align256((size_t)bh * (size_t)(d->dv / 16) * sizeof(int));
   const size_t nw = L.nseg > 1 ? (size_t)bh * (size_t)L.nseg : 0;
-  L.off_s0 = L.off_aff + align256(nw * DPACK * (size_t)(d->dv + DPACK) * sizeof(float));
+  const size_t nmaps = L.nseg > 1 ? (size_t)bh * (size_t)(L.nseg - 1) : 0;
+  L.off_s0 = L.off_aff + align256(nmaps * DPACK * (size_t)(d->dv + DPACK) * sizeof(float));
   L.total = L.off_s0 + nw * P_DIM * P_DIM * (size_t)d->dv * sizeof(float);
   return L;
 }
@@ -649,25 +657,27 @@ kata_status run_delta_chunked(const kata_forward_desc* d, const DeltaChunkLayout
   if (L.nseg == 1) {
     hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), (unsigned)bh),
                           dim3(512), 0, st, e1, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf,
-                          (const TIn*)v, beta, S0, ST, (TOut*)y, d->T, L.n_chunks, 1, L.n_chunks, (float*)nullptr);
+                          (const TIn*)v, beta, S0, ST, S0, (TOut*)y, d->T, L.n_chunks, 1, L.n_chunks,
+                          (float*)nullptr);
     return launch_status();
   }
-  // segments: their affine maps side by side, the chain of start states, their walks
+  // segments: the affine maps of all but the last segment side by side (the last
+  // segment's walk ends the sequence and exports S_T itself), the chain of start states,
+  // the segments' walks
   float* aff = (float*)(ws + L.off_aff);
   float* S0seg = (float*)(ws + L.off_s0);
-  const unsigned nw = (unsigned)(bh * L.nseg);
-  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV, true>), dim3((unsigned)((DV + DPACK) / 16), nw),
+  const unsigned nmaps = (unsigned)(bh * (L.nseg - 1)), nw = (unsigned)(bh * L.nseg);
+  hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV, true>), dim3((unsigned)((DV + DPACK) / 16), nmaps),
                         dim3(256), 0, st, e1, nullptr, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf,
-                        (const TIn*)v, beta, (const float*)nullptr, (float*)nullptr, (TOut*)nullptr, d->T,
-                        L.n_chunks, (int)L.nseg, L.seg_chunks, aff);
+                        (const TIn*)v, beta, S0, (float*)nullptr, (const float*)nullptr, (TOut*)nullptr, d->T,
+                        L.n_chunks, (int)(L.nseg - 1), L.seg_chunks, aff);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
-  if (allow_smem(kata::kata_delta_seg_combine<DV>, kata::SEG_COMBINE_SMEM) != KATA_OK) return KATA_ERR_LAUNCH;
   hipLaunchKernelGGL((kata::kata_delta_seg_combine<DV>), dim3((unsigned)(DV / 16), (unsigned)bh), dim3(kata::SEG_THREADS),
-                     kata::SEG_COMBINE_SMEM, st, (const float*)aff, S0, S0seg, ST, (int)L.nseg);
+                     0, st, (const float*)aff, S0, S0seg, (int)L.nseg);
   if (launch_status() != KATA_OK) return KATA_ERR_LAUNCH;
   hipExtLaunchKernelGGL((kata::kata_delta_chunk<TIn, TOut, DV>), dim3((unsigned)(DV / 16), nw), dim3(512), 0, st,
                         nullptr, e2, 0, prog, (const float*)U, (const float*)W, (const bf16*)Tf, (const TIn*)v, beta,
-                        (const float*)S0seg, (float*)nullptr, (TOut*)y, d->T, L.n_chunks, (int)L.nseg, L.seg_chunks,
+                        (const float*)S0seg, ST, S0, (TOut*)y, d->T, L.n_chunks, (int)L.nseg, L.seg_chunks,
                         (float*)nullptr);
   return launch_status();
 }

@@ -446,14 +446,18 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 //
 // Segments (nseg > 1).  Walk w = blockIdx.y (after the XCD remap) covers the chunks
 // [(w % nseg) seg_chunks, + seg_chunks) of sequence w / nseg, and S0 is that walk's start
-// state, [B*H*nseg, 256, dv] (ST unused).  The chunk transition is affine in S,
-// S <- (I - K^^T T diag(beta) K^) S + K^^T T diag(beta) V, so a segment maps its start
-// state to S_end = M S_start + b.  AFFINE walks (state waves only, 256 threads) compute
-// that map: the value columns from a zero start (b), and DPACK more columns with V = 0
+// state, [B*H*nseg, 256, dv].  The walk of the last segment exports ST (S0x: the
+// sequence's own initial state, whose antisymmetric part passes through).  The chunk
+// transition is affine in S, S <- (I - K^^T T diag(beta) K^) S + K^^T T diag(beta) V, so
+// a segment maps its start state to S_end = M S_start + b.  AFFINE walks (state waves
+// only, 256 threads) compute that map for every segment but the last (nseg = segments
+// - 1 there): the value columns from a zero start (b), and DPACK more columns with V = 0
 // that start from the packed unit vectors (column DV + i starts as slot i; M's column i),
-// and write the packed result, aff [B*H*nseg, DPACK, DV + DPACK].
-// kata_delta_seg_combine then chains the maps into every segment's start state, and the
-// segments' walks (y) run side by side instead of one after another.
+// and write the packed result, aff [B*H*nseg, DPACK, DV + DPACK].  S0 is then only a flag:
+// without an initial state, segment 0's start is 0, so its M is never used and its M
+// column blocks return at once.  kata_delta_seg_combine then chains the maps into every
+// segment's start state, and the segments' walks (y) run side by side instead of one
+// after another.
 constexpr int DKB = 5;   // feature K-blocks of the packed state: delta pairs (0,1) .. (8, 9 = none)
 
 template <typename TIn, typename TOut, int DV, bool AFFINE = false>
@@ -461,8 +465,8 @@ __global__ void __launch_bounds__(AFFINE ? 256 : 512, AFFINE ? 4 : 1)
 kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const float* __restrict__ Wh,
                  const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
-                 TOut* __restrict__ y, int64_t T, int64_t n_chunks, int nseg, int64_t seg_chunks,
-                 float* __restrict__ aff) {
+                 const float* S0x, TOut* __restrict__ y, int64_t T, int64_t n_chunks, int nseg,
+                 int64_t seg_chunks, float* __restrict__ aff) {
   constexpr bool SPLIT = sizeof(TIn) == 4;   // feature fragments split
   __shared__ __align__(16) float Us[DC][P_DIM];
   __shared__ __align__(16) float Wsm[DC][P_DIM];
@@ -489,13 +493,15 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     j = (int)(slot % NBLK);
   }
   const int64_t bh = bw / nseg;                       // sequence
-  const int64_t c0 = (bw % nseg) * seg_chunks;        // its first chunk
+  const int64_t seg = bw % nseg;                      // segment
+  const int64_t c0 = seg * seg_chunks;                // its first chunk
   const int64_t nch = min<int64_t>(seg_chunks, n_chunks - c0);   // chunks of this walk
   const int64_t tok0 = c0 * DC;
   const bool couple_on = !AFFINE && nseg == 1;        // progress coupling: whole-sequence walks
   constexpr int PF = AFFINE ? 1 : 2;                  // chunks of input prefetch
   const int col = 16 * j + n;                         // state column of this lane
   const bool vcols = !AFFINE || j < DV / 16;          // (workgroup-uniform) a value column block
+  if (AFFINE && !vcols && seg == 0 && !S0) return;    // segment 0 starts from 0: M unused
   // v and beta of this walk's tokens through range-checked buffers: rows past T read 0
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (bh * T + tok0) * DV, (T - tok0) * DV * (int64_t)sizeof(TIn));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + bh * T + tok0, (T - tok0) * 4);
@@ -761,10 +767,12 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     }
     return;
   }
-  // ST = S0 + the change of the packed state, at both entries (a, b) and (b, a) of each
-  // pair, written by the one lane that owns its slot (for delta = 8 the lanes a < 8).  That
-  // lane is also the only reader of these S0 entries, so S0 == ST is safe.
-  if (ST && state_role) {
+  // ST = S0x + the change of the packed state since the sequence's start, at both entries
+  // (a, b) and (b, a) of each pair, written by the one lane that owns its slot (for
+  // delta = 8 the lanes a < 8) in the walk of the last segment.  That lane is also the
+  // only reader of these S0x entries, so S0x == ST is safe.
+  auto s0x_at = [&](int a, int b) { return S0x[(bh * P_DIM * P_DIM + 16 * a + b) * DV + col]; };
+  if (ST && state_role && seg == nseg - 1) {
 #pragma unroll
     for (int jt = 0; jt < 3; ++jt) {
       if (jt < 2 || own8) {
@@ -774,9 +782,9 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
           const int a = 4 * g + r, b = (a + d) & 15;
           if (d == 8 && a >= 8) continue;
           float sab = 0.f, sba = 0.f, ch = Sacc[jt][r];
-          if (S0) {
-            sab = s0_at(a, b);
-            sba = s0_at(b, a);
+          if (S0x) {
+            sab = s0x_at(a, b);
+            sba = s0x_at(b, a);
             ch -= 0.5f * (sab + sba);
           }
           ST[(bh * P_DIM * P_DIM + 16 * a + b) * DV + col] = sab + ch;
@@ -788,14 +796,16 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
 }
 
 // grid (dv/16, B*H), block SEG_THREADS: the start state of every segment of a sequence
-// from the segments' affine maps (kata_delta_chunk<..., AFFINE>), in order:
+// from the affine maps of the segments before it (kata_delta_chunk<..., AFFINE>, aff
+// [B*H*(nseg - 1), DPACK, dv + DPACK]), in order:
 //   S_0 = the symmetric part of S0 (or 0),  S_{s+1} = M_s S_s + b_s   (packed, fp32),
 // written canonically (both mirror entries of each pair hold the packed value, which is
 // what the walk's initial read takes) to S0seg [B*H*nseg, 256, dv] for the segments'
-// walks; the final S_nseg is exported to ST as the whole-sequence walk exports it
-// (S0 + the packed change, at both entries, so S0's antisymmetric part passes through).
-// Per segment M_s (144 x 144) is staged in LDS (loaded into registers one segment ahead);
-// thread (rg, c) forms rows rg + 36 m (m < 4) of column c, four K entries per LDS read.
+// walks.  Without S0, M_0 is not formed (S_1 = b_0).  The walk of the last segment
+// exports the final state.  M_s S_s runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: fp32 products and sums): wave w forms rows 16w .. 16w+15 of
+// the 16 columns, with its rows of M_s in registers (loaded one segment ahead) and S_s in
+// LDS, column-major.
 __device__ __forceinline__ int pair_slot(int a, int b) {   // packed slot of the pair {a, b}
   int dlt = (b - a) & 15, aa = a;
   if (dlt > 8) {
@@ -807,87 +817,71 @@ __device__ __forceinline__ int pair_slot(int a, int b) {   // packed slot of the
   return 16 * dlt + aa;
 }
 
-constexpr int SEG_MSTR = DPACK + 4;           // LDS row stride of M (floats)
-constexpr int SEG_RG = 36;                    // row groups: rows rg + 36 m, m < 4
-constexpr int SEG_THREADS = SEG_RG * 16;      // 576: nine waves
-constexpr int SEG_PIECES = DPACK * (DPACK / 4) / SEG_THREADS;   // 16-byte pieces of M per thread (9)
-static_assert(SEG_RG * 4 == DPACK && SEG_PIECES * SEG_THREADS == DPACK * (DPACK / 4), "combine layout");
+constexpr int SEG_WAVES = DPACK / 16;         // 9: one 16-row block of the packed state each
+constexpr int SEG_THREADS = SEG_WAVES * WAVE;
+constexpr int SEG_STR = DPACK + 4;            // LDS column stride of the state (floats)
+constexpr int SEG_KB = DPACK / 16;            // 16-column groups of M per lane row
 
 template <int DV>
 __global__ void __launch_bounds__(SEG_THREADS)
-kata_delta_seg_combine(const float* __restrict__ aff, const float* S0, float* __restrict__ S0seg, float* ST,
+kata_delta_seg_combine(const float* __restrict__ aff, const float* __restrict__ S0, float* __restrict__ S0seg,
                        int nseg) {
   constexpr int NCOL = DV + DPACK;
-  extern __shared__ __align__(16) float cmb[];
-  float* Ms = cmb;                                  // [DPACK][SEG_MSTR]
-  float* Sp = cmb + DPACK * SEG_MSTR;               // [16][DPACK]: column-major packed state
-  const int tid = threadIdx.x;
+  __shared__ __align__(16) float Sp[16 * SEG_STR];   // [16 columns][DPACK slots] (padded)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
   const int j = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  const int rg = tid >> 4, c = tid & 15;
+  // MFMA lanes: A lane l holds A[l%16][k = l/16], B lane l holds B[k = l/16][l%16], D lane l
+  // holds D[4(l/16) + i][l%16].  Lane (n, g) holds M's row 16 wave + n at columns
+  // 16 kb + 4g .. +3; the MFMA (kb, i) takes its column 16 kb + 4g + i as K index g, and
+  // the state column n at the same slot as the B operand.
+  const int n = lane & 15, g = lane >> 4;
   auto s0_at = [&](int a, int b, int cc) { return S0[(bh * P_DIM * P_DIM + 16 * a + b) * DV + 16 * j + cc]; };
   for (int e = tid; e < DPACK * 16; e += SEG_THREADS) {
     const int slot = e >> 4, cc = e & 15;
     const int a = slot & 15, b = (a + (slot >> 4)) & 15;
-    Sp[cc * DPACK + slot] = S0 ? 0.5f * (s0_at(a, b, cc) + s0_at(b, a, cc)) : 0.f;
+    Sp[cc * SEG_STR + slot] = S0 ? 0.5f * (s0_at(a, b, cc) + s0_at(b, a, cc)) : 0.f;
   }
-  f32x4 mreg[SEG_PIECES];
-  float breg[4];
-  auto load_map = [&](int sg) {
-    const float* blk = aff + (bh * nseg + sg) * DPACK * NCOL;
+  // the maps are loaded two segments ahead into two register sets, which alternate
+  f32x4 ma[SEG_KB], mb[SEG_KB], ba, bb;
+  auto load_map = [&](int sg, f32x4 (&mr)[SEG_KB], f32x4& br) {
+    const float* blk = aff + (bh * (nseg - 1) + sg) * DPACK * NCOL;
 #pragma unroll
-    for (int r = 0; r < SEG_PIECES; ++r) {
-      const int e = tid + SEG_THREADS * r;
-      mreg[r] = *reinterpret_cast<const f32x4*>(blk + (e / (DPACK / 4)) * NCOL + DV + 4 * (e % (DPACK / 4)));
-    }
+    for (int kb = 0; kb < SEG_KB; ++kb)
+      mr[kb] = *reinterpret_cast<const f32x4*>(blk + (16 * wave + n) * NCOL + DV + 16 * kb + 4 * g);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) breg[m] = blk[(rg + SEG_RG * m) * NCOL + 16 * j + c];   // b
+    for (int i = 0; i < 4; ++i) br[i] = blk[(16 * wave + 4 * g + i) * NCOL + 16 * j + n];   // b
   };
-  load_map(0);
-  for (int sg = 0; sg < nseg; ++sg) {
+  // one segment: write its start state; unless it is the last, S <- M S + b (then the
+  // register set is free for the map two segments on)
+  auto step = [&](int sg, f32x4 (&mr)[SEG_KB], f32x4& br) {
     const int64_t bw = bh * nseg + sg;
-#pragma unroll
-    for (int r = 0; r < SEG_PIECES; ++r) {
-      const int e = tid + SEG_THREADS * r;
-      *reinterpret_cast<f32x4*>(Ms + (e / (DPACK / 4)) * SEG_MSTR + 4 * (e % (DPACK / 4))) = mreg[r];
-    }
-    float acc[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = breg[m];
-    __syncthreads();   // M staged; the previous step's state written
-    if (sg + 1 < nseg) load_map(sg + 1);
-    for (int e = tid; e < 256 * 16; e += SEG_THREADS) {   // this segment's start state
-      const int ab = e >> 4, cc = e & 15;
-      S0seg[(bw * 256 + ab) * DV + 16 * j + cc] = Sp[cc * DPACK + pair_slot(ab >> 4, ab & 15)];
-    }
-    for (int k = 0; k < DPACK; k += 4) {
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(Sp + c * DPACK + k);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(Ms + (rg + SEG_RG * m) * SEG_MSTR + k);
-        acc[m] += mv[0] * sv[0] + mv[1] * sv[1] + mv[2] * sv[2] + mv[3] * sv[3];
-      }
-    }
-    __syncthreads();   // every thread has read the state and M
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Sp[c * DPACK + rg + SEG_RG * m] = acc[m];
-  }
-  __syncthreads();
-  if (ST) {   // one thread per pair a <= b and column writes both entries (S0 == ST allowed)
+    __syncthreads();   // the previous step's state written
     for (int e = tid; e < 256 * 16; e += SEG_THREADS) {
-      const int ab = e >> 4, cc = e & 15, a = ab >> 4, b = ab & 15;
-      if (a > b) continue;
-      float sab = 0.f, sba = 0.f, ch = Sp[cc * DPACK + pair_slot(a, b)];
-      if (S0) {
-        sab = s0_at(a, b, cc);
-        sba = s0_at(b, a, cc);
-        ch -= 0.5f * (sab + sba);
-      }
-      ST[(bh * P_DIM * P_DIM + 16 * a + b) * DV + 16 * j + cc] = sab + ch;
-      if (a != b) ST[(bh * P_DIM * P_DIM + 16 * b + a) * DV + 16 * j + cc] = sba + ch;
+      const int ab = e >> 4, cc = e & 15;
+      S0seg[(bw * 256 + ab) * DV + 16 * j + cc] = Sp[cc * SEG_STR + pair_slot(ab >> 4, ab & 15)];
     }
+    if (sg + 1 >= nseg) return false;   // the last segment has no map
+    f32x4 acc = br;
+    if (sg > 0 || S0) {   // S_0 = 0 without S0: M_0 was not formed
+#pragma unroll
+      for (int kb = 0; kb < SEG_KB; ++kb) {
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(&Sp[n * SEG_STR + 16 * kb + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mr[kb][i], sv[i], acc, 0, 0, 0);
+      }
+    }
+    if (sg + 3 < nseg) load_map(sg + 2, mr, br);   // segments 0 .. nseg - 2 have maps
+    __syncthreads();   // every wave has read the state
+    *reinterpret_cast<f32x4*>(&Sp[n * SEG_STR + 16 * wave + 4 * g]) = acc;
+    return true;
+  };
+  load_map(0, ma, ba);   // (nseg >= 2: segment 0 has a map)
+  if (nseg > 2) load_map(1, mb, bb);
+  for (int sg = 0;; sg += 2) {
+    if (!step(sg, ma, ba) || !step(sg + 1, mb, bb)) break;
   }
 }
-constexpr int SEG_COMBINE_SMEM = (DPACK * SEG_MSTR + 16 * DPACK) * 4;
 
 }  // namespace kata

@@ -325,10 +325,11 @@ def test_delta_chunked_workspace_and_validation():
         return (x + 255) // 256 * 256
     # u^, w^ and T per chunk, then one progress counter per column-block workgroup of the walk;
     # 16 sequences fill 64 of 1024 workgroup slots, so the plan cuts each walk into 16
-    # segments of 128 chunks: their affine maps (144 x (64 + 144) floats) and start states
+    # segments of 128 chunks: the affine maps (144 x (64 + 144) floats) of all but the last
+    # segment, whose walk exports the final state, and every segment's start state
     # (256 x 64 floats)
     head = 2 * uw + 16 * chunks * 64 * 64 * 4 + align(16 * (64 // 16) * 4)
-    assert n.value == head + 16 * 16 * 144 * (64 + 144) * 4 + 16 * 16 * 256 * 64 * 4
+    assert n.value == head + align(16 * 15 * 144 * (64 + 144) * 4) + 16 * 16 * 256 * 64 * 4
     # one walk per sequence: no segment blocks
     d.scan = Bd.KATA_SCAN_SEQUENTIAL
     assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
@@ -336,7 +337,7 @@ def test_delta_chunked_workspace_and_validation():
     # explicit segments of 100 chunks: 21 per sequence, the last of 48 chunks
     d.scan, d.scan_leaf = Bd.KATA_SCAN_ASSOC, 100
     assert lib.kata_forward_delta_chunked_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == Bd.KATA_OK
-    assert n.value == head + 16 * 21 * 144 * 208 * 4 + 16 * 21 * 256 * 64 * 4
+    assert n.value == head + align(16 * 20 * 144 * 208 * 4) + 16 * 21 * 256 * 64 * 4
     segs, per = ctypes.c_int64(0), ctypes.c_int64(0)
     assert lib.kata_forward_delta_chunked_plan(ctypes.byref(d), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
     assert (segs.value, per.value) == (21, 100)
@@ -350,6 +351,15 @@ def test_delta_chunked_workspace_and_validation():
         e = Bd.make_desc(B, H, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
         assert lib.kata_forward_delta_chunked_plan(ctypes.byref(e), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
         assert (segs.value, per.value) == want, (B, H, T)
+    # explicit one-chunk segments: B*H*segments stays within the 65535 workgroup rows of a
+    # launch, so 4096 sequences of 2048 chunks get 15 segments of 137 chunks, not 2048
+    for B, H, T, leaf, want in [(256, 16, 131072, 1, (15, 137)), (1, 16, 131072, 1, (2048, 1)),
+                                (4095, 16, 640, 1, (1, 10)), (3, 5, 64 * 9000, 1, (3000, 3))]:
+        e = Bd.make_desc(B, H, T, 64, 64, 64, Bd.KATA_BF16, Bd.KATA_BF16)
+        e.scan_leaf = leaf
+        assert lib.kata_forward_delta_chunked_plan(ctypes.byref(e), ctypes.byref(segs), ctypes.byref(per)) == Bd.KATA_OK
+        assert (segs.value, per.value) == want, (B, H, T)
+        assert B * H * segs.value <= 65535 and segs.value * per.value >= T // 64
     assert lib.kata_forward_delta_chunked_plan(None, None, None) == Bd.KATA_ERR_NULL
     fake = ctypes.c_void_p(0x1000)
     for fields, status in [({"chunk": 128}, Bd.KATA_ERR_UNSUPPORTED), ({"d": 32}, Bd.KATA_ERR_UNSUPPORTED),

@@ -345,6 +345,42 @@ def test_delta_chunked_segments_against_oracle(dtype, leaf):
     assert eA <= 1e-5 * float(A0.abs().max())
 
 
+@pytest.mark.parametrize("T,leaf,with_s0", [(100, 1, True), (100, 1, False), (64, 1, True), (700, 3, False),
+                                             (129, 2, False)])
+def test_delta_chunked_segments_edges(T, leaf, with_s0):
+    """Segment edge cases, fp32 inputs: two segments (only segment 0 has an affine map; the
+    second segment's walk exports S_T), one chunk (the plan keeps one walk), a ragged last
+    segment, and no initial state (segment 0 starts from zero, so its M is not formed and
+    the chain starts from b_0), against the oracle's recurrence and the one-walk form."""
+    B, H, dv = 1, 2, 64
+    case = I.make_forward("mid", B=B, H=H, T=T, seed=240 + T + leaf)
+    q32, k32, v32 = (x.float() for x in (case.q, case.k, case.v))
+    beta = I.make_beta(B, H, T, seed=240 + T, lo=0.0, hi=1.0)
+    S0 = torch.randn((B, H, 256, dv), generator=torch.Generator().manual_seed(240 + T)) / 4
+    q, k, v, P, b, S0d = to_dev(q32, k32, v32, case.P, beta, S0)
+    s0 = S0d if with_s0 else None
+    pl = kata.forward_delta_chunked_plan(B, H, T, 64, dv, in_dtype=torch.float32, scan_leaf=leaf)
+    segs, nch = pl["segments"], -(-T // 64)
+    assert segs == -(-nch // leaf) and pl["segment_chunks"] == min(leaf, nch)
+    y, ST = kata.forward_delta_chunked(q, k, v, P, b, S0=s0, out_dtype=torch.float32, return_state=True,
+                                       scan_leaf=leaf)
+    y1, S1 = kata.forward_delta_chunked(q, k, v, P, b, S0=s0, out_dtype=torch.float32, return_state=True,
+                                        scan="sequential")
+    torch.cuda.synchronize()
+    yr, Sr = O.delta_recurrence(q32.double().numpy(), k32.double().numpy(), v32.double().numpy(),
+                                case.P.double().numpy(), beta.double().numpy(),
+                                S0.double().numpy() if with_s0 else None)
+    sy, sS = slice_rel(y.cpu().numpy(), yr), slice_rel(ST.cpu().numpy(), Sr)
+    dy, dS = slice_rel(y.cpu().numpy(), y1.cpu().numpy()), slice_rel(ST.cpu().numpy(), S1.cpu().numpy())
+    print(f"[delta segment edges T={T} leaf={leaf} S0={with_s0}] segments {segs}: y {sy:.3e} S_T {sS:.3e}; "
+          f"vs one walk y {dy:.3e} S {dS:.3e}", flush=True)
+    assert sy <= TOL_F32 and sS <= TOL_F32
+    assert dy <= TOL_F32 and dS <= TOL_F32
+    if with_s0:   # the antisymmetric part of S0 passes through the last segment's export
+        St, A0 = ST.cpu().reshape(B, H, 16, 16, dv), S0.reshape(B, H, 16, 16, dv)
+        assert float((St - St.transpose(2, 3) - (A0 - A0.transpose(2, 3))).abs().max()) <= 1e-5
+
+
 def test_delta_chunked_segments_beta_zero_keep_state_exactly():
     """beta = 0 with one-chunk segments: every map is the identity with b = 0 in exact
     arithmetic (no correction is formed), so the chain hands every segment S0's symmetric

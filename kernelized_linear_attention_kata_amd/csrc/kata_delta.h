@@ -591,11 +591,15 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
       bb[r] = in.pb[r];
     }
     if (state_role) {
+      // published with the read weights (1 on the diagonal, 2 off it, 0 for the repeated
+      // delta = 8 slots a >= 8): powers of two, so the products equal weighted features
+      // times S exactly
 #pragma unroll
       for (int jt = 0; jt < 3; ++jt) {
         if (jt < 2 || own8) {
           const int d = dl(jt);
-          const float sx[4] = {Sacc[jt][0], Sacc[jt][1], Sacc[jt][2], Sacc[jt][3]};
+          const float wt = d == 0 ? 1.f : (d == 8 ? (g < 2 ? 2.f : 0.f) : 2.f);
+          const float sx[4] = {Sacc[jt][0] * wt, Sacc[jt][1] * wt, Sacc[jt][2] * wt, Sacc[jt][3] * wt};
           put(SB, d >> 1, (d & 1) * 4, sx);
         }
       }
@@ -612,18 +616,15 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
 #pragma unroll
     for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const f32x4*>(xs + ((4 * g + 4 * m) & 15));
     auto comp = [&](int e) { return xr[(e >> 2) & 3][e & 3]; };
-    const float w8 = g < 2 ? 2.f : 0.f;                // read weight of slot (8, 4g + i)
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < DKB; ++kk) {
+    for (int kk = 0; kk < DKB; ++kk) {   // (the read weights ride on the published S)
       const int d0 = 2 * kk, d1 = 2 * kk + 1;
-      const float wt0 = d0 == 0 ? 1.f : (d0 == 8 ? w8 : 2.f);
-      const float wt1 = d1 == 9 ? 0.f : 2.f;
       float xf[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xf[i] = comp(i) * comp(i + d0) * wt0;
-        xf[4 + i] = comp(i) * comp(i + d1) * wt1;
+        xf[i] = comp(i) * comp(i + d0);
+        xf[4 + i] = d1 == 9 ? 0.f : comp(i) * comp(i + d1);
       }
       acc = mma<SPLIT, true>(make8<SPLIT>(xf), frag(SB, kk), acc);
     }

@@ -432,8 +432,8 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 //    state to the next;
 //  * output waves (4..7): wave 4 + m computes, for token block m, Q^ S, the causal score
 //    tiles (Q^ K^^T o M) and y = Q^ S + (Q^ K^^T o M) E, off that chain.
-// Each SIMD runs one wave of each role, so the output work overlaps the state chain.
-// Four barriers per chunk: S and the inputs staged | X written | E written | chunk done.
+// Each SIMD runs one wave of each role, so the output work overlaps the state chain, and
+// two walks share a CU (at most 128 VGPRs).  Four barriers per chunk: S and the inputs staged | X written | E written | chunk done.
 // Token-K fragments use the permuted order of the accumulator tiles: slot i < 4 of
 // K-block kk, lane group g is token 32kk + 4g + i, slot 4 + i is token 32kk + 16 + 4g + i
 // (and slot i < 4 of the feature K-block kk is (2kk, 4g + i), slot 4 + i is
@@ -461,7 +461,7 @@ kata_delta_prep(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 constexpr int DKB = 5;   // feature K-blocks of the packed state: delta pairs (0,1) .. (8, 9 = none)
 
 template <typename TIn, typename TOut, int DV, bool AFFINE = false>
-__global__ void __launch_bounds__(AFFINE ? 256 : 512, AFFINE ? 4 : 1)
+__global__ void __launch_bounds__(AFFINE ? 256 : 512, AFFINE ? 4 : 2)
 kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const float* __restrict__ Wh,
                  const bf16* __restrict__ Tf,
                  const TIn* __restrict__ v, const float* __restrict__ beta, const float* S0, float* ST,
@@ -498,7 +498,7 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   const int64_t nch = min<int64_t>(seg_chunks, n_chunks - c0);   // chunks of this walk
   const int64_t tok0 = c0 * DC;
   const bool couple_on = !AFFINE && nseg == 1;        // progress coupling: whole-sequence walks
-  constexpr int PF = AFFINE ? 1 : 2;                  // chunks of input prefetch
+  constexpr int PF = 1;                               // chunks of input prefetch (one set)
   const int col = 16 * j + n;                         // state column of this lane
   const bool vcols = !AFFINE || j < DV / 16;          // (workgroup-uniform) a value column block
   if (AFFINE && !vcols && seg == 0 && !S0) return;    // segment 0 starts from 0: M unused
@@ -548,27 +548,30 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     *reinterpret_cast<bf16x4*>(&SB[tid >> 6][DKB - 1][lane][4]) = z;
   }
 
-  // per-chunk inputs, prefetched PF chunks ahead into PF register sets (for two, the chunk
-  // loop is unrolled by two so each set has a static name).  The AFFINE walks prefetch one
-  // chunk ahead: one register set less keeps four of them on a CU.  Threads 0..255 stage u^, threads
-  // 256..511 w^ (AFFINE: threads 0..255 w^, no u^); the state waves also take T (their own
-  // hi/lo A-fragments), v and beta.
+  // per-chunk inputs, prefetched one chunk ahead into one register set (a second set, two
+  // chunks ahead, would cost the registers that let two walks, or four AFFINE walks, share
+  // a CU).  Threads 0..255 stage u^, threads 256..511 w^ (AFFINE: threads 0..255 w^, no
+  // u^); the state waves also take T (their own hi/lo A-fragments), v and beta.
   struct Inputs {
     f32x4 puw;
     Op8<true> pt[2];
     uint32_t pv[4];   // raw bits of v (converted at use)
     float pb[4];
   };
+  // T is fetched apart from the rest (fetch_t), after its one use in the step, so the
+  // step reads it from the register set itself with no copy.
+  auto fetch_t = [&](Inputs& in, int64_t c) {
+    const bf16* tf = Tf + (bh * n_chunks + c0 + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
+      in.pt[kk].lo = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16 + 8);
+    }
+  };
   auto fetch = [&](Inputs& in, int64_t c) {
     const int64_t rbase = (bh * n_chunks + c0 + c) * DC;
     in.puw = *reinterpret_cast<const f32x4*>(((AFFINE || !state_role) ? Wh : Uh) + rbase * P_DIM + 4 * (tid & 255));
     if (state_role) {
-      const bf16* tf = Tf + (bh * n_chunks + c0 + c) * (DC * DC * 2) + ((mb * 2) * WAVE + lane) * 16;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        in.pt[kk].hi = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16);
-        in.pt[kk].lo = *reinterpret_cast<const bf16x8*>(tf + kk * WAVE * 16 + 8);
-      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = (int)(c * DC) + 16 * mb + 4 * g + r;
@@ -583,7 +586,6 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
   auto step = [&](Inputs& in, int64_t c) {
     // ---- stage: inputs to LDS, packed S to B-fragments (K-block dl / 2, half dl % 2)
     *reinterpret_cast<f32x4*>(((AFFINE || !state_role) ? &Wsm[0][0] : &Us[0][0]) + 4 * (tid & 255)) = in.puw;
-    const Op8<true> tfr[2] = {in.pt[0], in.pt[1]};
     float vv[4], bb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -666,7 +668,8 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     if (state_role) {
       f32x4 accE = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(tfr[kk], frag(XB, kk), accE);
+      for (int kk = 0; kk < 2; ++kk) accE = mma<true, true>(in.pt[kk], frag(XB, kk), accE);
+      if (c + PF < nch) fetch_t(in, c + PF);
       const float ex[4] = {accE[0], accE[1], accE[2], accE[3]};
       put(EB, mb >> 1, (mb & 1) * 4, ex);
     } else {
@@ -740,19 +743,14 @@ kata_delta_chunk(int* __restrict__ prog, const float* __restrict__ Uh, const flo
     __syncthreads();
   };
 
-  Inputs ia{}, ib{};   // zeroed: the output waves load only puw and never read the rest
-  if (nch > 0) fetch(ia, 0);
-  if constexpr (PF == 1) {
-    for (int64_t c = 0; c < nch; ++c) step(ia, c);
-  } else {
-    if (nch > 1) fetch(ib, 1);
-    int64_t c = 0;
-    for (; c + 1 < nch; c += 2) {
-      if (couple_on && c % COUPLE_EVERY == 0) couple(c);
-      step(ia, c);
-      step(ib, c + 1);
-    }
-    if (c < nch) step(ia, c);
+  Inputs in{};   // zeroed: the output waves load only puw and never read the rest
+  if (nch > 0) {
+    fetch(in, 0);
+    if (state_role) fetch_t(in, 0);
+  }
+  for (int64_t c = 0; c < nch; ++c) {
+    if (couple_on && c % COUPLE_EVERY == 0) couple(c);
+    step(in, c);
   }
   if (couple_on && tid == 0)   // done: nobody waits for this workgroup any more
     __hip_atomic_store(myprog + j, (int)(nch + COUPLE_LAG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

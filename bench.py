@@ -1003,14 +1003,24 @@ def main():
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
     if args.copy_calibration:
+        # Plain device copies of MIB MiB: the reference for the HBM counters (1 GiB, five
+        # copies) and, at small sizes, the time a copy of a kernel's own bytes takes (after
+        # a clock settle, 400 copies cycling over 8 buffer pairs).
         import torch
         n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        pairs, launches = (8, 400) if args.copy_calibration <= 64 else (1, 5)
+        srcs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(pairs)]
+        dsts = [torch.empty_like(srcs[0]) for _ in range(pairs)]
+        if pairs > 1:
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < args.settle_s:
+                for i in range(pairs):
+                    dsts[i].copy_(srcs[(i + 3) % pairs])
+                torch.cuda.synchronize()
+        for i in range(launches):
+            dsts[i % pairs].copy_(srcs[(i + 3) % pairs])
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": launches}))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

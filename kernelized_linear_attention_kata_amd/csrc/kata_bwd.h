@@ -165,9 +165,9 @@ __device__ __forceinline__ Op4<true> read_pt(const bf16* PTs, int db, int lane) 
 }
 
 // Given the projected-space gradient of one 16-token block (lane (t, g) holds
-// d_t[4g + r], t = the block's token n): store P^T d_t (input-space gradient, bf16, four
-// consecutive columns per lane per 16-column block) and add d x^T to this wave's dP
-// accumulators.
+// d_t[4g + r], t = the block's token n): store P^T d_t (input-space gradient, bf16; lane
+// (t, g) forms columns 16 db + 4g + r, which store_row sends out as whole 128-byte rows)
+// and add d x^T to this wave's dP accumulators.
 // xr are the block's input rows as loaded for the projection (lane (t, g) holds
 // x_t[16 g + 8 kk + i]).  d^T comes from one identity MFMA per hi/lo half (exact), x^T
 // from column-selector MFMAs (exact), so dP takes one MFMA per half.
@@ -178,11 +178,10 @@ __device__ __forceinline__ void grad_head(const f32x4& d, const bf16* PTs, const
   const int n = lane & 15, g = lane >> 4;
   float dv4[4] = {d[0], d[1], d[2], d[3]};
   const Op4<true> df = make4<true>(dv4);
+  f32x4 o[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const f32x4 o = mma<true, true>(read_pt(PTs, db, lane), df, zero4());   // lane (t, g): column 16db + 4g + r
-    Store4<bf16>::st(out, row_byte + (16 * db + 4 * g) * 2, o);
-  }
+  for (int db = 0; db < 4; ++db) o[db] = mma<true, true>(read_pt(PTs, db, lane), df, zero4());   // column 16db + 4g + r
+  store_row<BS, bf16>(o, 1.f, out, row_byte / 2, n, g);
   // d^T: C[t][a] = sum_k d_t[k] [k == a]; lane (a, g) then holds d_{4g + r}[a]
   bf16x4 eye;
 #pragma unroll
@@ -885,9 +884,7 @@ kata_bwd_key(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16*
             O[nb] = mma<false, false>(load_vf<S>(gf, nullptr, jj, nb, lane), af, O[nb]);
         }
       }
-      const int row = ((t0 + s_loc) * 64 + 4 * g) * 2;
-#pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) Store4<bf16>::st(r_dv, row + nb * 32, O[nb]);
+      store_row<S, bf16>(O, 1.f, r_dv, (t0 + s_loc) * 64, s_loc, g);   // whole 128-byte rows
       if (c > 0) key_grad(chunk_t0(c - 1), (c - 1) & 1, kprev, dwprev);
       kprev[0] = kcur[0];
       kprev[1] = kcur[1];

@@ -284,16 +284,48 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
   den = row_pair_sum<32>(den);
   const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
   __amdgpu_buffer_rsrc_t ry = make_rsrc(y + bh * T * FL_DV, T * FL_DV * (int64_t)sizeof(TOut));
-  const int row = tq < T ? (int)(tq * FL_DV * (int64_t)sizeof(TOut)) : BUF_OOB;
+  if constexpr (IsBf16<TOut>::value) {
+    // The block's 128 x 64 bf16 output tile goes through the LDS ring, idle by now: a
+    // lane holds 4-column pieces of its query's row, which stored directly would leave
+    // as 16-byte pieces of 128-byte lines.  Read back as 16-byte pieces in row order,
+    // every store instruction writes 8 whole rows.
+    constexpr int OSTR = FL_DV + 8;                  // bf16 row stride: 144 B, 16-byte aligned
+    static_assert(FL_QB * OSTR * 2 <= FL_RING * FL_BUF_BYTES, "the output tile fits the ring");
+    bf16* ot = reinterpret_cast<bf16*>(sm);
+    __syncthreads();                                 // every wave is done with the last block
+    const int ql = 32 * wave + c32;                  // this lane's query within the block
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {                    // columns 32ct + 8j + 4hh .. +3
-      f32x4 o;
+      for (int j = 0; j < 4; ++j) {                  // columns 32ct + 8j + 4hh .. +3
+        bf16x4 b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = O[ct][4 * j + r] * inv;
-      const int col = 32 * ct + 8 * j + 4 * hh;
-      Store4<TOut>::st(ry, row >= BUF_OOB ? BUF_OOB : row + col * (int)sizeof(TOut), o);
+        for (int r = 0; r < 4; ++r) b[r] = (bf16)(O[ct][4 * j + r] * inv);
+        *reinterpret_cast<bf16x4*>(ot + ql * OSTR + 32 * ct + 8 * j + 4 * hh) = b;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < FL_QB * FL_DV / 8 / (64 * FL_WAVES); ++p) {
+      const int piece = p * 64 * FL_WAVES + tid;     // 8-column piece c8 of block row rl
+      const int rl = piece >> 3, c8 = piece & 7;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(ot + rl * OSTR + 8 * c8);
+      const int64_t tr = (int64_t)qb * FL_QB + rl;
+      const int off = tr < T ? (int)(tr * FL_DV * 2) + 16 * c8 : BUF_OOB;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), ry, off, 0, Y_STORE_POLICY);
+    }
+  } else {
+    const int row = tq < T ? (int)(tq * FL_DV * (int64_t)sizeof(TOut)) : BUF_OOB;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {                  // columns 32ct + 8j + 4hh .. +3
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = O[ct][4 * j + r] * inv;
+        const int col = 32 * ct + 8 * j + 4 * hh;
+        Store4<TOut>::st(ry, row >= BUF_OOB ? BUF_OOB : row + col * (int)sizeof(TOut), o);
+      }
     }
   }
 }

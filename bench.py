@@ -960,6 +960,37 @@ def bench_backward(args):
     print(json.dumps(result), flush=True)
 
 
+def stream_probe(args):
+    """Plain torch kernels over 512 MiB fp32 tensors (2 GiB per pattern, eight times the
+    last-level cache): a sum (pure read), a copy (1 read : 1 write) and addcmul (3 reads :
+    1 write, the intra pass's mix).  Each runs after the usual clock settle, 20 times, timed
+    with events; the JSON line gives each pattern's bytes moved per second."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = (512 << 20) // 4
+    a, b, c, d = (torch.full((n,), 1.0 + i, device=dev) for i in range(4))
+    acc = torch.empty((), device=dev)
+    pats = {"read": (lambda: torch.sum(a, dim=0, out=acc), 4 * n),
+            "copy_1r1w": (lambda: d.copy_(a), 8 * n),
+            "addcmul_3r1w": (lambda: torch.addcmul(a, b, c, out=d), 16 * n)}
+    out = {}
+    for name, (fn, nbytes) in pats.items():
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle_s:
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        out[name] = {"bytes": nbytes, "ms": round(ms, 4), "GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "frac_of_8TBps": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"probe": "plain torch streaming kernels, 512 MiB fp32 tensors", "patterns": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -999,9 +1030,15 @@ def main():
                     help="time the decay-gated forward (kata_forward_decay, gates in [0.9, 1]) instead")
     ap.add_argument("--bwd-cpu-tokens", type=int, default=16384,
                     help="prefix length of the oracle's backward sample (CPU baseline of --backward)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only time plain torch streaming kernels (pure read, 1:1 copy, 3 reads : 1 write) "
+                         "over footprints past the last-level cache: the memory system's practical rates")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args()
+    if args.stream_probe:
+        stream_probe(args)
+        return
     if args.copy_calibration:
         # Plain device copies of MIB MiB: the reference for the HBM counters (1 GiB, five
         # copies) and, at small sizes, the time a copy of a kernel's own bytes takes (after

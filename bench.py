@@ -34,6 +34,8 @@ stamps one.
     python bench.py --factors 2  # KATA-M2 (two concatenated PSD factors) on the long-context workload
     python bench.py --workload mid     # the forward on the mid workload (B=4 H=8 T=4096), warm and flushed
     python bench.py --workload lm340m  # the forward on the 340M-layer workload (B=8 H=16 T=2048)
+    python bench.py --stream-probe     # torch's streaming kernels (read, copy, 3:1) for the practical ceilings
+    python bench.py --copy-calibration MIB  # plain device copies (counter calibration; scan-sized copies)
 
 The decode mode prefills 256 streams x 16 heads with 8192 tokens (kata_forward with
 the final-state export), then times 1024 kata_decode_step calls, each of which reads

@@ -198,11 +198,6 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
   const int tq = q0 + c32;                           // this lane's query
   const bf16x8 ub = *reinterpret_cast<const bf16x8*>(base + (int64_t)tq * P_DIM + 8 * hh);
   const bf16x8 ubl = *reinterpret_cast<const bf16x8*>(base + (tpad + tq) * P_DIM + 8 * hh);
-  // the u loads must complete here, before any ring copy is in flight: consumed by an
-  // (empty) asm statement, they get their wait at this point; otherwise the loads sink
-  // below the first copies and their wait, at the first use of u in the loop, covers
-  // every copy in flight
-  asm volatile("" ::"v"(ub), "v"(ubl));
   f32x16 O[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -226,6 +221,11 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
 #pragma unroll
   for (int i = 0; i < FL_RING - 1; ++i)
     if (i < nkb) dma(i);
+  // the u loads complete here, together with the first ring copies (both in flight at
+  // once, one memory latency at the workgroup's start instead of two): consumed by an
+  // (empty) asm statement, they get their wait at this point; otherwise their wait
+  // sinks to the first use of u in the loop and covers every later copy in flight
+  asm volatile("" ::"v"(ub), "v"(ubl));
   for (int kb = 0; kb < nkb; ++kb) {
     // this wave's pieces of block kb have landed once at most the later blocks' are
     // outstanding; the barrier then makes every wave's pieces visible and also ends

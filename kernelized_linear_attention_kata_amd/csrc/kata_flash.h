@@ -147,11 +147,12 @@ constexpr int FL_W_BYTES = FL_KB * P_DIM * 2;
 constexpr int FL_V_BYTES = FL_KB * FL_DV * 2;
 constexpr int FL_PIECES = 12;   // 1 KB pieces per buffer
 constexpr int FL_BUF_BYTES = FL_PIECES * 1024;
-// Two buffers (the copy of block kb + 1 runs during block kb): 24 KB per workgroup, five
-// workgroups of four waves per CU (5 waves per SIMD, the register budget).  Measured
-// against it: three workgroups of eight waves (6 waves per SIMD) 3% slower; 16 KB buffers
-// whose last 4 KB were copies read past the workspace (zeros), so that eight waves had
-// equal shares, 6% slower; three 12 KB buffers at four workgroups per CU, 4% slower.
+// Two buffers (the copy of block kb + 1 runs during block kb): 24 KB per workgroup, six
+// workgroups of four waves per CU (6 waves per SIMD: 78 VGPRs, the register budget).
+// Measured against five per CU: three workgroups of eight waves (6 waves per SIMD) 3%
+// slower; 16 KB buffers whose last 4 KB were copies read past the workspace (zeros), so
+// that eight waves had equal shares, 6% slower; three 12 KB buffers at four workgroups per
+// CU, 4% slower (21% against the kernel with the staged output).
 constexpr int FL_RING = 2;
 constexpr int FL_DMA_PER_WAVE = FL_PIECES / FL_WAVES;
 static_assert(FL_PIECES % FL_WAVES == 0 && FL_PIECES * 1024 == 2 * FL_W_BYTES + FL_V_BYTES,
@@ -165,7 +166,7 @@ typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_s_waitcnt(((N) & 0xf) | (((N) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
 
 template <typename TOut>
-__global__ void __launch_bounds__(64 * FL_WAVES, 5)
+__global__ void __launch_bounds__(64 * FL_WAVES, 6)
 kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, int64_t tpad, int nbh) {
   __shared__ __align__(16) unsigned char sm[FL_RING * FL_BUF_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -248,12 +249,6 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
       if (!full && s0 > q0 + 31) continue;           // wave-uniform
       const bf16x8 wf = *reinterpret_cast<const bf16x8*>(Wl + (x * WAVE + lane) * 8);
       const bf16x8 wfl = *reinterpret_cast<const bf16x8*>(Wlo + (x * WAVE + lane) * 8);
-      bf16x8 vf[2][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          vf[a][ct] = *reinterpret_cast<const bf16x8*>(Vl + (((2 * x + a) * 2 + ct) * WAVE + lane) * 8);
       f32x16 zero16;
 #pragma unroll
       for (int i = 0; i < 16; ++i) zero16[i] = 0.f;
@@ -275,8 +270,11 @@ kata_flash_attn(const bf16* __restrict__ ws, TOut* __restrict__ y, int64_t T, in
           den += a2[8 * a + i];
           af[i] = (bf16)a2[8 * a + i];
         }
+        // V fragments read at their use, not with the score operands: 78 VGPRs, six
+        // workgroups per CU (reading all four up front needs 82 VGPRs, five per CU)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) O[ct] = mfma3232(vf[a][ct], af, O[ct]);
+        for (int ct = 0; ct < 2; ++ct)
+          O[ct] = mfma3232(*reinterpret_cast<const bf16x8*>(Vl + (((2 * x + a) * 2 + ct) * WAVE + lane) * 8), af, O[ct]);
       }
     }
   }
